@@ -1,0 +1,101 @@
+"""Exact decoders for the storage formats, written from the format definitions.
+
+TEST INFRASTRUCTURE ONLY (see the package docstring).
+
+* FP8 E4M3FN (OCP 8-bit floating point specification): 1 sign bit, 4 exponent
+  bits with bias 7, 3 mantissa bits; exponent 0 is subnormal (m/8 * 2^-6);
+  S.1111.111 is NaN; there is no infinity; largest finite value 448.
+* E2M1 (OCP Microscaling Formats v1.0, FP4): 1 sign bit (bit 3), 2 exponent
+  bits with bias 1, 1 mantissa bit: magnitudes {0, 0.5, 1, 1.5, 2, 3, 4, 6}.
+  Two elements per byte, element 2i in the low nibble (a reading: the pages
+  give no packing, only "FP4", blog §"SWA bounded replay").
+* E8M0 (OCP MX v1.0 shared scale): unsigned 8-bit exponent, value 2^(e-127),
+  0xFF is NaN.
+* bfloat16: the upper 16 bits of an IEEE binary32.
+
+All tables are computed here from these definitions; nothing is read from the
+GPU library.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+
+def _e4m3_value(code: int) -> float:
+    s = (code >> 7) & 1
+    e = (code >> 3) & 0xF
+    m = code & 0x7
+    if e == 0xF and m == 0x7:
+        return float("nan")
+    if e == 0:
+        v = (m / 8.0) * 2.0 ** (1 - 7)
+    else:
+        v = (1.0 + m / 8.0) * 2.0 ** (e - 7)
+    return -v if s else v
+
+
+def _e2m1_value(code: int) -> float:
+    s = (code >> 3) & 1
+    e = (code >> 1) & 0x3
+    m = code & 0x1
+    if e == 0:
+        v = m * 0.5                      # subnormal: m/2 * 2^(1-1)
+    else:
+        v = (1.0 + m / 2.0) * 2.0 ** (e - 1)
+    return -v if s else v
+
+
+E4M3_TABLE = np.array([_e4m3_value(c) for c in range(256)], dtype=np.float64)
+E2M1_TABLE = np.array([_e2m1_value(c) for c in range(16)], dtype=np.float64)
+
+
+def e4m3(codes: np.ndarray) -> np.ndarray:
+    """uint8 array of E4M3FN codes -> float64 values (same shape)."""
+    return E4M3_TABLE[np.asarray(codes, dtype=np.uint8)]
+
+
+def e2m1_unpack(packed: np.ndarray) -> np.ndarray:
+    """uint8 [..., D/2] packed E2M1 -> float64 [..., D]; element 2i = low nibble of byte i."""
+    p = np.asarray(packed, dtype=np.uint8)
+    lo = E2M1_TABLE[p & 0x0F]
+    hi = E2M1_TABLE[p >> 4]
+    out = np.empty(p.shape[:-1] + (2 * p.shape[-1],), dtype=np.float64)
+    out[..., 0::2] = lo
+    out[..., 1::2] = hi
+    return out
+
+
+def e8m0(e: np.ndarray) -> np.ndarray:
+    """uint8 E8M0 exponents -> float64 scales 2^(e-127); 255 -> NaN."""
+    e = np.asarray(e, dtype=np.int64)
+    out = np.ldexp(1.0, e - 127).astype(np.float64)
+    return np.where(e == 255, np.nan, out)
+
+
+def bf16(bits: np.ndarray) -> np.ndarray:
+    """uint16 bfloat16 bit patterns -> float64."""
+    b = np.asarray(bits).astype(np.uint32) << 16
+    return b.view(np.float32).astype(np.float64)
+
+
+def global_rows(codes: np.ndarray, e8: np.ndarray, rowscale) -> np.ndarray:
+    """Decode global-latent rows: V[j,d] = e2m1(nib(j,d)) * 2^(E[j, d//32]-127) * rho_j.
+
+    codes uint8 [R, D/2], e8 uint8 [R, D/32], rowscale float32 [R] or None (rho = 1).
+    """
+    vals = e2m1_unpack(codes)
+    R, D = vals.shape
+    scale = np.repeat(e8m0(e8), 32, axis=1)
+    assert scale.shape == (R, D)
+    v = vals * scale
+    if rowscale is not None:
+        v = v * np.asarray(rowscale, dtype=np.float64)[:, None]
+    return v
+
+
+def window_rows(codes: np.ndarray, scale) -> np.ndarray:
+    """Decode sliding-window rows: X[u,d] = e4m3(byte) * sigma_u (sigma = 1 when None)."""
+    x = e4m3(codes)
+    if scale is not None:
+        x = x * np.asarray(scale, dtype=np.float64)[..., None]
+    return x

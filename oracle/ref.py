@@ -1,0 +1,172 @@
+"""Reference (fp64) definitions of the three steps and of the fused decode step.
+
+TEST INFRASTRUCTURE ONLY (see the package docstring).
+
+Layout conventions shared with the GPU library's boundary (the arrays are the
+same bytes; the code is not shared):
+
+* sequence b owns cache rows [seq_start[b], seq_start[b+1]); its position j
+  is row seq_start[b] + j;
+* queries are grouped by sequence: queries of b are t in [q_start[b], q_start[b+1]);
+* q_pos[t] = p_t, the query's absolute position (the causal bound, inclusive);
+* the window buffer of sequence b holds W rows; row u has position swa_pos0[b] + u;
+* swa_clip[t] = s_t, the replay clip start (None: no clip).
+
+Readings where the pages are silent (each restated where it is used):
+  R1  indexer form S = sum_h w_h * max(0, kappa_j <q_h, k_j>)   [parity unpinned vs the pages]
+  R2  top-k order: score descending, ties to the lower position; output sorted
+      ascending by position, padded with -1
+  R3  K = V = the decoded latent row (multi-query attention over one latent
+      shared by all heads)                                      [parity unpinned vs the pages]
+  R4  one softmax over the union of selected global rows and visible window
+      rows; a position in both sets contributes twice (two representations)
+  R5  the window of query t is positions [max(p_t - W + 1, s_t, 0), p_t]
+      that exist in the buffer; rows before the clip s_t are excluded
+  R6  an empty row set gives O = 0 and LSE = -inf
+"""
+from __future__ import annotations
+
+import numpy as np
+
+from . import codecs
+
+
+def _q_seq(q_start: np.ndarray) -> np.ndarray:
+    q_start = np.asarray(q_start, dtype=np.int64)
+    counts = np.diff(q_start)
+    return np.repeat(np.arange(len(counts)), counts)
+
+
+def scored_positions(t, q_pos, seq_len, cand=None):
+    """J_t: the positions query t scores, with the column each score is stored in.
+
+    Dense mode: J_t = {0..p_t}, column = position.  Candidate mode (blog
+    §Kernels, "Logits MQA creux": late indexer layers take their top-k from a
+    fixed set of 16K candidate positions): J_t = {cand[t,i] : cand[t,i] <= p_t,
+    0 <= cand[t,i] < seq_len}, column = i.
+    """
+    p = int(q_pos[t])
+    if cand is None:
+        pos = np.arange(0, min(p, seq_len - 1) + 1, dtype=np.int64)
+        return pos, pos.copy()
+    c = np.asarray(cand[t], dtype=np.int64)
+    keep = (c >= 0) & (c <= p) & (c < seq_len)
+    cols = np.nonzero(keep)[0]
+    return c[cols], cols
+
+
+def score(qI, w, kI, kscale, seq_start, q_start, q_pos, cand=None, ld=None):
+    """Indexer scores S[t, col] (float64, -inf where nothing is scored).
+
+    Blog §Kernels ("Logits MQA creux"): the indexer produces one score per
+    context position, from which top-k positions are taken; the sparse variant
+    scores only the candidate set.  Reading R1 gives the per-position value:
+    S[t,j] = sum_h w[t,h] * max(0, kappa_j * sum_d qI[t,h,d] * kI[row(j),d]).
+    """
+    qI = np.asarray(qI)
+    T = qI.shape[0]
+    seq_start = np.asarray(seq_start, dtype=np.int64)
+    qs = _q_seq(q_start)
+    if ld is None:
+        ld = np.asarray(cand).shape[1] if cand is not None else int(np.max(q_pos)) + 1
+    S = np.full((T, ld), -np.inf, dtype=np.float64)
+    for t in range(T):
+        b = qs[t]
+        base = seq_start[b]
+        n = int(seq_start[b + 1] - base)
+        pos, cols = scored_positions(t, q_pos, n, cand)
+        if pos.size == 0:
+            continue
+        rows = base + pos
+        Q = codecs.e4m3(qI[t])                       # [Hi, Di]
+        K = codecs.e4m3(np.asarray(kI)[rows])        # [n, Di]
+        dots = K @ Q.T                               # [n, Hi]
+        if kscale is not None:
+            dots = dots * np.asarray(kscale, dtype=np.float64)[rows][:, None]
+        S[t, cols] = np.maximum(dots, 0.0) @ np.asarray(w[t], dtype=np.float64)
+    return S
+
+
+def topk(S, k, cand=None):
+    """Top-k positions per query (reading R2), int64 [T, k], ascending, -1 padded.
+
+    Entries equal to -inf are not in J_t and are never selected.  With a
+    candidate list the returned values are positions cand[t, col].
+    """
+    S = np.asarray(S, dtype=np.float64)
+    T, L = S.shape
+    out = np.full((T, k), -1, dtype=np.int64)
+    for t in range(T):
+        cols = np.nonzero(S[t] != -np.inf)[0]
+        pos = cols if cand is None else np.asarray(cand[t], dtype=np.int64)[cols]
+        order = np.lexsort((pos, -S[t, cols]))       # primary: -score, secondary: position
+        take = np.sort(pos[order[:k]])
+        out[t, :take.size] = take
+    return out
+
+
+def window_positions(t, b, q_pos, swa_pos0, swa_clip, W):
+    """Buffer slots u (and positions) visible to query t (reading R5)."""
+    p = int(q_pos[t])
+    lo = max(p - W + 1, 0)
+    if swa_clip is not None:
+        lo = max(lo, int(swa_clip[t]))
+    pos = int(swa_pos0[b]) + np.arange(W, dtype=np.int64)
+    u = np.nonzero((pos >= lo) & (pos <= p))[0]
+    return u, pos[u]
+
+
+def attend(q, kv_codes, kv_e8m0, kv_rowscale, idx, swa, swa_scale, swa_pos0, swa_clip,
+           seq_start, q_start, q_pos, W, sm_scale):
+    """Sparse MQA attention over selected global rows plus the visible window rows.
+
+    Blog §Kernels (MegaAttention with NVFP4 KV): sparse attention reading the
+    FP4 compressed KV; blog §"SWA bounded replay": a global KV shared across
+    layers in FP4 and an uncompressed FP8 window of the last 128 positions;
+    blog §"Performances agentiques": the KV latent is shared by all heads.
+    For each query t and head h (readings R3, R4, R6):
+        rows  = {V[j] : j in idx[t], j >= 0} + {X[u] : u visible (R5)}
+        l_x   = sm_scale * <q[t,h], row_x>
+        O     = sum_x exp(l_x - m) row_x / sum_x exp(l_x - m),   m = max_x l_x
+        LSE   = m + ln(sum_x exp(l_x - m))
+    q is bf16 bits (uint16 [T, Hq, D]); returns float64 O [T, Hq, D], LSE [T, Hq].
+    """
+    qv = codecs.bf16(q)
+    T, Hq, D = qv.shape
+    seq_start = np.asarray(seq_start, dtype=np.int64)
+    qs = _q_seq(q_start)
+    idx = np.asarray(idx, dtype=np.int64)
+    O = np.zeros((T, Hq, D), dtype=np.float64)
+    LSE = np.full((T, Hq), -np.inf, dtype=np.float64)
+    for t in range(T):
+        b = qs[t]
+        sel = idx[t][idx[t] >= 0]
+        rows = seq_start[b] + sel
+        Vg = codecs.global_rows(np.asarray(kv_codes)[rows], np.asarray(kv_e8m0)[rows],
+                                None if kv_rowscale is None else np.asarray(kv_rowscale)[rows])
+        u, _ = window_positions(t, b, q_pos, swa_pos0, swa_clip, W)
+        Xw = codecs.window_rows(np.asarray(swa)[b][u],
+                                None if swa_scale is None else np.asarray(swa_scale)[b][u])
+        R = np.concatenate([Vg.reshape(-1, D), Xw.reshape(-1, D)], axis=0)
+        if R.shape[0] == 0:
+            continue
+        L = sm_scale * (qv[t] @ R.T)                 # [Hq, nrows]
+        m = L.max(axis=1, keepdims=True)
+        e = np.exp(L - m)
+        Z = e.sum(axis=1, keepdims=True)
+        O[t] = (e @ R) / Z
+        LSE[t] = (m + np.log(Z))[:, 0]
+    return O, LSE
+
+
+def decode_step(wl_np: dict, k=None, cand=None):
+    """score -> topk -> attend on one batch (dict of numpy arrays, keys as in synth.Workload)."""
+    a = wl_np
+    k = a["k"] if k is None else k
+    S = score(a["qI"], a["w"], a["kI"], a.get("kscale"), a["seq_start"], a["q_start"],
+              a["q_pos"], cand=cand)
+    idx = topk(S, k, cand=cand)
+    O, LSE = attend(a["q"], a["kv_codes"], a["kv_e8m0"], a.get("kv_rowscale"), idx, a["swa"],
+                    a.get("swa_scale"), a["swa_pos0"], a.get("swa_clip"), a["seq_start"],
+                    a["q_start"], a["q_pos"], a["W"], a["sm_scale"])
+    return S, idx, O, LSE

@@ -1,0 +1,164 @@
+"""Shared test helpers: workload -> numpy views for the oracle, brute-force drivers, comparators."""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+import torch
+
+from oracle import brute
+
+
+def np_inputs(wl) -> dict:
+    """synth.Workload (any device) -> dict of numpy arrays in the oracle's argument names."""
+    w = wl.cpu()
+    a = {}
+    for name in ("seq_start", "q_start", "q_pos", "qI", "w", "kI", "kscale", "kv_codes",
+                 "kv_e8m0", "kv_rowscale", "swa", "swa_scale", "swa_pos0", "swa_clip", "cand"):
+        v = getattr(w, name)
+        a[name] = None if v is None else v.numpy()
+    a["q"] = w.q.view(torch.int16).numpy().view(np.uint16)
+    for name in ("k", "W", "sm_scale", "Hi", "Di", "Hq", "D", "T", "B", "max_ctx"):
+        a[name] = getattr(w, name)
+    return a
+
+
+def q_seq_of(a) -> list:
+    qs = []
+    for b in range(len(a["q_start"]) - 1):
+        qs += [b] * int(a["q_start"][b + 1] - a["q_start"][b])
+    return qs
+
+
+def brute_scores(a, cand=None) -> list:
+    """Per query: dict {column: score} from the scalar definition."""
+    out = []
+    qs = q_seq_of(a)
+    for t in range(a["T"]):
+        b = qs[t]
+        base = int(a["seq_start"][b])
+        n = int(a["seq_start"][b + 1]) - base
+        p = int(a["q_pos"][t])
+        cols = {}
+        if cand is None:
+            items = [(j, j) for j in range(0, min(p, n - 1) + 1)]
+        else:
+            items = [(i, int(c)) for i, c in enumerate(cand[t]) if 0 <= c <= p and c < n]
+        for col, j in items:
+            kap = None if a["kscale"] is None else a["kscale"][base + j]
+            cols[col] = brute.score_one(a["qI"][t], a["w"][t], a["kI"][base + j], kap)
+        out.append(cols)
+    return out
+
+
+def brute_attend(a, idx) -> tuple:
+    qs = q_seq_of(a)
+    T, Hq, D = a["q"].shape
+    O = np.zeros((T, Hq, D))
+    L = np.full((T, Hq), -np.inf)
+    W = a["W"]
+    for t in range(T):
+        b = qs[t]
+        base = int(a["seq_start"][b])
+        rows = []
+        for j in idx[t]:
+            if j < 0:
+                continue
+            r = base + int(j)
+            rho = None if a["kv_rowscale"] is None else a["kv_rowscale"][r]
+            rows.append(brute.global_row(a["kv_codes"][r], a["kv_e8m0"][r], rho))
+        p = int(a["q_pos"][t])
+        lo = max(p - W + 1, 0)
+        if a["swa_clip"] is not None:
+            lo = max(lo, int(a["swa_clip"][t]))
+        for u in range(W):
+            pos = int(a["swa_pos0"][b]) + u
+            if lo <= pos <= p:
+                sig = None if a["swa_scale"] is None else a["swa_scale"][b][u]
+                rows.append(brute.window_row(a["swa"][b][u], sig))
+        for h in range(Hq):
+            o, lse = brute.attend_one(a["q"][t][h], rows, a["sm_scale"])
+            O[t, h] = o
+            L[t, h] = lse
+    return O, L
+
+
+def topk_set_ok(S_ref, cand_pos, k, got, rel_gap=1e-5):
+    """Check a GPU top-k result against oracle scores (set semantics, near-tie band).
+
+    S_ref: float64 [L] oracle scores (-inf = not scored); cand_pos: positions of the
+    columns (or None for dense); got: int array [k] (ascending, -1 padded).
+    Returns (ok, message).  Outside a 1e-5-relative gap at the k-th score the set
+    must equal the oracle's exactly; inside it, every strictly-better position must
+    be present and every chosen one must lie within the band.
+    """
+    cols = np.nonzero(S_ref != -np.inf)[0]
+    pos = cols if cand_pos is None else np.asarray(cand_pos)[cols]
+    sc = S_ref[cols]
+    nvalid = cols.size
+    m = min(k, nvalid)
+    got = np.asarray(got)
+    if not np.all(got[m:] == -1):
+        return False, "padding mismatch"
+    g = got[:m]
+    if np.any(g < 0) or len(set(g.tolist())) != m:
+        return False, "invalid or duplicate positions"
+    if not np.all(np.diff(g) > 0):
+        return False, "not ascending"
+    order = np.lexsort((pos, -sc))
+    ref = np.sort(pos[order[:m]])
+    if m == nvalid or np.array_equal(ref, g):
+        return (np.array_equal(ref, g), "full set mismatch")
+    sk = sc[order[m - 1]]
+    sk1 = sc[order[m]]
+    band = rel_gap * abs(sk)
+    if sk - sk1 >= band and sk != sk1:
+        return False, f"set mismatch with clear gap ({sk} vs {sk1})"
+    score_of = dict(zip(pos.tolist(), sc.tolist()))
+    must = set(pos[sc > sk + band].tolist())
+    allowed = set(pos[sc >= sk - band].tolist())
+    gs = set(g.tolist())
+    if not must <= gs:
+        return False, "missing a strictly better position"
+    if not gs <= allowed:
+        return False, "chose a position outside the near-tie band"
+    # exact ties are decided by position: among equal scores the lower position wins
+    for p_ in gs:
+        s_ = score_of[p_]
+        better_lower = [q for q in pos[(sc == s_)].tolist() if q < p_ and q not in gs]
+        if better_lower:
+            return False, "tie-break by position violated"
+    return True, "near-tie band"
+
+
+def close_attention(O_gpu, O_ref, lse_gpu=None, lse_ref=None, atol=2e-3, rtol=1e-3, lse_tol=1e-4):
+    """Per (t, h): max|dO| <= atol and max|dO| <= rtol * max|O_ref|; |dLSE| <= lse_tol."""
+    d = np.abs(np.asarray(O_gpu, dtype=np.float64) - O_ref).max(axis=-1)
+    scale = np.abs(O_ref).max(axis=-1)
+    ok = (d <= atol) & (d <= rtol * scale + 1e-30)
+    msg = f"max|dO|={d.max():.3e}, worst ratio={(d / np.maximum(scale, 1e-30)).max():.3e}"
+    if lse_gpu is not None:
+        dl = np.abs(np.asarray(lse_gpu, dtype=np.float64) - lse_ref)
+        both_inf = np.isinf(lse_ref) & (np.asarray(lse_gpu) == lse_ref)
+        dl = np.where(both_inf, 0.0, dl)
+        ok &= dl <= lse_tol
+        msg += f", max|dLSE|={dl.max():.3e}"
+    return bool(ok.all()), msg
+
+
+def close_scores(S_gpu, S_ref, rtol=1e-4, floor=1e-7):
+    """|S_gpu - S_ref| <= rtol*|S_ref| + floor*max|S_ref| on scored entries; -inf must match."""
+    S_gpu = np.asarray(S_gpu, dtype=np.float64)
+    inf = S_ref == -np.inf
+    if not np.array_equal(S_gpu[inf], S_ref[inf]):
+        return False, "masked entries differ"
+    fin = ~inf
+    if not fin.any():
+        return True, "empty"
+    tol = rtol * np.abs(S_ref[fin]) + floor * np.abs(S_ref[fin]).max()
+    err = np.abs(S_gpu[fin] - S_ref[fin])
+    return bool((err <= tol).all()), f"max err {err.max():.3e}, worst ratio {(err / tol).max():.3f}"
+
+
+def fsum(xs):
+    return math.fsum(xs)

@@ -1,0 +1,347 @@
+"""Pins for the fp64 oracle (CPU only).
+
+Each test checks the oracle against something other than itself: the scalar
+loop versions (oracle.brute, own decoders, exact summation), exact integer
+arithmetic, hand-worked fixtures (tests/golden), torch's scaled-dot-product
+attention in float64, and invariants of the definitions (permutations,
+linearity, window clipping).
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import synth
+from oracle import brute, codecs, ref
+from helpers import brute_attend, brute_scores, np_inputs
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+TINY = dict(Hi=3, Di=8, k=6, Hq=2, D=64, W=8, rowscale=True)
+
+
+def tiny(seed=0, **kw):
+    p = dict(TINY)
+    p.update(kw)
+    return synth.generate("tiny", seed=seed, **p)
+
+
+# ----------------------------------------------------------------- score
+
+def test_score_hand_example():
+    g = json.load(open(os.path.join(GOLDEN, "hand_score_topk.json")))
+    qI = np.array([g["qI"]], dtype=np.uint8)
+    w = np.array([g["w"]], dtype=np.float32)
+    kI = np.array(g["kI"], dtype=np.uint8)
+    seq = np.array([0, 4]); qst = np.array([0, 1]); qpos = np.array([3])
+    S = ref.score(qI, w, kI, None, seq, qst, qpos)
+    assert S[0].tolist() == g["S"]
+    S2 = ref.score(qI, w, kI, np.array(g["kappa"], dtype=np.float32), seq, qst, qpos)
+    assert S2[0].tolist() == g["S_kappa"]
+    assert ref.topk(S, 2)[0].tolist() == g["top2"]
+    assert ref.topk(S, 3)[0].tolist() == g["top3"]
+
+
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_score_matches_brute(seed):
+    wl = synth.with_scales(tiny(seed, B=2, lengths=(20, 37)), seed=seed)
+    a = np_inputs(wl)
+    S = ref.score(a["qI"], a["w"], a["kI"], a["kscale"], a["seq_start"], a["q_start"], a["q_pos"])
+    bs = brute_scores(a)
+    for t in range(a["T"]):
+        scored = np.nonzero(S[t] != -np.inf)[0]
+        assert sorted(bs[t]) == scored.tolist()
+        for c, v in bs[t].items():
+            assert abs(S[t, c] - v) <= 1e-12 * max(1.0, abs(v))
+
+
+def test_score_candidates_match_brute():
+    wl = tiny(4, B=2, lengths=(20, 60), n_cand=40)
+    a = np_inputs(wl)
+    S = ref.score(a["qI"], a["w"], a["kI"], None, a["seq_start"], a["q_start"], a["q_pos"],
+                  cand=a["cand"])
+    bs = brute_scores(a, cand=a["cand"])
+    for t in range(a["T"]):
+        for c in range(S.shape[1]):
+            if c in bs[t]:
+                assert abs(S[t, c] - bs[t][c]) <= 1e-12 * max(1.0, abs(bs[t][c]))
+            else:
+                assert S[t, c] == -np.inf
+    # the shorter sequence's padding entries (past the query) are masked
+    assert np.isinf(S).any()
+
+
+def test_score_integer_inputs_exact():
+    # integer-valued E4M3 inputs and power-of-two weights: exact integer arithmetic
+    rng = np.random.default_rng(0)
+    ints = np.arange(-4, 5)
+    codes = synth.encode_e4m3(torch.tensor(ints, dtype=torch.float32)).numpy()
+    lut = dict(zip(codes.tolist(), ints.tolist()))
+    Hi, Di, n = 4, 16, 50
+    qI = rng.choice(codes, size=(1, Hi, Di)).astype(np.uint8)
+    kI = rng.choice(codes, size=(n, Di)).astype(np.uint8)
+    w = np.array([[0.5, 2.0, 0.25, 1.0]], dtype=np.float32)
+    S = ref.score(qI, w, kI, None, np.array([0, n]), np.array([0, 1]), np.array([n - 1]))
+    for j in range(n):
+        tot = 0
+        for h in range(Hi):
+            dot = sum(lut[int(qI[0, h, d])] * lut[int(kI[j, d])] for d in range(Di))
+            tot += float(w[0, h]) * max(0, dot)
+        assert S[0, j] == tot
+
+
+def test_score_one_hot_weight_and_negative_dots():
+    wl = tiny(5)
+    a = np_inputs(wl)
+    Hi = a["Hi"]
+    for h in range(Hi):
+        w = np.zeros_like(a["w"]); w[0, h] = 1.0
+        S = ref.score(a["qI"], w, a["kI"], None, a["seq_start"], a["q_start"], a["q_pos"])
+        Q = codecs.e4m3(a["qI"][0, h]); K = codecs.e4m3(a["kI"])
+        n = int(a["q_pos"][0]) + 1
+        assert np.array_equal(S[0, :n], np.maximum(K[:n] @ Q, 0.0))
+    # keys pointing against every head's query give exactly zero
+    qI = np.tile(synth.encode_e4m3(torch.ones(1, 1, 8)).numpy(), (1, 3, 1))
+    kI = synth.encode_e4m3(-torch.rand(10, 8) - 0.1).numpy()
+    S = ref.score(qI, np.ones((1, 3), np.float32), kI, None, np.array([0, 10]), np.array([0, 1]),
+                  np.array([9]))
+    assert np.all(S[0] == 0.0)
+
+
+def test_score_head_permutation_and_kappa_linearity():
+    wl = tiny(6, Hi=5)
+    a = np_inputs(wl)
+    args = (a["seq_start"], a["q_start"], a["q_pos"])
+    S = ref.score(a["qI"], a["w"], a["kI"], None, *args)
+    perm = np.array([3, 0, 4, 1, 2])
+    Sp = ref.score(a["qI"][:, perm], a["w"][:, perm], a["kI"], None, *args)
+    assert np.allclose(S, Sp, rtol=1e-13, atol=0)
+    kap = np.full(a["kI"].shape[0], 2.5, dtype=np.float32)
+    Sk = ref.score(a["qI"], a["w"], a["kI"], kap, *args)
+    assert np.allclose(Sk, 2.5 * S, rtol=1e-13, atol=0)
+
+
+# ----------------------------------------------------------------- top-k
+
+@pytest.mark.parametrize("seed", [0, 1])
+def test_topk_matches_brute(seed):
+    rng = np.random.default_rng(seed)
+    S = rng.standard_normal((3, 40))
+    S[1, 30:] = -np.inf
+    S[2, ::3] = S[2, 1]                 # exact ties
+    for k in (1, 5, 13, 40, 45):
+        got = ref.topk(S, k)
+        for t in range(3):
+            sc = {j: S[t, j] for j in range(40) if S[t, j] != -np.inf}
+            exp = brute.topk_positions(sc, k)
+            assert got[t, :len(exp)].tolist() == exp
+            assert np.all(got[t, len(exp):] == -1)
+
+
+def test_topk_constant_scores_take_lowest_positions():
+    S = np.zeros((1, 100))
+    assert ref.topk(S, 7)[0].tolist() == list(range(7))
+
+
+def test_topk_candidates_return_positions():
+    S = np.array([[0.1, 0.9, 0.5, -np.inf]])
+    cand = np.array([[10, 3, 7, 99]])
+    assert ref.topk(S, 2, cand=cand)[0].tolist() == [3, 7]
+    assert ref.topk(S, 5, cand=cand)[0].tolist() == [3, 7, 10, -1, -1]
+
+
+def test_topk_agrees_with_argpartition_away_from_ties():
+    rng = np.random.default_rng(7)
+    S = rng.standard_normal((4, 5000))
+    got = ref.topk(S, 100)
+    for t in range(4):
+        part = np.sort(np.argpartition(-S[t], 100)[:100])
+        assert np.array_equal(got[t], part)
+
+
+# ----------------------------------------------------------------- attend
+
+def _attend(a, idx, **over):
+    b = dict(a)
+    b.update(over)
+    return ref.attend(b["q"], b["kv_codes"], b["kv_e8m0"], b["kv_rowscale"], idx, b["swa"],
+                      b["swa_scale"], b["swa_pos0"], b["swa_clip"], b["seq_start"], b["q_start"],
+                      b["q_pos"], b["W"], b["sm_scale"])
+
+
+@pytest.mark.parametrize("seed,clip", [(0, False), (1, True)])
+def test_attend_matches_brute(seed, clip):
+    wl = synth.with_scales(tiny(seed, B=2, lengths=(20, 37)), seed=seed)
+    a = np_inputs(wl)
+    if clip:
+        a["swa_clip"] = (a["q_pos"] - 3).astype(np.int32)
+    S = ref.score(a["qI"], a["w"], a["kI"], a["kscale"], a["seq_start"], a["q_start"], a["q_pos"])
+    idx = ref.topk(S, a["k"])
+    O, L = _attend(a, idx)
+    Ob, Lb = brute_attend(a, idx)
+    assert np.allclose(O, Ob, rtol=1e-12, atol=1e-14)
+    assert np.allclose(L, Lb, rtol=1e-12, atol=1e-14)
+
+
+def test_attend_select_all_equals_dense_sdpa():
+    """k >= n: the sparse attention is dense attention over every row plus the window."""
+    wl = tiny(8, lengths=33, k=64, W=8)
+    a = np_inputs(wl)
+    n = 33
+    idx = np.arange(64)[None, :].copy(); idx[0, n:] = -1
+    O, L = _attend(a, idx)
+    rows = codecs.global_rows(a["kv_codes"][:n], a["kv_e8m0"][:n], a["kv_rowscale"][:n])
+    win = codecs.window_rows(a["swa"][0][a["W"] - 8:], None)      # window = last 8 positions
+    R = torch.tensor(np.concatenate([rows, win]), dtype=torch.float64)
+    q = torch.tensor(codecs.bf16(a["q"]), dtype=torch.float64)          # [1, Hq, D]
+    Hq = q.shape[1]
+    kv = R[None, None].expand(1, Hq, -1, -1)
+    o = torch.nn.functional.scaled_dot_product_attention(q[:, :, None, :], kv, kv,
+                                                         scale=a["sm_scale"])[:, :, 0]
+    lse = torch.logsumexp(a["sm_scale"] * (q[0] @ R.T), dim=-1)
+    assert np.allclose(O, o.numpy(), rtol=1e-12, atol=1e-14)
+    assert np.allclose(L[0], lse.numpy(), rtol=1e-12, atol=1e-14)
+
+
+def test_attend_single_row_and_identical_rows():
+    wl = tiny(9, lengths=40, W=8)
+    a = np_inputs(wl)
+    # one global row, window clipped to nothing: O = row, LSE = tau <q,row>
+    idx = np.full((1, 6), -1); idx[0, 0] = 17
+    clip = np.array([10_000], dtype=np.int32)
+    O, L = _attend(a, idx, swa_clip=clip)
+    row = codecs.global_rows(a["kv_codes"][17:18], a["kv_e8m0"][17:18], a["kv_rowscale"][17:18])[0]
+    q = codecs.bf16(a["q"][0])
+    assert np.allclose(O[0], np.broadcast_to(row, O[0].shape), rtol=1e-14, atol=0)
+    assert np.allclose(L[0], a["sm_scale"] * (q @ row), rtol=1e-13, atol=1e-15)
+    # all rows decode to the same vector -> O is that vector for any logits
+    b = dict(a)
+    b["kv_codes"] = np.tile(a["kv_codes"][17:18], (a["kv_codes"].shape[0], 1))
+    b["kv_e8m0"] = np.tile(a["kv_e8m0"][17:18], (a["kv_e8m0"].shape[0], 1))
+    b["kv_rowscale"] = np.full_like(a["kv_rowscale"], a["kv_rowscale"][17])
+    idx = np.arange(6)[None] * 3
+    O, _ = _attend(b, idx, swa_clip=clip)
+    assert np.allclose(O[0], np.broadcast_to(row, O[0].shape), rtol=1e-13, atol=1e-15)
+
+
+def test_attend_weights_sum_to_one():
+    # every row decodes to all-ones (E2M1 0x22 = [1, 1], E8M0 127; E4M3 0x38 = 1) -> O == 1
+    wl = tiny(10, lengths=40, W=8)
+    a = np_inputs(wl)
+    a["kv_codes"][:] = 0x22
+    a["kv_e8m0"][:] = 127
+    a["kv_rowscale"][:] = 1.0
+    a["swa"][:] = 0x38
+    idx = np.arange(6)[None] * 5
+    O, _ = _attend(a, idx)
+    assert np.allclose(O, 1.0, rtol=0, atol=1e-13)
+
+
+def test_attend_permutation_invariance_and_lse_merge():
+    wl = tiny(11, lengths=60, k=12, W=8)
+    a = np_inputs(wl)
+    S = ref.score(a["qI"], a["w"], a["kI"], None, a["seq_start"], a["q_start"], a["q_pos"])
+    idx = ref.topk(S, 12)
+    O, L = _attend(a, idx)
+    perm = idx[:, np.random.default_rng(0).permutation(12)]
+    Op, Lp = _attend(a, perm)
+    assert np.allclose(O, Op, rtol=1e-12, atol=1e-14) and np.allclose(L, Lp, rtol=1e-13)
+    # split the selected rows in two disjoint halves (no window on either side) and merge by LSE
+    none = np.array([10_000], dtype=np.int32)
+    h1 = idx.copy(); h1[:, 6:] = -1
+    h2 = idx.copy(); h2[:, :6] = -1
+    O1, L1 = _attend(a, h1, swa_clip=none)
+    O2, L2 = _attend(a, h2, swa_clip=none)
+    Oa, La = _attend(a, idx, swa_clip=none)
+    M = np.maximum(L1, L2)
+    e1, e2 = np.exp(L1 - M), np.exp(L2 - M)
+    Om = (e1[..., None] * O1 + e2[..., None] * O2) / (e1 + e2)[..., None]
+    assert np.allclose(Om, Oa, rtol=1e-12, atol=1e-14)
+    assert np.allclose(M + np.log(e1 + e2), La, rtol=1e-13)
+
+
+def test_attend_empty_set():
+    wl = tiny(12, lengths=40, W=8)
+    a = np_inputs(wl)
+    O, L = _attend(a, np.full((1, 6), -1), swa_clip=np.array([10_000], dtype=np.int32))
+    assert np.all(O == 0) and np.all(L == -np.inf)
+
+
+# ----------------------------------------------------------------- window clipping
+
+def _replay(H=50, nq=6, W=8, seed=13):
+    return np_inputs(tiny(seed, lengths=H, W=W, replay=(H, nq)))
+
+
+def test_clip_at_replay_start_leaves_one_window_row():
+    a = _replay()
+    s = int(a["swa_clip"][0])
+    for t in range(a["T"]):
+        u, pos = ref.window_positions(t, 0, a["q_pos"], a["swa_pos0"], a["swa_clip"], a["W"])
+        assert pos.min() == s and pos.max() == a["q_pos"][t]
+        assert len(u) == a["q_pos"][t] - s + 1
+    assert a["q_pos"][0] == s
+    u, _ = ref.window_positions(0, 0, a["q_pos"], a["swa_pos0"], a["swa_clip"], a["W"])
+    assert len(u) == 1
+
+
+def test_clip_excludes_rows_before_s_exactly():
+    # rows of the window before s never contribute: poison them with NaN codes
+    a = _replay()
+    idx = np.tile(np.arange(6)[None] * 4, (a["T"], 1))
+    O, L = _attend(a, idx)
+    s = int(a["swa_clip"][0])
+    b = dict(a)
+    b["swa"] = a["swa"].copy()
+    n_before = s - int(a["swa_pos0"][0])
+    b["swa"][0, :n_before] = 0x7F                 # E4M3 NaN
+    Ob, Lb = _attend(b, idx)
+    assert np.array_equal(O, Ob) and np.array_equal(L, Lb)
+    # ... while without a clip they do contribute (the NaN shows up)
+    On, _ = _attend(b, idx, swa_clip=None)
+    assert np.isnan(On).any()
+
+
+def test_loose_clip_equals_no_clip_and_w1_is_self_row():
+    a = np_inputs(tiny(14, lengths=40, W=8))
+    idx = np.arange(6)[None] * 2
+    O0, L0 = _attend(a, idx)
+    loose = (a["q_pos"] - a["W"] + 1 - 5).astype(np.int32)
+    O1, L1 = _attend(a, idx, swa_clip=loose)
+    assert np.array_equal(O0, O1) and np.array_equal(L0, L1)
+    u, pos = ref.window_positions(0, 0, a["q_pos"], a["swa_pos0"], None, 1)
+    assert pos.tolist() == [int(a["q_pos"][0])] or len(pos) == 0
+
+
+# ----------------------------------------------------------------- decode step
+
+def test_decode_step_is_composition():
+    wl = synth.with_scales(tiny(15, B=2, lengths=(25, 41)))
+    a = np_inputs(wl)
+    S, idx, O, L = ref.decode_step(a)
+    S2 = ref.score(a["qI"], a["w"], a["kI"], a["kscale"], a["seq_start"], a["q_start"], a["q_pos"])
+    idx2 = ref.topk(S2, a["k"])
+    O2, L2 = _attend(a, idx2)
+    assert np.array_equal(S, S2) and np.array_equal(idx, idx2)
+    assert np.array_equal(O, O2) and np.array_equal(L, L2)
+
+
+def test_window_membership_hand_cases():
+    # buffer rows u=0..3 hold positions 10..13; W = 4
+    q_pos = np.array([14, 13, 11, 9]); pos0 = np.array([10])
+    u, pos = ref.window_positions(0, 0, q_pos, pos0, None, 4)
+    assert pos.tolist() == [11, 12, 13]           # window [11, 14]; position 14 is not in the buffer
+    u, pos = ref.window_positions(1, 0, q_pos, pos0, None, 4)
+    assert pos.tolist() == [10, 11, 12, 13]       # window [10, 13]
+    u, pos = ref.window_positions(2, 0, q_pos, pos0, None, 4)
+    assert pos.tolist() == [10, 11]               # causal: nothing after the query
+    u, pos = ref.window_positions(3, 0, q_pos, pos0, None, 4)
+    assert pos.tolist() == []                     # query before the buffer
+    clip = np.array([12, 12, 12, 12])
+    u, pos = ref.window_positions(1, 0, q_pos, pos0, clip, 4)
+    assert pos.tolist() == [12, 13] and u.tolist() == [2, 3]
+    u, pos = ref.window_positions(1, 0, q_pos, np.array([13]), None, 1)
+    assert pos.tolist() == [13]                   # W = 1: the query's own row only
