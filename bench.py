@@ -1,0 +1,314 @@
+#!/usr/bin/env python3
+"""Benchmark of the sparse-MQA decode step on one MI355X.
+
+One step = one decode_step call over the whole batch: indexer scoring of every
+context position, top-k selection and sparse MQA attention over the selected FP4
+latent rows plus the FP8 window (the three stages of the method, in one call).
+Inputs are the seeded synthetic workloads of ``synth`` (already resident in HBM
+when timing starts).  Metric: context positions scored per second (higher is
+better) and microseconds per step, at 8K context (decode_8k, the primary line)
+and at 512K context (decode_512k, reported alongside).
+
+The step is timed twice: eager (one C-ABI call per step from Python) and as a
+replayed HIP graph of the same call; ``value`` uses the graph replay, whose
+outputs are checked bitwise against the eager step first.  Per-stage kernel
+time comes from HIP events around repeated calls of each stage's entry point
+on the same stream.  ``cpu_baseline`` times the fp64 CPU oracle on a bounded
+sample of the same workload.
+
+    python bench.py [--steps K] [--warmup W] [--workload decode_8k] [--also decode_512k]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "context tokens scored/s and decode-attention us/step at 8K and 512K ctx, 1 GPU"
+UNIT = "context tokens scored/s"
+HBM_PEAK_GBS = 8000.0
+MFMA_PEAK_TFLOPS = {"fp8": 5000.0, "bf16": 2500.0}
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="decode_8k")
+    ap.add_argument("--also", default="decode_512k", help="comma list of extra workloads ('' = none)")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--no-graph", action="store_true")
+    ap.add_argument("--stage-only", default="", help="time only this stage entry point (profiling)")
+    return ap.parse_args()
+
+
+# ---------------------------------------------------------------- algorithmic work per stage
+
+def work(wl):
+    """Algorithmic bytes / flops of each stage for one step (what the method must move/compute)."""
+    import numpy as np
+    lengths = np.array(wl.meta["lengths"], dtype=np.int64)
+    q_seq = np.array(wl.meta["q_seq"], dtype=np.int64)
+    q_pos = wl.q_pos.cpu().numpy().astype(np.int64)
+    scored = np.minimum(q_pos, lengths[q_seq] - 1) + 1
+    J = int(scored.sum())
+    keys_read = int(np.minimum(lengths, np.array([scored[q_seq == b].max() if (q_seq == b).any() else 0
+                                                   for b in range(wl.B)])).sum())
+    T, k, Hq, D, W, Hi, Di = wl.T, wl.k, wl.Hq, wl.D, wl.W, wl.Hi, wl.Di
+    row_b = D // 2 + D // 32 + (4 if wl.kv_rowscale is not None else 0)
+    # visible window rows per query
+    lo = np.maximum(q_pos - W + 1, 0)
+    if wl.swa_clip is not None:
+        lo = np.maximum(lo, wl.swa_clip.cpu().numpy())
+    pos0 = wl.swa_pos0.cpu().numpy()[q_seq]
+    vis = np.clip(np.minimum(q_pos, pos0 + W - 1) - np.maximum(lo, pos0) + 1, 0, W)
+    sel = np.minimum(scored, k)
+    out = {
+        "score": dict(bytes=keys_read * Di + J * 4, flops=2 * Hi * Di * J, mfma="fp8"),
+        "topk": dict(bytes=J * 4 + T * k * 4, flops=0, mfma=None),
+        "attend": dict(bytes=int(sel.sum()) * (row_b + 4) + wl.B * W * D + T * Hq * (D * 2 + D * 4 + 4),
+                       flops=int(4 * Hq * D * (sel + vis).sum()), mfma="bf16"),
+    }
+    return J, out
+
+
+def roofline(stage, w, seconds):
+    ai = w["flops"] / max(w["bytes"], 1)
+    if w["mfma"] and ai > MFMA_PEAK_TFLOPS[w["mfma"]] * 1e12 / (HBM_PEAK_GBS * 1e9):
+        ach = w["flops"] / seconds / 1e12
+        peak = MFMA_PEAK_TFLOPS[w["mfma"]]
+        return {"kernel": stage, "bound": "mfma", "achieved": round(ach, 3), "peak": peak,
+                "unit": "TFLOP/s", "frac": round(ach / peak, 4), "traffic": None,
+                "algorithmic_flops": w["flops"], "algorithmic_bytes": w["bytes"]}
+    ach = w["bytes"] / seconds / 1e9
+    return {"kernel": stage, "bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS,
+            "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": None,
+            "algorithmic_bytes": w["bytes"], "algorithmic_flops": w["flops"]}
+
+
+# ---------------------------------------------------------------- GPU measurement
+
+def measure(name, steps, warmup, use_graph, stage_only=""):
+    import torch
+    import synth
+    import fp8_kv_cache_sparse_amd as smqa
+
+    wl = synth.generate(name, seed=0, device="cuda")
+    J, w = work(wl)
+    L = smqa.Batch(wl.seq_start, wl.q_start, wl.q_pos, wl.max_ctx)
+    dev = wl.q.device
+    out = torch.empty((wl.T, wl.Hq, wl.D), dtype=torch.float32, device=dev)
+    lse = torch.empty((wl.T, wl.Hq), dtype=torch.float32, device=dev)
+    idx = torch.empty((wl.T, wl.k), dtype=torch.int32, device=dev)
+    n_cand = 0 if wl.cand is None else wl.cand.shape[1]
+    ws = torch.empty(smqa.decode_step_workspace_size(L, wl.k, n_cand, wl.W, wl.Hq, wl.D) + 256,
+                     dtype=torch.uint8, device=dev)
+    args = (L, wl.qI, wl.w, wl.kI, wl.kscale, wl.cand, wl.q, wl.kv_codes, wl.kv_e8m0, wl.kv_rowscale,
+            wl.swa, wl.swa_scale, wl.swa_pos0, wl.swa_clip, wl.k, wl.sm_scale)
+
+    def step():
+        smqa.decode_step(*args, out=out, lse=lse, idx=idx, workspace=ws)
+
+    # stage buffers
+    scores = torch.empty((wl.T, max(wl.max_ctx, 1)), dtype=torch.float32, device=dev)
+    idx2 = torch.empty_like(idx)
+    out2, lse2 = torch.empty_like(out), torch.empty_like(lse)
+
+    def st_score():
+        smqa.sparse_mqa_score(L, wl.qI, wl.w, wl.kI, wl.kscale, wl.cand, scores=scores)
+
+    def st_topk():
+        smqa.topk_select(L, scores, wl.k, cand=wl.cand, idx=idx2, workspace=ws)
+
+    def st_attend():
+        smqa.sparse_mqa_attend(L, wl.q, wl.kv_codes, wl.kv_e8m0, wl.kv_rowscale, idx2, wl.swa,
+                               wl.swa_scale, wl.swa_pos0, wl.swa_clip, wl.sm_scale, out=out2, lse=lse2,
+                               workspace=ws)
+
+    stages = {"score": st_score, "topk": st_topk, "attend": st_attend}
+    if stage_only:
+        fn = stages[stage_only]
+        st_score()
+        st_topk()
+        for _ in range(warmup):
+            fn()
+        torch.cuda.synchronize()
+        for _ in range(steps):
+            fn()
+        torch.cuda.synchronize()
+        return {"workload": name, "stage_only": stage_only}
+
+    print(f"[bench] {name}: warmup", file=sys.stderr, flush=True)
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    ref_out, ref_lse, ref_idx = out.clone(), lse.clone(), idx.clone()
+
+    print(f"[bench] {name}: eager x{steps}", file=sys.stderr, flush=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        step()
+    torch.cuda.synchronize()
+    eager_s = (time.perf_counter() - t0) / steps
+
+    graph_s = None
+    graph_ok = None
+    if use_graph:
+        try:
+            g = torch.cuda.CUDAGraph()
+            s = torch.cuda.Stream()
+            s.wait_stream(torch.cuda.current_stream())
+            with torch.cuda.stream(s):
+                step()
+            torch.cuda.current_stream().wait_stream(s)
+            torch.cuda.synchronize()
+            with torch.cuda.graph(g):
+                step()
+            torch.cuda.synchronize()
+            graph_ok = True
+            for _ in range(3):                     # every replay must reproduce the eager result
+                out.zero_()
+                g.replay()
+                torch.cuda.synchronize()
+                graph_ok &= bool(torch.equal(out, ref_out) and torch.equal(lse, ref_lse)
+                                 and torch.equal(idx, ref_idx))
+            if graph_ok:
+                print(f"[bench] {name}: graph x{steps}", file=sys.stderr, flush=True)
+                for _ in range(warmup):
+                    g.replay()
+                torch.cuda.synchronize()
+                t0 = time.perf_counter()
+                for _ in range(steps):
+                    g.replay()
+                torch.cuda.synchronize()
+                graph_s = (time.perf_counter() - t0) / steps
+        except Exception as e:  # graph capture unavailable: report eager only
+            print(f"[bench] graph capture failed: {e}", file=sys.stderr, flush=True)
+            graph_ok = False
+
+    # per-stage kernel time with HIP events on the launch stream
+    st_us = {}
+    st_score()
+    st_topk()
+    torch.cuda.synchronize()
+    for nm, fn in stages.items():
+        print(f"[bench] {name}: stage {nm} x{steps}", file=sys.stderr, flush=True)
+        for _ in range(2):
+            fn()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(steps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        st_us[nm] = e0.elapsed_time(e1) * 1e3 / steps
+    dom = max(st_us, key=st_us.get)
+    best_s = graph_s if graph_s else eager_s
+    res = {
+        "workload": name, "T": wl.T, "B": wl.B, "scored_positions": J,
+        "us_per_step": round(best_s * 1e6, 2),
+        "us_per_step_eager": round(eager_s * 1e6, 2),
+        "us_per_step_graph": None if graph_s is None else round(graph_s * 1e6, 2),
+        "graph_replay_matches_eager": graph_ok,
+        "tokens_scored_per_s": J / best_s,
+        "stage_us": {k: round(v, 2) for k, v in st_us.items()},
+        "stage_roofline": {k: roofline(k, w[k], st_us[k] * 1e-6) for k in st_us},
+        "roofline": roofline(dom, w[dom], st_us[dom] * 1e-6),
+        "config": dict(wl.meta["params"], lengths=(wl.meta["lengths"] if wl.B <= 8 else
+                                                  [min(wl.meta["lengths"]), max(wl.meta["lengths"])])),
+    }
+    del wl
+    torch.cuda.empty_cache()
+    return res
+
+
+# ---------------------------------------------------------------- CPU oracle baseline
+
+def cpu_baseline(name, seconds):
+    import numpy as np
+    import torch
+    import synth
+    from oracle import ref
+
+    wl = synth.generate(name, seed=0, device="cpu")
+    J, _ = work(wl)
+    a = {n: (None if getattr(wl, n) is None else getattr(wl, n).numpy())
+         for n in ("seq_start", "q_start", "q_pos", "qI", "w", "kI", "kscale", "kv_codes", "kv_e8m0",
+                   "kv_rowscale", "swa", "swa_scale", "swa_pos0", "swa_clip")}
+    a["q"] = wl.q.view(torch.int16).numpy().view(np.uint16)
+    a.update(k=wl.k, W=wl.W, sm_scale=wl.sm_scale)
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        cores = os.cpu_count()
+    reps = 0
+    t0 = time.perf_counter()
+    while True:
+        ref.decode_step(a)
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= seconds:
+            break
+    return {"value": J * reps / el, "unit": UNIT, "cores": cores, "kind": "oracle",
+            "sample": f"{reps} full fp64 oracle decode steps of {name} ({J} scored positions each), "
+                      f"{el:.1f} s", "s_per_step": el / reps}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU: --gpus {args.gpus} is not supported (the method's "
+              f"multi-GPU sharding is described, not built)", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import fp8_kv_cache_sparse_amd as smqa
+    smqa.load()
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    if args.stage_only:
+        measure(args.workload, args.steps, args.warmup, False, args.stage_only)
+        print(json.dumps({"stage_only": args.stage_only, "workload": args.workload}))
+        return
+    main_res = measure(args.workload, args.steps, args.warmup, not args.no_graph)
+    extra = {}
+    for nm in [x for x in args.also.split(",") if x]:
+        extra[nm] = measure(nm, args.steps, args.warmup, not args.no_graph)
+    cpu = None if args.no_cpu else cpu_baseline(args.workload, args.cpu_seconds)
+    cfg = main_res["config"]
+    line = {
+        "metric": METRIC,
+        "value": main_res["tokens_scored_per_s"],
+        "unit": UNIT,
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": main_res["us_per_step"] / 1e3,
+        "us_per_step": main_res["us_per_step"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp8 (score) + bf16/fp16 (attention) MFMA, fp32 accumulate",
+        "data": "synthetic",
+        "config": {"workload": args.workload, "batch": cfg["B"], "ctx": cfg["lengths"],
+                   "indexer": f"{cfg['Hi']}x{cfg['Di']} e4m3", "k": cfg["k"],
+                   "attention": f"{cfg['Hq']} heads x {cfg['D']} latent (e2m1 + e8m0/32"
+                                f"{' + f32 row scale' if cfg['rowscale'] else ''})",
+                   "window": cfg["W"], "parallelism": "none (1 GPU)"},
+        "roofline": main_res["roofline"],
+        "cpu_baseline": cpu,
+        "detail": main_res,
+        "also": extra,
+    }
+    print(json.dumps(line))
+
+
+if __name__ == "__main__":
+    main()

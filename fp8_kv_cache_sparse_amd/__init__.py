@@ -1,0 +1,10 @@
+"""Sparse-MQA decode path for AMD MI355X (gfx950): FP8 indexer scoring, top-k
+selection and attention over FP4 latent rows plus an FP8 sliding window.
+
+The computation lives in libsmqa.so (HIP kernels behind the C ABI declared in
+include/smqa.h); this package is its thin Python binding.
+"""
+from ._binding import (  # noqa: F401
+    Batch, Layout, SmqaError, load, version, sparse_mqa_score, topk_select, sparse_mqa_attend,
+    decode_step, decode_step_workspace_size, LIB_PATH,
+)

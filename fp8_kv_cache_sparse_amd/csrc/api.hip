@@ -1,0 +1,278 @@
+// C-ABI entry points of libsmqa: host-side validation, workspace carving and
+// launches on the caller's stream.  Every check runs before the first HIP call,
+// so argument errors are reported without touching a device.
+#include <cstdarg>
+#include <cstdio>
+#include <string>
+
+#include "common.h"
+
+namespace {
+
+thread_local std::string g_err;
+
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return code;
+}
+
+int hip_fail(hipError_t e, const char* where) {
+  return fail(SMQA_ERR_HIP, "%s: %s", where, hipGetErrorString(e));
+}
+
+bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+#define REQUIRE_PTR(p)                                               \
+  do {                                                               \
+    if (!(p)) return fail(SMQA_ERR_NULL, "%s is NULL", #p);          \
+  } while (0)
+#define REQUIRE_ALIGN(p, a)                                                          \
+  do {                                                                               \
+    if ((p) && !aligned((p), (a)))                                                   \
+      return fail(SMQA_ERR_ALIGN, "%s must be %d-byte aligned", #p, (int)(a));       \
+  } while (0)
+
+int check_layout(const smqa_layout* L) {
+  if (!L) return fail(SMQA_ERR_NULL, "layout is NULL");
+  if (L->num_seqs < 1) return fail(SMQA_ERR_SHAPE, "num_seqs = %d must be >= 1", L->num_seqs);
+  if (L->num_q < 0) return fail(SMQA_ERR_SHAPE, "num_q = %d must be >= 0", L->num_q);
+  if (!L->seq_start) return fail(SMQA_ERR_NULL, "layout.seq_start is NULL");
+  if (!L->q_start) return fail(SMQA_ERR_NULL, "layout.q_start is NULL");
+  if (L->num_q > 0 && !L->q_pos) return fail(SMQA_ERR_NULL, "layout.q_pos is NULL");
+  if (!aligned(L->seq_start, 8)) return fail(SMQA_ERR_ALIGN, "layout.seq_start must be 8-byte aligned");
+  if (!aligned(L->q_start, 4) || !aligned(L->q_pos, 4))
+    return fail(SMQA_ERR_ALIGN, "layout.q_start / q_pos must be 4-byte aligned");
+  if (L->num_q > 0 && L->max_ctx < 1) return fail(SMQA_ERR_SHAPE, "max_ctx = %d must be >= 1", L->max_ctx);
+  return SMQA_OK;
+}
+
+int check_score(const smqa_layout* L, const uint8_t* q_fp8, const float* w, const uint8_t* k_fp8,
+                const float* k_scale, const int32_t* cand, int32_t n_cand, int32_t Hi, int32_t Di,
+                const float* scores, int64_t ld, bool need_scores) {
+  REQUIRE_PTR(q_fp8);
+  REQUIRE_PTR(w);
+  REQUIRE_PTR(k_fp8);
+  if (need_scores) REQUIRE_PTR(scores);
+  if (Di != 64 && Di != 128) return fail(SMQA_ERR_UNSUPPORTED, "Di = %d: supported 64, 128", Di);
+  if (Hi < 1 || Hi > 128) return fail(SMQA_ERR_UNSUPPORTED, "Hi = %d: supported 1..128", Hi);
+  if (cand) {
+    if (n_cand < 1) return fail(SMQA_ERR_SHAPE, "n_cand = %d must be >= 1 with a candidate list", n_cand);
+    if (ld < n_cand) return fail(SMQA_ERR_SHAPE, "ld_scores = %lld < n_cand = %d", (long long)ld, n_cand);
+  } else if (ld < L->max_ctx) {
+    return fail(SMQA_ERR_SHAPE, "ld_scores = %lld < max_ctx = %d", (long long)ld, L->max_ctx);
+  }
+  REQUIRE_ALIGN(q_fp8, 16);
+  REQUIRE_ALIGN(k_fp8, 16);
+  REQUIRE_ALIGN(w, 4);
+  REQUIRE_ALIGN(k_scale, 4);
+  REQUIRE_ALIGN(cand, 4);
+  REQUIRE_ALIGN(scores, 4);
+  return SMQA_OK;
+}
+
+int check_topk(const smqa_layout* L, const float* scores, int64_t ld, const int32_t* cand,
+               int32_t n_cand, int32_t k, const int32_t* idx) {
+  REQUIRE_PTR(scores);
+  REQUIRE_PTR(idx);
+  if (k < 1 || k > 4096) return fail(SMQA_ERR_UNSUPPORTED, "k = %d: supported 1..4096", k);
+  if (cand) {
+    if (n_cand < 1) return fail(SMQA_ERR_SHAPE, "n_cand = %d must be >= 1 with a candidate list", n_cand);
+    if (ld < n_cand) return fail(SMQA_ERR_SHAPE, "ld_scores = %lld < n_cand = %d", (long long)ld, n_cand);
+  } else if (ld < L->max_ctx) {
+    return fail(SMQA_ERR_SHAPE, "ld_scores = %lld < max_ctx = %d", (long long)ld, L->max_ctx);
+  }
+  REQUIRE_ALIGN(scores, 4);
+  REQUIRE_ALIGN(cand, 4);
+  REQUIRE_ALIGN(idx, 4);
+  return SMQA_OK;
+}
+
+int check_attend(const uint16_t* q, const uint8_t* kv_codes, const uint8_t* kv_e8m0,
+                 const float* kv_rowscale, const int32_t* idx, int32_t k, const uint8_t* swa,
+                 const float* swa_scale, const int32_t* swa_pos0, const int32_t* swa_clip, int32_t W,
+                 int32_t Hq, int32_t D, float sm_scale, const float* out, const float* lse,
+                 bool need_idx) {
+  REQUIRE_PTR(q);
+  REQUIRE_PTR(kv_codes);
+  REQUIRE_PTR(kv_e8m0);
+  if (need_idx) REQUIRE_PTR(idx);
+  REQUIRE_PTR(swa);
+  REQUIRE_PTR(swa_pos0);
+  REQUIRE_PTR(out);
+  if (D % 128 != 0 || D < 128 || D > 2048)
+    return fail(SMQA_ERR_UNSUPPORTED, "D = %d: supported multiples of 128 in 128..2048", D);
+  if (Hq % 16 != 0 || Hq < 16 || Hq > 128)
+    return fail(SMQA_ERR_UNSUPPORTED, "Hq = %d: supported multiples of 16 in 16..128", Hq);
+  if (W < 1 || W > 128) return fail(SMQA_ERR_UNSUPPORTED, "W = %d: supported 1..128", W);
+  if (k < 1 || k > 4096) return fail(SMQA_ERR_UNSUPPORTED, "k = %d: supported 1..4096", k);
+  if (!(sm_scale == sm_scale)) return fail(SMQA_ERR_SHAPE, "sm_scale is NaN");
+  REQUIRE_ALIGN(q, 16);
+  REQUIRE_ALIGN(kv_codes, 16);
+  REQUIRE_ALIGN(kv_e8m0, 4);
+  REQUIRE_ALIGN(kv_rowscale, 4);
+  REQUIRE_ALIGN(idx, 4);
+  REQUIRE_ALIGN(swa, 16);
+  REQUIRE_ALIGN(swa_scale, 4);
+  REQUIRE_ALIGN(swa_pos0, 4);
+  REQUIRE_ALIGN(swa_clip, 4);
+  REQUIRE_ALIGN(out, 16);
+  REQUIRE_ALIGN(lse, 4);
+  return SMQA_OK;
+}
+
+int check_ws(void* ws, size_t have, size_t need) {
+  if (need == 0) return SMQA_OK;
+  if (!ws) return fail(SMQA_ERR_WORKSPACE, "workspace is NULL but %zu bytes are required", need);
+  if (!aligned(ws, 256)) return fail(SMQA_ERR_ALIGN, "workspace must be 256-byte aligned");
+  if (have < need) return fail(SMQA_ERR_WORKSPACE, "workspace has %zu bytes, %zu required", have, need);
+  return SMQA_OK;
+}
+
+int32_t score_cols(const smqa_layout* L, int32_t n_cand, bool cand) { return cand ? n_cand : L->max_ctx; }
+
+struct DecodeWs {
+  size_t scores_off, idx_off, topk_off, attend_off, total;
+};
+
+DecodeWs decode_ws_layout(const smqa_layout* L, int32_t k, int32_t ncols, int32_t W, int32_t Hq, int32_t D) {
+  DecodeWs d;
+  const size_t T = (size_t)L->num_q;
+  size_t off = 0;
+  d.scores_off = off;
+  off += smqa::align_up(T * (size_t)ncols * 4, 256);
+  d.idx_off = off;
+  off += smqa::align_up(T * (size_t)k * 4, 256);
+  d.topk_off = off;
+  off += smqa::align_up(smqa::topk_workspace_bytes(L->num_q, ncols, k), 256);
+  d.attend_off = off;
+  off += smqa::align_up(smqa::attend_workspace_bytes(L->num_q, k, W, Hq, D), 256);
+  d.total = off;
+  return d;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* smqa_last_error(void) { return g_err.c_str(); }
+
+const char* smqa_version(void) { return "smqa 0.1.0 gfx950"; }
+
+size_t smqa_topk_workspace_size(const smqa_layout* L, int32_t k, int32_t n_cand) {
+  if (check_layout(L) != SMQA_OK) return 0;
+  return smqa::topk_workspace_bytes(L->num_q, n_cand > 0 ? n_cand : L->max_ctx, k);
+}
+
+size_t smqa_attend_workspace_size(const smqa_layout* L, int32_t k, int32_t W, int32_t Hq, int32_t D) {
+  if (check_layout(L) != SMQA_OK) return 0;
+  return smqa::attend_workspace_bytes(L->num_q, k, W, Hq, D);
+}
+
+size_t smqa_decode_step_workspace_size(const smqa_layout* L, int32_t k, int32_t n_cand, int32_t W,
+                                       int32_t Hq, int32_t D) {
+  if (check_layout(L) != SMQA_OK) return 0;
+  return decode_ws_layout(L, k, n_cand > 0 ? n_cand : L->max_ctx, W, Hq, D).total;
+}
+
+int sparse_mqa_score(const smqa_layout* L, const uint8_t* q_fp8, const float* w, const uint8_t* k_fp8,
+                     const float* k_scale, const int32_t* cand, int32_t n_cand, int32_t Hi, int32_t Di,
+                     float* scores, int64_t ld_scores, void* stream) {
+  g_err.clear();
+  int st = check_layout(L);
+  if (st) return st;
+  if (L->num_q == 0) return SMQA_OK;
+  st = check_score(L, q_fp8, w, k_fp8, k_scale, cand, n_cand, Hi, Di, scores, ld_scores, true);
+  if (st) return st;
+  smqa::ScoreArgs a{L->seq_start, L->q_start, L->q_pos, L->num_seqs, L->num_q, L->max_ctx,
+                    q_fp8, w, k_fp8, k_scale, cand, cand ? n_cand : 0, Hi, Di, scores, ld_scores};
+  hipError_t e = smqa::launch_score(a, (hipStream_t)stream);
+  return e == hipSuccess ? SMQA_OK : hip_fail(e, "sparse_mqa_score launch");
+}
+
+int topk_select(const smqa_layout* L, const float* scores, int64_t ld_scores, const int32_t* cand,
+                int32_t n_cand, int32_t k, int32_t* idx_out, void* workspace, size_t workspace_bytes,
+                void* stream) {
+  g_err.clear();
+  int st = check_layout(L);
+  if (st) return st;
+  if (L->num_q == 0) return SMQA_OK;
+  st = check_topk(L, scores, ld_scores, cand, n_cand, k, idx_out);
+  if (st) return st;
+  const int32_t cols = score_cols(L, n_cand, cand != nullptr);
+  st = check_ws(workspace, workspace_bytes, smqa::topk_workspace_bytes(L->num_q, cols, k));
+  if (st) return st;
+  smqa::TopkArgs a{L->seq_start, L->q_start, L->q_pos, L->num_seqs, L->num_q, cols,
+                   scores, ld_scores, cand, cand ? n_cand : 0, k, idx_out, workspace};
+  hipError_t e = smqa::launch_topk(a, (hipStream_t)stream);
+  return e == hipSuccess ? SMQA_OK : hip_fail(e, "topk_select launch");
+}
+
+int sparse_mqa_attend(const smqa_layout* L, const uint16_t* q_bf16, const uint8_t* kv_codes,
+                      const uint8_t* kv_e8m0, const float* kv_rowscale, const int32_t* idx, int32_t k,
+                      const uint8_t* swa_fp8, const float* swa_scale, const int32_t* swa_pos0,
+                      const int32_t* swa_clip, int32_t W, int32_t Hq, int32_t D, float sm_scale,
+                      float* out, float* lse, void* workspace, size_t workspace_bytes, void* stream) {
+  g_err.clear();
+  int st = check_layout(L);
+  if (st) return st;
+  if (L->num_q == 0) return SMQA_OK;
+  st = check_attend(q_bf16, kv_codes, kv_e8m0, kv_rowscale, idx, k, swa_fp8, swa_scale, swa_pos0,
+                    swa_clip, W, Hq, D, sm_scale, out, lse, true);
+  if (st) return st;
+  st = check_ws(workspace, workspace_bytes, smqa::attend_workspace_bytes(L->num_q, k, W, Hq, D));
+  if (st) return st;
+  smqa::AttendArgs a{L->seq_start, L->q_start, L->q_pos, L->num_seqs, L->num_q, q_bf16, kv_codes,
+                     kv_e8m0, kv_rowscale, idx, k, swa_fp8, swa_scale, swa_pos0, swa_clip, W, Hq, D,
+                     sm_scale, out, lse, workspace};
+  hipError_t e = smqa::launch_attend(a, (hipStream_t)stream);
+  return e == hipSuccess ? SMQA_OK : hip_fail(e, "sparse_mqa_attend launch");
+}
+
+int decode_step(const smqa_layout* L, const uint8_t* q_fp8, const float* w, const uint8_t* k_fp8,
+                const float* k_scale, const int32_t* cand, int32_t n_cand, int32_t Hi, int32_t Di,
+                const uint16_t* q_bf16, const uint8_t* kv_codes, const uint8_t* kv_e8m0,
+                const float* kv_rowscale, const uint8_t* swa_fp8, const float* swa_scale,
+                const int32_t* swa_pos0, const int32_t* swa_clip, int32_t W, int32_t Hq, int32_t D,
+                float sm_scale, int32_t k, float* out, float* lse, int32_t* idx_out, void* workspace,
+                size_t workspace_bytes, void* stream) {
+  g_err.clear();
+  int st = check_layout(L);
+  if (st) return st;
+  if (L->num_q == 0) return SMQA_OK;
+  const int32_t cols = score_cols(L, n_cand, cand != nullptr);
+  // the score matrix lives in the workspace with ld = cols
+  st = check_score(L, q_fp8, w, k_fp8, k_scale, cand, n_cand, Hi, Di, nullptr, cols, false);
+  if (st) return st;
+  if (k < 1 || k > 4096) return fail(SMQA_ERR_UNSUPPORTED, "k = %d: supported 1..4096", k);
+  st = check_attend(q_bf16, kv_codes, kv_e8m0, kv_rowscale, idx_out, k, swa_fp8, swa_scale, swa_pos0,
+                    swa_clip, W, Hq, D, sm_scale, out, lse, false);
+  if (st) return st;
+  const DecodeWs d = decode_ws_layout(L, k, cols, W, Hq, D);
+  st = check_ws(workspace, workspace_bytes, d.total);
+  if (st) return st;
+  char* ws = (char*)workspace;
+  float* scores = (float*)(ws + d.scores_off);
+  int32_t* idx = idx_out ? idx_out : (int32_t*)(ws + d.idx_off);
+  hipStream_t s = (hipStream_t)stream;
+  smqa::ScoreArgs sa{L->seq_start, L->q_start, L->q_pos, L->num_seqs, L->num_q, L->max_ctx,
+                     q_fp8, w, k_fp8, k_scale, cand, cand ? n_cand : 0, Hi, Di, scores, cols};
+  hipError_t e = smqa::launch_score(sa, s);
+  if (e != hipSuccess) return hip_fail(e, "decode_step score launch");
+  smqa::TopkArgs ta{L->seq_start, L->q_start, L->q_pos, L->num_seqs, L->num_q, cols,
+                    scores, cols, cand, cand ? n_cand : 0, k, idx, ws + d.topk_off};
+  e = smqa::launch_topk(ta, s);
+  if (e != hipSuccess) return hip_fail(e, "decode_step topk launch");
+  smqa::AttendArgs aa{L->seq_start, L->q_start, L->q_pos, L->num_seqs, L->num_q, q_bf16, kv_codes,
+                      kv_e8m0, kv_rowscale, idx, k, swa_fp8, swa_scale, swa_pos0, swa_clip, W, Hq, D,
+                      sm_scale, out, lse, ws + d.attend_off};
+  e = smqa::launch_attend(aa, s);
+  if (e != hipSuccess) return hip_fail(e, "decode_step attend launch");
+  return SMQA_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,111 @@
+// Internal device/host helpers shared by the gfx950 kernels of libsmqa.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "smqa.h"
+
+namespace smqa {
+
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+typedef _Float16 v8h __attribute__((ext_vector_type(8)));
+typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+typedef _Float16 v2h __attribute__((ext_vector_type(2)));
+typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
+typedef unsigned v4u __attribute__((ext_vector_type(4)));
+typedef unsigned v2u __attribute__((ext_vector_type(2)));
+
+constexpr int kWave = 64;
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+// E8M0 exponent byte -> the float 2^(e-127) (e = 0 gives the subnormal 2^-127).
+__device__ __forceinline__ float e8m0_to_float(unsigned e) {
+  return e ? __uint_as_float(e << 23) : __uint_as_float(0x00400000u);
+}
+
+// Order-preserving map float -> uint32 (larger float -> larger key).
+// -inf (a masked score) and NaN map to 0, which marks "not in the scored set";
+// every finite score maps to a key >= 0x00800000.
+__device__ __forceinline__ unsigned score_key(float s) {
+  unsigned u = __float_as_uint(s);
+  if (s == -__builtin_inff() || s != s) return 0u;
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+// Largest b with q_start[b] <= t (queries are grouped by sequence).
+__device__ __forceinline__ int seq_of_query(const int32_t* q_start, int B, int t) {
+  int lo = 0, hi = B;
+  while (hi - lo > 1) {
+    int mid = (lo + hi) >> 1;
+    if (q_start[mid] <= t) lo = mid; else hi = mid;
+  }
+  return lo;
+}
+
+// ---------------------------------------------------------------- launchers
+// (defined in score.hip / topk.hip / attend.hip; arguments already validated)
+
+struct ScoreArgs {
+  const int64_t* seq_start;
+  const int32_t* q_start;
+  const int32_t* q_pos;
+  int32_t B, T, max_ctx;
+  const uint8_t* q_fp8;
+  const float* w;
+  const uint8_t* k_fp8;
+  const float* k_scale;
+  const int32_t* cand;
+  int32_t n_cand;
+  int32_t Hi, Di;
+  float* scores;
+  int64_t ld;
+};
+hipError_t launch_score(const ScoreArgs& a, hipStream_t s);
+
+struct TopkArgs {
+  const int64_t* seq_start;
+  const int32_t* q_start;
+  const int32_t* q_pos;
+  int32_t B, T, max_ctx;
+  const float* scores;
+  int64_t ld;
+  const int32_t* cand;
+  int32_t n_cand;
+  int32_t k;
+  int32_t* idx;
+  void* ws;
+};
+size_t topk_workspace_bytes(int32_t T, int32_t max_ctx, int32_t k);
+hipError_t launch_topk(const TopkArgs& a, hipStream_t s);
+
+struct AttendArgs {
+  const int64_t* seq_start;
+  const int32_t* q_start;
+  const int32_t* q_pos;
+  int32_t B, T;
+  const uint16_t* q;
+  const uint8_t* kv_codes;
+  const uint8_t* kv_e8m0;
+  const float* kv_rowscale;
+  const int32_t* idx;
+  int32_t k;
+  const uint8_t* swa;
+  const float* swa_scale;
+  const int32_t* swa_pos0;
+  const int32_t* swa_clip;
+  int32_t W, Hq, D;
+  float sm_scale;
+  float* out;
+  float* lse;
+  void* ws;
+};
+int attend_splits(int32_t T, int32_t k, int32_t W, int32_t Hq, int32_t D);
+size_t attend_workspace_bytes(int32_t T, int32_t k, int32_t W, int32_t Hq, int32_t D);
+hipError_t launch_attend(const AttendArgs& a, hipStream_t s);
+
+inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+}  // namespace smqa

@@ -1,0 +1,233 @@
+/*
+ * smqa.h — sparse multi-query attention decode path for AMD MI355X (gfx950).
+ *
+ * The operation (vLLM blog "DeepSeek-V4.1-Flash sur vLLM : 5x de débit
+ * agentique dès le jour 0", sections "SWA bounded replay" and "Kernels";
+ * CocoLoop digest, section "Les particularités du modèle lui-même"):
+ * a decoder layer reads two caches — a compressed global latent KV, shared by
+ * all heads and all layers, stored in FP4 at about 890 bytes per token, and an
+ * uncompressed FP8 sliding window over the last 128 positions.  Per query
+ * token it
+ *   1. scores context positions with a multi-head FP8 indexer
+ *      (sparse_mqa_score; blog §Kernels, "Logits MQA creux"),
+ *   2. keeps the top-k positions (topk_select; blog §TL;DR and §Kernels,
+ *      the DeepSelect top-k step),
+ *   3. attends over the selected FP4 latent rows plus the visible FP8 window
+ *      rows with one softmax (sparse_mqa_attend; blog §Kernels,
+ *      "MegaAttention avec KV compressé NVFP4"),
+ * and decode_step runs 1-3 in one call.  Bounded replay (blog §"Côté
+ * encodeur") re-runs the last 128 tokens of a prefix hit of length H with
+ * the window clipped at s = H - 128: pass per-query positions and swa_clip.
+ *
+ * Conventions for every entry point
+ * ---------------------------------
+ * - Array pointers are DEVICE pointers owned by the caller.  The library
+ *   never allocates, frees or synchronises; it enqueues kernels on `stream`
+ *   (a hipStream_t; NULL = the null stream) and returns.  Inputs must stay
+ *   valid until the stream reaches the work.  Outputs are overwritten.
+ * - Arguments are validated on the host before any HIP call.  On a
+ *   validation error nothing is launched, outputs are untouched and the call
+ *   returns a negative smqa_status; smqa_last_error() then describes it.
+ *   Values stored inside device arrays (positions, offsets, indices) are not
+ *   validated and must satisfy the stated ranges.
+ * - A failed launch returns SMQA_ERR_HIP.  Device faults surface at the
+ *   caller's next synchronisation.
+ * - Re-entrant; concurrent calls on different streams with different
+ *   workspaces are safe.
+ *
+ * Storage formats
+ * ---------------
+ * - FP8: OCP E4M3FN bytes (bias 7, max 448, 0x7F/0xFF NaN).
+ * - FP4: OCP MX E2M1 nibbles, element 2i in the low nibble of byte i, one
+ *   E8M0 exponent byte per 32 elements (scale 2^(e-127)), optional fp32 row
+ *   scale rho.  At D = 1664 a row is 832 + 52 + 4 = 888 bytes.
+ * - bf16 queries: raw bfloat16 bits.
+ * Inputs must be finite (no NaN codes).  The attention path stores decoded
+ * latent values in fp16 for the P*V product; this is exact when every E8M0
+ * exponent e of a nonzero block satisfies -23 <= e - 127 <= 13.
+ */
+#ifndef SMQA_H
+#define SMQA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  SMQA_OK = 0,
+  SMQA_ERR_NULL = -1,         /* a required pointer is NULL                          */
+  SMQA_ERR_SHAPE = -2,        /* inconsistent sizes (negative, ld too small, ...)    */
+  SMQA_ERR_ALIGN = -3,        /* a pointer violates its alignment requirement        */
+  SMQA_ERR_UNSUPPORTED = -4,  /* a size outside the supported limits (see below)     */
+  SMQA_ERR_WORKSPACE = -5,    /* workspace NULL or smaller than the size query says  */
+  SMQA_ERR_HIP = -6           /* a HIP launch failed                                 */
+} smqa_status;
+
+/*
+ * Ragged batch layout, shared by every call.
+ *   Sequence b owns cache rows [seq_start[b], seq_start[b+1]) of the global
+ *   latent and indexer-key arrays; its position j is row seq_start[b] + j.
+ *   Queries are grouped by sequence: the queries of b are
+ *   t in [q_start[b], q_start[b+1]) (decode: one per sequence).
+ *   q_pos[t] is the absolute position p_t of query t; it bounds everything the
+ *   query sees (causal, inclusive): scored positions j <= p_t, window rows at
+ *   positions <= p_t.
+ *   max_ctx (host) is an upper bound on the number of score columns of any
+ *   query: max_t(p_t) + 1 in dense mode, n_cand in candidate mode.
+ * Device arrays: seq_start int64 [B+1] (non-decreasing, seq_start[0] = 0),
+ * q_start int32 [B+1] (non-decreasing, q_start[B] = num_q), q_pos int32 [T]
+ * with 0 <= p_t.
+ */
+typedef struct {
+  int32_t num_seqs;           /* B >= 1                                     */
+  const int64_t* seq_start;   /* device int64 [B+1]                         */
+  int32_t num_q;              /* T >= 0                                     */
+  const int32_t* q_start;     /* device int32 [B+1]                         */
+  const int32_t* q_pos;       /* device int32 [T]                           */
+  int32_t max_ctx;            /* host bound on score columns per query      */
+} smqa_layout;
+
+/*
+ * Limits (SMQA_ERR_UNSUPPORTED beyond them):
+ *   indexer  Di in {64, 128}; 1 <= Hi <= 128
+ *   attention D % 128 == 0, 128 <= D <= 2048; Hq % 16 == 0, 16 <= Hq <= 128;
+ *             1 <= W <= 128
+ *   top-k    1 <= k <= 4096
+ * Alignment: q_fp8, k_fp8, kv_codes, swa_fp8, q_bf16, out: 16 bytes;
+ *            workspace: 256 bytes; every other pointer: 4 bytes.
+ */
+
+/*
+ * sparse_mqa_score — indexer scoring (blog §Kernels, "Logits MQA creux": one
+ * score per context position; late indexer layers score only a fixed set of
+ * 16K candidate positions, so their cost does not grow with the context).
+ *
+ *   S[t, j] = sum_{h < Hi} w[t,h] * max(0, kappa_j * sum_{d < Di} qI[t,h,d] * kI[row(j), d])
+ *
+ * Dense mode (cand == NULL): for every query t and every position
+ *   0 <= j <= min(p_t, len_b - 1), scores[t * ld_scores + j] = S[t, j].
+ *   Columns past that bound are not written.
+ * Candidate mode (cand != NULL): cand[t * n_cand + i] (i < n_cand) are
+ *   positions of query t's sequence, strictly ascending per query;
+ *   scores[t * ld_scores + i] = S[t, cand[t,i]], or -INFINITY when the
+ *   candidate is past p_t or past the sequence.
+ * q_fp8   uint8  [T][Hi][Di]  E4M3 indexer queries
+ * w       float  [T][Hi]      head weights (any sign)
+ * k_fp8   uint8  [N][Di]      E4M3 indexer keys, N = seq_start[B]
+ * k_scale float  [N] or NULL  per-key scale kappa (> 0; NULL = 1)
+ * scores  float  [T][ld_scores], ld_scores >= max_ctx (dense) / >= n_cand
+ * Arithmetic: FP8 x FP8 products are exact; sums are fp32.
+ */
+int sparse_mqa_score(const smqa_layout* L,
+                     const uint8_t* q_fp8, const float* w,
+                     const uint8_t* k_fp8, const float* k_scale,
+                     const int32_t* cand, int32_t n_cand,
+                     int32_t Hi, int32_t Di,
+                     float* scores, int64_t ld_scores,
+                     void* stream);
+
+/*
+ * topk_select — the k best positions per query (blog §TL;DR: DeepSelect, a
+ * top-k library for DeepSeek Sparse Attention; §Kernels: the indexer's top-k
+ * over the scored positions).
+ *
+ * Order: score descending, ties to the lower position.  The scored set of
+ * query t is columns 0..min(p_t, len_b - 1) (dense) or the columns whose
+ * score is not -INFINITY (candidate mode; positions are cand[t, col]).
+ * idx_out[t * k + i] receives the selected positions in ascending order;
+ * when the set has m < k entries, slots m..k-1 hold -1.  Bitwise
+ * deterministic.  scores is read only.
+ * workspace: smqa_topk_workspace_size() bytes, 256-byte aligned, contents
+ * need not be initialised; it is clobbered.
+ */
+int topk_select(const smqa_layout* L,
+                const float* scores, int64_t ld_scores,
+                const int32_t* cand, int32_t n_cand,
+                int32_t k, int32_t* idx_out,
+                void* workspace, size_t workspace_bytes,
+                void* stream);
+
+/*
+ * sparse_mqa_attend — multi-query attention of Hq heads over one shared
+ * latent (blog §"Performances agentiques": the KV latent is shared by all
+ * heads; §Kernels, MegaAttention: sparse attention reading the FP4 KV) over
+ *   the selected global rows   V[j] = e2m1 * 2^(E-127) * rho_j, j in idx[t] (j >= 0),
+ *   plus the window rows       X[u] = e4m3 * sigma_u at positions
+ *                              max(p_t - W + 1, s_t, 0) <= swa_pos0[b] + u <= p_t
+ * (blog §"SWA bounded replay": FP8 window of the last 128 positions; clipped
+ * at the replay start s = H - 128).  The latent row is both key and value.
+ * One softmax over the union, per head h:
+ *   l_x = sm_scale * <q[t,h], row_x>;  out[t,h] = sum_x softmax(l)_x row_x;
+ *   lse[t,h] = log(sum_x exp(l_x))   (natural log; -INFINITY and out = 0
+ *   when the query sees no row).
+ * q_bf16      uint16 [T][Hq][D]     bf16 bits
+ * kv_codes    uint8  [N][D/2]       E2M1 pairs
+ * kv_e8m0     uint8  [N][D/32]      block exponents
+ * kv_rowscale float  [N] or NULL    rho (NULL = 1)
+ * idx         int32  [T][k]         positions within the query's sequence,
+ *                                   0 <= j <= p_t and j < len_b, or -1 (skipped)
+ * swa_fp8     uint8  [B][W][D]      window rows; row u has position swa_pos0[b] + u
+ * swa_scale   float  [B][W] or NULL sigma (NULL = 1)
+ * swa_pos0    int32  [B]
+ * swa_clip    int32  [T] or NULL    s_t (NULL = no clip)
+ * out         float  [T][Hq][D]     lse float [T][Hq] or NULL
+ * workspace: smqa_attend_workspace_size() bytes (may be 0 -> workspace may be NULL).
+ * Arithmetic: q.row on bf16 MFMA with fp32 sums; softmax in fp32; P*V on fp16
+ * MFMA (P rounded to fp16 once) with fp32 sums; rho and sigma applied in fp32.
+ */
+int sparse_mqa_attend(const smqa_layout* L,
+                      const uint16_t* q_bf16,
+                      const uint8_t* kv_codes, const uint8_t* kv_e8m0, const float* kv_rowscale,
+                      const int32_t* idx, int32_t k,
+                      const uint8_t* swa_fp8, const float* swa_scale,
+                      const int32_t* swa_pos0, const int32_t* swa_clip,
+                      int32_t W, int32_t Hq, int32_t D, float sm_scale,
+                      float* out, float* lse,
+                      void* workspace, size_t workspace_bytes,
+                      void* stream);
+
+/*
+ * decode_step — sparse_mqa_score -> topk_select -> sparse_mqa_attend in one
+ * call on one stream, with the scores and the selection kept in the
+ * workspace (blog §Kernels: fusing the steps removes memory round trips and
+ * launches between them).  Arguments mean what they mean in the three calls;
+ * idx_out (int32 [T][k]) optionally receives the selection.  Works for any
+ * layout: decode (one query per sequence at p = len - 1) and bounded-replay
+ * chunks (several queries per sequence with swa_clip).
+ */
+int decode_step(const smqa_layout* L,
+                const uint8_t* q_fp8, const float* w,
+                const uint8_t* k_fp8, const float* k_scale,
+                const int32_t* cand, int32_t n_cand,
+                int32_t Hi, int32_t Di,
+                const uint16_t* q_bf16,
+                const uint8_t* kv_codes, const uint8_t* kv_e8m0, const float* kv_rowscale,
+                const uint8_t* swa_fp8, const float* swa_scale,
+                const int32_t* swa_pos0, const int32_t* swa_clip,
+                int32_t W, int32_t Hq, int32_t D, float sm_scale,
+                int32_t k,
+                float* out, float* lse, int32_t* idx_out,
+                void* workspace, size_t workspace_bytes,
+                void* stream);
+
+/* Workspace sizes in bytes (host-only arithmetic, no HIP call).  A NULL or
+ * inconsistent layout returns 0 and sets smqa_last_error(). */
+size_t smqa_topk_workspace_size(const smqa_layout* L, int32_t k, int32_t n_cand);
+size_t smqa_attend_workspace_size(const smqa_layout* L, int32_t k, int32_t W,
+                                  int32_t Hq, int32_t D);
+size_t smqa_decode_step_workspace_size(const smqa_layout* L, int32_t k, int32_t n_cand,
+                                       int32_t W, int32_t Hq, int32_t D);
+
+/* Thread-local description of the last non-OK return on this thread ("" if none). */
+const char* smqa_last_error(void);
+
+/* Library version string. */
+const char* smqa_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* SMQA_H */

@@ -131,8 +131,11 @@ def topk_set_ok(S_ref, cand_pos, k, got, rel_gap=1e-5):
     return True, "near-tie band"
 
 
-def close_attention(O_gpu, O_ref, lse_gpu=None, lse_ref=None, atol=2e-3, rtol=1e-3, lse_tol=1e-4):
-    """Per (t, h): max|dO| <= atol and max|dO| <= rtol * max|O_ref|; |dLSE| <= lse_tol."""
+def close_attention(O_gpu, O_ref, lse_gpu=None, lse_ref=None, atol=2e-3, rtol=1e-3, lse_tol=1e-4,
+                    lse_rtol=1e-6):
+    """Per (t, h): max|dO| <= atol and max|dO| <= rtol * max|O_ref|;
+    |dLSE| <= lse_tol + lse_rtol * |LSE_ref| (fp32 logits carry ~2^-24 relative error, which
+    dominates the absolute bar only once |LSE| reaches ~1e3)."""
     d = np.abs(np.asarray(O_gpu, dtype=np.float64) - O_ref).max(axis=-1)
     scale = np.abs(O_ref).max(axis=-1)
     ok = (d <= atol) & (d <= rtol * scale + 1e-30)
@@ -141,7 +144,7 @@ def close_attention(O_gpu, O_ref, lse_gpu=None, lse_ref=None, atol=2e-3, rtol=1e
         dl = np.abs(np.asarray(lse_gpu, dtype=np.float64) - lse_ref)
         both_inf = np.isinf(lse_ref) & (np.asarray(lse_gpu) == lse_ref)
         dl = np.where(both_inf, 0.0, dl)
-        ok &= dl <= lse_tol
+        ok &= dl <= lse_tol + lse_rtol * np.where(np.isinf(lse_ref), 0.0, np.abs(lse_ref))
         msg += f", max|dLSE|={dl.max():.3e}"
     return bool(ok.all()), msg
 
@@ -162,3 +165,74 @@ def close_scores(S_gpu, S_ref, rtol=1e-4, floor=1e-7):
 
 def fsum(xs):
     return math.fsum(xs)
+
+
+# ------------------------------------------------------------------ GPU call wrappers
+
+def announce(msg: str):
+    """Name the case on stdout before GPU work (flushed, so a fault still shows it)."""
+    print(f"[gpu-case] {msg}", flush=True)
+
+
+def gpu_batch(smqa, wl):
+    return smqa.Batch(wl.seq_start, wl.q_start, wl.q_pos, wl.max_ctx)
+
+
+def gpu_score(smqa, wl):
+    return smqa.sparse_mqa_score(gpu_batch(smqa, wl), wl.qI, wl.w, wl.kI, wl.kscale, wl.cand)
+
+
+def gpu_topk(smqa, wl, scores, k=None):
+    return smqa.topk_select(gpu_batch(smqa, wl), scores, wl.k if k is None else k, cand=wl.cand)
+
+
+def gpu_attend(smqa, wl, idx):
+    return smqa.sparse_mqa_attend(gpu_batch(smqa, wl), wl.q, wl.kv_codes, wl.kv_e8m0,
+                                  wl.kv_rowscale, idx, wl.swa, wl.swa_scale, wl.swa_pos0,
+                                  wl.swa_clip, wl.sm_scale)
+
+
+def gpu_decode(smqa, wl, k=None):
+    return smqa.decode_step(gpu_batch(smqa, wl), wl.qI, wl.w, wl.kI, wl.kscale, wl.cand, wl.q,
+                            wl.kv_codes, wl.kv_e8m0, wl.kv_rowscale, wl.swa, wl.swa_scale,
+                            wl.swa_pos0, wl.swa_clip, wl.k if k is None else k, wl.sm_scale)
+
+
+def oracle_scores_for(a, ts, cand=None):
+    """Oracle scores of the queries ts only (same columns as the full call)."""
+    ld = a["max_ctx"]
+    return np.stack([_score_one_query(a, t, cand, ld) for t in ts])
+
+
+def _score_one_query(a, t, cand, ld):
+    from oracle import ref
+    b = q_seq_of(a)[t]
+    base = int(a["seq_start"][b])
+    n = int(a["seq_start"][b + 1]) - base
+    seq = np.array([0, n], dtype=np.int64)
+    kI = a["kI"][base:base + n]
+    ks = None if a["kscale"] is None else a["kscale"][base:base + n]
+    return ref.score(a["qI"][t:t + 1], a["w"][t:t + 1], kI, ks, seq, np.array([0, 1]),
+                     a["q_pos"][t:t + 1], cand=None if cand is None else cand[t:t + 1], ld=ld)[0]
+
+
+def oracle_attend_for(a, ts, idx_rows):
+    """Oracle attention of queries ts with the given selections (rows of idx)."""
+    from oracle import ref
+    qs = q_seq_of(a)
+    O, L = [], []
+    for i, t in enumerate(ts):
+        b = qs[t]
+        base = int(a["seq_start"][b])
+        n = int(a["seq_start"][b + 1]) - base
+        o, l = ref.attend(a["q"][t:t + 1], a["kv_codes"][base:base + n], a["kv_e8m0"][base:base + n],
+                          None if a["kv_rowscale"] is None else a["kv_rowscale"][base:base + n],
+                          np.asarray(idx_rows[i])[None], a["swa"][b:b + 1],
+                          None if a["swa_scale"] is None else a["swa_scale"][b:b + 1],
+                          a["swa_pos0"][b:b + 1],
+                          None if a["swa_clip"] is None else a["swa_clip"][t:t + 1],
+                          np.array([0, n]), np.array([0, 1]), a["q_pos"][t:t + 1], a["W"],
+                          a["sm_scale"])
+        O.append(o[0])
+        L.append(l[0])
+    return np.stack(O), np.stack(L)

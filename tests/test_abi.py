@@ -1,0 +1,143 @@
+"""C-ABI boundary checks that need no GPU: the library loads, exports every entry
+point the header declares, and rejects bad arguments before any HIP call."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import fp8_kv_cache_sparse_amd as smqa
+from fp8_kv_cache_sparse_amd._binding import Layout
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "smqa.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(smqa.LIB_PATH), reason="libsmqa.so not built")
+
+A16 = 0x100000          # fake, suitably aligned device addresses: never dereferenced by validation
+A4 = 0x200004
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[\w\s\*]+?\b(\w+)\s*\(", text, flags=re.M)) -
+                  {"if", "while", "for", "return", "sizeof"})
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for n in ("sparse_mqa_score", "topk_select", "sparse_mqa_attend", "decode_step",
+              "smqa_topk_workspace_size", "smqa_attend_workspace_size",
+              "smqa_decode_step_workspace_size", "smqa_last_error", "smqa_version"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(smqa.LIB_PATH)
+    for n in declared_functions():
+        assert hasattr(lib, n), n
+
+
+def layout(B=1, T=1, max_ctx=8192, seq=A16, qs=A4, qp=A4):
+    return Layout(B, seq, T, qs, qp, max_ctx)
+
+
+def lib():
+    return smqa.load()
+
+
+def err():
+    return lib().smqa_last_error().decode()
+
+
+def score(L, **kw):
+    a = dict(q=A16, w=A4, k=A16, ks=None, cand=None, n_cand=0, Hi=64, Di=128, s=A4, ld=8192)
+    a.update(kw)
+    return lib().sparse_mqa_score(ctypes.byref(L) if L is not None else None, a["q"], a["w"], a["k"],
+                                  a["ks"], a["cand"], a["n_cand"], a["Hi"], a["Di"], a["s"], a["ld"], None)
+
+
+def test_score_validation():
+    L = layout()
+    assert score(None) == -1 and "layout" in err()
+    assert score(L, q=None) == -1 and "q_fp8" in err()
+    assert score(L, s=None) == -1
+    assert score(L, Di=96) == -4 and "Di" in err()
+    assert score(L, Hi=0) == -4 and score(L, Hi=129) == -4
+    assert score(L, ld=100) == -2 and "ld_scores" in err()
+    assert score(L, q=A16 + 8) == -3 and "aligned" in err()
+    assert score(L, cand=A4, n_cand=0) == -2
+    assert score(L, cand=A4, n_cand=300, ld=200) == -2
+    assert score(layout(B=0)) == -2
+    assert score(layout(T=-1)) == -2
+    assert score(layout(seq=None)) == -1
+    assert score(layout(seq=A16 + 4)) == -3
+    assert score(layout(max_ctx=0)) == -2
+    # zero queries: nothing to do, no launch
+    assert score(layout(T=0)) == 0
+
+
+def topk(L, k=2048, ws=None, nbytes=0, **kw):
+    a = dict(s=A4, ld=8192, cand=None, n_cand=0, idx=A4)
+    a.update(kw)
+    return lib().topk_select(ctypes.byref(L), a["s"], a["ld"], a["cand"], a["n_cand"], k, a["idx"],
+                             ws, nbytes, None)
+
+
+def test_topk_validation_and_workspace():
+    L = layout()
+    assert topk(L, k=0) == -4 and topk(L, k=4097) == -4
+    assert topk(L, idx=None) == -1
+    assert topk(L, ld=10) == -2
+    big = layout(max_ctx=100000)
+    need = lib().smqa_topk_workspace_size(ctypes.byref(big), 2048, 0)
+    assert need > 0
+    assert topk(big, ld=100000) == -5 and "workspace" in err()
+    assert topk(big, ld=100000, ws=A16 * 16, nbytes=need - 1) == -5
+    assert topk(big, ld=100000, ws=A16 * 16 + 16, nbytes=need) == -3
+    # short rows need no workspace
+    assert lib().smqa_topk_workspace_size(ctypes.byref(L), 2048, 0) == 0
+
+
+def attend(L, **kw):
+    a = dict(q=A16, c=A16, e=A4, rs=None, idx=A4, k=2048, swa=A16, ss=None, p0=A4, clip=None, W=128,
+             Hq=64, D=1664, sc=0.0245, out=A16, lse=None, ws=None, nb=0)
+    a.update(kw)
+    return lib().sparse_mqa_attend(ctypes.byref(L), a["q"], a["c"], a["e"], a["rs"], a["idx"], a["k"],
+                                   a["swa"], a["ss"], a["p0"], a["clip"], a["W"], a["Hq"], a["D"], a["sc"],
+                                   a["out"], a["lse"], a["ws"], a["nb"], None)
+
+
+def test_attend_validation():
+    L = layout()
+    assert attend(L, D=1600) == -4 and "D" in err()
+    assert attend(L, D=4096) == -4
+    assert attend(L, Hq=24) == -4 and attend(L, Hq=256) == -4
+    assert attend(L, W=0) == -4 and attend(L, W=129) == -4
+    assert attend(L, k=0) == -4
+    assert attend(L, swa=None) == -1 and attend(L, p0=None) == -1 and attend(L, idx=None) == -1
+    assert attend(L, out=A16 + 4) == -3
+    assert attend(L, sc=float("nan")) == -2
+    # one decode query needs split-KV partials -> workspace required
+    need = lib().smqa_attend_workspace_size(ctypes.byref(L), 2048, 128, 64, 1664)
+    assert need > 0
+    assert attend(L) == -5
+    assert attend(layout(T=0)) == 0
+
+
+def test_decode_step_workspace_covers_parts():
+    L = layout(max_ctx=524288, T=4, B=4)
+    total = lib().smqa_decode_step_workspace_size(ctypes.byref(L), 2048, 0, 128, 64, 1664)
+    scores = 4 * 524288 * 4
+    tk = lib().smqa_topk_workspace_size(ctypes.byref(L), 2048, 0)
+    at = lib().smqa_attend_workspace_size(ctypes.byref(L), 2048, 128, 64, 1664)
+    assert total >= scores + 4 * 2048 * 4 + tk + at
+    assert lib().smqa_decode_step_workspace_size(None, 2048, 0, 128, 64, 1664) == 0
+
+
+def test_error_string_cleared_on_success_path():
+    assert score(layout(Di=3) if False else layout(), Di=3) == -4
+    assert err() != ""
+    assert score(layout(T=0)) == 0
+    assert err() == ""

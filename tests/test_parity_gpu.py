@@ -1,0 +1,265 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 oracle.
+
+Comparators: scores within 1e-4 relative (floor 1e-7 of the row max) and
+bit-exact on integer-valued inputs; top-k sets exact outside a 1e-5-relative
+gap at the k-th score, and inside it every strictly-better position present
+and every chosen one within the band; attention per (query, head) within
+max|dO| <= 2e-3 and <= 1e-3 * max|O|, |dLSE| <= 1e-4, with the oracle run on the
+GPU's own selection.
+"""
+import numpy as np
+import pytest
+import torch
+
+import synth
+from oracle import ref
+from helpers import (announce, close_attention, close_scores, gpu_attend, gpu_decode, gpu_score,
+                     gpu_topk, np_inputs, oracle_attend_for, oracle_scores_for, q_seq_of, topk_set_ok)
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+
+
+def gen(name, seed=0, **kw):
+    announce(f"generate {name} seed={seed} {kw}")
+    return synth.generate(name, seed=seed, device=DEV, **kw)
+
+
+def sync():
+    torch.cuda.synchronize()
+
+
+# ------------------------------------------------------------------ score
+
+@pytest.mark.parametrize("name,kw", [
+    ("tiny", {}),
+    ("decode_8k", {}),
+    ("decode_8k", dict(B=3, lengths=(3000, 9000), Hi=40)),            # ragged, Hi not a multiple of 16
+    ("replay_h100k", dict(B=2, lengths=3000, replay=(3000, 40))),     # many queries per sequence
+])
+def test_score_dense(lib, name, kw):
+    wl = synth.with_scales(gen(name, **kw)) if name == "replay_h100k" else gen(name, **kw)
+    announce(f"score {name} T={wl.T} N={wl.N}")
+    S = gpu_score(lib, wl)
+    sync()
+    a = np_inputs(wl)
+    S_ref = ref.score(a["qI"], a["w"], a["kI"], a["kscale"], a["seq_start"], a["q_start"], a["q_pos"],
+                      ld=wl.max_ctx)
+    S_gpu = S.cpu().numpy().astype(np.float64)
+    S_gpu[S_ref == -np.inf] = -np.inf        # dense mode leaves columns past p_t unwritten
+    for t in range(wl.T):
+        ok, msg = close_scores(S_gpu[t], S_ref[t])
+        assert ok, f"query {t}: {msg}"
+
+
+def test_score_integer_inputs_bit_exact(lib):
+    announce("score integer-valued inputs")
+    g = torch.Generator(device=DEV).manual_seed(5)
+    ints = torch.randint(-4, 5, (1, 64, 128), generator=g, device=DEV).float()
+    keys = torch.randint(-4, 5, (5000, 128), generator=g, device=DEV).float()
+    wl = gen("decode_8k", lengths=5000)
+    wl.qI = synth.encode_e4m3(ints)
+    wl.kI = synth.encode_e4m3(keys)
+    wl.w = (2.0 ** torch.randint(-3, 3, (1, 64), generator=g, device=DEV).float()).contiguous()
+    S = gpu_score(lib, wl)
+    sync()
+    a = np_inputs(wl)
+    S_ref = ref.score(a["qI"], a["w"], a["kI"], None, a["seq_start"], a["q_start"], a["q_pos"])
+    assert np.array_equal(S.cpu().numpy()[0, :5000].astype(np.float64), S_ref[0, :5000])
+
+
+def test_score_candidates(lib):
+    wl = gen("decode_8k", B=2, lengths=(20000, 40000), n_cand=16384)
+    wl.q_pos[0] -= 777                       # some candidates lie past the query
+    announce(f"score candidates lengths={wl.meta['lengths']}")
+    S = gpu_score(lib, wl)
+    sync()
+    a = np_inputs(wl)
+    S_ref = ref.score(a["qI"], a["w"], a["kI"], None, a["seq_start"], a["q_start"], a["q_pos"],
+                      cand=a["cand"])
+    for t in range(wl.T):
+        ok, msg = close_scores(S.cpu().numpy()[t], S_ref[t])
+        assert ok, f"query {t}: {msg}"
+    assert np.isinf(S_ref).any()
+
+
+# ------------------------------------------------------------------ top-k
+
+def _topk_case(lib, S_host, k, cand=None, q_pos=None):
+    T, n = S_host.shape
+    seq_start = torch.tensor([0, 1 << 30], dtype=torch.int64, device=DEV)   # one long sequence
+    q_start = torch.tensor([0, T], dtype=torch.int32, device=DEV)
+    if q_pos is None:
+        q_pos = np.full(T, n - 1)
+    qp = torch.tensor(q_pos, dtype=torch.int32, device=DEV)
+    max_ctx = n if cand is None else cand.shape[1]
+    L = lib.Batch(seq_start, q_start, qp, int(max_ctx) if cand is not None else int(q_pos.max()) + 1)
+    S_dev = torch.tensor(S_host, dtype=torch.float32, device=DEV)
+    cd = None if cand is None else torch.tensor(cand, dtype=torch.int32, device=DEV)
+    idx = lib.topk_select(L, S_dev, k, cand=cd).cpu().numpy()
+    for t in range(T):
+        S_ref = S_host[t].astype(np.float32).astype(np.float64)
+        if cand is None:
+            S_ref = S_ref.copy()
+            S_ref[q_pos[t] + 1:] = -np.inf
+        ok, msg = topk_set_ok(S_ref, None if cand is None else cand[t], k, idx[t])
+        assert ok, f"query {t}: {msg}"
+        # exact where there is no near tie
+        exp = ref.topk(S_ref[None], k, cand=None if cand is None else cand[t:t + 1])[0]
+        if msg != "near-tie band":
+            assert np.array_equal(exp, idx[t])
+    return idx
+
+
+@pytest.mark.parametrize("n,k", [(8192, 2048), (4096, 256), (16384, 4096), (100_000, 2048),
+                                 (524_288, 2048), (30_000, 7)])
+def test_topk_random(lib, n, k):
+    announce(f"topk random n={n} k={k}")
+    rng = np.random.default_rng(n + k)
+    S = rng.standard_normal((3, n)).astype(np.float32) * 10 + 50
+    _topk_case(lib, S, k, q_pos=np.array([n - 1, n // 2, n - 3]))
+
+
+@pytest.mark.parametrize("n", [5000, 60_000])
+def test_topk_ties_take_lowest_positions(lib, n):
+    announce(f"topk constant scores n={n}")
+    S = np.zeros((2, n), dtype=np.float32)
+    S[1, ::2] = 1.0                                    # half the entries tie at the top
+    idx = _topk_case(lib, S, 2048)
+    assert idx[0].tolist() == list(range(2048))
+    assert idx[1].tolist() == list(range(0, 4096, 2))
+
+
+def test_topk_fewer_valid_than_k(lib):
+    announce("topk fewer than k")
+    rng = np.random.default_rng(1)
+    S = rng.standard_normal((2, 40000)).astype(np.float32)
+    idx = _topk_case(lib, S, 2048, q_pos=np.array([999, 30000]))
+    assert np.all(idx[0, 1000:] == -1) and idx[0, :1000].tolist() == list(range(1000))
+
+
+def test_topk_candidates_with_masked_entries(lib):
+    announce("topk candidates")
+    rng = np.random.default_rng(2)
+    n_cand = 20000
+    cand = np.stack([np.sort(rng.choice(200000, n_cand, replace=False)) for _ in range(2)])
+    S = rng.standard_normal((2, n_cand)).astype(np.float32)
+    S[0, 15000:] = -np.inf
+    _topk_case(lib, S, 2048, cand=cand.astype(np.int32))
+
+
+# ------------------------------------------------------------------ attention
+
+def _attend_check(lib, wl, idx_np=None):
+    a = np_inputs(wl)
+    if idx_np is None:
+        S = ref.score(a["qI"], a["w"], a["kI"], a["kscale"], a["seq_start"], a["q_start"], a["q_pos"])
+        idx_np = ref.topk(S, wl.k)
+    idx = torch.tensor(idx_np, dtype=torch.int32, device=DEV)
+    announce(f"attend {wl.name} T={wl.T} Hq={wl.Hq} D={wl.D} k={wl.k}")
+    out, lse = gpu_attend(lib, wl, idx)
+    sync()
+    a["swa_clip"] = None if wl.swa_clip is None else wl.swa_clip.cpu().numpy()
+    O, L = ref.attend(a["q"], a["kv_codes"], a["kv_e8m0"], a["kv_rowscale"], idx_np, a["swa"],
+                      a["swa_scale"], a["swa_pos0"], a["swa_clip"], a["seq_start"], a["q_start"],
+                      a["q_pos"], a["W"], a["sm_scale"])
+    ok, msg = close_attention(out.cpu().numpy(), O, lse.cpu().numpy(), L)
+    assert ok, msg
+    return out, lse
+
+
+@pytest.mark.parametrize("name,kw", [
+    ("tiny", {}),
+    ("decode_8k", dict(lengths=6000)),
+    ("decode_8k", dict(B=2, lengths=3000, Hq=32, D=1024, k=500)),       # 32-head workgroups
+    ("decode_8k", dict(B=3, lengths=(300, 2000), k=1000, W=100)),       # partial tiles, W % 32 != 0
+    ("replay_h100k", dict(B=2, lengths=4000, replay=(4000, 128))),       # clipped window
+])
+def test_attend(lib, name, kw):
+    _attend_check(lib, gen(name, **kw))
+
+
+def test_attend_with_scales_and_padding(lib):
+    wl = synth.with_scales(gen("decode_8k", B=2, lengths=(1500, 2500), k=2048))
+    a = np_inputs(wl)
+    S = ref.score(a["qI"], a["w"], a["kI"], a["kscale"], a["seq_start"], a["q_start"], a["q_pos"])
+    idx = ref.topk(S, wl.k)
+    assert (idx == -1).any()                          # fewer valid positions than k
+    _attend_check(lib, wl, idx)
+
+
+def test_attend_peaked_rows_respect_the_clip(lib):
+    """One dominant row decides O: a dominant window row just before the clip must be excluded,
+    one at the clip start included, and a selected global row at the k-th slot used."""
+    wl = gen("replay_h100k", B=1, lengths=3000, replay=(3000, 128))
+    s = int(wl.swa_clip[0])
+    W = wl.W
+    pos0 = int(wl.swa_pos0[0])
+    # make window row at position s-1 (excluded) and s (included) huge along q of query 0
+    q0 = wl.q[0].float()
+    direction = torch.sign(q0[0]).to(torch.float32)
+    big = synth.encode_e4m3(direction * 448.0)
+    u_excl, u_incl = s - 1 - pos0, s - pos0
+    if u_excl >= 0:
+        wl.swa[0, u_excl] = big
+    wl.swa[0, u_incl] = synth.encode_e4m3(direction * 300.0)
+    out, _ = _attend_check(lib, wl)
+    row_incl = wl.swa[0, u_incl].view(torch.float8_e4m3fn).float()
+    # head 0 of query 0 is dominated by the included row
+    assert torch.allclose(out[0, 0], row_incl, rtol=1e-2, atol=1e-2)
+
+
+# ------------------------------------------------------------------ decode step
+
+def _decode_check(lib, wl, ts=None):
+    announce(f"decode_step {wl.name} T={wl.T} N={wl.N} cand={wl.cand is not None}")
+    out, lse, idx = gpu_decode(lib, wl)
+    sync()
+    a = np_inputs(wl)
+    ts = list(range(wl.T)) if ts is None else ts
+    cand = a["cand"]
+    S_ref = oracle_scores_for(a, ts, cand)
+    idx_g = idx.cpu().numpy()
+    for i, t in enumerate(ts):
+        ok, msg = topk_set_ok(S_ref[i], None if cand is None else cand[t], wl.k, idx_g[t])
+        assert ok, f"query {t}: {msg}"
+    O, L = oracle_attend_for(a, ts, idx_g[ts])
+    ok, msg = close_attention(out.cpu().numpy()[ts], O, lse.cpu().numpy()[ts], L)
+    assert ok, msg
+    return out, lse, idx
+
+
+@pytest.mark.parametrize("name,kw", [
+    ("tiny", {}),
+    ("decode_8k", {}),
+    ("ragged_b32", dict(B=4, lengths=(16384, 30000))),
+    ("replay_h100k", dict(B=2, lengths=5000, replay=(5000, 128))),
+    ("decode_512k", dict(B=2, lengths=70000)),
+])
+def test_decode_step(lib, name, kw):
+    _decode_check(lib, gen(name, **kw))
+
+
+def test_decode_step_candidates(lib):
+    _decode_check(lib, gen("decode_512k", B=2, lengths=60000, n_cand=16384))
+
+
+# full sizes, in the configuration the benchmark times; sampled queries where the oracle is slow
+@pytest.mark.parametrize("name,ts", [
+    ("decode_8k", None),
+    ("decode_512k", None),
+    ("ragged_b32", [0, 7, 31]),
+    ("replay_h100k", [0, 1, 127, 128, 700, 1023]),
+])
+def test_decode_step_full_size(lib, name, ts):
+    _decode_check(lib, gen(name), ts)
+
+
+def test_decode_step_deterministic(lib):
+    wl = gen("ragged_b32", B=3, lengths=(20000, 40000))
+    announce("decode_step determinism")
+    o1, l1, i1 = gpu_decode(lib, wl)
+    o2, l2, i2 = gpu_decode(lib, wl)
+    sync()
+    assert torch.equal(i1, i2) and torch.equal(o1, o2) and torch.equal(l1, l2)
