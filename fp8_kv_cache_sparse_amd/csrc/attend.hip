@@ -4,27 +4,35 @@
 // positions and its clip at the replay start; section "Performances agentiques", one
 // KV latent shared by every head).
 //
-// Workgroup = (query t, group of 16*MT heads, contiguous range of 32-row tiles).
-// Tiles 0..ceil(k/32)-1 hold the selected global rows, the remaining ones the window
-// rows.  Per tile:
-//   stage    global rows: E2M1 codes + E8M0 bytes are gathered into LDS with 16-byte
-//            loads (window rows are read straight from global memory, L2-resident);
-//   Q.K^T    bf16 MFMA 16x16x32; every wave owns <= 2 slices of 128 dims of the
-//            contraction and keeps its slice of q in registers; FP4 -> bf16 via
-//            v_cvt_scalef32_pk_bf16_fp4 (exact); partial logits reduced through LDS;
-//   softmax  online, base-2, fp32; rho / sigma folded into the logit and into P;
-//   P.V      fp16 MFMA 16x16x32; every wave owns <= 2 slices of 128 output dims.  The
-//            B operand needs 8 rows of one column per lane: each lane converts a 4-byte
-//            word (8 dims) of 8 rows and transposes in registers with v_perm_b32, which
-//            makes one lane feed 8 MFMAs whose output columns are dims 8n+j.
-// Several tile ranges per (query, head group) are merged with their log-sum-exp in a
-// second kernel.
+// Workgroup = (query t, group of 16*MT heads, contiguous range of tiles), 8 waves.
+// A query's tiles are ceil(k/32) tiles of 32 selected global rows followed by the
+// 16-row tiles of window rows that overlap its visible window (fully clipped window
+// rows are never touched).
+//
+// Every tile goes through the same pipeline:
+//   prefetch  rows of tile i+2 gathered into registers with 16-byte loads (E2M1 codes
+//             + E8M0 bytes, or E4M3 bytes) while tiles i, i+1 compute;
+//   commit    registers -> one of two LDS tile buffers;
+//   Q.K^T     bf16 MFMA 16x16x32 over this wave's 128-dim slices of the contraction
+//             (q slice staged once in LDS); E2M1/E4M3 -> bf16 is exact
+//             (v_cvt_scalef32_pk_bf16_fp4 / _fp8); partial logits reduced through LDS;
+//   softmax   online, base 2, fp32; rho / sigma folded into the logit and into P;
+//   P.V       fp16 MFMA 16x16x32 into this wave's 128-dim output slices.  The B operand
+//             needs 8 rows of one column per lane: each lane converts one 4-byte word
+//             (8 dims) of 8 rows and transposes in registers with v_perm_b32, so one
+//             lane feeds 8 MFMAs whose output columns are dims 8n+j.
+// One iteration runs P.V of tile i and Q.K^T of tile i+1 back to back between two
+// barriers; waves own Q.K^T slices {w, w+8} and P.V slices {(w+3)%8, (w+3)%8+8}, which
+// balances that combined phase over waves and SIMDs when D/128 is not a multiple of 8.
+// Several tile ranges per (query, head group) are merged by log-sum-exp in a second
+// kernel.
 #include "common.h"
 
 namespace smqa {
 
 constexpr int kAttThreads = 512;
-constexpr int kRows = 32;
+constexpr int kGRows = 32;   // rows per tile of selected global rows
+constexpr int kWRows = 16;   // rows per tile of window rows
 
 template <class T>
 __device__ __forceinline__ unsigned bits_of(T x) {
@@ -35,25 +43,231 @@ __device__ __forceinline__ unsigned bits_of(T x) {
 template <int MT>
 struct AttSmem {
   static constexpr int kHG = 16 * MT;
-  int valid[kRows];
-  float rscale[kRows];
-  int64_t roff[kRows];
+  int valid[2][kGRows];
+  float rscale[2][kGRows];
   float m[kHG], l[kHG], alpha[kHG];
-  int any_valid;
-  int rescale;
   __attribute__((aligned(16))) _Float16 P[kHG][40];     // 80-byte rows: conflict-free b128 reads
-  float red[8][kHG][kRows];
-  __attribute__((aligned(16))) uint8_t e8[kRows][64];
+  float red[8][kHG][kGRows];
+  __attribute__((aligned(16))) uint8_t e8[2][kGRows][64];
 };
+
+// Per-workgroup constants of one query / head group / tile range.
+struct AttCtx {
+  int D, W, k, NSS, RS4, RS8, QS, BUF;
+  int ng, wt0, tb, te, gx0;
+  int b, p, lo_win, pos0;
+  int64_t base;
+  float lscale;
+};
+
+__device__ __forceinline__ v8bf cvt8_fp4_bf16(unsigned wd, float scl) {
+  v4u u;
+  u.x = bits_of(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(wd, scl, 0));
+  u.y = bits_of(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(wd, scl, 1));
+  u.z = bits_of(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(wd, scl, 2));
+  u.w = bits_of(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(wd, scl, 3));
+  return __builtin_bit_cast(v8bf, u);
+}
+
+__device__ __forceinline__ v8bf cvt8_fp8_bf16(unsigned w0, unsigned w1) {
+  v4u u;
+  u.x = bits_of(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, 1.0f, false));
+  u.y = bits_of(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, 1.0f, true));
+  u.z = bits_of(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, 1.0f, false));
+  u.w = bits_of(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, 1.0f, true));
+  return __builtin_bit_cast(v8bf, u);
+}
+
+// Partial logits of this wave's Q.K^T slices for one tile, written to red[wave].
+template <int MT, int NS>
+__device__ __forceinline__ void qk_tile(const AttCtx& c, AttSmem<MT>& sm, const uint8_t* buf, int slot,
+                                        bool fp8, const uint8_t* qs, int wave, int g, int n) {
+  v4f sacc[MT][2];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) sacc[mt][0] = sacc[mt][1] = v4f{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int s = 0; s < NS; ++s) {
+    const int ss = wave + 8 * s;
+    if (ss < c.NSS) {
+      // A operands: q of head 16*mt + n, dims 128*ss + 32*g + 8*i .. +8
+      v8bf qa[4][MT];
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+          qa[i][mt] = *(const v8bf*)(qs + (16 * mt + n) * c.QS + 2 * (128 * ss + 32 * g + 8 * i));
+      if (!fp8) {
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt) {
+          const int r = 16 * nt + n;
+          const v4u cw = *(const v4u*)(buf + r * c.RS4 + 64 * (r >> 3) + 64 * ss + 16 * g);
+          const float scl = e8m0_to_float(sm.e8[slot][r][4 * ss + g]);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const v8bf kb = cvt8_fp4_bf16(cw[i], scl);
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt)
+              sacc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[i][mt], kb, sacc[mt][nt], 0, 0, 0);
+          }
+        }
+      } else {
+        const uint8_t* src = buf + n * c.RS8 + 128 * ss + 32 * g;
+        const v4u c0 = *(const v4u*)src;
+        const v4u c1 = *(const v4u*)(src + 16);
+        const unsigned wds[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const v8bf kb = cvt8_fp8_bf16(wds[2 * i], wds[2 * i + 1]);
+#pragma unroll
+          for (int mt = 0; mt < MT; ++mt)
+            sacc[mt][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[i][mt], kb, sacc[mt][0], 0, 0, 0);
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) sm.red[wave][16 * mt + 4 * g + r][16 * nt + n] = sacc[mt][nt][r];
+}
+
+// Online softmax update for one tile (base 2): P = exp2(l - m_new) * row scale (fp16).
+template <int MT>
+__device__ __forceinline__ void softmax_tile(const AttCtx& c, AttSmem<MT>& sm, int slot, int tid) {
+  constexpr int TPH = 32 / MT;             // threads per head, all in one wave
+  const int h = tid / TPH;
+  const int x0 = (tid % TPH) * MT;
+  float sv[MT];
+  float tmax = -__builtin_inff();
+#pragma unroll
+  for (int e = 0; e < MT; ++e) {
+    const int x = x0 + e;
+    float acc = 0.0f;
+#pragma unroll
+    for (int w8 = 0; w8 < 8; ++w8) acc += sm.red[w8][h][x];
+    sv[e] = sm.valid[slot][x] ? acc * c.lscale * sm.rscale[slot][x] : -__builtin_inff();
+    tmax = fmaxf(tmax, sv[e]);
+  }
+#pragma unroll
+  for (int o2 = 1; o2 < TPH; o2 <<= 1) tmax = fmaxf(tmax, __shfl_xor(tmax, o2));
+  const float m_old = sm.m[h];             // read by every lane of the head before lane 0 writes
+  const float m_new = fmaxf(m_old, tmax);
+  const bool none = m_new == -__builtin_inff();
+  const float alpha = none ? 1.0f : exp2f(m_old - m_new);
+  float psum = 0.0f;
+#pragma unroll
+  for (int e = 0; e < MT; ++e) {
+    const int x = x0 + e;
+    const float pe = (none || !sm.valid[slot][x]) ? 0.0f : exp2f(sv[e] - m_new);
+    psum += pe;
+    sm.P[h][x] = (_Float16)(pe * sm.rscale[slot][x]);
+  }
+#pragma unroll
+  for (int o2 = 1; o2 < TPH; o2 <<= 1) psum += __shfl_xor(psum, o2);
+  if (tid % TPH == 0) {
+    sm.m[h] = m_new;
+    sm.l[h] = sm.l[h] * alpha + psum;
+    sm.alpha[h] = alpha;
+  }
+}
+
+// P.V of one tile into this wave's output slices.
+template <int MT, int NS>
+__device__ __forceinline__ void pv_tile(const AttCtx& c, const AttSmem<MT>& sm, const uint8_t* buf, int slot,
+                                        bool fp8, v4f (&o)[NS][8][MT], int wave, int g, int n) {
+  // rescale by alpha when the running max moved for any head of this wave's outputs
+  float al[MT][4];
+  bool moved = false;
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      al[mt][r] = sm.alpha[16 * mt + 4 * g + r];
+      moved |= al[mt][r] != 1.0f;
+    }
+  if (__ballot(moved)) {
+#pragma unroll
+    for (int s = 0; s < NS; ++s)
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) o[s][j][mt][r] *= al[mt][r];
+  }
+  v8h pa[MT];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) pa[mt] = *(const v8h*)(&sm.P[16 * mt + n][8 * g]);
+  const int cw0 = (wave + 3) & 7;
+#pragma unroll
+  for (int s = 0; s < NS; ++s) {
+    const int cc = cw0 + 8 * s;
+    if (cc < c.NSS) {
+      const int d0 = 128 * cc + 8 * n;
+      unsigned wd[8][2];
+      float scl[8];
+#pragma unroll
+      for (int rr = 0; rr < 8; ++rr) {
+        const int row = 8 * g + rr;
+        if (!fp8) {
+          wd[rr][0] = *(const unsigned*)(buf + row * c.RS4 + 64 * (row >> 3) + (d0 >> 1));
+          wd[rr][1] = 0u;
+          scl[rr] = e8m0_to_float(sm.e8[slot][row][d0 >> 5]);
+        } else {
+          v2u v = {0u, 0u};
+          if (row < kWRows) v = *(const v2u*)(buf + row * c.RS8 + d0);
+          wd[rr][0] = v.x;
+          wd[rr][1] = v.y;
+          scl[rr] = 1.0f;
+        }
+      }
+#pragma unroll
+      for (int bb = 0; bb < 4; ++bb) {
+        unsigned cv[8];
+#pragma unroll
+        for (int rr = 0; rr < 8; ++rr) {
+          if (!fp8) {
+            switch (bb) {
+              case 0: cv[rr] = bits_of(__builtin_amdgcn_cvt_scalef32_pk_f16_fp4(wd[rr][0], scl[rr], 0)); break;
+              case 1: cv[rr] = bits_of(__builtin_amdgcn_cvt_scalef32_pk_f16_fp4(wd[rr][0], scl[rr], 1)); break;
+              case 2: cv[rr] = bits_of(__builtin_amdgcn_cvt_scalef32_pk_f16_fp4(wd[rr][0], scl[rr], 2)); break;
+              default: cv[rr] = bits_of(__builtin_amdgcn_cvt_scalef32_pk_f16_fp4(wd[rr][0], scl[rr], 3)); break;
+            }
+          } else {
+            const unsigned src = wd[rr][bb >> 1];
+            cv[rr] = (bb & 1) ? bits_of(__builtin_amdgcn_cvt_scalef32_pk_f16_fp8(src, 1.0f, true))
+                              : bits_of(__builtin_amdgcn_cvt_scalef32_pk_f16_fp8(src, 1.0f, false));
+          }
+        }
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+          const unsigned sel = hh ? 0x07060302u : 0x05040100u;
+          v4u bv;
+          bv.x = __builtin_amdgcn_perm(cv[1], cv[0], sel);
+          bv.y = __builtin_amdgcn_perm(cv[3], cv[2], sel);
+          bv.z = __builtin_amdgcn_perm(cv[5], cv[4], sel);
+          bv.w = __builtin_amdgcn_perm(cv[7], cv[6], sel);
+          const v8h bj = __builtin_bit_cast(v8h, bv);
+#pragma unroll
+          for (int mt = 0; mt < MT; ++mt)
+            o[s][2 * bb + hh][mt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pa[mt], bj, o[s][2 * bb + hh][mt], 0, 0, 0);
+        }
+      }
+    }
+  }
+}
 
 template <int MT, int NS>
 __global__ __launch_bounds__(kAttThreads) void attend_kernel(AttendArgs a, int S, int ngroups, int total) {
   constexpr int kHG = 16 * MT;
   __shared__ AttSmem<MT> sm;
-  extern __shared__ __attribute__((aligned(16))) uint8_t raw[];   // 32 rows of E2M1 codes
+  extern __shared__ __attribute__((aligned(16))) uint8_t dyn[];
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63, g = lane >> 4, n = lane & 15;
+  (void)lane;
 
   // XCD-aware order: consecutive logical blocks (same query) land on one XCD.
   const int nb = gridDim.x;
@@ -64,38 +278,144 @@ __global__ __launch_bounds__(kAttThreads) void attend_kernel(AttendArgs a, int S
   const int grp = (logical / S) % ngroups;
   const int t = logical / (S * ngroups);
 
-  const int D = a.D, W = a.W, k = a.k, Hq = a.Hq;
-  const int NSS = D / 128;                 // 128-dim slices
-  const int RS = D / 2 + 16;               // LDS row stride of the code tile
-  const int b = seq_of_query(a.q_start, a.B, t);
-  const int64_t base = a.seq_start[b];
-  const int p = a.q_pos[t];
-  int lo_win = max(p - W + 1, 0);
-  if (a.swa_clip) lo_win = max(lo_win, a.swa_clip[t]);
-  const int pos0 = a.swa_pos0[b];
-  const int ng = (k + kRows - 1) / kRows;
-  const int ntiles = ng + (W + kRows - 1) / kRows;
-  const int tb = (int)((int64_t)split * ntiles / S);
-  const int te = (int)((int64_t)(split + 1) * ntiles / S);
+  AttCtx c;
+  c.D = a.D;
+  c.W = a.W;
+  c.k = a.k;
+  c.NSS = c.D / 128;
+  c.RS4 = c.D / 2 + 16;
+  c.RS8 = c.D + 16;
+  c.QS = 2 * c.D + 16;
+  c.BUF = (max(kGRows * c.RS4 + 4 * 64, kWRows * c.RS8) + 15) & ~15;
+  c.b = seq_of_query(a.q_start, a.B, t);
+  c.base = a.seq_start[c.b];
+  c.p = a.q_pos[t];
+  c.lo_win = max(c.p - c.W + 1, 0);
+  if (a.swa_clip) c.lo_win = max(c.lo_win, a.swa_clip[t]);
+  c.pos0 = a.swa_pos0[c.b];
+  c.lscale = a.sm_scale * kLog2e;
+  c.ng = (c.k + kGRows - 1) / kGRows;
+  // window tiles overlapping the visible slots [u_lo, u_hi]
+  const int u_lo = max(c.lo_win - c.pos0, 0);
+  const int u_hi = min(c.p - c.pos0, c.W - 1);
+  c.wt0 = u_lo / kWRows;
+  const int nwt = u_lo <= u_hi ? u_hi / kWRows - c.wt0 + 1 : 0;
+  const int ntiles = c.ng + nwt;
+  c.tb = (int)((int64_t)split * ntiles / S);
+  c.te = (int)((int64_t)(split + 1) * ntiles / S);
   const int h0 = grp * kHG;
-  const float lscale = a.sm_scale * kLog2e;
 
-  // q slices for Q.K^T (A operands): dims 128*ss + 32*g + 8*i .. +8, head h0 + 16*mt + n
-  v8bf qa[NS][4][MT];
-#pragma unroll
-  for (int s = 0; s < NS; ++s) {
-    const int ss = wave + 8 * s;
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt) {
-      const uint16_t* qrow = a.q + ((int64_t)t * Hq + h0 + 16 * mt + n) * D;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        v4u v = {0u, 0u, 0u, 0u};
-        if (ss < NSS) v = *(const v4u*)(qrow + 128 * ss + 32 * g + 8 * i);
-        qa[s][i][mt] = __builtin_bit_cast(v8bf, v);
-      }
+  uint8_t* bufs = dyn;                             // two tile buffers
+  uint8_t* qs = dyn + 2 * c.BUF;                   // q slice [kHG][QS]
+  int* sidx = (int*)(qs + kHG * c.QS);
+  c.gx0 = min(c.tb, c.ng) * kGRows;
+  const int gx1 = min(min(c.te, c.ng) * kGRows, c.k);
+  const int nsel = gx1 > c.gx0 ? gx1 - c.gx0 : 0;
+  float* srho = (float*)(sidx + nsel);
+  float* ssig = srho + nsel;
+
+  // ---- prologue: q slice, selected positions and row scales, window scales
+  {
+    const int per_row = c.D / 8;
+    for (int pc = tid; pc < kHG * per_row; pc += kAttThreads) {
+      const int h = pc / per_row, cc = pc - h * per_row;
+      *(v4u*)(qs + h * c.QS + 16 * cc) = *(const v4u*)(a.q + ((int64_t)t * a.Hq + h0 + h) * c.D + 8 * cc);
+    }
+    for (int x = c.gx0 + tid; x < gx1; x += kAttThreads) {
+      const int j = a.idx[(int64_t)t * c.k + x];
+      sidx[x - c.gx0] = j;
+      srho[x - c.gx0] = (j >= 0 && a.kv_rowscale) ? a.kv_rowscale[c.base + j] : 1.0f;
+    }
+    for (int u = tid; u < c.W; u += kAttThreads)
+      ssig[u] = a.swa_scale ? a.swa_scale[(int64_t)c.b * c.W + u] : 1.0f;
+    if (tid < kHG) {
+      sm.m[tid] = -__builtin_inff();
+      sm.l[tid] = 0.0f;
+      sm.alpha[tid] = 1.0f;
     }
   }
+  __syncthreads();
+
+  auto row_pos = [&](int tile, int r) -> int {     // selected position of global row r, or -1
+    const int x = tile * kGRows + r;
+    return x < c.k ? sidx[x - c.gx0] : -1;
+  };
+
+  // Every register is assigned on every path, so no loaded value is ever copied (a copy
+  // would wait for all outstanding loads, the prefetch included).
+  v4u pf[4];
+  unsigned pf_e8;
+  auto prefetch = [&](int tile) {
+    const bool glob = tile < c.ng;
+    const int wt = c.wt0 + (tile - c.ng);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int pc = tid + kAttThreads * u;
+      v4u v = {0u, 0u, 0u, 0u};
+      if (pc < c.D) {                              // a tile is D 16-byte pieces either way
+        if (glob) {
+          const int ppr = c.D / 32;
+          const int r = pc / ppr, cc = pc - r * ppr;
+          const int j = row_pos(tile, r);
+          if (j >= 0) v = *(const v4u*)(a.kv_codes + (c.base + j) * (c.D / 2) + 16 * cc);
+        } else {
+          const int ppr = c.D / 16;
+          const int r = pc / ppr, cc = pc - r * ppr;
+          const int uu = kWRows * wt + r;
+          if (uu < c.W) v = *(const v4u*)(a.swa + ((int64_t)c.b * c.W + uu) * c.D + 16 * cc);
+        }
+      }
+      pf[u] = v;
+    }
+    unsigned e = 0x7F7F7F7Fu;
+    const int epr = c.D / 128;
+    if (glob && tid < kGRows * epr) {
+      const int r = tid / epr, cc = tid - r * epr;
+      const int j = row_pos(tile, r);
+      if (j >= 0) e = *(const unsigned*)(a.kv_e8m0 + (c.base + j) * (c.D / 32) + 4 * cc);
+    }
+    pf_e8 = e;
+  };
+  auto commit = [&](int tile, int slot) {
+    const bool glob = tile < c.ng;
+    uint8_t* buf = bufs + slot * c.BUF;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int pc = tid + kAttThreads * u;
+      if (pc < c.D) {
+        if (glob) {
+          const int ppr = c.D / 32;
+          const int r = pc / ppr, cc = pc - r * ppr;
+          *(v4u*)(buf + r * c.RS4 + 64 * (r >> 3) + 16 * cc) = pf[u];
+        } else {
+          const int ppr = c.D / 16;
+          const int r = pc / ppr, cc = pc - r * ppr;
+          *(v4u*)(buf + r * c.RS8 + 16 * cc) = pf[u];
+        }
+      }
+    }
+    const int epr = c.D / 128;
+    if (glob && tid < kGRows * epr) {
+      const int r = tid / epr, cc = tid - r * epr;
+      *(unsigned*)(&sm.e8[slot][r][4 * cc]) = pf_e8;
+    }
+    if (tid < kGRows) {
+      bool valid;
+      float rs;
+      if (glob) {
+        const int j = row_pos(tile, tid);
+        valid = j >= 0;
+        rs = valid ? srho[tile * kGRows + tid - c.gx0] : 0.0f;
+      } else {
+        const int uu = kWRows * (c.wt0 + tile - c.ng) + tid;
+        const int pos = c.pos0 + uu;
+        valid = tid < kWRows && uu < c.W && pos >= c.lo_win && pos <= c.p;
+        rs = (tid < kWRows && uu < c.W) ? ssig[uu] : 0.0f;
+      }
+      sm.valid[slot][tid] = valid;
+      sm.rscale[slot][tid] = rs;
+    }
+  };
 
   v4f o[NS][8][MT];
 #pragma unroll
@@ -105,243 +425,34 @@ __global__ __launch_bounds__(kAttThreads) void attend_kernel(AttendArgs a, int S
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) o[s][j][mt] = v4f{0.f, 0.f, 0.f, 0.f};
 
-  if (tid < kHG) {
-    sm.m[tid] = -__builtin_inff();
-    sm.l[tid] = 0.0f;
+  // ---- pipeline fill: tile tb committed and scored, tile tb+1 in flight
+  const int tb = c.tb, te = c.te;
+  if (tb < te) {
+    prefetch(tb);
+    commit(tb, 0);
+    if (tb + 1 < te) prefetch(tb + 1);
   }
-  if (tid == 0) sm.rescale = 0;
+  __syncthreads();
+  if (tb < te) qk_tile<MT, NS>(c, sm, bufs, 0, tb >= c.ng, qs, wave, g, n);
+  __syncthreads();
+  if (tb < te) softmax_tile<MT>(c, sm, 0, tid);
 
-  for (int tile = tb; tile < te; ++tile) {
-    const bool is_swa = tile >= ng;
-    __syncthreads();
-    if (tid == 0) sm.any_valid = 0;
-    __syncthreads();
-    if (tid < kRows) {
-      bool valid;
-      int64_t roff;
-      float sc;
-      if (!is_swa) {
-        const int x = tile * kRows + tid;
-        const int j = x < k ? a.idx[(int64_t)t * k + x] : -1;
-        valid = j >= 0;
-        roff = valid ? base + j : -1;
-        sc = valid ? (a.kv_rowscale ? a.kv_rowscale[roff] : 1.0f) : 0.0f;
-      } else {
-        const int u = (tile - ng) * kRows + tid;
-        const int pos = pos0 + u;
-        valid = u < W && pos >= lo_win && pos <= p;
-        roff = u < W ? (int64_t)b * W + u : -1;
-        sc = (u < W && a.swa_scale) ? a.swa_scale[(int64_t)b * W + u] : 1.0f;
-      }
-      sm.valid[tid] = valid;
-      sm.roff[tid] = roff;
-      sm.rscale[tid] = sc;
-      if (valid) atomicOr(&sm.any_valid, 1);
+  for (int i = tb; i < te; ++i) {
+    const int cur = (i - tb) & 1, nxt = cur ^ 1;
+    if (i + 1 < te) {
+      commit(i + 1, nxt);
+      if (i + 2 < te) prefetch(i + 2);
     }
-    __syncthreads();
-    if (!sm.any_valid) continue;
-
-    if (!is_swa) {
-      const int ppr = D / 32;              // 16-byte pieces per row
-      for (int pc = tid; pc < kRows * ppr; pc += kAttThreads) {
-        const int r = pc / ppr, c = pc - r * ppr;
-        const int64_t ro = sm.roff[r];
-        v4u v = {0u, 0u, 0u, 0u};
-        if (ro >= 0) v = *(const v4u*)(a.kv_codes + ro * (D / 2) + 16 * c);
-        *(v4u*)(raw + r * RS + 64 * (r >> 3) + 16 * c) = v;
-      }
-      const int epr = D / 128;             // E8M0 dwords per row
-      for (int pc = tid; pc < kRows * epr; pc += kAttThreads) {
-        const int r = pc / epr, c = pc - r * epr;
-        const int64_t ro = sm.roff[r];
-        unsigned v = 0x7F7F7F7Fu;
-        if (ro >= 0) v = *(const unsigned*)(a.kv_e8m0 + ro * (D / 32) + 4 * c);
-        *(unsigned*)(&sm.e8[r][4 * c]) = v;
-      }
-      __syncthreads();
-    }
-
-    // ---------------- Q.K^T partial over this wave's dim slices
-    v4f sacc[MT][2];
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt) sacc[mt][0] = sacc[mt][1] = v4f{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int s = 0; s < NS; ++s) {
-      const int ss = wave + 8 * s;
-      if (ss < NSS) {
-#pragma unroll
-        for (int nt = 0; nt < 2; ++nt) {
-          const int r = 16 * nt + n;
-          v8bf kb[4];
-          if (!is_swa) {
-            const v4u c = *(const v4u*)(raw + r * RS + 64 * (r >> 3) + 64 * ss + 16 * g);
-            const float scl = e8m0_to_float(sm.e8[r][4 * ss + g]);
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              const unsigned wd = c[i];
-              v4u u4;
-              u4.x = bits_of(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(wd, scl, 0));
-              u4.y = bits_of(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(wd, scl, 1));
-              u4.z = bits_of(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(wd, scl, 2));
-              u4.w = bits_of(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(wd, scl, 3));
-              kb[i] = __builtin_bit_cast(v8bf, u4);
-            }
-          } else {
-            const int64_t ro = sm.roff[r];
-            v4u c0 = {0u, 0u, 0u, 0u}, c1 = {0u, 0u, 0u, 0u};
-            if (ro >= 0) {
-              const uint8_t* src = a.swa + ro * D + 128 * ss + 32 * g;
-              c0 = *(const v4u*)src;
-              c1 = *(const v4u*)(src + 16);
-            }
-            const unsigned wds[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              v4u u4;
-              u4.x = bits_of(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(wds[2 * i], 1.0f, false));
-              u4.y = bits_of(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(wds[2 * i], 1.0f, true));
-              u4.z = bits_of(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(wds[2 * i + 1], 1.0f, false));
-              u4.w = bits_of(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(wds[2 * i + 1], 1.0f, true));
-              kb[i] = __builtin_bit_cast(v8bf, u4);
-            }
-          }
-#pragma unroll
-          for (int i = 0; i < 4; ++i)
-#pragma unroll
-            for (int mt = 0; mt < MT; ++mt)
-              sacc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[s][i][mt], kb[i], sacc[mt][nt], 0, 0, 0);
-        }
-      }
-    }
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-      for (int nt = 0; nt < 2; ++nt)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) sm.red[wave][16 * mt + 4 * g + r][16 * nt + n] = sacc[mt][nt][r];
-    __syncthreads();
-
-    // ---------------- online softmax (base 2)
-    {
-      constexpr int TPH = 32 / MT;          // threads per head
-      const int h = tid / TPH;
-      const int x0 = (tid % TPH) * MT;
-      float sv[MT];
-      float tmax = -__builtin_inff();
-#pragma unroll
-      for (int e = 0; e < MT; ++e) {
-        const int x = x0 + e;
-        float acc = 0.0f;
-#pragma unroll
-        for (int w8 = 0; w8 < 8; ++w8) acc += sm.red[w8][h][x];
-        sv[e] = sm.valid[x] ? acc * lscale * sm.rscale[x] : -__builtin_inff();
-        tmax = fmaxf(tmax, sv[e]);
-      }
-#pragma unroll
-      for (int o2 = 1; o2 < TPH; o2 <<= 1) tmax = fmaxf(tmax, __shfl_xor(tmax, o2));
-      const float m_old = sm.m[h];
-      const float m_new = fmaxf(m_old, tmax);
-      const bool none = m_new == -__builtin_inff();
-      const float alpha = none ? 1.0f : exp2f(m_old - m_new);
-      float psum = 0.0f;
-#pragma unroll
-      for (int e = 0; e < MT; ++e) {
-        const int x = x0 + e;
-        const float pe = (none || !sm.valid[x]) ? 0.0f : exp2f(sv[e] - m_new);
-        psum += pe;
-        sm.P[h][x] = (_Float16)(pe * sm.rscale[x]);
-      }
-#pragma unroll
-      for (int o2 = 1; o2 < TPH; o2 <<= 1) psum += __shfl_xor(psum, o2);
-      __syncthreads();   // every thread has read m/l before they are updated
-      if (tid % TPH == 0) {
-        sm.m[h] = m_new;
-        sm.l[h] = sm.l[h] * alpha + psum;
-        sm.alpha[h] = alpha;
-        if (alpha != 1.0f) sm.rescale = 1;
-      }
-    }
-    __syncthreads();
-
-    // ---------------- P.V into this wave's output dim slices
-    if (sm.rescale) {
-#pragma unroll
-      for (int mt = 0; mt < MT; ++mt) {
-        float al[4];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) al[r] = sm.alpha[16 * mt + 4 * g + r];
-#pragma unroll
-        for (int s = 0; s < NS; ++s)
-#pragma unroll
-          for (int j = 0; j < 8; ++j)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) o[s][j][mt][r] *= al[r];
-      }
-    }
-    v8h pa[MT];
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt) pa[mt] = *(const v8h*)(&sm.P[16 * mt + n][8 * g]);
-#pragma unroll
-    for (int s = 0; s < NS; ++s) {
-      const int c = wave + 8 * s;
-      if (c < NSS) {
-        const int d0 = 128 * c + 8 * n;
-        unsigned wd[8][2];
-        float scl[8];
-#pragma unroll
-        for (int rr = 0; rr < 8; ++rr) {
-          const int row = 8 * g + rr;
-          if (!is_swa) {
-            wd[rr][0] = *(const unsigned*)(raw + row * RS + 64 * (row >> 3) + (d0 >> 1));
-            scl[rr] = e8m0_to_float(sm.e8[row][d0 >> 5]);
-          } else {
-            const int64_t ro = sm.roff[row];
-            v2u v = {0u, 0u};
-            if (ro >= 0) v = *(const v2u*)(a.swa + ro * D + d0);
-            wd[rr][0] = v.x;
-            wd[rr][1] = v.y;
-          }
-        }
-#pragma unroll
-        for (int bb = 0; bb < 4; ++bb) {
-          unsigned cv[8];
-#pragma unroll
-          for (int rr = 0; rr < 8; ++rr) {
-            if (!is_swa) {
-              switch (bb) {
-                case 0: cv[rr] = bits_of(__builtin_amdgcn_cvt_scalef32_pk_f16_fp4(wd[rr][0], scl[rr], 0)); break;
-                case 1: cv[rr] = bits_of(__builtin_amdgcn_cvt_scalef32_pk_f16_fp4(wd[rr][0], scl[rr], 1)); break;
-                case 2: cv[rr] = bits_of(__builtin_amdgcn_cvt_scalef32_pk_f16_fp4(wd[rr][0], scl[rr], 2)); break;
-                default: cv[rr] = bits_of(__builtin_amdgcn_cvt_scalef32_pk_f16_fp4(wd[rr][0], scl[rr], 3)); break;
-              }
-            } else {
-              const unsigned src = wd[rr][bb >> 1];
-              cv[rr] = (bb & 1) ? bits_of(__builtin_amdgcn_cvt_scalef32_pk_f16_fp8(src, 1.0f, true))
-                                : bits_of(__builtin_amdgcn_cvt_scalef32_pk_f16_fp8(src, 1.0f, false));
-            }
-          }
-#pragma unroll
-          for (int hh = 0; hh < 2; ++hh) {
-            const unsigned sel = hh ? 0x07060302u : 0x05040100u;
-            v4u bv;
-            bv.x = __builtin_amdgcn_perm(cv[1], cv[0], sel);
-            bv.y = __builtin_amdgcn_perm(cv[3], cv[2], sel);
-            bv.z = __builtin_amdgcn_perm(cv[5], cv[4], sel);
-            bv.w = __builtin_amdgcn_perm(cv[7], cv[6], sel);
-            const v8h bj = __builtin_bit_cast(v8h, bv);
-#pragma unroll
-            for (int mt = 0; mt < MT; ++mt)
-              o[s][2 * bb + hh][mt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pa[mt], bj, o[s][2 * bb + hh][mt], 0, 0, 0);
-          }
-        }
-      }
-    }
-    __syncthreads();
-    if (tid == 0) sm.rescale = 0;
+    __syncthreads();                               // P(i), tile i+1 and its row flags published
+    pv_tile<MT, NS>(c, sm, bufs + cur * c.BUF, cur, i >= c.ng, o, wave, g, n);
+    if (i + 1 < te) qk_tile<MT, NS>(c, sm, bufs + nxt * c.BUF, nxt, i + 1 >= c.ng, qs, wave, g, n);
+    __syncthreads();                               // partial logits of tile i+1 published
+    if (i + 1 < te) softmax_tile<MT>(c, sm, nxt, tid);
   }
   __syncthreads();
 
-  // ---------------- epilogue
+  // ---- epilogue
+  const int cw0 = (wave + 3) & 7;
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) {
 #pragma unroll
@@ -350,13 +461,13 @@ __global__ __launch_bounds__(kAttThreads) void attend_kernel(AttendArgs a, int S
       const int hg = h0 + hl;
       const float l = sm.l[hl];
       const float inv = (S == 1) ? (l > 0.0f ? 1.0f / l : 0.0f) : 1.0f;
-      float* dst = (S == 1) ? a.out + ((int64_t)t * Hq + hg) * D
-                            : (float*)a.ws + (((int64_t)split * a.T + t) * Hq + hg) * D;
+      float* dst = (S == 1) ? a.out + ((int64_t)t * a.Hq + hg) * c.D
+                            : (float*)a.ws + (((int64_t)split * a.T + t) * a.Hq + hg) * c.D;
 #pragma unroll
       for (int s = 0; s < NS; ++s) {
-        const int c = wave + 8 * s;
-        if (c < NSS) {
-          const int d0 = 128 * c + 8 * n;
+        const int cc = cw0 + 8 * s;
+        if (cc < c.NSS) {
+          const int d0 = 128 * cc + 8 * n;
           v4f lo = {o[s][0][mt][r] * inv, o[s][1][mt][r] * inv, o[s][2][mt][r] * inv, o[s][3][mt][r] * inv};
           v4f hi = {o[s][4][mt][r] * inv, o[s][5][mt][r] * inv, o[s][6][mt][r] * inv, o[s][7][mt][r] * inv};
           *(v4f*)(dst + d0) = lo;
@@ -369,57 +480,82 @@ __global__ __launch_bounds__(kAttThreads) void attend_kernel(AttendArgs a, int S
     const int hg = h0 + tid;
     const float m = sm.m[tid], l = sm.l[tid];
     if (S == 1) {
-      if (a.lse) a.lse[(int64_t)t * Hq + hg] = l > 0.0f ? (m + log2f(l)) * kLn2 : -__builtin_inff();
+      if (a.lse) a.lse[(int64_t)t * a.Hq + hg] = l > 0.0f ? (m + log2f(l)) * kLn2 : -__builtin_inff();
     } else {
-      float* ml = (float*)a.ws + (size_t)S * a.T * Hq * D;
-      const int64_t i = ((int64_t)split * a.T + t) * Hq + hg;
-      ml[2 * i] = m;
-      ml[2 * i + 1] = l;
+      float* ml = (float*)a.ws + (size_t)S * a.T * a.Hq * c.D;
+      const int64_t ii = ((int64_t)split * a.T + t) * a.Hq + hg;
+      ml[2 * ii] = m;
+      ml[2 * ii + 1] = l;
     }
   }
 }
 
+// out[t,h,d] = sum_s 2^(m_s - M) O_s[d] / sum_s 2^(m_s - M) l_s ; one thread per output dim.
 __global__ __launch_bounds__(256) void attend_merge_kernel(AttendArgs a, int S) {
-  const int th = blockIdx.x;
+  __shared__ float wts[64];
+  __shared__ float sL, sM;
+  const int th = blockIdx.y;
   const int t = th / a.Hq, h = th % a.Hq;
   const int D = a.D;
   const float* opart = (const float*)a.ws;
   const float* ml = opart + (size_t)S * a.T * a.Hq * D;
-  float M = -__builtin_inff();
-  for (int s = 0; s < S; ++s) M = fmaxf(M, ml[2 * (((int64_t)s * a.T + t) * a.Hq + h)]);
-  float L = 0.0f;
-  float wts[32];
-  for (int s = 0; s < S; ++s) {
-    const int64_t i = ((int64_t)s * a.T + t) * a.Hq + h;
-    const float ms = ml[2 * i], ls = ml[2 * i + 1];
+  const size_t sstride = (size_t)a.T * a.Hq * D;
+  if (threadIdx.x < 64) {
+    const int s = threadIdx.x;
+    float ms = -__builtin_inff(), ls = 0.0f;
+    if (s < S) {
+      const int64_t i = ((int64_t)s * a.T + t) * a.Hq + h;
+      ms = ml[2 * i];
+      ls = ml[2 * i + 1];
+    }
+    float M = ms;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) M = fmaxf(M, __shfl_xor(M, o));
     const float wv = (M == -__builtin_inff() || ls == 0.0f) ? 0.0f : exp2f(ms - M);
+    float L = wv * ls;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) L += __shfl_xor(L, o);
     wts[s] = wv;
-    L += wv * ls;
+    if (s == 0) {
+      sL = L;
+      sM = M;
+    }
   }
+  __syncthreads();
+  const float L = sL;
   const float inv = L > 0.0f ? 1.0f / L : 0.0f;
-  float* dst = a.out + ((int64_t)t * a.Hq + h) * D;
-  for (int d = threadIdx.x; d < D; d += 256) {
+  const int d = blockIdx.x * 256 + threadIdx.x;
+  if (d < D) {
+    const float* src = opart + ((int64_t)t * a.Hq + h) * D + d;
     float acc = 0.0f;
-    for (int s = 0; s < S; ++s) acc += wts[s] * opart[(((int64_t)s * a.T + t) * a.Hq + h) * D + d];
-    dst[d] = acc * inv;
+#pragma unroll 8
+    for (int s = 0; s < S; ++s) acc += wts[s] * src[s * sstride];
+    a.out[((int64_t)t * a.Hq + h) * D + d] = acc * inv;
   }
-  if (threadIdx.x == 0 && a.lse) a.lse[(int64_t)t * a.Hq + h] = L > 0.0f ? (M + log2f(L)) * kLn2 : -__builtin_inff();
+  if (blockIdx.x == 0 && threadIdx.x == 0 && a.lse)
+    a.lse[(int64_t)t * a.Hq + h] = L > 0.0f ? (sM + log2f(L)) * kLn2 : -__builtin_inff();
 }
 
-// 32 heads per workgroup when the q slices and output accumulators fit the register
-// file without spilling (D <= 1024); 16 heads otherwise.
+// 32 heads per workgroup when the output accumulators fit the register file without
+// spilling (D <= 1024); 16 heads otherwise.
 static int head_tiles(int Hq, int D) { return (Hq % 32 == 0 && D <= 1024) ? 2 : 1; }
+
+static int max_tiles(int32_t k, int32_t W) {
+  return (k + kGRows - 1) / kGRows + (W + kWRows - 1) / kWRows + 1;
+}
 
 int attend_splits(int32_t T, int32_t k, int32_t W, int32_t Hq, int32_t D) {
   const int MT = head_tiles(Hq, D);
   const int ngroups = Hq / (16 * MT);
-  const int ntiles = (k + kRows - 1) / kRows + (W + kRows - 1) / kRows;
+  const int ntiles = max_tiles(k, W);
   const int64_t base = (int64_t)T * ngroups;
   if (base <= 0) return 1;
+  // enough workgroups to cover the chip twice, but at least 4 tiles per split so the
+  // prefetch pipeline has work to overlap, and at most 16 partials per output
   int S = 1;
   if (base < 512) S = (int)((512 + base - 1) / base);
-  S = std::min(S, std::max(1, ntiles / 2));
-  S = std::min(S, 32);
+  S = std::min(S, std::max(1, ntiles / 4));
+  S = std::min(S, 16);
   return std::max(S, 1);
 }
 
@@ -435,11 +571,23 @@ static hipError_t launch_attend_t(const AttendArgs& a, hipStream_t s) {
   const int ngroups = a.Hq / (16 * MT);
   const int total = a.T * ngroups * S;
   const int nb = (total + 7) / 8 * 8;
-  const size_t raw_bytes = (size_t)kRows * (a.D / 2 + 16) + 4 * 64;
-  hipLaunchKernelGGL((attend_kernel<MT, NS>), dim3(nb), dim3(kAttThreads), raw_bytes, s, a, S, ngroups, total);
+  const int split_tiles = (max_tiles(a.k, a.W) + S - 1) / S + 1;
+  const size_t buf = (std::max<size_t>((size_t)kGRows * (a.D / 2 + 16) + 4 * 64,
+                                       (size_t)kWRows * (a.D + 16)) + 15) & ~(size_t)15;
+  const size_t dyn = 2 * buf + (size_t)16 * MT * (2 * a.D + 16) + (size_t)split_tiles * kGRows * 8 +
+                     (size_t)a.W * 4;
+  static bool attr_set[2][2] = {{false, false}, {false, false}};
+  if (!attr_set[MT - 1][NS - 1]) {
+    hipError_t e = hipFuncSetAttribute((const void*)attend_kernel<MT, NS>,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize,
+                                       160 * 1024 - (int)sizeof(AttSmem<MT>));
+    if (e != hipSuccess) return e;
+    attr_set[MT - 1][NS - 1] = true;
+  }
+  hipLaunchKernelGGL((attend_kernel<MT, NS>), dim3(nb), dim3(kAttThreads), dyn, s, a, S, ngroups, total);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || S == 1) return e;
-  hipLaunchKernelGGL(attend_merge_kernel, dim3(a.T * a.Hq), dim3(256), 0, s, a, S);
+  hipLaunchKernelGGL(attend_merge_kernel, dim3((a.D + 255) / 256, a.T * a.Hq), dim3(256), 0, s, a, S);
   return hipGetLastError();
 }
 

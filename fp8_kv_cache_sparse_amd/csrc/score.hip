@@ -72,13 +72,13 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel(ScoreArgs a) {
     if (col0 > s_pmax) return;
   }
 
-  // ---- this wave's keys (B operands), loaded once, kept as E4M3 bytes ----
+  // ---- this wave's keys (B operands), loaded and converted to bf16 once ----
   // Lane (g, n) holds position n of the tile and key bytes [g*Di/4, (g+1)*Di/4);
-  // K-step s uses bytes g*Di/4 + 8s .. +8 (converted to bf16 at use).  q uses the
-  // same byte->k assignment, so the sum over k is the full dot product.
+  // K-step s uses bytes g*Di/4 + 8s .. +8.  q uses the same byte->k assignment, so
+  // the sum over k is the full dot product.
   constexpr int NKS_MAX = 4;
   const int nks = Di / 32;
-  unsigned kraw[TPW][8];
+  v8bf kb[TPW][NKS_MAX];
   float kap[TPW];
   int kpos[TPW];
 #pragma unroll
@@ -101,8 +101,9 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel(ScoreArgs a) {
       lo = *(const v4u*)row;
       if (Di == 128) hi = *(const v4u*)(row + 16);
     }
-    kraw[i][0] = lo.x; kraw[i][1] = lo.y; kraw[i][2] = lo.z; kraw[i][3] = lo.w;
-    kraw[i][4] = hi.x; kraw[i][5] = hi.y; kraw[i][6] = hi.z; kraw[i][7] = hi.w;
+    const unsigned wds[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+#pragma unroll
+    for (int s2 = 0; s2 < NKS_MAX; ++s2) kb[i][s2] = fp8x8_to_bf16(wds[2 * s2], wds[2 * s2 + 1]);
     kap[i] = (ok && a.k_scale) ? a.k_scale[base + pos] : 1.0f;
   }
 
@@ -123,7 +124,9 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel(ScoreArgs a) {
       if (tid < 16 * MT) w_lds[tid] = tid < Hi ? a.w[(int64_t)t * Hi + tid] : 0.0f;
     }
     __syncthreads();
-    // heads outer, positions inner: only one 16-head slice of q is live at a time
+    // heads outer, positions inner: one 16-head slice of q is live at a time; the keys
+    // were converted once per block.  kappa > 0 commutes with the ReLU, so it scales the
+    // head sum instead of every term.
     float sum[TPW];
 #pragma unroll
     for (int i = 0; i < TPW; ++i) sum[i] = 0.0f;
@@ -149,11 +152,9 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel(ScoreArgs a) {
         v4f acc = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
         for (int s2 = 0; s2 < NKS_MAX; ++s2)
-          if (s2 < nks)
-            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                qa[s2], fp8x8_to_bf16(kraw[i][2 * s2], kraw[i][2 * s2 + 1]), acc, 0, 0, 0);
+          if (s2 < nks) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[s2], kb[i][s2], acc, 0, 0, 0);
 #pragma unroll
-        for (int r = 0; r < 4; ++r) sum[i] += wr[r] * fmaxf(acc[r] * kap[i], 0.0f);
+        for (int r = 0; r < 4; ++r) sum[i] += wr[r] * fmaxf(acc[r], 0.0f);
       }
     }
 #pragma unroll
@@ -163,6 +164,7 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel(ScoreArgs a) {
       float sm = sum[i];
       sm += __shfl_xor(sm, 16);
       sm += __shfl_xor(sm, 32);
+      sm *= kap[i];
       if (g == 0) {
         const int col = colbase + n;
         if (CAND) {

@@ -1,27 +1,31 @@
 // Top-k position selection on gfx950 (vLLM blog "DeepSeek-V4.1-Flash sur vLLM",
 // sections TL;DR and "Kernels": the DeepSelect top-k over the indexer scores).
 //
-// Order: score descending, ties to the lower position.  Every candidate is given
-// the 64-bit composite c = (key(score) << 32) | (0xFFFFFFFF - position), where
-// key() is the order-preserving float->uint32 map; composites are unique, so the
-// k largest composites are exactly the wanted set and the selection is a radix
-// select on c (11-bit digits, most significant first).
+// Order: score descending, ties to the lower position.  Column i of a query's
+// score row stands for position i (dense) or cand[i] (candidate lists are strictly
+// ascending), so "lower position" = "lower column".  Every column gets the 64-bit
+// composite c = (key(score) << 32) | (0xFFFFFFFF - column), key() being the
+// order-preserving float->uint32 map; composites are unique, so the k largest
+// composites are exactly the wanted set, found by radix select (11-bit digits,
+// most significant first).  The selection is recorded as a bitmap over columns
+// and read out in column order, which yields ascending positions without a sort.
 //
 // Short rows (<= kSmallN columns): one 1024-thread workgroup per query keeps the
 // keys in LDS and runs the whole select there.
 // Long rows: (1) many workgroups per query build a 4096-bin histogram of the top
 // 12 key bits; the last one to finish finds the bin d1 holding the k-th entry;
-// (2) many workgroups per query copy every entry above d1 to the output set and
-// every entry in d1 to a candidate buffer; (3) one workgroup per query finishes
-// the select inside d1 from LDS (or, if d1 is too full, by re-reading the row),
-// sorts the k positions and writes them.
+// (2) many workgroups per query write the bitmap words of their columns (every
+// entry above d1 selected) with wave ballots and append the entries of bin d1 to
+// a candidate list; (3) one workgroup per query finishes the select inside d1
+// (from LDS, or by re-reading the row when d1 holds more than kCap entries),
+// sets those bits, and reads the bitmap out in order.
 #include "common.h"
 
 namespace smqa {
 
 constexpr int kSmallN = 16384;
-constexpr int kChunk = 4096;
-constexpr int kCap = 12288;          // candidate-buffer capacity per query (entries of bin d1)
+constexpr int kChunk = 4096;          // columns per workgroup in the long-row kernels
+constexpr int kCap = 12288;           // candidate-list capacity per query (entries of bin d1)
 constexpr int kHistBins = 4096;
 
 struct TopkState {
@@ -30,47 +34,50 @@ struct TopkState {
   int cnt1;      // entries in bin d1
   int nvalid;    // entries in the scored set
   int done;      // finished histogram workgroups
-  int nsel;      // entries written to sel
-  int ncand;     // entries written to cand
-  int pad;
+  int ncand;     // entries appended to cand
+  int pad[2];
 };
 
 struct TopkWs {
   unsigned* hist;    // [T][4096]
   TopkState* st;     // [T]
-  int* sel;          // [T][k]
-  uint2* cand;       // [T][kCap]  {key, position}
+  uint2* cand;       // [T][kCap]  {key, column}
+  unsigned* bits;    // [T][bw]    selection bitmap over columns
+  int bw;            // bitmap words per query
 };
 
-static TopkWs carve(void* ws, int T, int k) {
+static int bitmap_words(int max_ctx) { return (max_ctx + kChunk - 1) / kChunk * (kChunk / 32); }
+
+static TopkWs carve(void* ws, int T, int max_ctx) {
   TopkWs w;
   char* p = (char*)ws;
   w.hist = (unsigned*)p;
   p += align_up((size_t)T * kHistBins * 4, 256);
   w.st = (TopkState*)p;
   p += align_up((size_t)T * sizeof(TopkState), 256);
-  w.sel = (int*)p;
-  p += align_up((size_t)T * k * 4, 256);
   w.cand = (uint2*)p;
+  p += align_up((size_t)T * kCap * 8, 256);
+  w.bits = (unsigned*)p;
+  w.bw = bitmap_words(max_ctx);
   return w;
 }
 
 size_t topk_workspace_bytes(int32_t T, int32_t max_ctx, int32_t k) {
+  (void)k;
   if (max_ctx <= kSmallN || T == 0) return 0;
   return align_up((size_t)T * kHistBins * 4, 256) + align_up((size_t)T * sizeof(TopkState), 256) +
-         align_up((size_t)T * k * 4, 256) + align_up((size_t)T * kCap * 8, 256);
+         align_up((size_t)T * kCap * 8, 256) + align_up((size_t)T * bitmap_words(max_ctx) * 4, 256);
 }
 
 // ------------------------------------------------------------------ helpers
 
-__device__ __forceinline__ uint64_t composite(unsigned key, int pos) {
-  return ((uint64_t)key << 32) | (uint64_t)(0xFFFFFFFFu - (unsigned)pos);
+__device__ __forceinline__ uint64_t composite(unsigned key, int col) {
+  return ((uint64_t)key << 32) | (uint64_t)(0xFFFFFFFFu - (unsigned)col);
 }
 
-__device__ __forceinline__ int ncols_of(const TopkArgs& a, int t, int* b_out) {
-  const int b = seq_of_query(a.q_start, a.B, t);
-  *b_out = b;
+__device__ __forceinline__ int ncols_of(const TopkArgs& a, int t) {
   if (a.cand) return a.n_cand;
+  const int b = seq_of_query(a.q_start, a.B, t);
   const int len = (int)(a.seq_start[b + 1] - a.seq_start[b]);
   return max(0, min(min(a.q_pos[t], len - 1) + 1, a.max_ctx));
 }
@@ -104,7 +111,8 @@ __device__ int block_exclusive_scan(int v, int* lds, int* total) {
 }
 
 // Find the digit d with count(digits > d) < need <= count(digits >= d) in hist[nbins].
-// Thread t owns bins nbins-1-t*per .. descending.  Result in sh[0] (digit), sh[1] (above).
+// Thread t owns bins nbins-1-t*per .. descending.  Result: sh[0] = digit (-1 if none),
+// sh[1] = count above it.
 template <int NT>
 __device__ void block_find_digit(const unsigned* hist, int nbins, int need, int* scan_lds, int* sh) {
   const int per = nbins / NT;
@@ -125,11 +133,51 @@ __device__ void block_find_digit(const unsigned* hist, int nbins, int need, int*
   __syncthreads();
 }
 
-// Radix select on composites from `src` (entries whose top `nbits` composite bits
-// equal those of `prefix`): returns tau such that exactly `need` of them have c >= tau.
+// Radix select on composites from `src` restricted to entries whose top `nbits`
+// bits equal those of `prefix`: returns tau such that exactly `need` of them have
+// c >= tau.
 template <int NT, class Src>
 __device__ uint64_t radix_refine(const Src& src, int n, int need, uint64_t prefix, int nbits,
                                  unsigned* hist, int* scan_lds, int* sh) {
+  // Leading bits shared by every matching entry carry no information: find them from
+  // the min and max composite and start the digits below them.
+  {
+    uint64_t lo = ~0ull, hi = 0ull;
+    for (int i = threadIdx.x; i < n; i += NT) {
+      uint64_t c;
+      if (!src.get(i, &c)) continue;
+      if (nbits > 0 && (c >> (64 - nbits)) != (prefix >> (64 - nbits))) continue;
+      lo = c < lo ? c : lo;
+      hi = c > hi ? c : hi;
+    }
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const uint64_t l2 = __shfl_xor(lo, o), h2 = __shfl_xor(hi, o);
+      lo = l2 < lo ? l2 : lo;
+      hi = h2 > hi ? h2 : hi;
+    }
+    uint64_t* red = (uint64_t*)hist;      // hist is free here
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    if (lane == 0) {
+      red[2 * wave] = lo;
+      red[2 * wave + 1] = hi;
+    }
+    __syncthreads();
+    lo = ~0ull;
+    hi = 0ull;
+    for (int i = 0; i < NT / 64; ++i) {
+      lo = red[2 * i] < lo ? red[2 * i] : lo;
+      hi = red[2 * i + 1] > hi ? red[2 * i + 1] : hi;
+    }
+    __syncthreads();
+    if (lo <= hi) {
+      const int common = lo == hi ? 64 : __clzll((long long)(lo ^ hi));
+      if (common > nbits) {
+        prefix = common == 64 ? lo : (lo >> (64 - common)) << (64 - common);
+        nbits = common;
+      }
+    }
+  }
   while (nbits < 64) {
     const int dbits = min(11, 64 - nbits);
     const int shift = 64 - nbits - dbits;
@@ -157,7 +205,7 @@ __device__ uint64_t radix_refine(const Src& src, int n, int need, uint64_t prefi
   return prefix;
 }
 
-// Wave-aggregated append: returns the slot for lanes with flag set.
+// Wave-aggregated append to an LDS or global counter: returns this lane's slot.
 __device__ __forceinline__ int wave_append(int* counter, bool flag) {
   const unsigned long long m = __ballot(flag);
   if (m == 0) return -1;
@@ -169,91 +217,92 @@ __device__ __forceinline__ int wave_append(int* counter, bool flag) {
   return base + __popcll(m & ((1ull << lane) - 1));
 }
 
-// Sort n_pad (power of two) ints ascending in LDS.
-template <int NT>
-__device__ void bitonic_sort(int* arr, int n_pad) {
-  for (int size = 2; size <= n_pad; size <<= 1) {
-    for (int stride = size >> 1; stride > 0; stride >>= 1) {
-      for (int i = threadIdx.x; i < (n_pad >> 1); i += NT) {
-        const int lo = 2 * stride * (i / stride) + (i % stride);
-        const int hi = lo + stride;
-        const bool asc = (lo & size) == 0;
-        const int x = arr[lo], y = arr[hi];
-        if ((x > y) == asc) {
-          arr[lo] = y;
-          arr[hi] = x;
-        }
-      }
-      __syncthreads();
+// Read the selection bitmap (nwords words, bit c = column c) out in column order:
+// dst[i] = position of the i-th selected column, then -1 up to k.
+template <int NT, bool ATOMIC_READ>
+__device__ void write_selection(const TopkArgs& a, int t, const unsigned* bits, int nwords,
+                                int32_t* dst, int* scan_lds) {
+  const int per = (nwords + NT - 1) / NT;
+  const int w0 = threadIdx.x * per, w1 = min(w0 + per, nwords);
+  auto word = [&](int i) -> unsigned {
+    if (ATOMIC_READ) return __hip_atomic_load(bits + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return bits[i];
+  };
+  int cnt = 0;
+  for (int i = w0; i < w1; ++i) cnt += __popc(word(i));
+  int total;
+  int off = block_exclusive_scan<NT>(cnt, scan_lds, &total);
+  for (int i = w0; i < w1; ++i) {
+    unsigned m = word(i);
+    while (m) {
+      const int bit = __ffs(m) - 1;
+      m &= m - 1;
+      if (off < a.k) dst[off] = pos_of(a, t, 32 * i + bit);
+      ++off;
     }
   }
-}
-
-__device__ __forceinline__ int pow2_at_least(int x) {
-  int p = 1;
-  while (p < x) p <<= 1;
-  return p;
-}
-
-template <int NT>
-__device__ void sort_and_write(int* outl, int cnt, int k, int32_t* dst) {
-  const int P = pow2_at_least(max(k, 2));
-  for (int i = cnt + threadIdx.x; i < P; i += NT) outl[i] = 0x7FFFFFFF;
-  __syncthreads();
-  bitonic_sort<NT>(outl, P);
-  for (int i = threadIdx.x; i < k; i += NT) dst[i] = i < cnt ? outl[i] : -1;
+  for (int i = min(total, a.k) + threadIdx.x; i < a.k; i += NT) dst[i] = -1;
 }
 
 // ------------------------------------------------------------------ short rows
 
 struct LdsKeySrc {
   const unsigned* keys;
-  const TopkArgs* a;
-  int t;
   __device__ bool get(int i, uint64_t* c) const {
     const unsigned key = keys[i];
     if (key == 0u) return false;
-    *c = composite(key, pos_of(*a, t, i));
+    *c = composite(key, i);
     return true;
   }
 };
 
 __global__ __launch_bounds__(1024) void topk_small_kernel(TopkArgs a) {
   constexpr int NT = 1024;
+  constexpr int PER = kSmallN / NT;
   __shared__ unsigned keys[kSmallN];
-  __shared__ unsigned hist[2048];
-  __shared__ int outl[4096];
+  __shared__ unsigned bits[kSmallN / 32];
+  __shared__ __attribute__((aligned(16))) unsigned hist[2048];
   __shared__ int scan_lds[NT / 64];
   __shared__ int sh[4];
   const int t = blockIdx.x;
-  int b;
-  const int ncols = ncols_of(a, t, &b);
+  const int ncols = ncols_of(a, t);
+  const float* row = a.scores + (int64_t)t * a.ld;
   if (threadIdx.x == 0) sh[2] = 0;
-  __syncthreads();
+  float v[PER];
+#pragma unroll
+  for (int u = 0; u < PER; ++u) {
+    const int i = threadIdx.x + NT * u;
+    v[u] = i < ncols ? row[i] : -__builtin_inff();
+  }
   int cnt = 0;
-  for (int i = threadIdx.x; i < ncols; i += NT) {
-    const unsigned key = score_key(a.scores[(int64_t)t * a.ld + i]);
-    keys[i] = key;
+#pragma unroll
+  for (int u = 0; u < PER; ++u) {
+    const unsigned key = score_key(v[u]);
+    keys[threadIdx.x + NT * u] = key;
     cnt += key != 0u;
   }
+  __syncthreads();
   if (cnt) atomicAdd(&sh[2], cnt);
   __syncthreads();
   const int nvalid = sh[2];
-  if (threadIdx.x == 0) sh[3] = 0;
-  __syncthreads();
-  LdsKeySrc src{keys, &a, t};
+  LdsKeySrc src{keys};
   uint64_t tau = 0;
   const bool all = nvalid <= a.k;
   if (!all) tau = radix_refine<NT>(src, ncols, a.k, 0ull, 0, hist, scan_lds, sh);
-  for (int i0 = 0; i0 < ncols; i0 += NT) {
-    const int i = i0 + threadIdx.x;
+  // bitmap: each wave covers 64 consecutive columns per step
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  for (int c0 = 64 * wave; c0 < kSmallN; c0 += 64 * (NT / 64)) {
+    const int i = c0 + lane;
     uint64_t c = 0;
-    const bool v = i < ncols && src.get(i, &c) && (all || c >= tau);
-    const int slot = wave_append(&sh[3], v);
-    if (v && slot < 4096) outl[slot] = pos_of(a, t, i);
+    const bool sel = i < ncols && src.get(i, &c) && (all || c >= tau);
+    const unsigned long long m = __ballot(sel);
+    if (lane == 0) {
+      bits[c0 / 32] = (unsigned)m;
+      bits[c0 / 32 + 1] = (unsigned)(m >> 32);
+    }
   }
   __syncthreads();
-  sort_and_write<NT>(outl, min(sh[3], a.k), a.k, a.idx + (int64_t)t * a.k);
+  write_selection<NT, false>(a, t, bits, (ncols + 31) / 32, a.idx + (int64_t)t * a.k, scan_lds);
 }
 
 // ------------------------------------------------------------------ long rows
@@ -264,24 +313,33 @@ __global__ void topk_zero_kernel(unsigned* p, size_t n_words) {
     p[i] = 0u;
 }
 
-__global__ __launch_bounds__(256) void topk_hist_kernel(TopkArgs a, TopkWs w) {
-  constexpr int NT = 256;
+constexpr int kLongThreads = 256;
+constexpr int kPerThread = kChunk / kLongThreads;
+
+__global__ __launch_bounds__(kLongThreads) void topk_hist_kernel(TopkArgs a, TopkWs w) {
+  constexpr int NT = kLongThreads;
   __shared__ unsigned hist[kHistBins];
   __shared__ int scan_lds[NT / 64];
   __shared__ int sh[4];
   const int t = blockIdx.y;
-  int b;
-  const int ncols = ncols_of(a, t, &b);
+  const int ncols = ncols_of(a, t);
   const int nch = (ncols + kChunk - 1) / kChunk;
   if ((int)blockIdx.x >= nch) return;
+  const int c0 = blockIdx.x * kChunk;
+  const float* row = a.scores + (int64_t)t * a.ld;
+  float v[kPerThread];
+#pragma unroll
+  for (int u = 0; u < kPerThread; ++u) {
+    const int i = c0 + threadIdx.x + NT * u;
+    v[u] = i < ncols ? row[i] : -__builtin_inff();
+  }
   for (int i = threadIdx.x; i < kHistBins; i += NT) hist[i] = 0;
   if (threadIdx.x == 0) sh[2] = 0;
   __syncthreads();
-  const int c0 = blockIdx.x * kChunk, c1 = min(c0 + kChunk, ncols);
-  const float* row = a.scores + (int64_t)t * a.ld;
   int cnt = 0;
-  for (int i = c0 + threadIdx.x; i < c1; i += NT) {
-    const unsigned key = score_key(row[i]);
+#pragma unroll
+  for (int u = 0; u < kPerThread; ++u) {
+    const unsigned key = score_key(v[u]);
     if (key) {
       atomicAdd(&hist[key >> 20], 1u);
       ++cnt;
@@ -293,13 +351,14 @@ __global__ __launch_bounds__(256) void topk_hist_kernel(TopkArgs a, TopkWs w) {
   for (int i = threadIdx.x; i < kHistBins; i += NT)
     if (hist[i]) atomicAdd(&gh[i], hist[i]);
   if (threadIdx.x == 0 && sh[2]) atomicAdd(&w.st[t].nvalid, sh[2]);
-  __threadfence();
+  // Device-scope atomics are performed at the memory side, coherent across XCDs; waiting
+  // for their completion orders them before the ticket without an L2 writeback.
+  __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   if (threadIdx.x == 0) sh[3] = (atomicAdd(&w.st[t].done, 1) == nch - 1);
   __syncthreads();
   if (!sh[3]) return;
-  // last workgroup of this query: find the bin holding the k-th entry
-  __threadfence();
+  // last workgroup of this query: find the bin holding the k-th entry (coherent loads)
   for (int i = threadIdx.x; i < kHistBins; i += NT)
     hist[i] = __hip_atomic_load(&gh[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   const int nvalid = __hip_atomic_load(&w.st[t].nvalid, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -320,49 +379,69 @@ __global__ __launch_bounds__(256) void topk_hist_kernel(TopkArgs a, TopkWs w) {
   }
 }
 
-__global__ __launch_bounds__(256) void topk_collect_kernel(TopkArgs a, TopkWs w) {
+__global__ __launch_bounds__(kLongThreads) void topk_collect_kernel(TopkArgs a, TopkWs w) {
+  constexpr int NT = kLongThreads;
+  __shared__ uint2 buf[kChunk];
+  __shared__ int nbuf, gbase;
   const int t = blockIdx.y;
-  int b;
-  const int ncols = ncols_of(a, t, &b);
+  const int ncols = ncols_of(a, t);
   const int c0 = blockIdx.x * kChunk;
   if (c0 >= ncols) return;
-  const int c1 = min(c0 + kChunk, ncols);
   const int d1 = w.st[t].d1;
   const bool keep_bin = d1 >= 0 && w.st[t].cnt1 <= kCap;
   const float* row = a.scores + (int64_t)t * a.ld;
-  int* sel = w.sel + (int64_t)t * a.k;
-  uint2* cand = w.cand + (int64_t)t * kCap;
-  for (int i0 = c0; i0 < c1; i0 += 256) {
-    const int i = i0 + threadIdx.x;
-    unsigned key = 0;
-    if (i < c1) key = score_key(row[i]);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  // wave `wave`, step u covers columns c0 + 64*(wave + 4u) + lane
+  float v[kPerThread];
+#pragma unroll
+  for (int u = 0; u < kPerThread; ++u) {
+    const int i = c0 + 64 * (wave + 4 * u) + lane;
+    v[u] = i < ncols ? row[i] : -__builtin_inff();
+  }
+  if (threadIdx.x == 0) nbuf = 0;
+  __syncthreads();
+  unsigned* bits = w.bits + (size_t)t * w.bw;
+#pragma unroll
+  for (int u = 0; u < kPerThread; ++u) {
+    const int cb = c0 + 64 * (wave + 4 * u);
+    const unsigned key = score_key(v[u]);
     const int digit = (int)(key >> 20);
     const bool up = key != 0u && (d1 < 0 || digit > d1);
     const bool in = key != 0u && keep_bin && digit == d1;
-    const int s1 = wave_append(&w.st[t].nsel, up);
-    if (up) sel[s1] = pos_of(a, t, i);
-    const int s2 = wave_append(&w.st[t].ncand, in);
-    if (in) cand[s2] = make_uint2(key, (unsigned)pos_of(a, t, i));
+    const unsigned long long m = __ballot(up);
+    if (lane == 0) {
+      bits[cb / 32] = (unsigned)m;
+      bits[cb / 32 + 1] = (unsigned)(m >> 32);
+    }
+    const int slot = wave_append(&nbuf, in);
+    if (in) buf[slot] = make_uint2(key, (unsigned)(cb + lane));
   }
+  __syncthreads();
+  const int nb = nbuf;
+  if (nb == 0) return;
+  if (threadIdx.x == 0) gbase = atomicAdd(&w.st[t].ncand, nb);
+  __syncthreads();
+  uint2* cand = w.cand + (int64_t)t * kCap;
+  for (int i = threadIdx.x; i < nb; i += NT)
+    if (gbase + i < kCap) cand[gbase + i] = buf[i];
 }
 
 struct LdsPairSrc {
   const unsigned* keys;
-  const int* pos;
+  const int* cols;
   __device__ bool get(int i, uint64_t* c) const {
-    *c = composite(keys[i], pos[i]);
+    *c = composite(keys[i], cols[i]);
     return true;
   }
 };
 
 struct GlobalBinSrc {
-  const TopkArgs* a;
-  int t;
+  const float* row;
   int d1;
   __device__ bool get(int i, uint64_t* c) const {
-    const unsigned key = score_key(a->scores[(int64_t)t * a->ld + i]);
+    const unsigned key = score_key(row[i]);
     if (key == 0u || (int)(key >> 20) != d1) return false;
-    *c = composite(key, pos_of(*a, t, i));
+    *c = composite(key, i);
     return true;
   }
 };
@@ -370,21 +449,16 @@ struct GlobalBinSrc {
 __global__ __launch_bounds__(1024) void topk_finish_kernel(TopkArgs a, TopkWs w) {
   constexpr int NT = 1024;
   __shared__ unsigned ck[kCap];
-  __shared__ int cp[kCap];
-  __shared__ unsigned hist[2048];
-  __shared__ int outl[4096];
+  __shared__ int cc[kCap];
+  __shared__ __attribute__((aligned(16))) unsigned hist[2048];
   __shared__ int scan_lds[NT / 64];
   __shared__ int sh[4];
   const int t = blockIdx.x;
-  int b;
-  const int ncols = ncols_of(a, t, &b);
+  const int ncols = ncols_of(a, t);
   const TopkState st = w.st[t];
-  const int above = st.above;
-  const int* sel = w.sel + (int64_t)t * a.k;
-  for (int i = threadIdx.x; i < above; i += NT) outl[i] = sel[i];
-  if (threadIdx.x == 0) sh[3] = above;
-  __syncthreads();
-  const int need = (st.d1 < 0 || ncols == 0) ? 0 : a.k - above;
+  unsigned* bits = w.bits + (size_t)t * w.bw;
+  const float* row = a.scores + (int64_t)t * a.ld;
+  const int need = (st.d1 < 0 || ncols == 0) ? 0 : a.k - st.above;
   if (need > 0) {
     const uint64_t prefix = (uint64_t)st.d1 << 52;
     if (st.cnt1 <= kCap) {
@@ -393,32 +467,28 @@ __global__ __launch_bounds__(1024) void topk_finish_kernel(TopkArgs a, TopkWs w)
       for (int i = threadIdx.x; i < nc; i += NT) {
         const uint2 e = cand[i];
         ck[i] = e.x;
-        cp[i] = (int)e.y;
+        cc[i] = (int)e.y;
       }
       __syncthreads();
-      LdsPairSrc src{ck, cp};
+      LdsPairSrc src{ck, cc};
       const uint64_t tau = radix_refine<NT>(src, nc, need, prefix, 12, hist, scan_lds, sh);
-      for (int i0 = 0; i0 < nc; i0 += NT) {
-        const int i = i0 + threadIdx.x;
-        uint64_t c = 0;
-        const bool v = i < nc && src.get(i, &c) && c >= tau;
-        const int slot = wave_append(&sh[3], v);
-        if (v && slot < 4096) outl[slot] = cp[i];
+      for (int i = threadIdx.x; i < nc; i += NT) {
+        uint64_t c;
+        src.get(i, &c);
+        if (c >= tau) atomicOr(&bits[cc[i] >> 5], 1u << (cc[i] & 31));
       }
     } else {
-      GlobalBinSrc src{&a, t, st.d1};
+      GlobalBinSrc src{row, st.d1};
       const uint64_t tau = radix_refine<NT>(src, ncols, need, prefix, 12, hist, scan_lds, sh);
-      for (int i0 = 0; i0 < ncols; i0 += NT) {
-        const int i = i0 + threadIdx.x;
-        uint64_t c = 0;
-        const bool v = i < ncols && src.get(i, &c) && c >= tau;
-        const int slot = wave_append(&sh[3], v);
-        if (v && slot < 4096) outl[slot] = pos_of(a, t, i);
+      for (int i = threadIdx.x; i < ncols; i += NT) {
+        uint64_t c;
+        if (src.get(i, &c) && c >= tau) atomicOr(&bits[i >> 5], 1u << (i & 31));
       }
     }
   }
+  __builtin_amdgcn_s_waitcnt(0);           // this workgroup's bit updates have completed
   __syncthreads();
-  sort_and_write<NT>(outl, min(sh[3], a.k), a.k, a.idx + (int64_t)t * a.k);
+  write_selection<NT, true>(a, t, bits, (ncols + 31) / 32, a.idx + (int64_t)t * a.k, scan_lds);
 }
 
 hipError_t launch_topk(const TopkArgs& a, hipStream_t s) {
@@ -427,13 +497,13 @@ hipError_t launch_topk(const TopkArgs& a, hipStream_t s) {
     hipLaunchKernelGGL(topk_small_kernel, dim3(a.T), dim3(1024), 0, s, a);
     return hipGetLastError();
   }
-  TopkWs w = carve(a.ws, a.T, a.k);
-  const size_t zero_words = ((char*)w.sel - (char*)w.hist) / 4;
+  TopkWs w = carve(a.ws, a.T, a.max_ctx);
+  const size_t zero_words = ((char*)w.cand - (char*)w.hist) / 4;
   const int zblocks = (int)std::min<size_t>((zero_words + 1023) / 1024, 2048);
   hipLaunchKernelGGL(topk_zero_kernel, dim3(zblocks), dim3(256), 0, s, w.hist, zero_words);
   const int nch = (a.max_ctx + kChunk - 1) / kChunk;
-  hipLaunchKernelGGL(topk_hist_kernel, dim3(nch, a.T), dim3(256), 0, s, a, w);
-  hipLaunchKernelGGL(topk_collect_kernel, dim3(nch, a.T), dim3(256), 0, s, a, w);
+  hipLaunchKernelGGL(topk_hist_kernel, dim3(nch, a.T), dim3(kLongThreads), 0, s, a, w);
+  hipLaunchKernelGGL(topk_collect_kernel, dim3(nch, a.T), dim3(kLongThreads), 0, s, a, w);
   hipLaunchKernelGGL(topk_finish_kernel, dim3(a.T), dim3(1024), 0, s, a, w);
   return hipGetLastError();
 }
