@@ -79,9 +79,10 @@ __device__ __forceinline__ v8bf cvt8_fp8_bf16(unsigned w0, unsigned w1) {
 }
 
 // Partial logits of this wave's Q.K^T slices for one tile, written to red[wave].
-template <int MT, int NS>
+template <int MT, int NS, bool FP8>
 __device__ __forceinline__ void qk_tile(const AttCtx& c, AttSmem<MT>& sm, const uint8_t* buf, int slot,
-                                        bool fp8, const uint8_t* qs, int wave, int g, int n) {
+                                        const uint8_t* qs, int wave, int g, int n) {
+  asm volatile("" : "+v"(g), "+v"(n));
   v4f sacc[MT][2];
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) sacc[mt][0] = sacc[mt][1] = v4f{0.f, 0.f, 0.f, 0.f};
@@ -96,7 +97,7 @@ __device__ __forceinline__ void qk_tile(const AttCtx& c, AttSmem<MT>& sm, const 
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt)
           qa[i][mt] = *(const v8bf*)(qs + (16 * mt + n) * c.QS + 2 * (128 * ss + 32 * g + 8 * i));
-      if (!fp8) {
+      if (!FP8) {
 #pragma unroll
         for (int nt = 0; nt < 2; ++nt) {
           const int r = 16 * nt + n;
@@ -174,9 +175,10 @@ __device__ __forceinline__ void softmax_tile(const AttCtx& c, AttSmem<MT>& sm, i
 }
 
 // P.V of one tile into this wave's output slices.
-template <int MT, int NS>
+template <int MT, int NS, bool FP8>
 __device__ __forceinline__ void pv_tile(const AttCtx& c, const AttSmem<MT>& sm, const uint8_t* buf, int slot,
-                                        bool fp8, v4f (&o)[NS][8][MT], int wave, int g, int n) {
+                                        v4f (&o)[NS][8][MT], int wave, int g, int n) {
+  asm volatile("" : "+v"(g), "+v"(n));
   // rescale by alpha when the running max moved for any head of this wave's outputs
   float al[MT][4];
   bool moved = false;
@@ -211,7 +213,7 @@ __device__ __forceinline__ void pv_tile(const AttCtx& c, const AttSmem<MT>& sm, 
 #pragma unroll
       for (int rr = 0; rr < 8; ++rr) {
         const int row = 8 * g + rr;
-        if (!fp8) {
+        if (!FP8) {
           wd[rr][0] = *(const unsigned*)(buf + row * c.RS4 + 64 * (row >> 3) + (d0 >> 1));
           wd[rr][1] = 0u;
           scl[rr] = e8m0_to_float(sm.e8[slot][row][d0 >> 5]);
@@ -228,7 +230,7 @@ __device__ __forceinline__ void pv_tile(const AttCtx& c, const AttSmem<MT>& sm, 
         unsigned cv[8];
 #pragma unroll
         for (int rr = 0; rr < 8; ++rr) {
-          if (!fp8) {
+          if (!FP8) {
             switch (bb) {
               case 0: cv[rr] = bits_of(__builtin_amdgcn_cvt_scalef32_pk_f16_fp4(wd[rr][0], scl[rr], 0)); break;
               case 1: cv[rr] = bits_of(__builtin_amdgcn_cvt_scalef32_pk_f16_fp4(wd[rr][0], scl[rr], 1)); break;
@@ -341,80 +343,81 @@ __global__ __launch_bounds__(kAttThreads) void attend_kernel(AttendArgs a, int S
     return x < c.k ? sidx[x - c.gx0] : -1;
   };
 
-  // Every register is assigned on every path, so no loaded value is ever copied (a copy
-  // would wait for all outstanding loads, the prefetch included).
+  // One code path for both tile kinds: the addresses are selected, never branched on,
+  // so no control-flow join sits between the loads and their use (a join after a load
+  // makes the compiler wait for every outstanding load, the prefetch included).
   v4u pf[4];
   unsigned pf_e8;
   auto prefetch = [&](int tile) {
+    int tid = threadIdx.x;                         // opaque: address math stays in the loop
+    asm volatile("" : "+v"(tid));
     const bool glob = tile < c.ng;
+    const int ppr = glob ? c.D / 32 : c.D / 16;    // 16-byte pieces per row; D pieces per tile
     const int wt = c.wt0 + (tile - c.ng);
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       const int pc = tid + kAttThreads * u;
+      const int r = pc / ppr, cc = pc - r * ppr;
+      const int j = (glob && pc < c.D) ? row_pos(tile, r) : -1;
+      const int uu = kWRows * wt + r;
+      const uint8_t* gsrc = a.kv_codes + (c.base + j) * (c.D / 2) + 16 * cc;
+      const uint8_t* wsrc = a.swa + ((int64_t)c.b * c.W + uu) * c.D + 16 * cc;
+      const bool ok = pc < c.D && (glob ? j >= 0 : uu < c.W);
       v4u v = {0u, 0u, 0u, 0u};
-      if (pc < c.D) {                              // a tile is D 16-byte pieces either way
-        if (glob) {
-          const int ppr = c.D / 32;
-          const int r = pc / ppr, cc = pc - r * ppr;
-          const int j = row_pos(tile, r);
-          if (j >= 0) v = *(const v4u*)(a.kv_codes + (c.base + j) * (c.D / 2) + 16 * cc);
-        } else {
-          const int ppr = c.D / 16;
-          const int r = pc / ppr, cc = pc - r * ppr;
-          const int uu = kWRows * wt + r;
-          if (uu < c.W) v = *(const v4u*)(a.swa + ((int64_t)c.b * c.W + uu) * c.D + 16 * cc);
-        }
-      }
+      if (ok) v = *(const v4u*)(glob ? gsrc : wsrc);
       pf[u] = v;
     }
-    unsigned e = 0x7F7F7F7Fu;
     const int epr = c.D / 128;
-    if (glob && tid < kGRows * epr) {
-      const int r = tid / epr, cc = tid - r * epr;
-      const int j = row_pos(tile, r);
-      if (j >= 0) e = *(const unsigned*)(a.kv_e8m0 + (c.base + j) * (c.D / 32) + 4 * cc);
-    }
+    const int re = tid / epr, ce = tid - re * epr;
+    const int je = (glob && tid < kGRows * epr) ? row_pos(tile, re) : -1;
+    unsigned e = 0x7F7F7F7Fu;
+    if (je >= 0) e = *(const unsigned*)(a.kv_e8m0 + (c.base + je) * (c.D / 32) + 4 * ce);
     pf_e8 = e;
   };
   auto commit = [&](int tile, int slot) {
-    const bool glob = tile < c.ng;
+    int tid = threadIdx.x;
+    asm volatile("" : "+v"(tid));
     uint8_t* buf = bufs + slot * c.BUF;
+    if (tile < c.ng) {
+      const int ppr = c.D / 32;
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int pc = tid + kAttThreads * u;
-      if (pc < c.D) {
-        if (glob) {
-          const int ppr = c.D / 32;
-          const int r = pc / ppr, cc = pc - r * ppr;
-          *(v4u*)(buf + r * c.RS4 + 64 * (r >> 3) + 16 * cc) = pf[u];
-        } else {
-          const int ppr = c.D / 16;
-          const int r = pc / ppr, cc = pc - r * ppr;
-          *(v4u*)(buf + r * c.RS8 + 16 * cc) = pf[u];
-        }
+      for (int u = 0; u < 4; ++u) {
+        const int pc = tid + kAttThreads * u;
+        const int r = pc / ppr, cc = pc - r * ppr;
+        if (pc < c.D) *(v4u*)(buf + r * c.RS4 + 64 * (r >> 3) + 16 * cc) = pf[u];
       }
-    }
-    const int epr = c.D / 128;
-    if (glob && tid < kGRows * epr) {
-      const int r = tid / epr, cc = tid - r * epr;
-      *(unsigned*)(&sm.e8[slot][r][4 * cc]) = pf_e8;
-    }
-    if (tid < kGRows) {
-      bool valid;
-      float rs;
-      if (glob) {
+      const int epr = c.D / 128;
+      if (tid < kGRows * epr) {
+        const int r = tid / epr, cc = tid - r * epr;
+        *(unsigned*)(&sm.e8[slot][r][4 * cc]) = pf_e8;
+      }
+      if (tid < kGRows) {
         const int j = row_pos(tile, tid);
-        valid = j >= 0;
-        rs = valid ? srho[tile * kGRows + tid - c.gx0] : 0.0f;
-      } else {
+        sm.valid[slot][tid] = j >= 0;
+        sm.rscale[slot][tid] = j >= 0 ? srho[tile * kGRows + tid - c.gx0] : 0.0f;
+      }
+    } else {
+      const int ppr = c.D / 16;
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int pc = tid + kAttThreads * u;
+        const int r = pc / ppr, cc = pc - r * ppr;
+        if (pc < c.D) *(v4u*)(buf + r * c.RS8 + 16 * cc) = pf[u];
+      }
+      if (tid < kGRows) {
         const int uu = kWRows * (c.wt0 + tile - c.ng) + tid;
         const int pos = c.pos0 + uu;
-        valid = tid < kWRows && uu < c.W && pos >= c.lo_win && pos <= c.p;
-        rs = (tid < kWRows && uu < c.W) ? ssig[uu] : 0.0f;
+        const bool in_buf = tid < kWRows && uu < c.W;
+        sm.valid[slot][tid] = in_buf && pos >= c.lo_win && pos <= c.p;
+        sm.rscale[slot][tid] = in_buf ? ssig[uu] : 0.0f;
       }
-      sm.valid[slot][tid] = valid;
-      sm.rscale[slot][tid] = rs;
     }
+  };
+
+  // Q.K^T / P.V of tile `tile` held in LDS slot `slot`; one uniform branch on its kind.
+  auto qk = [&](int tile, int slot) {
+    if (tile < c.ng) qk_tile<MT, NS, false>(c, sm, bufs + slot * c.BUF, slot, qs, wave, g, n);
+    else qk_tile<MT, NS, true>(c, sm, bufs + slot * c.BUF, slot, qs, wave, g, n);
   };
 
   v4f o[NS][8][MT];
@@ -433,7 +436,7 @@ __global__ __launch_bounds__(kAttThreads) void attend_kernel(AttendArgs a, int S
     if (tb + 1 < te) prefetch(tb + 1);
   }
   __syncthreads();
-  if (tb < te) qk_tile<MT, NS>(c, sm, bufs, 0, tb >= c.ng, qs, wave, g, n);
+  if (tb < te) qk(tb, 0);
   __syncthreads();
   if (tb < te) softmax_tile<MT>(c, sm, 0, tid);
 
@@ -444,8 +447,9 @@ __global__ __launch_bounds__(kAttThreads) void attend_kernel(AttendArgs a, int S
       if (i + 2 < te) prefetch(i + 2);
     }
     __syncthreads();                               // P(i), tile i+1 and its row flags published
-    pv_tile<MT, NS>(c, sm, bufs + cur * c.BUF, cur, i >= c.ng, o, wave, g, n);
-    if (i + 1 < te) qk_tile<MT, NS>(c, sm, bufs + nxt * c.BUF, nxt, i + 1 >= c.ng, qs, wave, g, n);
+    if (i < c.ng) pv_tile<MT, NS, false>(c, sm, bufs + cur * c.BUF, cur, o, wave, g, n);
+    else pv_tile<MT, NS, true>(c, sm, bufs + cur * c.BUF, cur, o, wave, g, n);
+    if (i + 1 < te) qk(i + 1, nxt);
     __syncthreads();                               // partial logits of tile i+1 published
     if (i + 1 < te) softmax_tile<MT>(c, sm, nxt, tid);
   }
