@@ -316,17 +316,76 @@ __global__ __launch_bounds__(kAttThreads) void attend_kernel(AttendArgs a, int S
   float* srho = (float*)(sidx + nsel);
   float* ssig = srho + nsel;
 
-  // ---- prologue: q slice, selected positions and row scales, window scales
+  auto row_pos = [&](int tile, int r) -> int {     // selected position of global row r, or -1
+    const int x = tile * kGRows + r;
+    return x < c.k ? sidx[x - c.gx0] : -1;
+  };
+
+  // Gather layout: a global tile is 32 FP4 rows of D/32 16-byte pieces, thread tid moving
+  // pieces (tid & 15) + 16u of row tid >> 4 and E8M0 word tid & 15 of that row; a window
+  // tile is 16 FP8 rows of D/16 pieces, thread tid moving pieces (tid & 31) + 32u of row
+  // tid >> 5.  Each load instruction of a wave reads 256-byte runs of 4 (2) rows.
+  // One code path for both tile kinds: addresses are selected, never branched on, so no
+  // control-flow join sits between a load and its use (a join after a load makes the
+  // compiler wait for every outstanding load, the prefetch included).
+  auto positions = [&](int tile) -> int {          // position of this thread's global row
+    int tid = threadIdx.x;                         // opaque: address math stays in the loop
+    asm volatile("" : "+v"(tid));
+    return tile < c.ng ? row_pos(tile, tid >> 4) : -1;
+  };
+  v4u pf[4];
+  unsigned pf_e8;
+  auto loads = [&](int tile, int j) {
+    int tid = threadIdx.x;
+    asm volatile("" : "+v"(tid));
+    const bool glob = tile < c.ng;
+    const int r = glob ? tid >> 4 : tid >> 5;
+    const int q = glob ? tid & 15 : tid & 31;
+    const int step = glob ? 16 : 32;
+    const int ppr = glob ? c.D / 32 : c.D / 16;
+    const int uu = kWRows * (c.wt0 + tile - c.ng) + r;
+    const uint8_t* gsrc = a.kv_codes + (c.base + j) * (c.D / 2);
+    const uint8_t* wsrc = a.swa + ((int64_t)c.b * c.W + uu) * c.D;
+    const uint8_t* src = glob ? gsrc : wsrc;
+    const bool row_ok = glob ? j >= 0 : uu < c.W;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int piece = q + step * u;
+      v4u v = {0u, 0u, 0u, 0u};
+      if (row_ok && piece < ppr) v = *(const v4u*)(src + 16 * piece);
+      pf[u] = v;
+    }
+    unsigned e = 0x7F7F7F7Fu;
+    if (glob && j >= 0 && (tid & 15) < c.D / 128)
+      e = *(const unsigned*)(a.kv_e8m0 + (c.base + j) * (c.D / 32) + 4 * (tid & 15));
+    pf_e8 = e;
+  };
+  auto prefetch = [&](int tile) { loads(tile, positions(tile)); };
+
+  // ---- prologue.  Every load of step (1) is unconditional (clamped addresses), so the
+  // compiler can count them exactly and keep the q slice in flight while it waits for
+  // the positions; (2) the first tile's rows and the split's row scales follow.
+  const int tb = c.tb, te = c.te;
   {
     const int per_row = c.D / 8;
-    for (int pc = tid; pc < kHG * per_row; pc += kAttThreads) {
+    const int nq = kHG * per_row;                  // <= 4096 16-byte pieces
+    const int32_t* ip = a.idx + (int64_t)t * c.k;
+    const int x0 = c.gx0 + tid;
+    const int j0 = ip[min(x0, c.k - 1)];
+    v4u qv[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int pc = min(tid + kAttThreads * u, nq - 1);
       const int h = pc / per_row, cc = pc - h * per_row;
-      *(v4u*)(qs + h * c.QS + 16 * cc) = *(const v4u*)(a.q + ((int64_t)t * a.Hq + h0 + h) * c.D + 8 * cc);
+      qv[u] = *(const v4u*)(a.q + ((int64_t)t * a.Hq + h0 + h) * c.D + 8 * cc);
     }
-    for (int x = c.gx0 + tid; x < gx1; x += kAttThreads) {
-      const int j = a.idx[(int64_t)t * c.k + x];
-      sidx[x - c.gx0] = j;
-      srho[x - c.gx0] = (j >= 0 && a.kv_rowscale) ? a.kv_rowscale[c.base + j] : 1.0f;
+    if (x0 < gx1) sidx[x0 - c.gx0] = j0;
+    for (int x = x0 + kAttThreads; x < gx1; x += kAttThreads) sidx[x - c.gx0] = ip[x];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int pc = tid + kAttThreads * u;
+      const int h = pc / per_row, cc = pc - h * per_row;
+      if (pc < nq) *(v4u*)(qs + h * c.QS + 16 * cc) = qv[u];
     }
     for (int u = tid; u < c.W; u += kAttThreads)
       ssig[u] = a.swa_scale ? a.swa_scale[(int64_t)c.b * c.W + u] : 1.0f;
@@ -337,73 +396,36 @@ __global__ __launch_bounds__(kAttThreads) void attend_kernel(AttendArgs a, int S
     }
   }
   __syncthreads();
+  if (tb < te) prefetch(tb);
+  for (int x = c.gx0 + tid; x < gx1; x += kAttThreads) {
+    const int j = sidx[x - c.gx0];
+    srho[x - c.gx0] = (j >= 0 && a.kv_rowscale) ? a.kv_rowscale[c.base + j] : 1.0f;
+  }
+  __syncthreads();
 
-  auto row_pos = [&](int tile, int r) -> int {     // selected position of global row r, or -1
-    const int x = tile * kGRows + r;
-    return x < c.k ? sidx[x - c.gx0] : -1;
-  };
 
-  // One code path for both tile kinds: the addresses are selected, never branched on,
-  // so no control-flow join sits between the loads and their use (a join after a load
-  // makes the compiler wait for every outstanding load, the prefetch included).
-  v4u pf[4];
-  unsigned pf_e8;
-  auto prefetch = [&](int tile) {
-    int tid = threadIdx.x;                         // opaque: address math stays in the loop
-    asm volatile("" : "+v"(tid));
-    const bool glob = tile < c.ng;
-    const int ppr = glob ? c.D / 32 : c.D / 16;    // 16-byte pieces per row; D pieces per tile
-    const int wt = c.wt0 + (tile - c.ng);
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int pc = tid + kAttThreads * u;
-      const int r = pc / ppr, cc = pc - r * ppr;
-      const int j = (glob && pc < c.D) ? row_pos(tile, r) : -1;
-      const int uu = kWRows * wt + r;
-      const uint8_t* gsrc = a.kv_codes + (c.base + j) * (c.D / 2) + 16 * cc;
-      const uint8_t* wsrc = a.swa + ((int64_t)c.b * c.W + uu) * c.D + 16 * cc;
-      const bool ok = pc < c.D && (glob ? j >= 0 : uu < c.W);
-      v4u v = {0u, 0u, 0u, 0u};
-      if (ok) v = *(const v4u*)(glob ? gsrc : wsrc);
-      pf[u] = v;
-    }
-    const int epr = c.D / 128;
-    const int re = tid / epr, ce = tid - re * epr;
-    const int je = (glob && tid < kGRows * epr) ? row_pos(tile, re) : -1;
-    unsigned e = 0x7F7F7F7Fu;
-    if (je >= 0) e = *(const unsigned*)(a.kv_e8m0 + (c.base + je) * (c.D / 32) + 4 * ce);
-    pf_e8 = e;
-  };
   auto commit = [&](int tile, int slot) {
     int tid = threadIdx.x;
     asm volatile("" : "+v"(tid));
     uint8_t* buf = bufs + slot * c.BUF;
     if (tile < c.ng) {
-      const int ppr = c.D / 32;
+      const int r = tid >> 4, q = tid & 15;
+      uint8_t* dst = buf + r * c.RS4 + 64 * (r >> 3);
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int pc = tid + kAttThreads * u;
-        const int r = pc / ppr, cc = pc - r * ppr;
-        if (pc < c.D) *(v4u*)(buf + r * c.RS4 + 64 * (r >> 3) + 16 * cc) = pf[u];
-      }
-      const int epr = c.D / 128;
-      if (tid < kGRows * epr) {
-        const int r = tid / epr, cc = tid - r * epr;
-        *(unsigned*)(&sm.e8[slot][r][4 * cc]) = pf_e8;
-      }
+      for (int u = 0; u < 4; ++u)
+        if (q + 16 * u < c.D / 32) *(v4u*)(dst + 16 * (q + 16 * u)) = pf[u];
+      if (q < c.D / 128) *(unsigned*)(&sm.e8[slot][r][4 * q]) = pf_e8;
       if (tid < kGRows) {
         const int j = row_pos(tile, tid);
         sm.valid[slot][tid] = j >= 0;
         sm.rscale[slot][tid] = j >= 0 ? srho[tile * kGRows + tid - c.gx0] : 0.0f;
       }
     } else {
-      const int ppr = c.D / 16;
+      const int r = tid >> 5, q = tid & 31;
+      uint8_t* dst = buf + r * c.RS8;
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int pc = tid + kAttThreads * u;
-        const int r = pc / ppr, cc = pc - r * ppr;
-        if (pc < c.D) *(v4u*)(buf + r * c.RS8 + 16 * cc) = pf[u];
-      }
+      for (int u = 0; u < 4; ++u)
+        if (q + 32 * u < c.D / 16) *(v4u*)(dst + 16 * (q + 32 * u)) = pf[u];
       if (tid < kGRows) {
         const int uu = kWRows * (c.wt0 + tile - c.ng) + tid;
         const int pos = c.pos0 + uu;
@@ -429,9 +451,7 @@ __global__ __launch_bounds__(kAttThreads) void attend_kernel(AttendArgs a, int S
       for (int mt = 0; mt < MT; ++mt) o[s][j][mt] = v4f{0.f, 0.f, 0.f, 0.f};
 
   // ---- pipeline fill: tile tb committed and scored, tile tb+1 in flight
-  const int tb = c.tb, te = c.te;
   if (tb < te) {
-    prefetch(tb);
     commit(tb, 0);
     if (tb + 1 < te) prefetch(tb + 1);
   }
@@ -554,12 +574,13 @@ int attend_splits(int32_t T, int32_t k, int32_t W, int32_t Hq, int32_t D) {
   const int ntiles = max_tiles(k, W);
   const int64_t base = (int64_t)T * ngroups;
   if (base <= 0) return 1;
-  // enough workgroups to cover the chip twice, but at least 4 tiles per split so the
-  // prefetch pipeline has work to overlap, and at most 16 partials per output
+  // one workgroup per CU (a workgroup fills a CU's LDS), at least 3 tiles per split so
+  // the prefetch pipeline has work to overlap its fixed start-up cost, and at most 32
+  // partials per output
   int S = 1;
-  if (base < 512) S = (int)((512 + base - 1) / base);
-  S = std::min(S, std::max(1, ntiles / 4));
-  S = std::min(S, 16);
+  if (base < 256) S = (int)((256 + base - 1) / base);
+  S = std::min(S, std::max(1, ntiles / 3));
+  S = std::min(S, 32);
   return std::max(S, 1);
 }
 

@@ -86,16 +86,72 @@ __device__ __forceinline__ int pos_of(const TopkArgs& a, int t, int col) {
   return a.cand ? a.cand[(int64_t)t * a.n_cand + col] : col;
 }
 
+// Inclusive prefix sum over a wave with DPP row shifts and row broadcasts: within each
+// row of 16 lanes by shifts of 1, 2, 4, 8 (lanes shifted in from outside the row read
+// 0), then the total of row 0 into row 1 and of row 2 into row 3, then the total of
+// rows 0-1 into rows 2-3.
+__device__ __forceinline__ int wave_inclusive_sum(int v) {
+  v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xf, 0xf, true);   // row_shr:1
+  v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xf, 0xf, true);   // row_shr:2
+  v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xf, 0xf, true);   // row_shr:4
+  v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xf, 0xf, true);   // row_shr:8
+  v += __builtin_amdgcn_update_dpp(0, v, 0x142, 0xa, 0xf, false);  // row_bcast:15 -> rows 1, 3
+  v += __builtin_amdgcn_update_dpp(0, v, 0x143, 0xc, 0xf, false);  // row_bcast:31 -> rows 2, 3
+  return v;
+}
+
+// Inclusive running maximum over a wave (unsigned; 0 is the identity), same DPP pattern.
+__device__ __forceinline__ unsigned wave_inclusive_max(unsigned v) {
+  v = max(v, (unsigned)__builtin_amdgcn_update_dpp(0, (int)v, 0x111, 0xf, 0xf, true));
+  v = max(v, (unsigned)__builtin_amdgcn_update_dpp(0, (int)v, 0x112, 0xf, 0xf, true));
+  v = max(v, (unsigned)__builtin_amdgcn_update_dpp(0, (int)v, 0x114, 0xf, 0xf, true));
+  v = max(v, (unsigned)__builtin_amdgcn_update_dpp(0, (int)v, 0x118, 0xf, 0xf, true));
+  v = max(v, (unsigned)__builtin_amdgcn_update_dpp(0, (int)v, 0x142, 0xa, 0xf, false));
+  v = max(v, (unsigned)__builtin_amdgcn_update_dpp(0, (int)v, 0x143, 0xc, 0xf, false));
+  return v;
+}
+
+// Digit search by one wave: hist[nbins] (nbins = 64 * per), lane l owning the per bins
+// below nbins - per * l, in descending order.  Writes sh[0] = d with
+// count(bins > d) < need <= count(bins >= d) (-1 if none) and sh[1] = count(bins > d).
+template <int PER>
+__device__ void wave_find_digit(const unsigned* hist, int need, int* sh) {
+  const int lane = threadIdx.x & 63;
+  const int top = 64 * PER - 1 - PER * lane;
+  unsigned h[PER];
+  int local = 0;
+#pragma unroll
+  for (int i = 0; i < PER; i += 4) {
+    const uint4 q = *(const uint4*)(&hist[top - i - 3]);
+    h[i] = q.w;
+    h[i + 1] = q.z;
+    h[i + 2] = q.y;
+    h[i + 3] = q.x;
+  }
+#pragma unroll
+  for (int i = 0; i < PER; ++i) local += (int)h[i];
+  const int incl = wave_inclusive_sum(local);
+  int cum = incl - local;
+  const int total = __builtin_amdgcn_readlane(incl, 63);
+  if (lane == 0 && total < need) sh[0] = -1;
+  if (cum < need && need <= incl) {
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int hv = (int)h[i];
+      if (cum < need && need <= cum + hv) {
+        sh[0] = top - i;
+        sh[1] = cum;
+      }
+      cum += hv;
+    }
+  }
+}
+
 // Exclusive prefix sum over the block (NT threads); lds needs NT/64 ints.
 template <int NT>
 __device__ int block_exclusive_scan(int v, int* lds, int* total) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  int x = v;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const int y = __shfl_up(x, o);
-    if (lane >= o) x += y;
-  }
+  const int x = wave_inclusive_sum(v);
   if (lane == 63) lds[wave] = x;
   __syncthreads();
   int wbase = 0, tot = 0;
@@ -246,63 +302,141 @@ __device__ void write_selection(const TopkArgs& a, int t, const unsigned* bits, 
 
 // ------------------------------------------------------------------ short rows
 
-struct LdsKeySrc {
-  const unsigned* keys;
-  __device__ bool get(int i, uint64_t* c) const {
-    const unsigned key = keys[i];
-    if (key == 0u) return false;
-    *c = composite(key, i);
-    return true;
-  }
-};
-
+// One 1024-thread workgroup per query.  Thread i owns columns 16i .. 16i+15 (keys staged
+// through LDS so the row is read with coalesced loads) and keeps their 32-bit keys in
+// registers.  Radix select over the keys finds tau with count(key > tau) < k <=
+// count(key >= tau); when several columns share the key tau, the lowest columns among
+// them are taken.  Column order is thread order, so one block-wide scan of a packed
+// (ties, greater) count pair yields both each thread's tie rank and its output offset,
+// and the selection comes out in ascending column order.
 __global__ __launch_bounds__(1024) void topk_small_kernel(TopkArgs a) {
   constexpr int NT = 1024;
-  constexpr int PER = kSmallN / NT;
-  __shared__ unsigned keys[kSmallN];
-  __shared__ unsigned bits[kSmallN / 32];
+  constexpr int PER = kSmallN / NT;               // 16
+  __shared__ __attribute__((aligned(16))) unsigned keys[kSmallN];
   __shared__ __attribute__((aligned(16))) unsigned hist[2048];
+  __shared__ unsigned red[2 * (NT / 64)];
   __shared__ int scan_lds[NT / 64];
   __shared__ int sh[4];
-  const int t = blockIdx.x;
-  const int ncols = ncols_of(a, t);
+  const int t = blockIdx.x, tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
   const float* row = a.scores + (int64_t)t * a.ld;
-  if (threadIdx.x == 0) sh[2] = 0;
+  // row loads first (bounded by the row width, known without any load), the query's
+  // column count (a chain of small dependent loads) meanwhile
   float v[PER];
 #pragma unroll
   for (int u = 0; u < PER; ++u) {
-    const int i = threadIdx.x + NT * u;
-    v[u] = i < ncols ? row[i] : -__builtin_inff();
+    const int col = tid + NT * u;
+    v[u] = col < a.max_ctx ? row[col] : -__builtin_inff();
   }
-  int cnt = 0;
+  const int ncols = ncols_of(a, t);
 #pragma unroll
   for (int u = 0; u < PER; ++u) {
-    const unsigned key = score_key(v[u]);
-    keys[threadIdx.x + NT * u] = key;
-    cnt += key != 0u;
+    const int col = tid + NT * u;
+    keys[col] = col < ncols ? score_key(v[u]) : 0u;
   }
   __syncthreads();
-  if (cnt) atomicAdd(&sh[2], cnt);
+  unsigned key[PER];
+#pragma unroll
+  for (int u = 0; u < PER; u += 4) {
+    const uint4 k4 = *(const uint4*)(&keys[PER * tid + u]);
+    key[u] = k4.x;
+    key[u + 1] = k4.y;
+    key[u + 2] = k4.z;
+    key[u + 3] = k4.w;
+  }
+  const int c0 = PER * tid;
+  // valid count and the min / max valid key (min as the max of ~key over valid keys)
+  int cnt = 0;
+  unsigned nlo = 0u, hi = 0u;
+#pragma unroll
+  for (int u = 0; u < PER; ++u) {
+    cnt += key[u] != 0u;
+    nlo = key[u] ? max(nlo, ~key[u]) : nlo;
+    hi = max(hi, key[u]);
+  }
+  cnt = wave_inclusive_sum(cnt);
+  nlo = wave_inclusive_max(nlo);
+  hi = wave_inclusive_max(hi);
+  if (lane == 63) {
+    scan_lds[wave] = cnt;
+    red[2 * wave] = nlo;
+    red[2 * wave + 1] = hi;
+  }
   __syncthreads();
-  const int nvalid = sh[2];
-  LdsKeySrc src{keys};
-  uint64_t tau = 0;
-  const bool all = nvalid <= a.k;
-  if (!all) tau = radix_refine<NT>(src, ncols, a.k, 0ull, 0, hist, scan_lds, sh);
-  // bitmap: each wave covers 64 consecutive columns per step
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  for (int c0 = 64 * wave; c0 < kSmallN; c0 += 64 * (NT / 64)) {
-    const int i = c0 + lane;
-    uint64_t c = 0;
-    const bool sel = i < ncols && src.get(i, &c) && (all || c >= tau);
-    const unsigned long long m = __ballot(sel);
-    if (lane == 0) {
-      bits[c0 / 32] = (unsigned)m;
-      bits[c0 / 32 + 1] = (unsigned)(m >> 32);
+  int nvalid = 0;
+  nlo = 0u;
+  hi = 0u;
+#pragma unroll
+  for (int i = 0; i < NT / 64; ++i) {
+    nvalid += scan_lds[i];
+    nlo = max(nlo, red[2 * i]);
+    hi = max(hi, red[2 * i + 1]);
+  }
+  unsigned lo = ~nlo;
+  __syncthreads();
+
+  unsigned tau = 1u;                               // every valid key is >= 1
+  int tie_need = NT * PER;                         // columns with key == tau to take
+  if (nvalid > a.k) {
+    // leading bits shared by every valid key carry no information
+    int nbits = lo == hi ? 32 : __clz((int)(lo ^ hi));
+    unsigned prefix = nbits == 32 ? lo : (nbits == 0 ? 0u : (lo >> (32 - nbits)) << (32 - nbits));
+    int need = a.k;
+    bool whole_bin = false;
+    while (nbits < 32) {
+      const int dbits = min(11, 32 - nbits);
+      const int shift = 32 - nbits - dbits;
+      const unsigned dmask = (1u << dbits) - 1u;
+      hist[2 * tid] = 0u;
+      hist[2 * tid + 1] = 0u;
+      __syncthreads();
+#pragma unroll
+      for (int u = 0; u < PER; ++u) {
+        const bool match = key[u] != 0u && (nbits == 0 || (key[u] >> (32 - nbits)) == (prefix >> (32 - nbits)));
+        if (match) atomicAdd(&hist[(key[u] >> shift) & dmask], 1u);
+      }
+      __syncthreads();
+      if (wave == 0) wave_find_digit<32>(hist, need, sh);
+      __syncthreads();
+      const int d = sh[0];
+      if (d < 0) break;                            // cannot happen: nvalid > k
+      const int above = sh[1];
+      const int inbin = (int)hist[d];
+      need -= above;
+      prefix |= (unsigned)d << shift;
+      nbits += dbits;
+      __syncthreads();                             // hist and sh are rewritten next pass
+      if (inbin == need) {                         // the whole bin is taken
+        whole_bin = true;
+        break;
+      }
+    }
+    tau = max(prefix, 1u);                         // a bin's lower bound may be the invalid key 0
+    if (!whole_bin) tie_need = need;               // tau fully resolved: `need` of its ties
+  }
+  // (ties, greater) counts packed in one scan: both fit in 16 bits
+  int ngt = 0, nties = 0;
+#pragma unroll
+  for (int u = 0; u < PER; ++u) {
+    ngt += key[u] > tau;
+    nties += key[u] == tau;
+  }
+  int total;
+  const int pre = block_exclusive_scan<NT>((nties << 16) | ngt, scan_lds, &total);
+  int tie_rank = pre >> 16;
+  int off = (pre & 0xFFFF) + min(tie_rank, tie_need);
+  const int nsel = (total & 0xFFFF) + min(total >> 16, tie_need);
+  int32_t* dst = a.idx + (int64_t)t * a.k;
+#pragma unroll
+  for (int u = 0; u < PER; ++u) {
+    bool sel = key[u] > tau;
+    if (key[u] == tau) sel = tie_rank++ < tie_need;
+    if (sel) {
+      if (off < a.k) dst[off] = pos_of(a, t, c0 + u);
+      ++off;
     }
   }
-  __syncthreads();
-  write_selection<NT, false>(a, t, bits, (ncols + 31) / 32, a.idx + (int64_t)t * a.k, scan_lds);
+  for (int i = min(nsel, a.k) + tid; i < a.k; i += NT) dst[i] = -1;
 }
 
 // ------------------------------------------------------------------ long rows
