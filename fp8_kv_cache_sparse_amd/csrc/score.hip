@@ -32,9 +32,21 @@ __device__ __forceinline__ v8bf fp8x8_to_bf16(unsigned w0, unsigned w1) {
   u.w = __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, 1.0f, true));
   return __builtin_bit_cast(v8bf, u);
 }
+// max(x, 0) as one integer max: non-negative floats order like their bit patterns, and
+// every negative float (and -0) is a negative int32.
+__device__ __forceinline__ float relu(float x) { return __int_as_float(max(__float_as_int(x), 0)); }
+
 constexpr int kQRow = 144;   // LDS bytes per head row (128 + 16 pad: conflict-free b128 reads)
 
-template <int MT, int TPW, bool CAND>
+// Raw keys of one block of positions for one lane: TPW tiles x DI/4 bytes.
+template <int TPW, int DI>
+struct RawKeys {
+  v4u lo[TPW], hi[TPW];
+  float kap[TPW];
+  int pos[TPW];   // position (CAND: from the list), -1 when the column is empty or invalid
+};
+
+template <int MT, int TPW, int DI, bool CAND>
 __global__ __launch_bounds__(kScoreThreads) void score_kernel(ScoreArgs a) {
   __shared__ __align__(16) uint8_t q_lds[16 * MT * kQRow];
   __shared__ float w_lds[16 * MT];
@@ -44,7 +56,8 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel(ScoreArgs a) {
   const int wave = tid >> 6, lane = tid & 63, g = lane >> 4, n = lane & 15;
   constexpr int kPosPerWave = 16 * TPW;
   constexpr int kPosPerWG = 4 * kPosPerWave;
-  const int Di = a.Di, Hi = a.Hi;
+  constexpr int NKS = DI / 32;
+  const int Hi = a.Hi;
 
   int b, t0, t1;
   if (CAND) {
@@ -58,154 +71,217 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel(ScoreArgs a) {
   }
   const int64_t base = a.seq_start[b];
   const int len = (int)(a.seq_start[b + 1] - base);
-  const int col0 = blockIdx.x * kPosPerWG;
-  if (CAND) {
-    if (col0 >= a.n_cand) return;
-  } else {
-    if (col0 >= len || t0 >= t1) return;
+  const int ncols = CAND ? a.n_cand : len;
+  int nblk = (ncols + kPosPerWG - 1) / kPosPerWG;
+  int blk = blockIdx.x;
+  if (blk >= nblk || t0 >= t1) return;
+  if (len == 0) {                                  // candidate mode only: nothing is visible
+    for (int c = blk * kPosPerWG + tid; c < a.n_cand; c += gridDim.x * kPosPerWG)
+      a.scores[(int64_t)t0 * a.ld + c] = -__builtin_inff();
+    return;
+  }
+
+  // Keys of block `bk` straight into registers: lane (g, n) holds position n of each tile
+  // and key bytes [g*DI/4, (g+1)*DI/4); MFMA K-step s uses bytes g*DI/4 + 8s .. +8, and q
+  // uses the same byte -> k assignment, so the k-sum is the full dot product.  Addresses
+  // of empty columns are clamped to the sequence's first row, so every load is issued.
+  auto load_keys = [&](int bk, RawKeys<TPW, DI>& r) {
+#pragma unroll
+    for (int i = 0; i < TPW; ++i) {
+      const int col = bk * kPosPerWG + wave * kPosPerWave + 16 * i + n;
+      int pos = col;
+      bool ok = col < ncols;
+      if (CAND) {
+        pos = ok ? a.cand[(int64_t)t0 * a.n_cand + col] : -1;
+        ok = ok && pos >= 0 && pos < len;
+      }
+      const int64_t rowi = base + (ok ? pos : 0);
+      const uint8_t* row = a.k_fp8 + rowi * DI + g * (DI / 4);
+      r.lo[i] = *(const v4u*)row;
+      if (DI == 128) r.hi[i] = *(const v4u*)(row + 16);
+      r.kap[i] = a.k_scale ? a.k_scale[rowi] : 1.0f;
+      r.pos[i] = ok ? pos : -1;
+    }
+  };
+
+  RawKeys<TPW, DI> raw;
+  load_keys(blk, raw);
+
+  // largest query position of the sequence: blocks past it are never scored (dense)
+  int pmax = 0x7FFFFFFF;
+  if (!CAND) {
     if (tid == 0) s_pmax = -1;
     __syncthreads();
     int pm = -1;
     for (int t = t0 + tid; t < t1; t += kScoreThreads) pm = max(pm, a.q_pos[t]);
     if (pm >= 0) atomicMax(&s_pmax, pm);
     __syncthreads();
-    if (col0 > s_pmax) return;
+    pmax = s_pmax;
+    nblk = min(nblk, pmax / kPosPerWG + 1);
   }
 
-  // ---- this wave's keys (B operands), loaded and converted to bf16 once ----
-  // Lane (g, n) holds position n of the tile and key bytes [g*Di/4, (g+1)*Di/4);
-  // K-step s uses bytes g*Di/4 + 8s .. +8.  q uses the same byte->k assignment, so
-  // the sum over k is the full dot product.
-  constexpr int NKS_MAX = 4;
-  const int nks = Di / 32;
-  v8bf kb[TPW][NKS_MAX];
-  float kap[TPW];
-  int kpos[TPW];
-#pragma unroll
-  for (int i = 0; i < TPW; ++i) {
-    const int col = col0 + wave * kPosPerWave + 16 * i + n;
-    int pos;
-    bool ok;
-    if (CAND) {
-      ok = col < a.n_cand;
-      pos = ok ? a.cand[(int64_t)t0 * a.n_cand + col] : -1;
-      ok = ok && pos >= 0 && pos < len;
-    } else {
-      pos = col;
-      ok = col < len;
+  auto stage_q = [&](int t) {
+    const int pieces_per_row = DI / 16;
+    const int total = 16 * MT * pieces_per_row;
+    for (int pc = tid; pc < total; pc += kScoreThreads) {
+      const int h = pc / pieces_per_row, c = pc % pieces_per_row;
+      v4u v = {0u, 0u, 0u, 0u};
+      if (h < Hi) v = *(const v4u*)(a.q_fp8 + ((int64_t)t * Hi + h) * DI + 16 * c);
+      *(v4u*)(q_lds + h * kQRow + 16 * c) = v;
     }
-    kpos[i] = ok ? pos : -1;
-    v4u lo = {0u, 0u, 0u, 0u}, hi = {0u, 0u, 0u, 0u};
-    if (ok) {
-      const uint8_t* row = a.k_fp8 + (base + pos) * Di + g * (Di / 4);
-      lo = *(const v4u*)row;
-      if (Di == 128) hi = *(const v4u*)(row + 16);
-    }
-    const unsigned wds[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
-#pragma unroll
-    for (int s2 = 0; s2 < NKS_MAX; ++s2) kb[i][s2] = fp8x8_to_bf16(wds[2 * s2], wds[2 * s2 + 1]);
-    kap[i] = (ok && a.k_scale) ? a.k_scale[base + pos] : 1.0f;
+    if (tid < 16 * MT) w_lds[tid] = tid < Hi ? a.w[(int64_t)t * Hi + tid] : 0.0f;
+  };
+  // One query per sequence (decode): q, w and the position are loaded once, so the block
+  // loop issues no load besides the key prefetch and never waits for it early.
+  const bool single = t1 - t0 == 1;
+  const int p0 = __builtin_amdgcn_readfirstlane(a.q_pos[t0]);
+  if (single) {
+    stage_q(t0);
+    __syncthreads();
   }
 
-  for (int t = t0; t < t1; ++t) {
-    const int p = a.q_pos[t];
-    if (!CAND && p < col0) continue;
-    __syncthreads();
-    // stage q[t] (heads padded to 16*MT with zeros) and w[t]
-    {
-      const int pieces_per_row = Di / 16;
-      const int total = 16 * MT * pieces_per_row;
-      for (int pc = tid; pc < total; pc += kScoreThreads) {
-        const int h = pc / pieces_per_row, c = pc % pieces_per_row;
-        v4u v = {0u, 0u, 0u, 0u};
-        if (h < Hi) v = *(const v4u*)(a.q_fp8 + ((int64_t)t * Hi + h) * Di + 16 * c);
-        *(v4u*)(q_lds + h * kQRow + 16 * c) = v;
-      }
-      if (tid < 16 * MT) w_lds[tid] = tid < Hi ? a.w[(int64_t)t * Hi + tid] : 0.0f;
-    }
-    __syncthreads();
-    // heads outer, positions inner: one 16-head slice of q is live at a time; the keys
-    // were converted once per block.  kappa > 0 commutes with the ReLU, so it scales the
-    // head sum instead of every term.
-    float sum[TPW];
-#pragma unroll
-    for (int i = 0; i < TPW; ++i) sum[i] = 0.0f;
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt) {
-      v8bf qa[NKS_MAX];
-      float wr[4];
-      {
-        const uint8_t* src = q_lds + (16 * mt + n) * kQRow + g * (Di / 4);
-        const v4u lo = *(const v4u*)src;
-        v4u hi = {0u, 0u, 0u, 0u};
-        if (Di == 128) hi = *(const v4u*)(src + 16);
-        const unsigned wds[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
-#pragma unroll
-        for (int s2 = 0; s2 < NKS_MAX; ++s2) qa[s2] = fp8x8_to_bf16(wds[2 * s2], wds[2 * s2 + 1]);
-#pragma unroll
-        for (int r = 0; r < 4; ++r) wr[r] = w_lds[16 * mt + 4 * g + r];
-      }
-#pragma unroll
-      for (int i = 0; i < TPW; ++i) {
-        const int colbase = col0 + wave * kPosPerWave + 16 * i;
-        if (!CAND && colbase > p) break;
-        v4f acc = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-        for (int s2 = 0; s2 < NKS_MAX; ++s2)
-          if (s2 < nks) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[s2], kb[i][s2], acc, 0, 0, 0);
-#pragma unroll
-        for (int r = 0; r < 4; ++r) sum[i] += wr[r] * fmaxf(acc[r], 0.0f);
-      }
-    }
+  // The next block's keys load while this block is scored.
+  auto score_block = [&](RawKeys<TPW, DI>& rk) {
+    // convert this block's keys (exact E4M3 -> bf16), then reuse rk for block + G
+    v8bf kb[TPW][NKS];
+    float kap[TPW];
+    int kpos[TPW];
 #pragma unroll
     for (int i = 0; i < TPW; ++i) {
-      const int colbase = col0 + wave * kPosPerWave + 16 * i;
-      if (!CAND && colbase > p) break;
-      float sm = sum[i];
-      sm += __shfl_xor(sm, 16);
-      sm += __shfl_xor(sm, 32);
-      sm *= kap[i];
-      if (g == 0) {
-        const int col = colbase + n;
-        if (CAND) {
-          if (col < a.n_cand) {
-            const bool valid = kpos[i] >= 0 && kpos[i] <= p;
-            a.scores[(int64_t)t * a.ld + col] = valid ? sm : -__builtin_inff();
+      const unsigned wds[8] = {rk.lo[i].x, rk.lo[i].y, rk.lo[i].z, rk.lo[i].w,
+                               rk.hi[i].x, rk.hi[i].y, rk.hi[i].z, rk.hi[i].w};
+#pragma unroll
+      for (int s2 = 0; s2 < NKS; ++s2) kb[i][s2] = fp8x8_to_bf16(wds[2 * s2], wds[2 * s2 + 1]);
+      kap[i] = rk.kap[i];
+      kpos[i] = rk.pos[i];
+    }
+    const int col0 = blk * kPosPerWG;
+    if (blk + (int)gridDim.x < nblk) load_keys(blk + gridDim.x, rk);
+
+      for (int t = t0; t < t1; ++t) {
+        const int p = single ? p0 : __builtin_amdgcn_readfirstlane(a.q_pos[t]);
+        if (!CAND && p < col0) continue;
+        if (!single) {
+          __syncthreads();
+          stage_q(t);
+          __syncthreads();
+        }
+        // heads outer, positions inner: one 16-head slice of q is live at a time; the TPW
+        // accumulator chains are interleaved so consecutive MFMAs are independent.  kappa > 0
+        // commutes with the ReLU, so it scales the head sum instead of every term.
+        float sum[TPW];
+#pragma unroll
+        for (int i = 0; i < TPW; ++i) sum[i] = 0.0f;
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) {
+          v8bf qa[NKS];
+          float wr[4];
+          {
+            const uint8_t* src = q_lds + (16 * mt + n) * kQRow + g * (DI / 4);
+            const v4u lo = *(const v4u*)src;
+            v4u hi = {0u, 0u, 0u, 0u};
+            if (DI == 128) hi = *(const v4u*)(src + 16);
+            const unsigned wds[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+#pragma unroll
+            for (int s2 = 0; s2 < NKS; ++s2) qa[s2] = fp8x8_to_bf16(wds[2 * s2], wds[2 * s2 + 1]);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) wr[r] = w_lds[16 * mt + 4 * g + r];
           }
-        } else if (col <= p && col < len) {
-          a.scores[(int64_t)t * a.ld + col] = sm;
+          v4f acc[TPW];
+#pragma unroll
+          for (int i = 0; i < TPW; ++i) acc[i] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+          for (int s2 = 0; s2 < NKS; ++s2)
+#pragma unroll
+            for (int i = 0; i < TPW; ++i)
+              acc[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[s2], kb[i][s2], acc[i], 0, 0, 0);
+#pragma unroll
+          for (int i = 0; i < TPW; ++i)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) sum[i] += wr[r] * relu(acc[i][r]);
+        }
+#pragma unroll
+        for (int i = 0; i < TPW; ++i) {
+          const int colbase = col0 + wave * kPosPerWave + 16 * i;
+          float sm = sum[i];
+          sm += __shfl_xor(sm, 16);
+          sm += __shfl_xor(sm, 32);
+          sm *= kap[i];
+          if (g == 0) {
+            const int col = colbase + n;
+            if (CAND) {
+              if (col < a.n_cand) {
+                const bool valid = kpos[i] >= 0 && kpos[i] <= p;
+                a.scores[(int64_t)t * a.ld + col] = valid ? sm : -__builtin_inff();
+              }
+            } else if (col <= p && col < len) {
+              a.scores[(int64_t)t * a.ld + col] = sm;
+            }
+          }
         }
       }
-    }
-  }
+  };
+
+  for (; blk < nblk; blk += gridDim.x) score_block(raw);
 }
 
-template <int MT, int TPW, bool CAND>
-static hipError_t launch_score_t(const ScoreArgs& a, hipStream_t s) {
+// Workgroups of this kernel that fit on the device at once (cached per instantiation).
+template <class K>
+static int resident_workgroups(K kernel) {
+  static int cached = 0;
+  if (cached == 0) {
+    int dev = 0, cus = 0, per_cu = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, kScoreThreads, 0) != hipSuccess ||
+        cus <= 0 || per_cu <= 0)
+      return 512;
+    cached = cus * per_cu;
+  }
+  return cached;
+}
+
+template <int MT, int TPW, int DI, bool CAND>
+static hipError_t launch_score_t(const ScoreArgs& a, hipStream_t s, bool persistent) {
   constexpr int per_wg = 4 * 16 * TPW;
-  dim3 grid;
-  if (CAND) grid = dim3((a.n_cand + per_wg - 1) / per_wg, a.T);
-  else grid = dim3((a.max_ctx + per_wg - 1) / per_wg, a.B);
-  if (grid.x == 0 || grid.y == 0) return hipSuccess;
-  hipLaunchKernelGGL((score_kernel<MT, TPW, CAND>), grid, dim3(kScoreThreads), 0, s, a);
+  const int rows = CAND ? a.T : a.B;
+  const int nblk = ((CAND ? a.n_cand : a.max_ctx) + per_wg - 1) / per_wg;
+  // persistent: exactly the workgroups that are resident at once, each looping over
+  // blocks with the next block's keys in flight; otherwise one block per workgroup
+  int gx = nblk;
+  if (persistent) {
+    const int res = resident_workgroups(score_kernel<MT, TPW, DI, CAND>);
+    gx = std::min(nblk, std::max(1, res / std::max(rows, 1)));
+  }
+  if (gx == 0 || rows == 0) return hipSuccess;
+  hipLaunchKernelGGL((score_kernel<MT, TPW, DI, CAND>), dim3(gx, rows), dim3(kScoreThreads), 0, s, a);
   return hipGetLastError();
 }
 
-template <int MT>
+template <int MT, int DI>
 static hipError_t launch_score_mt(const ScoreArgs& a, hipStream_t s) {
   // Small problems use 64 positions per workgroup to spread over more CUs.
   const int64_t cols = a.cand ? (int64_t)a.n_cand * a.T : (int64_t)a.max_ctx * a.B;
   const bool small = cols / 256 < 1024;
-  if (a.cand) return small ? launch_score_t<MT, 1, true>(a, s) : launch_score_t<MT, 4, true>(a, s);
-  return small ? launch_score_t<MT, 1, false>(a, s) : launch_score_t<MT, 4, false>(a, s);
+  if (a.cand) return small ? launch_score_t<MT, 1, DI, true>(a, s, false) : launch_score_t<MT, 4, DI, true>(a, s, true);
+  // Several queries per sequence make a block compute-bound (q is restaged per query), so
+  // every block gets its own workgroup; one query per sequence streams keys persistently.
+  const bool one_query_per_seq = a.T == a.B;
+  return small ? launch_score_t<MT, 1, DI, false>(a, s, false)
+               : launch_score_t<MT, 4, DI, false>(a, s, one_query_per_seq);
+}
+
+template <int DI>
+static hipError_t launch_score_di(const ScoreArgs& a, hipStream_t s) {
+  if (a.Hi <= 16) return launch_score_mt<1, DI>(a, s);
+  if (a.Hi <= 32) return launch_score_mt<2, DI>(a, s);
+  if (a.Hi <= 64) return launch_score_mt<4, DI>(a, s);
+  return launch_score_mt<8, DI>(a, s);
 }
 
 hipError_t launch_score(const ScoreArgs& a, hipStream_t s) {
   if (a.T == 0) return hipSuccess;
-  if (a.Hi <= 16) return launch_score_mt<1>(a, s);
-  if (a.Hi <= 32) return launch_score_mt<2>(a, s);
-  if (a.Hi <= 64) return launch_score_mt<4>(a, s);
-  return launch_score_mt<8>(a, s);
+  return a.Di == 128 ? launch_score_di<128>(a, s) : launch_score_di<64>(a, s);
 }
 
 }  // namespace smqa
