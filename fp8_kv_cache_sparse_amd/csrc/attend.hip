@@ -271,13 +271,16 @@ __global__ __launch_bounds__(kAttThreads) void attend_kernel(AttendArgs a, int S
   const int wave = tid >> 6, lane = tid & 63, g = lane >> 4, n = lane & 15;
   (void)lane;
 
-  // XCD-aware order: consecutive logical blocks (same query) land on one XCD.
+  // XCD-aware order: workgroups are dealt to the 8 XCDs round-robin, so logical block
+  // (bid & 7) * (nb / 8) + (bid >> 3) puts runs of consecutive logical blocks on one XCD.
+  // Head groups vary fastest: the workgroups that gather the same rows (one query, one
+  // tile range, every head group) share that XCD's L2.
   const int nb = gridDim.x;
   const int bid = blockIdx.x;
   const int logical = (bid & 7) * (nb >> 3) + (bid >> 3);
   if (logical >= total) return;
-  const int split = logical % S;
-  const int grp = (logical / S) % ngroups;
+  const int grp = logical % ngroups;
+  const int split = (logical / ngroups) % S;
   const int t = logical / (S * ngroups);
 
   AttCtx c;
