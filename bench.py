@@ -9,9 +9,11 @@ when timing starts).  Metric: context positions scored per second (higher is
 better) and microseconds per step, at 8K context (decode_8k, the primary line)
 and at 512K context (decode_512k, reported alongside).
 
-The step is timed twice: eager (one C-ABI call per step from Python) and as a
-replayed HIP graph of the same call (its outputs checked bitwise against the
-eager step first); ``value`` uses the faster of the two.  Per-stage kernel
+The step is timed three ways: eager (one C-ABI call per step from Python), as a
+replayed HIP graph of one call, and as a replayed graph of 10 consecutive calls
+(the GPU-side steady state of a captured decode, no host work between steps);
+graph outputs are checked bitwise against the eager step first.  ``value`` uses
+the fastest.  Per-stage kernel
 time comes from HIP events around repeated calls of each stage's entry point
 on the same stream.  ``cpu_baseline`` times the fp64 CPU oracle on a bounded
 sample of the same workload.
@@ -205,6 +207,7 @@ def measure(name, steps, warmup, use_graph, stage_only=""):
     eager_s = (time.perf_counter() - t0) / steps
 
     graph_s = None
+    chain_s = None
     graph_ok = None
     if use_graph:
         try:
@@ -235,6 +238,27 @@ def measure(name, steps, warmup, use_graph, stage_only=""):
                     g.replay()
                 torch.cuda.synchronize()
                 graph_s = (time.perf_counter() - t0) / steps
+                # GPU-side steady state: G consecutive steps in one graph, as inside a captured
+                # decode of a whole model (no host work between the steps)
+                G = max(1, min(10, steps))
+                gc = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(gc):
+                    for _ in range(G):
+                        step()
+                torch.cuda.synchronize()
+                out.zero_()
+                gc.replay()
+                torch.cuda.synchronize()
+                graph_ok &= bool(torch.equal(out, ref_out) and torch.equal(lse, ref_lse)
+                                 and torch.equal(idx, ref_idx))
+                reps = max(1, steps // G)
+                print(f"[bench] {name}: graph of {G} steps x{reps}", file=sys.stderr, flush=True)
+                torch.cuda.synchronize()
+                t0 = time.perf_counter()
+                for _ in range(reps):
+                    gc.replay()
+                torch.cuda.synchronize()
+                chain_s = (time.perf_counter() - t0) / (reps * G)
         except Exception as e:  # graph capture unavailable: report eager only
             print(f"[bench] graph capture failed: {e}", file=sys.stderr, flush=True)
             graph_ok = False
@@ -276,12 +300,13 @@ def measure(name, steps, warmup, use_graph, stage_only=""):
             best = e0.elapsed_time(e1)
         st_us[nm] = best * 1e3 / steps
     dom = max(st_us, key=st_us.get)
-    best_s = min(eager_s, graph_s) if graph_s else eager_s
+    best_s = min(x for x in (eager_s, graph_s, chain_s) if x)
     res = {
         "workload": name, "T": wl.T, "B": wl.B, "scored_positions": J,
         "us_per_step": round(best_s * 1e6, 2),
         "us_per_step_eager": round(eager_s * 1e6, 2),
         "us_per_step_graph": None if graph_s is None else round(graph_s * 1e6, 2),
+        "us_per_step_graph_chain": None if chain_s is None else round(chain_s * 1e6, 2),
         "graph_replay_matches_eager": graph_ok,
         "tokens_scored_per_s": J / best_s,
         "stage_us": {k: round(v, 2) for k, v in st_us.items()},

@@ -82,9 +82,6 @@ __device__ __forceinline__ int ncols_of(const TopkArgs& a, int t) {
   return max(0, min(min(a.q_pos[t], len - 1) + 1, a.max_ctx));
 }
 
-__device__ __forceinline__ int pos_of(const TopkArgs& a, int t, int col) {
-  return a.cand ? a.cand[(int64_t)t * a.n_cand + col] : col;
-}
 
 // Inclusive prefix sum over a wave with DPP row shifts and row broadcasts: within each
 // row of 16 lanes by shifts of 1, 2, 4, 8 (lanes shifted in from outside the row read
@@ -274,30 +271,57 @@ __device__ __forceinline__ int wave_append(int* counter, bool flag) {
 }
 
 // Read the selection bitmap (nwords words, bit c = column c) out in column order:
-// dst[i] = position of the i-th selected column, then -1 up to k.
+// dst[i] = position of the i-th selected column, then -1 up to k.  Rounds of NT*PER
+// words: each thread loads its PER consecutive words at once (one memory latency per
+// round), and one block scan of the per-thread counts gives the output offsets.  Dense
+// rows store columns directly; the candidate-list lookup is a separate loop, so the
+// dense stores never wait on a load.
 template <int NT, bool ATOMIC_READ>
 __device__ void write_selection(const TopkArgs& a, int t, const unsigned* bits, int nwords,
                                 int32_t* dst, int* scan_lds) {
-  const int per = (nwords + NT - 1) / NT;
-  const int w0 = threadIdx.x * per, w1 = min(w0 + per, nwords);
-  auto word = [&](int i) -> unsigned {
-    if (ATOMIC_READ) return __hip_atomic_load(bits + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    return bits[i];
-  };
-  int cnt = 0;
-  for (int i = w0; i < w1; ++i) cnt += __popc(word(i));
-  int total;
-  int off = block_exclusive_scan<NT>(cnt, scan_lds, &total);
-  for (int i = w0; i < w1; ++i) {
-    unsigned m = word(i);
-    while (m) {
-      const int bit = __ffs(m) - 1;
-      m &= m - 1;
-      if (off < a.k) dst[off] = pos_of(a, t, 32 * i + bit);
-      ++off;
+  constexpr int PER = 16;
+  int done = 0;
+  for (int r0 = 0; r0 < nwords; r0 += NT * PER) {
+    const int w0 = r0 + threadIdx.x * PER;
+    unsigned wv[PER];
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+      const int i = min(w0 + j, nwords - 1);
+      const unsigned v = ATOMIC_READ ? __hip_atomic_load(bits + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+                                     : bits[i];
+      wv[j] = w0 + j < nwords ? v : 0u;
     }
+    int cnt = 0;
+#pragma unroll
+    for (int j = 0; j < PER; ++j) cnt += __popc(wv[j]);
+    int total;
+    int off = done + block_exclusive_scan<NT>(cnt, scan_lds, &total);
+    if (a.cand) {
+#pragma unroll
+      for (int j = 0; j < PER; ++j) {
+        unsigned m = wv[j];
+        while (m) {
+          const int bit = __ffs(m) - 1;
+          m &= m - 1;
+          if (off < a.k) dst[off] = a.cand[(int64_t)t * a.n_cand + 32 * (w0 + j) + bit];
+          ++off;
+        }
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < PER; ++j) {
+        unsigned m = wv[j];
+        while (m) {
+          const int bit = __ffs(m) - 1;
+          m &= m - 1;
+          if (off < a.k) dst[off] = 32 * (w0 + j) + bit;
+          ++off;
+        }
+      }
+    }
+    done += total;
   }
-  for (int i = min(total, a.k) + threadIdx.x; i < a.k; i += NT) dst[i] = -1;
+  for (int i = min(done, a.k) + threadIdx.x; i < a.k; i += NT) dst[i] = -1;
 }
 
 // ------------------------------------------------------------------ short rows
@@ -427,12 +451,21 @@ __global__ __launch_bounds__(1024) void topk_small_kernel(TopkArgs a) {
   int off = (pre & 0xFFFF) + min(tie_rank, tie_need);
   const int nsel = (total & 0xFFFF) + min(total >> 16, tie_need);
   int32_t* dst = a.idx + (int64_t)t * a.k;
+  // positions first (a candidate list is read before any store), then the stores
+  int pos[PER];
+#pragma unroll
+  for (int u = 0; u < PER; ++u) pos[u] = c0 + u;
+  if (a.cand) {
+#pragma unroll
+    for (int u = 0; u < PER; ++u)
+      if (c0 + u < a.n_cand) pos[u] = a.cand[(int64_t)t * a.n_cand + c0 + u];
+  }
 #pragma unroll
   for (int u = 0; u < PER; ++u) {
     bool sel = key[u] > tau;
     if (key[u] == tau) sel = tie_rank++ < tie_need;
     if (sel) {
-      if (off < a.k) dst[off] = pos_of(a, t, c0 + u);
+      if (off < a.k) dst[off] = pos[u];
       ++off;
     }
   }
