@@ -36,7 +36,7 @@ __device__ __forceinline__ v8bf fp8x8_to_bf16(unsigned w0, unsigned w1) {
 // every negative float (and -0) is a negative int32.
 __device__ __forceinline__ float relu(float x) { return __int_as_float(max(__float_as_int(x), 0)); }
 
-constexpr int kQRow = 144;   // LDS bytes per head row (128 + 16 pad: conflict-free b128 reads)
+constexpr int kQRow = 272;   // LDS bytes per head row of bf16 q (256 + 16 pad: conflict-free b128 reads)
 
 // Raw keys of one block of positions for one lane: TPW tiles x DI/4 bytes.
 template <int TPW, int DI>
@@ -120,6 +120,7 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel(ScoreArgs a) {
     nblk = min(nblk, pmax / kPosPerWG + 1);
   }
 
+  // q of query t staged in LDS as bf16 (E4M3 -> bf16 exact), converted once per query
   auto stage_q = [&](int t) {
     const int pieces_per_row = DI / 16;
     const int total = 16 * MT * pieces_per_row;
@@ -127,7 +128,9 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel(ScoreArgs a) {
       const int h = pc / pieces_per_row, c = pc % pieces_per_row;
       v4u v = {0u, 0u, 0u, 0u};
       if (h < Hi) v = *(const v4u*)(a.q_fp8 + ((int64_t)t * Hi + h) * DI + 16 * c);
-      *(v4u*)(q_lds + h * kQRow + 16 * c) = v;
+      uint8_t* dst = q_lds + h * kQRow + 32 * c;
+      *(v8bf*)dst = fp8x8_to_bf16(v.x, v.y);
+      *(v8bf*)(dst + 16) = fp8x8_to_bf16(v.z, v.w);
     }
     if (tid < 16 * MT) w_lds[tid] = tid < Hi ? a.w[(int64_t)t * Hi + tid] : 0.0f;
   };
@@ -177,13 +180,9 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel(ScoreArgs a) {
           v8bf qa[NKS];
           float wr[4];
           {
-            const uint8_t* src = q_lds + (16 * mt + n) * kQRow + g * (DI / 4);
-            const v4u lo = *(const v4u*)src;
-            v4u hi = {0u, 0u, 0u, 0u};
-            if (DI == 128) hi = *(const v4u*)(src + 16);
-            const unsigned wds[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+            const uint8_t* src = q_lds + (16 * mt + n) * kQRow + 2 * g * (DI / 4);
 #pragma unroll
-            for (int s2 = 0; s2 < NKS; ++s2) qa[s2] = fp8x8_to_bf16(wds[2 * s2], wds[2 * s2 + 1]);
+            for (int s2 = 0; s2 < NKS; ++s2) qa[s2] = *(const v8bf*)(src + 16 * s2);
 #pragma unroll
             for (int r = 0; r < 4; ++r) wr[r] = w_lds[16 * mt + 4 * g + r];
           }
