@@ -224,6 +224,152 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel(ScoreArgs a) {
   for (; blk < nblk; blk += gridDim.x) score_block(raw);
 }
 
+// Buffer resource over [base, base + bytes): loads past the end return zeros without a
+// memory access and stores past it are dropped, so the streaming loop below issues every
+// load and store unconditionally (no branch, hence no conservative wait at a join).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t range_rsrc(const void* base, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes, 0x00020000);
+}
+
+// Dense scoring when each query streams its sequence's keys once (decode: one query per
+// sequence).  Same contraction as score_kernel; the difference is how HBM is kept busy:
+//  * q (bf16) and the head weights stay in registers for the whole stream;
+//  * each wave owns a two-block ring of raw keys, and a tile's registers are refilled with
+//    the tile two blocks ahead as soon as they are converted, so about two blocks of
+//    loads per wave are always in flight;
+//  * bounds come from the buffer resources (positions >= min(len, p + 1) read as zero
+//    and are never stored);
+//  * the four 16-position tiles of a block are reduced over the lane groups with one
+//    reduce-scatter (two permlane32 swaps, one permlane16 swap), after which lane l holds
+//    position 64 * wave + l, so kappa is one load and the block's scores one store.
+// Lane (g, n) of tile i holds key bytes [16g, 16g + 16) and [64 + 16g, 64 + 16g + 16) of
+// position 16i + n; q uses the same byte -> k assignment.
+template <int MT, int DI>
+__global__ __launch_bounds__(kScoreThreads) void score_stream_kernel(ScoreArgs a) {
+  __shared__ __align__(16) uint8_t q_lds[16 * MT * kQRow];
+  __shared__ float w_lds[16 * MT];
+  constexpr int TPW = 4, NKS = DI / 32, NH = DI / 64;
+  constexpr int kPosPerWG = 4 * 16 * TPW;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, g = lane >> 4, n = lane & 15;
+  const int b = blockIdx.y, G = gridDim.x;
+  const int t0 = a.q_start[b], t1 = a.q_start[b + 1];
+  const int64_t base = a.seq_start[b];
+  const int len = (int)(a.seq_start[b + 1] - base);
+  const bool has_scale = a.k_scale != nullptr;
+
+  struct Slot {
+    v4u k[TPW][NH];
+    float kap;
+  };
+
+  for (int t = t0; t < t1; ++t) {
+    const int p = __builtin_amdgcn_readfirstlane(a.q_pos[t]);
+    const int nvalid = min(len, p + 1);
+    const int nblk = (nvalid + kPosPerWG - 1) / kPosPerWG;
+    if ((int)blockIdx.x >= nblk) continue;
+
+    __syncthreads();   // the previous query's q is no longer read
+    for (int pc = tid; pc < 16 * MT * (DI / 16); pc += kScoreThreads) {
+      const int h = pc / (DI / 16), c = pc % (DI / 16);
+      v4u v = {0u, 0u, 0u, 0u};
+      if (h < a.Hi) v = *(const v4u*)(a.q_fp8 + ((int64_t)t * a.Hi + h) * DI + 16 * c);
+      uint8_t* dst = q_lds + h * kQRow + 32 * c;
+      *(v8bf*)dst = fp8x8_to_bf16(v.x, v.y);
+      *(v8bf*)(dst + 16) = fp8x8_to_bf16(v.z, v.w);
+    }
+    if (tid < 16 * MT) w_lds[tid] = tid < a.Hi ? a.w[(int64_t)t * a.Hi + tid] : 0.0f;
+    __syncthreads();
+    v8bf qa[MT][NKS];
+    float wr[MT][4];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+#pragma unroll
+      for (int s2 = 0; s2 < NKS; ++s2)
+        qa[mt][s2] = *(const v8bf*)(q_lds + (16 * mt + n) * kQRow + 2 * (64 * (s2 >> 1) + 16 * g + 8 * (s2 & 1)));
+#pragma unroll
+      for (int r = 0; r < 4; ++r) wr[mt][r] = w_lds[16 * mt + 4 * g + r];
+    }
+
+    const __amdgpu_buffer_rsrc_t kr = range_rsrc(a.k_fp8 + base * DI, nvalid * DI);
+    const __amdgpu_buffer_rsrc_t sr = range_rsrc(has_scale ? (const void*)(a.k_scale + base) : (const void*)a.k_fp8,
+                                                 has_scale ? nvalid * 4 : 0);
+    const __amdgpu_buffer_rsrc_t orr = range_rsrc(a.scores + (int64_t)t * a.ld, nvalid * 4);
+    const int koff = (wave * 64 + n) * DI + 16 * g;
+    const int poff = (wave * 64 + lane) * 4;
+
+    auto load_tile = [&](Slot& s, int bk, int i) {
+#pragma unroll
+      for (int h = 0; h < NH; ++h)
+        s.k[i][h] = __builtin_amdgcn_raw_buffer_load_b128(kr, (bk * kPosPerWG + 16 * i) * DI + koff + 64 * h, 0, 0);
+    };
+    auto load_kap = [&](Slot& s, int bk) {
+      s.kap = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(sr, bk * kPosPerWG * 4 + poff, 0, 0));
+    };
+    // Score block bk from s, refilling s with block nbk tile by tile.
+    auto run = [&](Slot& s, int bk, int nbk) {
+      float part[TPW];
+#pragma unroll
+      for (int i = 0; i < TPW; ++i) {
+        v8bf kb[NKS];
+#pragma unroll
+        for (int h = 0; h < NH; ++h) {
+          kb[2 * h] = fp8x8_to_bf16(s.k[i][h].x, s.k[i][h].y);
+          kb[2 * h + 1] = fp8x8_to_bf16(s.k[i][h].z, s.k[i][h].w);
+        }
+        load_tile(s, nbk, i);
+        v4f acc[MT];
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) acc[mt] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int s2 = 0; s2 < NKS; ++s2)
+#pragma unroll
+          for (int mt = 0; mt < MT; ++mt)
+            acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[mt][s2], kb[s2], acc[mt], 0, 0, 0);
+        float sm = 0.0f;
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) sm += wr[mt][r] * relu(acc[mt][r]);
+        part[i] = sm;
+      }
+      // reduce-scatter over the lane groups g: lane (g, n) ends with tile g's head sum
+      const auto x02 = __builtin_amdgcn_permlane32_swap(__float_as_uint(part[0]), __float_as_uint(part[2]), false, false);
+      const auto x13 = __builtin_amdgcn_permlane32_swap(__float_as_uint(part[1]), __float_as_uint(part[3]), false, false);
+      const float u = __uint_as_float(x02[0]) + __uint_as_float(x02[1]);
+      const float v = __uint_as_float(x13[0]) + __uint_as_float(x13[1]);
+      const auto y = __builtin_amdgcn_permlane16_swap(__float_as_uint(u), __float_as_uint(v), false, false);
+      const float tot = __uint_as_float(y[0]) + __uint_as_float(y[1]);
+      const float kap = has_scale ? s.kap : 1.0f;
+      load_kap(s, nbk);
+      __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(tot * kap), orr, bk * kPosPerWG * 4 + poff, 0, 0);
+    };
+
+    // Issue order matters: the loop consumes tiles in this order and waits on the count of
+    // loads issued after each one, so the scheduler may not reorder the prologue's loads.
+    int blk = blockIdx.x;
+    Slot r0, r1;
+#pragma unroll
+    for (int i = 0; i < TPW; ++i) {
+      load_tile(r0, blk, i);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    load_kap(r0, blk);
+#pragma unroll
+    for (int i = 0; i < TPW; ++i) {
+      __builtin_amdgcn_sched_barrier(0);
+      load_tile(r1, blk + G, i);
+    }
+    load_kap(r1, blk + G);
+    __builtin_amdgcn_sched_barrier(0);
+    for (; blk < nblk; blk += 2 * G) {
+      run(r0, blk, blk + 2 * G);
+      __builtin_amdgcn_sched_barrier(0);   // no conversion of r1 hoisted into r0's half
+      run(r1, blk + G, blk + 3 * G);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+}
+
 // Workgroups of this kernel that fit on the device at once (cached per instantiation).
 template <class K>
 static int resident_workgroups(K kernel) {
@@ -266,8 +412,19 @@ static hipError_t launch_score_mt(const ScoreArgs& a, hipStream_t s) {
   // Several queries per sequence make a block compute-bound (q is restaged per query), so
   // every block gets its own workgroup; one query per sequence streams keys persistently.
   const bool one_query_per_seq = a.T == a.B;
-  return small ? launch_score_t<MT, 1, DI, false>(a, s, false)
-               : launch_score_t<MT, 4, DI, false>(a, s, one_query_per_seq);
+  if (small) return launch_score_t<MT, 1, DI, false>(a, s, false);
+  if (one_query_per_seq && MT <= 4) {
+    const int per_wg = 4 * 16 * 4;
+    const int nblk = (a.max_ctx + per_wg - 1) / per_wg;
+    const int res = resident_workgroups(score_stream_kernel<MT <= 4 ? MT : 4, DI>);
+    const int gx = std::min(nblk, std::max(1, res / std::max(a.B, 1)));
+    // buffer offsets are 32-bit: every block the ring touches must stay below 2^31 bytes
+    if ((int64_t)(nblk + 4 * (int64_t)gx) * per_wg * DI < ((int64_t)1 << 31)) {
+      hipLaunchKernelGGL((score_stream_kernel<MT <= 4 ? MT : 4, DI>), dim3(gx, a.B), dim3(kScoreThreads), 0, s, a);
+      return hipGetLastError();
+    }
+  }
+  return launch_score_t<MT, 4, DI, false>(a, s, one_query_per_seq);
 }
 
 template <int DI>

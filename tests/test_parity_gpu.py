@@ -53,6 +53,51 @@ def test_score_dense(lib, name, kw):
         assert ok, f"query {t}: {msg}"
 
 
+# Long single-query-per-sequence rows take the streaming kernel (keys read once, two
+# blocks in flight per wave): every head-slice count it is built for, both key widths,
+# with and without key scales, ragged lengths that end mid-block.
+@pytest.mark.parametrize("Hi,Di,scaled", [(64, 128, True), (20, 64, False), (16, 128, False),
+                                          (48, 64, True)])
+def test_score_dense_streaming(lib, Hi, Di, scaled):
+    wl = gen("decode_8k", B=2, lengths=(131001, 160000), Hi=Hi, Di=Di)
+    if scaled:
+        wl = synth.with_scales(wl)
+    announce(f"score streaming Hi={Hi} Di={Di} lengths={wl.seq_start.tolist()}")
+    S = gpu_score(lib, wl)
+    sync()
+    a = np_inputs(wl)
+    S_ref = ref.score(a["qI"], a["w"], a["kI"], a["kscale"], a["seq_start"], a["q_start"], a["q_pos"],
+                      ld=wl.max_ctx)
+    S_gpu = S.cpu().numpy().astype(np.float64)
+    S_gpu[S_ref == -np.inf] = -np.inf
+    for t in range(wl.T):
+        ok, msg = close_scores(S_gpu[t], S_ref[t])
+        assert ok, f"query {t}: {msg}"
+
+
+def test_score_dense_streaming_uneven_queries(lib):
+    """As many queries as sequences, but two on one sequence (one mid-sequence) and none on
+    the other: the streaming kernel re-streams the keys per query and scores only j <= p."""
+    import dataclasses
+    wl = gen("decode_8k", B=2, lengths=150000)
+    n0 = int(wl.seq_start[1])
+    q_start = torch.tensor([0, 2, 2], dtype=torch.int32, device=DEV)
+    q_pos = torch.tensor([n0 - 1, 70001], dtype=torch.int32, device=DEV)
+    wl = dataclasses.replace(wl, q_start=q_start, q_pos=q_pos, max_ctx=n0)
+    announce("score streaming uneven queries")
+    S = gpu_score(lib, wl)
+    sync()
+    a = np_inputs(wl)
+    S_ref = ref.score(a["qI"], a["w"], a["kI"], a["kscale"], a["seq_start"], a["q_start"], a["q_pos"],
+                      ld=wl.max_ctx)
+    S_gpu = S.cpu().numpy().astype(np.float64)
+    assert np.isfinite(S_gpu[1, :70002]).all()
+    S_gpu[S_ref == -np.inf] = -np.inf
+    for t in range(wl.T):
+        ok, msg = close_scores(S_gpu[t], S_ref[t])
+        assert ok, f"query {t}: {msg}"
+
+
 def test_score_integer_inputs_bit_exact(lib):
     announce("score integer-valued inputs")
     g = torch.Generator(device=DEV).manual_seed(5)
