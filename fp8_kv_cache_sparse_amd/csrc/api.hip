@@ -189,7 +189,8 @@ int sparse_mqa_score(const smqa_layout* L, const uint8_t* q_fp8, const float* w,
   st = check_score(L, q_fp8, w, k_fp8, k_scale, cand, n_cand, Hi, Di, scores, ld_scores, true);
   if (st) return st;
   smqa::ScoreArgs a{L->seq_start, L->q_start, L->q_pos, L->num_seqs, L->num_q, L->max_ctx,
-                    q_fp8, w, k_fp8, k_scale, cand, cand ? n_cand : 0, Hi, Di, scores, ld_scores};
+                    q_fp8, w, k_fp8, k_scale, cand, cand ? n_cand : 0, Hi, Di, scores, ld_scores,
+                    nullptr};
   hipError_t e = smqa::launch_score(a, (hipStream_t)stream);
   return e == hipSuccess ? SMQA_OK : hip_fail(e, "sparse_mqa_score launch");
 }
@@ -260,12 +261,19 @@ int decode_step(const smqa_layout* L, const uint8_t* q_fp8, const float* w, cons
   int32_t* idx = idx_out ? idx_out : (int32_t*)(ws + d.idx_off);
   hipStream_t s = (hipStream_t)stream;
   smqa::ScoreArgs sa{L->seq_start, L->q_start, L->q_pos, L->num_seqs, L->num_q, L->max_ctx,
-                     q_fp8, w, k_fp8, k_scale, cand, cand ? n_cand : 0, Hi, Di, scores, cols};
-  hipError_t e = smqa::launch_score(sa, s);
-  if (e != hipSuccess) return hip_fail(e, "decode_step score launch");
+                     q_fp8, w, k_fp8, k_scale, cand, cand ? n_cand : 0, Hi, Di, scores, cols,
+                     nullptr};
   smqa::TopkArgs ta{L->seq_start, L->q_start, L->q_pos, L->num_seqs, L->num_q, cols,
                     scores, cols, cand, cand ? n_cand : 0, k, idx, ws + d.topk_off};
-  e = smqa::launch_topk(ta, s);
+  // When the streaming score kernel runs, it also builds the top-k's first-digit histogram.
+  hipError_t e = hipSuccess;
+  if (smqa::score_streams(sa)) {
+    e = smqa::launch_topk_prepare(ta, s, &sa.hist);
+    if (e != hipSuccess) return hip_fail(e, "decode_step topk launch");
+  }
+  e = smqa::launch_score(sa, s);
+  if (e != hipSuccess) return hip_fail(e, "decode_step score launch");
+  e = sa.hist ? smqa::launch_topk_from_hist(ta, s) : smqa::launch_topk(ta, s);
   if (e != hipSuccess) return hip_fail(e, "decode_step topk launch");
   smqa::AttendArgs aa{L->seq_start, L->q_start, L->q_pos, L->num_seqs, L->num_q, q_bf16, kv_codes,
                       kv_e8m0, kv_rowscale, idx, k, swa_fp8, swa_scale, swa_pos0, swa_clip, W, Hq, D,

@@ -62,8 +62,15 @@ struct ScoreArgs {
   int32_t Hi, Di;
   float* scores;
   int64_t ld;
+  // Optional (streaming kernel only): [T][kTopkBins] counts of the top 12 key bits of every
+  // scored position (score_key(s) >> 20), added with device atomics to a zeroed array.
+  unsigned* hist;
 };
 hipError_t launch_score(const ScoreArgs& a, hipStream_t s);
+// True when launch_score takes the streaming kernel, the one that can fill ScoreArgs::hist.
+bool score_streams(const ScoreArgs& a);
+
+constexpr int kTopkBins = 4096;   // top-k first digit: the top 12 bits of the order key
 
 struct TopkArgs {
   const int64_t* seq_start;
@@ -80,6 +87,11 @@ struct TopkArgs {
 };
 size_t topk_workspace_bytes(int32_t T, int32_t max_ctx, int32_t k);
 hipError_t launch_topk(const TopkArgs& a, hipStream_t s);
+// Split form for a producer that builds the first-digit histogram itself: prepare zeroes the
+// workspace state and returns the [T][kTopkBins] histogram to fill (nullptr when the rows are
+// short and the single-kernel path needs none); finish runs the rest of the selection.
+hipError_t launch_topk_prepare(const TopkArgs& a, hipStream_t s, unsigned** hist);
+hipError_t launch_topk_from_hist(const TopkArgs& a, hipStream_t s);
 
 struct AttendArgs {
   const int64_t* seq_start;

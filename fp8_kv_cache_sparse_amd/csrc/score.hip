@@ -241,13 +241,18 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t range_rsrc(const void* base, i
 //    and are never stored);
 //  * the four 16-position tiles of a block are reduced over the lane groups with one
 //    reduce-scatter (two permlane32 swaps, one permlane16 swap), after which lane l holds
-//    position 64 * wave + l, so kappa is one load and the block's scores one store.
+//    position 64 * wave + l, so kappa is one load and the block's scores one store;
+//  * HIST: each score's top-k order key also goes into an LDS histogram of its top 12
+//    bits (one LDS atomic per lane per block), whose nonzero bins are added to the
+//    query's global histogram when the stream ends, so the top-k needs no pass of its own
+//    to find the first digit.
 // Lane (g, n) of tile i holds key bytes [16g, 16g + 16) and [64 + 16g, 64 + 16g + 16) of
 // position 16i + n; q uses the same byte -> k assignment.
-template <int MT, int DI>
+template <int MT, int DI, bool HIST>
 __global__ __launch_bounds__(kScoreThreads) void score_stream_kernel(ScoreArgs a) {
   __shared__ __align__(16) uint8_t q_lds[16 * MT * kQRow];
   __shared__ float w_lds[16 * MT];
+  __shared__ unsigned khist[HIST ? kTopkBins : 1];
   constexpr int TPW = 4, NKS = DI / 32, NH = DI / 64;
   constexpr int kPosPerWG = 4 * 16 * TPW;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, g = lane >> 4, n = lane & 15;
@@ -264,11 +269,15 @@ __global__ __launch_bounds__(kScoreThreads) void score_stream_kernel(ScoreArgs a
 
   for (int t = t0; t < t1; ++t) {
     const int p = __builtin_amdgcn_readfirstlane(a.q_pos[t]);
-    const int nvalid = min(len, p + 1);
+    // (readfirstlane: keeps the compiler from treating the buffer resources built from it
+    // as divergent, which would wrap every load in a waterfall loop)
+    const int nvalid = __builtin_amdgcn_readfirstlane(min(min(len, p + 1), a.max_ctx));
     const int nblk = (nvalid + kPosPerWG - 1) / kPosPerWG;
     if ((int)blockIdx.x >= nblk) continue;
 
-    __syncthreads();   // the previous query's q is no longer read
+    __syncthreads();   // the previous query's q and histogram are no longer read
+    if (HIST)
+      for (int i = tid; i < kTopkBins; i += kScoreThreads) khist[i] = 0u;
     for (int pc = tid; pc < 16 * MT * (DI / 16); pc += kScoreThreads) {
       const int h = pc / (DI / 16), c = pc % (DI / 16);
       v4u v = {0u, 0u, 0u, 0u};
@@ -341,7 +350,12 @@ __global__ __launch_bounds__(kScoreThreads) void score_stream_kernel(ScoreArgs a
       const float tot = __uint_as_float(y[0]) + __uint_as_float(y[1]);
       const float kap = has_scale ? s.kap : 1.0f;
       load_kap(s, nbk);
-      __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(tot * kap), orr, bk * kPosPerWG * 4 + poff, 0, 0);
+      const float sc = tot * kap;
+      __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(sc), orr, bk * kPosPerWG * 4 + poff, 0, 0);
+      if (HIST) {   // positions past the row count in bin 0, which the top-k ignores
+        const unsigned key = bk * kPosPerWG + wave * 64 + lane < nvalid ? score_key(sc) : 0u;
+        atomicAdd(&khist[key >> 20], 1u);
+      }
     };
 
     // Issue order matters: the loop consumes tiles in this order and waits on the count of
@@ -366,6 +380,14 @@ __global__ __launch_bounds__(kScoreThreads) void score_stream_kernel(ScoreArgs a
       __builtin_amdgcn_sched_barrier(0);   // no conversion of r1 hoisted into r0's half
       run(r1, blk + G, blk + 3 * G);
       __builtin_amdgcn_sched_barrier(0);
+    }
+    if (HIST) {
+      __syncthreads();
+      unsigned* gh = a.hist + (int64_t)t * kTopkBins;
+      for (int i = tid; i < kTopkBins; i += kScoreThreads) {
+        const unsigned c = khist[i];
+        if (i > 0 && c) atomicAdd(&gh[i], c);
+      }
     }
   }
 }
@@ -403,26 +425,51 @@ static hipError_t launch_score_t(const ScoreArgs& a, hipStream_t s, bool persist
   return hipGetLastError();
 }
 
+// Problems of fewer than 1024 blocks of 256 positions use 64 positions per workgroup to
+// spread over more CUs.
+static bool small_problem(const ScoreArgs& a) {
+  const int64_t cols = a.cand ? (int64_t)a.n_cand * a.T : (int64_t)a.max_ctx * a.B;
+  return cols / 256 < 1024;
+}
+
+// Whether the streaming kernel applies, and its grid width (workgroups per sequence):
+// resident workgroups shared over the sequences, at most kMaxStreamGrid, so that every block
+// the key ring touches (up to 4 grid strides past the row) has a 32-bit buffer offset.
+constexpr int kMaxStreamGrid = 2048;
+
+static bool stream_applies(const ScoreArgs& a) {
+  if (a.T == 0 || a.cand || a.T != a.B || a.Hi > 64 || small_problem(a)) return false;
+  const int per_wg = 4 * 16 * 4;
+  const int64_t nblk = (a.max_ctx + per_wg - 1) / per_wg;
+  return (nblk + 4 * (int64_t)kMaxStreamGrid) * per_wg * a.Di < ((int64_t)1 << 31);
+}
+
+static int stream_grid(const ScoreArgs& a, int resident) {
+  const int per_wg = 4 * 16 * 4;
+  const int nblk = (a.max_ctx + per_wg - 1) / per_wg;
+  return std::min(std::min(nblk, kMaxStreamGrid), std::max(1, resident / std::max(a.B, 1)));
+}
+
+bool score_streams(const ScoreArgs& a) { return stream_applies(a); }
+
 template <int MT, int DI>
 static hipError_t launch_score_mt(const ScoreArgs& a, hipStream_t s) {
-  // Small problems use 64 positions per workgroup to spread over more CUs.
-  const int64_t cols = a.cand ? (int64_t)a.n_cand * a.T : (int64_t)a.max_ctx * a.B;
-  const bool small = cols / 256 < 1024;
+  const bool small = small_problem(a);
   if (a.cand) return small ? launch_score_t<MT, 1, DI, true>(a, s, false) : launch_score_t<MT, 4, DI, true>(a, s, true);
   // Several queries per sequence make a block compute-bound (q is restaged per query), so
   // every block gets its own workgroup; one query per sequence streams keys persistently.
   const bool one_query_per_seq = a.T == a.B;
   if (small) return launch_score_t<MT, 1, DI, false>(a, s, false);
-  if (one_query_per_seq && MT <= 4) {
-    const int per_wg = 4 * 16 * 4;
-    const int nblk = (a.max_ctx + per_wg - 1) / per_wg;
-    const int res = resident_workgroups(score_stream_kernel<MT <= 4 ? MT : 4, DI>);
-    const int gx = std::min(nblk, std::max(1, res / std::max(a.B, 1)));
-    // buffer offsets are 32-bit: every block the ring touches must stay below 2^31 bytes
-    if ((int64_t)(nblk + 4 * (int64_t)gx) * per_wg * DI < ((int64_t)1 << 31)) {
-      hipLaunchKernelGGL((score_stream_kernel<MT <= 4 ? MT : 4, DI>), dim3(gx, a.B), dim3(kScoreThreads), 0, s, a);
-      return hipGetLastError();
+  if (stream_applies(a)) {
+    constexpr int M = MT <= 4 ? MT : 4;
+    if (a.hist) {
+      const int gx = stream_grid(a, resident_workgroups(score_stream_kernel<M, DI, true>));
+      hipLaunchKernelGGL((score_stream_kernel<M, DI, true>), dim3(gx, a.B), dim3(kScoreThreads), 0, s, a);
+    } else {
+      const int gx = stream_grid(a, resident_workgroups(score_stream_kernel<M, DI, false>));
+      hipLaunchKernelGGL((score_stream_kernel<M, DI, false>), dim3(gx, a.B), dim3(kScoreThreads), 0, s, a);
     }
+    return hipGetLastError();
   }
   return launch_score_t<MT, 4, DI, false>(a, s, one_query_per_seq);
 }

@@ -18,7 +18,9 @@
 // entry above d1 selected) with wave ballots and append the entries of bin d1 to
 // a candidate list; (3) one workgroup per query finishes the select inside d1
 // (from LDS, or by re-reading the row when d1 holds more than kCap entries),
-// sets those bits, and reads the bitmap out in order.
+// sets those bits, and reads the bitmap out in order.  When the producer of the
+// scores already built the histogram (the streaming score kernel), step (1) is
+// skipped and every step-(2) workgroup finds d1 from the histogram itself.
 #include "common.h"
 
 namespace smqa {
@@ -26,7 +28,7 @@ namespace smqa {
 constexpr int kSmallN = 16384;
 constexpr int kChunk = 4096;          // columns per workgroup in the long-row kernels
 constexpr int kCap = 12288;           // candidate-list capacity per query (entries of bin d1)
-constexpr int kHistBins = 4096;
+constexpr int kHistBins = kTopkBins;
 
 struct TopkState {
   int d1;        // threshold bin of the top 12 key bits; -1: every valid entry is selected
@@ -483,6 +485,19 @@ __global__ void topk_zero_kernel(unsigned* p, size_t n_words) {
 constexpr int kLongThreads = 256;
 constexpr int kPerThread = kChunk / kLongThreads;
 
+struct Threshold {
+  int d1, above, cnt1;
+};
+
+// From the first-digit histogram (in LDS) of a row with nvalid scored entries: the bin d1
+// holding the k-th entry, the count above it and its own count (d1 = -1: all are taken).
+template <int NT>
+__device__ Threshold find_threshold(const unsigned* hist, int nvalid, int k, int* scan_lds, int* sh) {
+  if (nvalid <= k) return Threshold{-1, nvalid, 0};
+  block_find_digit<NT>(hist, kHistBins, k, scan_lds, sh);
+  return Threshold{sh[0], sh[1], (int)hist[sh[0]]};
+}
+
 __global__ __launch_bounds__(kLongThreads) void topk_hist_kernel(TopkArgs a, TopkWs w) {
   constexpr int NT = kLongThreads;
   __shared__ unsigned hist[kHistBins];
@@ -530,32 +545,29 @@ __global__ __launch_bounds__(kLongThreads) void topk_hist_kernel(TopkArgs a, Top
     hist[i] = __hip_atomic_load(&gh[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   const int nvalid = __hip_atomic_load(&w.st[t].nvalid, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   __syncthreads();
-  if (nvalid <= a.k) {
-    if (threadIdx.x == 0) {
-      w.st[t].d1 = -1;
-      w.st[t].above = nvalid;
-      w.st[t].cnt1 = 0;
-    }
-    return;
-  }
-  block_find_digit<NT>(hist, kHistBins, a.k, scan_lds, sh);
+  const Threshold th = find_threshold<NT>(hist, nvalid, a.k, scan_lds, sh);
   if (threadIdx.x == 0) {
-    w.st[t].d1 = sh[0];
-    w.st[t].above = sh[1];
-    w.st[t].cnt1 = (int)hist[sh[0]];
+    w.st[t].d1 = th.d1;
+    w.st[t].above = th.above;
+    w.st[t].cnt1 = th.cnt1;
   }
 }
 
+// FROM_HIST: the histogram was filled by the score producer; each workgroup reads it (16 KB,
+// coherent loads issued with the row loads) and finds d1 itself, and the query's first
+// chunk publishes it for the finish kernel.  Otherwise d1 comes from the histogram kernel.
+template <bool FROM_HIST>
 __global__ __launch_bounds__(kLongThreads) void topk_collect_kernel(TopkArgs a, TopkWs w) {
   constexpr int NT = kLongThreads;
   __shared__ uint2 buf[kChunk];
+  __shared__ unsigned hist[FROM_HIST ? kHistBins : 1];
+  __shared__ int scan_lds[NT / 64];
+  __shared__ int sh[4];
   __shared__ int nbuf, gbase;
   const int t = blockIdx.y;
   const int ncols = ncols_of(a, t);
   const int c0 = blockIdx.x * kChunk;
   if (c0 >= ncols) return;
-  const int d1 = w.st[t].d1;
-  const bool keep_bin = d1 >= 0 && w.st[t].cnt1 <= kCap;
   const float* row = a.scores + (int64_t)t * a.ld;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   // wave `wave`, step u covers columns c0 + 64*(wave + 4u) + lane
@@ -565,6 +577,38 @@ __global__ __launch_bounds__(kLongThreads) void topk_collect_kernel(TopkArgs a, 
     const int i = c0 + 64 * (wave + 4 * u) + lane;
     v[u] = i < ncols ? row[i] : -__builtin_inff();
   }
+  int d1, cnt1;
+  if (FROM_HIST) {
+    constexpr int PER = kHistBins / NT;
+    const unsigned* gh = w.hist + (size_t)t * kHistBins;
+    unsigned hv[PER];
+#pragma unroll
+    for (int j = 0; j < PER; ++j)
+      hv[j] = __hip_atomic_load(&gh[threadIdx.x + NT * j], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    int cnt = 0;
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+      const int bin = threadIdx.x + NT * j;
+      const unsigned c = bin == 0 ? 0u : hv[j];     // bin 0 holds only key 0 (not scored)
+      hist[bin] = c;
+      cnt += (int)c;
+    }
+    int nvalid;
+    block_exclusive_scan<NT>(cnt, scan_lds, &nvalid);
+    const Threshold th = find_threshold<NT>(hist, nvalid, a.k, scan_lds, sh);
+    d1 = th.d1;
+    cnt1 = th.cnt1;
+    if (blockIdx.x == 0 && threadIdx.x == 0) {
+      w.st[t].d1 = th.d1;
+      w.st[t].above = th.above;
+      w.st[t].cnt1 = th.cnt1;
+      w.st[t].nvalid = nvalid;
+    }
+  } else {
+    d1 = w.st[t].d1;
+    cnt1 = w.st[t].cnt1;
+  }
+  const bool keep_bin = d1 >= 0 && cnt1 <= kCap;
   if (threadIdx.x == 0) nbuf = 0;
   __syncthreads();
   unsigned* bits = w.bits + (size_t)t * w.bw;
@@ -664,13 +708,35 @@ hipError_t launch_topk(const TopkArgs& a, hipStream_t s) {
     hipLaunchKernelGGL(topk_small_kernel, dim3(a.T), dim3(1024), 0, s, a);
     return hipGetLastError();
   }
+  unsigned* hist = nullptr;
+  hipError_t e = launch_topk_prepare(a, s, &hist);
+  if (e != hipSuccess) return e;
   TopkWs w = carve(a.ws, a.T, a.max_ctx);
+  const int nch = (a.max_ctx + kChunk - 1) / kChunk;
+  hipLaunchKernelGGL(topk_hist_kernel, dim3(nch, a.T), dim3(kLongThreads), 0, s, a, w);
+  hipLaunchKernelGGL(topk_collect_kernel<false>, dim3(nch, a.T), dim3(kLongThreads), 0, s, a, w);
+  hipLaunchKernelGGL(topk_finish_kernel, dim3(a.T), dim3(1024), 0, s, a, w);
+  return hipGetLastError();
+}
+
+hipError_t launch_topk_prepare(const TopkArgs& a, hipStream_t s, unsigned** hist) {
+  *hist = nullptr;
+  if (a.T == 0 || a.max_ctx <= kSmallN) return hipSuccess;
+  TopkWs w = carve(a.ws, a.T, a.max_ctx);
+  // histogram and per-query state (counters start at zero)
   const size_t zero_words = ((char*)w.cand - (char*)w.hist) / 4;
   const int zblocks = (int)std::min<size_t>((zero_words + 1023) / 1024, 2048);
   hipLaunchKernelGGL(topk_zero_kernel, dim3(zblocks), dim3(256), 0, s, w.hist, zero_words);
+  *hist = w.hist;
+  return hipGetLastError();
+}
+
+hipError_t launch_topk_from_hist(const TopkArgs& a, hipStream_t s) {
+  if (a.T == 0) return hipSuccess;
+  if (a.max_ctx <= kSmallN) return launch_topk(a, s);
+  TopkWs w = carve(a.ws, a.T, a.max_ctx);
   const int nch = (a.max_ctx + kChunk - 1) / kChunk;
-  hipLaunchKernelGGL(topk_hist_kernel, dim3(nch, a.T), dim3(kLongThreads), 0, s, a, w);
-  hipLaunchKernelGGL(topk_collect_kernel, dim3(nch, a.T), dim3(kLongThreads), 0, s, a, w);
+  hipLaunchKernelGGL(topk_collect_kernel<true>, dim3(nch, a.T), dim3(kLongThreads), 0, s, a, w);
   hipLaunchKernelGGL(topk_finish_kernel, dim3(a.T), dim3(1024), 0, s, a, w);
   return hipGetLastError();
 }

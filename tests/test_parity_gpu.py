@@ -286,6 +286,32 @@ def test_decode_step(lib, name, kw):
     _decode_check(lib, gen(name, **kw))
 
 
+# Long single-query rows: the streaming score kernel also builds the top-k's first-digit
+# histogram, and the top-k skips its own histogram pass.
+def _with_queries(wl, q_start, q_pos):
+    import dataclasses
+    qs = torch.tensor(q_start, dtype=torch.int32, device=DEV)
+    qp = torch.tensor(q_pos, dtype=torch.int32, device=DEV)
+    T = len(q_pos)
+    assert T == wl.T, "the helper keeps the per-query tensors, so T must not change"
+    return dataclasses.replace(wl, q_start=qs, q_pos=qp, max_ctx=int(max(q_pos)) + 1)
+
+
+def test_decode_step_streaming_histogram(lib):
+    _decode_check(lib, gen("decode_512k", B=2, lengths=(140000, 160000)))
+
+
+def test_decode_step_streaming_short_query(lib):
+    """One query sees fewer positions than k (everything scored is selected)."""
+    wl = gen("decode_512k", B=2, lengths=150000)
+    _decode_check(lib, _with_queries(wl, [0, 1, 2], [149999, 1500]))
+
+
+def test_decode_step_streaming_two_queries_one_sequence(lib):
+    wl = gen("decode_512k", B=2, lengths=150000)
+    _decode_check(lib, _with_queries(wl, [0, 2, 2], [149999, 90001]))
+
+
 def test_decode_step_candidates(lib):
     _decode_check(lib, gen("decode_512k", B=2, lengths=60000, n_cand=16384))
 
