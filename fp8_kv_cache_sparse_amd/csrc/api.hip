@@ -190,7 +190,7 @@ int sparse_mqa_score(const smqa_layout* L, const uint8_t* q_fp8, const float* w,
   if (st) return st;
   smqa::ScoreArgs a{L->seq_start, L->q_start, L->q_pos, L->num_seqs, L->num_q, L->max_ctx,
                     q_fp8, w, k_fp8, k_scale, cand, cand ? n_cand : 0, Hi, Di, scores, ld_scores,
-                    nullptr};
+                    nullptr, nullptr, 0};
   hipError_t e = smqa::launch_score(a, (hipStream_t)stream);
   return e == hipSuccess ? SMQA_OK : hip_fail(e, "sparse_mqa_score launch");
 }
@@ -262,14 +262,18 @@ int decode_step(const smqa_layout* L, const uint8_t* q_fp8, const float* w, cons
   hipStream_t s = (hipStream_t)stream;
   smqa::ScoreArgs sa{L->seq_start, L->q_start, L->q_pos, L->num_seqs, L->num_q, L->max_ctx,
                      q_fp8, w, k_fp8, k_scale, cand, cand ? n_cand : 0, Hi, Di, scores, cols,
-                     nullptr};
+                     nullptr, nullptr, 0};
   smqa::TopkArgs ta{L->seq_start, L->q_start, L->q_pos, L->num_seqs, L->num_q, cols,
                     scores, cols, cand, cand ? n_cand : 0, k, idx, ws + d.topk_off};
   // When the streaming score kernel runs, it also builds the top-k's first-digit histogram.
   hipError_t e = hipSuccess;
   if (smqa::score_streams(sa)) {
-    e = smqa::launch_topk_prepare(ta, s, &sa.hist);
+    smqa::TopkFill fill{nullptr, nullptr, 0};
+    e = smqa::launch_topk_prepare(ta, s, &fill);
     if (e != hipSuccess) return hip_fail(e, "decode_step topk launch");
+    sa.hist = fill.hist;
+    sa.qcols = fill.qcols;
+    sa.qcols_stride = fill.qcols_stride;
   }
   e = smqa::launch_score(sa, s);
   if (e != hipSuccess) return hip_fail(e, "decode_step score launch");

@@ -63,8 +63,11 @@ struct ScoreArgs {
   float* scores;
   int64_t ld;
   // Optional (streaming kernel only): [T][kTopkBins] counts of the top 12 key bits of every
-  // scored position (score_key(s) >> 20), added with device atomics to a zeroed array.
+  // scored position (score_key(s) >> 20), added with device atomics to a zeroed array, and
+  // each query's number of scored columns, stored at qcols[t * qcols_stride].
   unsigned* hist;
+  int32_t* qcols;
+  int32_t qcols_stride;
 };
 hipError_t launch_score(const ScoreArgs& a, hipStream_t s);
 // True when launch_score takes the streaming kernel, the one that can fill ScoreArgs::hist.
@@ -90,7 +93,12 @@ hipError_t launch_topk(const TopkArgs& a, hipStream_t s);
 // Split form for a producer that builds the first-digit histogram itself: prepare zeroes the
 // workspace state and returns the [T][kTopkBins] histogram to fill (nullptr when the rows are
 // short and the single-kernel path needs none); finish runs the rest of the selection.
-hipError_t launch_topk_prepare(const TopkArgs& a, hipStream_t s, unsigned** hist);
+struct TopkFill {
+  unsigned* hist;       // [T][kTopkBins], zeroed
+  int32_t* qcols;       // scored columns of query t at qcols[t * qcols_stride]
+  int32_t qcols_stride;
+};
+hipError_t launch_topk_prepare(const TopkArgs& a, hipStream_t s, TopkFill* fill);
 hipError_t launch_topk_from_hist(const TopkArgs& a, hipStream_t s);
 
 struct AttendArgs {

@@ -273,6 +273,7 @@ __global__ __launch_bounds__(kScoreThreads) void score_stream_kernel(ScoreArgs a
     // as divergent, which would wrap every load in a waterfall loop)
     const int nvalid = __builtin_amdgcn_readfirstlane(min(min(len, p + 1), a.max_ctx));
     const int nblk = (nvalid + kPosPerWG - 1) / kPosPerWG;
+    if (HIST && blockIdx.x == 0 && tid == 0) a.qcols[(int64_t)t * a.qcols_stride] = nvalid;
     if ((int)blockIdx.x >= nblk) continue;
 
     __syncthreads();   // the previous query's q and histogram are no longer read

@@ -37,7 +37,8 @@ struct TopkState {
   int nvalid;    // entries in the scored set
   int done;      // finished histogram workgroups
   int ncand;     // entries appended to cand
-  int pad[2];
+  int ncols;     // columns of the query's row (stored by whoever builds the histogram)
+  int pad;
 };
 
 struct TopkWs {
@@ -168,35 +169,46 @@ __device__ int block_exclusive_scan(int v, int* lds, int* total) {
 // Find the digit d with count(digits > d) < need <= count(digits >= d) in hist[nbins].
 // Thread t owns bins nbins-1-t*per .. descending.  Result: sh[0] = digit (-1 if none),
 // sh[1] = count above it.
+// nbins / NT must be a multiple of 4: each thread reads its bins as 16-byte vectors (lanes
+// 16 bytes apart, no bank conflicts when nbins / NT == 4).
 template <int NT>
 __device__ void block_find_digit(const unsigned* hist, int nbins, int need, int* scan_lds, int* sh) {
   const int per = nbins / NT;
   const int top = nbins - 1 - threadIdx.x * per;
   int local = 0;
-  for (int i = 0; i < per; ++i) local += (int)hist[top - i];
+  for (int i = 0; i < per; i += 4) {
+    const uint4 q = *(const uint4*)&hist[top - i - 3];
+    local += (int)(q.x + q.y + q.z + q.w);
+  }
   if (threadIdx.x == 0) sh[0] = -1;
   int tot;
   int cum = block_exclusive_scan<NT>(local, scan_lds, &tot);
-  for (int i = 0; i < per; ++i) {
-    const int h = (int)hist[top - i];
-    if (cum < need && need <= cum + h) {
-      sh[0] = top - i;
-      sh[1] = cum;
+  for (int i = 0; i < per; i += 4) {
+    const uint4 q = *(const uint4*)&hist[top - i - 3];
+    const int hv[4] = {(int)q.w, (int)q.z, (int)q.y, (int)q.x};   // bins top-i, top-i-1, ...
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      if (cum < need && need <= cum + hv[u]) {
+        sh[0] = top - i - u;
+        sh[1] = cum;
+      }
+      cum += hv[u];
     }
-    cum += h;
   }
   __syncthreads();
 }
 
 // Radix select on composites from `src` restricted to entries whose top `nbits`
 // bits equal those of `prefix`: returns tau such that exactly `need` of them have
-// c >= tau.
-template <int NT, class Src>
+// c >= tau.  Digits of DBITS bits (hist holds 2^DBITS bins).  SKIP_COMMON first finds
+// the leading bits shared by every matching entry (one extra pass over the source) and
+// starts the digits below them: worth it when a pass is expensive (a global row).
+template <int NT, int DBITS, bool SKIP_COMMON, class Src>
 __device__ uint64_t radix_refine(const Src& src, int n, int need, uint64_t prefix, int nbits,
                                  unsigned* hist, int* scan_lds, int* sh) {
-  // Leading bits shared by every matching entry carry no information: find them from
-  // the min and max composite and start the digits below them.
-  {
+  constexpr int NBINS = 1 << DBITS;
+  static_assert(NBINS % (4 * NT) == 0, "block_find_digit reads 4 bins per vector");
+  if (SKIP_COMMON) {
     uint64_t lo = ~0ull, hi = 0ull;
     for (int i = threadIdx.x; i < n; i += NT) {
       uint64_t c;
@@ -234,10 +246,10 @@ __device__ uint64_t radix_refine(const Src& src, int n, int need, uint64_t prefi
     }
   }
   while (nbits < 64) {
-    const int dbits = min(11, 64 - nbits);
+    const int dbits = min(DBITS, 64 - nbits);
     const int shift = 64 - nbits - dbits;
     const uint64_t dmask = (1ull << dbits) - 1;
-    for (int i = threadIdx.x; i < 2048; i += NT) hist[i] = 0;
+    for (int i = threadIdx.x; i < NBINS; i += NT) hist[i] = 0;
     __syncthreads();
     for (int i = threadIdx.x; i < n; i += NT) {
       uint64_t c;
@@ -246,7 +258,7 @@ __device__ uint64_t radix_refine(const Src& src, int n, int need, uint64_t prefi
       atomicAdd(&hist[(c >> shift) & dmask], 1u);
     }
     __syncthreads();
-    block_find_digit<NT>(hist, 2048, need, scan_lds, sh);
+    block_find_digit<NT>(hist, NBINS, need, scan_lds, sh);
     const int d = sh[0];
     if (d < 0) break;                    // fewer matching entries than `need`: keep what matched
     const int above = sh[1];
@@ -272,58 +284,79 @@ __device__ __forceinline__ int wave_append(int* counter, bool flag) {
   return base + __popcll(m & ((1ull << lane) - 1));
 }
 
-// Read the selection bitmap (nwords words, bit c = column c) out in column order:
-// dst[i] = position of the i-th selected column, then -1 up to k.  Rounds of NT*PER
-// words: each thread loads its PER consecutive words at once (one memory latency per
-// round), and one block scan of the per-thread counts gives the output offsets.  Dense
-// rows store columns directly; the candidate-list lookup is a separate loop, so the
-// dense stores never wait on a load.
-template <int NT, bool ATOMIC_READ>
+// Read the selection out in column order: dst[i] = position of the i-th selected column,
+// then -1 up to k.  Selected = the bits of `bits` (nwords words over the columns, written by
+// an earlier kernel) plus the nwin columns win[] (in LDS).  Rounds of NT*PER words: each
+// thread puts its PER consecutive words in the LDS bitmap `lbits` (transposed: word j of
+// thread i at j * NT + i, so every access of a wave is conflict-free), the round's winners
+// are OR-ed in, one block scan of the per-thread counts gives each thread its output offset,
+// each thread writes its columns to the LDS staging array `out` (k entries), and the round's
+// outputs are copied to dst with coalesced stores (positions looked up in the candidate
+// list there, in parallel).  first[] holds this thread's words of the first round, loaded
+// by the caller in advance (garbage past nwords is masked here).
+constexpr int kSelPer = 16;
+template <int NT>
 __device__ void write_selection(const TopkArgs& a, int t, const unsigned* bits, int nwords,
-                                int32_t* dst, int* scan_lds) {
-  constexpr int PER = 16;
+                                const uint4 (&first)[kSelPer / 4], const int* win, int nwin,
+                                unsigned* lbits, int* out, int32_t* dst, int* scan_lds) {
+  constexpr int PER = kSelPer;
   int done = 0;
-  for (int r0 = 0; r0 < nwords; r0 += NT * PER) {
+  for (int r0 = 0; r0 < nwords && done < a.k; r0 += NT * PER) {
     const int w0 = r0 + threadIdx.x * PER;
+    // w0 is a multiple of 16 and the per-query bitmap a multiple of 128 words, so a group
+    // that starts below nwords lies inside it
+    uint4 g4[PER / 4];
+#pragma unroll
+    for (int j = 0; j < PER / 4; ++j)
+      g4[j] = r0 == 0 ? first[j] : w0 < nwords ? *(const uint4*)(bits + w0 + 4 * j) : make_uint4(0u, 0u, 0u, 0u);
     unsigned wv[PER];
 #pragma unroll
-    for (int j = 0; j < PER; ++j) {
-      const int i = min(w0 + j, nwords - 1);
-      const unsigned v = ATOMIC_READ ? __hip_atomic_load(bits + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
-                                     : bits[i];
-      wv[j] = w0 + j < nwords ? v : 0u;
+    for (int j = 0; j < PER / 4; ++j) {
+      wv[4 * j] = g4[j].x;
+      wv[4 * j + 1] = g4[j].y;
+      wv[4 * j + 2] = g4[j].z;
+      wv[4 * j + 3] = g4[j].w;
+    }
+#pragma unroll
+    for (int j = 0; j < PER; ++j)
+      if (w0 + j >= nwords) wv[j] = 0u;
+    if (nwin > 0) {                      // uniform
+#pragma unroll
+      for (int j = 0; j < PER; ++j) lbits[j * NT + threadIdx.x] = wv[j];
+      __syncthreads();
+      for (int i = threadIdx.x; i < nwin; i += NT) {
+        const int wi = (win[i] >> 5) - r0;
+        if (wi >= 0 && wi < NT * PER) atomicOr(&lbits[(wi % PER) * NT + wi / PER], 1u << (win[i] & 31));
+      }
+      __syncthreads();
+#pragma unroll
+      for (int j = 0; j < PER; ++j) wv[j] = lbits[j * NT + threadIdx.x];
     }
     int cnt = 0;
 #pragma unroll
     for (int j = 0; j < PER; ++j) cnt += __popc(wv[j]);
     int total;
-    int off = done + block_exclusive_scan<NT>(cnt, scan_lds, &total);
-    if (a.cand) {
+    int off = block_exclusive_scan<NT>(cnt, scan_lds, &total);
+    const int nout = min(total, a.k - done);
+    if (off < nout) {
 #pragma unroll
       for (int j = 0; j < PER; ++j) {
         unsigned m = wv[j];
-        while (m) {
-          const int bit = __ffs(m) - 1;
+        while (m && off < nout) {
+          out[off++] = 32 * (w0 + j) + __ffs(m) - 1;
           m &= m - 1;
-          if (off < a.k) dst[off] = a.cand[(int64_t)t * a.n_cand + 32 * (w0 + j) + bit];
-          ++off;
-        }
-      }
-    } else {
-#pragma unroll
-      for (int j = 0; j < PER; ++j) {
-        unsigned m = wv[j];
-        while (m) {
-          const int bit = __ffs(m) - 1;
-          m &= m - 1;
-          if (off < a.k) dst[off] = 32 * (w0 + j) + bit;
-          ++off;
         }
       }
     }
-    done += total;
+    __syncthreads();
+    for (int o = threadIdx.x; o < nout; o += NT) {
+      const int col = out[o];
+      dst[done + o] = a.cand ? a.cand[(int64_t)t * a.n_cand + col] : col;
+    }
+    done += nout;
+    __syncthreads();                     // lbits and out are rewritten by the next round
   }
-  for (int i = min(done, a.k) + threadIdx.x; i < a.k; i += NT) dst[i] = -1;
+  for (int i = done + threadIdx.x; i < a.k; i += NT) dst[i] = -1;
 }
 
 // ------------------------------------------------------------------ short rows
@@ -505,6 +538,7 @@ __global__ __launch_bounds__(kLongThreads) void topk_hist_kernel(TopkArgs a, Top
   __shared__ int sh[4];
   const int t = blockIdx.y;
   const int ncols = ncols_of(a, t);
+  if (blockIdx.x == 0 && threadIdx.x == 0) w.st[t].ncols = ncols;
   const int nch = (ncols + kChunk - 1) / kChunk;
   if ((int)blockIdx.x >= nch) return;
   const int c0 = blockIdx.x * kChunk;
@@ -554,48 +588,72 @@ __global__ __launch_bounds__(kLongThreads) void topk_hist_kernel(TopkArgs a, Top
 }
 
 // FROM_HIST: the histogram was filled by the score producer; each workgroup reads it (16 KB,
-// coherent loads issued with the row loads) and finds d1 itself, and the query's first
-// chunk publishes it for the finish kernel.  Otherwise d1 comes from the histogram kernel.
+// issued with the row loads) and finds d1 itself, and the query's first chunk publishes it
+// for the finish kernel.  Otherwise d1 comes from the histogram kernel.
 template <bool FROM_HIST>
 __global__ __launch_bounds__(kLongThreads) void topk_collect_kernel(TopkArgs a, TopkWs w) {
   constexpr int NT = kLongThreads;
   __shared__ uint2 buf[kChunk];
-  __shared__ unsigned hist[FROM_HIST ? kHistBins : 1];
   __shared__ int scan_lds[NT / 64];
   __shared__ int sh[4];
   __shared__ int nbuf, gbase;
   const int t = blockIdx.y;
-  const int ncols = ncols_of(a, t);
   const int c0 = blockIdx.x * kChunk;
-  if (c0 >= ncols) return;
   const float* row = a.scores + (int64_t)t * a.ld;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  // Every load is issued before the query's column count arrives: the row bounded by the
+  // host's max_ctx (<= ld), then masked to the query's own count.
   // wave `wave`, step u covers columns c0 + 64*(wave + 4u) + lane
+  const TopkState st0 = w.st[t];
   float v[kPerThread];
 #pragma unroll
   for (int u = 0; u < kPerThread; ++u) {
     const int i = c0 + 64 * (wave + 4 * u) + lane;
-    v[u] = i < ncols ? row[i] : -__builtin_inff();
+    v[u] = i < a.max_ctx ? row[i] : -__builtin_inff();
   }
   int d1, cnt1;
   if (FROM_HIST) {
+    // Thread i holds bins [16i, 16i + 16) in registers (four 16-byte loads; the histogram
+    // was completed by an earlier kernel, so plain loads see it).  One block scan of the
+    // per-thread counts gives the total and, as total - prefix - own, the count above each
+    // thread's bins, so the thread holding the k-th entry finds d1 in its own registers.
     constexpr int PER = kHistBins / NT;
-    const unsigned* gh = w.hist + (size_t)t * kHistBins;
+    const uint4* gh = (const uint4*)(w.hist + (size_t)t * kHistBins + PER * threadIdx.x);
+    uint4 h4[PER / 4];
+#pragma unroll
+    for (int j = 0; j < PER / 4; ++j) h4[j] = gh[j];
+    if (threadIdx.x == 0) h4[0].x = 0u;                 // bin 0 holds only key 0 (not scored)
     unsigned hv[PER];
 #pragma unroll
-    for (int j = 0; j < PER; ++j)
-      hv[j] = __hip_atomic_load(&gh[threadIdx.x + NT * j], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    for (int j = 0; j < PER / 4; ++j) {
+      hv[4 * j] = h4[j].x;
+      hv[4 * j + 1] = h4[j].y;
+      hv[4 * j + 2] = h4[j].z;
+      hv[4 * j + 3] = h4[j].w;
+    }
     int cnt = 0;
 #pragma unroll
-    for (int j = 0; j < PER; ++j) {
-      const int bin = threadIdx.x + NT * j;
-      const unsigned c = bin == 0 ? 0u : hv[j];     // bin 0 holds only key 0 (not scored)
-      hist[bin] = c;
-      cnt += (int)c;
-    }
+    for (int j = 0; j < PER; ++j) cnt += (int)hv[j];
+    if (c0 >= st0.ncols) return;                     // uniform: before any barrier
+    if (threadIdx.x == 0) sh[0] = -1;
     int nvalid;
-    block_exclusive_scan<NT>(cnt, scan_lds, &nvalid);
-    const Threshold th = find_threshold<NT>(hist, nvalid, a.k, scan_lds, sh);
+    const int pre = block_exclusive_scan<NT>(cnt, scan_lds, &nvalid);
+    if (nvalid > a.k) {
+      int above = nvalid - pre - cnt;
+      if (above < a.k && a.k <= above + cnt) {
+#pragma unroll
+        for (int j = PER - 1; j >= 0; --j) {
+          if (above < a.k && a.k <= above + (int)hv[j]) {
+            sh[0] = PER * threadIdx.x + j;
+            sh[1] = above;
+            sh[2] = (int)hv[j];
+          }
+          above += (int)hv[j];
+        }
+      }
+    }
+    __syncthreads();
+    const Threshold th = nvalid <= a.k ? Threshold{-1, nvalid, 0} : Threshold{sh[0], sh[1], sh[2]};
     d1 = th.d1;
     cnt1 = th.cnt1;
     if (blockIdx.x == 0 && threadIdx.x == 0) {
@@ -605,9 +663,14 @@ __global__ __launch_bounds__(kLongThreads) void topk_collect_kernel(TopkArgs a, 
       w.st[t].nvalid = nvalid;
     }
   } else {
-    d1 = w.st[t].d1;
-    cnt1 = w.st[t].cnt1;
+    if (c0 >= st0.ncols) return;
+    d1 = st0.d1;
+    cnt1 = st0.cnt1;
   }
+  const int ncols = st0.ncols;
+#pragma unroll
+  for (int u = 0; u < kPerThread; ++u)
+    if (c0 + 64 * (wave + 4 * u) + lane >= ncols) v[u] = -__builtin_inff();
   const bool keep_bin = d1 >= 0 && cnt1 <= kCap;
   if (threadIdx.x == 0) nbuf = 0;
   __syncthreads();
@@ -657,49 +720,88 @@ struct GlobalBinSrc {
   }
 };
 
+// One workgroup per query: the select inside the threshold bin d1 (need = k - above of its
+// entries), then the read-out.  The bin's entries come from the candidate list (in LDS)
+// or, when it overflowed, from the row itself.  Winners are collected in LDS, and the
+// read-out merges them with the collect kernel's bitmap, so nothing is written to global
+// memory and read back.
+constexpr int kRefineBits = 12;
 __global__ __launch_bounds__(1024) void topk_finish_kernel(TopkArgs a, TopkWs w) {
   constexpr int NT = 1024;
-  __shared__ unsigned ck[kCap];
-  __shared__ int cc[kCap];
-  __shared__ __attribute__((aligned(16))) unsigned hist[2048];
+  // ck | cc while refining, then the read-out's LDS bitmap (2 * kCap >= NT * 16 words)
+  __shared__ __attribute__((aligned(16))) unsigned pool[2 * kCap];
+  // refine histogram, then the winners' columns (need <= k <= 4096 of them)
+  __shared__ __attribute__((aligned(16))) unsigned hist[1 << kRefineBits];
   __shared__ int scan_lds[NT / 64];
   __shared__ int sh[4];
+  __shared__ int nwin;
+  __shared__ int out[4096];           // read-out staging (k <= 4096)
+  static_assert(2 * kCap >= NT * kSelPer, "read-out bitmap does not fit");
+  unsigned* ck = pool;
+  int* cc = (int*)(pool + kCap);
+  int* win = (int*)hist;
   const int t = blockIdx.x;
-  const int ncols = ncols_of(a, t);
-  const TopkState st = w.st[t];
-  unsigned* bits = w.bits + (size_t)t * w.bw;
+  const unsigned* bits = w.bits + (size_t)t * w.bw;
   const float* row = a.scores + (int64_t)t * a.ld;
+  const uint2* cand = w.cand + (int64_t)t * kCap;
+  // Loads that need nothing from the state go out with it: the read-out's first-round
+  // bitmap words (inside the query's bw words whenever the group starts inside them) and
+  // the first kPre candidates of the list (inside its kCap slots).
+  constexpr int kPre = 3;
+  const TopkState st = w.st[t];
+  uint4 first[kSelPer / 4];
+#pragma unroll
+  for (int j = 0; j < kSelPer / 4; ++j)
+    first[j] = kSelPer * (int)threadIdx.x < w.bw ? *(const uint4*)(bits + kSelPer * threadIdx.x + 4 * j)
+                                                  : make_uint4(0u, 0u, 0u, 0u);
+  uint2 pre[kPre];
+#pragma unroll
+  for (int j = 0; j < kPre; ++j) pre[j] = cand[threadIdx.x + NT * j];
+  const int ncols = st.ncols;
   const int need = (st.d1 < 0 || ncols == 0) ? 0 : a.k - st.above;
+  if (threadIdx.x == 0) nwin = 0;
   if (need > 0) {
     const uint64_t prefix = (uint64_t)st.d1 << 52;
     if (st.cnt1 <= kCap) {
-      const uint2* cand = w.cand + (int64_t)t * kCap;
       const int nc = min(st.ncand, kCap);
-      for (int i = threadIdx.x; i < nc; i += NT) {
+#pragma unroll
+      for (int j = 0; j < kPre; ++j) {
+        const int i = threadIdx.x + NT * j;
+        if (i < nc) {
+          ck[i] = pre[j].x;
+          cc[i] = (int)pre[j].y;
+        }
+      }
+      for (int i = threadIdx.x + NT * kPre; i < nc; i += NT) {
         const uint2 e = cand[i];
         ck[i] = e.x;
         cc[i] = (int)e.y;
       }
       __syncthreads();
       LdsPairSrc src{ck, cc};
-      const uint64_t tau = radix_refine<NT>(src, nc, need, prefix, 12, hist, scan_lds, sh);
-      for (int i = threadIdx.x; i < nc; i += NT) {
-        uint64_t c;
-        src.get(i, &c);
-        if (c >= tau) atomicOr(&bits[cc[i] >> 5], 1u << (cc[i] & 31));
+      const uint64_t tau = radix_refine<NT, kRefineBits, false>(src, nc, need, prefix, 12, hist, scan_lds, sh);
+      for (int i0 = 0; i0 < nc; i0 += NT) {
+        const int i = i0 + threadIdx.x;
+        uint64_t c = 0;
+        if (i < nc) src.get(i, &c);
+        const int slot = wave_append(&nwin, i < nc && c >= tau);
+        if (slot >= 0 && i < nc && c >= tau) win[slot] = cc[i];
       }
     } else {
       GlobalBinSrc src{row, st.d1};
-      const uint64_t tau = radix_refine<NT>(src, ncols, need, prefix, 12, hist, scan_lds, sh);
-      for (int i = threadIdx.x; i < ncols; i += NT) {
-        uint64_t c;
-        if (src.get(i, &c) && c >= tau) atomicOr(&bits[i >> 5], 1u << (i & 31));
+      const uint64_t tau = radix_refine<NT, kRefineBits, true>(src, ncols, need, prefix, 12, hist, scan_lds, sh);
+      for (int i0 = 0; i0 < ncols; i0 += NT) {
+        const int i = i0 + threadIdx.x;
+        uint64_t c = 0;
+        const bool sel = i < ncols && src.get(i, &c) && c >= tau;
+        const int slot = wave_append(&nwin, sel);
+        if (sel) win[slot] = i;
       }
     }
   }
-  __builtin_amdgcn_s_waitcnt(0);           // this workgroup's bit updates have completed
   __syncthreads();
-  write_selection<NT, true>(a, t, bits, (ncols + 31) / 32, a.idx + (int64_t)t * a.k, scan_lds);
+  write_selection<NT>(a, t, bits, (ncols + 31) / 32, first, win, nwin, pool, out, a.idx + (int64_t)t * a.k,
+                      scan_lds);
 }
 
 hipError_t launch_topk(const TopkArgs& a, hipStream_t s) {
@@ -708,8 +810,8 @@ hipError_t launch_topk(const TopkArgs& a, hipStream_t s) {
     hipLaunchKernelGGL(topk_small_kernel, dim3(a.T), dim3(1024), 0, s, a);
     return hipGetLastError();
   }
-  unsigned* hist = nullptr;
-  hipError_t e = launch_topk_prepare(a, s, &hist);
+  TopkFill fill;
+  hipError_t e = launch_topk_prepare(a, s, &fill);
   if (e != hipSuccess) return e;
   TopkWs w = carve(a.ws, a.T, a.max_ctx);
   const int nch = (a.max_ctx + kChunk - 1) / kChunk;
@@ -719,15 +821,16 @@ hipError_t launch_topk(const TopkArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
-hipError_t launch_topk_prepare(const TopkArgs& a, hipStream_t s, unsigned** hist) {
-  *hist = nullptr;
+hipError_t launch_topk_prepare(const TopkArgs& a, hipStream_t s, TopkFill* fill) {
+  *fill = TopkFill{nullptr, nullptr, 0};
   if (a.T == 0 || a.max_ctx <= kSmallN) return hipSuccess;
   TopkWs w = carve(a.ws, a.T, a.max_ctx);
   // histogram and per-query state (counters start at zero)
   const size_t zero_words = ((char*)w.cand - (char*)w.hist) / 4;
   const int zblocks = (int)std::min<size_t>((zero_words + 1023) / 1024, 2048);
   hipLaunchKernelGGL(topk_zero_kernel, dim3(zblocks), dim3(256), 0, s, w.hist, zero_words);
-  *hist = w.hist;
+  static_assert(sizeof(TopkState) % 4 == 0, "state stride in ints");
+  *fill = TopkFill{w.hist, &w.st[0].ncols, (int32_t)(sizeof(TopkState) / 4)};
   return hipGetLastError();
 }
 
