@@ -18,7 +18,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libsmqa.so")
-SOURCES = ["api.hip", "score.hip", "topk.hip", "attend.hip"]
+SOURCES = ["api.hip", "score.hip", "topk.hip", "attend.hip", "attend_sd.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

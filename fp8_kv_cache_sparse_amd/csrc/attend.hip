@@ -1082,7 +1082,7 @@ size_t attend_workspace_bytes(int32_t T, int32_t k, int32_t W, int32_t Hq, int32
   return (size_t)S * T * Hq * D * 4 + (size_t)S * T * Hq * 8;
 }
 
-static hipError_t launch_merge(const AttendArgs& a, int S, hipStream_t s) {
+hipError_t launch_attend_merge(const AttendArgs& a, int S, hipStream_t s) {
   if (S == 1) return hipSuccess;
   hipLaunchKernelGGL(attend_merge_kernel, dim3((a.D + 255) / 256, a.T * a.Hq), dim3(256), 0, s, a, S);
   return hipGetLastError();
@@ -1112,7 +1112,7 @@ static hipError_t launch_lat(const AttendArgs& a, const AttPlan& p, hipStream_t 
   hipLaunchKernelGGL((lat::attend_kernel<MT, NS>), dim3(nb), dim3(lat::kAttThreads), dyn, s, a, p.S,
                      p.ngroups, total);
   e = hipGetLastError();
-  return e != hipSuccess ? e : launch_merge(a, p.S, s);
+  return e != hipSuccess ? e : launch_attend_merge(a, p.S, s);
 }
 
 template <int D>
@@ -1130,9 +1130,11 @@ static hipError_t launch_thr(const AttendArgs& a, const AttPlan& p, hipStream_t 
     hipLaunchKernelGGL((thr::attend_kernel<2, D>), dim3(nb), dim3(thr::kAttThreads), dyn, s, a, p.S,
                        p.ngroups, total);
     e = hipGetLastError();
-    return e != hipSuccess ? e : launch_merge(a, p.S, s);
+    return e != hipSuccess ? e : launch_attend_merge(a, p.S, s);
   }
 }
+
+hipError_t launch_attend_sd(const AttendArgs& a, int S, hipStream_t s);
 
 hipError_t launch_attend(const AttendArgs& a, hipStream_t s) {
   if (a.T == 0) return hipSuccess;
@@ -1141,6 +1143,7 @@ hipError_t launch_attend(const AttendArgs& a, hipStream_t s) {
     if (a.D <= 1024) return p.MT == 2 ? launch_lat<2, 1>(a, p, s) : launch_lat<1, 1>(a, p, s);
     return launch_lat<1, 2>(a, p, s);
   }
+  if (a.D <= 1664) return launch_attend_sd(a, p.S, s);
   switch (a.D) {
 #define SMQA_ATTEND_D(d) case d: return launch_thr<d>(a, p, s);
     SMQA_ATTEND_D(128) SMQA_ATTEND_D(256) SMQA_ATTEND_D(384) SMQA_ATTEND_D(512)

@@ -1,0 +1,654 @@
+// Sparse multi-query attention, split over the latent dimension inside a workgroup
+// (vLLM blog "DeepSeek-V4.1-Flash sur vLLM": section "Kernels", MegaAttention reading the
+// compressed FP4 KV; section "SWA bounded replay", the FP8 window of the last 128
+// positions and its clip at the replay start; section "Performances agentiques", one KV
+// latent shared by every head, so K = V = the latent row).
+//
+// A workgroup (8 waves, one per 2 SIMD slots) owns one query, 32 heads and a contiguous
+// range of tiles: ceil(k/32) tiles of 32 selected FP4 rows, then the 16-row tiles of FP8
+// window rows that overlap the query's visible window.  Wave w owns a contiguous run of
+// 32-dim latent blocks (the E8M0 block size) for both products, so every dequantised
+// value feeds 32 heads of MFMA work and no wave converts a value another wave needs.
+//
+//   gather   global_load_lds_dwordx4 straight into one of three LDS tile buffers (rows
+//            padded so both read patterns below are bank-conflict free); the raw E8M0
+//            bytes and the row scales land beside them.  Tile i+2 is in flight while tile
+//            i+1 is scored and tile i is accumulated.
+//   Q.K^T    v_mfma_f32_32x32x16_bf16, heads x rows: each lane reads 8 dims of one row
+//            (ds_read_b32 for E2M1, ds_read_b64 for E4M3) and converts them exactly to
+//            bf16 with the block's E8M0 scale (v_cvt_scalef32_pk_bf16_*); q stays in
+//            registers.  Each wave's partial logits over its blocks go to LDS.
+//   softmax  every wave sums the 8 partials of 4 heads, applies tau * log2(e) and the row
+//            scale and updates the exact running max (so the largest P of a head is exactly
+//            1 in fp16); the accumulators of a group of 8 heads are rescaled only when one
+//            of their maxima moved.
+//   P.V      v_mfma_f32_32x32x16_f16, heads x dims: the B operand (8 rows of one dim per
+//            lane) comes straight from the row-major tile through the LDS transpose reads
+//            ds_read_b64_tr_b4 (E2M1: 16 rows of one dim per lane) and ds_read_b64_tr_b8
+//            (E4M3), is converted to fp16 with scale 1 and multiplied by the rows' block
+//            scales (v_pk_mul_f16, exact while -24 <= e - 127 <= 15); P carries the row
+//            scale rho (or sigma).
+//
+// Several tile ranges of one (query, head group) leave unnormalised partials that
+// attend_merge_kernel combines by log-sum-exp.
+#include <type_traits>
+
+#include "common.h"
+
+namespace smqa {
+
+hipError_t launch_attend_merge(const AttendArgs& a, int S, hipStream_t s);
+
+namespace sd {
+
+typedef float v16f __attribute__((ext_vector_type(16)));
+typedef int v2i __attribute__((ext_vector_type(2)));
+typedef _Float16 v2h __attribute__((ext_vector_type(2)));
+
+constexpr int kThreads = 512;
+constexpr int kRows = 32;     // selected global rows per tile
+constexpr int kWRows = 16;    // window rows per tile
+constexpr int kNBuf = 4;      // tile buffers in LDS: tiles i-1 (P.V), i (Q.K^T), i+1, i+2 in flight
+
+constexpr int align16(int x) { return (x + 15) & ~15; }
+
+// LDS geometry for latent width D (compile time, so every offset is an immediate).
+template <int D>
+struct Geo {
+  static constexpr int NB = D / 32;                 // 32-dim blocks
+  static constexpr int BPW = NB / 8;                // blocks of every wave
+  static constexpr int EXTRA = NB % 8;              // waves 0..EXTRA-1 own one more (0 or 4)
+  static constexpr int NBW = BPW + (EXTRA ? 1 : 0); // most blocks of one wave
+  static constexpr int RS4 = D / 2 + 16;            // E2M1 row stride (16 * odd dwords / 4)
+  static constexpr int RS8 = D + 16;                // E4M3 row stride
+  static constexpr int E8S = D / 32;                // raw E8M0 bytes per row
+  // one tile buffer: codes | raw E8M0 [32][E8S] | row scales [4 loader waves][8]
+  static constexpr int CODES = kRows * RS4;
+  static constexpr int E8 = CODES;
+  static constexpr int RHO = align16(E8 + kRows * E8S);
+  static constexpr int BUF = align16(RHO + kRows * 4);
+  // shared areas after the buffers
+  static constexpr int RING = kNBuf * BUF;                      // positions [4][32]
+  static constexpr int SCH = RING + kNBuf * kRows * 4;          // [2][NB][16] u32: f16 scale pairs
+  static constexpr int RED = SCH + 2 * NB * 16 * 4;             // [8 waves][32 heads][32 rows] f32
+  static constexpr int PS = RED + 8 * 32 * kRows * 4;           // P [32 heads][40] f16
+  static constexpr int RI = PS + 32 * 40 * 2;                   // logit scale[32], P scale[32]
+  static constexpr int MR = RI + 2 * 32 * 4;                    // mref[32] alpha[32] lsum[32]
+  static constexpr int LDS = MR + 3 * 32 * 4;
+  // global loads a loader wave issues per tile (fixed, so vmcnt can wait for the older tile)
+  static constexpr int PIECES8 = D / 16;                        // 16-byte pieces of an E4M3 row
+  static constexpr int NLOAD4 = kRows / 4 + 2 + 1;              // 8 code rows, 2 E8M0, rho
+  static constexpr int NLOAD8 = (kWRows / 4) * (PIECES8 > 64 ? 2 : 1) + 1;  // 4 rows, sigma
+  static_assert(kWRows * RS8 <= CODES, "a window tile must fit a buffer");
+  static_assert(EXTRA == 0 || EXTRA == 4, "D must be a multiple of 128");
+  static_assert(LDS <= 160 * 1024, "LDS budget");
+};
+
+struct Ctx {
+  int k, W;
+  int ng, wt0, tb, te, gx1;
+  int b, p, lo_win, pos0;
+  int64_t base;
+  float lscale;
+};
+
+template <class T>
+__device__ __forceinline__ T lds(const uint8_t* p) { return *(const T*)p; }
+
+__device__ __forceinline__ v8bf cvt8_fp4_bf16(unsigned wd, float scl) {
+  v4u u;
+  u.x = __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(wd, scl, 0));
+  u.y = __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(wd, scl, 1));
+  u.z = __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(wd, scl, 2));
+  u.w = __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(wd, scl, 3));
+  return __builtin_bit_cast(v8bf, u);
+}
+
+__device__ __forceinline__ v8bf cvt8_fp8_bf16(v2u w) {
+  v4u u;
+  u.x = __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w.x, 1.0f, false));
+  u.y = __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w.x, 1.0f, true));
+  u.z = __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w.y, 1.0f, false));
+  u.w = __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w.y, 1.0f, true));
+  return __builtin_bit_cast(v8bf, u);
+}
+
+// E2M1 nibble pair `sel` of wd (two consecutive rows after a transpose read), exact fp16.
+__device__ __forceinline__ v2h fp4x2_f16(unsigned wd, int sel) {
+  switch (sel) {
+    case 0: return __builtin_bit_cast(v2h, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(wd, 1.0f, 0));
+    case 1: return __builtin_bit_cast(v2h, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(wd, 1.0f, 1));
+    case 2: return __builtin_bit_cast(v2h, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(wd, 1.0f, 2));
+    default: return __builtin_bit_cast(v2h, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(wd, 1.0f, 3));
+  }
+}
+
+// s_waitcnt with only the vector-memory counter bounded (gfx9 encoding: vmcnt in bits 3:0,
+// expcnt 6:4 and lgkmcnt 11:8 left at their maxima).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 16, "vmcnt immediate");
+  __builtin_amdgcn_s_waitcnt(0x0F70 | N);
+}
+
+// An opaque copy of a per-lane value: re-deriving lane offsets inside each stage keeps the
+// compiler from hoisting dozens of loop-invariant addresses into registers.
+__device__ __forceinline__ int opq(int v) {
+  asm volatile("" : "+v"(v));
+  return v;
+}
+
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), CTRL, 0xF, 0xF, false));
+}
+// Reduction over each 16-lane row: quad swaps, half-row mirror, row mirror (DPP).
+template <bool MAX>
+__device__ __forceinline__ float row_reduce(float v) {
+  auto op = [](float x, float y) { return MAX ? fmaxf(x, y) : x + y; };
+  v = op(v, dpp_f<0xB1>(v));                      // quad_perm [1,0,3,2]
+  v = op(v, dpp_f<0x4E>(v));                      // quad_perm [2,3,0,1]
+  v = op(v, dpp_f<0x141>(v));                     // row_half_mirror
+  v = op(v, dpp_f<0x140>(v));                     // row_mirror
+  return v;
+}
+
+// One tile of global loads straight into LDS (global_load_lds: each lane's bytes land at
+// the wave-uniform LDS address M0 + lane * size).  Written as inline assembly so that the
+// compiler does not treat every later LDS read as possibly aliasing an in-flight load (it
+// would wait for all of them, the prefetch included); the kernel bounds the vector-memory
+// counter itself before the barrier that publishes a tile.  Every wave issues a fixed
+// number of these per tile kind; rows that take no part read a harmless in-bounds dummy
+// (the query's own q row) instead of being skipped.
+__device__ __forceinline__ void gload16(const void* src, unsigned m0) {
+  asm volatile("global_load_lds_dwordx4 %0, off" ::"v"(src), "{m0}"(m0) : "memory");
+}
+__device__ __forceinline__ void gload4(const void* src, unsigned m0) {
+  asm volatile("global_load_lds_dword %0, off" ::"v"(src), "{m0}"(m0) : "memory");
+}
+
+template <int D>
+__global__ __launch_bounds__(kThreads) void attend_kernel(AttendArgs a, int S, int ngroups, int total) {
+  using G = Geo<D>;
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
+  // Per-lane roles (re-derived from an opaque lane id inside each stage):
+  //   r32 = lane & 31, kh = lane >> 5    MFMA 32x32 operand lane: column / k-half
+  //   i16 = lane & 15, hh = lane >> 4 & 1 transpose-read lane, dim half of a block
+#define SMQA_LANE_ROLES                                                                   \
+  const int ln_ = opq(lane);                                                              \
+  const int r32 = ln_ & 31, kh = ln_ >> 5, i16 = ln_ & 15, hh = (ln_ >> 4) & 1;          \
+  (void)r32; (void)kh; (void)i16; (void)hh;
+
+  // XCD-aware order: workgroups are dealt to the 8 XCDs round-robin, so logical block
+  // (bid & 7) * (nb / 8) + (bid >> 3) keeps runs of consecutive logical blocks on one XCD;
+  // the head groups of one query (same rows) are consecutive and share that XCD's L2.
+  const int nb = gridDim.x;
+  const int bid = blockIdx.x;
+  const int logical = (bid & 7) * (nb >> 3) + (bid >> 3);
+  if (logical >= total) return;
+  const int grp = logical % ngroups;
+  const int split = (logical / ngroups) % S;
+  const int t = logical / (S * ngroups);
+  const int h0 = grp * 32;
+
+  Ctx c;
+  c.k = a.k;
+  c.W = a.W;
+  c.b = seq_of_query(a.q_start, a.B, t);
+  c.base = a.seq_start[c.b];
+  c.p = a.q_pos[t];
+  c.lo_win = max(c.p - c.W + 1, 0);
+  if (a.swa_clip) c.lo_win = max(c.lo_win, a.swa_clip[t]);
+  c.pos0 = a.swa_pos0[c.b];
+  c.lscale = a.sm_scale * kLog2e;
+  c.ng = (c.k + kRows - 1) / kRows;
+  const int u_lo = max(c.lo_win - c.pos0, 0);
+  const int u_hi = min(c.p - c.pos0, c.W - 1);
+  c.wt0 = u_lo / kWRows;
+  const int nwt = u_lo <= u_hi ? u_hi / kWRows - c.wt0 + 1 : 0;
+  const int ntiles = c.ng + nwt;
+  c.tb = (int)((int64_t)split * ntiles / S);
+  c.te = (int)((int64_t)(split + 1) * ntiles / S);
+  c.gx1 = min(min(c.te, c.ng) * kRows, c.k);       // global rows of this split end here
+
+  float* mref = (float*)(smem + G::MR);
+  float* malpha = mref + 32;
+  float* mlsum = mref + 64;
+  float* rl = (float*)(smem + G::RI);
+  float* rp = rl + 32;
+  const uint8_t* dummy = (const uint8_t*)(a.q + (int64_t)t * a.Hq * D);
+  // LDS byte address of a location in the dynamic array (the M0 operand of the loads): the
+  // dynamic array starts right after the kernel's static LDS
+  auto lds_addr = [&](const uint8_t* p) __attribute__((always_inline)) -> unsigned {
+    return __builtin_amdgcn_readfirstlane(__builtin_amdgcn_groupstaticsize() + (unsigned)(p - smem));
+  };
+
+  // wave w's blocks [b0, b0 + BPW + (w < EXTRA))
+  const int b0 = wave * G::BPW + min(wave, G::EXTRA);
+
+  // ---- loads of one tile: positions (into the ring) and rows (into a buffer).  Waves 4..7
+  // (one 32-dim block fewer than waves 0..3 when the block count is uneven) do all loads.
+  const int wq = wave - 4;                          // loader index, valid for waves 4..7
+  auto load_pos = [&](int tile, int rslot) __attribute__((always_inline)) {       // wave 4, lanes 0..31
+    const int ln = opq(lane);
+    const int x = tile * kRows + (ln & 31);
+    const void* src = x < c.gx1 ? (const void*)(a.idx + (int64_t)t * c.k + x) : (const void*)dummy;
+    if (ln < kRows) gload4(src, lds_addr(smem + G::RING + rslot * kRows * 4));
+  };
+  auto issue = [&](int tile, int slot, int rslot) __attribute__((always_inline)) {
+    const int ln = opq(lane);
+    uint8_t* B = smem + slot * G::BUF;
+    if (tile < c.ng) {
+      constexpr int per_row = D / 128;              // E8M0 dwords per row
+      const int* pos = (const int*)(smem + G::RING) + rslot * kRows;
+      const int xt = tile * kRows;
+      // every position this wave needs, read before one wait: all 32 (for the code rows),
+      // the rows of its two E8M0 loads, the rows of its rho lanes
+      const int pall = pos[ln & 31];
+      const int re0 = 8 * wq + ln / per_row, re1 = re0 + 4;
+      const int pe0 = pos[re0 & 31], pe1 = pos[re1 & 31];
+      const int rr = 4 * (ln & 7) + wq;
+      const int pr = pos[rr];
+      // code rows 4u + wq, u = 0..7
+#pragma unroll
+      for (int u = 0; u < kRows / 4; ++u) {
+        const int r = 4 * u + wq;
+        const int j = __builtin_amdgcn_readlane(pall, r);
+        const bool ok = xt + r < c.gx1 && j >= 0;
+        const uint8_t* src = ok ? a.kv_codes + (c.base + j) * (D / 2) : dummy;
+        if (ln < D / 32) gload16(src + 16 * ln, lds_addr(B + r * G::RS4));
+      }
+      // raw E8M0: rows 8wq + 4h .. +4, contiguous
+      {
+        const int dd = ln % per_row;
+        const bool ok0 = xt + re0 < c.gx1 && pe0 >= 0, ok1 = xt + re1 < c.gx1 && pe1 >= 0;
+        const uint8_t* s0 = ok0 ? a.kv_e8m0 + (c.base + pe0) * (D / 32) : dummy;
+        const uint8_t* s1 = ok1 ? a.kv_e8m0 + (c.base + pe1) * (D / 32) : dummy;
+        if (ln < 4 * per_row) {
+          gload4(s0 + 4 * dd, lds_addr(B + G::E8 + 8 * wq * G::E8S));
+          gload4(s1 + 4 * dd, lds_addr(B + G::E8 + (8 * wq + 4) * G::E8S));
+        }
+      }
+      {  // rho of rows 4u + wq, u = lane < 8 -> RHO[wq][u]
+        const bool ok = a.kv_rowscale && xt + rr < c.gx1 && pr >= 0;
+        const void* src = ok ? (const void*)(a.kv_rowscale + c.base + pr) : (const void*)dummy;
+        if (ln < 8) gload4(src, lds_addr(B + G::RHO + 32 * wq));
+      }
+    } else {
+      // window tile: rows 4u + wq, u = 0..3; D/16 pieces of 16 bytes per row (two loads
+      // when > 64)
+      const int wt = c.wt0 + tile - c.ng;
+#pragma unroll
+      for (int u = 0; u < kWRows / 4; ++u) {
+        const int r = 4 * u + wq;
+        const int uu = kWRows * wt + r;
+        const uint8_t* src = uu < c.W ? a.swa + ((int64_t)c.b * c.W + uu) * D : dummy;
+        if (ln < (G::PIECES8 < 64 ? G::PIECES8 : 64)) gload16(src + 16 * ln, lds_addr(B + r * G::RS8));
+        if constexpr (G::PIECES8 > 64) {
+          if (ln < G::PIECES8 - 64) gload16(src + 1024 + 16 * ln, lds_addr(B + r * G::RS8 + 1024));
+        }
+      }
+      {  // sigma of rows 4u + wq, u = lane < 4 -> RHO[wq][u]
+        const int uu = kWRows * wt + 4 * (ln & 3) + wq;
+        const bool ok = a.swa_scale && uu < c.W;
+        const void* src = ok ? (const void*)(a.swa_scale + (int64_t)c.b * c.W + uu) : (const void*)dummy;
+        if (ln < 4) gload4(src, lds_addr(B + G::RHO + 32 * wq));
+      }
+    }
+  };
+
+  // ---- prologue: softmax state, q in registers, positions of the first three tiles,
+  // rows of the first two
+  if (tid < 32) {
+    mref[tid] = -__builtin_inff();
+    malpha[tid] = 1.0f;
+  }
+  // A operands of Q.K^T: head h0 + r32, dims 32 b + 16 kh + 8 cc .. +8 of block b = b0 + i
+  v8bf qa[G::NBW][2];
+  {
+    SMQA_LANE_ROLES
+    const uint16_t* qrow = a.q + ((int64_t)t * a.Hq + h0 + r32) * D + 16 * kh;
+#pragma unroll
+    for (int i = 0; i < G::NBW; ++i)
+#pragma unroll
+      for (int cc = 0; cc < 2; ++cc) {
+        v4u v = {0u, 0u, 0u, 0u};
+        if (i < G::BPW || wave < G::EXTRA) v = *(const v4u*)(qrow + 32 * (b0 + i) + 8 * cc);
+        qa[i][cc] = __builtin_bit_cast(v8bf, v);
+      }
+  }
+  const int tb = c.tb, te = c.te;
+  if (wave == 4) {
+    for (int u = 0; u < 3; ++u)
+      if (tb + u < te && tb + u < c.ng) load_pos(tb + u, u);
+  }
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  if (wave >= 4) {
+    if (tb < te) issue(tb, 0, 0);
+    if (tb + 1 < te) issue(tb + 1, 1, 1);
+  }
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+
+  // ---- Q.K^T of one tile (FP4 = global rows, else window rows): this wave's partial
+  // logits [32 heads][32 rows] to LDS.  Lane (r32, kh) of MFMA cc supplies dims
+  // 32 b + 16 kh + 8 cc .. +8 of row r32 (one 8-byte read covers both cc for E2M1).
+  auto qk = [&](auto FP4, int slot) __attribute__((always_inline)) {
+    SMQA_LANE_ROLES
+    const uint8_t* B = smem + slot * G::BUF;
+    v16f acc;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) acc[e] = 0.0f;
+    if constexpr (decltype(FP4)::value) {
+      const uint8_t* rowp = B + r32 * G::RS4 + 8 * kh + 16 * b0;
+      const uint8_t* e8p = B + G::E8 + r32 * G::E8S + b0;
+#pragma unroll
+      for (int i = 0; i < G::NBW; ++i) {
+        if (i < G::BPW || wave < G::EXTRA) {
+          // E8M0 e -> 2^(e-127) as the float e << 23 (e = 0, below 4e-38 in magnitude, gives 0)
+          const float scl = __uint_as_float((unsigned)lds<uint8_t>(e8p + i) << 23);
+          const v2u wd = lds<v2u>(rowp + 16 * i);
+          acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[i][0], cvt8_fp4_bf16(wd.x, scl), acc, 0, 0, 0);
+          acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[i][1], cvt8_fp4_bf16(wd.y, scl), acc, 0, 0, 0);
+        }
+      }
+    } else {
+      const uint8_t* rowp = B + (r32 & 15) * G::RS8 + 16 * kh + 32 * b0;
+#pragma unroll
+      for (int i = 0; i < G::NBW; ++i) {
+        if (i < G::BPW || wave < G::EXTRA) {
+          const v4u wd = lds<v4u>(rowp + 32 * i);
+          acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[i][0], cvt8_fp8_bf16(v2u{wd.x, wd.y}), acc, 0, 0, 0);
+          acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[i][1], cvt8_fp8_bf16(v2u{wd.z, wd.w}), acc, 0, 0, 0);
+        }
+      }
+    }
+    // acc[4 q4 + e] is the logit of head 8 q4 + 4 kh + e, row r32 -> red[wave][head][row]
+    float* red = (float*)(smem + G::RED) + wave * 32 * kRows + r32;
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) red[(8 * q4 + 4 * kh + e) * kRows] = acc[4 * q4 + e];
+  };
+
+  // ---- per-tile row data, computed while the tile is scored: the logit multiplier
+  // tau * log2(e) * (rho or sigma), 0 for rows that take no part, the P multiplier (rho
+  // or sigma), and the V-operand block scales as fp16 pairs (rows 2pp, 2pp+1; zero for
+  // rows that take no part) or, for a window tile, 16-bit row masks in pairs.
+  auto convert = [&](auto FP4, int tile, int slot, int rslot, int sslot) __attribute__((always_inline)) {
+    const int ct = opq(tid) - 256;                 // waves 4..7: 0..255
+    const int ln = ct & 63;
+    const uint8_t* B = smem + slot * G::BUF;
+    unsigned* sch = (unsigned*)(smem + G::SCH) + sslot * G::NB * 16;
+    if constexpr (decltype(FP4)::value) {
+      const int* pos = (const int*)(smem + G::RING) + rslot * kRows;
+      // rows that take part, as a bit mask (every loader wave computes it)
+      const int pl = pos[ln & 31];
+      const unsigned vmask = (unsigned)__builtin_amdgcn_ballot_w64(ln < kRows && tile * kRows + ln < c.gx1 && pl >= 0);
+      // blocks 4 bq .. 4 bq + 3 of rows 2 pp, 2 pp + 1 (one dword of raw E8M0 per row)
+      const int pp = ct & 15, bq = ct >> 4;
+      if (bq < G::NB / 4) {
+        const unsigned w0 = lds<unsigned>(B + G::E8 + (2 * pp) * G::E8S + 4 * bq);
+        const unsigned w1 = lds<unsigned>(B + G::E8 + (2 * pp + 1) * G::E8S + 4 * bq);
+        const bool v0 = (vmask >> (2 * pp)) & 1u, v1 = (vmask >> (2 * pp + 1)) & 1u;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          // E8M0 e -> 2^(e-127) as the float e << 23 (e = 0 gives 0); exact in fp16 for
+          // -24 <= e - 127 <= 15
+          const float f0 = v0 ? __uint_as_float(((w0 >> (8 * j)) & 0xFFu) << 23) : 0.0f;
+          const float f1 = v1 ? __uint_as_float(((w1 >> (8 * j)) & 0xFFu) << 23) : 0.0f;
+          sch[(4 * bq + j) * 16 + pp] = __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_pkrtz(f0, f1));
+        }
+      }
+      if (ct < kRows) {
+        const bool v = (vmask >> ct) & 1u;
+        const float m = a.kv_rowscale ? ((const float*)(B + G::RHO))[8 * (ct & 3) + (ct >> 2)] : 1.0f;
+        rl[ct] = v ? c.lscale * m : 0.0f;
+        rp[ct] = v ? m : 0.0f;
+      }
+    } else if (ct < kRows) {
+      const int uu = kWRows * (c.wt0 + tile - c.ng) + ct;
+      const int pos = c.pos0 + uu;
+      const bool v = ct < kWRows && uu < c.W && pos >= c.lo_win && pos <= c.p;
+      const unsigned vb = (unsigned)__builtin_amdgcn_ballot_w64(v);   // rows 0..15 of wave 4
+      const float m = a.swa_scale ? ((const float*)(B + G::RHO))[8 * (ct & 3) + ((ct & 15) >> 2)] : 1.0f;
+      rl[ct] = v ? c.lscale * m : 0.0f;
+      rp[ct] = v ? m : 0.0f;
+      if (ct < kWRows / 2) {
+        const unsigned pr = (vb >> (2 * ct)) & 3u;
+        sch[ct] = ((pr & 1u) ? 0x0000FFFFu : 0u) | ((pr & 2u) ? 0xFFFF0000u : 0u);
+      }
+    }
+  };
+
+  // ---- softmax of one tile: wave w owns heads 4w .. 4w+3; lane l takes head
+  // 4w + l / 16 and rows 2 (l % 16), +1, so a head's max is a 16-lane reduction
+  float lpart = 0.0f;                              // this lane's share of the head's row sum
+  auto softmax = [&]() __attribute__((always_inline)) {
+    const int ln_ = opq(lane);
+    const int sh = 4 * wave + (ln_ >> 4), srow = 2 * (ln_ & 15);
+    const float* red = (const float*)(smem + G::RED) + sh * kRows + srow;
+    const float2 lsr = *(const float2*)(rl + srow);
+    const float2 psr = *(const float2*)(rp + srow);
+    const float mo = mref[sh];
+    float s0 = 0.0f, s1 = 0.0f;
+#pragma unroll
+    for (int w8 = 0; w8 < 8; ++w8) {
+      const float2 v = *(const float2*)(red + w8 * 32 * kRows);
+      s0 += v.x;
+      s1 += v.y;
+    }
+    const bool ok0 = lsr.x != 0.0f, ok1 = lsr.y != 0.0f;
+    s0 = ok0 ? s0 * lsr.x : -__builtin_inff();
+    s1 = ok1 ? s1 * lsr.y : -__builtin_inff();
+    const float tmax = row_reduce<true>(fmaxf(s0, s1));
+    const float mn = fmaxf(mo, tmax);
+    const float al = mn == mo ? 1.0f : __builtin_amdgcn_exp2f(mo - mn);
+    const float p0 = ok0 ? __builtin_amdgcn_exp2f(s0 - mn) : 0.0f;
+    const float p1 = ok1 ? __builtin_amdgcn_exp2f(s1 - mn) : 0.0f;
+    lpart = lpart * al + (p0 + p1);
+    *(v2h*)((_Float16*)(smem + G::PS) + sh * 40 + srow) = v2h{(_Float16)(p0 * psr.x), (_Float16)(p1 * psr.y)};
+    if ((ln_ & 15) == 0) {
+      mref[sh] = mn;
+      malpha[sh] = al;
+    }
+  };
+
+  // ---- P.V of one tile into the output accumulators
+  v16f o[G::NBW];
+#pragma unroll
+  for (int i = 0; i < G::NBW; ++i)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) o[i][e] = 0.0f;
+
+  auto pv = [&](auto FP4, int slot, int sslot) __attribute__((always_inline)) {
+    SMQA_LANE_ROLES
+    const uint8_t* B = smem + slot * G::BUF;
+    const unsigned* sch = (const unsigned*)(smem + G::SCH) + sslot * G::NB * 16;
+    // rescale when the running max of a group of 8 heads (4 per k-half) moved: one
+    // uniform branch per group, so only groups whose max moved pay for the multiplies
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4) {
+      const v4f al = *(const v4f*)(malpha + 8 * q4 + 4 * kh);
+      const bool moved = al.x != 1.0f || al.y != 1.0f || al.z != 1.0f || al.w != 1.0f;
+      if (__builtin_amdgcn_ballot_w64(moved)) {
+#pragma unroll
+        for (int i = 0; i < G::NBW; ++i)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) o[i][4 * q4 + e] *= al[e];
+      }
+    }
+    const _Float16* P = (const _Float16*)(smem + G::PS);
+    if constexpr (decltype(FP4)::value) {
+      // k-slot 8 kh + j of MFMA s <-> row 16 kh + 8 s + j
+      const v8h pa0 = *(const v8h*)(P + r32 * 40 + 16 * kh);
+      const v8h pa1 = *(const v8h*)(P + r32 * 40 + 16 * kh + 8);
+      const uint8_t* tp = B + (16 * kh + i16) * G::RS4 + 8 * hh + 16 * b0;
+      const unsigned* sp = sch + 16 * b0 + 8 * kh;
+#pragma unroll
+      for (int i = 0; i < G::NBW; ++i) {
+        if (i < G::BPW || wave < G::EXTRA) {
+          const v2i raw = __builtin_amdgcn_ds_read_tr4_b64_v2i32(
+              (__attribute__((address_space(3))) v2i*)(tp + 16 * i));
+          const v4u s0 = *(const v4u*)(sp + 16 * i);
+          const v4u s1 = *(const v4u*)(sp + 16 * i + 4);
+          const unsigned sc[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
+          unsigned wv[8];
+#pragma unroll
+          for (int kk = 0; kk < 8; ++kk) {
+            const v2h f = fp4x2_f16((unsigned)raw[kk >> 2], kk & 3) * __builtin_bit_cast(v2h, sc[kk]);
+            wv[kk] = __builtin_bit_cast(unsigned, f);
+          }
+          o[i] = __builtin_amdgcn_mfma_f32_32x32x16_f16(pa0, __builtin_bit_cast(v8h, v4u{wv[0], wv[1], wv[2], wv[3]}),
+                                                       o[i], 0, 0, 0);
+          o[i] = __builtin_amdgcn_mfma_f32_32x32x16_f16(pa1, __builtin_bit_cast(v8h, v4u{wv[4], wv[5], wv[6], wv[7]}),
+                                                       o[i], 0, 0, 0);
+        }
+      }
+    } else {
+      // k-slot 8 kh + j <-> window row 8 kh + j
+      const v8h pa = *(const v8h*)(P + r32 * 40 + 8 * kh);
+      const v4u mk = *(const v4u*)(sch + 4 * kh);
+      const uint8_t* tp = B + (8 * kh + (i16 >> 1)) * G::RS8 + 16 * hh + 8 * (i16 & 1) + 32 * b0;
+#pragma unroll
+      for (int i = 0; i < G::NBW; ++i) {
+        if (i < G::BPW || wave < G::EXTRA) {
+          const v2i raw = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+              (__attribute__((address_space(3))) v2i*)(tp + 32 * i));
+          v4u bw;
+          bw.x = __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8((unsigned)raw.x, 1.0f, false)) & mk.x;
+          bw.y = __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8((unsigned)raw.x, 1.0f, true)) & mk.y;
+          bw.z = __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8((unsigned)raw.y, 1.0f, false)) & mk.z;
+          bw.w = __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8((unsigned)raw.y, 1.0f, true)) & mk.w;
+          o[i] = __builtin_amdgcn_mfma_f32_32x32x16_f16(pa, __builtin_bit_cast(v8h, bw), o[i], 0, 0, 0);
+        }
+      }
+    }
+  };
+
+  // ---- pipeline.  Iteration i: gather tile i+2 (and the positions of tile i+3), build the
+  // row data of tile i, P.V of tile i-1, Q.K^T of tile i; barrier; softmax of tile i and
+  // wait for tile i+1; barrier.  Tiles are global (E2M1) rows first, then window (E4M3)
+  // rows, so the iterations run as separate loops per pair of kinds and no inner loop
+  // branches on the kind.
+  using KN = std::integral_constant<int, 0>;      // no tile
+  using KG = std::integral_constant<int, 1>;      // global E2M1 tile
+  using KW = std::integral_constant<int, 2>;      // window E4M3 tile
+  auto body = [&](auto PVK, auto QKK, int i) __attribute__((always_inline)) {
+    constexpr int pvk = decltype(PVK)::value, qkk = decltype(QKK)::value;
+    const int n = i - tb;
+    const bool more = i + 2 < te;
+    const bool more_g = i + 2 < c.ng;
+    if (wave >= 4) {
+      if (wave == 4 && i + 3 < te && i + 3 < c.ng) load_pos(i + 3, (n + 3) & 3);
+      if (more) issue(i + 2, (n + 2) & 3, (n + 2) & 3);
+      if constexpr (qkk != 0) convert(std::integral_constant<bool, qkk == 1>{}, i, n & 3, n & 3, n & 1);
+    }
+    if constexpr (pvk != 0) pv(std::integral_constant<bool, pvk == 1>{}, (n - 1) & 3, (n - 1) & 1);
+    if constexpr (qkk != 0) qk(std::integral_constant<bool, qkk == 1>{}, n & 3);
+    __syncthreads();                               // partial logits and row data of tile i
+    if constexpr (qkk != 0) softmax();
+    // tile i+1 (and the positions of tile i+3) landed; tile i+2 may still be in flight
+    if (wave >= 4) {
+      if (!more) __builtin_amdgcn_s_waitcnt(0);
+      else if (more_g) wait_vmcnt<G::NLOAD4>();
+      else wait_vmcnt<G::NLOAD8>();
+    }
+    __syncthreads();                               // P(i), tile i+1 published
+  };
+  if (tb < te) {
+    const int ng = c.ng;
+    int i = tb;
+    if (i < ng) body(KN{}, KG{}, i);
+    else body(KN{}, KW{}, i);
+    for (++i; i < te && i < ng; ++i) body(KG{}, KG{}, i);
+    if (i < te && i == ng) body(KG{}, KW{}, i++);
+    for (; i < te; ++i) body(KW{}, KW{}, i);
+    if (te - 1 < ng) body(KG{}, KN{}, te);
+    else body(KW{}, KN{}, te);
+  }
+
+  // ---- epilogue: row sums, outputs of this wave's blocks, LSE / partial state
+  SMQA_LANE_ROLES
+  {
+    const float l = row_reduce<false>(lpart);
+    if (i16 == 0) mlsum[4 * wave + (lane >> 4)] = l;
+  }
+  __syncthreads();
+  float inv[16];
+#pragma unroll
+  for (int q4 = 0; q4 < 4; ++q4)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const float l = mlsum[8 * q4 + 4 * kh + e];
+      inv[4 * q4 + e] = (S == 1) ? (l > 0.0f ? 1.0f / l : 0.0f) : 1.0f;
+    }
+  float* dst = (S == 1) ? a.out + ((int64_t)t * a.Hq + h0) * D
+                        : (float*)a.ws + (((int64_t)split * a.T + t) * a.Hq + h0) * D;
+#pragma unroll
+  for (int i = 0; i < G::NBW; ++i) {
+    if (i < G::BPW || wave < G::EXTRA) {
+      const int d = 32 * (b0 + i) + r32;
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int hl = 8 * q4 + 4 * kh + e;
+          dst[(int64_t)hl * D + d] = o[i][4 * q4 + e] * inv[4 * q4 + e];
+        }
+    }
+  }
+  if (tid < 32) {
+    const int hg = h0 + tid;
+    const float m = mref[tid], l = mlsum[tid];
+    if (S == 1) {
+      if (a.lse) a.lse[(int64_t)t * a.Hq + hg] = l > 0.0f ? (m + log2f(l)) * kLn2 : -__builtin_inff();
+    } else {
+      float* ml = (float*)a.ws + (size_t)S * a.T * a.Hq * D;
+      const int64_t ii = ((int64_t)split * a.T + t) * a.Hq + hg;
+      ml[2 * ii] = m;
+      ml[2 * ii + 1] = l;
+    }
+  }
+}
+
+template <int D>
+hipError_t launch(const AttendArgs& a, int S, hipStream_t s) {
+  using G = Geo<D>;
+  const int ngroups = a.Hq / 32;
+  const int total = a.T * ngroups * S;
+  const int nb = (total + 7) / 8 * 8;
+  static bool attr = false;
+  if (!attr) {
+    hipError_t e = hipFuncSetAttribute((const void*)attend_kernel<D>,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, G::LDS);
+    if (e != hipSuccess) return e;
+    attr = true;
+  }
+  hipLaunchKernelGGL(attend_kernel<D>, dim3(nb), dim3(kThreads), G::LDS, s, a, S, ngroups, total);
+  hipError_t e = hipGetLastError();
+  return e != hipSuccess ? e : launch_attend_merge(a, S, s);
+}
+
+}  // namespace sd
+
+// Dimension-split attention for Hq % 32 == 0 and D <= 1664 (the register budget of 8
+// waves holding 32 heads of outputs and q, and four tile buffers in LDS); returns
+// hipErrorInvalidValue otherwise.
+hipError_t launch_attend_sd(const AttendArgs& a, int S, hipStream_t s) {
+  switch (a.D) {
+#define SMQA_SD_D(d) case d: return sd::launch<d>(a, S, s);
+    SMQA_SD_D(128) SMQA_SD_D(256) SMQA_SD_D(384) SMQA_SD_D(512)
+    SMQA_SD_D(640) SMQA_SD_D(768) SMQA_SD_D(896) SMQA_SD_D(1024)
+    SMQA_SD_D(1152) SMQA_SD_D(1280) SMQA_SD_D(1408) SMQA_SD_D(1536)
+    SMQA_SD_D(1664)
+#undef SMQA_SD_D
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace smqa
