@@ -10,10 +10,10 @@
 // 32-dim latent blocks (the E8M0 block size) for both products, so every dequantised
 // value feeds 32 heads of MFMA work and no wave converts a value another wave needs.
 //
-//   gather   global_load_lds_dwordx4 straight into one of three LDS tile buffers (rows
-//            padded so both read patterns below are bank-conflict free); the raw E8M0
-//            bytes and the row scales land beside them.  Tile i+2 is in flight while tile
-//            i+1 is scored and tile i is accumulated.
+//   gather   global_load_lds_dwordx4 straight into one of four LDS tile buffers (rows
+//            padded so both read patterns below are bank-conflict free), issued by all 8
+//            waves; the raw E8M0 bytes and the row scales land beside them.  Tile i+2 is
+//            in flight while tile i is scored and tile i-1 is accumulated.
 //   Q.K^T    v_mfma_f32_32x32x16_bf16, heads x rows: each lane reads 8 dims of one row
 //            (ds_read_b32 for E2M1, ds_read_b64 for E4M3) and converts them exactly to
 //            bf16 with the block's E8M0 scale (v_cvt_scalef32_pk_bf16_*); q stays in
@@ -77,8 +77,8 @@ struct Geo {
   static constexpr int LDS = MR + 3 * 32 * 4;
   // global loads a loader wave issues per tile (fixed, so vmcnt can wait for the older tile)
   static constexpr int PIECES8 = D / 16;                        // 16-byte pieces of an E4M3 row
-  static constexpr int NLOAD4 = kRows / 4 + 2 + 1;              // 8 code rows, 2 E8M0, rho
-  static constexpr int NLOAD8 = (kWRows / 4) * (PIECES8 > 64 ? 2 : 1) + 1;  // 4 rows, sigma
+  static constexpr int NLOAD4 = kRows / 8 + 1 + 1;              // 4 code rows, E8M0, rho
+  static constexpr int NLOAD8 = (kWRows / 8) * (PIECES8 > 64 ? 2 : 1) + 1;  // 2 rows, sigma
   static_assert(kWRows * RS8 <= CODES, "a window tile must fit a buffer");
   static_assert(EXTRA == 0 || EXTRA == 4, "D must be a multiple of 128");
   static_assert(LDS <= 160 * 1024, "LDS budget");
@@ -229,9 +229,8 @@ __global__ __launch_bounds__(kThreads) void attend_kernel(AttendArgs a, int S, i
   // wave w's blocks [b0, b0 + BPW + (w < EXTRA))
   const int b0 = wave * G::BPW + min(wave, G::EXTRA);
 
-  // ---- loads of one tile: positions (into the ring) and rows (into a buffer).  Waves 4..7
-  // (one 32-dim block fewer than waves 0..3 when the block count is uneven) do all loads.
-  const int wq = wave - 4;                          // loader index, valid for waves 4..7
+  // ---- loads of one tile: positions (into the ring) and rows (into a buffer).  Every wave
+  // loads rows 8u + wave of the tile, so the loads of a tile are spread over all 8 waves.
   auto load_pos = [&](int tile, int rslot) __attribute__((always_inline)) {       // wave 4, lanes 0..31
     const int ln = opq(lane);
     const int x = tile * kRows + (ln & 31);
@@ -248,42 +247,38 @@ __global__ __launch_bounds__(kThreads) void attend_kernel(AttendArgs a, int S, i
       // every position this wave needs, read before one wait: all 32 (for the code rows),
       // the rows of its two E8M0 loads, the rows of its rho lanes
       const int pall = pos[ln & 31];
-      const int re0 = 8 * wq + ln / per_row, re1 = re0 + 4;
-      const int pe0 = pos[re0 & 31], pe1 = pos[re1 & 31];
-      const int rr = 4 * (ln & 7) + wq;
+      const int re = 4 * wave + ln / per_row;
+      const int pe = pos[re & 31];
+      const int rr = 8 * (ln & 3) + wave;
       const int pr = pos[rr];
-      // code rows 4u + wq, u = 0..7
+      // code rows 8u + wave, u = 0..3
 #pragma unroll
-      for (int u = 0; u < kRows / 4; ++u) {
-        const int r = 4 * u + wq;
+      for (int u = 0; u < kRows / 8; ++u) {
+        const int r = 8 * u + wave;
         const int j = __builtin_amdgcn_readlane(pall, r);
         const bool ok = xt + r < c.gx1 && j >= 0;
         const uint8_t* src = ok ? a.kv_codes + (c.base + j) * (D / 2) : dummy;
         if (ln < D / 32) gload16(src + 16 * ln, lds_addr(B + r * G::RS4));
       }
-      // raw E8M0: rows 8wq + 4h .. +4, contiguous
+      // raw E8M0: rows 4 wave .. +4, contiguous
       {
         const int dd = ln % per_row;
-        const bool ok0 = xt + re0 < c.gx1 && pe0 >= 0, ok1 = xt + re1 < c.gx1 && pe1 >= 0;
-        const uint8_t* s0 = ok0 ? a.kv_e8m0 + (c.base + pe0) * (D / 32) : dummy;
-        const uint8_t* s1 = ok1 ? a.kv_e8m0 + (c.base + pe1) * (D / 32) : dummy;
-        if (ln < 4 * per_row) {
-          gload4(s0 + 4 * dd, lds_addr(B + G::E8 + 8 * wq * G::E8S));
-          gload4(s1 + 4 * dd, lds_addr(B + G::E8 + (8 * wq + 4) * G::E8S));
-        }
+        const bool ok = xt + re < c.gx1 && pe >= 0;
+        const uint8_t* s0 = ok ? a.kv_e8m0 + (c.base + pe) * (D / 32) : dummy;
+        if (ln < 4 * per_row) gload4(s0 + 4 * dd, lds_addr(B + G::E8 + 4 * wave * G::E8S));
       }
-      {  // rho of rows 4u + wq, u = lane < 8 -> RHO[wq][u]
+      {  // rho of rows 8u + wave, u = lane < 4 -> RHO[wave][u]
         const bool ok = a.kv_rowscale && xt + rr < c.gx1 && pr >= 0;
         const void* src = ok ? (const void*)(a.kv_rowscale + c.base + pr) : (const void*)dummy;
-        if (ln < 8) gload4(src, lds_addr(B + G::RHO + 32 * wq));
+        if (ln < 4) gload4(src, lds_addr(B + G::RHO + 16 * wave));
       }
     } else {
-      // window tile: rows 4u + wq, u = 0..3; D/16 pieces of 16 bytes per row (two loads
+      // window tile: rows 8u + wave, u = 0..1; D/16 pieces of 16 bytes per row (two loads
       // when > 64)
       const int wt = c.wt0 + tile - c.ng;
 #pragma unroll
-      for (int u = 0; u < kWRows / 4; ++u) {
-        const int r = 4 * u + wq;
+      for (int u = 0; u < kWRows / 8; ++u) {
+        const int r = 8 * u + wave;
         const int uu = kWRows * wt + r;
         const uint8_t* src = uu < c.W ? a.swa + ((int64_t)c.b * c.W + uu) * D : dummy;
         if (ln < (G::PIECES8 < 64 ? G::PIECES8 : 64)) gload16(src + 16 * ln, lds_addr(B + r * G::RS8));
@@ -291,11 +286,11 @@ __global__ __launch_bounds__(kThreads) void attend_kernel(AttendArgs a, int S, i
           if (ln < G::PIECES8 - 64) gload16(src + 1024 + 16 * ln, lds_addr(B + r * G::RS8 + 1024));
         }
       }
-      {  // sigma of rows 4u + wq, u = lane < 4 -> RHO[wq][u]
-        const int uu = kWRows * wt + 4 * (ln & 3) + wq;
+      {  // sigma of rows 8u + wave, u = lane < 2 -> RHO[wave][u]
+        const int uu = kWRows * wt + 8 * (ln & 1) + wave;
         const bool ok = a.swa_scale && uu < c.W;
         const void* src = ok ? (const void*)(a.swa_scale + (int64_t)c.b * c.W + uu) : (const void*)dummy;
-        if (ln < 4) gload4(src, lds_addr(B + G::RHO + 32 * wq));
+        if (ln < 2) gload4(src, lds_addr(B + G::RHO + 16 * wave));
       }
     }
   };
@@ -327,10 +322,8 @@ __global__ __launch_bounds__(kThreads) void attend_kernel(AttendArgs a, int S, i
   }
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
-  if (wave >= 4) {
-    if (tb < te) issue(tb, 0, 0);
-    if (tb + 1 < te) issue(tb + 1, 1, 1);
-  }
+  if (tb < te) issue(tb, 0, 0);
+  if (tb + 1 < te) issue(tb + 1, 1, 1);
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
 
@@ -406,7 +399,7 @@ __global__ __launch_bounds__(kThreads) void attend_kernel(AttendArgs a, int S, i
       }
       if (ct < kRows) {
         const bool v = (vmask >> ct) & 1u;
-        const float m = a.kv_rowscale ? ((const float*)(B + G::RHO))[8 * (ct & 3) + (ct >> 2)] : 1.0f;
+        const float m = a.kv_rowscale ? ((const float*)(B + G::RHO))[4 * (ct & 7) + (ct >> 3)] : 1.0f;
         rl[ct] = v ? c.lscale * m : 0.0f;
         rp[ct] = v ? m : 0.0f;
       }
@@ -415,7 +408,7 @@ __global__ __launch_bounds__(kThreads) void attend_kernel(AttendArgs a, int S, i
       const int pos = c.pos0 + uu;
       const bool v = ct < kWRows && uu < c.W && pos >= c.lo_win && pos <= c.p;
       const unsigned vb = (unsigned)__builtin_amdgcn_ballot_w64(v);   // rows 0..15 of wave 4
-      const float m = a.swa_scale ? ((const float*)(B + G::RHO))[8 * (ct & 3) + ((ct & 15) >> 2)] : 1.0f;
+      const float m = a.swa_scale ? ((const float*)(B + G::RHO))[4 * (ct & 7) + ((ct & 15) >> 3)] : 1.0f;
       rl[ct] = v ? c.lscale * m : 0.0f;
       rp[ct] = v ? m : 0.0f;
       if (ct < kWRows / 2) {
@@ -543,21 +536,19 @@ __global__ __launch_bounds__(kThreads) void attend_kernel(AttendArgs a, int S, i
     const int n = i - tb;
     const bool more = i + 2 < te;
     const bool more_g = i + 2 < c.ng;
-    if (wave >= 4) {
-      if (wave == 4 && i + 3 < te && i + 3 < c.ng) load_pos(i + 3, (n + 3) & 3);
-      if (more) issue(i + 2, (n + 2) & 3, (n + 2) & 3);
-      if constexpr (qkk != 0) convert(std::integral_constant<bool, qkk == 1>{}, i, n & 3, n & 3, n & 1);
+    if (wave == 4 && i + 3 < te && i + 3 < c.ng) load_pos(i + 3, (n + 3) & 3);
+    if (more) issue(i + 2, (n + 2) & 3, (n + 2) & 3);
+    if constexpr (qkk != 0) {
+      if (wave >= 4) convert(std::integral_constant<bool, qkk == 1>{}, i, n & 3, n & 3, n & 1);
     }
     if constexpr (pvk != 0) pv(std::integral_constant<bool, pvk == 1>{}, (n - 1) & 3, (n - 1) & 1);
     if constexpr (qkk != 0) qk(std::integral_constant<bool, qkk == 1>{}, n & 3);
     __syncthreads();                               // partial logits and row data of tile i
     if constexpr (qkk != 0) softmax();
     // tile i+1 (and the positions of tile i+3) landed; tile i+2 may still be in flight
-    if (wave >= 4) {
-      if (!more) __builtin_amdgcn_s_waitcnt(0);
-      else if (more_g) wait_vmcnt<G::NLOAD4>();
-      else wait_vmcnt<G::NLOAD8>();
-    }
+    if (!more) __builtin_amdgcn_s_waitcnt(0);
+    else if (more_g) wait_vmcnt<G::NLOAD4>();
+    else wait_vmcnt<G::NLOAD8>();
     __syncthreads();                               // P(i), tile i+1 published
   };
   if (tb < te) {
