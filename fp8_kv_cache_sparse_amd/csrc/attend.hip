@@ -997,6 +997,9 @@ __global__ __launch_bounds__(kAttThreads) void attend_kernel(AttendArgs a, int S
 
 // ================================================================ merge and dispatch
 // out[t,h,d] = sum_s 2^(m_s - M) O_s[d] / sum_s 2^(m_s - M) l_s ; one thread per output dim.
+// Every thread issues its S partial loads before the weights are known, so the whole merge
+// costs one round trip to memory (SMAX >= S partials per output, at most 64).
+template <int SMAX>
 __global__ __launch_bounds__(256) void attend_merge_kernel(AttendArgs a, int S) {
   __shared__ float wts[64];
   __shared__ float sL, sM;
@@ -1006,6 +1009,13 @@ __global__ __launch_bounds__(256) void attend_merge_kernel(AttendArgs a, int S) 
   const float* opart = (const float*)a.ws;
   const float* ml = opart + (size_t)S * a.T * a.Hq * D;
   const size_t sstride = (size_t)a.T * a.Hq * D;
+  const int d = blockIdx.x * 256 + threadIdx.x;
+  float v[SMAX];
+  {
+    const float* src = opart + ((int64_t)t * a.Hq + h) * D + (d < D ? d : 0);
+#pragma unroll
+    for (int s = 0; s < SMAX; ++s) v[s] = s < S ? src[s * sstride] : 0.0f;
+  }
   if (threadIdx.x < 64) {
     const int s = threadIdx.x;
     float ms = -__builtin_inff(), ls = 0.0f;
@@ -1030,12 +1040,11 @@ __global__ __launch_bounds__(256) void attend_merge_kernel(AttendArgs a, int S) 
   __syncthreads();
   const float L = sL;
   const float inv = L > 0.0f ? 1.0f / L : 0.0f;
-  const int d = blockIdx.x * 256 + threadIdx.x;
   if (d < D) {
-    const float* src = opart + ((int64_t)t * a.Hq + h) * D + d;
     float acc = 0.0f;
-#pragma unroll 8
-    for (int s = 0; s < S; ++s) acc += wts[s] * src[s * sstride];
+#pragma unroll
+    for (int s = 0; s < SMAX; ++s)
+      if (s < S) acc += wts[s] * v[s];
     a.out[((int64_t)t * a.Hq + h) * D + d] = acc * inv;
   }
   if (blockIdx.x == 0 && threadIdx.x == 0 && a.lse)
@@ -1057,7 +1066,9 @@ struct AttPlan {
 
 static AttPlan attend_plan(int32_t T, int32_t k, int32_t W, int32_t Hq, int32_t D) {
   AttPlan p;
-  p.wide = Hq % 32 == 0 && D <= 1792 && (int64_t)T * (Hq / 32) >= 64;
+  // the dimension-split kernel for every query count it supports; the 16-head-group
+  // kernels for the rest (the 32-head tile kernel only once there are enough workgroups)
+  p.wide = Hq % 32 == 0 && (D <= 1664 || (D <= 1792 && (int64_t)T * (Hq / 32) >= 64));
   p.MT = p.wide ? 2 : ((Hq % 32 == 0 && D <= 1024) ? 2 : 1);
   p.ngroups = Hq / (16 * p.MT);
   const int ntiles = max_tiles(k, W);
@@ -1084,7 +1095,10 @@ size_t attend_workspace_bytes(int32_t T, int32_t k, int32_t W, int32_t Hq, int32
 
 hipError_t launch_attend_merge(const AttendArgs& a, int S, hipStream_t s) {
   if (S == 1) return hipSuccess;
-  hipLaunchKernelGGL(attend_merge_kernel, dim3((a.D + 255) / 256, a.T * a.Hq), dim3(256), 0, s, a, S);
+  const dim3 grid((a.D + 255) / 256, a.T * a.Hq);
+  if (S <= 16) hipLaunchKernelGGL(attend_merge_kernel<16>, grid, dim3(256), 0, s, a, S);
+  else if (S <= 32) hipLaunchKernelGGL(attend_merge_kernel<32>, grid, dim3(256), 0, s, a, S);
+  else hipLaunchKernelGGL(attend_merge_kernel<64>, grid, dim3(256), 0, s, a, S);
   return hipGetLastError();
 }
 

@@ -167,6 +167,45 @@ __device__ __forceinline__ void gload4(const void* src, unsigned m0) {
   asm volatile("global_load_lds_dword %0, off" ::"v"(src), "{m0}"(m0) : "memory");
 }
 
+// The per-query values: q_pos[t], swa_clip[t] and the sequence of query t (the largest b
+// with q_start[b] <= t) with its seq_start and swa_pos0 entries, by a 64-way search: each
+// lane reads one sample of the three arrays, so for B <= 64 everything arrives in a single
+// round trip to memory.
+struct SeqInfo {
+  int b;
+  int64_t base;
+  int pos0;
+  int p;
+  int clip;
+};
+__device__ __forceinline__ SeqInfo locate_seq(const AttendArgs& a, int t, int lane) {
+  int lo = 0, hi = a.B;
+  const int extra = lane == 0 ? a.q_pos[t] : (lane == 1 && a.swa_clip ? a.swa_clip[t] : 0);
+  for (;;) {
+    const int step = (hi - lo + 63) / 64;
+    const int idx = lo + lane * step;
+    const bool in = idx < hi;
+    const int qs = in ? a.q_start[idx] : 0;
+    const int64_t ss = in ? a.seq_start[idx] : 0;
+    const int p0 = in ? a.swa_pos0[idx] : 0;
+    asm volatile("" ::"v"(qs), "v"(ss), "v"(p0), "v"(extra));   // one wait for all four loads
+    const int L = max(__builtin_popcountll(__builtin_amdgcn_ballot_w64(in && qs <= t)) - 1, 0);
+    if (step == 1) {
+      SeqInfo r;
+      r.b = lo + L;
+      const uint64_t u = (uint64_t)ss;
+      r.base = (int64_t)(((uint64_t)(unsigned)__builtin_amdgcn_readlane((int)(u >> 32), L) << 32) |
+                         (unsigned)__builtin_amdgcn_readlane((int)u, L));
+      r.pos0 = __builtin_amdgcn_readlane(p0, L);
+      r.p = __builtin_amdgcn_readlane(extra, 0);
+      r.clip = __builtin_amdgcn_readlane(extra, 1);
+      return r;
+    }
+    lo += L * step;
+    hi = min(lo + step, hi);
+  }
+}
+
 template <int D>
 __global__ __launch_bounds__(kThreads) void attend_kernel(AttendArgs a, int S, int ngroups, int total) {
   using G = Geo<D>;
@@ -189,29 +228,23 @@ __global__ __launch_bounds__(kThreads) void attend_kernel(AttendArgs a, int S, i
   const int bid = blockIdx.x;
   const int logical = (bid & 7) * (nb >> 3) + (bid >> 3);
   if (logical >= total) return;
-  const int grp = logical % ngroups;
-  const int split = (logical / ngroups) % S;
-  const int t = logical / (S * ngroups);
+  const int grp = __builtin_amdgcn_readfirstlane(logical % ngroups);
+  const int split = __builtin_amdgcn_readfirstlane((logical / ngroups) % S);
+  const int t = __builtin_amdgcn_readfirstlane(logical / (S * ngroups));
   const int h0 = grp * 32;
 
+  // Tile ranges are cut from the largest possible tile count (every window tile of the
+  // ring), so a split's global tiles, and the positions of its first ones, are known
+  // before any per-query value has been read; the window part of a range is clipped to
+  // the query's visible window once those values arrive.
   Ctx c;
   c.k = a.k;
   c.W = a.W;
-  c.b = seq_of_query(a.q_start, a.B, t);
-  c.base = a.seq_start[c.b];
-  c.p = a.q_pos[t];
-  c.lo_win = max(c.p - c.W + 1, 0);
-  if (a.swa_clip) c.lo_win = max(c.lo_win, a.swa_clip[t]);
-  c.pos0 = a.swa_pos0[c.b];
   c.lscale = a.sm_scale * kLog2e;
   c.ng = (c.k + kRows - 1) / kRows;
-  const int u_lo = max(c.lo_win - c.pos0, 0);
-  const int u_hi = min(c.p - c.pos0, c.W - 1);
-  c.wt0 = u_lo / kWRows;
-  const int nwt = u_lo <= u_hi ? u_hi / kWRows - c.wt0 + 1 : 0;
-  const int ntiles = c.ng + nwt;
-  c.tb = (int)((int64_t)split * ntiles / S);
-  c.te = (int)((int64_t)(split + 1) * ntiles / S);
+  const int nominal = c.ng + (c.W + kWRows - 1) / kWRows;
+  c.tb = (int)((int64_t)split * nominal / S);
+  c.te = (int)((int64_t)(split + 1) * nominal / S);
   c.gx1 = min(min(c.te, c.ng) * kRows, c.k);       // global rows of this split end here
 
   float* mref = (float*)(smem + G::MR);
@@ -295,11 +328,11 @@ __global__ __launch_bounds__(kThreads) void attend_kernel(AttendArgs a, int S, i
     }
   };
 
-  // ---- prologue: softmax state, q in registers, positions of the first three tiles,
-  // rows of the first two
-  if (tid < 32) {
-    mref[tid] = -__builtin_inff();
-    malpha[tid] = 1.0f;
+  // ---- prologue: positions of the first three tiles, q and the per-query values (one
+  // round trip), then the rows of the first two tiles
+  if (wave == 4) {
+    for (int u = 0; u < 3; ++u)
+      if (c.tb + u < c.te && c.tb + u < c.ng) load_pos(c.tb + u, u);
   }
   // A operands of Q.K^T: head h0 + r32, dims 32 b + 16 kh + 8 cc .. +8 of block b = b0 + i
   v8bf qa[G::NBW][2];
@@ -315,11 +348,27 @@ __global__ __launch_bounds__(kThreads) void attend_kernel(AttendArgs a, int S, i
         qa[i][cc] = __builtin_bit_cast(v8bf, v);
       }
   }
-  const int tb = c.tb, te = c.te;
-  if (wave == 4) {
-    for (int u = 0; u < 3; ++u)
-      if (tb + u < te && tb + u < c.ng) load_pos(tb + u, u);
+  {
+    const SeqInfo si = locate_seq(a, t, lane);
+    c.b = si.b;
+    c.base = si.base;
+    c.pos0 = si.pos0;
+    c.p = si.p;
+    c.lo_win = max(max(c.p - c.W + 1, 0), si.clip);
   }
+  if (tid < 32) {
+    mref[tid] = -__builtin_inff();
+    malpha[tid] = 1.0f;
+  }
+  {
+    const int u_lo = max(c.lo_win - c.pos0, 0);
+    const int u_hi = min(c.p - c.pos0, c.W - 1);
+    c.wt0 = u_lo / kWRows;
+    const int nwt = u_lo <= u_hi ? u_hi / kWRows - c.wt0 + 1 : 0;
+    c.te = min(c.te, c.ng + nwt);
+    c.tb = min(c.tb, c.te);
+  }
+  const int tb = c.tb, te = c.te;
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   if (tb < te) issue(tb, 0, 0);
