@@ -83,12 +83,13 @@ def work(wl):
 
 # kernels behind each stage's entry point (what rocprofv3 lists for it)
 STAGE_KERNELS = {
-    "score": "score_kernel",
+    "score": "score_kernel | score_stream_kernel (one query per sequence, long rows)",
     "topk": "topk_small_kernel (rows <= 16384) | topk_zero/hist/collect/finish_kernel",
-    "attend": "attend_kernel + attend_merge_kernel (split partials)",
+    "attend": "sd::attend_kernel (dimension split; lat::/thr:: for other head counts and widths) "
+              "+ attend_merge_kernel (split partials)",
 }
 TRAFFIC_MD = os.path.join(ROOT, "profiles", "pmc_traffic.md")
-SOURCES = {"score": ["score.hip"], "topk": ["topk.hip"], "attend": ["attend.hip"]}
+SOURCES = {"score": ["score.hip"], "topk": ["topk.hip"], "attend": ["attend.hip", "attend_sd.hip"]}
 
 
 def source_digest(stage):
