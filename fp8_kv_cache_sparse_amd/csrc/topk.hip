@@ -379,6 +379,7 @@ __global__ __launch_bounds__(1024) void topk_small_kernel(TopkArgs a) {
   const int t = blockIdx.x, tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const float* row = a.scores + (int64_t)t * a.ld;
+  static_assert(2 * NT == 2048, "two histogram bins per thread");
   // row loads first (bounded by the row width, known without any load), the query's
   // column count (a chain of small dependent loads) meanwhile
   float v[PER];
@@ -393,6 +394,8 @@ __global__ __launch_bounds__(1024) void topk_small_kernel(TopkArgs a) {
     const int col = tid + NT * u;
     keys[col] = col < ncols ? score_key(v[u]) : 0u;
   }
+  hist[2 * tid] = 0u;                              // zero for the first radix pass
+  hist[2 * tid + 1] = 0u;
   __syncthreads();
   unsigned key[PER];
 #pragma unroll
@@ -446,25 +449,40 @@ __global__ __launch_bounds__(1024) void topk_small_kernel(TopkArgs a) {
       const int dbits = min(11, 32 - nbits);
       const int shift = 32 - nbits - dbits;
       const unsigned dmask = (1u << dbits) - 1u;
-      hist[2 * tid] = 0u;
-      hist[2 * tid + 1] = 0u;
-      __syncthreads();
 #pragma unroll
       for (int u = 0; u < PER; ++u) {
         const bool match = key[u] != 0u && (nbits == 0 || (key[u] >> (32 - nbits)) == (prefix >> (32 - nbits)));
         if (match) atomicAdd(&hist[(key[u] >> shift) & dmask], 1u);
       }
       __syncthreads();
-      if (wave == 0) wave_find_digit<32>(hist, need, sh);
+      // the digit, over the whole block: thread i holds bins 2047 - 2i and 2046 - 2i (the
+      // bins count down with the thread index, so a prefix sum counts the keys above)
+      const int h1 = (int)hist[2047 - 2 * tid], h0 = (int)hist[2046 - 2 * tid];
+      const int local = h1 + h0;
+      const int incl = wave_inclusive_sum(local);
+      if (lane == 63) scan_lds[wave] = incl;
+      if (tid == 0) sh[0] = -1;
+      __syncthreads();
+      int cum = incl - local;
+#pragma unroll
+      for (int i = 0; i < NT / 64; ++i)
+        if (i < wave) cum += scan_lds[i];
+      if (cum < need && need <= cum + local) {
+        const bool upper = need <= cum + h1;
+        sh[0] = upper ? 2047 - 2 * tid : 2046 - 2 * tid;
+        sh[1] = upper ? cum : cum + h1;
+        sh[2] = upper ? h1 : h0;
+      }
+      hist[2 * tid] = 0u;                          // every bin was read before the barrier
+      hist[2 * tid + 1] = 0u;
       __syncthreads();
       const int d = sh[0];
       if (d < 0) break;                            // cannot happen: nvalid > k
       const int above = sh[1];
-      const int inbin = (int)hist[d];
+      const int inbin = sh[2];
       need -= above;
       prefix |= (unsigned)d << shift;
       nbits += dbits;
-      __syncthreads();                             // hist and sh are rewritten next pass
       if (inbin == need) {                         // the whole bin is taken
         whole_bin = true;
         break;
@@ -495,16 +513,20 @@ __global__ __launch_bounds__(1024) void topk_small_kernel(TopkArgs a) {
     for (int u = 0; u < PER; ++u)
       if (c0 + u < a.n_cand) pos[u] = a.cand[(int64_t)t * a.n_cand + c0 + u];
   }
+  // the selection is staged in LDS (the key array is free: the keys are in registers)
+  // and written out with coalesced stores
+  int* stage = (int*)keys;
 #pragma unroll
   for (int u = 0; u < PER; ++u) {
     bool sel = key[u] > tau;
     if (key[u] == tau) sel = tie_rank++ < tie_need;
     if (sel) {
-      if (off < a.k) dst[off] = pos[u];
+      if (off < a.k) stage[off] = pos[u];
       ++off;
     }
   }
-  for (int i = min(nsel, a.k) + tid; i < a.k; i += NT) dst[i] = -1;
+  __syncthreads();
+  for (int i = tid; i < a.k; i += NT) dst[i] = i < nsel ? stage[i] : -1;
 }
 
 // ------------------------------------------------------------------ long rows
