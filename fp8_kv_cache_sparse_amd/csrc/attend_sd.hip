@@ -26,7 +26,8 @@
 //            lane) comes straight from the row-major tile through the LDS transpose reads
 //            ds_read_b64_tr_b4 (E2M1: 16 rows of one dim per lane) and ds_read_b64_tr_b8
 //            (E4M3), is converted to fp16 with scale 1 and multiplied by the rows' block
-//            scales (v_pk_mul_f16, exact while -24 <= e - 127 <= 15); P carries the row
+//            scales (v_pk_mul_f16: the scale is exact in fp16 for -24 <= e - 127 <= 15, the
+//            product for -23 <= e - 127 <= 13); P carries the row
 //            scale rho (or sigma).
 //
 // Several tile ranges of one (query, head group) leave unnormalised partials that
