@@ -423,7 +423,7 @@ __global__ __launch_bounds__(kThreads) void attend_kernel(AttendArgs a, int S, i
   // or sigma), and the V-operand block scales as fp16 pairs (rows 2pp, 2pp+1; zero for
   // rows that take no part) or, for a window tile, 16-bit row masks in pairs.
   auto convert = [&](auto FP4, int tile, int slot, int rslot, int sslot) __attribute__((always_inline)) {
-    const int ct = opq(tid) - 256;                 // waves 4..7: 0..255
+    const int ct = opq(tid);                       // waves 0..3: 0..255
     const int ln = ct & 63;
     const uint8_t* B = smem + slot * G::BUF;
     unsigned* sch = (unsigned*)(smem + G::SCH) + sslot * G::NB * 16;
@@ -457,7 +457,7 @@ __global__ __launch_bounds__(kThreads) void attend_kernel(AttendArgs a, int S, i
       const int uu = kWRows * (c.wt0 + tile - c.ng) + ct;
       const int pos = c.pos0 + uu;
       const bool v = ct < kWRows && uu < c.W && pos >= c.lo_win && pos <= c.p;
-      const unsigned vb = (unsigned)__builtin_amdgcn_ballot_w64(v);   // rows 0..15 of wave 4
+      const unsigned vb = (unsigned)__builtin_amdgcn_ballot_w64(v);   // rows 0..15 of wave 0
       const float m = a.swa_scale ? ((const float*)(B + G::RHO))[4 * (ct & 7) + ((ct & 15) >> 3)] : 1.0f;
       rl[ct] = v ? c.lscale * m : 0.0f;
       rp[ct] = v ? m : 0.0f;
@@ -588,11 +588,13 @@ __global__ __launch_bounds__(kThreads) void attend_kernel(AttendArgs a, int S, i
     const bool more_g = i + 2 < c.ng;
     if (wave == 4 && i + 3 < te && i + 3 < c.ng) load_pos(i + 3, (n + 3) & 3);
     if (more) issue(i + 2, (n + 2) & 3, (n + 2) & 3);
-    if constexpr (qkk != 0) {
-      if (wave >= 4) convert(std::integral_constant<bool, qkk == 1>{}, i, n & 3, n & 3, n & 1);
-    }
     if constexpr (pvk != 0) pv(std::integral_constant<bool, pvk == 1>{}, (n - 1) & 3, (n - 1) & 1);
     if constexpr (qkk != 0) qk(std::integral_constant<bool, qkk == 1>{}, n & 3);
+    // waves 0..3 build the row data of tile i after their products, in time they would
+    // otherwise spend waiting at the barrier for waves 4..7 (per-phase cycle counters)
+    if constexpr (qkk != 0) {
+      if (wave < 4) convert(std::integral_constant<bool, qkk == 1>{}, i, n & 3, n & 3, n & 1);
+    }
     __syncthreads();                               // partial logits and row data of tile i
     if constexpr (qkk != 0) softmax();
     // tile i+1 (and the positions of tile i+3) landed; tile i+2 may still be in flight
