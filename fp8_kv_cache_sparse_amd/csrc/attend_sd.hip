@@ -265,7 +265,7 @@ __global__ __launch_bounds__(kThreads) void attend_kernel(AttendArgs a, int S, i
 
   // ---- loads of one tile: positions (into the ring) and rows (into a buffer).  Every wave
   // loads rows 8u + wave of the tile, so the loads of a tile are spread over all 8 waves.
-  auto load_pos = [&](int tile, int rslot) __attribute__((always_inline)) {       // wave 4, lanes 0..31
+  auto load_pos = [&](int tile, int rslot) __attribute__((always_inline)) {       // wave 0, lanes 0..31
     const int ln = opq(lane);
     const int x = tile * kRows + (ln & 31);
     const void* src = x < c.gx1 ? (const void*)(a.idx + (int64_t)t * c.k + x) : (const void*)dummy;
@@ -331,7 +331,7 @@ __global__ __launch_bounds__(kThreads) void attend_kernel(AttendArgs a, int S, i
 
   // ---- prologue: positions of the first three tiles, q and the per-query values (one
   // round trip), then the rows of the first two tiles
-  if (wave == 4) {
+  if (wave == 0) {
     for (int u = 0; u < 3; ++u)
       if (c.tb + u < c.te && c.tb + u < c.ng) load_pos(c.tb + u, u);
   }
@@ -586,10 +586,13 @@ __global__ __launch_bounds__(kThreads) void attend_kernel(AttendArgs a, int S, i
     const int n = i - tb;
     const bool more = i + 2 < te;
     const bool more_g = i + 2 < c.ng;
-    if (wave == 4 && i + 3 < te && i + 3 < c.ng) load_pos(i + 3, (n + 3) & 3);
-    if (more) issue(i + 2, (n + 2) & 3, (n + 2) & 3);
+    if (wave == 0 && i + 3 < te && i + 3 < c.ng) load_pos(i + 3, (n + 3) & 3);
+    // waves 0..3 issue the loads of tile i+2 before their products, waves 4..7 after them,
+    // so half the waves queue for the vector-memory path while the other half run MFMAs
+    if (more && wave < 4) issue(i + 2, (n + 2) & 3, (n + 2) & 3);
     if constexpr (pvk != 0) pv(std::integral_constant<bool, pvk == 1>{}, (n - 1) & 3, (n - 1) & 1);
     if constexpr (qkk != 0) qk(std::integral_constant<bool, qkk == 1>{}, n & 3);
+    if (more && wave >= 4) issue(i + 2, (n + 2) & 3, (n + 2) & 3);
     // waves 0..3 build the row data of tile i after their products, in time they would
     // otherwise spend waiting at the barrier for waves 4..7 (per-phase cycle counters)
     if constexpr (qkk != 0) {
