@@ -47,9 +47,10 @@ struct RawKeys {
 };
 
 template <int MT, int TPW, int DI, bool CAND>
-__global__ __launch_bounds__(kScoreThreads) void score_kernel(ScoreArgs a) {
-  __shared__ __align__(16) uint8_t q_lds[16 * MT * kQRow];
-  __shared__ float w_lds[16 * MT];
+__global__ __launch_bounds__(kScoreThreads, 2) void score_kernel(ScoreArgs a) {
+  // two q buffers: query t is scored from one while query t+1 is written to the other
+  __shared__ __align__(16) uint8_t q_lds[2][16 * MT * kQRow];
+  __shared__ float w_lds[2][16 * MT];
   __shared__ int s_pmax;
 
   const int tid = threadIdx.x;
@@ -120,26 +121,49 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel(ScoreArgs a) {
     nblk = min(nblk, pmax / kPosPerWG + 1);
   }
 
-  // q of query t staged in LDS as bf16 (E4M3 -> bf16 exact), converted once per query
-  auto stage_q = [&](int t) {
-    const int pieces_per_row = DI / 16;
-    const int total = 16 * MT * pieces_per_row;
-    for (int pc = tid; pc < total; pc += kScoreThreads) {
-      const int h = pc / pieces_per_row, c = pc % pieces_per_row;
-      v4u v = {0u, 0u, 0u, 0u};
-      if (h < Hi) v = *(const v4u*)(a.q_fp8 + ((int64_t)t * Hi + h) * DI + 16 * c);
-      uint8_t* dst = q_lds + h * kQRow + 32 * c;
-      *(v8bf*)dst = fp8x8_to_bf16(v.x, v.y);
-      *(v8bf*)(dst + 16) = fp8x8_to_bf16(v.z, v.w);
+  // q of query t staged in LDS as bf16 (E4M3 -> bf16 exact), converted once per query:
+  // fetch_q reads it into registers (16 bytes of E4M3 per piece), put_q converts and
+  // stores it into one of the two buffers
+  constexpr int kQPieces = 16 * MT * (DI / 16);
+  constexpr int kQPer = (kQPieces + kScoreThreads - 1) / kScoreThreads;
+  struct QRegs {
+    v4u v[kQPer];
+    float w;
+  };
+  auto fetch_q = [&](int t, QRegs& r) {
+#pragma unroll
+    for (int u = 0; u < kQPer; ++u) {
+      const int pc = tid + kScoreThreads * u;
+      const int h = pc / (DI / 16), c = pc % (DI / 16);
+      r.v[u] = v4u{0u, 0u, 0u, 0u};
+      if (pc < kQPieces && h < Hi) r.v[u] = *(const v4u*)(a.q_fp8 + ((int64_t)t * Hi + h) * DI + 16 * c);
     }
-    if (tid < 16 * MT) w_lds[tid] = tid < Hi ? a.w[(int64_t)t * Hi + tid] : 0.0f;
+    r.w = tid < 16 * MT && tid < Hi ? a.w[(int64_t)t * Hi + tid] : 0.0f;
+  };
+  auto put_q = [&](int buf, const QRegs& r) {
+#pragma unroll
+    for (int u = 0; u < kQPer; ++u) {
+      const int pc = tid + kScoreThreads * u;
+      const int h = pc / (DI / 16), c = pc % (DI / 16);
+      if (pc < kQPieces) {
+        uint8_t* dst = q_lds[buf] + h * kQRow + 32 * c;
+        *(v8bf*)dst = fp8x8_to_bf16(r.v[u].x, r.v[u].y);
+        *(v8bf*)(dst + 16) = fp8x8_to_bf16(r.v[u].z, r.v[u].w);
+      }
+    }
+    if (tid < 16 * MT) w_lds[buf][tid] = r.w;
+  };
+  auto stage_q = [&](int t, int buf) {
+    QRegs r;
+    fetch_q(t, r);
+    put_q(buf, r);
   };
   // One query per sequence (decode): q, w and the position are loaded once, so the block
   // loop issues no load besides the key prefetch and never waits for it early.
   const bool single = t1 - t0 == 1;
   const int p0 = __builtin_amdgcn_readfirstlane(a.q_pos[t0]);
   if (single) {
-    stage_q(t0);
+    stage_q(t0, 0);
     __syncthreads();
   }
 
@@ -161,14 +185,19 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel(ScoreArgs a) {
     const int col0 = blk * kPosPerWG;
     if (blk + (int)gridDim.x < nblk) load_keys(blk + gridDim.x, rk);
 
+      // several queries: q of query t+1 is read while query t is scored and written to the
+      // other buffer after it, one barrier per query
+      if (!single) {
+        __syncthreads();                       // the previous block's last q is no longer read
+        stage_q(t0, 0);
+        __syncthreads();
+      }
       for (int t = t0; t < t1; ++t) {
+        const int buf = single ? 0 : (t - t0) & 1;
+        QRegs nq;
+        if (!single && t + 1 < t1) fetch_q(t + 1, nq);
         const int p = single ? p0 : __builtin_amdgcn_readfirstlane(a.q_pos[t]);
-        if (!CAND && p < col0) continue;
-        if (!single) {
-          __syncthreads();
-          stage_q(t);
-          __syncthreads();
-        }
+        if (CAND || p >= col0) {
         // heads outer, positions inner: one 16-head slice of q is live at a time; the TPW
         // accumulator chains are interleaved so consecutive MFMAs are independent.  kappa > 0
         // commutes with the ReLU, so it scales the head sum instead of every term.
@@ -180,11 +209,11 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel(ScoreArgs a) {
           v8bf qa[NKS];
           float wr[4];
           {
-            const uint8_t* src = q_lds + (16 * mt + n) * kQRow + 2 * g * (DI / 4);
+            const uint8_t* src = q_lds[buf] + (16 * mt + n) * kQRow + 2 * g * (DI / 4);
 #pragma unroll
             for (int s2 = 0; s2 < NKS; ++s2) qa[s2] = *(const v8bf*)(src + 16 * s2);
 #pragma unroll
-            for (int r = 0; r < 4; ++r) wr[r] = w_lds[16 * mt + 4 * g + r];
+            for (int r = 0; r < 4; ++r) wr[r] = w_lds[buf][16 * mt + 4 * g + r];
           }
           v4f acc[TPW];
 #pragma unroll
@@ -217,6 +246,11 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel(ScoreArgs a) {
               a.scores[(int64_t)t * a.ld + col] = sm;
             }
           }
+        }
+        }
+        if (!single && t + 1 < t1) {
+          put_q(buf ^ 1, nq);
+          __syncthreads();
         }
       }
   };
