@@ -1158,15 +1158,8 @@ hipError_t launch_attend(const AttendArgs& a, hipStream_t s) {
     return launch_lat<1, 2>(a, p, s);
   }
   if (a.D <= 1664) return launch_attend_sd(a, p.S, s);
-  switch (a.D) {
-#define SMQA_ATTEND_D(d) case d: return launch_thr<d>(a, p, s);
-    SMQA_ATTEND_D(128) SMQA_ATTEND_D(256) SMQA_ATTEND_D(384) SMQA_ATTEND_D(512)
-    SMQA_ATTEND_D(640) SMQA_ATTEND_D(768) SMQA_ATTEND_D(896) SMQA_ATTEND_D(1024)
-    SMQA_ATTEND_D(1152) SMQA_ATTEND_D(1280) SMQA_ATTEND_D(1408) SMQA_ATTEND_D(1536)
-    SMQA_ATTEND_D(1664) SMQA_ATTEND_D(1792)
-#undef SMQA_ATTEND_D
-    default: return hipErrorInvalidValue;
-  }
+  if (a.D == 1792) return launch_thr<1792>(a, p, s);   // the plan takes no other width here
+  return hipErrorInvalidValue;
 }
 
 }  // namespace smqa

@@ -225,6 +225,24 @@ def test_attend(lib, name, kw):
     _attend_check(lib, gen(name, **kw))
 
 
+# Every attention kernel and latent width class: the dimension-split kernel with one block per
+# wave pair (D = 128: waves 4..7 own no block), an even split (D = 512) and an uneven one
+# (D = 640); the 16-head kernel for few queries at D = 1792 and for head counts that are not
+# a multiple of 32; the 32-head tile kernel at D = 1792 with 64 (query, head group) pairs;
+# and the widest latent the boundary accepts (D = 2048).
+@pytest.mark.parametrize("name,kw", [
+    ("decode_8k", dict(B=2, lengths=1500, Hq=32, D=128, k=256)),
+    ("decode_8k", dict(B=2, lengths=1500, Hq=64, D=512, k=256)),
+    ("decode_8k", dict(B=2, lengths=(700, 1500), Hq=32, D=640, k=300)),
+    ("decode_8k", dict(B=1, lengths=1500, Hq=64, D=1792, k=256)),
+    ("decode_8k", dict(B=2, lengths=1500, Hq=48, D=768, k=256)),
+    ("decode_8k", dict(B=2, lengths=1500, Hq=32, D=2048, k=256)),
+    ("replay_h100k", dict(B=1, lengths=2000, replay=(2000, 32), Hq=64, D=1792, k=256)),
+])
+def test_attend_widths_and_head_counts(lib, name, kw):
+    _attend_check(lib, gen(name, **kw))
+
+
 def test_attend_with_scales_and_padding(lib):
     wl = synth.with_scales(gen("decode_8k", B=2, lengths=(1500, 2500), k=2048))
     a = np_inputs(wl)
