@@ -478,12 +478,16 @@ __global__ __launch_bounds__(kThreads) void attend_kernel(AttendArgs a, int S, i
     const float2 lsr = *(const float2*)(rl + srow);
     const float2 psr = *(const float2*)(rp + srow);
     const float mo = mref[sh];
+    // the 8 waves' partial logits, read before any is added (one LDS round trip)
+    float2 v[8];
+#pragma unroll
+    for (int w8 = 0; w8 < 8; ++w8) v[w8] = *(const float2*)(red + w8 * 32 * kRows);
+    __builtin_amdgcn_sched_barrier(0);
     float s0 = 0.0f, s1 = 0.0f;
 #pragma unroll
     for (int w8 = 0; w8 < 8; ++w8) {
-      const float2 v = *(const float2*)(red + w8 * 32 * kRows);
-      s0 += v.x;
-      s1 += v.y;
+      s0 += v[w8].x;
+      s1 += v[w8].y;
     }
     const bool ok0 = lsr.x != 0.0f, ok1 = lsr.y != 0.0f;
     s0 = ok0 ? s0 * lsr.x : -__builtin_inff();
