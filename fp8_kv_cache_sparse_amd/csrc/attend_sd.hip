@@ -518,9 +518,13 @@ __global__ __launch_bounds__(kThreads) void attend_kernel(AttendArgs a, int S, i
     const unsigned* sch = (const unsigned*)(smem + G::SCH) + sslot * G::NB * 16;
     // rescale when the running max of a group of 8 heads (4 per k-half) moved: one
     // uniform branch per group, so only groups whose max moved pay for the multiplies
+    v4f alq[4];
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4) alq[q4] = *(const v4f*)(malpha + 8 * q4 + 4 * kh);
+    __builtin_amdgcn_sched_barrier(0);             // the four reads in one LDS round trip
 #pragma unroll
     for (int q4 = 0; q4 < 4; ++q4) {
-      const v4f al = *(const v4f*)(malpha + 8 * q4 + 4 * kh);
+      const v4f al = alq[q4];
       const bool moved = al.x != 1.0f || al.y != 1.0f || al.z != 1.0f || al.w != 1.0f;
       if (__builtin_amdgcn_ballot_w64(moved)) {
 #pragma unroll
