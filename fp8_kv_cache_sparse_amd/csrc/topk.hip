@@ -553,6 +553,11 @@ __device__ Threshold find_threshold(const unsigned* hist, int nvalid, int k, int
   return Threshold{sh[0], sh[1], (int)hist[sh[0]]};
 }
 
+// A workgroup counts HC consecutive chunks of a row into one LDS histogram before adding its
+// nonzero bins to the query's global one: on long rows the global atomics, not the row
+// reads, bound this kernel (HC = 4 from 20 chunks per row on; shorter rows keep one chunk
+// per workgroup for parallelism).
+template <int HC>
 __global__ __launch_bounds__(kLongThreads) void topk_hist_kernel(TopkArgs a, TopkWs w) {
   constexpr int NT = kLongThreads;
   __shared__ unsigned hist[kHistBins];
@@ -561,22 +566,23 @@ __global__ __launch_bounds__(kLongThreads) void topk_hist_kernel(TopkArgs a, Top
   const int t = blockIdx.y;
   const int ncols = ncols_of(a, t);
   if (blockIdx.x == 0 && threadIdx.x == 0) w.st[t].ncols = ncols;
-  const int nch = (ncols + kChunk - 1) / kChunk;
+  const int nch = (ncols + HC * kChunk - 1) / (HC * kChunk);
   if ((int)blockIdx.x >= nch) return;
-  const int c0 = blockIdx.x * kChunk;
+  const int c0 = blockIdx.x * HC * kChunk;
   const float* row = a.scores + (int64_t)t * a.ld;
-  float v[kPerThread];
-#pragma unroll
-  for (int u = 0; u < kPerThread; ++u) {
-    const int i = c0 + threadIdx.x + NT * u;
-    v[u] = i < ncols ? row[i] : -__builtin_inff();
-  }
   for (int i = threadIdx.x; i < kHistBins; i += NT) hist[i] = 0;
   if (threadIdx.x == 0) sh[2] = 0;
   __syncthreads();
+  // every load of the workgroup's columns goes out before the first is counted
+  float v[HC * kPerThread];
+#pragma unroll
+  for (int u = 0; u < HC * kPerThread; ++u) {
+    const int i = c0 + threadIdx.x + NT * u;
+    v[u] = i < ncols ? row[i] : -__builtin_inff();
+  }
   int cnt = 0;
 #pragma unroll
-  for (int u = 0; u < kPerThread; ++u) {
+  for (int u = 0; u < HC * kPerThread; ++u) {
     const unsigned key = score_key(v[u]);
     if (key) {
       atomicAdd(&hist[key >> 20], 1u);
@@ -837,7 +843,11 @@ hipError_t launch_topk(const TopkArgs& a, hipStream_t s) {
   if (e != hipSuccess) return e;
   TopkWs w = carve(a.ws, a.T, a.max_ctx);
   const int nch = (a.max_ctx + kChunk - 1) / kChunk;
-  hipLaunchKernelGGL(topk_hist_kernel, dim3(nch, a.T), dim3(kLongThreads), 0, s, a, w);
+  if (nch >= 20) {
+    hipLaunchKernelGGL(topk_hist_kernel<4>, dim3((nch + 3) / 4, a.T), dim3(kLongThreads), 0, s, a, w);
+  } else {
+    hipLaunchKernelGGL(topk_hist_kernel<1>, dim3(nch, a.T), dim3(kLongThreads), 0, s, a, w);
+  }
   hipLaunchKernelGGL(topk_collect_kernel<false>, dim3(nch, a.T), dim3(kLongThreads), 0, s, a, w);
   hipLaunchKernelGGL(topk_finish_kernel, dim3(a.T), dim3(1024), 0, s, a, w);
   return hipGetLastError();
