@@ -12,8 +12,9 @@
 //
 //   gather   global_load_lds_dwordx4 straight into one of four LDS tile buffers (rows
 //            padded so both read patterns below are bank-conflict free), issued by all 8
-//            waves; the raw E8M0 bytes and the row scales land beside them.  Tile i+2 is
-//            in flight while tile i is scored and tile i-1 is accumulated.
+//            waves (waves 0-3 before their products, waves 4-7 after them); the raw E8M0
+//            bytes and the row scales land beside them.  Tile i+2 is in flight while tile
+//            i is scored and tile i-1 is accumulated.
 //   Q.K^T    v_mfma_f32_32x32x16_bf16, heads x rows: each lane reads 8 dims of one row
 //            (ds_read_b32 for E2M1, ds_read_b64 for E4M3) and converts them exactly to
 //            bf16 with the block's E8M0 scale (v_cvt_scalef32_pk_bf16_*); q stays in
@@ -27,8 +28,7 @@
 //            ds_read_b64_tr_b4 (E2M1: 16 rows of one dim per lane) and ds_read_b64_tr_b8
 //            (E4M3), is converted to fp16 with scale 1 and multiplied by the rows' block
 //            scales (v_pk_mul_f16: the scale is exact in fp16 for -24 <= e - 127 <= 15, the
-//            product for -23 <= e - 127 <= 13); P carries the row
-//            scale rho (or sigma).
+//            product for -23 <= e - 127 <= 13); P carries the row scale rho (or sigma).
 //
 // Several tile ranges of one (query, head group) leave unnormalised partials that
 // attend_merge_kernel combines by log-sum-exp.
@@ -581,9 +581,9 @@ __global__ __launch_bounds__(kThreads) void attend_kernel(AttendArgs a, int S, i
     }
   };
 
-  // ---- pipeline.  Iteration i: gather tile i+2 (and the positions of tile i+3), build the
-  // row data of tile i, P.V of tile i-1, Q.K^T of tile i; barrier; softmax of tile i and
-  // wait for tile i+1; barrier.  Tiles are global (E2M1) rows first, then window (E4M3)
+  // ---- pipeline.  Iteration i: gather tile i+2 (and the positions of tile i+3), P.V of
+  // tile i-1, Q.K^T of tile i, build the row data of tile i; barrier; softmax of tile i
+  // and wait for tile i+1; barrier.  Tiles are global (E2M1) rows first, then window (E4M3)
   // rows, so the iterations run as separate loops per pair of kinds and no inner loop
   // branches on the kind.
   using KN = std::integral_constant<int, 0>;      // no tile
