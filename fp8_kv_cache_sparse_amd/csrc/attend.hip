@@ -996,65 +996,13 @@ __global__ __launch_bounds__(kAttThreads) void attend_kernel(AttendArgs a, int S
 }  // namespace thr
 
 // ================================================================ merge and dispatch
-// out[t,h,d] = sum_s 2^(m_s - M) O_s[d] / sum_s 2^(m_s - M) l_s ; one thread per output dim.
-// Every thread issues its S partial loads before the weights are known, so the whole merge
-// costs one round trip to memory (SMAX >= S partials per output, at most 64).
+// out[t,h,d] = sum_s 2^(m_s - M) O_s[d] / sum_s 2^(m_s - M) l_s ; four consecutive output
+// dims per thread with 16-byte loads and stores (the boundary requires a 256-byte aligned
+// workspace and a 16-byte aligned output; D is a multiple of 128).  Every thread issues its
+// S partial loads before the weights are known, so the merge costs one round trip to
+// memory (SMAX >= S partials per output, at most 64).
 template <int SMAX>
-__global__ __launch_bounds__(256) void attend_merge_kernel(AttendArgs a, int S) {
-  __shared__ float wts[64];
-  __shared__ float sL, sM;
-  const int th = blockIdx.y;
-  const int t = th / a.Hq, h = th % a.Hq;
-  const int D = a.D;
-  const float* opart = (const float*)a.ws;
-  const float* ml = opart + (size_t)S * a.T * a.Hq * D;
-  const size_t sstride = (size_t)a.T * a.Hq * D;
-  const int d = blockIdx.x * 256 + threadIdx.x;
-  float v[SMAX];
-  {
-    const float* src = opart + ((int64_t)t * a.Hq + h) * D + (d < D ? d : 0);
-#pragma unroll
-    for (int s = 0; s < SMAX; ++s) v[s] = s < S ? src[s * sstride] : 0.0f;
-  }
-  if (threadIdx.x < 64) {
-    const int s = threadIdx.x;
-    float ms = -__builtin_inff(), ls = 0.0f;
-    if (s < S) {
-      const int64_t i = ((int64_t)s * a.T + t) * a.Hq + h;
-      ms = ml[2 * i];
-      ls = ml[2 * i + 1];
-    }
-    float M = ms;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) M = fmaxf(M, __shfl_xor(M, o));
-    const float wv = (M == -__builtin_inff() || ls == 0.0f) ? 0.0f : exp2f(ms - M);
-    float L = wv * ls;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) L += __shfl_xor(L, o);
-    wts[s] = wv;
-    if (s == 0) {
-      sL = L;
-      sM = M;
-    }
-  }
-  __syncthreads();
-  const float L = sL;
-  const float inv = L > 0.0f ? 1.0f / L : 0.0f;
-  if (d < D) {
-    float acc = 0.0f;
-#pragma unroll
-    for (int s = 0; s < SMAX; ++s)
-      if (s < S) acc += wts[s] * v[s];
-    a.out[((int64_t)t * a.Hq + h) * D + d] = acc * inv;
-  }
-  if (blockIdx.x == 0 && threadIdx.x == 0 && a.lse)
-    a.lse[(int64_t)t * a.Hq + h] = L > 0.0f ? (sM + log2f(L)) * kLn2 : -__builtin_inff();
-}
-
-// The same merge with four consecutive dims per thread (16-byte loads and stores), for
-// 16-byte aligned workspace and output: a quarter of the load instructions.
-template <int SMAX>
-__global__ __launch_bounds__(128) void attend_merge4_kernel(AttendArgs a, int S) {
+__global__ __launch_bounds__(128) void attend_merge_kernel(AttendArgs a, int S) {
   __shared__ float wts[64];
   __shared__ float sL, sM;
   const int th = blockIdx.y;
@@ -1149,17 +1097,10 @@ size_t attend_workspace_bytes(int32_t T, int32_t k, int32_t W, int32_t Hq, int32
 
 hipError_t launch_attend_merge(const AttendArgs& a, int S, hipStream_t s) {
   if (S == 1) return hipSuccess;
-  if ((((uintptr_t)a.ws | (uintptr_t)a.out) & 15) == 0) {
-    const dim3 grid4((a.D / 4 + 127) / 128, a.T * a.Hq);
-    if (S <= 16) hipLaunchKernelGGL(attend_merge4_kernel<16>, grid4, dim3(128), 0, s, a, S);
-    else if (S <= 32) hipLaunchKernelGGL(attend_merge4_kernel<32>, grid4, dim3(128), 0, s, a, S);
-    else hipLaunchKernelGGL(attend_merge4_kernel<64>, grid4, dim3(128), 0, s, a, S);
-    return hipGetLastError();
-  }
-  const dim3 grid((a.D + 255) / 256, a.T * a.Hq);
-  if (S <= 16) hipLaunchKernelGGL(attend_merge_kernel<16>, grid, dim3(256), 0, s, a, S);
-  else if (S <= 32) hipLaunchKernelGGL(attend_merge_kernel<32>, grid, dim3(256), 0, s, a, S);
-  else hipLaunchKernelGGL(attend_merge_kernel<64>, grid, dim3(256), 0, s, a, S);
+  const dim3 grid((a.D / 4 + 127) / 128, a.T * a.Hq);
+  if (S <= 16) hipLaunchKernelGGL(attend_merge_kernel<16>, grid, dim3(128), 0, s, a, S);
+  else if (S <= 32) hipLaunchKernelGGL(attend_merge_kernel<32>, grid, dim3(128), 0, s, a, S);
+  else hipLaunchKernelGGL(attend_merge_kernel<64>, grid, dim3(128), 0, s, a, S);
   return hipGetLastError();
 }
 
