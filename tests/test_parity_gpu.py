@@ -243,6 +243,21 @@ def test_attend_widths_and_head_counts(lib, name, kw):
     _attend_check(lib, gen(name, **kw))
 
 
+def test_attend_empty_and_window_only_rows(lib):
+    """No selected global rows at all (every index -1): query 0 also sees no window row (its
+    clip lies past its position), so its output is 0 and its LSE -inf; the others attend to
+    their window rows only."""
+    wl = gen("replay_h100k", B=1, lengths=2000, replay=(2000, 4))
+    clip = wl.swa_clip.clone()
+    clip[0] = wl.q_pos[0] + 1
+    import dataclasses
+    wl = dataclasses.replace(wl, swa_clip=clip)
+    idx = np.full((wl.T, wl.k), -1, dtype=np.int32)
+    out, lse = _attend_check(lib, wl, idx)
+    assert torch.all(out[0] == 0) and torch.all(torch.isneginf(lse[0]))
+    assert torch.all(torch.isfinite(lse[1:]))
+
+
 def test_attend_with_scales_and_padding(lib):
     wl = synth.with_scales(gen("decode_8k", B=2, lengths=(1500, 2500), k=2048))
     a = np_inputs(wl)
