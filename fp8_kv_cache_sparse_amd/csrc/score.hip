@@ -228,22 +228,43 @@ __global__ __launch_bounds__(kScoreThreads, 2) void score_kernel(ScoreArgs a) {
 #pragma unroll
             for (int r = 0; r < 4; ++r) sum[i] += wr[r] * relu(acc[i][r]);
         }
+        if constexpr (TPW == 4) {
+          // reduce-scatter over the lane groups g (two permlane32 swaps, one permlane16
+          // swap): lane (g, n) ends with the head sum of tile g, position n, so the wave's
+          // 64 scores go out in one coalesced store
+          const auto x02 = __builtin_amdgcn_permlane32_swap(__float_as_uint(sum[0]), __float_as_uint(sum[2]), false, false);
+          const auto x13 = __builtin_amdgcn_permlane32_swap(__float_as_uint(sum[1]), __float_as_uint(sum[3]), false, false);
+          const float u = __uint_as_float(x02[0]) + __uint_as_float(x02[1]);
+          const float v = __uint_as_float(x13[0]) + __uint_as_float(x13[1]);
+          const auto y = __builtin_amdgcn_permlane16_swap(__float_as_uint(u), __float_as_uint(v), false, false);
+          const float tot = __uint_as_float(y[0]) + __uint_as_float(y[1]);
+          const float kg = g == 0 ? kap[0] : g == 1 ? kap[1] : g == 2 ? kap[2] : kap[3];
+          const float sm = tot * kg;
+          const int col = col0 + wave * kPosPerWave + lane;
+          if (CAND) {
+            const int kp = g == 0 ? kpos[0] : g == 1 ? kpos[1] : g == 2 ? kpos[2] : kpos[3];
+            if (col < a.n_cand) a.scores[(int64_t)t * a.ld + col] = kp >= 0 && kp <= p ? sm : -__builtin_inff();
+          } else if (col <= p && col < len) {
+            a.scores[(int64_t)t * a.ld + col] = sm;
+          }
+        } else {
 #pragma unroll
-        for (int i = 0; i < TPW; ++i) {
-          const int colbase = col0 + wave * kPosPerWave + 16 * i;
-          float sm = sum[i];
-          sm += __shfl_xor(sm, 16);
-          sm += __shfl_xor(sm, 32);
-          sm *= kap[i];
-          if (g == 0) {
-            const int col = colbase + n;
-            if (CAND) {
-              if (col < a.n_cand) {
-                const bool valid = kpos[i] >= 0 && kpos[i] <= p;
-                a.scores[(int64_t)t * a.ld + col] = valid ? sm : -__builtin_inff();
+          for (int i = 0; i < TPW; ++i) {
+            const int colbase = col0 + wave * kPosPerWave + 16 * i;
+            float sm = sum[i];
+            sm += __shfl_xor(sm, 16);
+            sm += __shfl_xor(sm, 32);
+            sm *= kap[i];
+            if (g == 0) {
+              const int col = colbase + n;
+              if (CAND) {
+                if (col < a.n_cand) {
+                  const bool valid = kpos[i] >= 0 && kpos[i] <= p;
+                  a.scores[(int64_t)t * a.ld + col] = valid ? sm : -__builtin_inff();
+                }
+              } else if (col <= p && col < len) {
+                a.scores[(int64_t)t * a.ld + col] = sm;
               }
-            } else if (col <= p && col < len) {
-              a.scores[(int64_t)t * a.ld + col] = sm;
             }
           }
         }
