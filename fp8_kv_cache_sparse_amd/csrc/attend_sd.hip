@@ -279,7 +279,7 @@ __global__ __launch_bounds__(kThreads) void attend_kernel(AttendArgs a, int S, i
       const int* pos = (const int*)(smem + G::RING) + rslot * kRows;
       const int xt = tile * kRows;
       // every position this wave needs, read before one wait: all 32 (for the code rows),
-      // the rows of its two E8M0 loads, the rows of its rho lanes
+      // the rows of its E8M0 load, the rows of its rho lanes
       const int pall = pos[ln & 31];
       const int re = 4 * wave + ln / per_row;
       const int pe = pos[re & 31];
