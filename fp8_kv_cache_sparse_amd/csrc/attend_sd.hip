@@ -262,6 +262,10 @@ __global__ __launch_bounds__(kThreads) void attend_kernel(AttendArgs a, int S, i
 
   // wave w's blocks [b0, b0 + BPW + (w < EXTRA))
   const int b0 = wave * G::BPW + min(wave, G::EXTRA);
+  // the query's sequence in the latent cache (set by the prologue)
+  const uint8_t* codes_base = nullptr;
+  const uint8_t* e8_base = nullptr;
+  const float* rho_base = nullptr;
 
   // ---- loads of one tile: positions (into the ring) and rows (into a buffer).  Every wave
   // loads rows 8u + wave of the tile, so the loads of a tile are spread over all 8 waves.
@@ -290,20 +294,21 @@ __global__ __launch_bounds__(kThreads) void attend_kernel(AttendArgs a, int S, i
       for (int u = 0; u < kRows / 8; ++u) {
         const int r = 8 * u + wave;
         const int j = __builtin_amdgcn_readlane(pall, r);
-        const bool ok = xt + r < c.gx1 && j >= 0;
-        const uint8_t* src = ok ? a.kv_codes + (c.base + j) * (D / 2) : dummy;
+        const bool ok = (xt + r < c.gx1) & (j >= 0);
+        const uint8_t* row = codes_base + (int64_t)j * (D / 2);   // formed for every j, used when ok
+        const uint8_t* src = ok ? row : dummy;
         if (ln < D / 32) gload16(src + 16 * ln, lds_addr(B + r * G::RS4));
       }
       // raw E8M0: rows 4 wave .. +4, contiguous
       {
         const int dd = ln % per_row;
         const bool ok = xt + re < c.gx1 && pe >= 0;
-        const uint8_t* s0 = ok ? a.kv_e8m0 + (c.base + pe) * (D / 32) : dummy;
+        const uint8_t* s0 = ok ? e8_base + (int64_t)pe * (D / 32) : dummy;
         if (ln < 4 * per_row) gload4(s0 + 4 * dd, lds_addr(B + G::E8 + 4 * wave * G::E8S));
       }
       {  // rho of rows 8u + wave, u = lane < 4 -> RHO[wave][u]
         const bool ok = a.kv_rowscale && xt + rr < c.gx1 && pr >= 0;
-        const void* src = ok ? (const void*)(a.kv_rowscale + c.base + pr) : (const void*)dummy;
+        const void* src = ok ? (const void*)(rho_base + pr) : (const void*)dummy;
         if (ln < 4) gload4(src, lds_addr(B + G::RHO + 16 * wave));
       }
     } else {
@@ -353,6 +358,9 @@ __global__ __launch_bounds__(kThreads) void attend_kernel(AttendArgs a, int S, i
     const SeqInfo si = locate_seq(a, t, lane);
     c.b = si.b;
     c.base = si.base;
+    codes_base = a.kv_codes + si.base * (D / 2);
+    e8_base = a.kv_e8m0 + si.base * (D / 32);
+    rho_base = a.kv_rowscale ? a.kv_rowscale + si.base : nullptr;
     c.pos0 = si.pos0;
     c.p = si.p;
     c.lo_win = max(max(c.p - c.W + 1, 0), si.clip);
