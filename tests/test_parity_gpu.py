@@ -367,3 +367,49 @@ def test_decode_step_deterministic(lib):
     o2, l2, i2 = gpu_decode(lib, wl)
     sync()
     assert torch.equal(i1, i2) and torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+# decode_step inside a captured HIP graph (no allocation, memset or host synchronisation in
+# the call): every replay, with unrelated eager work between replays, must reproduce the
+# eager call bit for bit.
+@pytest.mark.parametrize("name,kw", [
+    ("decode_8k", {}),                                        # short rows, split attention
+    ("decode_512k", dict(B=2, lengths=70000)),                # long rows: zeroing, histogram
+    ("replay_h100k", dict(B=1, lengths=5000, replay=(5000, 64))),
+])
+def test_decode_step_graph_replay(lib, name, kw):
+    wl = gen(name, **kw)
+    announce(f"decode_step graph replay {name}")
+    L = lib.Batch(wl.seq_start, wl.q_start, wl.q_pos, wl.max_ctx)
+    n_cand = 0 if wl.cand is None else wl.cand.shape[1]
+    out = torch.empty((wl.T, wl.Hq, wl.D), dtype=torch.float32, device=DEV)
+    lse = torch.empty((wl.T, wl.Hq), dtype=torch.float32, device=DEV)
+    idx = torch.empty((wl.T, wl.k), dtype=torch.int32, device=DEV)
+    ws = torch.empty(lib.decode_step_workspace_size(L, wl.k, n_cand, wl.W, wl.Hq, wl.D) + 256,
+                     dtype=torch.uint8, device=DEV)
+    args = (L, wl.qI, wl.w, wl.kI, wl.kscale, wl.cand, wl.q, wl.kv_codes, wl.kv_e8m0, wl.kv_rowscale,
+            wl.swa, wl.swa_scale, wl.swa_pos0, wl.swa_clip, wl.k, wl.sm_scale)
+    step = lambda: lib.decode_step(*args, out=out, lse=lse, idx=idx, workspace=ws)
+    step()
+    sync()
+    ref_out, ref_lse, ref_idx = out.clone(), lse.clone(), idx.clone()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        step()
+    torch.cuda.current_stream().wait_stream(s)
+    sync()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    sync()
+    noise = torch.randn(1 << 20, device=DEV)
+    for r in range(3):
+        out.zero_(); lse.zero_(); idx.zero_(); ws.zero_()
+        noise.mul_(1.0001)                                   # eager work between replays
+        sync()
+        g.replay()
+        sync()
+        assert torch.equal(idx, ref_idx), f"replay {r}: idx"
+        assert torch.equal(out, ref_out), f"replay {r}: out"
+        assert torch.equal(lse, ref_lse), f"replay {r}: lse"
