@@ -23,6 +23,8 @@ Readings where the pages are silent (each restated where it is used):
   R5  the window of query t is positions [max(p_t - W + 1, s_t, 0), p_t]
       that exist in the buffer; rows before the clip s_t are excluded
   R6  an empty row set gives O = 0 and LSE = -inf
+  R7  the FP8 global cache (the baseline format) is E4M3 rows with one fp32
+      scale per row
 """
 from __future__ import annotations
 
@@ -116,6 +118,36 @@ def window_positions(t, b, q_pos, swa_pos0, swa_clip, W):
     return u, pos[u]
 
 
+def _attend_union(q, global_of, idx, swa, swa_scale, swa_pos0, swa_clip, seq_start, q_start,
+                  q_pos, W, sm_scale):
+    """One softmax per (query, head) over the selected global rows plus the visible window
+    rows; global_of(cache_rows) decodes the selected rows of the global cache."""
+    qv = codecs.bf16(q)
+    T, Hq, D = qv.shape
+    seq_start = np.asarray(seq_start, dtype=np.int64)
+    qs = _q_seq(q_start)
+    idx = np.asarray(idx, dtype=np.int64)
+    O = np.zeros((T, Hq, D), dtype=np.float64)
+    LSE = np.full((T, Hq), -np.inf, dtype=np.float64)
+    for t in range(T):
+        b = qs[t]
+        sel = idx[t][idx[t] >= 0]
+        Vg = global_of(seq_start[b] + sel)
+        u, _ = window_positions(t, b, q_pos, swa_pos0, swa_clip, W)
+        Xw = codecs.window_rows(np.asarray(swa)[b][u],
+                                None if swa_scale is None else np.asarray(swa_scale)[b][u])
+        R = np.concatenate([Vg.reshape(-1, D), Xw.reshape(-1, D)], axis=0)
+        if R.shape[0] == 0:
+            continue
+        L = sm_scale * (qv[t] @ R.T)                 # [Hq, nrows]
+        m = L.max(axis=1, keepdims=True)
+        e = np.exp(L - m)
+        Z = e.sum(axis=1, keepdims=True)
+        O[t] = (e @ R) / Z
+        LSE[t] = (m + np.log(Z))[:, 0]
+    return O, LSE
+
+
 def attend(q, kv_codes, kv_e8m0, kv_rowscale, idx, swa, swa_scale, swa_pos0, swa_clip,
            seq_start, q_start, q_pos, W, sm_scale):
     """Sparse MQA attention over selected global rows plus the visible window rows.
@@ -131,32 +163,33 @@ def attend(q, kv_codes, kv_e8m0, kv_rowscale, idx, swa, swa_scale, swa_pos0, swa
         LSE   = m + ln(sum_x exp(l_x - m))
     q is bf16 bits (uint16 [T, Hq, D]); returns float64 O [T, Hq, D], LSE [T, Hq].
     """
-    qv = codecs.bf16(q)
-    T, Hq, D = qv.shape
-    seq_start = np.asarray(seq_start, dtype=np.int64)
-    qs = _q_seq(q_start)
-    idx = np.asarray(idx, dtype=np.int64)
-    O = np.zeros((T, Hq, D), dtype=np.float64)
-    LSE = np.full((T, Hq), -np.inf, dtype=np.float64)
-    for t in range(T):
-        b = qs[t]
-        sel = idx[t][idx[t] >= 0]
-        rows = seq_start[b] + sel
-        Vg = codecs.global_rows(np.asarray(kv_codes)[rows], np.asarray(kv_e8m0)[rows],
-                                None if kv_rowscale is None else np.asarray(kv_rowscale)[rows])
-        u, _ = window_positions(t, b, q_pos, swa_pos0, swa_clip, W)
-        Xw = codecs.window_rows(np.asarray(swa)[b][u],
-                                None if swa_scale is None else np.asarray(swa_scale)[b][u])
-        R = np.concatenate([Vg.reshape(-1, D), Xw.reshape(-1, D)], axis=0)
-        if R.shape[0] == 0:
-            continue
-        L = sm_scale * (qv[t] @ R.T)                 # [Hq, nrows]
-        m = L.max(axis=1, keepdims=True)
-        e = np.exp(L - m)
-        Z = e.sum(axis=1, keepdims=True)
-        O[t] = (e @ R) / Z
-        LSE[t] = (m + np.log(Z))[:, 0]
-    return O, LSE
+    codes, e8 = np.asarray(kv_codes), np.asarray(kv_e8m0)
+    rs = None if kv_rowscale is None else np.asarray(kv_rowscale)
+
+    def global_of(rows):
+        return codecs.global_rows(codes[rows], e8[rows], None if rs is None else rs[rows])
+    return _attend_union(q, global_of, idx, swa, swa_scale, swa_pos0, swa_clip, seq_start,
+                         q_start, q_pos, W, sm_scale)
+
+
+def attend_fp8kv(q, kv_fp8, kv_rowscale, idx, swa, swa_scale, swa_pos0, swa_clip,
+                 seq_start, q_start, q_pos, W, sm_scale):
+    """The same attention over an FP8 global cache (the format the FP4 cache replaces).
+
+    CocoLoop digest §"Les particularités du modèle lui-même" and blog §Kernels:
+    the NVFP4 global KV is about 45% smaller than the FP8 cache used before it.
+    Reading R7: that FP8 cache holds each latent row as D E4M3 bytes times one
+    fp32 row scale rho_j (the window's format), V[j, d] = e4m3(byte) * rho_j;
+    everything else is `attend`.  kv_fp8 uint8 [N, D], kv_rowscale float32 [N]
+    or None (rho = 1).
+    """
+    codes = np.asarray(kv_fp8)
+    rs = None if kv_rowscale is None else np.asarray(kv_rowscale)
+
+    def global_of(rows):
+        return codecs.window_rows(codes[rows], None if rs is None else rs[rows])
+    return _attend_union(q, global_of, idx, swa, swa_scale, swa_pos0, swa_clip, seq_start,
+                         q_start, q_pos, W, sm_scale)
 
 
 def decode_step(wl_np: dict, k=None, cand=None):

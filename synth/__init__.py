@@ -85,6 +85,8 @@ class Workload:
     swa_pos0: torch.Tensor           # int32 [B]           position of window row 0
     swa_clip: Optional[torch.Tensor]     # int32 [T] or None   clip start s_t
     cand: Optional[torch.Tensor] = None  # int32 [T, n_cand]   ascending candidate positions
+    kv_fp8: Optional[torch.Tensor] = None        # uint8 [N, D]  E4M3 global latent (FP8 cache)
+    kv_fp8_scale: Optional[torch.Tensor] = None  # float32 [N]   its row scales
     meta: dict = field(default_factory=dict)
 
     @property
@@ -303,6 +305,31 @@ def generate(name: str, seed: int = 0, device="cpu", n_cand: Optional[int] = Non
         cand=None if cand is None else t(cand, torch.int32),
         meta=dict(seed=seed, lengths=lengths.tolist(), q_seq=q_seq.tolist(), params=p),
     )
+
+
+def encode_fp8_rows(x: torch.Tensor):
+    """float32 rows [R, D] -> (E4M3 bytes [R, D], fp32 row scale [R]): each row is divided
+    by rho = amax|row| / 448 (1 for a zero row) and rounded to E4M3."""
+    amax = x.abs().amax(dim=1)
+    rho = torch.where(amax > 0, amax / 448.0, torch.ones_like(amax))
+    return encode_e4m3(x / rho[:, None]), rho
+
+
+def with_fp8_kv(wl: Workload, seed: int = 2) -> Workload:
+    """Attach an FP8 global latent cache of the same shape (fresh N(0,1) rows, E4M3 with a
+    row scale): the input of the FP8-KV baseline attention."""
+    dev = wl.kI.device
+    g = torch.Generator(device=dev)
+    g.manual_seed(seed)
+    kv = torch.empty((wl.N, wl.D), dtype=torch.uint8, device=dev)
+    rho = torch.empty((wl.N,), dtype=torch.float32, device=dev)
+
+    def put(r0, x):
+        c, r = encode_fp8_rows(x)
+        kv[r0:r0 + x.shape[0]] = c
+        rho[r0:r0 + x.shape[0]] = r
+    _randn_rows(g, wl.N, wl.D, dev, put)
+    return dataclasses.replace(wl, kv_fp8=kv, kv_fp8_scale=rho)
 
 
 def with_scales(wl: Workload, seed: int = 1) -> Workload:

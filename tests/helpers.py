@@ -14,7 +14,8 @@ def np_inputs(wl) -> dict:
     w = wl.cpu()
     a = {}
     for name in ("seq_start", "q_start", "q_pos", "qI", "w", "kI", "kscale", "kv_codes",
-                 "kv_e8m0", "kv_rowscale", "swa", "swa_scale", "swa_pos0", "swa_clip", "cand"):
+                 "kv_e8m0", "kv_rowscale", "swa", "swa_scale", "swa_pos0", "swa_clip", "cand",
+                 "kv_fp8", "kv_fp8_scale"):
         v = getattr(w, name)
         a[name] = None if v is None else v.numpy()
     a["q"] = w.q.view(torch.int16).numpy().view(np.uint16)
@@ -51,7 +52,8 @@ def brute_scores(a, cand=None) -> list:
     return out
 
 
-def brute_attend(a, idx) -> tuple:
+def brute_attend(a, idx, fp8kv=False) -> tuple:
+    """Scalar-loop attention; fp8kv takes the global rows from kv_fp8 / kv_fp8_scale."""
     qs = q_seq_of(a)
     T, Hq, D = a["q"].shape
     O = np.zeros((T, Hq, D))
@@ -65,6 +67,10 @@ def brute_attend(a, idx) -> tuple:
             if j < 0:
                 continue
             r = base + int(j)
+            if fp8kv:
+                rho = None if a["kv_fp8_scale"] is None else a["kv_fp8_scale"][r]
+                rows.append(brute.window_row(a["kv_fp8"][r], rho))
+                continue
             rho = None if a["kv_rowscale"] is None else a["kv_rowscale"][r]
             rows.append(brute.global_row(a["kv_codes"][r], a["kv_e8m0"][r], rho))
         p = int(a["q_pos"][t])

@@ -270,6 +270,53 @@ def test_attend_empty_set():
     assert np.all(O == 0) and np.all(L == -np.inf)
 
 
+# ----------------------------------------------------------------- attend over an FP8 cache
+
+def _attend8(a, idx, **over):
+    b = dict(a)
+    b.update(over)
+    return ref.attend_fp8kv(b["q"], b["kv_fp8"], b["kv_fp8_scale"], idx, b["swa"], b["swa_scale"],
+                            b["swa_pos0"], b["swa_clip"], b["seq_start"], b["q_start"], b["q_pos"],
+                            b["W"], b["sm_scale"])
+
+
+@pytest.mark.parametrize("seed,clip", [(0, False), (1, True)])
+def test_attend_fp8kv_matches_brute(seed, clip):
+    wl = synth.with_fp8_kv(synth.with_scales(tiny(seed, B=2, lengths=(20, 37)), seed=seed), seed=seed)
+    a = np_inputs(wl)
+    if clip:
+        a["swa_clip"] = (a["q_pos"] - 3).astype(np.int32)
+    rng = np.random.default_rng(seed)
+    idx = np.full((a["T"], a["k"]), -1, dtype=np.int64)
+    for t, b in enumerate([0, 1]):
+        n = int(a["seq_start"][b + 1] - a["seq_start"][b])
+        m = min(a["k"] - 1, n)
+        idx[t, :m] = np.sort(rng.choice(min(n, int(a["q_pos"][t]) + 1), size=m, replace=False))
+    O, L = _attend8(a, idx)
+    Ob, Lb = brute_attend(a, idx, fp8kv=True)
+    assert np.allclose(O, Ob, rtol=1e-12, atol=1e-14)
+    assert np.allclose(L, Lb, rtol=1e-12, atol=1e-14)
+    a["kv_fp8_scale"] = None                         # rho = 1
+    O, L = _attend8(a, idx)
+    Ob, Lb = brute_attend(a, idx, fp8kv=True)
+    assert np.allclose(O, Ob, rtol=1e-12, atol=1e-14)
+
+
+def test_attend_fp8kv_of_an_exact_reencoding_equals_fp4():
+    """Every FP4 row value e2m1 * 2^(E-127) here is an E4M3 value: the FP8 cache holding the
+    same values (row scale rho unchanged) must give the FP4 cache's attention exactly."""
+    wl = synth.with_scales(tiny(3, B=2, lengths=(30, 45)), seed=3)
+    a = np_inputs(wl)
+    vals = codecs.global_rows(a["kv_codes"], a["kv_e8m0"], None)
+    e4 = synth.encode_e4m3(torch.tensor(vals, dtype=torch.float32)).numpy()
+    assert np.array_equal(codecs.e4m3(e4), vals)     # the re-encoding is exact
+    S = ref.score(a["qI"], a["w"], a["kI"], a["kscale"], a["seq_start"], a["q_start"], a["q_pos"])
+    idx = ref.topk(S, a["k"])
+    O4, L4 = _attend(a, idx)
+    O8, L8 = _attend8(a, idx, kv_fp8=e4, kv_fp8_scale=a["kv_rowscale"])
+    assert np.array_equal(O4, O8) and np.array_equal(L4, L8)
+
+
 # ----------------------------------------------------------------- window clipping
 
 def _replay(H=50, nq=6, W=8, seed=13):
