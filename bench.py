@@ -135,7 +135,7 @@ def roofline(stage, w, seconds, workload=None):
 
 # ---------------------------------------------------------------- GPU measurement
 
-def measure(name, steps, warmup, use_graph, stage_only=""):
+def measure(name, steps, warmup, use_graph, stage_only="", fp8_baseline=True):
     import torch
     import synth
     import fp8_kv_cache_sparse_amd as smqa
@@ -181,6 +181,11 @@ def measure(name, steps, warmup, use_graph, stage_only=""):
     stages = {"score": st_score, "topk": st_topk, "attend": st_attend}
     if stage_only == "copy":
         stages["copy"] = st_copy
+    if stage_only == "attend_fp8kv":
+        wl8s = synth.with_fp8_kv(wl)
+        stages["attend_fp8kv"] = lambda: smqa.sparse_mqa_attend_fp8kv(
+            L, wl.q, wl8s.kv_fp8, wl8s.kv_fp8_scale, idx2, wl.swa, wl.swa_scale, wl.swa_pos0,
+            wl.swa_clip, wl.sm_scale, out=out2, lse=lse2, workspace=ws)
     if stage_only:
         fn = stages[stage_only]
         st_score()
@@ -270,8 +275,8 @@ def measure(name, steps, warmup, use_graph, stage_only=""):
     st_score()
     st_topk()
     torch.cuda.synchronize()
-    for nm, fn in stages.items():
-        print(f"[bench] {name}: stage {nm} x{steps}", file=sys.stderr, flush=True)
+
+    def timed_us(fn):
         for _ in range(2):
             fn()
         torch.cuda.synchronize()
@@ -299,7 +304,31 @@ def measure(name, steps, warmup, use_graph, stage_only=""):
             e1.record()
             torch.cuda.synchronize()
             best = e0.elapsed_time(e1)
-        st_us[nm] = best * 1e3 / steps
+        return best * 1e3 / steps
+
+    for nm, fn in stages.items():
+        print(f"[bench] {name}: stage {nm} x{steps}", file=sys.stderr, flush=True)
+        st_us[nm] = timed_us(fn)
+
+    # the same attention over an FP8 global cache (E4M3 rows + row scale, the format the FP4
+    # cache replaces) on the same selection: what the FP4 format saves
+    fp8kv = None
+    if fp8_baseline and wl.Hq % 32 == 0 and wl.D <= 1664:
+        print(f"[bench] {name}: FP8-cache attention x{steps}", file=sys.stderr, flush=True)
+        wl8 = synth.with_fp8_kv(wl)
+        torch.cuda.synchronize()
+
+        def st_attend8():
+            smqa.sparse_mqa_attend_fp8kv(L, wl.q, wl8.kv_fp8, wl8.kv_fp8_scale, idx2, wl.swa,
+                                         wl.swa_scale, wl.swa_pos0, wl.swa_clip, wl.sm_scale,
+                                         out=out2, lse=lse2, workspace=ws)
+        us8 = timed_us(st_attend8)
+        row4 = wl.D // 2 + wl.D // 32 + (4 if wl.kv_rowscale is not None else 0)
+        fp8kv = {"attend_us_fp8_cache": round(us8, 2), "attend_us_fp4_cache": round(st_us["attend"], 2),
+                 "fp8_over_fp4_time": round(us8 / st_us["attend"], 3),
+                 "global_row_bytes": {"fp4": row4, "fp8": wl.D + 4},
+                 "kernel": "attend: sd::attend_kernel<D, G8=true> (16-row E4M3 global tiles) + attend_merge_kernel"}
+        del wl8
     dom = max(st_us, key=st_us.get)
     best_s = min(x for x in (eager_s, graph_s, chain_s) if x)
     res = {
@@ -312,6 +341,7 @@ def measure(name, steps, warmup, use_graph, stage_only=""):
         "tokens_scored_per_s": J / best_s,
         "stage_us": {k: round(v, 2) for k, v in st_us.items()},
         "stage_roofline": {k: roofline(k, w[k], st_us[k] * 1e-6, name) for k in st_us},
+        "fp8_cache_baseline": fp8kv,
         "roofline": roofline(dom, w[dom], st_us[dom] * 1e-6, name),
         "config": dict(wl.meta["params"], lengths=(wl.meta["lengths"] if wl.B <= 8 else
                                                   [min(wl.meta["lengths"]), max(wl.meta["lengths"])])),

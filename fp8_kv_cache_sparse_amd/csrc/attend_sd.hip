@@ -207,9 +207,13 @@ __device__ __forceinline__ SeqInfo locate_seq(const AttendArgs& a, int t, int la
   }
 }
 
-template <int D>
+// G8: the global cache holds E4M3 rows with a row scale (the FP8 cache the FP4 format
+// replaced) instead of E2M1 + E8M0; its tiles are then 16 gathered rows that take the
+// window tiles' products.
+template <int D, bool G8>
 __global__ __launch_bounds__(kThreads) void attend_kernel(AttendArgs a, int S, int ngroups, int total) {
   using G = Geo<D>;
+  constexpr int GR = G8 ? kWRows : kRows;         // global rows per tile
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
 
   const int tid = threadIdx.x;
@@ -242,11 +246,11 @@ __global__ __launch_bounds__(kThreads) void attend_kernel(AttendArgs a, int S, i
   c.k = a.k;
   c.W = a.W;
   c.lscale = a.sm_scale * kLog2e;
-  c.ng = (c.k + kRows - 1) / kRows;
+  c.ng = (c.k + GR - 1) / GR;
   const int nominal = c.ng + (c.W + kWRows - 1) / kWRows;
   c.tb = (int)((int64_t)split * nominal / S);
   c.te = (int)((int64_t)(split + 1) * nominal / S);
-  c.gx1 = min(min(c.te, c.ng) * kRows, c.k);       // global rows of this split end here
+  c.gx1 = min(min(c.te, c.ng) * GR, c.k);          // global rows of this split end here
 
   float* mref = (float*)(smem + G::MR);
   float* malpha = mref + 32;
@@ -269,47 +273,71 @@ __global__ __launch_bounds__(kThreads) void attend_kernel(AttendArgs a, int S, i
 
   // ---- loads of one tile: positions (into the ring) and rows (into a buffer).  Every wave
   // loads rows 8u + wave of the tile, so the loads of a tile are spread over all 8 waves.
-  auto load_pos = [&](int tile, int rslot) __attribute__((always_inline)) {       // wave 0, lanes 0..31
+  auto load_pos = [&](int tile, int rslot) __attribute__((always_inline)) {       // wave 0, lanes 0..GR-1
     const int ln = opq(lane);
-    const int x = tile * kRows + (ln & 31);
+    const int x = tile * GR + (ln & 31);
     const void* src = x < c.gx1 ? (const void*)(a.idx + (int64_t)t * c.k + x) : (const void*)dummy;
-    if (ln < kRows) gload4(src, lds_addr(smem + G::RING + rslot * kRows * 4));
+    if (ln < GR) gload4(src, lds_addr(smem + G::RING + rslot * kRows * 4));
   };
   auto issue = [&](int tile, int slot, int rslot) __attribute__((always_inline)) {
     const int ln = opq(lane);
     uint8_t* B = smem + slot * G::BUF;
     if (tile < c.ng) {
-      constexpr int per_row = D / 128;              // E8M0 dwords per row
-      const int* pos = (const int*)(smem + G::RING) + rslot * kRows;
-      const int xt = tile * kRows;
-      // every position this wave needs, read before one wait: all 32 (for the code rows),
-      // the rows of its E8M0 load, the rows of its rho lanes
-      const int pall = pos[ln & 31];
-      const int re = 4 * wave + ln / per_row;
-      const int pe = pos[re & 31];
-      const int rr = 8 * (ln & 3) + wave;
-      const int pr = pos[rr];
-      // code rows 8u + wave, u = 0..3
+      if constexpr (G8) {
+        // FP8 global tile: rows 8u + wave, u = 0..1, gathered by position; the row scales
+        // of rows 8u + wave, u = lane < 2 -> RHO[wave][u]
+        const int* pos = (const int*)(smem + G::RING) + rslot * kRows;
+        const int xt = tile * kWRows;
+        const int pall = pos[ln & 15];
+        const int rr = 8 * (ln & 1) + wave;
+        const int pr = pos[rr];
 #pragma unroll
-      for (int u = 0; u < kRows / 8; ++u) {
-        const int r = 8 * u + wave;
-        const int j = __builtin_amdgcn_readlane(pall, r);
-        const bool ok = (xt + r < c.gx1) & (j >= 0);
-        const uint8_t* row = codes_base + (int64_t)j * (D / 2);   // formed for every j, used when ok
-        const uint8_t* src = ok ? row : dummy;
-        if (ln < D / 32) gload16(src + 16 * ln, lds_addr(B + r * G::RS4));
-      }
-      // raw E8M0: rows 4 wave .. +4, contiguous
-      {
-        const int dd = ln % per_row;
-        const bool ok = xt + re < c.gx1 && pe >= 0;
-        const uint8_t* s0 = ok ? e8_base + (int64_t)pe * (D / 32) : dummy;
-        if (ln < 4 * per_row) gload4(s0 + 4 * dd, lds_addr(B + G::E8 + 4 * wave * G::E8S));
-      }
-      {  // rho of rows 8u + wave, u = lane < 4 -> RHO[wave][u]
+        for (int u = 0; u < kWRows / 8; ++u) {
+          const int r = 8 * u + wave;
+          const int j = __builtin_amdgcn_readlane(pall, r);
+          const bool ok = (xt + r < c.gx1) & (j >= 0);
+          const uint8_t* src = ok ? codes_base + (int64_t)j * D : dummy;
+          if (ln < (G::PIECES8 < 64 ? G::PIECES8 : 64)) gload16(src + 16 * ln, lds_addr(B + r * G::RS8));
+          if constexpr (G::PIECES8 > 64) {
+            if (ln < G::PIECES8 - 64) gload16(src + 1024 + 16 * ln, lds_addr(B + r * G::RS8 + 1024));
+          }
+        }
         const bool ok = a.kv_rowscale && xt + rr < c.gx1 && pr >= 0;
         const void* src = ok ? (const void*)(rho_base + pr) : (const void*)dummy;
-        if (ln < 4) gload4(src, lds_addr(B + G::RHO + 16 * wave));
+        if (ln < 2) gload4(src, lds_addr(B + G::RHO + 16 * wave));
+      } else {
+        constexpr int per_row = D / 128;              // E8M0 dwords per row
+        const int* pos = (const int*)(smem + G::RING) + rslot * kRows;
+        const int xt = tile * kRows;
+        // every position this wave needs, read before one wait: all 32 (for the code rows),
+        // the rows of its E8M0 load, the rows of its rho lanes
+        const int pall = pos[ln & 31];
+        const int re = 4 * wave + ln / per_row;
+        const int pe = pos[re & 31];
+        const int rr = 8 * (ln & 3) + wave;
+        const int pr = pos[rr];
+        // code rows 8u + wave, u = 0..3
+#pragma unroll
+        for (int u = 0; u < kRows / 8; ++u) {
+          const int r = 8 * u + wave;
+          const int j = __builtin_amdgcn_readlane(pall, r);
+          const bool ok = (xt + r < c.gx1) & (j >= 0);
+          const uint8_t* row = codes_base + (int64_t)j * (D / 2);   // formed for every j, used when ok
+          const uint8_t* src = ok ? row : dummy;
+          if (ln < D / 32) gload16(src + 16 * ln, lds_addr(B + r * G::RS4));
+        }
+        // raw E8M0: rows 4 wave .. +4, contiguous
+        {
+          const int dd = ln % per_row;
+          const bool ok = xt + re < c.gx1 && pe >= 0;
+          const uint8_t* s0 = ok ? e8_base + (int64_t)pe * (D / 32) : dummy;
+          if (ln < 4 * per_row) gload4(s0 + 4 * dd, lds_addr(B + G::E8 + 4 * wave * G::E8S));
+        }
+        {  // rho of rows 8u + wave, u = lane < 4 -> RHO[wave][u]
+          const bool ok = a.kv_rowscale && xt + rr < c.gx1 && pr >= 0;
+          const void* src = ok ? (const void*)(rho_base + pr) : (const void*)dummy;
+          if (ln < 4) gload4(src, lds_addr(B + G::RHO + 16 * wave));
+        }
       }
     } else {
       // window tile: rows 8u + wave, u = 0..1; D/16 pieces of 16 bytes per row (two loads
@@ -358,8 +386,8 @@ __global__ __launch_bounds__(kThreads) void attend_kernel(AttendArgs a, int S, i
     const SeqInfo si = locate_seq(a, t, lane);
     c.b = si.b;
     c.base = si.base;
-    codes_base = a.kv_codes + si.base * (D / 2);
-    e8_base = a.kv_e8m0 + si.base * (D / 32);
+    codes_base = a.kv_codes + si.base * (G8 ? D : D / 2);
+    e8_base = G8 ? nullptr : a.kv_e8m0 + si.base * (D / 32);
     rho_base = a.kv_rowscale ? a.kv_rowscale + si.base : nullptr;
     c.pos0 = si.pos0;
     c.p = si.p;
@@ -430,12 +458,13 @@ __global__ __launch_bounds__(kThreads) void attend_kernel(AttendArgs a, int S, i
   // tau * log2(e) * (rho or sigma), 0 for rows that take no part, the P multiplier (rho
   // or sigma), and the V-operand block scales as fp16 pairs (rows 2pp, 2pp+1; zero for
   // rows that take no part) or, for a window tile, 16-bit row masks in pairs.
-  auto convert = [&](auto FP4, int tile, int slot, int rslot, int sslot) __attribute__((always_inline)) {
+  auto convert = [&](auto KIND, int tile, int slot, int rslot, int sslot) __attribute__((always_inline)) {
+    constexpr int kind = decltype(KIND)::value;    // 1 E2M1 global, 2 window, 3 E4M3 global
     const int ct = opq(tid);                       // waves 0..3: 0..255
     const int ln = ct & 63;
     const uint8_t* B = smem + slot * G::BUF;
     unsigned* sch = (unsigned*)(smem + G::SCH) + sslot * G::NB * 16;
-    if constexpr (decltype(FP4)::value) {
+    if constexpr (kind == 1) {
       const int* pos = (const int*)(smem + G::RING) + rslot * kRows;
       // rows that take part, as a bit mask (every loader wave computes it)
       const int pl = pos[ln & 31];
@@ -462,11 +491,18 @@ __global__ __launch_bounds__(kThreads) void attend_kernel(AttendArgs a, int S, i
         rp[ct] = v ? m : 0.0f;
       }
     } else if (ct < kRows) {
-      const int uu = kWRows * (c.wt0 + tile - c.ng) + ct;
-      const int pos = c.pos0 + uu;
-      const bool v = ct < kWRows && uu < c.W && pos >= c.lo_win && pos <= c.p;
+      bool v;
+      if constexpr (kind == 3) {
+        const int pl = ((const int*)(smem + G::RING) + rslot * kRows)[ct & 15];
+        v = ct < kWRows && tile * kWRows + ct < c.gx1 && pl >= 0;
+      } else {
+        const int uu = kWRows * (c.wt0 + tile - c.ng) + ct;
+        const int pos = c.pos0 + uu;
+        v = ct < kWRows && uu < c.W && pos >= c.lo_win && pos <= c.p;
+      }
       const unsigned vb = (unsigned)__builtin_amdgcn_ballot_w64(v);   // rows 0..15 of wave 0
-      const float m = a.swa_scale ? ((const float*)(B + G::RHO))[4 * (ct & 7) + ((ct & 15) >> 3)] : 1.0f;
+      const bool scaled = kind == 3 ? a.kv_rowscale != nullptr : a.swa_scale != nullptr;
+      const float m = scaled ? ((const float*)(B + G::RHO))[4 * (ct & 7) + ((ct & 15) >> 3)] : 1.0f;
       rl[ct] = v ? c.lscale * m : 0.0f;
       rp[ct] = v ? m : 0.0f;
       if (ct < kWRows / 2) {
@@ -595,7 +631,7 @@ __global__ __launch_bounds__(kThreads) void attend_kernel(AttendArgs a, int S, i
   // rows, so the iterations run as separate loops per pair of kinds and no inner loop
   // branches on the kind.
   using KN = std::integral_constant<int, 0>;      // no tile
-  using KG = std::integral_constant<int, 1>;      // global E2M1 tile
+  using KG = std::integral_constant<int, G8 ? 3 : 1>;   // global tile (E2M1, or E4M3 when G8)
   using KW = std::integral_constant<int, 2>;      // window E4M3 tile
   auto body = [&](auto PVK, auto QKK, int i) __attribute__((always_inline)) {
     constexpr int pvk = decltype(PVK)::value, qkk = decltype(QKK)::value;
@@ -612,13 +648,13 @@ __global__ __launch_bounds__(kThreads) void attend_kernel(AttendArgs a, int S, i
     // waves 0..3 build the row data of tile i after their products, in time they would
     // otherwise spend waiting at the barrier for waves 4..7 (per-phase cycle counters)
     if constexpr (qkk != 0) {
-      if (wave < 4) convert(std::integral_constant<bool, qkk == 1>{}, i, n & 3, n & 3, n & 1);
+      if (wave < 4) convert(QKK, i, n & 3, n & 3, n & 1);
     }
     __syncthreads();                               // partial logits and row data of tile i
     if constexpr (qkk != 0) softmax();
     // tile i+1 (and the positions of tile i+3) landed; tile i+2 may still be in flight
     if (!more) __builtin_amdgcn_s_waitcnt(0);
-    else if (more_g) wait_vmcnt<G::NLOAD4>();
+    else if (!G8 && more_g) wait_vmcnt<G::NLOAD4>();
     else wait_vmcnt<G::NLOAD8>();
     __syncthreads();                               // P(i), tile i+1 published
   };
@@ -678,7 +714,7 @@ __global__ __launch_bounds__(kThreads) void attend_kernel(AttendArgs a, int S, i
   }
 }
 
-template <int D>
+template <int D, bool G8>
 hipError_t launch(const AttendArgs& a, int S, hipStream_t s) {
   using G = Geo<D>;
   const int ngroups = a.Hq / 32;
@@ -686,12 +722,12 @@ hipError_t launch(const AttendArgs& a, int S, hipStream_t s) {
   const int nb = (total + 7) / 8 * 8;
   static bool attr = false;
   if (!attr) {
-    hipError_t e = hipFuncSetAttribute((const void*)attend_kernel<D>,
+    hipError_t e = hipFuncSetAttribute((const void*)attend_kernel<D, G8>,
                                        hipFuncAttributeMaxDynamicSharedMemorySize, G::LDS);
     if (e != hipSuccess) return e;
     attr = true;
   }
-  hipLaunchKernelGGL(attend_kernel<D>, dim3(nb), dim3(kThreads), G::LDS, s, a, S, ngroups, total);
+  hipLaunchKernelGGL((attend_kernel<D, G8>), dim3(nb), dim3(kThreads), G::LDS, s, a, S, ngroups, total);
   hipError_t e = hipGetLastError();
   return e != hipSuccess ? e : launch_attend_merge(a, S, s);
 }
@@ -699,11 +735,12 @@ hipError_t launch(const AttendArgs& a, int S, hipStream_t s) {
 }  // namespace sd
 
 // Dimension-split attention for Hq % 32 == 0 and D <= 1664 (the register budget of 8
-// waves holding 32 heads of outputs and q, and four tile buffers in LDS); returns
-// hipErrorInvalidValue otherwise.
+// waves holding 32 heads of outputs and q, and four tile buffers in LDS), over the FP4
+// global cache or, with a.kv_fp8, the FP8 one; returns hipErrorInvalidValue otherwise.
 hipError_t launch_attend_sd(const AttendArgs& a, int S, hipStream_t s) {
   switch (a.D) {
-#define SMQA_SD_D(d) case d: return sd::launch<d>(a, S, s);
+#define SMQA_SD_D(d) \
+  case d: return a.kv_fp8 ? sd::launch<d, true>(a, S, s) : sd::launch<d, false>(a, S, s);
     SMQA_SD_D(128) SMQA_SD_D(256) SMQA_SD_D(384) SMQA_SD_D(512)
     SMQA_SD_D(640) SMQA_SD_D(768) SMQA_SD_D(896) SMQA_SD_D(1024)
     SMQA_SD_D(1152) SMQA_SD_D(1280) SMQA_SD_D(1408) SMQA_SD_D(1536)

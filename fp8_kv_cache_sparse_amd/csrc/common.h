@@ -121,10 +121,12 @@ struct AttendArgs {
   float* out;
   float* lse;
   void* ws;
+  int32_t kv_fp8;             // 1: kv_codes holds E4M3 rows [N][D] (kv_e8m0 unused)
 };
 int attend_splits(int32_t T, int32_t k, int32_t W, int32_t Hq, int32_t D);
 size_t attend_workspace_bytes(int32_t T, int32_t k, int32_t W, int32_t Hq, int32_t D);
 hipError_t launch_attend(const AttendArgs& a, hipStream_t s);
+hipError_t launch_attend_fp8kv(const AttendArgs& a, hipStream_t s);
 
 inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 

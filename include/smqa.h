@@ -190,6 +190,31 @@ int sparse_mqa_attend(const smqa_layout* L,
                       void* stream);
 
 /*
+ * sparse_mqa_attend_fp8kv — sparse_mqa_attend over an FP8 global cache, the
+ * format the FP4 cache replaced (CocoLoop digest, section "Les
+ * particularités du modèle lui-même": the NVFP4 global KV is about 45%
+ * smaller than the FP8 one; blog §Kernels).  A baseline for measuring what
+ * the FP4 format saves; the selected global rows are
+ *   V[j] = e4m3 * rho_j,  j in idx[t] (j >= 0)
+ * and everything else (window, clip, softmax, outputs, workspace size from
+ * smqa_attend_workspace_size, errors) is as in sparse_mqa_attend.
+ * kv_fp8      uint8  [N][D]         E4M3 latent rows, 16-byte aligned
+ * kv_rowscale float  [N] or NULL    rho (> 0; NULL = 1)
+ * Limits: those of sparse_mqa_attend plus Hq % 32 == 0 and D <= 1664.
+ * Arithmetic as in sparse_mqa_attend (E4M3 values are exact in bf16 and fp16).
+ */
+int sparse_mqa_attend_fp8kv(const smqa_layout* L,
+                            const uint16_t* q_bf16,
+                            const uint8_t* kv_fp8, const float* kv_rowscale,
+                            const int32_t* idx, int32_t k,
+                            const uint8_t* swa_fp8, const float* swa_scale,
+                            const int32_t* swa_pos0, const int32_t* swa_clip,
+                            int32_t W, int32_t Hq, int32_t D, float sm_scale,
+                            float* out, float* lse,
+                            void* workspace, size_t workspace_bytes,
+                            void* stream);
+
+/*
  * decode_step — sparse_mqa_score -> topk_select -> sparse_mqa_attend in one
  * call on one stream, with the scores and the selection kept in the
  * workspace (blog §Kernels: fusing the steps removes memory round trips and

@@ -315,9 +315,10 @@ def encode_fp8_rows(x: torch.Tensor):
     return encode_e4m3(x / rho[:, None]), rho
 
 
-def with_fp8_kv(wl: Workload, seed: int = 2) -> Workload:
+def with_fp8_kv(wl: Workload, seed: int = 2, rowscale: bool = True) -> Workload:
     """Attach an FP8 global latent cache of the same shape (fresh N(0,1) rows, E4M3 with a
-    row scale): the input of the FP8-KV baseline attention."""
+    row scale, or without one the N(0,1) values rounded to E4M3 as they are): the input of
+    the FP8-KV baseline attention."""
     dev = wl.kI.device
     g = torch.Generator(device=dev)
     g.manual_seed(seed)
@@ -325,11 +326,12 @@ def with_fp8_kv(wl: Workload, seed: int = 2) -> Workload:
     rho = torch.empty((wl.N,), dtype=torch.float32, device=dev)
 
     def put(r0, x):
-        c, r = encode_fp8_rows(x)
+        c, r = encode_fp8_rows(x) if rowscale else (encode_e4m3(x), None)
         kv[r0:r0 + x.shape[0]] = c
-        rho[r0:r0 + x.shape[0]] = r
+        if rowscale:
+            rho[r0:r0 + x.shape[0]] = r
     _randn_rows(g, wl.N, wl.D, dev, put)
-    return dataclasses.replace(wl, kv_fp8=kv, kv_fp8_scale=rho)
+    return dataclasses.replace(wl, kv_fp8=kv, kv_fp8_scale=rho if rowscale else None)
 
 
 def with_scales(wl: Workload, seed: int = 1) -> Workload:

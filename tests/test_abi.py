@@ -27,7 +27,8 @@ def declared_functions():
 
 def test_header_declares_the_boundary():
     names = declared_functions()
-    for n in ("sparse_mqa_score", "topk_select", "sparse_mqa_attend", "decode_step",
+    for n in ("sparse_mqa_score", "topk_select", "sparse_mqa_attend", "sparse_mqa_attend_fp8kv",
+              "decode_step",
               "smqa_topk_workspace_size", "smqa_attend_workspace_size",
               "smqa_decode_step_workspace_size", "smqa_last_error", "smqa_version"):
         assert n in names
@@ -124,6 +125,26 @@ def test_attend_validation():
     assert need > 0
     assert attend(L) == -5
     assert attend(layout(T=0)) == 0
+
+
+def attend8(L, **kw):
+    a = dict(q=A16, c=A16, rs=None, idx=A4, k=2048, swa=A16, ss=None, p0=A4, clip=None, W=128,
+             Hq=64, D=1664, sc=0.0245, out=A16, lse=None, ws=None, nb=0)
+    a.update(kw)
+    return lib().sparse_mqa_attend_fp8kv(ctypes.byref(L), a["q"], a["c"], a["rs"], a["idx"], a["k"],
+                                         a["swa"], a["ss"], a["p0"], a["clip"], a["W"], a["Hq"],
+                                         a["D"], a["sc"], a["out"], a["lse"], a["ws"], a["nb"], None)
+
+
+def test_attend_fp8kv_validation():
+    L = layout()
+    assert attend8(L, Hq=48) == -4 and "Hq" in err()        # only 32-head groups
+    assert attend8(L, D=1792) == -4 and attend8(L, D=1600) == -4
+    assert attend8(L, c=None) == -1 and attend8(L, idx=None) == -1
+    assert attend8(L, c=A16 + 4) == -3
+    assert attend8(L, k=5000) == -4 and attend8(L, W=0) == -4
+    assert attend8(L) == -5                                  # split partials need the workspace
+    assert attend8(layout(T=0)) == 0
 
 
 def test_decode_step_workspace_covers_parts():

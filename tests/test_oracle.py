@@ -296,7 +296,10 @@ def test_attend_fp8kv_matches_brute(seed, clip):
     Ob, Lb = brute_attend(a, idx, fp8kv=True)
     assert np.allclose(O, Ob, rtol=1e-12, atol=1e-14)
     assert np.allclose(L, Lb, rtol=1e-12, atol=1e-14)
-    a["kv_fp8_scale"] = None                         # rho = 1
+    a = np_inputs(synth.with_fp8_kv(wl, seed=seed, rowscale=False))     # rho = 1
+    if clip:
+        a["swa_clip"] = (a["q_pos"] - 3).astype(np.int32)
+    assert a["kv_fp8_scale"] is None
     O, L = _attend8(a, idx)
     Ob, Lb = brute_attend(a, idx, fp8kv=True)
     assert np.allclose(O, Ob, rtol=1e-12, atol=1e-14)

@@ -13,7 +13,8 @@ import torch
 
 import synth
 from oracle import ref
-from helpers import (announce, close_attention, close_scores, gpu_attend, gpu_decode, gpu_score,
+from helpers import (announce, close_attention, close_scores, gpu_attend, gpu_attend_fp8kv,
+                     gpu_decode, gpu_score,
                      gpu_topk, np_inputs, oracle_attend_for, oracle_scores_for, q_seq_of, topk_set_ok)
 
 pytestmark = pytest.mark.gpu
@@ -286,6 +287,60 @@ def test_attend_peaked_rows_respect_the_clip(lib):
     row_incl = wl.swa[0, u_incl].view(torch.float8_e4m3fn).float()
     # head 0 of query 0 is dominated by the included row
     assert torch.allclose(out[0, 0], row_incl, rtol=1e-2, atol=1e-2)
+
+
+# ------------------------------------------------------------------ attend over an FP8 cache
+
+def _attend8_check(lib, wl, idx_np=None):
+    a = np_inputs(wl)
+    if idx_np is None:
+        S = ref.score(a["qI"], a["w"], a["kI"], a["kscale"], a["seq_start"], a["q_start"], a["q_pos"])
+        idx_np = ref.topk(S, wl.k)
+    idx = torch.tensor(idx_np, dtype=torch.int32, device=DEV)
+    announce(f"attend_fp8kv {wl.name} T={wl.T} Hq={wl.Hq} D={wl.D} k={wl.k}")
+    out, lse = gpu_attend_fp8kv(lib, wl, idx)
+    sync()
+    O, L = ref.attend_fp8kv(a["q"], a["kv_fp8"], a["kv_fp8_scale"], idx_np, a["swa"],
+                            a["swa_scale"], a["swa_pos0"], a["swa_clip"], a["seq_start"],
+                            a["q_start"], a["q_pos"], a["W"], a["sm_scale"])
+    ok, msg = close_attention(out.cpu().numpy(), O, lse.cpu().numpy(), L)
+    assert ok, msg
+    return out, lse
+
+
+# 16-row global tiles: k = 2048 (whole tiles), k = 1000 and 300 (a partial last tile), the
+# dimension-split widths of one, an even and an uneven block share per wave, the clipped
+# replay window, row scales on both caches and none.
+@pytest.mark.parametrize("name,kw,scales", [
+    ("decode_8k", dict(lengths=6000), True),
+    ("decode_8k", dict(B=3, lengths=(300, 2000), k=1000, W=100), False),
+    ("decode_8k", dict(B=2, lengths=1500, Hq=32, D=128, k=256), True),
+    ("decode_8k", dict(B=2, lengths=1500, Hq=64, D=512, k=256), False),
+    ("decode_8k", dict(B=2, lengths=(700, 1500), Hq=32, D=640, k=300), True),
+    ("replay_h100k", dict(B=2, lengths=4000, replay=(4000, 128)), True),
+])
+def test_attend_fp8kv(lib, name, kw, scales):
+    wl = synth.with_fp8_kv(gen(name, **kw), rowscale=scales)
+    if scales:
+        wl = synth.with_scales(wl)
+    _attend8_check(lib, wl)
+
+
+def test_attend_fp8kv_window_only_and_padding(lib):
+    """Every index -1 (window rows only; query 0 sees none), then a selection padded with -1."""
+    import dataclasses
+    wl = synth.with_fp8_kv(gen("replay_h100k", B=1, lengths=2000, replay=(2000, 4)))
+    clip = wl.swa_clip.clone()
+    clip[0] = wl.q_pos[0] + 1
+    wl = dataclasses.replace(wl, swa_clip=clip)
+    out, lse = _attend8_check(lib, wl, np.full((wl.T, wl.k), -1, dtype=np.int32))
+    assert torch.all(out[0] == 0) and torch.all(torch.isneginf(lse[0]))
+    wl = synth.with_fp8_kv(gen("decode_8k", B=2, lengths=(1500, 2500), k=2048))
+    a = np_inputs(wl)
+    S = ref.score(a["qI"], a["w"], a["kI"], a["kscale"], a["seq_start"], a["q_start"], a["q_pos"])
+    idx = ref.topk(S, wl.k)
+    assert (idx == -1).any()
+    _attend8_check(lib, wl, idx)
 
 
 # ------------------------------------------------------------------ decode step
