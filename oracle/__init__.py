@@ -24,6 +24,9 @@ What it computes (sources: the vLLM blog post "DeepSeek-V4.1-Flash sur vLLM :
 * ``ref.attend_fp8kv`` — the same attention over an FP8 global cache (E4M3
   rows times a row scale), the format the FP4 cache replaced (digest §"Les
   particularités du modèle lui-même": the FP4 cache is about 45% smaller).
+* ``ref.attend_nvfp4`` — the same attention over a global cache in the NVFP4
+  layout the pages name (E2M1, an E4M3 scale per 16 elements, an fp32 tensor
+  scale).
 * ``ref.decode_step`` — the three in sequence.
 * ``brute`` — the same definitions as pure-Python loops for tiny inputs.
 
@@ -32,7 +35,7 @@ decoded exactly from the stored bytes (``codecs``).  Readings taken where the
 pages are silent are listed in the design doc of the repository and restated at
 each function.
 
-Parity status: codecs, score, topk, attend and attend_fp8kv are pinned by closed forms,
+Parity status: codecs, score, topk, attend, attend_fp8kv and attend_nvfp4 are pinned by closed forms,
 brute force, textbook special cases and invariants (tests/test_oracle.py,
 tests/test_codecs.py, tests/golden/).  Two readings cannot be pinned against
 any number printed on the pages — the ReLU-weighted indexer form and K = V

@@ -49,6 +49,17 @@ def global_row(codes_row, e8_row, rho) -> list:
     return out
 
 
+def nvfp4_row(codes_row, scales_row, rho, g) -> list:
+    out = []
+    D = 2 * len(codes_row)
+    for d in range(D):
+        byte = int(codes_row[d // 2])
+        nib = (byte >> 4) if (d & 1) else (byte & 15)
+        v = e2m1_scalar(nib) * e4m3_scalar(int(scales_row[d // 16])) * float(g)
+        out.append(v * (1.0 if rho is None else float(rho)))
+    return out
+
+
 def window_row(codes_row, sigma) -> list:
     return [e4m3_scalar(int(c)) * (1.0 if sigma is None else float(sigma)) for c in codes_row]
 

@@ -93,6 +93,23 @@ def global_rows(codes: np.ndarray, e8: np.ndarray, rowscale) -> np.ndarray:
     return v
 
 
+def nvfp4_rows(codes: np.ndarray, scales: np.ndarray, rowscale, tensor_scale: float) -> np.ndarray:
+    """Decode NVFP4 latent rows: V[j,d] = e2m1(nib(j,d)) * e4m3(S[j, d//16]) * rho_j * g.
+
+    The NVFP4 layout: E2M1 elements with one E4M3 scale per 16 elements and one fp32 scale g
+    for the whole tensor; rho (optional, None = 1) is an extra fp32 row scale.  codes uint8
+    [R, D/2], scales uint8 [R, D/16].
+    """
+    vals = e2m1_unpack(codes)
+    R, D = vals.shape
+    sc = np.repeat(e4m3(scales), 16, axis=1)
+    assert sc.shape == (R, D)
+    v = vals * sc * float(tensor_scale)
+    if rowscale is not None:
+        v = v * np.asarray(rowscale, dtype=np.float64)[:, None]
+    return v
+
+
 def window_rows(codes: np.ndarray, scale) -> np.ndarray:
     """Decode sliding-window rows: X[u,d] = e4m3(byte) * sigma_u (sigma = 1 when None)."""
     x = e4m3(codes)

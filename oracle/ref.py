@@ -25,6 +25,8 @@ Readings where the pages are silent (each restated where it is used):
   R6  an empty row set gives O = 0 and LSE = -inf
   R7  the FP8 global cache (the baseline format) is E4M3 rows with one fp32
       scale per row
+  R8  NVFP4 = E2M1 with one E4M3 scale per 16 elements and one fp32 tensor
+      scale (the pages name the format only)
 """
 from __future__ import annotations
 
@@ -188,6 +190,26 @@ def attend_fp8kv(q, kv_fp8, kv_rowscale, idx, swa, swa_scale, swa_pos0, swa_clip
 
     def global_of(rows):
         return codecs.window_rows(codes[rows], None if rs is None else rs[rows])
+    return _attend_union(q, global_of, idx, swa, swa_scale, swa_pos0, swa_clip, seq_start,
+                         q_start, q_pos, W, sm_scale)
+
+
+def attend_nvfp4(q, kv_codes, kv_scales, kv_rowscale, kv_global_scale, idx, swa, swa_scale,
+                 swa_pos0, swa_clip, seq_start, q_start, q_pos, W, sm_scale):
+    """The same attention over a global cache in the NVFP4 layout.
+
+    Blog §Kernels and CocoLoop digest §"Les particularités du modèle lui-même" name the
+    global KV format NVFP4: E2M1 elements, one E4M3 scale per 16 consecutive elements and
+    one fp32 scale g per tensor (reading R8), V[j, d] = e2m1 * e4m3(S[j, d // 16]) * rho_j * g
+    with the optional fp32 row scale rho of the MX layout kept; everything else is `attend`.
+    kv_codes uint8 [N, D/2], kv_scales uint8 [N, D/16], kv_rowscale float32 [N] or None.
+    """
+    codes, sc = np.asarray(kv_codes), np.asarray(kv_scales)
+    rs = None if kv_rowscale is None else np.asarray(kv_rowscale)
+
+    def global_of(rows):
+        return codecs.nvfp4_rows(codes[rows], sc[rows], None if rs is None else rs[rows],
+                                 kv_global_scale)
     return _attend_union(q, global_of, idx, swa, swa_scale, swa_pos0, swa_clip, seq_start,
                          q_start, q_pos, W, sm_scale)
 

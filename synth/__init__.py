@@ -87,6 +87,9 @@ class Workload:
     cand: Optional[torch.Tensor] = None  # int32 [T, n_cand]   ascending candidate positions
     kv_fp8: Optional[torch.Tensor] = None        # uint8 [N, D]  E4M3 global latent (FP8 cache)
     kv_fp8_scale: Optional[torch.Tensor] = None  # float32 [N]   its row scales
+    kv_nv_codes: Optional[torch.Tensor] = None   # uint8 [N, D/2]  NVFP4 global latent: E2M1
+    kv_nv_scales: Optional[torch.Tensor] = None  # uint8 [N, D/16] E4M3 scale per 16 elements
+    kv_nv_global: float = 1.0                    # its fp32 tensor scale
     meta: dict = field(default_factory=dict)
 
     @property
@@ -332,6 +335,38 @@ def with_fp8_kv(wl: Workload, seed: int = 2, rowscale: bool = True) -> Workload:
             rho[r0:r0 + x.shape[0]] = r
     _randn_rows(g, wl.N, wl.D, dev, put)
     return dataclasses.replace(wl, kv_fp8=kv, kv_fp8_scale=rho if rowscale else None)
+
+
+def encode_nvfp4(x: torch.Tensor, g: float):
+    """float32 rows [R, D] -> (E2M1 codes uint8 [R, D/2], E4M3 scales uint8 [R, D/16]) for
+    tensor scale g: each 16-element block gets the E4M3 scale s = RNE(amax / 6 / g) and its
+    elements are rounded to E2M1 after division by s * g (0 for an all-zero block)."""
+    R, D = x.shape
+    assert D % 16 == 0
+    blocks = x.view(R, D // 16, 16)
+    bmax = blocks.abs().amax(dim=2)
+    sc = encode_e4m3(bmax / 6.0 / g)
+    sv = sc.view(torch.float8_e4m3fn).to(torch.float32) * g
+    y = torch.where(sv[..., None] > 0, blocks / sv[..., None], torch.zeros_like(blocks))
+    codes = _e2m1_round(y).view(R, D).to(torch.int32)
+    packed = (codes[:, 0::2] | (codes[:, 1::2] << 4)).to(torch.uint8)
+    return packed, sc
+
+
+def with_nvfp4_kv(wl: Workload, seed: int = 3, g: float = 2.0 ** -8) -> Workload:
+    """Attach a global latent cache in the NVFP4 layout (fresh N(0,1) rows, tensor scale g)."""
+    dev = wl.kI.device
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(seed)
+    codes = torch.empty((wl.N, wl.D // 2), dtype=torch.uint8, device=dev)
+    scales = torch.empty((wl.N, wl.D // 16), dtype=torch.uint8, device=dev)
+
+    def put(r0, x):
+        c, sc = encode_nvfp4(x, g)
+        codes[r0:r0 + x.shape[0]] = c
+        scales[r0:r0 + x.shape[0]] = sc
+    _randn_rows(gen, wl.N, wl.D, dev, put)
+    return dataclasses.replace(wl, kv_nv_codes=codes, kv_nv_scales=scales, kv_nv_global=g)
 
 
 def with_scales(wl: Workload, seed: int = 1) -> Workload:

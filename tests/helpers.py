@@ -15,11 +15,11 @@ def np_inputs(wl) -> dict:
     a = {}
     for name in ("seq_start", "q_start", "q_pos", "qI", "w", "kI", "kscale", "kv_codes",
                  "kv_e8m0", "kv_rowscale", "swa", "swa_scale", "swa_pos0", "swa_clip", "cand",
-                 "kv_fp8", "kv_fp8_scale"):
+                 "kv_fp8", "kv_fp8_scale", "kv_nv_codes", "kv_nv_scales"):
         v = getattr(w, name)
         a[name] = None if v is None else v.numpy()
     a["q"] = w.q.view(torch.int16).numpy().view(np.uint16)
-    for name in ("k", "W", "sm_scale", "Hi", "Di", "Hq", "D", "T", "B", "max_ctx"):
+    for name in ("k", "W", "sm_scale", "Hi", "Di", "Hq", "D", "T", "B", "max_ctx", "kv_nv_global"):
         a[name] = getattr(w, name)
     return a
 
@@ -52,8 +52,9 @@ def brute_scores(a, cand=None) -> list:
     return out
 
 
-def brute_attend(a, idx, fp8kv=False) -> tuple:
-    """Scalar-loop attention; fp8kv takes the global rows from kv_fp8 / kv_fp8_scale."""
+def brute_attend(a, idx, fp8kv=False, nvfp4=False) -> tuple:
+    """Scalar-loop attention; fp8kv takes the global rows from kv_fp8 / kv_fp8_scale, nvfp4
+    from kv_nv_codes / kv_nv_scales / kv_nv_global (with the row scale kv_rowscale)."""
     qs = q_seq_of(a)
     T, Hq, D = a["q"].shape
     O = np.zeros((T, Hq, D))
@@ -72,6 +73,10 @@ def brute_attend(a, idx, fp8kv=False) -> tuple:
                 rows.append(brute.window_row(a["kv_fp8"][r], rho))
                 continue
             rho = None if a["kv_rowscale"] is None else a["kv_rowscale"][r]
+            if nvfp4:
+                rows.append(brute.nvfp4_row(a["kv_nv_codes"][r], a["kv_nv_scales"][r], rho,
+                                            a["kv_nv_global"]))
+                continue
             rows.append(brute.global_row(a["kv_codes"][r], a["kv_e8m0"][r], rho))
         p = int(a["q_pos"][t])
         lo = max(p - W + 1, 0)

@@ -320,6 +320,62 @@ def test_attend_fp8kv_of_an_exact_reencoding_equals_fp4():
     assert np.array_equal(O4, O8) and np.array_equal(L4, L8)
 
 
+def _attend_nv(a, idx, **over):
+    b = dict(a)
+    b.update(over)
+    return ref.attend_nvfp4(b["q"], b["kv_nv_codes"], b["kv_nv_scales"], b["kv_rowscale"],
+                            b["kv_nv_global"], idx, b["swa"], b["swa_scale"], b["swa_pos0"],
+                            b["swa_clip"], b["seq_start"], b["q_start"], b["q_pos"], b["W"],
+                            b["sm_scale"])
+
+
+@pytest.mark.parametrize("seed,clip,rowscale", [(0, False, True), (1, True, False)])
+def test_attend_nvfp4_matches_brute(seed, clip, rowscale):
+    wl = synth.with_nvfp4_kv(synth.with_scales(tiny(seed, B=2, lengths=(20, 37), rowscale=rowscale),
+                                               seed=seed), seed=seed, g=0.75)
+    a = np_inputs(wl)
+    if clip:
+        a["swa_clip"] = (a["q_pos"] - 3).astype(np.int32)
+    S = ref.score(a["qI"], a["w"], a["kI"], a["kscale"], a["seq_start"], a["q_start"], a["q_pos"])
+    idx = ref.topk(S, a["k"])
+    O, L = _attend_nv(a, idx)
+    Ob, Lb = brute_attend(a, idx, nvfp4=True)
+    assert np.allclose(O, Ob, rtol=1e-12, atol=1e-14)
+    assert np.allclose(L, Lb, rtol=1e-12, atol=1e-14)
+
+
+def test_attend_nvfp4_of_an_exact_reencoding_equals_mx():
+    """The MX layout's power-of-two block scales 2^(E-127) are E4M3 values here: the same E2M1
+    codes with those scales written per 16 elements (tensor scale 1) must give the MX
+    layout's attention exactly."""
+    wl = synth.with_scales(tiny(4, B=2, lengths=(30, 45)), seed=4)
+    a = np_inputs(wl)
+    pw = codecs.e8m0(a["kv_e8m0"])                                  # [N, D/32]
+    e4 = synth.encode_e4m3(torch.tensor(np.repeat(pw, 2, axis=1), dtype=torch.float32)).numpy()
+    assert np.array_equal(codecs.e4m3(e4), np.repeat(pw, 2, axis=1))   # exact re-encoding
+    S = ref.score(a["qI"], a["w"], a["kI"], a["kscale"], a["seq_start"], a["q_start"], a["q_pos"])
+    idx = ref.topk(S, a["k"])
+    Om, Lm = _attend(a, idx)
+    On, Ln = _attend_nv(a, idx, kv_nv_codes=a["kv_codes"], kv_nv_scales=e4, kv_nv_global=1.0)
+    assert np.array_equal(Om, On) and np.array_equal(Lm, Ln)
+
+
+def test_nvfp4_tensor_scale_is_linear_in_the_rows():
+    """Scaling g by 2 doubles every decoded global row (checked on the decoder) and, with the
+    row-free window empty, leaves the attention weights those of the logits doubled."""
+    wl = synth.with_nvfp4_kv(tiny(5, lengths=40), seed=5, g=0.5)
+    a = np_inputs(wl)
+    r1 = codecs.nvfp4_rows(a["kv_nv_codes"][:8], a["kv_nv_scales"][:8], None, 0.5)
+    r2 = codecs.nvfp4_rows(a["kv_nv_codes"][:8], a["kv_nv_scales"][:8], None, 1.0)
+    assert np.array_equal(2 * r1, r2)
+    idx = np.arange(a["k"])[None, :] % 40
+    idx = np.sort(np.unique(idx))[None, :a["k"]]
+    clip = np.array([10_000], dtype=np.int32)                       # no window row
+    O1, _ = _attend_nv(a, idx, swa_clip=clip, kv_nv_global=0.5)
+    O2, _ = _attend_nv(a, idx, swa_clip=clip, kv_nv_global=1.0, sm_scale=a["sm_scale"] / 2)
+    assert np.allclose(2 * O1, O2, rtol=1e-12, atol=1e-14)
+
+
 # ----------------------------------------------------------------- window clipping
 
 def _replay(H=50, nq=6, W=8, seed=13):
