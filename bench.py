@@ -181,6 +181,12 @@ def measure(name, steps, warmup, use_graph, stage_only="", fp8_baseline=True):
     stages = {"score": st_score, "topk": st_topk, "attend": st_attend}
     if stage_only == "copy":
         stages["copy"] = st_copy
+    if stage_only == "attend_nvfp4":
+        wlns = synth.with_nvfp4_kv(wl)
+        stages["attend_nvfp4"] = lambda: smqa.sparse_mqa_attend_nvfp4(
+            L, wl.q, wlns.kv_nv_codes, wlns.kv_nv_scales, wl.kv_rowscale, wlns.kv_nv_global, idx2,
+            wl.swa, wl.swa_scale, wl.swa_pos0, wl.swa_clip, wl.sm_scale, out=out2, lse=lse2,
+            workspace=ws)
     if stage_only == "attend_fp8kv":
         wl8s = synth.with_fp8_kv(wl)
         stages["attend_fp8kv"] = lambda: smqa.sparse_mqa_attend_fp8kv(
@@ -311,7 +317,7 @@ def measure(name, steps, warmup, use_graph, stage_only="", fp8_baseline=True):
         st_us[nm] = timed_us(fn)
 
     # the same attention over an FP8 global cache (E4M3 rows + row scale, the format the FP4
-    # cache replaces) on the same selection: what the FP4 format saves
+    # cache replaces) and over the NVFP4 layout, on the same selection: what the formats cost
     fp8kv = None
     if fp8_baseline and wl.Hq % 32 == 0 and wl.D <= 1664:
         print(f"[bench] {name}: FP8-cache attention x{steps}", file=sys.stderr, flush=True)
@@ -323,12 +329,26 @@ def measure(name, steps, warmup, use_graph, stage_only="", fp8_baseline=True):
                                          wl.swa_scale, wl.swa_pos0, wl.swa_clip, wl.sm_scale,
                                          out=out2, lse=lse2, workspace=ws)
         us8 = timed_us(st_attend8)
-        row4 = wl.D // 2 + wl.D // 32 + (4 if wl.kv_rowscale is not None else 0)
-        fp8kv = {"attend_us_fp8_cache": round(us8, 2), "attend_us_fp4_cache": round(st_us["attend"], 2),
-                 "fp8_over_fp4_time": round(us8 / st_us["attend"], 3),
-                 "global_row_bytes": {"fp4": row4, "fp8": wl.D + 4},
-                 "kernel": "attend: sd::attend_kernel<D, G8=true> (16-row E4M3 global tiles) + attend_merge_kernel"}
         del wl8
+        print(f"[bench] {name}: NVFP4-cache attention x{steps}", file=sys.stderr, flush=True)
+        wln = synth.with_nvfp4_kv(wl)
+        torch.cuda.synchronize()
+
+        def st_attend_nv():
+            smqa.sparse_mqa_attend_nvfp4(L, wl.q, wln.kv_nv_codes, wln.kv_nv_scales, wl.kv_rowscale,
+                                         wln.kv_nv_global, idx2, wl.swa, wl.swa_scale, wl.swa_pos0,
+                                         wl.swa_clip, wl.sm_scale, out=out2, lse=lse2, workspace=ws)
+        usn = timed_us(st_attend_nv)
+        del wln
+        rs = 4 if wl.kv_rowscale is not None else 0
+        fp8kv = {"attend_us": {"mx_fp4": round(st_us["attend"], 2), "nvfp4": round(usn, 2),
+                               "fp8": round(us8, 2)},
+                 "fp8_over_mx_fp4_time": round(us8 / st_us["attend"], 3),
+                 "nvfp4_over_mx_fp4_time": round(usn / st_us["attend"], 3),
+                 "global_row_bytes": {"mx_fp4": wl.D // 2 + wl.D // 32 + rs,
+                                      "nvfp4": wl.D // 2 + wl.D // 16 + rs, "fp8": wl.D + 4},
+                 "kernel": "attend: sd::attend_kernel<D, F> (F = MX FP4 / NVFP4 / FP8 rows in "
+                           "16-row tiles) + attend_merge_kernel"}
     dom = max(st_us, key=st_us.get)
     best_s = min(x for x in (eager_s, graph_s, chain_s) if x)
     res = {
@@ -341,7 +361,7 @@ def measure(name, steps, warmup, use_graph, stage_only="", fp8_baseline=True):
         "tokens_scored_per_s": J / best_s,
         "stage_us": {k: round(v, 2) for k, v in st_us.items()},
         "stage_roofline": {k: roofline(k, w[k], st_us[k] * 1e-6, name) for k in st_us},
-        "fp8_cache_baseline": fp8kv,
+        "global_cache_formats": fp8kv,
         "roofline": roofline(dom, w[dom], st_us[dom] * 1e-6, name),
         "config": dict(wl.meta["params"], lengths=(wl.meta["lengths"] if wl.B <= 8 else
                                                   [min(wl.meta["lengths"]), max(wl.meta["lengths"])])),

@@ -55,6 +55,8 @@ _SIGS = {
                                _P, _P, _P, _S, _P]),
     "sparse_mqa_attend_fp8kv": (_I, [_LP, _P, _P, _P, _P, _I, _P, _P, _P, _P, _I, _I, _I, _F,
                                      _P, _P, _P, _S, _P]),
+    "sparse_mqa_attend_nvfp4": (_I, [_LP, _P, _P, _P, _P, _F, _P, _I, _P, _P, _P, _P, _I, _I, _I,
+                                     _F, _P, _P, _P, _S, _P]),
     "decode_step": (_I, [_LP, _P, _P, _P, _P, _P, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P, _P,
                          _I, _I, _I, _F, _I, _P, _P, _P, _P, _S, _P]),
     "smqa_topk_workspace_size": (_S, [_LP, _I, _I]),
@@ -252,6 +254,41 @@ def sparse_mqa_attend_fp8kv(L: Batch, q, kv_fp8, kv_rowscale, idx, swa, swa_scal
                                        k, _ptr(swa), _ptr(swa_scale), _ptr(swa_pos0),
                                        _ptr(swa_clip), W, Hq, D, float(sm_scale), _ptr(out),
                                        _ptr(lse), wp, wb, _stream(stream)))
+    return out, lse
+
+
+def sparse_mqa_attend_nvfp4(L: Batch, q, kv_codes, kv_scales, kv_rowscale, kv_global_scale: float,
+                            idx, swa, swa_scale, swa_pos0, swa_clip, sm_scale: float, out=None,
+                            lse=None, workspace=None, stream=None):
+    """Sparse MQA attention over an NVFP4 global cache -> (out float32 [T, Hq, D], lse)."""
+    lib = load()
+    _dev(q, "q", torch.bfloat16, 3)
+    _dev(kv_codes, "kv_codes", torch.uint8, 2)
+    _dev(kv_scales, "kv_scales", torch.uint8, 2)
+    _dev(kv_rowscale, "kv_rowscale", torch.float32, 1)
+    _dev(idx, "idx", torch.int32, 2)
+    _dev(swa, "swa", _U8, 3)
+    _dev(swa_scale, "swa_scale", torch.float32, 2)
+    _dev(swa_pos0, "swa_pos0", torch.int32, 1)
+    _dev(swa_clip, "swa_clip", torch.int32, 1)
+    T, Hq, D = q.shape
+    W = swa.shape[1]
+    k = idx.shape[1]
+    if out is None:
+        out = torch.empty((T, Hq, D), dtype=torch.float32, device=q.device)
+    if lse is None:
+        lse = torch.empty((T, Hq), dtype=torch.float32, device=q.device)
+    _dev(out, "out", torch.float32, 3)
+    _dev(lse, "lse", torch.float32, 2)
+    need = lib.smqa_attend_workspace_size(L.ref, k, W, Hq, D)
+    if workspace is None:
+        workspace = _workspace(need, q.device)
+    wp, wb = _ws_ptr(workspace)
+    _check(lib.sparse_mqa_attend_nvfp4(L.ref, _ptr(q), _ptr(kv_codes), _ptr(kv_scales),
+                                       _ptr(kv_rowscale), float(kv_global_scale), _ptr(idx), k,
+                                       _ptr(swa), _ptr(swa_scale), _ptr(swa_pos0), _ptr(swa_clip),
+                                       W, Hq, D, float(sm_scale), _ptr(out), _ptr(lse), wp, wb,
+                                       _stream(stream)))
     return out, lse
 
 

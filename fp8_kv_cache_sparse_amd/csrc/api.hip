@@ -1,6 +1,7 @@
 // C-ABI entry points of libsmqa: host-side validation, workspace carving and
 // launches on the caller's stream.  Every check runs before the first HIP call,
 // so argument errors are reported without touching a device.
+#include <cmath>
 #include <cstdarg>
 #include <cstdio>
 #include <string>
@@ -255,9 +256,39 @@ int sparse_mqa_attend_fp8kv(const smqa_layout* L, const uint16_t* q_bf16, const 
   if (st) return st;
   smqa::AttendArgs a{L->seq_start, L->q_start, L->q_pos, L->num_seqs, L->num_q, q_bf16, kv_fp8,
                      nullptr, kv_rowscale, idx, k, swa_fp8, swa_scale, swa_pos0, swa_clip, W, Hq, D,
-                     sm_scale, out, lse, workspace, 1};
-  hipError_t e = smqa::launch_attend_fp8kv(a, (hipStream_t)stream);
+                     sm_scale, out, lse, workspace, 1, 1.0f};
+  hipError_t e = smqa::launch_attend_fmt(a, (hipStream_t)stream);
   return e == hipSuccess ? SMQA_OK : hip_fail(e, "sparse_mqa_attend_fp8kv launch");
+}
+
+int sparse_mqa_attend_nvfp4(const smqa_layout* L, const uint16_t* q_bf16, const uint8_t* kv_codes,
+                            const uint8_t* kv_scales, const float* kv_rowscale, float kv_global_scale,
+                            const int32_t* idx, int32_t k, const uint8_t* swa_fp8,
+                            const float* swa_scale, const int32_t* swa_pos0, const int32_t* swa_clip,
+                            int32_t W, int32_t Hq, int32_t D, float sm_scale, float* out, float* lse,
+                            void* workspace, size_t workspace_bytes, void* stream) {
+  g_err.clear();
+  int st = check_layout(L);
+  if (st) return st;
+  if (L->num_q == 0) return SMQA_OK;
+  st = check_attend(q_bf16, kv_codes, kv_scales, kv_rowscale, idx, k, swa_fp8, swa_scale, swa_pos0,
+                    swa_clip, W, Hq, D, sm_scale, out, lse, true);
+  if (st) return st;
+  if (Hq % 32 != 0 || D > 1664)
+    return fail(SMQA_ERR_UNSUPPORTED, "NVFP4 global cache: Hq = %d, D = %d; supported Hq %% 32 == 0, D <= 1664",
+                Hq, D);
+  if (!(kv_global_scale >= 1e-30f && kv_global_scale <= 1e30f))
+    return fail(SMQA_ERR_SHAPE, "kv_global_scale must lie in [1e-30, 1e30]");
+  int ex = 0;
+  std::frexp(kv_global_scale, &ex);              // g = f * 2^ex, f in [0.5, 1)
+  const float K = std::ldexp(1.0f, 1 - ex);      // g * K = 2 f in [1, 2)
+  st = check_ws(workspace, workspace_bytes, smqa::attend_workspace_bytes(L->num_q, k, W, Hq, D));
+  if (st) return st;
+  smqa::AttendArgs a{L->seq_start, L->q_start, L->q_pos, L->num_seqs, L->num_q, q_bf16, kv_codes,
+                     kv_scales, kv_rowscale, idx, k, swa_fp8, swa_scale, swa_pos0, swa_clip, W, Hq, D,
+                     sm_scale, out, lse, workspace, 2, kv_global_scale, K};
+  hipError_t e = smqa::launch_attend_fmt(a, (hipStream_t)stream);
+  return e == hipSuccess ? SMQA_OK : hip_fail(e, "sparse_mqa_attend_nvfp4 launch");
 }
 
 int decode_step(const smqa_layout* L, const uint8_t* q_fp8, const float* w, const uint8_t* k_fp8,

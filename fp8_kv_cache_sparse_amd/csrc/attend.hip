@@ -1152,12 +1152,12 @@ static hipError_t launch_thr(const AttendArgs& a, const AttPlan& p, hipStream_t 
 
 hipError_t launch_attend_sd(const AttendArgs& a, int S, hipStream_t s);
 
-// FP8 global cache: only the dimension-split kernel reads it (Hq % 32 == 0, D <= 1664,
-// checked by the caller); the split count and workspace are those of the FP4 call.
-hipError_t launch_attend_fp8kv(const AttendArgs& a, hipStream_t s) {
+// FP8 and NVFP4 global caches: only the dimension-split kernel reads them (Hq % 32 == 0,
+// D <= 1664, checked by the caller); the split count and workspace are those of the MX call.
+hipError_t launch_attend_fmt(const AttendArgs& a, hipStream_t s) {
   if (a.T == 0) return hipSuccess;
   const AttPlan p = attend_plan(a.T, a.k, a.W, a.Hq, a.D);
-  if (!p.wide || a.D > 1664 || !a.kv_fp8) return hipErrorInvalidValue;
+  if (!p.wide || a.D > 1664 || (a.kv_fmt != 1 && a.kv_fmt != 2)) return hipErrorInvalidValue;
   return launch_attend_sd(a, p.S, s);
 }
 

@@ -30,6 +30,16 @@
 //            scales (v_pk_mul_f16: the scale is exact in fp16 for -24 <= e - 127 <= 15, the
 //            product for -23 <= e - 127 <= 13); P carries the row scale rho (or sigma).
 //
+// Two more global-cache formats take the same pipeline.  FP8 rows (E4M3 with a row scale,
+// the format the FP4 cache replaced) come in 16-row tiles that take the window tiles'
+// products.  NVFP4 (E2M1 with an E4M3 scale per 16 elements and a tensor scale; CocoLoop
+// digest, section "Les particularités du modèle lui-même") keeps the 32-row E2M1 tiles; its
+// scale dwords land block-major ([dword][row]) so that Q.K^T reads one byte per lane and
+// P.V the 16 rows of a transpose read from 64 contiguous bytes, paired by v_perm.  Both
+// products multiply fp16 codes (converted with scale 1) by the fp16 block scale, exactly;
+// the scaled conversions are meant for power-of-two (E8M0) scales and are not trusted with
+// an E4M3 one.  Q.K^T then runs on fp16 MFMA, q converted to fp16 once.
+//
 // Several tile ranges of one (query, head group) leave unnormalised partials that
 // attend_merge_kernel combines by log-sum-exp.
 #include <type_traits>
@@ -53,8 +63,13 @@ constexpr int kNBuf = 4;      // tile buffers in LDS: tiles i-1 (P.V), i (Q.K^T)
 
 constexpr int align16(int x) { return (x + 15) & ~15; }
 
-// LDS geometry for latent width D (compile time, so every offset is an immediate).
-template <int D>
+// Global cache formats: MX FP4 (E2M1, E8M0 per 32, fp32 row scale), FP8 rows (E4M3, row
+// scale) and NVFP4 (E2M1, E4M3 per 16, row scale, fp32 tensor scale).
+constexpr int kMX = 0, kFP8 = 1, kNV = 2;
+
+// LDS geometry for latent width D and global format F (compile time, so every offset is an
+// immediate).
+template <int D, int F>
 struct Geo {
   static constexpr int NB = D / 32;                 // 32-dim blocks
   static constexpr int BPW = NB / 8;                // blocks of every wave
@@ -62,23 +77,28 @@ struct Geo {
   static constexpr int NBW = BPW + (EXTRA ? 1 : 0); // most blocks of one wave
   static constexpr int RS4 = D / 2 + 16;            // E2M1 row stride (16 * odd dwords / 4)
   static constexpr int RS8 = D + 16;                // E4M3 row stride
-  static constexpr int E8S = D / 32;                // raw E8M0 bytes per row
-  // one tile buffer: codes | raw E8M0 [32][E8S] | row scales [4 loader waves][8]
+  static constexpr int E8S = D / 32;                // raw E8M0 bytes per row (MX)
+  static constexpr int NQ = D / 64;                 // dwords of E4M3 block scales per row (NV)
+  // one tile buffer: codes | block scales | row scales [4 loader waves][8]; the block scales
+  // are the raw E8M0 bytes [32 rows][E8S] (MX) or the E4M3 scale dwords [NQ][32 rows] (NV,
+  // block-major, so the 16 rows of one transpose read are 64 contiguous bytes)
   static constexpr int CODES = kRows * RS4;
   static constexpr int E8 = CODES;
-  static constexpr int RHO = align16(E8 + kRows * E8S);
+  static constexpr int RHO = align16(E8 + (F == kNV ? NQ * kRows * 4 : kRows * E8S));
   static constexpr int BUF = align16(RHO + kRows * 4);
   // shared areas after the buffers
   static constexpr int RING = kNBuf * BUF;                      // positions [4][32]
-  static constexpr int SCH = RING + kNBuf * kRows * 4;          // [2][NB][16] u32: f16 scale pairs
-  static constexpr int RED = SCH + 2 * NB * 16 * 4;             // [8 waves][32 heads][32 rows] f32
+  static constexpr int SCHN = F == kMX ? NB * 16 : 16;          // u32 per slot: MX f16 scale pairs
+  static constexpr int SCH = RING + kNBuf * kRows * 4;          // [2][SCHN]: scale pairs / row masks
+  static constexpr int RED = SCH + 2 * SCHN * 4;                // [8 waves][32 heads][32 rows] f32
   static constexpr int PS = RED + 8 * 32 * kRows * 4;           // P [32 heads][40] f16
   static constexpr int RI = PS + 32 * 40 * 2;                   // logit scale[32], P scale[32]
   static constexpr int MR = RI + 2 * 32 * 4;                    // mref[32] alpha[32] lsum[32]
   static constexpr int LDS = MR + 3 * 32 * 4;
   // global loads a loader wave issues per tile (fixed, so vmcnt can wait for the older tile)
   static constexpr int PIECES8 = D / 16;                        // 16-byte pieces of an E4M3 row
-  static constexpr int NLOAD4 = kRows / 8 + 1 + 1;              // 4 code rows, E8M0, rho
+  static constexpr int NSC = F == kNV ? (D / 128 + 7) / 8 : 1;  // block-scale loads per wave
+  static constexpr int NLOAD4 = kRows / 8 + NSC + 1;            // 4 code rows, block scales, rho
   static constexpr int NLOAD8 = (kWRows / 8) * (PIECES8 > 64 ? 2 : 1) + 1;  // 2 rows, sigma
   static_assert(kWRows * RS8 <= CODES, "a window tile must fit a buffer");
   static_assert(EXTRA == 0 || EXTRA == 4, "D must be a multiple of 128");
@@ -207,12 +227,14 @@ __device__ __forceinline__ SeqInfo locate_seq(const AttendArgs& a, int t, int la
   }
 }
 
-// G8: the global cache holds E4M3 rows with a row scale (the FP8 cache the FP4 format
-// replaced) instead of E2M1 + E8M0; its tiles are then 16 gathered rows that take the
-// window tiles' products.
-template <int D, bool G8>
+// F = kFP8: the global cache holds E4M3 rows with a row scale (the FP8 cache the FP4 format
+// replaced); its tiles are then 16 gathered rows that take the window tiles' products.
+// F = kNV: E2M1 with an E4M3 scale per 16 elements (a.kv_e8m0 points at them) and the
+// tensor scale a.kv_gscale; the tiles are those of the MX format.
+template <int D, int F>
 __global__ __launch_bounds__(kThreads) void attend_kernel(AttendArgs a, int S, int ngroups, int total) {
-  using G = Geo<D>;
+  using G = Geo<D, F>;
+  constexpr bool G8 = F == kFP8, NV = F == kNV;
   constexpr int GR = G8 ? kWRows : kRows;         // global rows per tile
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
 
@@ -326,8 +348,20 @@ __global__ __launch_bounds__(kThreads) void attend_kernel(AttendArgs a, int S, i
           const uint8_t* src = ok ? row : dummy;
           if (ln < D / 32) gload16(src + 16 * ln, lds_addr(B + r * G::RS4));
         }
-        // raw E8M0: rows 4 wave .. +4, contiguous
-        {
+        if constexpr (NV) {
+          // E4M3 scale dwords q = 2m + lane / 32 of row lane % 32 -> table[q][row]: D/128
+          // loads of 64 lanes per tile, dealt round the waves (the surplus repeat a load
+          // another wave makes: same bytes to the same place)
+          const int row = ln & 31;
+          const bool ok = (xt + row < c.gx1) & (pall >= 0);
+#pragma unroll
+          for (int u = 0; u < G::NSC; ++u) {
+            const int m = (wave + 8 * u) % (D / 128);
+            const int q = 2 * m + (ln >> 5);
+            const uint8_t* src = ok ? e8_base + (int64_t)pall * (D / 16) + 4 * q : dummy;
+            gload4(src, lds_addr(B + G::E8 + 2 * m * kRows * 4));
+          }
+        } else {  // raw E8M0: rows 4 wave .. +4, contiguous
           const int dd = ln % per_row;
           const bool ok = xt + re < c.gx1 && pe >= 0;
           const uint8_t* s0 = ok ? e8_base + (int64_t)pe * (D / 32) : dummy;
@@ -379,7 +413,18 @@ __global__ __launch_bounds__(kThreads) void attend_kernel(AttendArgs a, int S, i
       for (int cc = 0; cc < 2; ++cc) {
         v4u v = {0u, 0u, 0u, 0u};
         if (i < G::BPW || wave < G::EXTRA) v = *(const v4u*)(qrow + 32 * (b0 + i) + 8 * cc);
-        qa[i][cc] = __builtin_bit_cast(v8bf, v);
+        if constexpr (NV) {
+          // NVFP4 scores in fp16: bf16 -> fp16 is exact for 2^-14 <= |q| <= 65504
+          v8h h;
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            h[2 * j] = (_Float16)__uint_as_float(v[j] << 16);
+            h[2 * j + 1] = (_Float16)__uint_as_float(v[j] & 0xFFFF0000u);
+          }
+          qa[i][cc] = __builtin_bit_cast(v8bf, h);
+        } else {
+          qa[i][cc] = __builtin_bit_cast(v8bf, v);
+        }
       }
   }
   {
@@ -387,7 +432,7 @@ __global__ __launch_bounds__(kThreads) void attend_kernel(AttendArgs a, int S, i
     c.b = si.b;
     c.base = si.base;
     codes_base = a.kv_codes + si.base * (G8 ? D : D / 2);
-    e8_base = G8 ? nullptr : a.kv_e8m0 + si.base * (D / 32);
+    e8_base = G8 ? nullptr : a.kv_e8m0 + si.base * (NV ? D / 16 : D / 32);
     rho_base = a.kv_rowscale ? a.kv_rowscale + si.base : nullptr;
     c.pos0 = si.pos0;
     c.p = si.p;
@@ -425,14 +470,34 @@ __global__ __launch_bounds__(kThreads) void attend_kernel(AttendArgs a, int S, i
     if constexpr (decltype(FP4)::value) {
       const uint8_t* rowp = B + r32 * G::RS4 + 8 * kh + 16 * b0;
       const uint8_t* e8p = B + G::E8 + r32 * G::E8S + b0;
+      const uint8_t* nvp = B + G::E8 + r32 * 4 + kh;
 #pragma unroll
       for (int i = 0; i < G::NBW; ++i) {
         if (i < G::BPW || wave < G::EXTRA) {
-          // E8M0 e -> 2^(e-127) as the float e << 23 (e = 0, below 4e-38 in magnitude, gives 0)
-          const float scl = __uint_as_float((unsigned)lds<uint8_t>(e8p + i) << 23);
           const v2u wd = lds<v2u>(rowp + 16 * i);
-          acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[i][0], cvt8_fp4_bf16(wd.x, scl), acc, 0, 0, 0);
-          acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[i][1], cvt8_fp4_bf16(wd.y, scl), acc, 0, 0, 0);
+          if constexpr (NV) {
+            // the E4M3 scale of 16-block 2 (b0 + i) + kh: byte 2 ((b0 + i) & 1) + kh of dword
+            // (b0 + i) / 2 of the row.  The codes go to fp16 with scale 1 and are multiplied
+            // by the fp16 scale (exact), against q in fp16.
+            const int bb = b0 + i;
+            const unsigned byte = lds<uint8_t>(nvp + (bb >> 1) * (kRows * 4) + 2 * (bb & 1));
+            const v2h s2 = __builtin_bit_cast(v2h, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(byte * 0x101u, 1.0f, false));
+#pragma unroll
+            for (int cc = 0; cc < 2; ++cc) {
+              const unsigned w = cc ? wd.y : wd.x;
+              const v4u bw = {__builtin_bit_cast(unsigned, fp4x2_f16(w, 0) * s2),
+                              __builtin_bit_cast(unsigned, fp4x2_f16(w, 1) * s2),
+                              __builtin_bit_cast(unsigned, fp4x2_f16(w, 2) * s2),
+                              __builtin_bit_cast(unsigned, fp4x2_f16(w, 3) * s2)};
+              acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(v8h, qa[i][cc]),
+                                                           __builtin_bit_cast(v8h, bw), acc, 0, 0, 0);
+            }
+          } else {
+            // E8M0 e -> 2^(e-127) as the float e << 23 (e = 0, below 4e-38 in magnitude, gives 0)
+            const float scl = __uint_as_float((unsigned)lds<uint8_t>(e8p + i) << 23);
+            acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[i][0], cvt8_fp4_bf16(wd.x, scl), acc, 0, 0, 0);
+            acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[i][1], cvt8_fp4_bf16(wd.y, scl), acc, 0, 0, 0);
+          }
         }
       }
     } else {
@@ -441,8 +506,21 @@ __global__ __launch_bounds__(kThreads) void attend_kernel(AttendArgs a, int S, i
       for (int i = 0; i < G::NBW; ++i) {
         if (i < G::BPW || wave < G::EXTRA) {
           const v4u wd = lds<v4u>(rowp + 32 * i);
-          acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[i][0], cvt8_fp8_bf16(v2u{wd.x, wd.y}), acc, 0, 0, 0);
-          acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[i][1], cvt8_fp8_bf16(v2u{wd.z, wd.w}), acc, 0, 0, 0);
+          if constexpr (NV) {                    // q is held in fp16 here (E4M3 is exact in fp16)
+#pragma unroll
+            for (int cc = 0; cc < 2; ++cc) {
+              const unsigned w0 = cc ? wd.z : wd.x, w1 = cc ? wd.w : wd.y;
+              const v4u bw = {__builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w0, 1.0f, false)),
+                              __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w0, 1.0f, true)),
+                              __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w1, 1.0f, false)),
+                              __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w1, 1.0f, true))};
+              acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(v8h, qa[i][cc]),
+                                                           __builtin_bit_cast(v8h, bw), acc, 0, 0, 0);
+            }
+          } else {
+            acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[i][0], cvt8_fp8_bf16(v2u{wd.x, wd.y}), acc, 0, 0, 0);
+            acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[i][1], cvt8_fp8_bf16(v2u{wd.z, wd.w}), acc, 0, 0, 0);
+          }
         }
       }
     }
@@ -463,7 +541,7 @@ __global__ __launch_bounds__(kThreads) void attend_kernel(AttendArgs a, int S, i
     const int ct = opq(tid);                       // waves 0..3: 0..255
     const int ln = ct & 63;
     const uint8_t* B = smem + slot * G::BUF;
-    unsigned* sch = (unsigned*)(smem + G::SCH) + sslot * G::NB * 16;
+    unsigned* sch = (unsigned*)(smem + G::SCH) + sslot * G::SCHN;
     if constexpr (kind == 1) {
       const int* pos = (const int*)(smem + G::RING) + rslot * kRows;
       // rows that take part, as a bit mask (every loader wave computes it)
@@ -471,7 +549,15 @@ __global__ __launch_bounds__(kThreads) void attend_kernel(AttendArgs a, int S, i
       const unsigned vmask = (unsigned)__builtin_amdgcn_ballot_w64(ln < kRows && tile * kRows + ln < c.gx1 && pl >= 0);
       // blocks 4 bq .. 4 bq + 3 of rows 2 pp, 2 pp + 1 (one dword of raw E8M0 per row)
       const int pp = ct & 15, bq = ct >> 4;
-      if (bq < G::NB / 4) {
+      if constexpr (NV) {
+        // rows that take no part get zero block scales, so that their (dummy) codes give
+        // exact zeros in P.V; the products read the table only after the next barrier
+        if (vmask != 0xFFFFFFFFu) {
+          unsigned* tbl = (unsigned*)(B + G::E8);
+          for (int e = ct; e < G::NQ * kRows; e += 256)
+            if (!((vmask >> (e & 31)) & 1u)) tbl[e] = 0u;
+        }
+      } else if (bq < G::NB / 4) {
         const unsigned w0 = lds<unsigned>(B + G::E8 + (2 * pp) * G::E8S + 4 * bq);
         const unsigned w1 = lds<unsigned>(B + G::E8 + (2 * pp + 1) * G::E8S + 4 * bq);
         const bool v0 = (vmask >> (2 * pp)) & 1u, v1 = (vmask >> (2 * pp + 1)) & 1u;
@@ -487,8 +573,11 @@ __global__ __launch_bounds__(kThreads) void attend_kernel(AttendArgs a, int S, i
       if (ct < kRows) {
         const bool v = (vmask >> ct) & 1u;
         const float m = a.kv_rowscale ? ((const float*)(B + G::RHO))[4 * (ct & 7) + (ct >> 3)] : 1.0f;
-        rl[ct] = v ? c.lscale * m : 0.0f;
-        rp[ct] = v ? m : 0.0f;
+        // the NVFP4 tensor scale g: the logits take rho * g; P takes rho * g * K with K the
+        // power of two that puts g * K in [1, 2), and the epilogue 1 / K (P * rho * g alone
+        // would fall into fp16 subnormals for the usual g ~ amax / 2688)
+        rl[ct] = v ? (NV ? c.lscale * m * a.kv_gscale : c.lscale * m) : 0.0f;
+        rp[ct] = v ? (NV ? m * (a.kv_gscale * a.kv_pscale) : m) : 0.0f;
       }
     } else if (ct < kRows) {
       bool v;
@@ -504,7 +593,7 @@ __global__ __launch_bounds__(kThreads) void attend_kernel(AttendArgs a, int S, i
       const bool scaled = kind == 3 ? a.kv_rowscale != nullptr : a.swa_scale != nullptr;
       const float m = scaled ? ((const float*)(B + G::RHO))[4 * (ct & 7) + ((ct & 15) >> 3)] : 1.0f;
       rl[ct] = v ? c.lscale * m : 0.0f;
-      rp[ct] = v ? m : 0.0f;
+      rp[ct] = v ? (NV ? m * a.kv_pscale : m) : 0.0f;    // NVFP4: window P carries K too
       if (ct < kWRows / 2) {
         const unsigned pr = (vb >> (2 * ct)) & 3u;
         sch[ct] = ((pr & 1u) ? 0x0000FFFFu : 0u) | ((pr & 2u) ? 0xFFFF0000u : 0u);
@@ -559,7 +648,7 @@ __global__ __launch_bounds__(kThreads) void attend_kernel(AttendArgs a, int S, i
   auto pv = [&](auto FP4, int slot, int sslot) __attribute__((always_inline)) {
     SMQA_LANE_ROLES
     const uint8_t* B = smem + slot * G::BUF;
-    const unsigned* sch = (const unsigned*)(smem + G::SCH) + sslot * G::NB * 16;
+    const unsigned* sch = (const unsigned*)(smem + G::SCH) + sslot * G::SCHN;
     // rescale when the running max of a group of 8 heads (4 per k-half) moved: one
     // uniform branch per group, so only groups whose max moved pay for the multiplies
     v4f alq[4];
@@ -584,24 +673,54 @@ __global__ __launch_bounds__(kThreads) void attend_kernel(AttendArgs a, int S, i
       const v8h pa1 = *(const v8h*)(P + r32 * 40 + 16 * kh + 8);
       const uint8_t* tp = B + (16 * kh + i16) * G::RS4 + 8 * hh + 16 * b0;
       const unsigned* sp = sch + 16 * b0 + 8 * kh;
+      const uint8_t* nvp = B + G::E8 + 16 * kh * 4;
 #pragma unroll
       for (int i = 0; i < G::NBW; ++i) {
         if (i < G::BPW || wave < G::EXTRA) {
           const v2i raw = __builtin_amdgcn_ds_read_tr4_b64_v2i32(
               (__attribute__((address_space(3))) v2i*)(tp + 16 * i));
-          const v4u s0 = *(const v4u*)(sp + 16 * i);
-          const v4u s1 = *(const v4u*)(sp + 16 * i + 4);
-          const unsigned sc[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
-          unsigned wv[8];
+          if constexpr (NV) {
+            // the scales of 16-block 2 (b0 + i) + hh for rows 16 kh + 8 s + 0..7 (MFMA s):
+            // byte e = 2 ((b0 + i) & 1) + hh of 8 consecutive table dwords, paired by rows
+            // (v_perm) and converted exactly to fp16; one half at a time, since hoisting
+            // more scale reads would run out of registers
+            const int bb = b0 + i;
+            const uint8_t* tq = nvp + (bb >> 1) * (kRows * 4);
+            const unsigned e = 2 * (bb & 1) + hh;
+            const unsigned sel = 0x0C0C0000u | ((4u + e) << 8) | e;
 #pragma unroll
-          for (int kk = 0; kk < 8; ++kk) {
-            const v2h f = fp4x2_f16((unsigned)raw[kk >> 2], kk & 3) * __builtin_bit_cast(v2h, sc[kk]);
-            wv[kk] = __builtin_bit_cast(unsigned, f);
+            for (int hs = 0; hs < 2; ++hs) {
+              const v4u d0 = lds<v4u>(tq + 32 * hs), d1 = lds<v4u>(tq + 32 * hs + 16);
+              const unsigned d[8] = {d0.x, d0.y, d0.z, d0.w, d1.x, d1.y, d1.z, d1.w};
+              unsigned wv[4];
+#pragma unroll
+              for (int kk = 0; kk < 4; ++kk) {
+                const unsigned scp = __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(
+                                                                      __builtin_amdgcn_perm(d[2 * kk + 1], d[2 * kk], sel),
+                                                                      1.0f, false));
+                const v2h f = fp4x2_f16((unsigned)raw[hs], kk) * __builtin_bit_cast(v2h, scp);
+                wv[kk] = __builtin_bit_cast(unsigned, f);
+              }
+              o[i] = __builtin_amdgcn_mfma_f32_32x32x16_f16(hs ? pa1 : pa0,
+                                                           __builtin_bit_cast(v8h, v4u{wv[0], wv[1], wv[2], wv[3]}),
+                                                           o[i], 0, 0, 0);
+              __builtin_amdgcn_sched_barrier(0);
+            }
+          } else {
+            const v4u s0 = *(const v4u*)(sp + 16 * i);
+            const v4u s1 = *(const v4u*)(sp + 16 * i + 4);
+            const unsigned sc[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
+            unsigned wv[8];
+#pragma unroll
+            for (int kk = 0; kk < 8; ++kk) {
+              const v2h f = fp4x2_f16((unsigned)raw[kk >> 2], kk & 3) * __builtin_bit_cast(v2h, sc[kk]);
+              wv[kk] = __builtin_bit_cast(unsigned, f);
+            }
+            o[i] = __builtin_amdgcn_mfma_f32_32x32x16_f16(pa0, __builtin_bit_cast(v8h, v4u{wv[0], wv[1], wv[2], wv[3]}),
+                                                         o[i], 0, 0, 0);
+            o[i] = __builtin_amdgcn_mfma_f32_32x32x16_f16(pa1, __builtin_bit_cast(v8h, v4u{wv[4], wv[5], wv[6], wv[7]}),
+                                                         o[i], 0, 0, 0);
           }
-          o[i] = __builtin_amdgcn_mfma_f32_32x32x16_f16(pa0, __builtin_bit_cast(v8h, v4u{wv[0], wv[1], wv[2], wv[3]}),
-                                                       o[i], 0, 0, 0);
-          o[i] = __builtin_amdgcn_mfma_f32_32x32x16_f16(pa1, __builtin_bit_cast(v8h, v4u{wv[4], wv[5], wv[6], wv[7]}),
-                                                       o[i], 0, 0, 0);
         }
       }
     } else {
@@ -683,7 +802,7 @@ __global__ __launch_bounds__(kThreads) void attend_kernel(AttendArgs a, int S, i
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const float l = mlsum[8 * q4 + 4 * kh + e];
-      inv[4 * q4 + e] = (S == 1) ? (l > 0.0f ? 1.0f / l : 0.0f) : 1.0f;
+      inv[4 * q4 + e] = ((S == 1) ? (l > 0.0f ? 1.0f / l : 0.0f) : 1.0f) * (NV ? 1.0f / a.kv_pscale : 1.0f);
     }
   float* dst = (S == 1) ? a.out + ((int64_t)t * a.Hq + h0) * D
                         : (float*)a.ws + (((int64_t)split * a.T + t) * a.Hq + h0) * D;
@@ -714,20 +833,20 @@ __global__ __launch_bounds__(kThreads) void attend_kernel(AttendArgs a, int S, i
   }
 }
 
-template <int D, bool G8>
+template <int D, int F>
 hipError_t launch(const AttendArgs& a, int S, hipStream_t s) {
-  using G = Geo<D>;
+  using G = Geo<D, F>;
   const int ngroups = a.Hq / 32;
   const int total = a.T * ngroups * S;
   const int nb = (total + 7) / 8 * 8;
   static bool attr = false;
   if (!attr) {
-    hipError_t e = hipFuncSetAttribute((const void*)attend_kernel<D, G8>,
+    hipError_t e = hipFuncSetAttribute((const void*)attend_kernel<D, F>,
                                        hipFuncAttributeMaxDynamicSharedMemorySize, G::LDS);
     if (e != hipSuccess) return e;
     attr = true;
   }
-  hipLaunchKernelGGL((attend_kernel<D, G8>), dim3(nb), dim3(kThreads), G::LDS, s, a, S, ngroups, total);
+  hipLaunchKernelGGL((attend_kernel<D, F>), dim3(nb), dim3(kThreads), G::LDS, s, a, S, ngroups, total);
   hipError_t e = hipGetLastError();
   return e != hipSuccess ? e : launch_attend_merge(a, S, s);
 }
@@ -736,11 +855,15 @@ hipError_t launch(const AttendArgs& a, int S, hipStream_t s) {
 
 // Dimension-split attention for Hq % 32 == 0 and D <= 1664 (the register budget of 8
 // waves holding 32 heads of outputs and q, and four tile buffers in LDS), over the FP4
-// global cache or, with a.kv_fp8, the FP8 one; returns hipErrorInvalidValue otherwise.
+// global cache in the format a.kv_fmt (MX FP4, FP8 rows, NVFP4); returns
+// hipErrorInvalidValue otherwise.
 hipError_t launch_attend_sd(const AttendArgs& a, int S, hipStream_t s) {
   switch (a.D) {
-#define SMQA_SD_D(d) \
-  case d: return a.kv_fp8 ? sd::launch<d, true>(a, S, s) : sd::launch<d, false>(a, S, s);
+#define SMQA_SD_D(d)                                              \
+  case d:                                                         \
+    return a.kv_fmt == sd::kFP8  ? sd::launch<d, sd::kFP8>(a, S, s) \
+           : a.kv_fmt == sd::kNV ? sd::launch<d, sd::kNV>(a, S, s)  \
+                                 : sd::launch<d, sd::kMX>(a, S, s);
     SMQA_SD_D(128) SMQA_SD_D(256) SMQA_SD_D(384) SMQA_SD_D(512)
     SMQA_SD_D(640) SMQA_SD_D(768) SMQA_SD_D(896) SMQA_SD_D(1024)
     SMQA_SD_D(1152) SMQA_SD_D(1280) SMQA_SD_D(1408) SMQA_SD_D(1536)

@@ -121,12 +121,17 @@ struct AttendArgs {
   float* out;
   float* lse;
   void* ws;
-  int32_t kv_fp8;             // 1: kv_codes holds E4M3 rows [N][D] (kv_e8m0 unused)
+  // global cache format: 0 MX FP4 (kv_codes E2M1, kv_e8m0 E8M0 per 32); 1 FP8 (kv_codes E4M3
+  // rows [N][D], kv_e8m0 unused); 2 NVFP4 (kv_codes E2M1, kv_e8m0 E4M3 per 16, tensor scale
+  // kv_gscale)
+  int32_t kv_fmt;
+  float kv_gscale;
+  float kv_pscale;            // NVFP4: the power of two K with kv_gscale * K in [1, 2)
 };
 int attend_splits(int32_t T, int32_t k, int32_t W, int32_t Hq, int32_t D);
 size_t attend_workspace_bytes(int32_t T, int32_t k, int32_t W, int32_t Hq, int32_t D);
 hipError_t launch_attend(const AttendArgs& a, hipStream_t s);
-hipError_t launch_attend_fp8kv(const AttendArgs& a, hipStream_t s);
+hipError_t launch_attend_fmt(const AttendArgs& a, hipStream_t s);
 
 inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 

@@ -215,6 +215,39 @@ int sparse_mqa_attend_fp8kv(const smqa_layout* L,
                             void* stream);
 
 /*
+ * sparse_mqa_attend_nvfp4 — sparse_mqa_attend over a global cache in the
+ * NVFP4 layout (blog §Kernels, MegaAttention reading the NVFP4 KV; CocoLoop
+ * digest, section "Les particularités du modèle lui-même": the global KV is
+ * stored in NVFP4): E2M1 elements with one E4M3 scale per 16 elements and one
+ * fp32 scale per tensor.  The selected global rows are
+ *   V[j, d] = e2m1 * e4m3(S[j, d/16]) * rho_j * g,  j in idx[t] (j >= 0)
+ * and everything else (window, clip, softmax, outputs, workspace size from
+ * smqa_attend_workspace_size, errors) is as in sparse_mqa_attend.
+ * kv_codes        uint8 [N][D/2]   E2M1 pairs (element 2i in the low nibble), 16-byte aligned
+ * kv_scales       uint8 [N][D/16]  E4M3 block scales, 4-byte aligned
+ * kv_rowscale     float [N] or NULL  optional extra row scale rho (> 0; NULL = 1)
+ * kv_global_scale g, the tensor scale, in [1e-30, 1e30] (else SMQA_ERR_SHAPE);
+ *                 the window scales must satisfy sigma_u <= 32768 * g (P carries
+ *                 sigma times a power of two near 1/g in fp16)
+ * Limits: those of sparse_mqa_attend plus Hq % 32 == 0 and D <= 1664.
+ * Arithmetic as in sparse_mqa_attend except that q.row runs on fp16 MFMA:
+ * q is converted to fp16 once (exact for 2^-14 <= |q| <= 65504; |q| must
+ * stay below 65504), e2m1 * e4m3 is exact in fp16; rho * g multiplies the
+ * logits in fp32.
+ */
+int sparse_mqa_attend_nvfp4(const smqa_layout* L,
+                            const uint16_t* q_bf16,
+                            const uint8_t* kv_codes, const uint8_t* kv_scales,
+                            const float* kv_rowscale, float kv_global_scale,
+                            const int32_t* idx, int32_t k,
+                            const uint8_t* swa_fp8, const float* swa_scale,
+                            const int32_t* swa_pos0, const int32_t* swa_clip,
+                            int32_t W, int32_t Hq, int32_t D, float sm_scale,
+                            float* out, float* lse,
+                            void* workspace, size_t workspace_bytes,
+                            void* stream);
+
+/*
  * decode_step — sparse_mqa_score -> topk_select -> sparse_mqa_attend in one
  * call on one stream, with the scores and the selection kept in the
  * workspace (blog §Kernels: fusing the steps removes memory round trips and

@@ -208,6 +208,12 @@ def gpu_attend_fp8kv(smqa, wl, idx):
                                         wl.swa, wl.swa_scale, wl.swa_pos0, wl.swa_clip, wl.sm_scale)
 
 
+def gpu_attend_nvfp4(smqa, wl, idx):
+    return smqa.sparse_mqa_attend_nvfp4(gpu_batch(smqa, wl), wl.q, wl.kv_nv_codes, wl.kv_nv_scales,
+                                        wl.kv_rowscale, wl.kv_nv_global, idx, wl.swa, wl.swa_scale,
+                                        wl.swa_pos0, wl.swa_clip, wl.sm_scale)
+
+
 def gpu_decode(smqa, wl, k=None):
     return smqa.decode_step(gpu_batch(smqa, wl), wl.qI, wl.w, wl.kI, wl.kscale, wl.cand, wl.q,
                             wl.kv_codes, wl.kv_e8m0, wl.kv_rowscale, wl.swa, wl.swa_scale,

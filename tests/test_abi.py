@@ -28,6 +28,7 @@ def declared_functions():
 def test_header_declares_the_boundary():
     names = declared_functions()
     for n in ("sparse_mqa_score", "topk_select", "sparse_mqa_attend", "sparse_mqa_attend_fp8kv",
+              "sparse_mqa_attend_nvfp4",
               "decode_step",
               "smqa_topk_workspace_size", "smqa_attend_workspace_size",
               "smqa_decode_step_workspace_size", "smqa_last_error", "smqa_version"):
@@ -145,6 +146,29 @@ def test_attend_fp8kv_validation():
     assert attend8(L, k=5000) == -4 and attend8(L, W=0) == -4
     assert attend8(L) == -5                                  # split partials need the workspace
     assert attend8(layout(T=0)) == 0
+
+
+def attend_nv(L, **kw):
+    a = dict(q=A16, c=A16, s=A4, rs=None, g=1.0, idx=A4, k=2048, swa=A16, ss=None, p0=A4, clip=None,
+             W=128, Hq=64, D=1664, sc=0.0245, out=A16, lse=None, ws=None, nb=0)
+    a.update(kw)
+    return lib().sparse_mqa_attend_nvfp4(ctypes.byref(L), a["q"], a["c"], a["s"], a["rs"], a["g"],
+                                         a["idx"], a["k"], a["swa"], a["ss"], a["p0"], a["clip"],
+                                         a["W"], a["Hq"], a["D"], a["sc"], a["out"], a["lse"], a["ws"],
+                                         a["nb"], None)
+
+
+def test_attend_nvfp4_validation():
+    L = layout()
+    assert attend_nv(L, Hq=48) == -4 and "Hq" in err()
+    assert attend_nv(L, D=1792) == -4
+    assert attend_nv(L, s=None) == -1 and attend_nv(L, c=None) == -1
+    assert attend_nv(L, s=A4 + 2) == -3 and attend_nv(L, c=A16 + 4) == -3
+    assert attend_nv(L, g=0.0) == -2 and attend_nv(L, g=float("nan")) == -2
+    assert attend_nv(L, g=float("inf")) == -2 and attend_nv(L, g=-1.0) == -2
+    assert attend_nv(L, g=1e-31) == -2 and attend_nv(L, g=2e30) == -2
+    assert attend_nv(L) == -5
+    assert attend_nv(layout(T=0)) == 0
 
 
 def test_decode_step_workspace_covers_parts():

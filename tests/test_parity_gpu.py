@@ -14,7 +14,7 @@ import torch
 import synth
 from oracle import ref
 from helpers import (announce, close_attention, close_scores, gpu_attend, gpu_attend_fp8kv,
-                     gpu_decode, gpu_score,
+                     gpu_attend_nvfp4, gpu_decode, gpu_score,
                      gpu_topk, np_inputs, oracle_attend_for, oracle_scores_for, q_seq_of, topk_set_ok)
 
 pytestmark = pytest.mark.gpu
@@ -341,6 +341,59 @@ def test_attend_fp8kv_window_only_and_padding(lib):
     idx = ref.topk(S, wl.k)
     assert (idx == -1).any()
     _attend8_check(lib, wl, idx)
+
+
+# ------------------------------------------------------------------ attend over an NVFP4 cache
+
+def _attend_nv_check(lib, wl, idx_np=None):
+    a = np_inputs(wl)
+    if idx_np is None:
+        S = ref.score(a["qI"], a["w"], a["kI"], a["kscale"], a["seq_start"], a["q_start"], a["q_pos"])
+        idx_np = ref.topk(S, wl.k)
+    idx = torch.tensor(idx_np, dtype=torch.int32, device=DEV)
+    announce(f"attend_nvfp4 {wl.name} T={wl.T} Hq={wl.Hq} D={wl.D} k={wl.k}")
+    out, lse = gpu_attend_nvfp4(lib, wl, idx)
+    sync()
+    O, L = ref.attend_nvfp4(a["q"], a["kv_nv_codes"], a["kv_nv_scales"], a["kv_rowscale"],
+                            a["kv_nv_global"], idx_np, a["swa"], a["swa_scale"], a["swa_pos0"],
+                            a["swa_clip"], a["seq_start"], a["q_start"], a["q_pos"], a["W"],
+                            a["sm_scale"])
+    ok, msg = close_attention(out.cpu().numpy(), O, lse.cpu().numpy(), L)
+    assert ok, msg
+    return out, lse
+
+
+# MX-sized 32-row tiles with E4M3 block scales per 16: whole and partial tiles, one, an even
+# and an uneven block share per wave (D = 128 / 512 / 640: 1, 4 and 13 scale loads per tile),
+# the clipped replay window, with and without the extra row scale.
+@pytest.mark.parametrize("name,kw", [
+    ("decode_8k", dict(lengths=6000)),
+    ("decode_8k", dict(B=3, lengths=(300, 2000), k=1000, W=100, rowscale=False)),
+    ("decode_8k", dict(B=2, lengths=1500, Hq=32, D=128, k=256)),
+    ("decode_8k", dict(B=2, lengths=1500, Hq=64, D=512, k=256, rowscale=False)),
+    ("decode_8k", dict(B=2, lengths=(700, 1500), Hq=32, D=640, k=300)),
+    ("replay_h100k", dict(B=2, lengths=4000, replay=(4000, 128))),
+])
+def test_attend_nvfp4(lib, name, kw):
+    _attend_nv_check(lib, synth.with_scales(synth.with_nvfp4_kv(gen(name, **kw))))
+
+
+def test_attend_nvfp4_window_only_and_padding(lib):
+    """Every index -1 (window rows only; query 0 sees none), then a selection padded with -1
+    (the padded rows' dummy scales must not reach the output)."""
+    import dataclasses
+    wl = synth.with_nvfp4_kv(gen("replay_h100k", B=1, lengths=2000, replay=(2000, 4)))
+    clip = wl.swa_clip.clone()
+    clip[0] = wl.q_pos[0] + 1
+    wl = dataclasses.replace(wl, swa_clip=clip)
+    out, lse = _attend_nv_check(lib, wl, np.full((wl.T, wl.k), -1, dtype=np.int32))
+    assert torch.all(out[0] == 0) and torch.all(torch.isneginf(lse[0]))
+    wl = synth.with_nvfp4_kv(gen("decode_8k", B=2, lengths=(1500, 2500), k=2048), g=0.01)
+    a = np_inputs(wl)
+    S = ref.score(a["qI"], a["w"], a["kI"], a["kscale"], a["seq_start"], a["q_start"], a["q_pos"])
+    idx = ref.topk(S, wl.k)
+    assert (idx == -1).any()
+    _attend_nv_check(lib, wl, idx)
 
 
 # ------------------------------------------------------------------ decode step
