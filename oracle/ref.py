@@ -23,9 +23,9 @@ Readings where the pages are silent (each restated where it is used):
   R5  the window of query t is positions [max(p_t - W + 1, s_t, 0), p_t]
       that exist in the buffer; rows before the clip s_t are excluded
   R6  an empty row set gives O = 0 and LSE = -inf
-  R7  the FP8 global cache (the baseline format) is E4M3 rows with one fp32
+  R14 the FP8 global cache (the baseline format) is E4M3 rows with one fp32
       scale per row
-  R8  NVFP4 = E2M1 with one E4M3 scale per 16 elements and one fp32 tensor
+  R15 NVFP4 = E2M1 with one E4M3 scale per 16 elements and one fp32 tensor
       scale (the pages name the format only)
 """
 from __future__ import annotations
@@ -180,7 +180,7 @@ def attend_fp8kv(q, kv_fp8, kv_rowscale, idx, swa, swa_scale, swa_pos0, swa_clip
 
     CocoLoop digest §"Les particularités du modèle lui-même" and blog §Kernels:
     the NVFP4 global KV is about 45% smaller than the FP8 cache used before it.
-    Reading R7: that FP8 cache holds each latent row as D E4M3 bytes times one
+    Reading R14: that FP8 cache holds each latent row as D E4M3 bytes times one
     fp32 row scale rho_j (the window's format), V[j, d] = e4m3(byte) * rho_j;
     everything else is `attend`.  kv_fp8 uint8 [N, D], kv_rowscale float32 [N]
     or None (rho = 1).
@@ -200,7 +200,7 @@ def attend_nvfp4(q, kv_codes, kv_scales, kv_rowscale, kv_global_scale, idx, swa,
 
     Blog §Kernels and CocoLoop digest §"Les particularités du modèle lui-même" name the
     global KV format NVFP4: E2M1 elements, one E4M3 scale per 16 consecutive elements and
-    one fp32 scale g per tensor (reading R8), V[j, d] = e2m1 * e4m3(S[j, d // 16]) * rho_j * g
+    one fp32 scale g per tensor (reading R15), V[j, d] = e2m1 * e4m3(S[j, d // 16]) * rho_j * g
     with the optional fp32 row scale rho of the MX layout kept; everything else is `attend`.
     kv_codes uint8 [N, D/2], kv_scales uint8 [N, D/16], kv_rowscale float32 [N] or None.
     """
