@@ -27,6 +27,8 @@ What it computes (sources: the vLLM blog post "DeepSeek-V4.1-Flash sur vLLM :
 * ``ref.attend_nvfp4`` — the same attention over a global cache in the NVFP4
   layout the pages name (E2M1, an E4M3 scale per 16 elements, an fp32 tensor
   scale).
+* ``ref.attend_fused`` — MegaAttention's fused form (blog §Kernels): query
+  RoPE, the attention, inverse RoPE on the output and FP8 conversion.
 * ``ref.decode_step`` — the three in sequence.
 * ``brute`` — the same definitions as pure-Python loops for tiny inputs.
 

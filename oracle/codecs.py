@@ -78,6 +78,31 @@ def bf16(bits: np.ndarray) -> np.ndarray:
     return b.view(np.float32).astype(np.float64)
 
 
+def bf16_round(x: np.ndarray) -> np.ndarray:
+    """float values -> uint16 bfloat16 bits: to float32 (round to nearest even), then the top
+    16 bits rounded to nearest even (the two-step rounding an fp32 computation makes)."""
+    b = np.asarray(x, dtype=np.float64).astype(np.float32).view(np.uint32).astype(np.uint64)
+    r = (b + 0x7FFF + ((b >> 16) & 1)) >> 16
+    return r.astype(np.uint16)
+
+
+_E4M3_POS = np.array([_e4m3_value(c) for c in range(0x7F)], dtype=np.float64)   # 0x00..0x7E
+
+
+def e4m3_encode(x: np.ndarray) -> np.ndarray:
+    """float values -> OCP E4M3FN codes: the nearest finite value, ties to the even code (the
+    one whose mantissa ends in 0), magnitudes above 448 saturated to 448; the sign bit is
+    the input's (-0 and a negative value that rounds to zero give 0x80)."""
+    x = np.asarray(x, dtype=np.float64)
+    a = np.minimum(np.abs(x), 448.0)
+    hi = np.clip(np.searchsorted(_E4M3_POS, a, side="left"), 0, 0x7E)
+    lo = np.clip(hi - 1, 0, 0x7E)
+    dlo, dhi = a - _E4M3_POS[lo], _E4M3_POS[hi] - a
+    pick_hi = (dhi < dlo) | ((dhi == dlo) & (hi % 2 == 0))
+    code = np.where(pick_hi, hi, lo).astype(np.uint8)
+    return np.where(np.signbit(x), code | 0x80, code).astype(np.uint8)
+
+
 def global_rows(codes: np.ndarray, e8: np.ndarray, rowscale) -> np.ndarray:
     """Decode global-latent rows: V[j,d] = e2m1(nib(j,d)) * 2^(E[j, d//32]-127) * rho_j.
 

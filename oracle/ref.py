@@ -27,6 +27,11 @@ Readings where the pages are silent (each restated where it is used):
       scale per row
   R15 NVFP4 = E2M1 with one E4M3 scale per 16 elements and one fp32 tensor
       scale (the pages name the format only)
+  R16 fused RoPE: the last 2R latent dims rotate in consecutive pairs by
+      per-query angles the caller gives as cos / sin; the rotated query is
+      rounded to bf16 before the products
+  R17 FP8 output: per (query, head) row, scale = amax / 448, E4M3 codes of
+      x / scale rounded to nearest even, in float32
 """
 from __future__ import annotations
 
@@ -212,6 +217,59 @@ def attend_nvfp4(q, kv_codes, kv_scales, kv_rowscale, kv_global_scale, idx, swa,
                                  kv_global_scale)
     return _attend_union(q, global_of, idx, swa, swa_scale, swa_pos0, swa_clip, seq_start,
                          q_start, q_pos, W, sm_scale)
+
+
+def rope_rotate(x, rope_cos, rope_sin, inverse=False):
+    """Rotate the last 2 * R entries of x[t, h, :] in consecutive pairs (2i, 2i+1) by the
+    angle of query t (cos / sin float32 [T, R]; reading R16): forward
+    (a, b) -> (a c - b s, a s + b c), inverse by the opposite angle
+    (a, b) -> (a c + b s, -a s + b c).  float64 result."""
+    x = np.array(x, dtype=np.float64)
+    c = np.asarray(rope_cos, dtype=np.float64)[:, None, :]
+    s = np.asarray(rope_sin, dtype=np.float64)[:, None, :]
+    R = c.shape[-1]
+    if R == 0:
+        return x
+    D = x.shape[-1]
+    a = x[..., D - 2 * R::2].copy()
+    b = x[..., D - 2 * R + 1::2].copy()
+    if inverse:
+        s = -s
+    x[..., D - 2 * R::2] = a * c - b * s
+    x[..., D - 2 * R + 1::2] = a * s + b * c
+    return x
+
+
+def fp8_quantize(x):
+    """Per row (last axis) of float32 values: scale = amax / 448 and codes = E4M3(x / scale),
+    both divisions in float32 (reading R17); an all-zero row gives scale 0 and zero codes."""
+    x = np.asarray(x, dtype=np.float32)
+    amax = np.abs(x).max(axis=-1)
+    scale = (amax / np.float32(448.0)).astype(np.float32)
+    safe = np.where(scale > 0, scale, np.float32(1.0)).astype(np.float32)
+    y = (x / safe[..., None]).astype(np.float32)
+    codes = codecs.e4m3_encode(y)
+    codes = np.where((scale > 0)[..., None], codes, np.uint8(0)).astype(np.uint8)
+    return codes, scale
+
+
+def attend_fused(q, rope_cos, rope_sin, kv_codes, kv_e8m0, kv_rowscale, idx, swa, swa_scale,
+                 swa_pos0, swa_clip, seq_start, q_start, q_pos, W, sm_scale):
+    """MegaAttention's fused form (blog §Kernels, #56935): query RoPE, the sparse attention,
+    inverse RoPE on the output and FP8 conversion of the result for the output projection.
+
+    q is the unrotated bf16 query; its last 2R dims are rotated by query t's angles and the
+    result is rounded to bf16 (the attention's operand precision, reading R16); O is then
+    `attend`'s output, rotated back by the same angles (float64), and quantised per
+    (t, h) row by `fp8_quantize` of its float32 value.
+    Returns (O_rot float64 [T, Hq, D], LSE [T, Hq], codes uint8 [T, Hq, D], scale [T, Hq]).
+    """
+    qr = codecs.bf16_round(rope_rotate(codecs.bf16(q), rope_cos, rope_sin))
+    O, LSE = attend(qr, kv_codes, kv_e8m0, kv_rowscale, idx, swa, swa_scale, swa_pos0, swa_clip,
+                    seq_start, q_start, q_pos, W, sm_scale)
+    Oi = rope_rotate(O, rope_cos, rope_sin, inverse=True)
+    codes, scale = fp8_quantize(Oi.astype(np.float32))
+    return Oi, LSE, codes, scale
 
 
 def decode_step(wl_np: dict, k=None, cand=None):

@@ -147,3 +147,26 @@ def test_row_bytes_match_pages():
     assert synth.WORKLOADS["decode_8k"]["W"] == pc["window_positions"]["value"]
     H, nq = synth.WORKLOADS["replay_h100k"]["replay"]
     assert nq == pc["replay_clip_offset"]["value"]
+
+
+def test_e4m3_encoder_matches_torch_cast():
+    """The oracle's round-to-nearest-even E4M3 encoder against torch's float8_e4m3fn cast
+    (after clamping to +-448, which torch does not saturate), sign of zero included."""
+    rng = np.random.default_rng(7)
+    x = np.concatenate([rng.standard_normal(100_000) * s for s in (1e-3, 1.0, 30.0, 300.0)])
+    x = np.concatenate([x, [0.0, -0.0, 448.0, 460.0, 1e9, -1e9, 2.0 ** -10, -(2.0 ** -10),
+                            2.0 ** -9 * 1.5, 2.0 ** -11]]).astype(np.float32)
+    mine = codecs.e4m3_encode(x)
+    ref = torch.tensor(np.clip(x, -448, 448)).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(mine, ref)
+    # a tie between two codes goes to the even one: 1.0625 lies halfway between 1.0 (0x38)
+    # and 1.125 (0x39), 1.1875 between 1.125 and 1.25 (0x3A)
+    assert codecs.e4m3_encode(np.array([1.0625, 1.1875])).tolist() == [0x38, 0x3A]
+
+
+def test_bf16_round_matches_torch():
+    rng = np.random.default_rng(8)
+    x = rng.standard_normal(100_000) * 10.0 ** rng.integers(-5, 5, 100_000)
+    mine = codecs.bf16_round(x)
+    ref = torch.tensor(x.astype(np.float32)).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(mine, ref)

@@ -376,6 +376,109 @@ def test_nvfp4_tensor_scale_is_linear_in_the_rows():
     assert np.allclose(2 * O1, O2, rtol=1e-12, atol=1e-14)
 
 
+# ----------------------------------------------------------------- fused RoPE / FP8 epilogue
+
+def _angles(T, R, seed=0):
+    th = np.random.default_rng(seed).uniform(-np.pi, np.pi, (T, R))
+    return np.cos(th).astype(np.float32), np.sin(th).astype(np.float32)
+
+
+def test_rope_closed_forms():
+    rng = np.random.default_rng(1)
+    x = rng.standard_normal((2, 3, 16))
+    one, zero = np.ones((2, 4), np.float32), np.zeros((2, 4), np.float32)
+    assert np.array_equal(ref.rope_rotate(x, one, zero), x)             # angle 0
+    y = ref.rope_rotate(x, zero, one)                                    # 90 degrees
+    assert np.array_equal(y[..., :8], x[..., :8])                        # only the last 2R dims
+    assert np.array_equal(y[..., 8::2], -x[..., 9::2]) and np.array_equal(y[..., 9::2], x[..., 8::2])
+    c, s_ = _angles(2, 4)
+    z = ref.rope_rotate(x, c, s_)
+    back = ref.rope_rotate(z, c, s_, inverse=True)
+    # float32 cos / sin satisfy c^2 + s^2 = 1 only to ~1e-7: the inverse undoes the rotation
+    # up to that factor, and a rotation scales each pair's squared norm by exactly it
+    k = (c.astype(np.float64) ** 2 + s_.astype(np.float64) ** 2)[:, None, :]
+    assert np.allclose(back[..., :8], x[..., :8], rtol=0, atol=0)
+    assert np.allclose(back[..., 8::2], x[..., 8::2] * k, rtol=1e-13, atol=1e-15)
+    assert np.allclose(back[..., 9::2], x[..., 9::2] * k, rtol=1e-13, atol=1e-15)
+    n0 = x[..., 8::2] ** 2 + x[..., 9::2] ** 2
+    n1 = z[..., 8::2] ** 2 + z[..., 9::2] ** 2
+    assert np.allclose(n1, n0 * k, rtol=1e-13)
+
+
+def test_fp8_quantize_closed_forms():
+    rng = np.random.default_rng(2)
+    x = rng.standard_normal((3, 5, 64)).astype(np.float32)
+    x[1, 2] = 0.0
+    codes, scale = ref.fp8_quantize(x)
+    assert scale[1, 2] == 0 and not codes[1, 2].any()
+    am = np.abs(x).argmax(axis=-1)
+    for i in range(3):
+        for j in range(5):
+            if (i, j) != (1, 2):
+                assert codes[i, j, am[i, j]] & 0x7F == 0x7E                  # the amax maps to 448
+    deq = codecs.e4m3(codes) * scale[..., None]
+    # E4M3 keeps 3 mantissa bits: normal values within 2^-4 relative, subnormals within
+    # half their spacing 2^-9 * scale
+    assert np.all(np.abs(deq - x) <= np.maximum(np.abs(x) * 2.0 ** -4, 2.0 ** -10 * scale[..., None]) + 1e-30)
+
+
+def test_attend_fused_without_rope_is_attend_then_quantise():
+    wl = synth.with_scales(tiny(6, B=2, lengths=(30, 45)), seed=6)
+    a = np_inputs(wl)
+    S = ref.score(a["qI"], a["w"], a["kI"], a["kscale"], a["seq_start"], a["q_start"], a["q_pos"])
+    idx = ref.topk(S, a["k"])
+    O, L = _attend(a, idx)
+    z = np.zeros((a["T"], 0), np.float32)
+    Of, Lf, codes, scale = ref.attend_fused(a["q"], z, z, a["kv_codes"], a["kv_e8m0"], a["kv_rowscale"],
+                                            idx, a["swa"], a["swa_scale"], a["swa_pos0"], a["swa_clip"],
+                                            a["seq_start"], a["q_start"], a["q_pos"], a["W"], a["sm_scale"])
+    assert np.array_equal(Of, O) and np.array_equal(Lf, L)
+    c2, s2 = ref.fp8_quantize(O.astype(np.float32))
+    assert np.array_equal(codes, c2) and np.array_equal(scale, s2)
+
+
+def test_attend_fused_rope_only_touches_the_rope_dims():
+    """Rows whose last 2R dims are zero: the query's rotation cannot change any logit, so the
+    output equals plain attention, and its (zero) rotary part stays zero after the inverse."""
+    wl = synth.with_scales(tiny(7, B=2, lengths=(30, 45)), seed=7)
+    a = np_inputs(wl)
+    R, D = 8, a["D"]
+    a["kv_codes"] = a["kv_codes"].copy()
+    a["kv_codes"][:, (D - 2 * R) // 2:] = 0
+    a["swa"] = a["swa"].copy()
+    a["swa"][..., D - 2 * R:] = 0
+    S = ref.score(a["qI"], a["w"], a["kI"], a["kscale"], a["seq_start"], a["q_start"], a["q_pos"])
+    idx = ref.topk(S, a["k"])
+    O, L = _attend(a, idx)
+    c, s_ = _angles(a["T"], R, seed=3)
+    Of, Lf, _, _ = ref.attend_fused(a["q"], c, s_, a["kv_codes"], a["kv_e8m0"], a["kv_rowscale"], idx,
+                                    a["swa"], a["swa_scale"], a["swa_pos0"], a["swa_clip"],
+                                    a["seq_start"], a["q_start"], a["q_pos"], a["W"], a["sm_scale"])
+    assert np.array_equal(Of, O) and np.array_equal(Lf, L)
+    assert not Of[..., D - 2 * R:].any()
+
+
+def test_attend_fused_single_row_returns_the_unrotated_row():
+    """One selected row and no window row: O is that row, so the output is the row rotated
+    back by the query's angle (closed form), whatever q is."""
+    wl = tiny(8, lengths=40, W=8)
+    a = np_inputs(wl)
+    R, D = 4, a["D"]
+    idx = np.full((1, a["k"]), -1)
+    idx[0, 0] = 17
+    c, s_ = _angles(1, R, seed=4)
+    Of, _, _, _ = ref.attend_fused(a["q"], c, s_, a["kv_codes"], a["kv_e8m0"], a["kv_rowscale"], idx,
+                                   a["swa"], None, a["swa_pos0"], np.array([10_000], np.int32),
+                                   a["seq_start"], a["q_start"], a["q_pos"], a["W"], a["sm_scale"])
+    row = codecs.global_rows(a["kv_codes"][17:18], a["kv_e8m0"][17:18], a["kv_rowscale"][17:18])[0]
+    exp = row.copy()
+    cc, ss = c[0].astype(np.float64), s_[0].astype(np.float64)
+    e, o = row[D - 2 * R::2], row[D - 2 * R + 1::2]
+    exp[D - 2 * R::2] = e * cc + o * ss
+    exp[D - 2 * R + 1::2] = -e * ss + o * cc
+    assert np.allclose(Of[0], exp[None, :], rtol=1e-13, atol=1e-15)
+
+
 # ----------------------------------------------------------------- window clipping
 
 def _replay(H=50, nq=6, W=8, seed=13):
