@@ -57,6 +57,9 @@ _SIGS = {
                                      _P, _P, _P, _S, _P]),
     "sparse_mqa_attend_nvfp4": (_I, [_LP, _P, _P, _P, _P, _F, _P, _I, _P, _P, _P, _P, _I, _I, _I,
                                      _F, _P, _P, _P, _S, _P]),
+    "sparse_mqa_attend_fused": (_I, [_LP, _P, _P, _P, _I, _P, _P, _P, _P, _I, _P, _P, _P, _P, _I,
+                                     _I, _I, _F, _P, _P, _P, _P, _P, _S, _P]),
+    "smqa_attend_fused_workspace_size": (_S, [_LP, _I, _I, _I, _I]),
     "decode_step": (_I, [_LP, _P, _P, _P, _P, _P, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P, _P,
                          _I, _I, _I, _F, _I, _P, _P, _P, _P, _S, _P]),
     "smqa_topk_workspace_size": (_S, [_LP, _I, _I]),
@@ -290,6 +293,52 @@ def sparse_mqa_attend_nvfp4(L: Batch, q, kv_codes, kv_scales, kv_rowscale, kv_gl
                                        W, Hq, D, float(sm_scale), _ptr(out), _ptr(lse), wp, wb,
                                        _stream(stream)))
     return out, lse
+
+
+def sparse_mqa_attend_fused(L: Batch, q, rope_cos, rope_sin, kv_codes, kv_e8m0, kv_rowscale, idx,
+                            swa, swa_scale, swa_pos0, swa_clip, sm_scale: float, out_fp8=None,
+                            out_scale=None, out=None, lse=None, want_out=True, workspace=None,
+                            stream=None):
+    """Query RoPE -> attention -> inverse RoPE -> FP8 in one call.
+    -> (out_fp8 uint8 [T, Hq, D], out_scale float32 [T, Hq], out float32 or None, lse)."""
+    lib = load()
+    _dev(q, "q", torch.bfloat16, 3)
+    _dev(rope_cos, "rope_cos", torch.float32, 2)
+    _dev(rope_sin, "rope_sin", torch.float32, 2)
+    _dev(kv_codes, "kv_codes", torch.uint8, 2)
+    _dev(kv_e8m0, "kv_e8m0", torch.uint8, 2)
+    _dev(kv_rowscale, "kv_rowscale", torch.float32, 1)
+    _dev(idx, "idx", torch.int32, 2)
+    _dev(swa, "swa", _U8, 3)
+    _dev(swa_scale, "swa_scale", torch.float32, 2)
+    _dev(swa_pos0, "swa_pos0", torch.int32, 1)
+    _dev(swa_clip, "swa_clip", torch.int32, 1)
+    T, Hq, D = q.shape
+    W = swa.shape[1]
+    k = idx.shape[1]
+    R = 0 if rope_cos is None else rope_cos.shape[1]
+    if out_fp8 is None:
+        out_fp8 = torch.empty((T, Hq, D), dtype=torch.uint8, device=q.device)
+    if out_scale is None:
+        out_scale = torch.empty((T, Hq), dtype=torch.float32, device=q.device)
+    if out is None and want_out:
+        out = torch.empty((T, Hq, D), dtype=torch.float32, device=q.device)
+    if lse is None:
+        lse = torch.empty((T, Hq), dtype=torch.float32, device=q.device)
+    _dev(out_fp8, "out_fp8", torch.uint8, 3)
+    _dev(out_scale, "out_scale", torch.float32, 2)
+    _dev(out, "out", torch.float32, 3)
+    _dev(lse, "lse", torch.float32, 2)
+    need = lib.smqa_attend_fused_workspace_size(L.ref, k, W, Hq, D)
+    if workspace is None:
+        workspace = _workspace(need, q.device)
+    wp, wb = _ws_ptr(workspace)
+    _check(lib.sparse_mqa_attend_fused(L.ref, _ptr(q), _ptr(rope_cos), _ptr(rope_sin), R,
+                                       _ptr(kv_codes), _ptr(kv_e8m0), _ptr(kv_rowscale), _ptr(idx), k,
+                                       _ptr(swa), _ptr(swa_scale), _ptr(swa_pos0), _ptr(swa_clip), W,
+                                       Hq, D, float(sm_scale), _ptr(out_fp8), _ptr(out_scale),
+                                       _ptr(out), _ptr(lse), wp, wb, _stream(stream)))
+    return out_fp8, out_scale, out, lse
 
 
 def decode_step_workspace_size(L: Batch, k: int, n_cand: int, W: int, Hq: int, D: int) -> int:

@@ -174,6 +174,12 @@ size_t smqa_attend_workspace_size(const smqa_layout* L, int32_t k, int32_t W, in
   return smqa::attend_workspace_bytes(L->num_q, k, W, Hq, D);
 }
 
+size_t smqa_attend_fused_workspace_size(const smqa_layout* L, int32_t k, int32_t W, int32_t Hq,
+                                        int32_t D) {
+  if (check_layout(L) != SMQA_OK) return 0;
+  return smqa::attend_fused_workspace_bytes(L->num_q, k, W, Hq, D);
+}
+
 size_t smqa_decode_step_workspace_size(const smqa_layout* L, int32_t k, int32_t n_cand, int32_t W,
                                        int32_t Hq, int32_t D) {
   if (check_layout(L) != SMQA_OK) return 0;
@@ -289,6 +295,47 @@ int sparse_mqa_attend_nvfp4(const smqa_layout* L, const uint16_t* q_bf16, const 
                      sm_scale, out, lse, workspace, 2, kv_global_scale, K};
   hipError_t e = smqa::launch_attend_fmt(a, (hipStream_t)stream);
   return e == hipSuccess ? SMQA_OK : hip_fail(e, "sparse_mqa_attend_nvfp4 launch");
+}
+
+int sparse_mqa_attend_fused(const smqa_layout* L, const uint16_t* q_bf16, const float* rope_cos,
+                            const float* rope_sin, int32_t rope_pairs, const uint8_t* kv_codes,
+                            const uint8_t* kv_e8m0, const float* kv_rowscale, const int32_t* idx,
+                            int32_t k, const uint8_t* swa_fp8, const float* swa_scale,
+                            const int32_t* swa_pos0, const int32_t* swa_clip, int32_t W, int32_t Hq,
+                            int32_t D, float sm_scale, uint8_t* out_fp8, float* out_scale, float* out,
+                            float* lse, void* workspace, size_t workspace_bytes, void* stream) {
+  g_err.clear();
+  int st = check_layout(L);
+  if (st) return st;
+  if (L->num_q == 0) return SMQA_OK;
+  // out is optional here: out_fp8 stands in for it in the shared checks
+  st = check_attend(q_bf16, kv_codes, kv_e8m0, kv_rowscale, idx, k, swa_fp8, swa_scale, swa_pos0,
+                    swa_clip, W, Hq, D, sm_scale, out ? out : (const float*)out_fp8, lse, true);
+  if (st) return st;
+  REQUIRE_PTR(out_fp8);
+  REQUIRE_PTR(out_scale);
+  REQUIRE_ALIGN(out_fp8, 16);
+  REQUIRE_ALIGN(out_scale, 4);
+  if (Hq % 32 != 0 || D > 1664)
+    return fail(SMQA_ERR_UNSUPPORTED, "fused attention: Hq = %d, D = %d; supported Hq %% 32 == 0, D <= 1664",
+                Hq, D);
+  if (rope_pairs < 0 || rope_pairs % 4 != 0 || 2 * rope_pairs > D)
+    return fail(SMQA_ERR_UNSUPPORTED, "rope_pairs = %d: supported multiples of 4 with 2 * rope_pairs <= D",
+                rope_pairs);
+  if (rope_pairs > 0) {
+    REQUIRE_PTR(rope_cos);
+    REQUIRE_PTR(rope_sin);
+    REQUIRE_ALIGN(rope_cos, 16);
+    REQUIRE_ALIGN(rope_sin, 16);
+  }
+  st = check_ws(workspace, workspace_bytes, smqa::attend_fused_workspace_bytes(L->num_q, k, W, Hq, D));
+  if (st) return st;
+  smqa::AttendArgs a{L->seq_start, L->q_start, L->q_pos, L->num_seqs, L->num_q, q_bf16, kv_codes,
+                     kv_e8m0, kv_rowscale, idx, k, swa_fp8, swa_scale, swa_pos0, swa_clip, W, Hq, D,
+                     sm_scale, out, lse, workspace, 0, 1.0f, 1.0f, rope_pairs > 0 ? rope_cos : nullptr,
+                     rope_pairs > 0 ? rope_sin : nullptr, rope_pairs, 1, out_fp8, out_scale};
+  hipError_t e = smqa::launch_attend_fused(a, (hipStream_t)stream);
+  return e == hipSuccess ? SMQA_OK : hip_fail(e, "sparse_mqa_attend_fused launch");
 }
 
 int decode_step(const smqa_layout* L, const uint8_t* q_fp8, const float* w, const uint8_t* k_fp8,

@@ -1053,6 +1053,96 @@ __global__ __launch_bounds__(128) void attend_merge_kernel(AttendArgs a, int S) 
     a.lse[(int64_t)t * a.Hq + h] = L > 0.0f ? (sM + log2f(L)) * kLn2 : -__builtin_inff();
 }
 
+// MegaAttention's epilogue (blog §Kernels: inverse RoPE on the output and FP8 conversion,
+// written for the output projection): one workgroup per (query, head) merges the S split
+// partials by log-sum-exp (4 dims per thread), rotates the pairs of the last
+// 2 * rope_pairs dims back by the query's angle in fp32, takes the row's amax and writes
+// E4M3 codes of x / (amax / 448) (fp32 divisions, round to nearest even) with that scale.
+template <int SMAX>
+__global__ __launch_bounds__(512) void attend_fused_epilogue_kernel(AttendArgs a, int S) {
+  __shared__ float wts[64];
+  __shared__ float sL, sM;
+  __shared__ float wmax[8];
+  const int th = blockIdx.x;
+  const int t = th / a.Hq, h = th % a.Hq;
+  const int D = a.D;
+  const float* opart = (const float*)a.ws;
+  const float* ml = opart + (size_t)S * a.T * a.Hq * D;
+  const size_t sstride = (size_t)a.T * a.Hq * D;
+  const int d = 4 * threadIdx.x;
+  const bool act = d < D;
+  v4f v[SMAX];
+  {
+    const float* src = opart + ((int64_t)t * a.Hq + h) * D + (act ? d : 0);
+#pragma unroll
+    for (int s = 0; s < SMAX; ++s) v[s] = s < S ? *(const v4f*)(src + s * sstride) : v4f{0.0f, 0.0f, 0.0f, 0.0f};
+  }
+  if (threadIdx.x < 64) {
+    const int s = threadIdx.x;
+    float ms = -__builtin_inff(), ls = 0.0f;
+    if (s < S) {
+      const int64_t i = ((int64_t)s * a.T + t) * a.Hq + h;
+      ms = ml[2 * i];
+      ls = ml[2 * i + 1];
+    }
+    float M = ms;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) M = fmaxf(M, __shfl_xor(M, o));
+    const float wv = (M == -__builtin_inff() || ls == 0.0f) ? 0.0f : exp2f(ms - M);
+    float L = wv * ls;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) L += __shfl_xor(L, o);
+    wts[s] = wv;
+    if (s == 0) {
+      sL = L;
+      sM = M;
+    }
+  }
+  __syncthreads();
+  const float L = sL;
+  const float inv = L > 0.0f ? 1.0f / L : 0.0f;
+  v4f acc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+  for (int s = 0; s < SMAX; ++s)
+    if (s < S) acc += wts[s] * v[s];
+  acc *= inv;
+  const int r0 = D - 2 * a.rope_pairs;
+  if (act && a.rope_pairs > 0 && d >= r0) {
+    const int64_t pj = (int64_t)t * a.rope_pairs + (d - r0) / 2;
+    const float c0 = a.rope_cos[pj], s0 = a.rope_sin[pj], c1 = a.rope_cos[pj + 1], s1 = a.rope_sin[pj + 1];
+    const float x0 = acc[0], x1 = acc[1], x2 = acc[2], x3 = acc[3];
+    acc[0] = __builtin_fmaf(x0, c0, x1 * s0);
+    acc[1] = __builtin_fmaf(-x0, s0, x1 * c0);
+    acc[2] = __builtin_fmaf(x2, c1, x3 * s1);
+    acc[3] = __builtin_fmaf(-x2, s1, x3 * c1);
+  }
+  // the row's amax: lanes, then the 8 waves through LDS
+  float mx = act ? fmaxf(fmaxf(fabsf(acc[0]), fabsf(acc[1])), fmaxf(fabsf(acc[2]), fabsf(acc[3]))) : 0.0f;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
+  if ((threadIdx.x & 63) == 0) wmax[threadIdx.x >> 6] = mx;
+  __syncthreads();
+  float amax = wmax[0];
+#pragma unroll
+  for (int w = 1; w < 8; ++w) amax = fmaxf(amax, wmax[w]);
+  const float scale = amax / 448.0f;
+  const int64_t row = (int64_t)t * a.Hq + h;
+  if (act) {
+    unsigned codes = 0u;
+    if (scale > 0.0f) {
+      const float y0 = acc[0] / scale, y1 = acc[1] / scale, y2 = acc[2] / scale, y3 = acc[3] / scale;
+      codes = (unsigned)__builtin_amdgcn_cvt_pk_fp8_f32(y0, y1, 0, false);
+      codes = (unsigned)__builtin_amdgcn_cvt_pk_fp8_f32(y2, y3, (int)codes, true);
+    }
+    *(unsigned*)(a.out_fp8 + row * D + d) = codes;
+    if (a.out) *(v4f*)(a.out + row * D + d) = acc;
+  }
+  if (threadIdx.x == 0) {
+    a.out_scale[row] = scale;
+    if (a.lse) a.lse[row] = L > 0.0f ? (sM + log2f(L)) * kLn2 : -__builtin_inff();
+  }
+}
+
 static int max_tiles(int32_t k, int32_t W) {
   return (k + kGRows - 1) / kGRows + (W + kWRows - 1) / kWRows + 1;
 }
@@ -1151,6 +1241,29 @@ static hipError_t launch_thr(const AttendArgs& a, const AttPlan& p, hipStream_t 
 }
 
 hipError_t launch_attend_sd(const AttendArgs& a, int S, hipStream_t s);
+
+size_t attend_fused_workspace_bytes(int32_t T, int32_t k, int32_t W, int32_t Hq, int32_t D) {
+  const int S = attend_splits(T, k, W, Hq, D);
+  return (size_t)S * T * Hq * D * 4 + (size_t)S * T * Hq * 8;
+}
+
+// The fused form: the dimension-split kernel (MX cache, Hq % 32 == 0, D <= 1664, checked by
+// the caller) with the query RoPE and split partials always in the workspace (no plain
+// merge), then the epilogue kernel.
+hipError_t launch_attend_fused(const AttendArgs& a0, hipStream_t s) {
+  if (a0.T == 0) return hipSuccess;
+  const AttPlan p = attend_plan(a0.T, a0.k, a0.W, a0.Hq, a0.D);
+  if (!p.wide || a0.D > 1664 || a0.kv_fmt != 0 || !a0.out_fp8 || !a0.out_scale) return hipErrorInvalidValue;
+  AttendArgs a = a0;
+  a.partials = 1;
+  hipError_t e = launch_attend_sd(a, p.S, s);
+  if (e != hipSuccess) return e;
+  const dim3 grid(a.T * a.Hq);
+  if (p.S <= 16) hipLaunchKernelGGL(attend_fused_epilogue_kernel<16>, grid, dim3(512), 0, s, a, p.S);
+  else if (p.S <= 32) hipLaunchKernelGGL(attend_fused_epilogue_kernel<32>, grid, dim3(512), 0, s, a, p.S);
+  else hipLaunchKernelGGL(attend_fused_epilogue_kernel<64>, grid, dim3(512), 0, s, a, p.S);
+  return hipGetLastError();
+}
 
 // FP8 and NVFP4 global caches: only the dimension-split kernel reads them (Hq % 32 == 0,
 // D <= 1664, checked by the caller); the split count and workspace are those of the MX call.

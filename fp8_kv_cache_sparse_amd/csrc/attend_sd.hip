@@ -413,6 +413,27 @@ __global__ __launch_bounds__(kThreads) void attend_kernel(AttendArgs a, int S, i
       for (int cc = 0; cc < 2; ++cc) {
         v4u v = {0u, 0u, 0u, 0u};
         if (i < G::BPW || wave < G::EXTRA) v = *(const v4u*)(qrow + 32 * (b0 + i) + 8 * cc);
+        if constexpr (F == kMX) {
+          // fused query RoPE (blog §Kernels, MegaAttention): the pairs (2j, 2j+1) of the last
+          // 2 * rope_pairs dims rotate by query t's angle in fp32, then round to bf16 (RNE)
+          const int r0 = D - 2 * a.rope_pairs;
+          const int d0 = 32 * (b0 + i) + 16 * kh + 8 * cc;
+          if (a.rope_pairs > 0 && d0 >= r0 && (i < G::BPW || wave < G::EXTRA)) {
+            const int64_t pj = (int64_t)t * a.rope_pairs + (d0 - r0) / 2;
+            const v4f cs = *(const v4f*)(a.rope_cos + pj);
+            const v4f sn = *(const v4f*)(a.rope_sin + pj);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+              const float x0 = __uint_as_float(v[j] << 16), x1 = __uint_as_float(v[j] & 0xFFFF0000u);
+              const float y0 = __builtin_fmaf(x0, cs[j], -(x1 * sn[j]));
+              const float y1 = __builtin_fmaf(x0, sn[j], x1 * cs[j]);
+              const unsigned b0r = __float_as_uint(y0), b1r = __float_as_uint(y1);
+              const unsigned h0 = (b0r + 0x7FFFu + ((b0r >> 16) & 1u)) >> 16;
+              const unsigned h1 = (b1r + 0x7FFFu + ((b1r >> 16) & 1u)) >> 16;
+              v[j] = h0 | (h1 << 16);
+            }
+          }
+        }
         if constexpr (NV) {
           // NVFP4 scores in fp16: bf16 -> fp16 is exact for 2^-14 <= |q| <= 65504
           v8h h;
@@ -796,16 +817,18 @@ __global__ __launch_bounds__(kThreads) void attend_kernel(AttendArgs a, int S, i
     if (i16 == 0) mlsum[4 * wave + (lane >> 4)] = l;
   }
   __syncthreads();
+  // one split writes the normalised output itself, unless the fused epilogue takes partials
+  const bool direct = S == 1 && !a.partials;
   float inv[16];
 #pragma unroll
   for (int q4 = 0; q4 < 4; ++q4)
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const float l = mlsum[8 * q4 + 4 * kh + e];
-      inv[4 * q4 + e] = ((S == 1) ? (l > 0.0f ? 1.0f / l : 0.0f) : 1.0f) * (NV ? 1.0f / a.kv_pscale : 1.0f);
+      inv[4 * q4 + e] = (direct ? (l > 0.0f ? 1.0f / l : 0.0f) : 1.0f) * (NV ? 1.0f / a.kv_pscale : 1.0f);
     }
-  float* dst = (S == 1) ? a.out + ((int64_t)t * a.Hq + h0) * D
-                        : (float*)a.ws + (((int64_t)split * a.T + t) * a.Hq + h0) * D;
+  float* dst = direct ? a.out + ((int64_t)t * a.Hq + h0) * D
+                      : (float*)a.ws + (((int64_t)split * a.T + t) * a.Hq + h0) * D;
 #pragma unroll
   for (int i = 0; i < G::NBW; ++i) {
     if (i < G::BPW || wave < G::EXTRA) {
@@ -822,7 +845,7 @@ __global__ __launch_bounds__(kThreads) void attend_kernel(AttendArgs a, int S, i
   if (tid < 32) {
     const int hg = h0 + tid;
     const float m = mref[tid], l = mlsum[tid];
-    if (S == 1) {
+    if (direct) {
       if (a.lse) a.lse[(int64_t)t * a.Hq + hg] = l > 0.0f ? (m + log2f(l)) * kLn2 : -__builtin_inff();
     } else {
       float* ml = (float*)a.ws + (size_t)S * a.T * a.Hq * D;
@@ -848,7 +871,8 @@ hipError_t launch(const AttendArgs& a, int S, hipStream_t s) {
   }
   hipLaunchKernelGGL((attend_kernel<D, F>), dim3(nb), dim3(kThreads), G::LDS, s, a, S, ngroups, total);
   hipError_t e = hipGetLastError();
-  return e != hipSuccess ? e : launch_attend_merge(a, S, s);
+  // the fused form (a.partials) merges in its own epilogue kernel
+  return e != hipSuccess ? e : (a.partials ? hipSuccess : launch_attend_merge(a, S, s));
 }
 
 }  // namespace sd

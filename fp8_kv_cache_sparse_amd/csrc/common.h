@@ -127,11 +127,22 @@ struct AttendArgs {
   int32_t kv_fmt;
   float kv_gscale;
   float kv_pscale;            // NVFP4: the power of two K with kv_gscale * K in [1, 2)
+  // fused epilogue (MX format only): the last 2 * rope_pairs latent dims of q are rotated by
+  // (rope_cos, rope_sin)[t] before the products; partials = 1 writes split partials even
+  // for one split; out_fp8 / out_scale receive the quantised, inversely rotated output
+  const float* rope_cos;
+  const float* rope_sin;
+  int32_t rope_pairs;
+  int32_t partials;
+  uint8_t* out_fp8;
+  float* out_scale;
 };
 int attend_splits(int32_t T, int32_t k, int32_t W, int32_t Hq, int32_t D);
 size_t attend_workspace_bytes(int32_t T, int32_t k, int32_t W, int32_t Hq, int32_t D);
 hipError_t launch_attend(const AttendArgs& a, hipStream_t s);
 hipError_t launch_attend_fmt(const AttendArgs& a, hipStream_t s);
+size_t attend_fused_workspace_bytes(int32_t T, int32_t k, int32_t W, int32_t Hq, int32_t D);
+hipError_t launch_attend_fused(const AttendArgs& a, hipStream_t s);
 
 inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 

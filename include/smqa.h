@@ -248,6 +248,45 @@ int sparse_mqa_attend_nvfp4(const smqa_layout* L,
                             void* stream);
 
 /*
+ * sparse_mqa_attend_fused — MegaAttention's fused form (blog §Kernels,
+ * "MegaAttention avec KV compressé NVFP4": query RoPE, the sparse attention,
+ * inverse RoPE on the output and FP8 conversion in one pass, written for the
+ * output projection) over the FP4 (MX) cache of sparse_mqa_attend:
+ *   q'      = q with the pairs (2i, 2i+1) of its last 2R dims (R = rope_pairs)
+ *             rotated by query t's angle: (a, b) -> (a c - b s, a s + b c),
+ *             c = rope_cos[t][i], s = rope_sin[t][i]; computed in fp32 and
+ *             rounded to bf16 (nearest even) for the products
+ *   O       = sparse_mqa_attend(q', ...)
+ *   O'      = O with the same pairs rotated back: (a, b) -> (a c + b s, -a s + b c)
+ *   out_scale[t,h] = max_d |O'[t,h,d]| / 448,
+ *   out_fp8[t,h,d] = E4M3(O'[t,h,d] / out_scale[t,h]) (fp32 divisions, nearest
+ *             even; an all-zero row gives scale 0 and zero codes)
+ * so out_fp8 * out_scale approximates O' within E4M3's 2^-4 relative step.
+ * rope_cos, rope_sin float [T][R], 16-byte aligned (may be NULL when R = 0);
+ *             the angles of each query's position (frequencies, scaling and the
+ *             position itself are the caller's)
+ * rope_pairs  R: a multiple of 4 with 2R <= D (0 = no rotation)
+ * out_fp8     uint8 [T][Hq][D], 16-byte aligned;  out_scale float [T][Hq]
+ * out         float [T][Hq][D] or NULL: O' in fp32 (optional)
+ * lse         float [T][Hq] or NULL (of the rotated query's logits)
+ * workspace:  smqa_attend_fused_workspace_size() bytes (never 0: the split
+ *             partials always go through it).
+ * Limits: those of sparse_mqa_attend plus Hq % 32 == 0 and D <= 1664; other
+ * arguments as in sparse_mqa_attend.
+ */
+int sparse_mqa_attend_fused(const smqa_layout* L,
+                            const uint16_t* q_bf16,
+                            const float* rope_cos, const float* rope_sin, int32_t rope_pairs,
+                            const uint8_t* kv_codes, const uint8_t* kv_e8m0, const float* kv_rowscale,
+                            const int32_t* idx, int32_t k,
+                            const uint8_t* swa_fp8, const float* swa_scale,
+                            const int32_t* swa_pos0, const int32_t* swa_clip,
+                            int32_t W, int32_t Hq, int32_t D, float sm_scale,
+                            uint8_t* out_fp8, float* out_scale, float* out, float* lse,
+                            void* workspace, size_t workspace_bytes,
+                            void* stream);
+
+/*
  * decode_step — sparse_mqa_score -> topk_select -> sparse_mqa_attend in one
  * call on one stream, with the scores and the selection kept in the
  * workspace (blog §Kernels: fusing the steps removes memory round trips and
@@ -276,6 +315,8 @@ int decode_step(const smqa_layout* L,
 size_t smqa_topk_workspace_size(const smqa_layout* L, int32_t k, int32_t n_cand);
 size_t smqa_attend_workspace_size(const smqa_layout* L, int32_t k, int32_t W,
                                   int32_t Hq, int32_t D);
+size_t smqa_attend_fused_workspace_size(const smqa_layout* L, int32_t k, int32_t W,
+                                        int32_t Hq, int32_t D);
 size_t smqa_decode_step_workspace_size(const smqa_layout* L, int32_t k, int32_t n_cand,
                                        int32_t W, int32_t Hq, int32_t D);
 

@@ -214,6 +214,12 @@ def gpu_attend_nvfp4(smqa, wl, idx):
                                         wl.swa_pos0, wl.swa_clip, wl.sm_scale)
 
 
+def gpu_attend_fused(smqa, wl, idx, rope_cos, rope_sin, want_out=True):
+    return smqa.sparse_mqa_attend_fused(gpu_batch(smqa, wl), wl.q, rope_cos, rope_sin, wl.kv_codes,
+                                        wl.kv_e8m0, wl.kv_rowscale, idx, wl.swa, wl.swa_scale,
+                                        wl.swa_pos0, wl.swa_clip, wl.sm_scale, want_out=want_out)
+
+
 def gpu_decode(smqa, wl, k=None):
     return smqa.decode_step(gpu_batch(smqa, wl), wl.qI, wl.w, wl.kI, wl.kscale, wl.cand, wl.q,
                             wl.kv_codes, wl.kv_e8m0, wl.kv_rowscale, wl.swa, wl.swa_scale,

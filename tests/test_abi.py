@@ -28,7 +28,7 @@ def declared_functions():
 def test_header_declares_the_boundary():
     names = declared_functions()
     for n in ("sparse_mqa_score", "topk_select", "sparse_mqa_attend", "sparse_mqa_attend_fp8kv",
-              "sparse_mqa_attend_nvfp4",
+              "sparse_mqa_attend_nvfp4", "sparse_mqa_attend_fused", "smqa_attend_fused_workspace_size",
               "decode_step",
               "smqa_topk_workspace_size", "smqa_attend_workspace_size",
               "smqa_decode_step_workspace_size", "smqa_last_error", "smqa_version"):
@@ -169,6 +169,35 @@ def test_attend_nvfp4_validation():
     assert attend_nv(L, g=1e-31) == -2 and attend_nv(L, g=2e30) == -2
     assert attend_nv(L) == -5
     assert attend_nv(layout(T=0)) == 0
+
+
+def attend_fused(L, **kw):
+    a = dict(q=A16, rc=A16, rs_=A16, R=32, c=A16, e=A4, rs=None, idx=A4, k=2048, swa=A16, ss=None,
+             p0=A4, clip=None, W=128, Hq=64, D=1664, sc=0.0245, o8=A16, osc=A4, out=None, lse=None,
+             ws=None, nb=0)
+    a.update(kw)
+    return lib().sparse_mqa_attend_fused(ctypes.byref(L), a["q"], a["rc"], a["rs_"], a["R"], a["c"],
+                                         a["e"], a["rs"], a["idx"], a["k"], a["swa"], a["ss"], a["p0"],
+                                         a["clip"], a["W"], a["Hq"], a["D"], a["sc"], a["o8"], a["osc"],
+                                         a["out"], a["lse"], a["ws"], a["nb"], None)
+
+
+def test_attend_fused_validation():
+    L = layout()
+    assert attend_fused(L, R=6) == -4 and "rope_pairs" in err()
+    assert attend_fused(L, R=836) == -4 and attend_fused(L, R=-4) == -4
+    assert attend_fused(L, rc=None) == -1 and attend_fused(L, rs_=None) == -1
+    assert attend_fused(L, R=0, rc=None, rs_=None) == -5          # no rotation: tables optional
+    assert attend_fused(L, rc=A16 + 4) == -3
+    assert attend_fused(L, o8=None) == -1 and attend_fused(L, osc=None) == -1
+    assert attend_fused(L, o8=A16 + 4) == -3 and attend_fused(L, out=A16 + 4) == -3
+    assert attend_fused(L, Hq=48) == -4 and attend_fused(L, D=1792) == -4
+    need = lib().smqa_attend_fused_workspace_size(ctypes.byref(L), 2048, 128, 64, 1664)
+    assert need > 0
+    assert attend_fused(L) == -5
+    # one query per 32-head group pair still needs the partials: never 0
+    assert lib().smqa_attend_fused_workspace_size(ctypes.byref(layout(T=64, B=64)), 64, 16, 64, 128) > 0
+    assert attend_fused(layout(T=0)) == 0
 
 
 def test_decode_step_workspace_covers_parts():

@@ -405,6 +405,25 @@ def test_rope_closed_forms():
     assert np.allclose(n1, n0 * k, rtol=1e-13)
 
 
+def test_rope_query_bf16_agrees_with_the_float64_rotation():
+    """The float32 rotation rounded to bf16 is the float64 rotation rounded to bf16 except
+    where the float64 value lies within a few float32 ulps of a bf16 rounding midpoint;
+    with angle 0 it is the query itself, and with 90 degrees the exact swap."""
+    wl = tiny(9, lengths=40)
+    a = np_inputs(wl)
+    c, s_ = _angles(a["T"], 8, seed=9)
+    got = ref.rope_query_bf16(a["q"], c, s_)
+    exact = codecs.bf16_round(ref.rope_rotate(codecs.bf16(a["q"]), c, s_))
+    assert (got != exact).mean() < 1e-3
+    assert np.all(np.abs(codecs.bf16(got) - codecs.bf16(exact)) <= 2.0 ** -7 * np.abs(codecs.bf16(exact)))
+    one, zero = np.ones_like(c), np.zeros_like(s_)
+    assert np.array_equal(ref.rope_query_bf16(a["q"], one, zero), a["q"])
+    sw = ref.rope_query_bf16(a["q"], zero, one)
+    D = a["D"]
+    assert np.array_equal(codecs.bf16(sw[..., D - 16::2]), -codecs.bf16(a["q"][..., D - 15::2]))
+    assert np.array_equal(sw[..., D - 15::2], a["q"][..., D - 16::2])
+
+
 def test_fp8_quantize_closed_forms():
     rng = np.random.default_rng(2)
     x = rng.standard_normal((3, 5, 64)).astype(np.float32)

@@ -14,7 +14,7 @@ import torch
 import synth
 from oracle import ref
 from helpers import (announce, close_attention, close_scores, gpu_attend, gpu_attend_fp8kv,
-                     gpu_attend_nvfp4, gpu_decode, gpu_score,
+                     gpu_attend_fused, gpu_attend_nvfp4, gpu_decode, gpu_score,
                      gpu_topk, np_inputs, oracle_attend_for, oracle_scores_for, q_seq_of, topk_set_ok)
 
 pytestmark = pytest.mark.gpu
@@ -394,6 +394,50 @@ def test_attend_nvfp4_window_only_and_padding(lib):
     idx = ref.topk(S, wl.k)
     assert (idx == -1).any()
     _attend_nv_check(lib, wl, idx)
+
+
+# ------------------------------------------------------------------ fused RoPE / FP8 epilogue
+
+def _angles(T, R, seed):
+    g = torch.Generator().manual_seed(seed)
+    th = (torch.rand((T, R), generator=g, dtype=torch.float64) * 2 - 1) * 3.14159
+    return th.cos().float().to(DEV), th.sin().float().to(DEV)
+
+
+# The rotary part of DeepSeek-style latents (64 dims) and a short one, on whole and partial
+# tiles, one and several splits, the clipped replay window; the FP8 codes and scales must
+# equal the oracle's quantiser applied to the GPU's own fp32 output, bit for bit.
+@pytest.mark.parametrize("name,kw,R", [
+    ("decode_8k", dict(lengths=6000), 32),
+    ("decode_8k", dict(B=3, lengths=(300, 2000), k=1000, W=100), 32),
+    ("decode_8k", dict(B=2, lengths=1500, Hq=32, D=128, k=256), 4),
+    ("decode_8k", dict(B=2, lengths=(700, 1500), Hq=32, D=640, k=300), 0),
+    ("replay_h100k", dict(B=2, lengths=4000, replay=(4000, 128)), 32),
+])
+def test_attend_fused(lib, name, kw, R):
+    wl = synth.with_scales(gen(name, **kw))
+    a = np_inputs(wl)
+    S = ref.score(a["qI"], a["w"], a["kI"], a["kscale"], a["seq_start"], a["q_start"], a["q_pos"])
+    idx_np = ref.topk(S, wl.k)
+    idx = torch.tensor(idx_np, dtype=torch.int32, device=DEV)
+    c, s_ = _angles(wl.T, R, seed=R + wl.T)
+    announce(f"attend_fused {wl.name} T={wl.T} Hq={wl.Hq} D={wl.D} k={wl.k} R={R}")
+    o8, osc, out, lse = gpu_attend_fused(lib, wl, idx, c if R else None, s_ if R else None)
+    sync()
+    Oi, L, _, _ = ref.attend_fused(a["q"], c.cpu().numpy(), s_.cpu().numpy(), a["kv_codes"], a["kv_e8m0"],
+                                   a["kv_rowscale"], idx_np, a["swa"], a["swa_scale"], a["swa_pos0"],
+                                   a["swa_clip"], a["seq_start"], a["q_start"], a["q_pos"], a["W"],
+                                   a["sm_scale"])
+    ok, msg = close_attention(out.cpu().numpy(), Oi, lse.cpu().numpy(), L)
+    assert ok, msg
+    codes, scale = ref.fp8_quantize(out.cpu().numpy())
+    assert np.array_equal(osc.cpu().numpy(), scale)
+    bad = np.nonzero(o8.cpu().numpy() != codes)
+    assert bad[0].size == 0, f"{bad[0].size} codes differ, e.g. {o8.cpu().numpy()[bad][:4]} vs {codes[bad][:4]}"
+    # without the fp32 output the codes are the same
+    o8b, oscb, outb, _ = gpu_attend_fused(lib, wl, idx, c if R else None, s_ if R else None, want_out=False)
+    sync()
+    assert outb is None and torch.equal(o8b, o8) and torch.equal(oscb, osc)
 
 
 # ------------------------------------------------------------------ decode step
