@@ -340,6 +340,25 @@ def measure(name, steps, warmup, use_graph, stage_only="", fp8_baseline=True):
                                          wl.swa_clip, wl.sm_scale, out=out2, lse=lse2, workspace=ws)
         usn = timed_us(st_attend_nv)
         del wln
+        # MegaAttention's fused form on the MX cache: query RoPE (64 rotary dims), the same
+        # attention, inverse RoPE and per-row FP8 output in one call
+        fused_us = None
+        if wl.D >= 64:
+            R = 32
+            th = torch.arange(wl.T * R, device=dev, dtype=torch.float32).view(wl.T, R) * 0.001
+            rc, rsn = th.cos().contiguous(), th.sin().contiguous()
+            o8 = torch.empty((wl.T, wl.Hq, wl.D), dtype=torch.uint8, device=dev)
+            osc = torch.empty((wl.T, wl.Hq), dtype=torch.float32, device=dev)
+            wsf = torch.empty(smqa.load().smqa_attend_fused_workspace_size(L.ref, wl.k, wl.W, wl.Hq, wl.D)
+                              + 256, dtype=torch.uint8, device=dev)
+            print(f"[bench] {name}: fused RoPE/FP8 attention x{steps}", file=sys.stderr, flush=True)
+
+            def st_fused():
+                smqa.sparse_mqa_attend_fused(L, wl.q, rc, rsn, wl.kv_codes, wl.kv_e8m0, wl.kv_rowscale,
+                                             idx2, wl.swa, wl.swa_scale, wl.swa_pos0, wl.swa_clip,
+                                             wl.sm_scale, out_fp8=o8, out_scale=osc, want_out=False,
+                                             lse=lse2, workspace=wsf)
+            fused_us = round(timed_us(st_fused), 2)
         rs = 4 if wl.kv_rowscale is not None else 0
         fp8kv = {"attend_us": {"mx_fp4": round(st_us["attend"], 2), "nvfp4": round(usn, 2),
                                "fp8": round(us8, 2)},
@@ -348,7 +367,10 @@ def measure(name, steps, warmup, use_graph, stage_only="", fp8_baseline=True):
                  "global_row_bytes": {"mx_fp4": wl.D // 2 + wl.D // 32 + rs,
                                       "nvfp4": wl.D // 2 + wl.D // 16 + rs, "fp8": wl.D + 4},
                  "kernel": "attend: sd::attend_kernel<D, F> (F = MX FP4 / NVFP4 / FP8 rows in "
-                           "16-row tiles) + attend_merge_kernel"}
+                           "16-row tiles) + attend_merge_kernel",
+                 "fused_rope_fp8_us": fused_us,
+                 "fused_kernel": "sd::attend_kernel<D, MX> with query RoPE + attend_fused_epilogue_kernel "
+                                 "(inverse RoPE, E4M3 output)"}
     dom = max(st_us, key=st_us.get)
     best_s = min(x for x in (eager_s, graph_s, chain_s) if x)
     res = {

@@ -1057,7 +1057,7 @@ __global__ __launch_bounds__(128) void attend_merge_kernel(AttendArgs a, int S) 
 // written for the output projection): one workgroup per (query, head) merges the S split
 // partials by log-sum-exp (4 dims per thread), rotates the pairs of the last
 // 2 * rope_pairs dims back by the query's angle in fp32, takes the row's amax and writes
-// E4M3 codes of x / (amax / 448) (fp32 divisions, round to nearest even) with that scale.
+// E4M3 codes of x * (448 / amax) (fp32, round to nearest even) with the scale amax / 448.
 template <int SMAX>
 __global__ __launch_bounds__(512) void attend_fused_epilogue_kernel(AttendArgs a, int S) {
   __shared__ float wts[64];
@@ -1126,11 +1126,12 @@ __global__ __launch_bounds__(512) void attend_fused_epilogue_kernel(AttendArgs a
 #pragma unroll
   for (int w = 1; w < 8; ++w) amax = fmaxf(amax, wmax[w]);
   const float scale = amax / 448.0f;
+  const float rq = amax > 0.0f ? 448.0f / amax : 0.0f;
   const int64_t row = (int64_t)t * a.Hq + h;
   if (act) {
     unsigned codes = 0u;
-    if (scale > 0.0f) {
-      const float y0 = acc[0] / scale, y1 = acc[1] / scale, y2 = acc[2] / scale, y3 = acc[3] / scale;
+    if (amax > 0.0f) {
+      const float y0 = acc[0] * rq, y1 = acc[1] * rq, y2 = acc[2] * rq, y3 = acc[3] * rq;
       codes = (unsigned)__builtin_amdgcn_cvt_pk_fp8_f32(y0, y1, 0, false);
       codes = (unsigned)__builtin_amdgcn_cvt_pk_fp8_f32(y2, y3, (int)codes, true);
     }
@@ -1248,16 +1249,19 @@ size_t attend_fused_workspace_bytes(int32_t T, int32_t k, int32_t W, int32_t Hq,
 }
 
 // The fused form: the dimension-split kernel (MX cache, Hq % 32 == 0, D <= 1664, checked by
-// the caller) with the query RoPE and split partials always in the workspace (no plain
-// merge), then the epilogue kernel.
+// the caller) with the query RoPE; with one split its epilogue writes the FP8 output, with
+// several the partials go to the workspace (no plain merge) and the epilogue kernel runs.
 hipError_t launch_attend_fused(const AttendArgs& a0, hipStream_t s) {
   if (a0.T == 0) return hipSuccess;
   const AttPlan p = attend_plan(a0.T, a0.k, a0.W, a0.Hq, a0.D);
   if (!p.wide || a0.D > 1664 || a0.kv_fmt != 0 || !a0.out_fp8 || !a0.out_scale) return hipErrorInvalidValue;
   AttendArgs a = a0;
-  a.partials = 1;
+  // one split: the attention kernel's own epilogue rotates back and quantises; several:
+  // partials, then the epilogue kernel
+  a.kv_fmt = p.S > 1 ? 4 : 3;                    // the fused instantiations of the MX kernel
+  a.partials = p.S > 1 ? 1 : 0;
   hipError_t e = launch_attend_sd(a, p.S, s);
-  if (e != hipSuccess) return e;
+  if (e != hipSuccess || p.S == 1) return e;
   const dim3 grid(a.T * a.Hq);
   if (p.S <= 16) hipLaunchKernelGGL(attend_fused_epilogue_kernel<16>, grid, dim3(512), 0, s, a, p.S);
   else if (p.S <= 32) hipLaunchKernelGGL(attend_fused_epilogue_kernel<32>, grid, dim3(512), 0, s, a, p.S);

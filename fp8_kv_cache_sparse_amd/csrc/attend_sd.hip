@@ -65,7 +65,12 @@ constexpr int align16(int x) { return (x + 15) & ~15; }
 
 // Global cache formats: MX FP4 (E2M1, E8M0 per 32, fp32 row scale), FP8 rows (E4M3, row
 // scale) and NVFP4 (E2M1, E4M3 per 16, row scale, fp32 tensor scale).
-constexpr int kMX = 0, kFP8 = 1, kNV = 2;
+// MegaAttention's fused form over the MX format has two instantiations of its own (so the
+// plain kernel keeps its registers and neither ends in a branch between two epilogues):
+// kMXF, query RoPE and the FP8 epilogue in the kernel (one split), and kMXR, query RoPE
+// with split partials for attend_fused_epilogue_kernel.
+constexpr int kMX = 0, kFP8 = 1, kNV = 2, kMXF = 3, kMXR = 4;
+constexpr bool mx_like(int F) { return F == kMX || F == kMXF || F == kMXR; }
 
 // LDS geometry for latent width D and global format F (compile time, so every offset is an
 // immediate).
@@ -88,7 +93,7 @@ struct Geo {
   static constexpr int BUF = align16(RHO + kRows * 4);
   // shared areas after the buffers
   static constexpr int RING = kNBuf * BUF;                      // positions [4][32]
-  static constexpr int SCHN = F == kMX ? NB * 16 : 16;          // u32 per slot: MX f16 scale pairs
+  static constexpr int SCHN = mx_like(F) ? NB * 16 : 16;       // u32 per slot: MX f16 scale pairs
   static constexpr int SCH = RING + kNBuf * kRows * 4;          // [2][SCHN]: scale pairs / row masks
   static constexpr int RED = SCH + 2 * SCHN * 4;                // [8 waves][32 heads][32 rows] f32
   static constexpr int PS = RED + 8 * 32 * kRows * 4;           // P [32 heads][40] f16
@@ -103,6 +108,7 @@ struct Geo {
   static_assert(kWRows * RS8 <= CODES, "a window tile must fit a buffer");
   static_assert(EXTRA == 0 || EXTRA == 4, "D must be a multiple of 128");
   static_assert(LDS <= 160 * 1024, "LDS budget");
+  static_assert(32 * D <= kNBuf * BUF, "the fused epilogue stages 32 rows of FP8 codes in the tile buffers");
 };
 
 struct Ctx {
@@ -413,7 +419,7 @@ __global__ __launch_bounds__(kThreads) void attend_kernel(AttendArgs a, int S, i
       for (int cc = 0; cc < 2; ++cc) {
         v4u v = {0u, 0u, 0u, 0u};
         if (i < G::BPW || wave < G::EXTRA) v = *(const v4u*)(qrow + 32 * (b0 + i) + 8 * cc);
-        if constexpr (F == kMX) {
+        if constexpr (F == kMXF || F == kMXR) {
           // fused query RoPE (blog §Kernels, MegaAttention): the pairs (2j, 2j+1) of the last
           // 2 * rope_pairs dims rotate by query t's angle in fp32, then round to bf16 (RNE)
           const int r0 = D - 2 * a.rope_pairs;
@@ -818,7 +824,7 @@ __global__ __launch_bounds__(kThreads) void attend_kernel(AttendArgs a, int S, i
   }
   __syncthreads();
   // one split writes the normalised output itself, unless the fused epilogue takes partials
-  const bool direct = S == 1 && !a.partials;
+  const bool direct = F == kMXR ? false : S == 1;
   float inv[16];
 #pragma unroll
   for (int q4 = 0; q4 < 4; ++q4)
@@ -827,19 +833,99 @@ __global__ __launch_bounds__(kThreads) void attend_kernel(AttendArgs a, int S, i
       const float l = mlsum[8 * q4 + 4 * kh + e];
       inv[4 * q4 + e] = (direct ? (l > 0.0f ? 1.0f / l : 0.0f) : 1.0f) * (NV ? 1.0f / a.kv_pscale : 1.0f);
     }
-  float* dst = direct ? a.out + ((int64_t)t * a.Hq + h0) * D
-                      : (float*)a.ws + (((int64_t)split * a.T + t) * a.Hq + h0) * D;
+  if constexpr (F == kMXF) {
+    {
+      // MegaAttention's epilogue in place (one split; blog §Kernels): the normalised outputs
+      // are rotated back on the rotary pairs (the partner dim is the neighbouring lane, so a
+      // DPP pair swap), then each head's amax over all 8 waves' dims gives the scale of its
+      // E4M3 codes.  The same fp32 formulas as attend_fused_epilogue_kernel.
+      const int r0 = D - 2 * a.rope_pairs;
 #pragma unroll
-  for (int i = 0; i < G::NBW; ++i) {
-    if (i < G::BPW || wave < G::EXTRA) {
-      const int d = 32 * (b0 + i) + r32;
+      for (int i = 0; i < G::NBW; ++i) {
+        if (i < G::BPW || wave < G::EXTRA) {
+          const int d = 32 * (b0 + i) + r32;
+          const bool rot = a.rope_pairs > 0 && d >= r0;
+          float c = 1.0f, sn = 0.0f;
+          if (rot) {
+            const int64_t pj = (int64_t)t * a.rope_pairs + (d - r0) / 2;
+            c = a.rope_cos[pj];
+            sn = a.rope_sin[pj];
+          }
 #pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int hl = 8 * q4 + 4 * kh + e;
-          dst[(int64_t)hl * D + d] = o[i][4 * q4 + e] * inv[4 * q4 + e];
+          for (int j = 0; j < 16; ++j) {
+            const float x = o[i][j] * inv[j];
+            const float xp = dpp_f<0xB1>(x);                  // the other dim of the pair
+            o[i][j] = !rot ? x : ((r32 & 1) ? __builtin_fmaf(-xp, sn, x * c) : __builtin_fmaf(x, c, xp * sn));
+          }
         }
+        __builtin_amdgcn_sched_barrier(0);             // one block at a time (registers)
+      }
+      // per head: amax over this lane's blocks, the 32 lanes of its k-half (two DPP rows)
+      // and the 8 waves (LDS)
+      float* amx = (float*)(smem + G::RED);             // [8 waves][32 heads], then scales [32]
+      float* hsc = amx + 8 * 32;
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        float m = 0.0f;
+#pragma unroll
+        for (int i = 0; i < G::NBW; ++i)
+          if (i < G::BPW || wave < G::EXTRA) m = fmaxf(m, fabsf(o[i][j]));
+        m = row_reduce<true>(m);
+        m = fmaxf(m, __shfl_xor(m, 16));
+        if (r32 == 0) amx[wave * 32 + 8 * (j >> 2) + 4 * kh + (j & 3)] = m;
+      }
+      __syncthreads();
+      if (tid < 32) {
+        float m = amx[tid];
+#pragma unroll
+        for (int w = 1; w < 8; ++w) m = fmaxf(m, amx[w * 32 + tid]);
+        hsc[tid] = m > 0.0f ? 448.0f / m : 0.0f;        // the quantisation multiplier
+        a.out_scale[(int64_t)t * a.Hq + h0 + tid] = m / 448.0f;
+      }
+      __syncthreads();
+      v4f rq[4];
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) rq[q4] = *(const v4f*)(hsc + 8 * q4 + 4 * kh);
+      // codes staged in the (idle) tile buffers as [32 heads][D] bytes, then stored 16 bytes
+      // a lane
+      uint8_t* stage = smem;
+      float* df = a.out ? a.out + ((int64_t)t * a.Hq + h0) * D : nullptr;
+#pragma unroll
+      for (int i = 0; i < G::NBW; ++i) {
+        if (i < G::BPW || wave < G::EXTRA) {
+          const int d = 32 * (b0 + i) + r32;
+#pragma unroll
+          for (int q4 = 0; q4 < 4; ++q4)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const int hl = 8 * q4 + 4 * kh + e;
+              const float y = o[i][4 * q4 + e];
+              const float r = rq[q4][e];
+              const unsigned code = r > 0.0f ? (unsigned)__builtin_amdgcn_cvt_pk_fp8_f32(y * r, 0.0f, 0, false) & 0xFFu : 0u;
+              stage[hl * D + d] = (uint8_t)code;
+              if (df) df[(int64_t)hl * D + d] = y;
+            }
+        }
+      }
+      __syncthreads();
+      uint8_t* d8 = a.out_fp8 + ((int64_t)t * a.Hq + h0) * D;   // 32 consecutive rows of D bytes
+      for (int x = tid; x < 32 * D / 16; x += kThreads) *(v4u*)(d8 + 16 * x) = *(const v4u*)(stage + 16 * x);
+    }
+  } else {
+    float* dst = direct ? a.out + ((int64_t)t * a.Hq + h0) * D
+                        : (float*)a.ws + (((int64_t)split * a.T + t) * a.Hq + h0) * D;
+#pragma unroll
+    for (int i = 0; i < G::NBW; ++i) {
+      if (i < G::BPW || wave < G::EXTRA) {
+        const int d = 32 * (b0 + i) + r32;
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int hl = 8 * q4 + 4 * kh + e;
+            dst[(int64_t)hl * D + d] = o[i][4 * q4 + e] * inv[4 * q4 + e];
+          }
+      }
     }
   }
   if (tid < 32) {
@@ -871,8 +957,8 @@ hipError_t launch(const AttendArgs& a, int S, hipStream_t s) {
   }
   hipLaunchKernelGGL((attend_kernel<D, F>), dim3(nb), dim3(kThreads), G::LDS, s, a, S, ngroups, total);
   hipError_t e = hipGetLastError();
-  // the fused form (a.partials) merges in its own epilogue kernel
-  return e != hipSuccess ? e : (a.partials ? hipSuccess : launch_attend_merge(a, S, s));
+  // the fused form merges in its own epilogue (kernel)
+  return e != hipSuccess ? e : ((F == kMXF || F == kMXR) ? hipSuccess : launch_attend_merge(a, S, s));
 }
 
 }  // namespace sd
@@ -885,9 +971,11 @@ hipError_t launch_attend_sd(const AttendArgs& a, int S, hipStream_t s) {
   switch (a.D) {
 #define SMQA_SD_D(d)                                              \
   case d:                                                         \
-    return a.kv_fmt == sd::kFP8  ? sd::launch<d, sd::kFP8>(a, S, s) \
-           : a.kv_fmt == sd::kNV ? sd::launch<d, sd::kNV>(a, S, s)  \
-                                 : sd::launch<d, sd::kMX>(a, S, s);
+    return a.kv_fmt == sd::kFP8   ? sd::launch<d, sd::kFP8>(a, S, s)  \
+           : a.kv_fmt == sd::kNV  ? sd::launch<d, sd::kNV>(a, S, s)   \
+           : a.kv_fmt == sd::kMXF ? sd::launch<d, sd::kMXF>(a, S, s)  \
+           : a.kv_fmt == sd::kMXR ? sd::launch<d, sd::kMXR>(a, S, s)  \
+                                  : sd::launch<d, sd::kMX>(a, S, s);
     SMQA_SD_D(128) SMQA_SD_D(256) SMQA_SD_D(384) SMQA_SD_D(512)
     SMQA_SD_D(640) SMQA_SD_D(768) SMQA_SD_D(896) SMQA_SD_D(1024)
     SMQA_SD_D(1152) SMQA_SD_D(1280) SMQA_SD_D(1408) SMQA_SD_D(1536)

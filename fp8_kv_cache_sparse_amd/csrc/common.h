@@ -123,7 +123,8 @@ struct AttendArgs {
   void* ws;
   // global cache format: 0 MX FP4 (kv_codes E2M1, kv_e8m0 E8M0 per 32); 1 FP8 (kv_codes E4M3
   // rows [N][D], kv_e8m0 unused); 2 NVFP4 (kv_codes E2M1, kv_e8m0 E4M3 per 16, tensor scale
-  // kv_gscale)
+  // kv_gscale); 3 / 4 MX with the fused query RoPE and FP8 epilogue in the kernel / with
+  // split partials (set by launch_attend_fused)
   int32_t kv_fmt;
   float kv_gscale;
   float kv_pscale;            // NVFP4: the power of two K with kv_gscale * K in [1, 2)

@@ -259,8 +259,9 @@ int sparse_mqa_attend_nvfp4(const smqa_layout* L,
  *   O       = sparse_mqa_attend(q', ...)
  *   O'      = O with the same pairs rotated back: (a, b) -> (a c + b s, -a s + b c)
  *   out_scale[t,h] = max_d |O'[t,h,d]| / 448,
- *   out_fp8[t,h,d] = E4M3(O'[t,h,d] / out_scale[t,h]) (fp32 divisions, nearest
- *             even; an all-zero row gives scale 0 and zero codes)
+ *   out_fp8[t,h,d] = E4M3(O'[t,h,d] * (448 / amax)) (fp32: one division per
+ *             row, one product per element, nearest even; an all-zero row gives
+ *             scale 0 and zero codes)
  * so out_fp8 * out_scale approximates O' within E4M3's 2^-4 relative step.
  * rope_cos, rope_sin float [T][R], 16-byte aligned (may be NULL when R = 0);
  *             the angles of each query's position (frequencies, scaling and the

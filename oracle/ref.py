@@ -32,7 +32,7 @@ Readings where the pages are silent (each restated where it is used):
       rounded to bf16 before the products, the rotation evaluated in float32
       with one fused multiply-add per output (the precision of the decision)
   R17 FP8 output: per (query, head) row, scale = amax / 448, E4M3 codes of
-      x / scale rounded to nearest even, in float32
+      x * (448 / amax) rounded to nearest even, in float32
 """
 from __future__ import annotations
 
@@ -268,13 +268,15 @@ def rope_query_bf16(q, rope_cos, rope_sin):
 
 
 def fp8_quantize(x):
-    """Per row (last axis) of float32 values: scale = amax / 448 and codes = E4M3(x / scale),
-    both divisions in float32 (reading R17); an all-zero row gives scale 0 and zero codes."""
+    """Per row (last axis) of float32 values: scale = amax / 448 (the dequantisation factor)
+    and codes = E4M3(x * r) with r = 448 / amax, every operation in float32 (reading R17);
+    an all-zero row gives scale 0 and zero codes."""
     x = np.asarray(x, dtype=np.float32)
     amax = np.abs(x).max(axis=-1)
     scale = (amax / np.float32(448.0)).astype(np.float32)
-    safe = np.where(scale > 0, scale, np.float32(1.0)).astype(np.float32)
-    y = (x / safe[..., None]).astype(np.float32)
+    safe = np.where(amax > 0, amax, np.float32(1.0)).astype(np.float32)
+    r = (np.float32(448.0) / safe).astype(np.float32)
+    y = (x * r[..., None]).astype(np.float32)
     codes = codecs.e4m3_encode(y)
     codes = np.where((scale > 0)[..., None], codes, np.uint8(0)).astype(np.uint8)
     return codes, scale
