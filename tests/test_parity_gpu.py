@@ -440,6 +440,40 @@ def test_attend_fused(lib, name, kw, R):
     assert outb is None and torch.equal(o8b, o8) and torch.equal(oscb, osc)
 
 
+def test_attend_fused_zero_rows_and_window_only(lib):
+    """A query that sees no row gives an all-zero output: scale 0 and zero codes; the others
+    attend to their window rows only (every index -1)."""
+    import dataclasses
+    wl = gen("replay_h100k", B=1, lengths=2000, replay=(2000, 4))
+    clip = wl.swa_clip.clone()
+    clip[0] = wl.q_pos[0] + 1
+    wl = dataclasses.replace(wl, swa_clip=clip)
+    a = np_inputs(wl)
+    idx_np = np.full((wl.T, wl.k), -1, dtype=np.int32)
+    idx = torch.tensor(idx_np, device=DEV)
+    c, s_ = _angles(wl.T, 32, seed=5)
+    announce(f"attend_fused zero rows T={wl.T}")
+    o8, osc, out, lse = gpu_attend_fused(lib, wl, idx, c, s_)
+    sync()
+    assert torch.all(o8[0] == 0) and torch.all(osc[0] == 0) and torch.all(out[0] == 0)
+    Oi, L, _, _ = ref.attend_fused(a["q"], c.cpu().numpy(), s_.cpu().numpy(), a["kv_codes"], a["kv_e8m0"],
+                                   a["kv_rowscale"], idx_np, a["swa"], a["swa_scale"], a["swa_pos0"],
+                                   a["swa_clip"], a["seq_start"], a["q_start"], a["q_pos"], a["W"],
+                                   a["sm_scale"])
+    ok, msg = close_attention(out.cpu().numpy(), Oi, lse.cpu().numpy(), L)
+    assert ok, msg
+    codes, scale = ref.fp8_quantize(out.cpu().numpy())
+    assert np.array_equal(o8.cpu().numpy(), codes) and np.array_equal(osc.cpu().numpy(), scale)
+
+
+def test_attend_nvfp4_small_tensor_scale(lib):
+    """g = 2^-12 puts the block scales near the top of E4M3 (~100-400) and the window P
+    multiplier sigma * K near 4096: both within the documented range."""
+    wl = synth.with_nvfp4_kv(gen("decode_8k", B=2, lengths=(3000, 5000), k=1024), g=2.0 ** -12)
+    assert int(wl.kv_nv_scales.max()) <= 0x7E
+    _attend_nv_check(lib, synth.with_scales(wl))
+
+
 # ------------------------------------------------------------------ decode step
 
 def _decode_check(lib, wl, ts=None):
