@@ -262,7 +262,7 @@ int sparse_mqa_attend_fp8kv(const smqa_layout* L, const uint16_t* q_bf16, const 
   if (st) return st;
   smqa::AttendArgs a{L->seq_start, L->q_start, L->q_pos, L->num_seqs, L->num_q, q_bf16, kv_fp8,
                      nullptr, kv_rowscale, idx, k, swa_fp8, swa_scale, swa_pos0, swa_clip, W, Hq, D,
-                     sm_scale, out, lse, workspace, 1, 1.0f};
+                     sm_scale, out, lse, workspace, smqa::kKvFP8, 1.0f};
   hipError_t e = smqa::launch_attend_fmt(a, (hipStream_t)stream);
   return e == hipSuccess ? SMQA_OK : hip_fail(e, "sparse_mqa_attend_fp8kv launch");
 }
@@ -292,7 +292,7 @@ int sparse_mqa_attend_nvfp4(const smqa_layout* L, const uint16_t* q_bf16, const 
   if (st) return st;
   smqa::AttendArgs a{L->seq_start, L->q_start, L->q_pos, L->num_seqs, L->num_q, q_bf16, kv_codes,
                      kv_scales, kv_rowscale, idx, k, swa_fp8, swa_scale, swa_pos0, swa_clip, W, Hq, D,
-                     sm_scale, out, lse, workspace, 2, kv_global_scale, K};
+                     sm_scale, out, lse, workspace, smqa::kKvNV, kv_global_scale, K};
   hipError_t e = smqa::launch_attend_fmt(a, (hipStream_t)stream);
   return e == hipSuccess ? SMQA_OK : hip_fail(e, "sparse_mqa_attend_nvfp4 launch");
 }
@@ -332,8 +332,9 @@ int sparse_mqa_attend_fused(const smqa_layout* L, const uint16_t* q_bf16, const 
   if (st) return st;
   smqa::AttendArgs a{L->seq_start, L->q_start, L->q_pos, L->num_seqs, L->num_q, q_bf16, kv_codes,
                      kv_e8m0, kv_rowscale, idx, k, swa_fp8, swa_scale, swa_pos0, swa_clip, W, Hq, D,
-                     sm_scale, out, lse, workspace, 0, 1.0f, 1.0f, rope_pairs > 0 ? rope_cos : nullptr,
-                     rope_pairs > 0 ? rope_sin : nullptr, rope_pairs, 1, out_fp8, out_scale};
+                     sm_scale, out, lse, workspace, smqa::kKvMX, 1.0f, 1.0f,
+                     rope_pairs > 0 ? rope_cos : nullptr, rope_pairs > 0 ? rope_sin : nullptr, rope_pairs,
+                     out_fp8, out_scale};
   hipError_t e = smqa::launch_attend_fused(a, (hipStream_t)stream);
   return e == hipSuccess ? SMQA_OK : hip_fail(e, "sparse_mqa_attend_fused launch");
 }

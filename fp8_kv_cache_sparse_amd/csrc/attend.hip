@@ -1254,12 +1254,11 @@ size_t attend_fused_workspace_bytes(int32_t T, int32_t k, int32_t W, int32_t Hq,
 hipError_t launch_attend_fused(const AttendArgs& a0, hipStream_t s) {
   if (a0.T == 0) return hipSuccess;
   const AttPlan p = attend_plan(a0.T, a0.k, a0.W, a0.Hq, a0.D);
-  if (!p.wide || a0.D > 1664 || a0.kv_fmt != 0 || !a0.out_fp8 || !a0.out_scale) return hipErrorInvalidValue;
+  if (!p.wide || a0.D > 1664 || a0.kv_fmt != kKvMX || !a0.out_fp8 || !a0.out_scale) return hipErrorInvalidValue;
   AttendArgs a = a0;
   // one split: the attention kernel's own epilogue rotates back and quantises; several:
   // partials, then the epilogue kernel
-  a.kv_fmt = p.S > 1 ? 4 : 3;                    // the fused instantiations of the MX kernel
-  a.partials = p.S > 1 ? 1 : 0;
+  a.kv_fmt = p.S > 1 ? kKvMXR : kKvMXF;
   hipError_t e = launch_attend_sd(a, p.S, s);
   if (e != hipSuccess || p.S == 1) return e;
   const dim3 grid(a.T * a.Hq);
@@ -1274,7 +1273,7 @@ hipError_t launch_attend_fused(const AttendArgs& a0, hipStream_t s) {
 hipError_t launch_attend_fmt(const AttendArgs& a, hipStream_t s) {
   if (a.T == 0) return hipSuccess;
   const AttPlan p = attend_plan(a.T, a.k, a.W, a.Hq, a.D);
-  if (!p.wide || a.D > 1664 || (a.kv_fmt != 1 && a.kv_fmt != 2)) return hipErrorInvalidValue;
+  if (!p.wide || a.D > 1664 || (a.kv_fmt != kKvFP8 && a.kv_fmt != kKvNV)) return hipErrorInvalidValue;
   return launch_attend_sd(a, p.S, s);
 }
 

@@ -69,7 +69,7 @@ constexpr int align16(int x) { return (x + 15) & ~15; }
 // plain kernel keeps its registers and neither ends in a branch between two epilogues):
 // kMXF, query RoPE and the FP8 epilogue in the kernel (one split), and kMXR, query RoPE
 // with split partials for attend_fused_epilogue_kernel.
-constexpr int kMX = 0, kFP8 = 1, kNV = 2, kMXF = 3, kMXR = 4;
+constexpr int kMX = kKvMX, kFP8 = kKvFP8, kNV = kKvNV, kMXF = kKvMXF, kMXR = kKvMXR;
 constexpr bool mx_like(int F) { return F == kMX || F == kMXF || F == kMXR; }
 
 // LDS geometry for latent width D and global format F (compile time, so every offset is an

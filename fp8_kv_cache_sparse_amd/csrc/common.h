@@ -101,6 +101,13 @@ struct TopkFill {
 hipError_t launch_topk_prepare(const TopkArgs& a, hipStream_t s, TopkFill* fill);
 hipError_t launch_topk_from_hist(const TopkArgs& a, hipStream_t s);
 
+// Global cache formats of AttendArgs::kv_fmt.  kKvMX: kv_codes E2M1, kv_e8m0 E8M0 per 32.
+// kKvFP8: kv_codes E4M3 rows [N][D], kv_e8m0 unused.  kKvNV: kv_codes E2M1, kv_e8m0 E4M3 per
+// 16, tensor scale kv_gscale.  kKvMXF / kKvMXR: the MX format with MegaAttention's fused query
+// RoPE and FP8 epilogue, in the attention kernel (one split) / through split partials (set by
+// launch_attend_fused only).
+enum KvFmt : int32_t { kKvMX = 0, kKvFP8 = 1, kKvNV = 2, kKvMXF = 3, kKvMXR = 4 };
+
 struct AttendArgs {
   const int64_t* seq_start;
   const int32_t* q_start;
@@ -121,20 +128,15 @@ struct AttendArgs {
   float* out;
   float* lse;
   void* ws;
-  // global cache format: 0 MX FP4 (kv_codes E2M1, kv_e8m0 E8M0 per 32); 1 FP8 (kv_codes E4M3
-  // rows [N][D], kv_e8m0 unused); 2 NVFP4 (kv_codes E2M1, kv_e8m0 E4M3 per 16, tensor scale
-  // kv_gscale); 3 / 4 MX with the fused query RoPE and FP8 epilogue in the kernel / with
-  // split partials (set by launch_attend_fused)
-  int32_t kv_fmt;
+  int32_t kv_fmt;             // KvFmt
   float kv_gscale;
   float kv_pscale;            // NVFP4: the power of two K with kv_gscale * K in [1, 2)
-  // fused epilogue (MX format only): the last 2 * rope_pairs latent dims of q are rotated by
-  // (rope_cos, rope_sin)[t] before the products; partials = 1 writes split partials even
-  // for one split; out_fp8 / out_scale receive the quantised, inversely rotated output
+  // fused epilogue (kKvMXF / kKvMXR): the last 2 * rope_pairs latent dims of q are rotated by
+  // (rope_cos, rope_sin)[t] before the products; out_fp8 / out_scale receive the quantised,
+  // inversely rotated output
   const float* rope_cos;
   const float* rope_sin;
   int32_t rope_pairs;
-  int32_t partials;
   uint8_t* out_fp8;
   float* out_scale;
 };
