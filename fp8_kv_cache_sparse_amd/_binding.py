@@ -62,6 +62,8 @@ _SIGS = {
     "smqa_attend_fused_workspace_size": (_S, [_LP, _I, _I, _I, _I]),
     "decode_step": (_I, [_LP, _P, _P, _P, _P, _P, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P, _P,
                          _I, _I, _I, _F, _I, _P, _P, _P, _P, _S, _P]),
+    "decode_step_fused": (_I, [_LP, _P, _P, _P, _P, _P, _I, _I, _I, _P, _P, _P, _I, _P, _P, _P, _P,
+                               _P, _P, _P, _I, _I, _I, _F, _I, _P, _P, _P, _P, _P, _P, _S, _P]),
     "smqa_topk_workspace_size": (_S, [_LP, _I, _I]),
     "smqa_attend_workspace_size": (_S, [_LP, _I, _I, _I, _I]),
     "smqa_decode_step_workspace_size": (_S, [_LP, _I, _I, _I, _I, _I]),
@@ -382,3 +384,51 @@ def decode_step(L: Batch, q_fp8, w, k_fp8, k_scale, cand, q, kv_codes, kv_e8m0, 
                            float(sm_scale), k, _ptr(out), _ptr(lse), _ptr(idx), wp, wb,
                            _stream(stream)))
     return out, lse, idx
+
+
+def decode_step_fused(L: Batch, q_fp8, w, k_fp8, k_scale, cand, q, rope_cos, rope_sin, kv_codes,
+                      kv_e8m0, kv_rowscale, swa, swa_scale, swa_pos0, swa_clip, k: int,
+                      sm_scale: float, out_fp8=None, out_scale=None, out=None, lse=None, idx=None,
+                      want_out=True, workspace=None, stream=None):
+    """score -> top-k -> fused attention (query RoPE, inverse RoPE, FP8 output) in one call
+    -> (out_fp8, out_scale, out or None, lse, idx)."""
+    lib = load()
+    for t_, n_, dt, nd in ((q_fp8, "q_fp8", _U8, 3), (w, "w", torch.float32, 2), (k_fp8, "k_fp8", _U8, 2),
+                           (k_scale, "k_scale", torch.float32, 1), (cand, "cand", torch.int32, 2),
+                           (q, "q", torch.bfloat16, 3), (rope_cos, "rope_cos", torch.float32, 2),
+                           (rope_sin, "rope_sin", torch.float32, 2), (kv_codes, "kv_codes", torch.uint8, 2),
+                           (kv_e8m0, "kv_e8m0", torch.uint8, 2), (kv_rowscale, "kv_rowscale", torch.float32, 1),
+                           (swa, "swa", _U8, 3), (swa_scale, "swa_scale", torch.float32, 2),
+                           (swa_pos0, "swa_pos0", torch.int32, 1), (swa_clip, "swa_clip", torch.int32, 1)):
+        _dev(t_, n_, dt, nd)
+    T, Hi, Di = q_fp8.shape
+    _, Hq, D = q.shape
+    W = swa.shape[1]
+    R = 0 if rope_cos is None else rope_cos.shape[1]
+    n_cand = 0 if cand is None else cand.shape[1]
+    dev = q.device
+    if out_fp8 is None:
+        out_fp8 = torch.empty((T, Hq, D), dtype=torch.uint8, device=dev)
+    if out_scale is None:
+        out_scale = torch.empty((T, Hq), dtype=torch.float32, device=dev)
+    if out is None and want_out:
+        out = torch.empty((T, Hq, D), dtype=torch.float32, device=dev)
+    if lse is None:
+        lse = torch.empty((T, Hq), dtype=torch.float32, device=dev)
+    if idx is None:
+        idx = torch.empty((T, k), dtype=torch.int32, device=dev)
+    for t_, n_, dt, nd in ((out_fp8, "out_fp8", torch.uint8, 3), (out_scale, "out_scale", torch.float32, 2),
+                           (out, "out", torch.float32, 3), (lse, "lse", torch.float32, 2),
+                           (idx, "idx", torch.int32, 2)):
+        _dev(t_, n_, dt, nd)
+    need = lib.smqa_decode_step_workspace_size(L.ref, k, n_cand, W, Hq, D)
+    if workspace is None:
+        workspace = _workspace(need, dev)
+    wp, wb = _ws_ptr(workspace)
+    _check(lib.decode_step_fused(L.ref, _ptr(q_fp8), _ptr(w), _ptr(k_fp8), _ptr(k_scale), _ptr(cand), n_cand,
+                                 Hi, Di, _ptr(q), _ptr(rope_cos), _ptr(rope_sin), R, _ptr(kv_codes),
+                                 _ptr(kv_e8m0), _ptr(kv_rowscale), _ptr(swa), _ptr(swa_scale),
+                                 _ptr(swa_pos0), _ptr(swa_clip), W, Hq, D, float(sm_scale), k,
+                                 _ptr(out_fp8), _ptr(out_scale), _ptr(out), _ptr(lse), _ptr(idx), wp, wb,
+                                 _stream(stream)))
+    return out_fp8, out_scale, out, lse, idx

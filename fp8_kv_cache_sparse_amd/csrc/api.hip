@@ -126,6 +126,28 @@ int check_attend(const uint16_t* q, const uint8_t* kv_codes, const uint8_t* kv_e
   return SMQA_OK;
 }
 
+// The extra arguments of the fused form (MegaAttention's query RoPE and FP8 output).
+int check_fused(const float* rope_cos, const float* rope_sin, int32_t rope_pairs, int32_t Hq,
+                int32_t D, const uint8_t* out_fp8, const float* out_scale) {
+  REQUIRE_PTR(out_fp8);
+  REQUIRE_PTR(out_scale);
+  REQUIRE_ALIGN(out_fp8, 16);
+  REQUIRE_ALIGN(out_scale, 4);
+  if (Hq % 32 != 0 || D > 1664)
+    return fail(SMQA_ERR_UNSUPPORTED, "fused attention: Hq = %d, D = %d; supported Hq %% 32 == 0, D <= 1664",
+                Hq, D);
+  if (rope_pairs < 0 || rope_pairs % 4 != 0 || 2 * rope_pairs > D)
+    return fail(SMQA_ERR_UNSUPPORTED, "rope_pairs = %d: supported multiples of 4 with 2 * rope_pairs <= D",
+                rope_pairs);
+  if (rope_pairs > 0) {
+    REQUIRE_PTR(rope_cos);
+    REQUIRE_PTR(rope_sin);
+    REQUIRE_ALIGN(rope_cos, 16);
+    REQUIRE_ALIGN(rope_sin, 16);
+  }
+  return SMQA_OK;
+}
+
 int check_ws(void* ws, size_t have, size_t need) {
   if (need == 0) return SMQA_OK;
   if (!ws) return fail(SMQA_ERR_WORKSPACE, "workspace is NULL but %zu bytes are required", need);
@@ -312,22 +334,8 @@ int sparse_mqa_attend_fused(const smqa_layout* L, const uint16_t* q_bf16, const 
   st = check_attend(q_bf16, kv_codes, kv_e8m0, kv_rowscale, idx, k, swa_fp8, swa_scale, swa_pos0,
                     swa_clip, W, Hq, D, sm_scale, out ? out : (const float*)out_fp8, lse, true);
   if (st) return st;
-  REQUIRE_PTR(out_fp8);
-  REQUIRE_PTR(out_scale);
-  REQUIRE_ALIGN(out_fp8, 16);
-  REQUIRE_ALIGN(out_scale, 4);
-  if (Hq % 32 != 0 || D > 1664)
-    return fail(SMQA_ERR_UNSUPPORTED, "fused attention: Hq = %d, D = %d; supported Hq %% 32 == 0, D <= 1664",
-                Hq, D);
-  if (rope_pairs < 0 || rope_pairs % 4 != 0 || 2 * rope_pairs > D)
-    return fail(SMQA_ERR_UNSUPPORTED, "rope_pairs = %d: supported multiples of 4 with 2 * rope_pairs <= D",
-                rope_pairs);
-  if (rope_pairs > 0) {
-    REQUIRE_PTR(rope_cos);
-    REQUIRE_PTR(rope_sin);
-    REQUIRE_ALIGN(rope_cos, 16);
-    REQUIRE_ALIGN(rope_sin, 16);
-  }
+  st = check_fused(rope_cos, rope_sin, rope_pairs, Hq, D, out_fp8, out_scale);
+  if (st) return st;
   st = check_ws(workspace, workspace_bytes, smqa::attend_fused_workspace_bytes(L->num_q, k, W, Hq, D));
   if (st) return st;
   smqa::AttendArgs a{L->seq_start, L->q_start, L->q_pos, L->num_seqs, L->num_q, q_bf16, kv_codes,
@@ -339,13 +347,26 @@ int sparse_mqa_attend_fused(const smqa_layout* L, const uint16_t* q_bf16, const 
   return e == hipSuccess ? SMQA_OK : hip_fail(e, "sparse_mqa_attend_fused launch");
 }
 
-int decode_step(const smqa_layout* L, const uint8_t* q_fp8, const float* w, const uint8_t* k_fp8,
-                const float* k_scale, const int32_t* cand, int32_t n_cand, int32_t Hi, int32_t Di,
-                const uint16_t* q_bf16, const uint8_t* kv_codes, const uint8_t* kv_e8m0,
-                const float* kv_rowscale, const uint8_t* swa_fp8, const float* swa_scale,
-                const int32_t* swa_pos0, const int32_t* swa_clip, int32_t W, int32_t Hq, int32_t D,
-                float sm_scale, int32_t k, float* out, float* lse, int32_t* idx_out, void* workspace,
-                size_t workspace_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// The fused form's extra outputs of a decode step (NULL: the plain step).
+struct FusedOut {
+  const float* rope_cos;
+  const float* rope_sin;
+  int32_t rope_pairs;
+  uint8_t* out_fp8;
+  float* out_scale;
+};
+
+int decode_step_impl(const smqa_layout* L, const uint8_t* q_fp8, const float* w, const uint8_t* k_fp8,
+                     const float* k_scale, const int32_t* cand, int32_t n_cand, int32_t Hi, int32_t Di,
+                     const uint16_t* q_bf16, const uint8_t* kv_codes, const uint8_t* kv_e8m0,
+                     const float* kv_rowscale, const uint8_t* swa_fp8, const float* swa_scale,
+                     const int32_t* swa_pos0, const int32_t* swa_clip, int32_t W, int32_t Hq, int32_t D,
+                     float sm_scale, int32_t k, float* out, float* lse, int32_t* idx_out, void* workspace,
+                     size_t workspace_bytes, void* stream, const FusedOut* fz) {
   g_err.clear();
   int st = check_layout(L);
   if (st) return st;
@@ -355,9 +376,15 @@ int decode_step(const smqa_layout* L, const uint8_t* q_fp8, const float* w, cons
   st = check_score(L, q_fp8, w, k_fp8, k_scale, cand, n_cand, Hi, Di, nullptr, cols, false);
   if (st) return st;
   if (k < 1 || k > 4096) return fail(SMQA_ERR_UNSUPPORTED, "k = %d: supported 1..4096", k);
+  // the fused form's fp32 output is optional: out_fp8 stands in for it in the shared checks
+  const float* out_chk = (fz && !out) ? (const float*)fz->out_fp8 : out;
   st = check_attend(q_bf16, kv_codes, kv_e8m0, kv_rowscale, idx_out, k, swa_fp8, swa_scale, swa_pos0,
-                    swa_clip, W, Hq, D, sm_scale, out, lse, false);
+                    swa_clip, W, Hq, D, sm_scale, out_chk, lse, false);
   if (st) return st;
+  if (fz) {
+    st = check_fused(fz->rope_cos, fz->rope_sin, fz->rope_pairs, Hq, D, fz->out_fp8, fz->out_scale);
+    if (st) return st;
+  }
   const DecodeWs d = decode_ws_layout(L, k, cols, W, Hq, D);
   st = check_ws(workspace, workspace_bytes, d.total);
   if (st) return st;
@@ -387,9 +414,48 @@ int decode_step(const smqa_layout* L, const uint8_t* q_fp8, const float* w, cons
   smqa::AttendArgs aa{L->seq_start, L->q_start, L->q_pos, L->num_seqs, L->num_q, q_bf16, kv_codes,
                       kv_e8m0, kv_rowscale, idx, k, swa_fp8, swa_scale, swa_pos0, swa_clip, W, Hq, D,
                       sm_scale, out, lse, ws + d.attend_off};
-  e = smqa::launch_attend(aa, s);
+  if (fz) {
+    aa.rope_pairs = fz->rope_pairs;
+    aa.rope_cos = fz->rope_pairs > 0 ? fz->rope_cos : nullptr;
+    aa.rope_sin = fz->rope_pairs > 0 ? fz->rope_sin : nullptr;
+    aa.out_fp8 = fz->out_fp8;
+    aa.out_scale = fz->out_scale;
+    e = smqa::launch_attend_fused(aa, s);
+  } else {
+    e = smqa::launch_attend(aa, s);
+  }
   if (e != hipSuccess) return hip_fail(e, "decode_step attend launch");
   return SMQA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int decode_step(const smqa_layout* L, const uint8_t* q_fp8, const float* w, const uint8_t* k_fp8,
+                const float* k_scale, const int32_t* cand, int32_t n_cand, int32_t Hi, int32_t Di,
+                const uint16_t* q_bf16, const uint8_t* kv_codes, const uint8_t* kv_e8m0,
+                const float* kv_rowscale, const uint8_t* swa_fp8, const float* swa_scale,
+                const int32_t* swa_pos0, const int32_t* swa_clip, int32_t W, int32_t Hq, int32_t D,
+                float sm_scale, int32_t k, float* out, float* lse, int32_t* idx_out, void* workspace,
+                size_t workspace_bytes, void* stream) {
+  return decode_step_impl(L, q_fp8, w, k_fp8, k_scale, cand, n_cand, Hi, Di, q_bf16, kv_codes, kv_e8m0,
+                          kv_rowscale, swa_fp8, swa_scale, swa_pos0, swa_clip, W, Hq, D, sm_scale, k, out,
+                          lse, idx_out, workspace, workspace_bytes, stream, nullptr);
+}
+
+int decode_step_fused(const smqa_layout* L, const uint8_t* q_fp8, const float* w, const uint8_t* k_fp8,
+                      const float* k_scale, const int32_t* cand, int32_t n_cand, int32_t Hi, int32_t Di,
+                      const uint16_t* q_bf16, const float* rope_cos, const float* rope_sin,
+                      int32_t rope_pairs, const uint8_t* kv_codes, const uint8_t* kv_e8m0,
+                      const float* kv_rowscale, const uint8_t* swa_fp8, const float* swa_scale,
+                      const int32_t* swa_pos0, const int32_t* swa_clip, int32_t W, int32_t Hq, int32_t D,
+                      float sm_scale, int32_t k, uint8_t* out_fp8, float* out_scale, float* out, float* lse,
+                      int32_t* idx_out, void* workspace, size_t workspace_bytes, void* stream) {
+  const FusedOut fz{rope_cos, rope_sin, rope_pairs, out_fp8, out_scale};
+  return decode_step_impl(L, q_fp8, w, k_fp8, k_scale, cand, n_cand, Hi, Di, q_bf16, kv_codes, kv_e8m0,
+                          kv_rowscale, swa_fp8, swa_scale, swa_pos0, swa_clip, W, Hq, D, sm_scale, k, out,
+                          lse, idx_out, workspace, workspace_bytes, stream, &fz);
 }
 
 }  // extern "C"

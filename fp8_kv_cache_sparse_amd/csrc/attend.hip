@@ -1243,9 +1243,10 @@ static hipError_t launch_thr(const AttendArgs& a, const AttPlan& p, hipStream_t 
 
 hipError_t launch_attend_sd(const AttendArgs& a, int S, hipStream_t s);
 
+// One split quantises in the attention kernel itself: the partials, and so the workspace,
+// are those of the plain call.
 size_t attend_fused_workspace_bytes(int32_t T, int32_t k, int32_t W, int32_t Hq, int32_t D) {
-  const int S = attend_splits(T, k, W, Hq, D);
-  return (size_t)S * T * Hq * D * 4 + (size_t)S * T * Hq * 8;
+  return attend_workspace_bytes(T, k, W, Hq, D);
 }
 
 // The fused form: the dimension-split kernel (MX cache, Hq % 32 == 0, D <= 1664, checked by

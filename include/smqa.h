@@ -270,8 +270,8 @@ int sparse_mqa_attend_nvfp4(const smqa_layout* L,
  * out_fp8     uint8 [T][Hq][D], 16-byte aligned;  out_scale float [T][Hq]
  * out         float [T][Hq][D] or NULL: O' in fp32 (optional)
  * lse         float [T][Hq] or NULL (of the rotated query's logits)
- * workspace:  smqa_attend_fused_workspace_size() bytes (never 0: the split
- *             partials always go through it).
+ * workspace:  smqa_attend_fused_workspace_size() bytes (the split partials;
+ *             0 when one split suffices, as for sparse_mqa_attend).
  * Limits: those of sparse_mqa_attend plus Hq % 32 == 0 and D <= 1664; other
  * arguments as in sparse_mqa_attend.
  */
@@ -310,6 +310,31 @@ int decode_step(const smqa_layout* L,
                 float* out, float* lse, int32_t* idx_out,
                 void* workspace, size_t workspace_bytes,
                 void* stream);
+
+/*
+ * decode_step_fused — decode_step with MegaAttention's fused form as its
+ * attention (sparse_mqa_attend_fused: query RoPE by rope_cos / rope_sin on the
+ * last 2 * rope_pairs dims, inverse RoPE and FP8 output): the output
+ * projection's input comes out of one call.  Arguments mean what they mean in
+ * decode_step and sparse_mqa_attend_fused (out, the fp32 output, is optional;
+ * out_fp8 and out_scale are required); the workspace is
+ * smqa_decode_step_workspace_size() bytes; the limits are those of both.
+ */
+int decode_step_fused(const smqa_layout* L,
+                      const uint8_t* q_fp8, const float* w,
+                      const uint8_t* k_fp8, const float* k_scale,
+                      const int32_t* cand, int32_t n_cand,
+                      int32_t Hi, int32_t Di,
+                      const uint16_t* q_bf16,
+                      const float* rope_cos, const float* rope_sin, int32_t rope_pairs,
+                      const uint8_t* kv_codes, const uint8_t* kv_e8m0, const float* kv_rowscale,
+                      const uint8_t* swa_fp8, const float* swa_scale,
+                      const int32_t* swa_pos0, const int32_t* swa_clip,
+                      int32_t W, int32_t Hq, int32_t D, float sm_scale,
+                      int32_t k,
+                      uint8_t* out_fp8, float* out_scale, float* out, float* lse, int32_t* idx_out,
+                      void* workspace, size_t workspace_bytes,
+                      void* stream);
 
 /* Workspace sizes in bytes (host-only arithmetic, no HIP call).  A NULL or
  * inconsistent layout returns 0 and sets smqa_last_error(). */

@@ -29,6 +29,7 @@ def test_header_declares_the_boundary():
     names = declared_functions()
     for n in ("sparse_mqa_score", "topk_select", "sparse_mqa_attend", "sparse_mqa_attend_fp8kv",
               "sparse_mqa_attend_nvfp4", "sparse_mqa_attend_fused", "smqa_attend_fused_workspace_size",
+              "decode_step_fused",
               "decode_step",
               "smqa_topk_workspace_size", "smqa_attend_workspace_size",
               "smqa_decode_step_workspace_size", "smqa_last_error", "smqa_version"):
@@ -195,8 +196,11 @@ def test_attend_fused_validation():
     need = lib().smqa_attend_fused_workspace_size(ctypes.byref(L), 2048, 128, 64, 1664)
     assert need > 0
     assert attend_fused(L) == -5
-    # one query per 32-head group pair still needs the partials: never 0
-    assert lib().smqa_attend_fused_workspace_size(ctypes.byref(layout(T=64, B=64)), 64, 16, 64, 128) > 0
+    # one split quantises in the attention kernel: the workspace is the plain call's
+    for T, kk, W in ((1, 2048, 128), (64, 64, 16), (512, 2048, 128)):
+        Lx = layout(T=T, B=T)
+        assert (lib().smqa_attend_fused_workspace_size(ctypes.byref(Lx), kk, W, 64, 1664) ==
+                lib().smqa_attend_workspace_size(ctypes.byref(Lx), kk, W, 64, 1664))
     assert attend_fused(layout(T=0)) == 0
 
 

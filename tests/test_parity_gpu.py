@@ -507,6 +507,38 @@ def test_decode_step(lib, name, kw):
 
 # Long single-query rows: the streaming score kernel also builds the top-k's first-digit
 # histogram, and the top-k skips its own histogram pass.
+# decode_step with MegaAttention's fused attention: several splits (one decode query) and
+# one split (a 128-query replay chunk, quantised inside the attention kernel).
+@pytest.mark.parametrize("name,kw", [
+    ("decode_8k", dict(lengths=6000)),
+    ("replay_h100k", dict(B=1, lengths=3000, replay=(3000, 128))),
+])
+def test_decode_step_fused(lib, name, kw):
+    wl = gen(name, **kw)
+    c, s_ = _angles(wl.T, 32, seed=wl.T)
+    L = lib.Batch(wl.seq_start, wl.q_start, wl.q_pos, wl.max_ctx)
+    announce(f"decode_step_fused {wl.name} T={wl.T}")
+    o8, osc, out, lse, idx = lib.decode_step_fused(L, wl.qI, wl.w, wl.kI, wl.kscale, wl.cand, wl.q, c, s_,
+                                                   wl.kv_codes, wl.kv_e8m0, wl.kv_rowscale, wl.swa,
+                                                   wl.swa_scale, wl.swa_pos0, wl.swa_clip, wl.k, wl.sm_scale)
+    _, _, idx_plain = gpu_decode(lib, wl)
+    sync()
+    assert torch.equal(idx, idx_plain)                 # the same selection as the plain step
+    a = np_inputs(wl)
+    idx_g = idx.cpu().numpy()
+    S_ref = oracle_scores_for(a, [0], a["cand"])
+    ok, msg = topk_set_ok(S_ref[0], None, wl.k, idx_g[0])
+    assert ok, msg
+    Oi, Lr, _, _ = ref.attend_fused(a["q"], c.cpu().numpy(), s_.cpu().numpy(), a["kv_codes"], a["kv_e8m0"],
+                                    a["kv_rowscale"], idx_g, a["swa"], a["swa_scale"], a["swa_pos0"],
+                                    a["swa_clip"], a["seq_start"], a["q_start"], a["q_pos"], a["W"],
+                                    a["sm_scale"])
+    ok, msg = close_attention(out.cpu().numpy(), Oi, lse.cpu().numpy(), Lr)
+    assert ok, msg
+    codes, scale = ref.fp8_quantize(out.cpu().numpy())
+    assert np.array_equal(o8.cpu().numpy(), codes) and np.array_equal(osc.cpu().numpy(), scale)
+
+
 def _with_queries(wl, q_start, q_pos):
     import dataclasses
     qs = torch.tensor(q_start, dtype=torch.int32, device=DEV)
