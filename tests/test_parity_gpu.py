@@ -631,3 +631,49 @@ def test_decode_step_graph_replay(lib, name, kw):
         assert torch.equal(idx, ref_idx), f"replay {r}: idx"
         assert torch.equal(out, ref_out), f"replay {r}: out"
         assert torch.equal(lse, ref_lse), f"replay {r}: lse"
+
+
+@pytest.mark.parametrize("name,kw", [
+    ("decode_8k", dict(lengths=5000)),                                    # several splits
+    ("replay_h100k", dict(B=1, lengths=3000, replay=(3000, 128))),        # one split
+])
+def test_decode_step_fused_graph_replay(lib, name, kw):
+    """The fused decode step captured into a HIP graph: three replays, with eager work and a
+    cleared workspace and outputs between them, each equal to the eager call bit for bit."""
+    wl = gen(name, **kw)
+    announce(f"decode_step_fused graph replay {name}")
+    L = lib.Batch(wl.seq_start, wl.q_start, wl.q_pos, wl.max_ctx)
+    c, s_ = _angles(wl.T, 32, seed=11)
+    o8 = torch.empty((wl.T, wl.Hq, wl.D), dtype=torch.uint8, device=DEV)
+    osc = torch.empty((wl.T, wl.Hq), dtype=torch.float32, device=DEV)
+    lse = torch.empty((wl.T, wl.Hq), dtype=torch.float32, device=DEV)
+    idx = torch.empty((wl.T, wl.k), dtype=torch.int32, device=DEV)
+    ws = torch.empty(lib.decode_step_workspace_size(L, wl.k, 0, wl.W, wl.Hq, wl.D) + 256,
+                     dtype=torch.uint8, device=DEV)
+    step = lambda: lib.decode_step_fused(L, wl.qI, wl.w, wl.kI, wl.kscale, None, wl.q, c, s_, wl.kv_codes,
+                                         wl.kv_e8m0, wl.kv_rowscale, wl.swa, wl.swa_scale, wl.swa_pos0,
+                                         wl.swa_clip, wl.k, wl.sm_scale, out_fp8=o8, out_scale=osc,
+                                         lse=lse, idx=idx, want_out=False, workspace=ws)
+    step()
+    sync()
+    ref8, refs, refl, refi = o8.clone(), osc.clone(), lse.clone(), idx.clone()
+    st = torch.cuda.Stream()
+    st.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(st):
+        step()
+    torch.cuda.current_stream().wait_stream(st)
+    sync()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    sync()
+    noise = torch.randn(1 << 20, device=DEV)
+    for r in range(3):
+        o8.zero_(); osc.zero_(); lse.zero_(); idx.zero_(); ws.zero_()
+        noise.mul_(1.0001)
+        sync()
+        g.replay()
+        sync()
+        assert torch.equal(idx, refi), f"replay {r}: idx"
+        assert torch.equal(o8, ref8) and torch.equal(osc, refs), f"replay {r}: fp8 output"
+        assert torch.equal(lse, refl), f"replay {r}: lse"
