@@ -413,6 +413,8 @@ def _angles(T, R, seed):
     ("decode_8k", dict(B=2, lengths=1500, Hq=32, D=128, k=256), 4),
     ("decode_8k", dict(B=2, lengths=(700, 1500), Hq=32, D=640, k=300), 0),
     ("replay_h100k", dict(B=2, lengths=4000, replay=(4000, 128)), 32),
+    ("decode_8k", dict(B=2, lengths=(900, 1800), Hq=96, D=512, k=300), 256),   # every dim rotary
+    ("replay_h100k", dict(B=1, lengths=2500, replay=(2500, 128), Hq=96, D=512, k=500), 64),
 ])
 def test_attend_fused(lib, name, kw, R):
     wl = synth.with_scales(gen(name, **kw))
