@@ -254,14 +254,18 @@ int sparse_mqa_attend_nvfp4(const smqa_layout* L,
  * output projection) over the FP4 (MX) cache of sparse_mqa_attend:
  *   q'      = q with the pairs (2i, 2i+1) of its last 2R dims (R = rope_pairs)
  *             rotated by query t's angle: (a, b) -> (a c - b s, a s + b c),
- *             c = rope_cos[t][i], s = rope_sin[t][i]; computed in fp32 and
- *             rounded to bf16 (nearest even) for the products
+ *             c = rope_cos[t][i], s = rope_sin[t][i], rounded to bf16 (nearest
+ *             even) for the products.  The rotation is evaluated in fp32 (one
+ *             fused multiply-add per output), so an exact value within fp32
+ *             rounding of a bf16 midpoint may take the neighbouring bf16 value.
  *   O       = sparse_mqa_attend(q', ...)
  *   O'      = O with the same pairs rotated back: (a, b) -> (a c + b s, -a s + b c)
  *   out_scale[t,h] = max_d |O'[t,h,d]| / 448,
- *   out_fp8[t,h,d] = E4M3(O'[t,h,d] * (448 / amax)) (fp32: one division per
- *             row, one product per element, nearest even; an all-zero row gives
- *             scale 0 and zero codes)
+ *   out_fp8[t,h,d] = E4M3(O'[t,h,d] * 448 / amax), nearest even (an all-zero
+ *             row gives scale 0 and zero codes).  Evaluated in fp32 as
+ *             O' * (448 / amax): one division per row, one product per element,
+ *             so a value within 2^-22 relative of a rounding midpoint may take
+ *             the neighbouring code.
  * so out_fp8 * out_scale approximates O' within E4M3's 2^-4 relative step.
  * rope_cos, rope_sin float [T][R], 16-byte aligned (may be NULL when R = 0);
  *             the angles of each query's position (frequencies, scaling and the

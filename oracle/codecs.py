@@ -79,11 +79,18 @@ def bf16(bits: np.ndarray) -> np.ndarray:
 
 
 def bf16_round(x: np.ndarray) -> np.ndarray:
-    """float values -> uint16 bfloat16 bits: to float32 (round to nearest even), then the top
-    16 bits rounded to nearest even (the two-step rounding an fp32 computation makes)."""
-    b = np.asarray(x, dtype=np.float64).astype(np.float32).view(np.uint32).astype(np.uint64)
-    r = (b + 0x7FFF + ((b >> 16) & 1)) >> 16
-    return r.astype(np.uint16)
+    """float values -> uint16 bfloat16 bits, rounded once to the nearest bfloat16 (ties to the
+    even significand).  bfloat16 keeps 8 significant bits: a value with binary exponent e
+    (2^(e-1) <= |x| < 2^e) lies on a grid of spacing 2^(e-8), and below the smallest normal
+    2^-126 on the subnormal grid of spacing 2^-133.  Scaling by a power of two is exact, so
+    the rounding is numpy's round-half-to-even on the integer grid.  Overflow gives inf."""
+    x = np.asarray(x, dtype=np.float64)
+    _, e = np.frexp(x)
+    q = np.maximum(e.astype(np.int64) - 8, -133)
+    y = np.ldexp(np.round(np.ldexp(x, -q)), q)
+    with np.errstate(over="ignore"):
+        f = y.astype(np.float32)          # exact: y has at most 8 significant bits
+    return (f.view(np.uint32) >> 16).astype(np.uint16)
 
 
 _E4M3_POS = np.array([_e4m3_value(c) for c in range(0x7F)], dtype=np.float64)   # 0x00..0x7E

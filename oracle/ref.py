@@ -29,10 +29,10 @@ Readings where the pages are silent (each restated where it is used):
       scale (the pages name the format only)
   R16 fused RoPE: the last 2R latent dims rotate in consecutive pairs by
       per-query angles the caller gives as cos / sin; the rotated query is
-      rounded to bf16 before the products, the rotation evaluated in float32
-      with one fused multiply-add per output (the precision of the decision)
-  R17 FP8 output: per (query, head) row, scale = amax / 448, E4M3 codes of
-      x * (448 / amax) rounded to nearest even, in float32
+      rounded once to bf16 (nearest even) before the products
+  R17 FP8 output: per (query, head) row, scale = amax / 448 and codes =
+      E4M3(x * 448 / amax), nearest even, saturating at 448 (an all-zero row:
+      scale 0, codes 0)
 """
 from __future__ import annotations
 
@@ -241,44 +241,26 @@ def rope_rotate(x, rope_cos, rope_sin, inverse=False):
     return x
 
 
-def _fma32(a, b, c):
-    """float32 fused multiply-add: a * b is exact in float64 (24 + 24 bits), the sum is
-    rounded once more to float64 and then to float32 (a double rounding only where the
-    float64 sum itself rounds, which needs an exponent gap of about 30)."""
-    return (a.astype(np.float64) * b.astype(np.float64) + c.astype(np.float64)).astype(np.float32)
-
-
-def rope_query_bf16(q, rope_cos, rope_sin):
-    """The rotated query as the attention's bf16 operand (reading R16): the rounding to bf16
-    decides a code, so the rotation is evaluated in the precision the kernel uses for it,
-    a' = fma(a, c, -fl(b s)) and b' = fma(a, s, fl(b c)) in float32, then rounded to bf16
-    (nearest even).  q uint16 bf16 bits [T, Hq, D] -> uint16 bits."""
-    R = np.asarray(rope_cos).shape[-1]
-    if R == 0:
+def rope_query(q, rope_cos, rope_sin):
+    """The rotated query as the attention's bf16 operand (reading R16): the pairs of the last
+    2R dims rotated in float64 by `rope_rotate`, then rounded once to bf16 (nearest even).
+    q uint16 bf16 bits [T, Hq, D] -> uint16 bits."""
+    if np.asarray(rope_cos).shape[-1] == 0:
         return np.asarray(q).copy()
-    x = codecs.bf16(q).astype(np.float32)
-    D = x.shape[-1]
-    c = np.asarray(rope_cos, dtype=np.float32)[:, None, :]
-    s = np.asarray(rope_sin, dtype=np.float32)[:, None, :]
-    a, b = x[..., D - 2 * R::2], x[..., D - 2 * R + 1::2]
-    y = x.copy()
-    y[..., D - 2 * R::2] = _fma32(a, c, -(b * s))
-    y[..., D - 2 * R + 1::2] = _fma32(a, s, b * c)
-    return codecs.bf16_round(y)
+    return codecs.bf16_round(rope_rotate(codecs.bf16(q), rope_cos, rope_sin))
 
 
 def fp8_quantize(x):
-    """Per row (last axis) of float32 values: scale = amax / 448 (the dequantisation factor)
-    and codes = E4M3(x * r) with r = 448 / amax, every operation in float32 (reading R17);
-    an all-zero row gives scale 0 and zero codes."""
-    x = np.asarray(x, dtype=np.float32)
+    """Per row (last axis): scale = amax / 448, the factor that maps the codes back, and
+    codes = E4M3(x * 448 / amax), nearest even, saturating at 448 (reading R17), evaluated in
+    float64; an all-zero row gives scale 0 and zero codes.  Returns (codes uint8, scale
+    float64)."""
+    x = np.asarray(x, dtype=np.float64)
     amax = np.abs(x).max(axis=-1)
-    scale = (amax / np.float32(448.0)).astype(np.float32)
-    safe = np.where(amax > 0, amax, np.float32(1.0)).astype(np.float32)
-    r = (np.float32(448.0) / safe).astype(np.float32)
-    y = (x * r[..., None]).astype(np.float32)
-    codes = codecs.e4m3_encode(y)
-    codes = np.where((scale > 0)[..., None], codes, np.uint8(0)).astype(np.uint8)
+    scale = amax / 448.0
+    safe = np.where(amax > 0, amax, 1.0)
+    codes = codecs.e4m3_encode(x * 448.0 / safe[..., None])
+    codes = np.where((amax > 0)[..., None], codes, np.uint8(0)).astype(np.uint8)
     return codes, scale
 
 
@@ -288,16 +270,16 @@ def attend_fused(q, rope_cos, rope_sin, kv_codes, kv_e8m0, kv_rowscale, idx, swa
     inverse RoPE on the output and FP8 conversion of the result for the output projection.
 
     q is the unrotated bf16 query; its last 2R dims are rotated by query t's angles and the
-    result is rounded to bf16 (`rope_query_bf16`, reading R16); O is then
-    `attend`'s output, rotated back by the same angles (float64), and quantised per
-    (t, h) row by `fp8_quantize` of its float32 value.
+    result is rounded to bf16 (`rope_query`, reading R16); O is then `attend`'s output,
+    rotated back by the same angles, and quantised per (t, h) row by `fp8_quantize`
+    (reading R17), everything in float64.
     Returns (O_rot float64 [T, Hq, D], LSE [T, Hq], codes uint8 [T, Hq, D], scale [T, Hq]).
     """
-    qr = rope_query_bf16(q, rope_cos, rope_sin)
+    qr = rope_query(q, rope_cos, rope_sin)
     O, LSE = attend(qr, kv_codes, kv_e8m0, kv_rowscale, idx, swa, swa_scale, swa_pos0, swa_clip,
                     seq_start, q_start, q_pos, W, sm_scale)
     Oi = rope_rotate(O, rope_cos, rope_sin, inverse=True)
-    codes, scale = fp8_quantize(Oi.astype(np.float32))
+    codes, scale = fp8_quantize(Oi)
     return Oi, LSE, codes, scale
 
 

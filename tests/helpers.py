@@ -174,6 +174,80 @@ def close_scores(S_gpu, S_ref, rtol=1e-4, floor=1e-7):
     return bool((err <= tol).all()), f"max err {err.max():.3e}, worst ratio {(err / tol).max():.3f}"
 
 
+def _e4m3_half_step(y):
+    """Half the spacing of the E4M3 grid at magnitude |y| <= 448: 2^(E-4) in the binade
+    [2^E, 2^(E+1)) (3 mantissa bits), 2^-10 on the subnormal grid below 2^-6."""
+    _, e = np.frexp(np.maximum(np.abs(y), 2.0 ** -6))       # |y| in [2^(e-1), 2^e)
+    return np.ldexp(1.0, e.astype(np.int64) - 5)
+
+
+def fp8_output_ok(codes_gpu, scale_gpu, O_ref, err):
+    """The fused attention's FP8 output against the oracle's own float64 O' (reading R17:
+    scale = amax / 448, codes = E4M3(x * 448 / amax), nearest even).
+
+    err[t, h] bounds max_d |x_gpu - x_ref| of the output the GPU quantised (the attention
+    tolerance, or the error measured on its fp32 output).  Then |amax_gpu - amax_ref| <= err
+    too, and the GPU's pre-rounding value y_gpu = x_gpu * 448 / amax_gpu (plus its fp32
+    rounding, < 2^-21 relative) lies within
+        delta = 448 * err * (amax + |x|) / (amax * (amax - err)) + 2^-21 |y|
+    of the oracle's y = x_ref * 448 / amax_ref.  So every code must lie between
+    E4M3(y - delta) and E4M3(y + delta): equal to the oracle's code except where y sits within
+    delta of a rounding midpoint, where the neighbouring code is allowed as well.  Also
+    |scale_gpu - scale_ref| <= err / 448 (+ one fp32 rounding) and the dequantised output
+    codes * scale stays within half an E4M3 step (plus delta) of O' and err.
+    Returns (ok, message)."""
+    from oracle import codecs
+    O_ref = np.asarray(O_ref, dtype=np.float64)
+    c = np.asarray(codes_gpu, dtype=np.uint8)
+    sg = np.asarray(scale_gpu, dtype=np.float64)
+    err = np.broadcast_to(np.asarray(err, dtype=np.float64), O_ref.shape[:-1])
+    amax = np.abs(O_ref).max(axis=-1)
+    scale_ref = amax / 448.0
+    ds = np.abs(sg - scale_ref)
+    ok_s = ds <= err / 448.0 + 2.0 ** -23 * scale_ref
+    live = amax > err                                 # rows whose amax the bound pins
+    safe = np.where(live, amax, 1.0)[..., None]
+    e3 = err[..., None]
+    y = O_ref * 448.0 / safe
+    delta = 448.0 * e3 * (safe + np.abs(O_ref)) / (safe * (safe - np.where(live[..., None], e3, 0.0)))
+    delta = delta + 2.0 ** -21 * np.abs(y)
+    lo = codecs.e4m3(codecs.e4m3_encode(y - delta))
+    hi = codecs.e4m3(codecs.e4m3_encode(y + delta))
+    v = codecs.e4m3(c)
+    ok_c = np.where(live[..., None], (v >= lo) & (v <= hi), True)
+    # a row the bound cannot pin (amax <= err): its codes only have to dequantise near O'
+    deq = v * sg[..., None]
+    bound = (_e4m3_half_step(np.abs(y) + delta) + delta) * scale_ref[..., None] * (1 + 2.0 ** -20) + e3
+    ok_d = np.abs(deq - O_ref) <= bound + 1e-30
+    ok = bool(ok_s.all() and ok_c.all() and ok_d.all())
+    exact = codecs.e4m3_encode(y)
+    n_amb = int((live[..., None] & (lo != hi)).sum())
+    n_diff = int((live[..., None] & (codecs.e4m3(exact) != v)).sum())
+    msg = (f"scale max|d|={ds.max():.3e}, codes outside band={int((~ok_c).sum())}, "
+           f"dequant outside bound={int((~ok_d).sum())}, codes != oracle's={n_diff} "
+           f"(ambiguous {n_amb} of {v.size})")
+    return ok, msg
+
+
+def fp8_output_checks(codes_gpu, scale_gpu, O_ref, out_gpu=None, atol=2e-3, rtol=1e-3):
+    """fp8_output_ok with err = the attention tolerance (the contract), then, when the GPU's
+    fp32 output is available, with err = its measured error (tight), and the oracle's
+    quantiser applied to that fp32 output with err = 0 (only the kernel's fp32 rounding)."""
+    O_ref = np.asarray(O_ref, dtype=np.float64)
+    amax = np.abs(O_ref).max(axis=-1)
+    ok, msg = fp8_output_ok(codes_gpu, scale_gpu, O_ref, np.minimum(atol, rtol * amax))
+    assert ok, f"against O' with the tolerance band: {msg}"
+    if out_gpu is None:
+        return msg
+    x = np.asarray(out_gpu, dtype=np.float64)
+    meas = np.abs(x - O_ref).max(axis=-1) * (1 + 1e-6) + 1e-12 * amax
+    ok, msg2 = fp8_output_ok(codes_gpu, scale_gpu, O_ref, meas)
+    assert ok, f"against O' with the measured-error band: {msg2}"
+    ok, msg3 = fp8_output_ok(codes_gpu, scale_gpu, x, np.zeros_like(amax))
+    assert ok, f"against the quantiser on the GPU's own fp32 output: {msg3}"
+    return msg2
+
+
 def fsum(xs):
     return math.fsum(xs)
 

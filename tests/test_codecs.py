@@ -167,6 +167,14 @@ def test_e4m3_encoder_matches_torch_cast():
 def test_bf16_round_matches_torch():
     rng = np.random.default_rng(8)
     x = rng.standard_normal(100_000) * 10.0 ** rng.integers(-5, 5, 100_000)
-    mine = codecs.bf16_round(x)
-    ref = torch.tensor(x.astype(np.float32)).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    x32 = x.astype(np.float32)
+    mine = codecs.bf16_round(x32)
+    ref = torch.tensor(x32).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
     assert np.array_equal(mine, ref)
+    # one rounding from float64, not two: 1 + 2^-8 + 2^-30 lies just above the midpoint
+    # between 1 (0x3F80) and 1 + 2^-7 (0x3F81), so it rounds up; going through float32 first
+    # would land exactly on the midpoint and round to the even 0x3F80.  The midpoint itself
+    # goes to the even pattern; subnormals round on the 2^-133 grid.
+    assert codecs.bf16_round(np.array([1 + 2.0 ** -8 + 2.0 ** -30, 1 + 2.0 ** -8,
+                                       1 + 3 * 2.0 ** -8, 1.5 * 2.0 ** -133, -0.0])).tolist() == \
+        [0x3F81, 0x3F80, 0x3F82, 0x0002, 0x8000]

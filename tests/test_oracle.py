@@ -9,6 +9,7 @@ linearity, window clipping).
 import json
 import math
 import os
+from fractions import Fraction
 
 import numpy as np
 import pytest
@@ -405,21 +406,45 @@ def test_rope_closed_forms():
     assert np.allclose(n1, n0 * k, rtol=1e-13)
 
 
-def test_rope_query_bf16_agrees_with_the_float64_rotation():
-    """The float32 rotation rounded to bf16 is the float64 rotation rounded to bf16 except
-    where the float64 value lies within a few float32 ulps of a bf16 rounding midpoint;
-    with angle 0 it is the query itself, and with 90 degrees the exact swap."""
+def _bf16_nearest_exact(x: Fraction) -> int:
+    """Brute force: the bfloat16 bit pattern nearest to the exact rational x (ties to the even
+    pattern), searched among the neighbours of x's float32 rounding with exact distances."""
+    import struct
+    f = struct.unpack("<I", struct.pack("<f", float(x)))[0] >> 16
+    best = None
+    for bits in (f - 1, f, f + 1):
+        bits &= 0xFFFF
+        v = brute.bf16_scalar(bits)
+        if not math.isfinite(v):
+            continue
+        key = (abs(Fraction(v) - x), bits & 1)
+        if best is None or key < best[0]:
+            best = (key, bits)
+    return best[1]
+
+
+def test_rope_query_is_the_exact_rotation_rounded_once():
+    """Every rotated dim equals the exact rational rotation a c - b s / a s + b c of the bf16
+    query by the float32 angles, rounded once to the nearest bf16 (brute force with exact
+    fractions); the other dims are untouched; angle 0 gives the query itself and 90 degrees
+    the exact swap."""
     wl = tiny(9, lengths=40)
     a = np_inputs(wl)
-    c, s_ = _angles(a["T"], 8, seed=9)
-    got = ref.rope_query_bf16(a["q"], c, s_)
-    exact = codecs.bf16_round(ref.rope_rotate(codecs.bf16(a["q"]), c, s_))
-    assert (got != exact).mean() < 1e-3
-    assert np.all(np.abs(codecs.bf16(got) - codecs.bf16(exact)) <= 2.0 ** -7 * np.abs(codecs.bf16(exact)))
+    R, D = 8, a["D"]
+    c, s_ = _angles(a["T"], R, seed=9)
+    got = ref.rope_query(a["q"], c, s_)
+    assert np.array_equal(got[..., :D - 2 * R], a["q"][..., :D - 2 * R])
+    for t in range(a["T"]):
+        for h in range(0, a["Hq"], 5):
+            for i in range(R):
+                qa = Fraction(brute.bf16_scalar(a["q"][t, h, D - 2 * R + 2 * i]))
+                qb = Fraction(brute.bf16_scalar(a["q"][t, h, D - 2 * R + 2 * i + 1]))
+                ci, si = Fraction(float(c[t, i])), Fraction(float(s_[t, i]))
+                assert got[t, h, D - 2 * R + 2 * i] == _bf16_nearest_exact(qa * ci - qb * si)
+                assert got[t, h, D - 2 * R + 2 * i + 1] == _bf16_nearest_exact(qa * si + qb * ci)
     one, zero = np.ones_like(c), np.zeros_like(s_)
-    assert np.array_equal(ref.rope_query_bf16(a["q"], one, zero), a["q"])
-    sw = ref.rope_query_bf16(a["q"], zero, one)
-    D = a["D"]
+    assert np.array_equal(ref.rope_query(a["q"], one, zero), a["q"])
+    sw = ref.rope_query(a["q"], zero, one)
     assert np.array_equal(codecs.bf16(sw[..., D - 16::2]), -codecs.bf16(a["q"][..., D - 15::2]))
     assert np.array_equal(sw[..., D - 15::2], a["q"][..., D - 16::2])
 
@@ -439,6 +464,51 @@ def test_fp8_quantize_closed_forms():
     # E4M3 keeps 3 mantissa bits: normal values within 2^-4 relative, subnormals within
     # half their spacing 2^-9 * scale
     assert np.all(np.abs(deq - x) <= np.maximum(np.abs(x) * 2.0 ** -4, 2.0 ** -10 * scale[..., None]) + 1e-30)
+    # amax = 448 makes the scale 1 and the codes the plain E4M3 rounding: exact values stay,
+    # midpoints go to the even code (1.0625 -> 1.0 = 0x38, 1.1875 -> 1.25 = 0x3A), negative
+    # values keep their sign, the subnormal midpoint 2^-10 goes to zero
+    row = np.array([448.0, 1.0625, 1.1875, -3.25, 2.0 ** -10, -(2.0 ** -9) * 3, 447.0, 0.0])
+    codes, scale = ref.fp8_quantize(row)
+    assert scale == 1.0
+    assert codes.tolist() == [0x7E, 0x38, 0x3A, 0xC5, 0x00, 0x83, 0x7E, 0x00]
+    # scaling the row by a power of two scales the scale and keeps the codes
+    c2, s2 = ref.fp8_quantize(row * 2.0 ** -20)
+    assert np.array_equal(c2, codes) and s2 == 2.0 ** -20
+    # a row that is not a power of two: x * 448 / amax in exact arithmetic (1/3 of the amax
+    # maps to 149.33.., between the codes 144 (0x71) and 160 -> 144; -1.5 maps to -224 = 0xF6)
+    c3, s3 = ref.fp8_quantize(np.array([3.0, 1.0, -1.5]))
+    assert s3 == 3.0 / 448.0 and c3.tolist() == [0x7E, 0x71, 0xF6]
+
+
+def test_fp8_output_comparator_catches_planted_mistakes():
+    """The fused output's comparator: the oracle's own codes pass with a zero error band; a
+    code moved by one step away from a midpoint, a wrong scale, or codes of a different row
+    fail; with a measured error band a code at an ambiguous midpoint may take either
+    neighbour but no other."""
+    from helpers import fp8_output_ok
+    rng = np.random.default_rng(4)
+    O = rng.standard_normal((2, 3, 96))
+    codes, scale = ref.fp8_quantize(O)
+    zero = np.zeros(O.shape[:-1])
+    assert fp8_output_ok(codes, scale, O, zero)[0]
+    bad = codes.copy()
+    y = O * 448.0 / np.abs(O).max(axis=-1, keepdims=True)
+    far = np.argmax((np.abs(y[0, 0]) > 20) & (np.abs(y[0, 0]) < 200))
+    bad[0, 0, far] = bad[0, 0, far] + 1                      # next magnitude: one step off
+    assert not fp8_output_ok(bad, scale, O, zero)[0]
+    assert not fp8_output_ok(codes, scale * 1.01, O, zero)[0]
+    assert not fp8_output_ok(codes[:, ::-1], scale, O, zero)[0]
+    # put one element exactly on a midpoint: 1.0625 * amax / 448 -> either 0x38 or 0x39
+    # passes once the band is nonzero, 0x3A does not
+    O2 = O.copy()
+    amax = np.abs(O2[1, 2]).max()
+    O2[1, 2, 5] = 1.0625 * amax / 448.0
+    c2, s2 = ref.fp8_quantize(O2)
+    eps = np.full(O.shape[:-1], 1e-9)
+    for code, want in ((0x38, True), (0x39, True), (0x3A, False)):
+        c = c2.copy()
+        c[1, 2, 5] = code
+        assert fp8_output_ok(c, s2, O2, eps)[0] is want, code
 
 
 def test_attend_fused_without_rope_is_attend_then_quantise():
@@ -452,7 +522,7 @@ def test_attend_fused_without_rope_is_attend_then_quantise():
                                             idx, a["swa"], a["swa_scale"], a["swa_pos0"], a["swa_clip"],
                                             a["seq_start"], a["q_start"], a["q_pos"], a["W"], a["sm_scale"])
     assert np.array_equal(Of, O) and np.array_equal(Lf, L)
-    c2, s2 = ref.fp8_quantize(O.astype(np.float32))
+    c2, s2 = ref.fp8_quantize(O)
     assert np.array_equal(codes, c2) and np.array_equal(scale, s2)
 
 

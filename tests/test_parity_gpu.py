@@ -13,8 +13,8 @@ import torch
 
 import synth
 from oracle import ref
-from helpers import (announce, close_attention, close_scores, gpu_attend, gpu_attend_fp8kv,
-                     gpu_attend_fused, gpu_attend_nvfp4, gpu_decode, gpu_score,
+from helpers import (announce, close_attention, close_scores, fp8_output_checks, gpu_attend,
+                     gpu_attend_fp8kv, gpu_attend_fused, gpu_attend_nvfp4, gpu_decode, gpu_score,
                      gpu_topk, np_inputs, oracle_attend_for, oracle_scores_for, q_seq_of, topk_set_ok)
 
 pytestmark = pytest.mark.gpu
@@ -405,8 +405,10 @@ def _angles(T, R, seed):
 
 
 # The rotary part of DeepSeek-style latents (64 dims) and a short one, on whole and partial
-# tiles, one and several splits, the clipped replay window; the FP8 codes and scales must
-# equal the oracle's quantiser applied to the GPU's own fp32 output, bit for bit.
+# tiles, one and several splits, the clipped replay window.  The FP8 codes and scales are
+# checked against the oracle's own O' (equal codes except where the oracle's pre-rounding
+# value lies within the error band of an E4M3 rounding midpoint), and the oracle's quantiser
+# applied to the GPU's own fp32 output must reproduce them up to the kernel's fp32 rounding.
 @pytest.mark.parametrize("name,kw,R", [
     ("decode_8k", dict(lengths=6000), 32),
     ("decode_8k", dict(B=3, lengths=(300, 2000), k=1000, W=100), 32),
@@ -432,10 +434,7 @@ def test_attend_fused(lib, name, kw, R):
                                    a["sm_scale"])
     ok, msg = close_attention(out.cpu().numpy(), Oi, lse.cpu().numpy(), L)
     assert ok, msg
-    codes, scale = ref.fp8_quantize(out.cpu().numpy())
-    assert np.array_equal(osc.cpu().numpy(), scale)
-    bad = np.nonzero(o8.cpu().numpy() != codes)
-    assert bad[0].size == 0, f"{bad[0].size} codes differ, e.g. {o8.cpu().numpy()[bad][:4]} vs {codes[bad][:4]}"
+    print(fp8_output_checks(o8.cpu().numpy(), osc.cpu().numpy(), Oi, out.cpu().numpy()))
     # without the fp32 output the codes are the same
     o8b, oscb, outb, _ = gpu_attend_fused(lib, wl, idx, c if R else None, s_ if R else None, want_out=False)
     sync()
@@ -464,8 +463,7 @@ def test_attend_fused_zero_rows_and_window_only(lib):
                                    a["sm_scale"])
     ok, msg = close_attention(out.cpu().numpy(), Oi, lse.cpu().numpy(), L)
     assert ok, msg
-    codes, scale = ref.fp8_quantize(out.cpu().numpy())
-    assert np.array_equal(o8.cpu().numpy(), codes) and np.array_equal(osc.cpu().numpy(), scale)
+    fp8_output_checks(o8.cpu().numpy(), osc.cpu().numpy(), Oi, out.cpu().numpy())
 
 
 def test_attend_nvfp4_small_tensor_scale(lib):
@@ -537,8 +535,7 @@ def test_decode_step_fused(lib, name, kw):
                                     a["sm_scale"])
     ok, msg = close_attention(out.cpu().numpy(), Oi, lse.cpu().numpy(), Lr)
     assert ok, msg
-    codes, scale = ref.fp8_quantize(out.cpu().numpy())
-    assert np.array_equal(o8.cpu().numpy(), codes) and np.array_equal(osc.cpu().numpy(), scale)
+    fp8_output_checks(o8.cpu().numpy(), osc.cpu().numpy(), Oi, out.cpu().numpy())
 
 
 def _with_queries(wl, q_start, q_pos):
