@@ -50,7 +50,7 @@ _LP = ctypes.POINTER(Layout)
 
 _SIGS = {
     "sparse_mqa_score": (_I, [_LP, _P, _P, _P, _P, _P, _I, _I, _I, _P, _L, _P]),
-    "topk_select": (_I, [_LP, _P, _L, _P, _I, _I, _P, _P, _S, _P]),
+    "topk_select": (_I, [_LP, _P, _L, _P, _I, _I, _P, _P, _P, _S, _P]),
     "sparse_mqa_attend": (_I, [_LP, _P, _P, _P, _P, _P, _I, _P, _P, _P, _P, _I, _I, _I, _F,
                                _P, _P, _P, _S, _P]),
     "sparse_mqa_attend_fp8kv": (_I, [_LP, _P, _P, _P, _P, _I, _P, _P, _P, _P, _I, _I, _I, _F,
@@ -67,6 +67,7 @@ _SIGS = {
     "smqa_topk_workspace_size": (_S, [_LP, _I, _I]),
     "smqa_attend_workspace_size": (_S, [_LP, _I, _I, _I, _I]),
     "smqa_decode_step_workspace_size": (_S, [_LP, _I, _I, _I, _I, _I]),
+    "smqa_attend_plan": (_I, [_LP, _I, _I, _I, _I, _P, _P]),
     "smqa_last_error": (ctypes.c_char_p, []),
     "smqa_version": (ctypes.c_char_p, []),
 }
@@ -178,8 +179,10 @@ def sparse_mqa_score(L: Batch, q_fp8, w, k_fp8, k_scale=None, cand=None, scores=
     return scores
 
 
-def topk_select(L: Batch, scores, k: int, cand=None, idx=None, workspace=None, stream=None):
-    """Top-k positions -> int32 [T, k], ascending, -1 padded."""
+def topk_select(L: Batch, scores, k: int, cand=None, idx=None, workspace=None, stream=None,
+                val=None, want_val=False):
+    """Top-k positions -> int32 [T, k], ascending, -1 padded; with want_val (or val given)
+    also their scores -> (idx, val float32 [T, k], -inf padded)."""
     lib = load()
     _dev(scores, "scores", torch.float32, 2)
     _dev(cand, "cand", torch.int32, 2)
@@ -187,13 +190,16 @@ def topk_select(L: Batch, scores, k: int, cand=None, idx=None, workspace=None, s
     if idx is None:
         idx = torch.empty((L.T, k), dtype=torch.int32, device=scores.device)
     _dev(idx, "idx", torch.int32, 2)
+    if want_val and val is None:
+        val = torch.empty((L.T, k), dtype=torch.float32, device=scores.device)
+    _dev(val, "val", torch.float32, 2)
     need = lib.smqa_topk_workspace_size(L.ref, k, n_cand)
     if workspace is None:
         workspace = _workspace(need, scores.device)
     wp, wb = _ws_ptr(workspace)
     _check(lib.topk_select(L.ref, _ptr(scores), scores.shape[1], _ptr(cand), n_cand, k, _ptr(idx),
-                           wp, wb, _stream(stream)))
-    return idx
+                           _ptr(val), wp, wb, _stream(stream)))
+    return (idx, val) if val is not None else idx
 
 
 def sparse_mqa_attend(L: Batch, q, kv_codes, kv_e8m0, kv_rowscale, idx, swa, swa_scale, swa_pos0,

@@ -77,7 +77,7 @@ int check_score(const smqa_layout* L, const uint8_t* q_fp8, const float* w, cons
 }
 
 int check_topk(const smqa_layout* L, const float* scores, int64_t ld, const int32_t* cand,
-               int32_t n_cand, int32_t k, const int32_t* idx) {
+               int32_t n_cand, int32_t k, const int32_t* idx, const float* val) {
   REQUIRE_PTR(scores);
   REQUIRE_PTR(idx);
   if (k < 1 || k > 4096) return fail(SMQA_ERR_UNSUPPORTED, "k = %d: supported 1..4096", k);
@@ -90,6 +90,7 @@ int check_topk(const smqa_layout* L, const float* scores, int64_t ld, const int3
   REQUIRE_ALIGN(scores, 4);
   REQUIRE_ALIGN(cand, 4);
   REQUIRE_ALIGN(idx, 4);
+  REQUIRE_ALIGN(val, 4);
   return SMQA_OK;
 }
 
@@ -148,6 +149,18 @@ int check_fused(const float* rope_cos, const float* rope_sin, int32_t rope_pairs
   return SMQA_OK;
 }
 
+// The attention plan of a call: some shapes the limits accept need more LDS per workgroup
+// than a CU has at every split count (wide latents with large k over 16-head groups).
+int check_plan(const smqa_layout* L, int32_t k, int32_t W, int32_t Hq, int32_t D) {
+  int32_t lds = 0;
+  if (smqa::attend_splits(L->num_q, k, W, Hq, D, &lds) == 0)
+    return fail(SMQA_ERR_UNSUPPORTED,
+                "attention with T = %d, k = %d, W = %d, Hq = %d, D = %d needs %d bytes of LDS per "
+                "workgroup at every split count (%d available)",
+                L->num_q, k, W, Hq, D, lds, smqa::kLdsBytes);
+  return SMQA_OK;
+}
+
 int check_ws(void* ws, size_t have, size_t need) {
   if (need == 0) return SMQA_OK;
   if (!ws) return fail(SMQA_ERR_WORKSPACE, "workspace is NULL but %zu bytes are required", need);
@@ -192,19 +205,38 @@ size_t smqa_topk_workspace_size(const smqa_layout* L, int32_t k, int32_t n_cand)
 }
 
 size_t smqa_attend_workspace_size(const smqa_layout* L, int32_t k, int32_t W, int32_t Hq, int32_t D) {
-  if (check_layout(L) != SMQA_OK) return 0;
+  g_err.clear();
+  if (check_layout(L) != SMQA_OK || check_plan(L, k, W, Hq, D) != SMQA_OK) return 0;
   return smqa::attend_workspace_bytes(L->num_q, k, W, Hq, D);
+}
+
+int smqa_attend_plan(const smqa_layout* L, int32_t k, int32_t W, int32_t Hq, int32_t D, int32_t* splits,
+                     int32_t* lds_bytes) {
+  g_err.clear();
+  int st = check_layout(L);
+  if (st) return st;
+  if (D % 128 != 0 || D < 128 || D > 2048 || Hq % 16 != 0 || Hq < 16 || Hq > 128 || W < 1 || W > 128 ||
+      k < 1 || k > 4096)
+    return fail(SMQA_ERR_UNSUPPORTED, "attention shape outside the limits (k = %d, W = %d, Hq = %d, D = %d)",
+                k, W, Hq, D);
+  int32_t lds = 0;
+  const int32_t S = smqa::attend_splits(L->num_q, k, W, Hq, D, &lds);
+  if (splits) *splits = S;
+  if (lds_bytes) *lds_bytes = lds;
+  return check_plan(L, k, W, Hq, D);
 }
 
 size_t smqa_attend_fused_workspace_size(const smqa_layout* L, int32_t k, int32_t W, int32_t Hq,
                                         int32_t D) {
-  if (check_layout(L) != SMQA_OK) return 0;
+  g_err.clear();
+  if (check_layout(L) != SMQA_OK || check_plan(L, k, W, Hq, D) != SMQA_OK) return 0;
   return smqa::attend_fused_workspace_bytes(L->num_q, k, W, Hq, D);
 }
 
 size_t smqa_decode_step_workspace_size(const smqa_layout* L, int32_t k, int32_t n_cand, int32_t W,
                                        int32_t Hq, int32_t D) {
-  if (check_layout(L) != SMQA_OK) return 0;
+  g_err.clear();
+  if (check_layout(L) != SMQA_OK || check_plan(L, k, W, Hq, D) != SMQA_OK) return 0;
   return decode_ws_layout(L, k, n_cand > 0 ? n_cand : L->max_ctx, W, Hq, D).total;
 }
 
@@ -219,25 +251,25 @@ int sparse_mqa_score(const smqa_layout* L, const uint8_t* q_fp8, const float* w,
   if (st) return st;
   smqa::ScoreArgs a{L->seq_start, L->q_start, L->q_pos, L->num_seqs, L->num_q, L->max_ctx,
                     q_fp8, w, k_fp8, k_scale, cand, cand ? n_cand : 0, Hi, Di, scores, ld_scores,
-                    nullptr, nullptr, 0};
+                    nullptr, nullptr, 0, true};
   hipError_t e = smqa::launch_score(a, (hipStream_t)stream);
   return e == hipSuccess ? SMQA_OK : hip_fail(e, "sparse_mqa_score launch");
 }
 
 int topk_select(const smqa_layout* L, const float* scores, int64_t ld_scores, const int32_t* cand,
-                int32_t n_cand, int32_t k, int32_t* idx_out, void* workspace, size_t workspace_bytes,
-                void* stream) {
+                int32_t n_cand, int32_t k, int32_t* idx_out, float* val_out, void* workspace,
+                size_t workspace_bytes, void* stream) {
   g_err.clear();
   int st = check_layout(L);
   if (st) return st;
   if (L->num_q == 0) return SMQA_OK;
-  st = check_topk(L, scores, ld_scores, cand, n_cand, k, idx_out);
+  st = check_topk(L, scores, ld_scores, cand, n_cand, k, idx_out, val_out);
   if (st) return st;
   const int32_t cols = score_cols(L, n_cand, cand != nullptr);
   st = check_ws(workspace, workspace_bytes, smqa::topk_workspace_bytes(L->num_q, cols, k));
   if (st) return st;
   smqa::TopkArgs a{L->seq_start, L->q_start, L->q_pos, L->num_seqs, L->num_q, cols,
-                   scores, ld_scores, cand, cand ? n_cand : 0, k, idx_out, workspace};
+                   scores, ld_scores, cand, cand ? n_cand : 0, k, idx_out, workspace, val_out};
   hipError_t e = smqa::launch_topk(a, (hipStream_t)stream);
   return e == hipSuccess ? SMQA_OK : hip_fail(e, "topk_select launch");
 }
@@ -253,6 +285,8 @@ int sparse_mqa_attend(const smqa_layout* L, const uint16_t* q_bf16, const uint8_
   if (L->num_q == 0) return SMQA_OK;
   st = check_attend(q_bf16, kv_codes, kv_e8m0, kv_rowscale, idx, k, swa_fp8, swa_scale, swa_pos0,
                     swa_clip, W, Hq, D, sm_scale, out, lse, true);
+  if (st) return st;
+  st = check_plan(L, k, W, Hq, D);
   if (st) return st;
   st = check_ws(workspace, workspace_bytes, smqa::attend_workspace_bytes(L->num_q, k, W, Hq, D));
   if (st) return st;
@@ -276,6 +310,8 @@ int sparse_mqa_attend_fp8kv(const smqa_layout* L, const uint16_t* q_bf16, const 
   // kv_fp8 stands in for kv_codes and kv_e8m0 in the shared checks
   st = check_attend(q_bf16, kv_fp8, kv_fp8, kv_rowscale, idx, k, swa_fp8, swa_scale, swa_pos0,
                     swa_clip, W, Hq, D, sm_scale, out, lse, true);
+  if (st) return st;
+  st = check_plan(L, k, W, Hq, D);
   if (st) return st;
   if (Hq % 32 != 0 || D > 1664)
     return fail(SMQA_ERR_UNSUPPORTED, "FP8 global cache: Hq = %d, D = %d; supported Hq %% 32 == 0, D <= 1664",
@@ -301,6 +337,8 @@ int sparse_mqa_attend_nvfp4(const smqa_layout* L, const uint16_t* q_bf16, const 
   if (L->num_q == 0) return SMQA_OK;
   st = check_attend(q_bf16, kv_codes, kv_scales, kv_rowscale, idx, k, swa_fp8, swa_scale, swa_pos0,
                     swa_clip, W, Hq, D, sm_scale, out, lse, true);
+  if (st) return st;
+  st = check_plan(L, k, W, Hq, D);
   if (st) return st;
   if (Hq % 32 != 0 || D > 1664)
     return fail(SMQA_ERR_UNSUPPORTED, "NVFP4 global cache: Hq = %d, D = %d; supported Hq %% 32 == 0, D <= 1664",
@@ -333,6 +371,8 @@ int sparse_mqa_attend_fused(const smqa_layout* L, const uint16_t* q_bf16, const 
   // out is optional here: out_fp8 stands in for it in the shared checks
   st = check_attend(q_bf16, kv_codes, kv_e8m0, kv_rowscale, idx, k, swa_fp8, swa_scale, swa_pos0,
                     swa_clip, W, Hq, D, sm_scale, out ? out : (const float*)out_fp8, lse, true);
+  if (st) return st;
+  st = check_plan(L, k, W, Hq, D);
   if (st) return st;
   st = check_fused(rope_cos, rope_sin, rope_pairs, Hq, D, out_fp8, out_scale);
   if (st) return st;
@@ -380,6 +420,8 @@ int decode_step_impl(const smqa_layout* L, const uint8_t* q_fp8, const float* w,
   const float* out_chk = (fz && !out) ? (const float*)fz->out_fp8 : out;
   st = check_attend(q_bf16, kv_codes, kv_e8m0, kv_rowscale, idx_out, k, swa_fp8, swa_scale, swa_pos0,
                     swa_clip, W, Hq, D, sm_scale, out_chk, lse, false);
+  if (st) return st;
+  st = check_plan(L, k, W, Hq, D);
   if (st) return st;
   if (fz) {
     st = check_fused(fz->rope_cos, fz->rope_sin, fz->rope_pairs, Hq, D, fz->out_fp8, fz->out_scale);

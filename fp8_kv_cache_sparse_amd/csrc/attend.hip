@@ -1155,7 +1155,27 @@ static int max_tiles(int32_t k, int32_t W) {
 struct AttPlan {
   bool wide;
   int MT, ngroups, S;
+  int lds;                 // bytes per workgroup, static + dynamic
 };
+
+int sd_lds_bytes(int32_t D);   // attend_sd.hip: the dimension-split kernel's (fixed) LDS
+
+// LDS of one workgroup (static + dynamic) for a plan with S splits.  The positions of a
+// workgroup's tile range are staged whole, so the dynamic part shrinks as S grows.
+static size_t plan_lds(const AttPlan& p, int32_t k, int32_t W, int32_t D, int S) {
+  const size_t split_tiles = (size_t)(max_tiles(k, W) + S - 1) / S + 1;
+  if (p.wide && D <= 1664) return (size_t)sd_lds_bytes(D);
+  if (p.wide) {                                  // thr, D = 1792
+    return 2 * (size_t)thr::Geo<1792>::BUF + split_tiles * kGRows * 8 + (size_t)W * 4 +
+           sizeof(thr::AttSmem<2>);
+  }
+  const size_t buf = (std::max<size_t>((size_t)kGRows * (D / 2 + 16) + 4 * 64, (size_t)kWRows * (D + 16)) +
+                      15) & ~(size_t)15;
+  const size_t stat = p.MT == 2 ? sizeof(lat::AttSmem<2>) : sizeof(lat::AttSmem<1>);
+  return 2 * buf + (size_t)16 * p.MT * (2 * D + 16) + split_tiles * kGRows * 8 + (size_t)W * 4 + stat;
+}
+
+constexpr int kMaxSplits = 64;                   // the merge kernels take up to 64 partials
 
 static AttPlan attend_plan(int32_t T, int32_t k, int32_t W, int32_t Hq, int32_t D) {
   AttPlan p;
@@ -1172,17 +1192,23 @@ static AttPlan attend_plan(int32_t T, int32_t k, int32_t W, int32_t Hq, int32_t 
   int S = 1;
   if (base > 0 && base < 256) S = (int)((256 + base - 1) / base);
   S = std::min(S, std::max(1, ntiles / 3));
-  p.S = std::max(std::min(S, 32), 1);
+  S = std::max(std::min(S, 32), 1);
+  // then as many more splits as it takes for a workgroup's LDS to fit the CU's
+  while (S < kMaxSplits && plan_lds(p, k, W, D, S) > (size_t)kLdsBytes) ++S;
+  p.lds = (int)plan_lds(p, k, W, D, S);
+  p.S = p.lds <= kLdsBytes ? S : 0;
   return p;
 }
 
-int attend_splits(int32_t T, int32_t k, int32_t W, int32_t Hq, int32_t D) {
-  return attend_plan(T, k, W, Hq, D).S;
+int attend_splits(int32_t T, int32_t k, int32_t W, int32_t Hq, int32_t D, int32_t* lds) {
+  const AttPlan p = attend_plan(T, k, W, Hq, D);
+  if (lds) *lds = p.lds;
+  return p.S;
 }
 
 size_t attend_workspace_bytes(int32_t T, int32_t k, int32_t W, int32_t Hq, int32_t D) {
   const int S = attend_splits(T, k, W, Hq, D);
-  if (S == 1) return 0;
+  if (S <= 1) return 0;
   return (size_t)S * T * Hq * D * 4 + (size_t)S * T * Hq * 8;
 }
 
@@ -1195,15 +1221,6 @@ hipError_t launch_attend_merge(const AttendArgs& a, int S, hipStream_t s) {
   return hipGetLastError();
 }
 
-template <class K>
-static hipError_t allow_lds(K kernel, int static_bytes, bool& done) {
-  if (done) return hipSuccess;
-  hipError_t e = hipFuncSetAttribute((const void*)kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                     160 * 1024 - static_bytes);
-  if (e == hipSuccess) done = true;
-  return e;
-}
-
 template <int MT, int NS>
 static hipError_t launch_lat(const AttendArgs& a, const AttPlan& p, hipStream_t s) {
   const int total = a.T * p.ngroups * p.S;
@@ -1213,8 +1230,8 @@ static hipError_t launch_lat(const AttendArgs& a, const AttPlan& p, hipStream_t 
                                        (size_t)kWRows * (a.D + 16)) + 15) & ~(size_t)15;
   const size_t dyn = 2 * buf + (size_t)16 * MT * (2 * a.D + 16) + (size_t)split_tiles * kGRows * 8 +
                      (size_t)a.W * 4;
-  static bool attr = false;
-  hipError_t e = allow_lds(lat::attend_kernel<MT, NS>, (int)sizeof(lat::AttSmem<MT>), attr);
+  static PerDevice attr;
+  hipError_t e = allow_dynamic_lds(lat::attend_kernel<MT, NS>, kLdsBytes - (int)sizeof(lat::AttSmem<MT>), attr);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((lat::attend_kernel<MT, NS>), dim3(nb), dim3(lat::kAttThreads), dyn, s, a, p.S,
                      p.ngroups, total);
@@ -1231,8 +1248,8 @@ static hipError_t launch_thr(const AttendArgs& a, const AttPlan& p, hipStream_t 
     const int nb = (total + 7) / 8 * 8;
     const int split_tiles = (max_tiles(a.k, a.W) + p.S - 1) / p.S + 1;
     const size_t dyn = 2 * (size_t)thr::Geo<D>::BUF + (size_t)split_tiles * kGRows * 8 + (size_t)a.W * 4;
-    static bool attr = false;
-    hipError_t e = allow_lds(thr::attend_kernel<2, D>, (int)sizeof(thr::AttSmem<2>), attr);
+    static PerDevice attr;
+    hipError_t e = allow_dynamic_lds(thr::attend_kernel<2, D>, kLdsBytes - (int)sizeof(thr::AttSmem<2>), attr);
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL((thr::attend_kernel<2, D>), dim3(nb), dim3(thr::kAttThreads), dyn, s, a, p.S,
                        p.ngroups, total);
@@ -1255,7 +1272,7 @@ size_t attend_fused_workspace_bytes(int32_t T, int32_t k, int32_t W, int32_t Hq,
 hipError_t launch_attend_fused(const AttendArgs& a0, hipStream_t s) {
   if (a0.T == 0) return hipSuccess;
   const AttPlan p = attend_plan(a0.T, a0.k, a0.W, a0.Hq, a0.D);
-  if (!p.wide || a0.D > 1664 || a0.kv_fmt != kKvMX || !a0.out_fp8 || !a0.out_scale) return hipErrorInvalidValue;
+  if (p.S == 0 || !p.wide || a0.D > 1664 || a0.kv_fmt != kKvMX || !a0.out_fp8 || !a0.out_scale) return hipErrorInvalidValue;
   AttendArgs a = a0;
   // one split: the attention kernel's own epilogue rotates back and quantises; several:
   // partials, then the epilogue kernel
@@ -1274,13 +1291,14 @@ hipError_t launch_attend_fused(const AttendArgs& a0, hipStream_t s) {
 hipError_t launch_attend_fmt(const AttendArgs& a, hipStream_t s) {
   if (a.T == 0) return hipSuccess;
   const AttPlan p = attend_plan(a.T, a.k, a.W, a.Hq, a.D);
-  if (!p.wide || a.D > 1664 || (a.kv_fmt != kKvFP8 && a.kv_fmt != kKvNV)) return hipErrorInvalidValue;
+  if (p.S == 0 || !p.wide || a.D > 1664 || (a.kv_fmt != kKvFP8 && a.kv_fmt != kKvNV)) return hipErrorInvalidValue;
   return launch_attend_sd(a, p.S, s);
 }
 
 hipError_t launch_attend(const AttendArgs& a, hipStream_t s) {
   if (a.T == 0) return hipSuccess;
   const AttPlan p = attend_plan(a.T, a.k, a.W, a.Hq, a.D);
+  if (p.S == 0) return hipErrorInvalidValue;
   if (!p.wide) {
     if (a.D <= 1024) return p.MT == 2 ? launch_lat<2, 1>(a, p, s) : launch_lat<1, 1>(a, p, s);
     return launch_lat<1, 2>(a, p, s);

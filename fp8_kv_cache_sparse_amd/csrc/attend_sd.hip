@@ -52,6 +52,18 @@ hipError_t launch_attend_merge(const AttendArgs& a, int S, hipStream_t s);
 
 namespace sd {
 
+// fp64 -> bf16 bits, rounded once to the nearest bf16 (ties to even).  A normal bf16 keeps 8
+// significant bits, i.e. drops the low 45 of the fp64 significand: an integer
+// round-half-even at bit 45 (a carry moves into the exponent, as it should).  Below 2^-126
+// the bf16 grid is the subnormal one, spacing 2^-133.  The result is exact in fp32.
+__device__ __forceinline__ unsigned bf16_rne(double y) {
+  if (__builtin_fabs(y) < 0x1p-126) y = __builtin_rint(y * 0x1p133) * 0x1p-133;
+  unsigned long long u = (unsigned long long)__double_as_longlong(y);
+  u = (u + 0x0FFFFFFFFFFFull + ((u >> 45) & 1ull)) & ~0x1FFFFFFFFFFFull;
+  return __float_as_uint((float)__longlong_as_double((long long)u)) >> 16;
+}
+
+
 typedef float v16f __attribute__((ext_vector_type(16)));
 typedef int v2i __attribute__((ext_vector_type(2)));
 typedef _Float16 v2h __attribute__((ext_vector_type(2)));
@@ -421,7 +433,9 @@ __global__ __launch_bounds__(kThreads) void attend_kernel(AttendArgs a, int S, i
         if (i < G::BPW || wave < G::EXTRA) v = *(const v4u*)(qrow + 32 * (b0 + i) + 8 * cc);
         if constexpr (F == kMXF || F == kMXR) {
           // fused query RoPE (blog §Kernels, MegaAttention): the pairs (2j, 2j+1) of the last
-          // 2 * rope_pairs dims rotate by query t's angle in fp32, then round to bf16 (RNE)
+          // 2 * rope_pairs dims rotate by query t's angle, rounded once to bf16 (RNE).  In
+          // fp64 the products of a bf16 and an fp32 value are exact, so each output is the
+          // exact rotation rounded once to fp64 and then once to bf16.
           const int r0 = D - 2 * a.rope_pairs;
           const int d0 = 32 * (b0 + i) + 16 * kh + 8 * cc;
           if (a.rope_pairs > 0 && d0 >= r0 && (i < G::BPW || wave < G::EXTRA)) {
@@ -430,13 +444,11 @@ __global__ __launch_bounds__(kThreads) void attend_kernel(AttendArgs a, int S, i
             const v4f sn = *(const v4f*)(a.rope_sin + pj);
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-              const float x0 = __uint_as_float(v[j] << 16), x1 = __uint_as_float(v[j] & 0xFFFF0000u);
-              const float y0 = __builtin_fmaf(x0, cs[j], -(x1 * sn[j]));
-              const float y1 = __builtin_fmaf(x0, sn[j], x1 * cs[j]);
-              const unsigned b0r = __float_as_uint(y0), b1r = __float_as_uint(y1);
-              const unsigned h0 = (b0r + 0x7FFFu + ((b0r >> 16) & 1u)) >> 16;
-              const unsigned h1 = (b1r + 0x7FFFu + ((b1r >> 16) & 1u)) >> 16;
-              v[j] = h0 | (h1 << 16);
+              const double x0 = __uint_as_float(v[j] << 16), x1 = __uint_as_float(v[j] & 0xFFFF0000u);
+              const double c = cs[j], sj = sn[j];
+              const double y0 = __builtin_fma(x0, c, -(x1 * sj));
+              const double y1 = __builtin_fma(x0, sj, x1 * c);
+              v[j] = bf16_rne(y0) | (bf16_rne(y1) << 16);
             }
           }
         }
@@ -948,13 +960,9 @@ hipError_t launch(const AttendArgs& a, int S, hipStream_t s) {
   const int ngroups = a.Hq / 32;
   const int total = a.T * ngroups * S;
   const int nb = (total + 7) / 8 * 8;
-  static bool attr = false;
-  if (!attr) {
-    hipError_t e = hipFuncSetAttribute((const void*)attend_kernel<D, F>,
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, G::LDS);
-    if (e != hipSuccess) return e;
-    attr = true;
-  }
+  static_assert(G::LDS <= kLdsBytes, "the tile ring and softmax state must fit one CU's LDS");
+  static PerDevice attr;
+  if (hipError_t e = allow_dynamic_lds(attend_kernel<D, F>, G::LDS, attr); e != hipSuccess) return e;
   hipLaunchKernelGGL((attend_kernel<D, F>), dim3(nb), dim3(kThreads), G::LDS, s, a, S, ngroups, total);
   hipError_t e = hipGetLastError();
   // the fused form merges in its own epilogue (kernel)
@@ -962,6 +970,20 @@ hipError_t launch(const AttendArgs& a, int S, hipStream_t s) {
 }
 
 }  // namespace sd
+
+int sd_lds_bytes(int32_t D) {
+  switch (D) {
+#define SMQA_SD_LDS(d) \
+  case d:             \
+    return sd::Geo<d, sd::kMX>::LDS;
+    SMQA_SD_LDS(128) SMQA_SD_LDS(256) SMQA_SD_LDS(384) SMQA_SD_LDS(512)
+    SMQA_SD_LDS(640) SMQA_SD_LDS(768) SMQA_SD_LDS(896) SMQA_SD_LDS(1024)
+    SMQA_SD_LDS(1152) SMQA_SD_LDS(1280) SMQA_SD_LDS(1408) SMQA_SD_LDS(1536)
+    SMQA_SD_LDS(1664)
+#undef SMQA_SD_LDS
+    default: return 0;
+  }
+}
 
 // Dimension-split attention for Hq % 32 == 0 and D <= 1664 (the register budget of 8
 // waves holding 32 heads of outputs and q, and four tile buffers in LDS), over the FP4

@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <atomic>
+
 #include "smqa.h"
 
 namespace smqa {
@@ -35,6 +37,11 @@ __device__ __forceinline__ unsigned score_key(float s) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
+// Inverse of score_key on the keys of finite scores (>= 0x00800000).
+__device__ __forceinline__ float key_score(unsigned key) {
+  return __uint_as_float((key & 0x80000000u) ? (key ^ 0x80000000u) : ~key);
+}
+
 // Largest b with q_start[b] <= t (queries are grouped by sequence).
 __device__ __forceinline__ int seq_of_query(const int32_t* q_start, int B, int t) {
   int lo = 0, hi = B;
@@ -44,6 +51,33 @@ __device__ __forceinline__ int seq_of_query(const int32_t* q_start, int B, int t
   }
   return lo;
 }
+
+// ---------------------------------------------------------------- host-side caches
+
+// A value computed once per device by host code (a kernel attribute set, an occupancy
+// query).  Thread safe: racing callers may both compute it, which is harmless because the
+// computation is idempotent; 0 means "not yet".  Devices past kMaxDevices are not cached.
+constexpr int kMaxDevices = 64;
+struct PerDevice {
+  std::atomic<int> v[kMaxDevices];
+};
+
+inline int current_device() {
+  int d = 0;
+  return hipGetDevice(&d) == hipSuccess ? d : 0;
+}
+
+// Raise `kernel`'s dynamic-LDS limit to `bytes` once per device.
+template <class K>
+inline hipError_t allow_dynamic_lds(K kernel, int bytes, PerDevice& done) {
+  const int dev = current_device();
+  if (dev < kMaxDevices && done.v[dev].load(std::memory_order_acquire)) return hipSuccess;
+  hipError_t e = hipFuncSetAttribute((const void*)kernel, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+  if (e == hipSuccess && dev < kMaxDevices) done.v[dev].store(1, std::memory_order_release);
+  return e;
+}
+
+constexpr int kLdsBytes = 160 * 1024;   // LDS of one gfx950 compute unit
 
 // ---------------------------------------------------------------- launchers
 // (defined in score.hip / topk.hip / attend.hip; arguments already validated)
@@ -68,6 +102,9 @@ struct ScoreArgs {
   unsigned* hist;
   int32_t* qcols;
   int32_t qcols_stride;
+  // Write -inf into the columns no score goes to: dense, [min(p_t, len_b - 1) + 1, ld);
+  // candidate mode, [n_cand, ld) (the public call; decode_step's internal rows skip it).
+  bool fill_tail;
 };
 hipError_t launch_score(const ScoreArgs& a, hipStream_t s);
 // True when launch_score takes the streaming kernel, the one that can fill ScoreArgs::hist.
@@ -87,6 +124,7 @@ struct TopkArgs {
   int32_t k;
   int32_t* idx;
   void* ws;
+  float* val;           // optional [T][k]: the score of each selected position, -inf for padding
 };
 size_t topk_workspace_bytes(int32_t T, int32_t max_ctx, int32_t k);
 hipError_t launch_topk(const TopkArgs& a, hipStream_t s);
@@ -140,7 +178,10 @@ struct AttendArgs {
   uint8_t* out_fp8;
   float* out_scale;
 };
-int attend_splits(int32_t T, int32_t k, int32_t W, int32_t Hq, int32_t D);
+// Tile-range splits per (query, head group) of a call of this shape, or 0 when no split
+// count fits the workgroup's LDS (the call is unsupported); lds receives the bytes per
+// workgroup (static + dynamic) of the chosen plan.
+int attend_splits(int32_t T, int32_t k, int32_t W, int32_t Hq, int32_t D, int32_t* lds = nullptr);
 size_t attend_workspace_bytes(int32_t T, int32_t k, int32_t W, int32_t Hq, int32_t D);
 hipError_t launch_attend(const AttendArgs& a, hipStream_t s);
 hipError_t launch_attend_fmt(const AttendArgs& a, hipStream_t s);

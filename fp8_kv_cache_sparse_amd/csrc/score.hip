@@ -36,6 +36,13 @@ __device__ __forceinline__ v8bf fp8x8_to_bf16(unsigned w0, unsigned w1) {
 // every negative float (and -0) is a negative int32.
 __device__ __forceinline__ float relu(float x) { return __int_as_float(max(__float_as_int(x), 0)); }
 
+// -inf into columns [from, a.ld) of query t's score row, spread over the workgroups along x.
+__device__ __forceinline__ void fill_tail(const ScoreArgs& a, int t, int from) {
+  for (int64_t c = from + (int64_t)blockIdx.x * kScoreThreads + threadIdx.x; c < a.ld;
+       c += (int64_t)gridDim.x * kScoreThreads)
+    a.scores[(int64_t)t * a.ld + c] = -__builtin_inff();
+}
+
 constexpr int kQRow = 272;   // LDS bytes per head row of bf16 q (256 + 16 pad: conflict-free b128 reads)
 
 // Raw keys of one block of positions for one lane: TPW tiles x DI/4 bytes.
@@ -73,6 +80,11 @@ __global__ __launch_bounds__(kScoreThreads, 2) void score_kernel(ScoreArgs a) {
   const int64_t base = a.seq_start[b];
   const int len = (int)(a.seq_start[b + 1] - base);
   const int ncols = CAND ? a.n_cand : len;
+  if (a.fill_tail) {
+    if (CAND) fill_tail(a, t0, a.n_cand);
+    else
+      for (int t = t0; t < t1; ++t) fill_tail(a, t, min(a.q_pos[t], len - 1) + 1);
+  }
   int nblk = (ncols + kPosPerWG - 1) / kPosPerWG;
   int blk = blockIdx.x;
   if (blk >= nblk || t0 >= t1) return;
@@ -329,6 +341,7 @@ __global__ __launch_bounds__(kScoreThreads) void score_stream_kernel(ScoreArgs a
     const int nvalid = __builtin_amdgcn_readfirstlane(min(min(len, p + 1), a.max_ctx));
     const int nblk = (nvalid + kPosPerWG - 1) / kPosPerWG;
     if (HIST && blockIdx.x == 0 && tid == 0) a.qcols[(int64_t)t * a.qcols_stride] = nvalid;
+    if (a.fill_tail) fill_tail(a, t, nvalid);
     if ((int)blockIdx.x >= nblk) continue;
 
     __syncthreads();   // the previous query's q and histogram are no longer read
@@ -448,20 +461,22 @@ __global__ __launch_bounds__(kScoreThreads) void score_stream_kernel(ScoreArgs a
   }
 }
 
-// Workgroups of this kernel that fit on the device at once (cached per instantiation).
+// Workgroups of this kernel that fit on the current device at once (cached per
+// instantiation and device).
 template <class K>
 static int resident_workgroups(K kernel) {
-  static int cached = 0;
-  if (cached == 0) {
-    int dev = 0, cus = 0, per_cu = 0;
-    if (hipGetDevice(&dev) != hipSuccess ||
-        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-        hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, kScoreThreads, 0) != hipSuccess ||
-        cus <= 0 || per_cu <= 0)
-      return 512;
-    cached = cus * per_cu;
+  static PerDevice cache;
+  const int dev = current_device();
+  if (dev < kMaxDevices) {
+    if (const int c = cache.v[dev].load(std::memory_order_acquire)) return c;
   }
-  return cached;
+  int cus = 0, per_cu = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, kScoreThreads, 0) != hipSuccess ||
+      cus <= 0 || per_cu <= 0)
+    return 512;
+  if (dev < kMaxDevices) cache.v[dev].store(cus * per_cu, std::memory_order_release);
+  return cus * per_cu;
 }
 
 template <int MT, int TPW, int DI, bool CAND>

@@ -349,14 +349,19 @@ __device__ void write_selection(const TopkArgs& a, int t, const unsigned* bits, 
       }
     }
     __syncthreads();
+    float* vdst = a.val ? a.val + (int64_t)t * a.k : nullptr;
     for (int o = threadIdx.x; o < nout; o += NT) {
       const int col = out[o];
       dst[done + o] = a.cand ? a.cand[(int64_t)t * a.n_cand + col] : col;
+      if (vdst) vdst[done + o] = a.scores[(int64_t)t * a.ld + col];
     }
     done += nout;
     __syncthreads();                     // lbits and out are rewritten by the next round
   }
-  for (int i = done + threadIdx.x; i < a.k; i += NT) dst[i] = -1;
+  for (int i = done + threadIdx.x; i < a.k; i += NT) {
+    dst[i] = -1;
+    if (a.val) a.val[(int64_t)t * a.k + i] = -__builtin_inff();
+  }
 }
 
 // ------------------------------------------------------------------ short rows
@@ -515,18 +520,28 @@ __global__ __launch_bounds__(1024) void topk_small_kernel(TopkArgs a) {
   }
   // the selection is staged in LDS (the key array is free: the keys are in registers)
   // and written out with coalesced stores
+  // (scores, when asked for, are the exact inverses of the keys, staged next to them)
   int* stage = (int*)keys;
+  float* vstage = (float*)(keys + 4096);
+  static_assert(kSmallN >= 2 * 4096, "position and score staging for k <= 4096");
 #pragma unroll
   for (int u = 0; u < PER; ++u) {
     bool sel = key[u] > tau;
     if (key[u] == tau) sel = tie_rank++ < tie_need;
     if (sel) {
-      if (off < a.k) stage[off] = pos[u];
+      if (off < a.k) {
+        stage[off] = pos[u];
+        if (a.val) vstage[off] = key_score(key[u]);
+      }
       ++off;
     }
   }
   __syncthreads();
   for (int i = tid; i < a.k; i += NT) dst[i] = i < nsel ? stage[i] : -1;
+  if (a.val) {
+    float* vdst = a.val + (int64_t)t * a.k;
+    for (int i = tid; i < a.k; i += NT) vdst[i] = i < nsel ? vstage[i] : -__builtin_inff();
+  }
 }
 
 // ------------------------------------------------------------------ long rows

@@ -32,8 +32,10 @@
  *   validated and must satisfy the stated ranges.
  * - A failed launch returns SMQA_ERR_HIP.  Device faults surface at the
  *   caller's next synchronisation.
- * - Re-entrant; concurrent calls on different streams with different
- *   workspaces are safe.
+ * - Re-entrant and thread safe: the library's only state is a thread-local
+ *   error string and per-device caches of kernel attributes, filled once
+ *   with atomic flags.  Concurrent calls on different streams with
+ *   different workspaces are safe.
  *
  * Storage formats
  * ---------------
@@ -108,12 +110,14 @@ typedef struct {
  *   S[t, j] = sum_{h < Hi} w[t,h] * max(0, kappa_j * sum_{d < Di} qI[t,h,d] * kI[row(j), d])
  *
  * Dense mode (cand == NULL): for every query t and every position
- *   0 <= j <= min(p_t, len_b - 1), scores[t * ld_scores + j] = S[t, j].
- *   Columns past that bound are not written.
+ *   0 <= j <= min(p_t, len_b - 1), scores[t * ld_scores + j] = S[t, j];
+ *   the columns past that bound, up to ld_scores, receive -INFINITY.
  * Candidate mode (cand != NULL): cand[t * n_cand + i] (i < n_cand) are
  *   positions of query t's sequence, strictly ascending per query;
  *   scores[t * ld_scores + i] = S[t, cand[t,i]], or -INFINITY when the
- *   candidate is past p_t or past the sequence.
+ *   candidate is past p_t or past the sequence; columns n_cand .. ld_scores-1
+ *   receive -INFINITY.
+ * Every entry of the [T][ld_scores] array is written.
  * q_fp8   uint8  [T][Hi][Di]  E4M3 indexer queries
  * w       float  [T][Hi]      head weights (any sign)
  * k_fp8   uint8  [N][Di]      E4M3 indexer keys, N = seq_start[B]
@@ -138,7 +142,9 @@ int sparse_mqa_score(const smqa_layout* L,
  * query t is columns 0..min(p_t, len_b - 1) (dense) or the columns whose
  * score is not -INFINITY (candidate mode; positions are cand[t, col]).
  * idx_out[t * k + i] receives the selected positions in ascending order;
- * when the set has m < k entries, slots m..k-1 hold -1.  Bitwise
+ * when the set has m < k entries, slots m..k-1 hold -1.  val_out (float
+ * [T][k], or NULL) receives the score of each selected position, bit for bit
+ * the input entry, and -INFINITY in the padding slots.  Bitwise
  * deterministic.  scores is read only.
  * workspace: smqa_topk_workspace_size() bytes, 256-byte aligned, contents
  * need not be initialised; it is clobbered.
@@ -146,7 +152,7 @@ int sparse_mqa_score(const smqa_layout* L,
 int topk_select(const smqa_layout* L,
                 const float* scores, int64_t ld_scores,
                 const int32_t* cand, int32_t n_cand,
-                int32_t k, int32_t* idx_out,
+                int32_t k, int32_t* idx_out, float* val_out,
                 void* workspace, size_t workspace_bytes,
                 void* stream);
 
@@ -254,10 +260,11 @@ int sparse_mqa_attend_nvfp4(const smqa_layout* L,
  * output projection) over the FP4 (MX) cache of sparse_mqa_attend:
  *   q'      = q with the pairs (2i, 2i+1) of its last 2R dims (R = rope_pairs)
  *             rotated by query t's angle: (a, b) -> (a c - b s, a s + b c),
- *             c = rope_cos[t][i], s = rope_sin[t][i], rounded to bf16 (nearest
- *             even) for the products.  The rotation is evaluated in fp32 (one
- *             fused multiply-add per output), so an exact value within fp32
- *             rounding of a bf16 midpoint may take the neighbouring bf16 value.
+ *             c = rope_cos[t][i], s = rope_sin[t][i], rounded once to bf16
+ *             (nearest even) for the products.  The rotation is evaluated in
+ *             fp64, where the products are exact, so q' is the bf16 nearest to
+ *             the rotation (one bf16 unit of q' moves a flat-softmax output by
+ *             about 1e-3 of its magnitude, so the rounding is not left loose).
  *   O       = sparse_mqa_attend(q', ...)
  *   O'      = O with the same pairs rotated back: (a, b) -> (a c + b s, -a s + b c)
  *   out_scale[t,h] = max_d |O'[t,h,d]| / 448,
@@ -341,7 +348,8 @@ int decode_step_fused(const smqa_layout* L,
                       void* stream);
 
 /* Workspace sizes in bytes (host-only arithmetic, no HIP call).  A NULL or
- * inconsistent layout returns 0 and sets smqa_last_error(). */
+ * inconsistent layout, or an attention shape smqa_attend_plan rejects, returns 0 and
+ * sets smqa_last_error(). */
 size_t smqa_topk_workspace_size(const smqa_layout* L, int32_t k, int32_t n_cand);
 size_t smqa_attend_workspace_size(const smqa_layout* L, int32_t k, int32_t W,
                                   int32_t Hq, int32_t D);
@@ -349,6 +357,17 @@ size_t smqa_attend_fused_workspace_size(const smqa_layout* L, int32_t k, int32_t
                                         int32_t Hq, int32_t D);
 size_t smqa_decode_step_workspace_size(const smqa_layout* L, int32_t k, int32_t n_cand,
                                        int32_t W, int32_t Hq, int32_t D);
+
+/* How the attention calls run a batch of this shape (host-only arithmetic, no HIP
+ * call): *splits receives the number of tile ranges each (query, head group) is cut into
+ * (their partial results are merged by log-sum-exp; 1 = no partials, no workspace) and
+ * *lds_bytes the LDS one workgroup uses (static + dynamic) at that split count; either
+ * pointer may be NULL.  Returns SMQA_OK, SMQA_ERR_UNSUPPORTED for a shape outside the
+ * limits or one whose workgroup needs more than a compute unit's 160 KiB of LDS at every
+ * split count (every attention call and workspace query rejects such a shape the same
+ * way), or the layout's error. */
+int smqa_attend_plan(const smqa_layout* L, int32_t k, int32_t W, int32_t Hq, int32_t D,
+                     int32_t* splits, int32_t* lds_bytes);
 
 /* Thread-local description of the last non-OK return on this thread ("" if none). */
 const char* smqa_last_error(void);

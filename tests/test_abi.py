@@ -32,7 +32,7 @@ def test_header_declares_the_boundary():
               "decode_step_fused",
               "decode_step",
               "smqa_topk_workspace_size", "smqa_attend_workspace_size",
-              "smqa_decode_step_workspace_size", "smqa_last_error", "smqa_version"):
+              "smqa_decode_step_workspace_size", "smqa_attend_plan", "smqa_last_error", "smqa_version"):
         assert n in names
 
 
@@ -82,16 +82,17 @@ def test_score_validation():
 
 
 def topk(L, k=2048, ws=None, nbytes=0, **kw):
-    a = dict(s=A4, ld=8192, cand=None, n_cand=0, idx=A4)
+    a = dict(s=A4, ld=8192, cand=None, n_cand=0, idx=A4, val=None)
     a.update(kw)
     return lib().topk_select(ctypes.byref(L), a["s"], a["ld"], a["cand"], a["n_cand"], k, a["idx"],
-                             ws, nbytes, None)
+                             a["val"], ws, nbytes, None)
 
 
 def test_topk_validation_and_workspace():
     L = layout()
     assert topk(L, k=0) == -4 and topk(L, k=4097) == -4
     assert topk(L, idx=None) == -1
+    assert topk(L, val=A4 + 2) == -3 and "val" in err()
     assert topk(L, ld=10) == -2
     big = layout(max_ctx=100000)
     need = lib().smqa_topk_workspace_size(ctypes.byref(big), 2048, 0)
@@ -219,3 +220,37 @@ def test_error_string_cleared_on_success_path():
     assert err() != ""
     assert score(layout(T=0)) == 0
     assert err() == ""
+
+
+def test_attend_plan_fits_the_lds_at_every_supported_shape():
+    """Walk the header's limit table (D, Hq, k, W) over query counts that take each kernel
+    (few and many (query, head group) pairs) through the host plan: every shape either gets
+    a split count whose workgroup fits a CU's 160 KiB of LDS, or is rejected as unsupported
+    by the plan query and by every size query and attention call alike."""
+    l = lib()
+    S = ctypes.c_int32()
+    lds = ctypes.c_int32()
+    rejected = []
+    for D in range(128, 2049, 128):
+        for Hq in (16, 32, 48, 64, 96, 128):
+            for k in (1, 256, 2048, 4096):
+                for W in (1, 128):
+                    for T in (1, 4, 64, 1024):
+                        L = layout(T=T, B=T)
+                        st = l.smqa_attend_plan(ctypes.byref(L), k, W, Hq, D, ctypes.byref(S), ctypes.byref(lds))
+                        if st == 0:
+                            assert 1 <= S.value <= 64
+                            assert 0 < lds.value <= 160 * 1024, (D, Hq, k, W, T, S.value, lds.value)
+                            need = l.smqa_attend_workspace_size(ctypes.byref(L), k, W, Hq, D)
+                            assert (need == 0) == (S.value == 1)
+                        else:
+                            assert st == -4 and "LDS" in err()
+                            rejected.append((D, Hq, k, W, T))
+                            assert l.smqa_attend_workspace_size(ctypes.byref(L), k, W, Hq, D) == 0
+                            assert attend(L, k=k, W=W, Hq=Hq, D=D, ws=A16 * 16, nb=1 << 40) == -4
+    assert not rejected, rejected[:5]
+    # the shapes that overflowed a single-split plan now take more splits
+    L = layout(T=64, B=64)
+    assert l.smqa_attend_plan(ctypes.byref(L), 2048, 128, 64, 2048, ctypes.byref(S), ctypes.byref(lds)) == 0
+    assert S.value > 1 and lds.value <= 160 * 1024
+    assert l.smqa_attend_plan(ctypes.byref(L), 2048, 128, 60, 2048, None, None) == -4   # Hq % 16

@@ -48,7 +48,6 @@ def test_score_dense(lib, name, kw):
     S_ref = ref.score(a["qI"], a["w"], a["kI"], a["kscale"], a["seq_start"], a["q_start"], a["q_pos"],
                       ld=wl.max_ctx)
     S_gpu = S.cpu().numpy().astype(np.float64)
-    S_gpu[S_ref == -np.inf] = -np.inf        # dense mode leaves columns past p_t unwritten
     for t in range(wl.T):
         ok, msg = close_scores(S_gpu[t], S_ref[t])
         assert ok, f"query {t}: {msg}"
@@ -70,7 +69,6 @@ def test_score_dense_streaming(lib, Hi, Di, scaled):
     S_ref = ref.score(a["qI"], a["w"], a["kI"], a["kscale"], a["seq_start"], a["q_start"], a["q_pos"],
                       ld=wl.max_ctx)
     S_gpu = S.cpu().numpy().astype(np.float64)
-    S_gpu[S_ref == -np.inf] = -np.inf
     for t in range(wl.T):
         ok, msg = close_scores(S_gpu[t], S_ref[t])
         assert ok, f"query {t}: {msg}"
@@ -93,7 +91,6 @@ def test_score_dense_streaming_uneven_queries(lib):
                       ld=wl.max_ctx)
     S_gpu = S.cpu().numpy().astype(np.float64)
     assert np.isfinite(S_gpu[1, :70002]).all()
-    S_gpu[S_ref == -np.inf] = -np.inf
     for t in range(wl.T):
         ok, msg = close_scores(S_gpu[t], S_ref[t])
         assert ok, f"query {t}: {msg}"
@@ -130,6 +127,35 @@ def test_score_candidates(lib):
     assert np.isinf(S_ref).any()
 
 
+@pytest.mark.parametrize("name,kw,n_cand", [
+    ("decode_8k", dict(B=3, lengths=(3000, 9000)), None),               # short rows
+    ("decode_8k", dict(B=2, lengths=(131001, 140000)), None),           # the streaming kernel
+    ("replay_h100k", dict(B=2, lengths=3000, replay=(3000, 40)), None),  # many queries per sequence
+    ("decode_8k", dict(B=2, lengths=(20000, 40000)), 4000),             # candidate lists
+])
+def test_score_writes_every_column(lib, name, kw, n_cand):
+    """Every entry of the [T][ld] score array is written: the columns past each query's
+    position (and past its sequence), and past the candidate list, up to an ld wider than
+    needed, hold -inf; the rest are the scores."""
+    wl = gen(name, n_cand=n_cand, **kw)
+    if n_cand is None and wl.T > 1:
+        wl.q_pos[1] -= 500                                  # a query well inside its sequence
+    ld = (wl.max_ctx if n_cand is None else n_cand) + 77
+    S = torch.full((wl.T, ld), 7.0, dtype=torch.float32, device=DEV)
+    announce(f"score every column {name} T={wl.T} ld={ld} cand={n_cand}")
+    lib.sparse_mqa_score(lib.Batch(wl.seq_start, wl.q_start, wl.q_pos, wl.max_ctx), wl.qI, wl.w, wl.kI,
+                         wl.kscale, wl.cand, scores=S)
+    sync()
+    a = np_inputs(wl)
+    S_ref = ref.score(a["qI"], a["w"], a["kI"], a["kscale"], a["seq_start"], a["q_start"], a["q_pos"],
+                      cand=a["cand"], ld=ld)
+    S_gpu = S.cpu().numpy().astype(np.float64)
+    assert not (S_gpu == 7.0).any()
+    for t in range(wl.T):
+        ok, msg = close_scores(S_gpu[t], S_ref[t])
+        assert ok, f"query {t}: {msg}"
+
+
 # ------------------------------------------------------------------ top-k
 
 def _topk_case(lib, S_host, k, cand=None, q_pos=None):
@@ -143,8 +169,17 @@ def _topk_case(lib, S_host, k, cand=None, q_pos=None):
     L = lib.Batch(seq_start, q_start, qp, int(max_ctx) if cand is not None else int(q_pos.max()) + 1)
     S_dev = torch.tensor(S_host, dtype=torch.float32, device=DEV)
     cd = None if cand is None else torch.tensor(cand, dtype=torch.int32, device=DEV)
-    idx = lib.topk_select(L, S_dev, k, cand=cd).cpu().numpy()
+    idx, val = lib.topk_select(L, S_dev, k, cand=cd, want_val=True)
+    idx, val = idx.cpu().numpy(), val.cpu().numpy()
+    # without val_out the selection is the same
+    assert np.array_equal(lib.topk_select(L, S_dev, k, cand=cd).cpu().numpy(), idx)
     for t in range(T):
+        # val_out: the selected entries' scores, bit for bit, -inf in the padding
+        sel = idx[t] >= 0
+        cols = idx[t][sel] if cand is None else np.searchsorted(cand[t], idx[t][sel])
+        assert np.array_equal(val[t][sel].view(np.uint32),
+                              S_host[t].astype(np.float32)[cols].view(np.uint32))
+        assert np.all(val[t][~sel] == -np.inf)
         S_ref = S_host[t].astype(np.float32).astype(np.float64)
         if cand is None:
             S_ref = S_ref.copy()
@@ -230,7 +265,8 @@ def test_attend(lib, name, kw):
 # wave pair (D = 128: waves 4..7 own no block), an even split (D = 512) and an uneven one
 # (D = 640); the 16-head kernel for few queries at D = 1792 and for head counts that are not
 # a multiple of 32; the 32-head tile kernel at D = 1792 with 64 (query, head group) pairs;
-# and the widest latent the boundary accepts (D = 2048).
+# and the widest latent the boundary accepts (D = 2048), also at a size whose LDS decides
+# the split count.
 @pytest.mark.parametrize("name,kw", [
     ("decode_8k", dict(B=2, lengths=1500, Hq=32, D=128, k=256)),
     ("decode_8k", dict(B=2, lengths=1500, Hq=64, D=512, k=256)),
@@ -239,6 +275,9 @@ def test_attend(lib, name, kw):
     ("decode_8k", dict(B=2, lengths=1500, Hq=48, D=768, k=256)),
     ("decode_8k", dict(B=2, lengths=1500, Hq=32, D=2048, k=256)),
     ("replay_h100k", dict(B=1, lengths=2000, replay=(2000, 32), Hq=64, D=1792, k=256)),
+    # 64 queries at the widest latent with k = 2048: one split would need ~175 KB of LDS per
+    # workgroup, so the plan takes more splits until a workgroup fits the CU's 160 KiB
+    ("decode_8k", dict(B=64, lengths=2100, Hq=64, D=2048, k=2048)),
 ])
 def test_attend_widths_and_head_counts(lib, name, kw):
     _attend_check(lib, gen(name, **kw))
