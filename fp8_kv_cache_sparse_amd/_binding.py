@@ -62,6 +62,8 @@ _SIGS = {
     "smqa_attend_fused_workspace_size": (_S, [_LP, _I, _I, _I, _I]),
     "decode_step": (_I, [_LP, _P, _P, _P, _P, _P, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P, _P,
                          _I, _I, _I, _F, _I, _P, _P, _P, _P, _S, _P]),
+    "decode_step_noalloc": (_I, [_LP, _P, _P, _P, _P, _P, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P, _P,
+                                 _I, _I, _I, _F, _I, _P, _P, _P, _P]),
     "decode_step_fused": (_I, [_LP, _P, _P, _P, _P, _P, _I, _I, _I, _P, _P, _P, _I, _P, _P, _P, _P,
                                _P, _P, _P, _I, _I, _I, _F, _I, _P, _P, _P, _P, _P, _P, _S, _P]),
     "smqa_topk_workspace_size": (_S, [_LP, _I, _I]),
@@ -389,6 +391,35 @@ def decode_step(L: Batch, q_fp8, w, k_fp8, k_scale, cand, q, kv_codes, kv_e8m0, 
                            _ptr(swa), _ptr(swa_scale), _ptr(swa_pos0), _ptr(swa_clip), W, Hq, D,
                            float(sm_scale), k, _ptr(out), _ptr(lse), _ptr(idx), wp, wb,
                            _stream(stream)))
+    return out, lse, idx
+
+
+def decode_step_noalloc(L: Batch, q_fp8, w, k_fp8, k_scale, cand, q, kv_codes, kv_e8m0, kv_rowscale, swa,
+                        swa_scale, swa_pos0, swa_clip, k: int, sm_scale: float, out, lse, idx=None,
+                        stream=None):
+    """decode_step on the library's device scratch buffer: the caller passes the outputs
+    (out float32 [T, Hq, D], lse float32 [T, Hq], idx int32 [T, k] or None) and nothing is
+    allocated, by this function or the library."""
+    lib = load()
+    for t_, n_, d_, nd in ((q_fp8, "q_fp8", _U8, 3), (w, "w", torch.float32, 2),
+                           (k_fp8, "k_fp8", _U8, 2), (k_scale, "k_scale", torch.float32, 1),
+                           (cand, "cand", torch.int32, 2), (q, "q", torch.bfloat16, 3),
+                           (kv_codes, "kv_codes", torch.uint8, 2), (kv_e8m0, "kv_e8m0", torch.uint8, 2),
+                           (kv_rowscale, "kv_rowscale", torch.float32, 1), (swa, "swa", _U8, 3),
+                           (swa_scale, "swa_scale", torch.float32, 2),
+                           (swa_pos0, "swa_pos0", torch.int32, 1), (swa_clip, "swa_clip", torch.int32, 1),
+                           (out, "out", torch.float32, 3), (lse, "lse", torch.float32, 2),
+                           (idx, "idx", torch.int32, 2)):
+        _dev(t_, n_, d_, nd)
+    T, Hi, Di = q_fp8.shape
+    _, Hq, D = q.shape
+    W = swa.shape[1]
+    n_cand = 0 if cand is None else cand.shape[1]
+    _check(lib.decode_step_noalloc(L.ref, _ptr(q_fp8), _ptr(w), _ptr(k_fp8), _ptr(k_scale), _ptr(cand),
+                                   n_cand, Hi, Di, _ptr(q), _ptr(kv_codes), _ptr(kv_e8m0),
+                                   _ptr(kv_rowscale), _ptr(swa), _ptr(swa_scale), _ptr(swa_pos0),
+                                   _ptr(swa_clip), W, Hq, D, float(sm_scale), k, _ptr(out), _ptr(lse),
+                                   _ptr(idx), _stream(stream)))
     return out, lse, idx
 
 

@@ -1,12 +1,18 @@
 // C-ABI entry points of libsmqa: host-side validation, workspace carving and
 // launches on the caller's stream.  Every check runs before the first HIP call,
 // so argument errors are reported without touching a device.
+#include <atomic>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
 #include <string>
 
 #include "common.h"
+
+// Device-resident workspace of decode_step_noalloc, for callers that cannot allocate.  Every
+// GPU the library runs on holds its own copy until the process ends.  In host code this
+// name is only a stand-in for the symbol: its device address comes from hipGetSymbolAddress.
+static __device__ __align__(256) uint8_t scratch[SMQA_NOALLOC_SCRATCH_BYTES];
 
 namespace {
 
@@ -391,6 +397,33 @@ int sparse_mqa_attend_fused(const smqa_layout* L, const uint16_t* q_bf16, const 
 
 namespace {
 
+// Device address of `scratch` on the current device, looked up once per device (the first
+// call on it) and kept; nullptr with the HIP error in *err when the lookup fails.
+void* scratch_ptr(hipError_t* err) {
+  static std::atomic<void*> ptrs[smqa::kMaxDevices];
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) {
+    *err = e;
+    return nullptr;
+  }
+  if (dev < smqa::kMaxDevices) {
+    if (void* p = ptrs[dev].load(std::memory_order_acquire)) return p;
+  }
+  void* p = nullptr;
+  e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+  if (e != hipSuccess || !p) {
+    *err = e != hipSuccess ? e : hipErrorInvalidSymbol;
+    return nullptr;
+  }
+  if (dev < smqa::kMaxDevices) ptrs[dev].store(p, std::memory_order_release);
+  return p;
+}
+
+}  // namespace
+
+namespace {
+
 // The fused form's extra outputs of a decode step (NULL: the plain step).
 struct FusedOut {
   const float* rope_cos;
@@ -406,7 +439,7 @@ int decode_step_impl(const smqa_layout* L, const uint8_t* q_fp8, const float* w,
                      const float* kv_rowscale, const uint8_t* swa_fp8, const float* swa_scale,
                      const int32_t* swa_pos0, const int32_t* swa_clip, int32_t W, int32_t Hq, int32_t D,
                      float sm_scale, int32_t k, float* out, float* lse, int32_t* idx_out, void* workspace,
-                     size_t workspace_bytes, void* stream, const FusedOut* fz) {
+                     size_t workspace_bytes, void* stream, const FusedOut* fz, bool use_scratch = false) {
   g_err.clear();
   int st = check_layout(L);
   if (st) return st;
@@ -428,6 +461,18 @@ int decode_step_impl(const smqa_layout* L, const uint8_t* q_fp8, const float* w,
     if (st) return st;
   }
   const DecodeWs d = decode_ws_layout(L, k, cols, W, Hq, D);
+  if (use_scratch) {
+    // every argument is checked: only now is the device touched, for the scratch address
+    if (d.total > (size_t)SMQA_NOALLOC_SCRATCH_BYTES)
+      return fail(SMQA_ERR_WORKSPACE,
+                  "decode_step_noalloc: this batch needs %zu bytes of workspace, more than the %zu-byte "
+                  "device scratch buffer; call decode_step with a workspace instead",
+                  d.total, (size_t)SMQA_NOALLOC_SCRATCH_BYTES);
+    hipError_t e = hipSuccess;
+    workspace = scratch_ptr(&e);
+    if (!workspace) return hip_fail(e, "decode_step_noalloc: scratch buffer address");
+    workspace_bytes = SMQA_NOALLOC_SCRATCH_BYTES;
+  }
   st = check_ws(workspace, workspace_bytes, d.total);
   if (st) return st;
   char* ws = (char*)workspace;
@@ -484,6 +529,18 @@ int decode_step(const smqa_layout* L, const uint8_t* q_fp8, const float* w, cons
   return decode_step_impl(L, q_fp8, w, k_fp8, k_scale, cand, n_cand, Hi, Di, q_bf16, kv_codes, kv_e8m0,
                           kv_rowscale, swa_fp8, swa_scale, swa_pos0, swa_clip, W, Hq, D, sm_scale, k, out,
                           lse, idx_out, workspace, workspace_bytes, stream, nullptr);
+}
+
+int decode_step_noalloc(const smqa_layout* L, const uint8_t* q_fp8, const float* w, const uint8_t* k_fp8,
+                        const float* k_scale, const int32_t* cand, int32_t n_cand, int32_t Hi, int32_t Di,
+                        const uint16_t* q_bf16, const uint8_t* kv_codes, const uint8_t* kv_e8m0,
+                        const float* kv_rowscale, const uint8_t* swa_fp8, const float* swa_scale,
+                        const int32_t* swa_pos0, const int32_t* swa_clip, int32_t W, int32_t Hq,
+                        int32_t D, float sm_scale, int32_t k, float* out, float* lse, int32_t* idx_out,
+                        void* stream) {
+  return decode_step_impl(L, q_fp8, w, k_fp8, k_scale, cand, n_cand, Hi, Di, q_bf16, kv_codes, kv_e8m0,
+                          kv_rowscale, swa_fp8, swa_scale, swa_pos0, swa_clip, W, Hq, D, sm_scale, k, out,
+                          lse, idx_out, nullptr, 0, stream, nullptr, true);
 }
 
 int decode_step_fused(const smqa_layout* L, const uint8_t* q_fp8, const float* w, const uint8_t* k_fp8,

@@ -323,6 +323,38 @@ int decode_step(const smqa_layout* L,
                 void* stream);
 
 /*
+ * decode_step_noalloc — decode_step for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the same computation, arguments, outputs and errors, without the
+ * workspace arguments.  The workspace is a device array inside the library,
+ * SMQA_NOALLOC_SCRATCH_BYTES bytes per GPU, held from the library's first use on
+ * that GPU until the process ends; its address is looked up on the first call on
+ * each device.  The call allocates nothing and frees nothing.
+ * - A batch whose decode_step workspace (smqa_decode_step_workspace_size) exceeds
+ *   SMQA_NOALLOC_SCRATCH_BYTES returns SMQA_ERR_WORKSPACE before any HIP call
+ *   (96 MiB covers decode batches up to 4 x 512K positions or 32 x 64K; a
+ *   1024-query replay chunk does not fit: use decode_step).
+ * - Every call on one GPU shares that GPU's array, which keeps the last call's
+ *   contents; the step clears what must start at zero itself.  Calls that
+ *   overlap on one GPU (different streams, or threads) race on the array and must
+ *   be serialised by the caller.
+ */
+#define SMQA_NOALLOC_SCRATCH_BYTES (96u << 20)
+int decode_step_noalloc(const smqa_layout* L,
+                        const uint8_t* q_fp8, const float* w,
+                        const uint8_t* k_fp8, const float* k_scale,
+                        const int32_t* cand, int32_t n_cand,
+                        int32_t Hi, int32_t Di,
+                        const uint16_t* q_bf16,
+                        const uint8_t* kv_codes, const uint8_t* kv_e8m0, const float* kv_rowscale,
+                        const uint8_t* swa_fp8, const float* swa_scale,
+                        const int32_t* swa_pos0, const int32_t* swa_clip,
+                        int32_t W, int32_t Hq, int32_t D, float sm_scale,
+                        int32_t k,
+                        float* out, float* lse, int32_t* idx_out,
+                        void* stream);
+
+/*
  * decode_step_fused — decode_step with MegaAttention's fused form as its
  * attention (sparse_mqa_attend_fused: query RoPE by rope_cos / rope_sin on the
  * last 2 * rope_pairs dims, inverse RoPE and FP8 output): the output

@@ -29,7 +29,7 @@ def test_header_declares_the_boundary():
     names = declared_functions()
     for n in ("sparse_mqa_score", "topk_select", "sparse_mqa_attend", "sparse_mqa_attend_fp8kv",
               "sparse_mqa_attend_nvfp4", "sparse_mqa_attend_fused", "smqa_attend_fused_workspace_size",
-              "decode_step_fused",
+              "decode_step_fused", "decode_step_noalloc",
               "decode_step",
               "smqa_topk_workspace_size", "smqa_attend_workspace_size",
               "smqa_decode_step_workspace_size", "smqa_attend_plan", "smqa_last_error", "smqa_version"):
@@ -254,3 +254,33 @@ def test_attend_plan_fits_the_lds_at_every_supported_shape():
     assert l.smqa_attend_plan(ctypes.byref(L), 2048, 128, 64, 2048, ctypes.byref(S), ctypes.byref(lds)) == 0
     assert S.value > 1 and lds.value <= 160 * 1024
     assert l.smqa_attend_plan(ctypes.byref(L), 2048, 128, 60, 2048, None, None) == -4   # Hq % 16
+
+
+def decode_noalloc(L, **kw):
+    a = dict(qI=A16, w=A4, kI=A16, ks=None, cand=None, n_cand=0, Hi=64, Di=128, q=A16, c=A16, e=A4,
+             rs=None, swa=A16, ss=None, p0=A4, clip=None, W=128, Hq=64, D=1664, sc=0.0245, k=2048,
+             out=A16, lse=None, idx=None)
+    a.update(kw)
+    return lib().decode_step_noalloc(ctypes.byref(L), a["qI"], a["w"], a["kI"], a["ks"], a["cand"],
+                                     a["n_cand"], a["Hi"], a["Di"], a["q"], a["c"], a["e"], a["rs"],
+                                     a["swa"], a["ss"], a["p0"], a["clip"], a["W"], a["Hq"], a["D"],
+                                     a["sc"], a["k"], a["out"], a["lse"], a["idx"], None)
+
+
+def test_decode_step_noalloc_rejects_before_any_hip_call():
+    """The no-allocation step validates everything on the host first: bad arguments, and a
+    batch whose workspace exceeds the 96 MiB device scratch buffer (a 1024-query replay
+    chunk), return an error without a device."""
+    cap = 96 << 20
+    L = layout(T=1024, B=8, max_ctx=100000)
+    need = lib().smqa_decode_step_workspace_size(ctypes.byref(L), 2048, 0, 128, 64, 1664)
+    assert need > cap
+    assert decode_noalloc(L) == -5 and "scratch" in err()
+    assert decode_noalloc(layout(), q=None) == -1
+    assert decode_noalloc(layout(), Di=96) == -4
+    assert decode_noalloc(layout(), out=A16 + 4) == -3
+    assert decode_noalloc(layout(T=0)) == 0
+    # the decode batches of the benchmark fit
+    for B, T, n in ((1, 1, 8192), (32, 32, 65536), (4, 4, 524288)):
+        Lb = layout(T=T, B=B, max_ctx=n)
+        assert 0 < lib().smqa_decode_step_workspace_size(ctypes.byref(Lb), 2048, 0, 128, 64, 1664) <= cap
