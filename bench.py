@@ -4,21 +4,24 @@
 One step = one decode_step call over the whole batch: indexer scoring of every
 context position, top-k selection and sparse MQA attention over the selected FP4
 latent rows plus the FP8 window (the three stages of the method, in one call).
-Inputs are the seeded synthetic workloads of ``synth`` (already resident in HBM
-when timing starts).  Metric: context positions scored per second (higher is
-better) and microseconds per step, at 8K context (decode_8k, the primary line)
-and at 512K context (decode_512k, reported alongside).
+Inputs are the seeded synthetic workloads of ``synth``, resident in HBM when
+timing starts.
 
-The step is timed three ways: eager (one C-ABI call per step from Python), as a
-replayed HIP graph of one call, and as a replayed graph of 10 consecutive calls
-(the GPU-side steady state of a captured decode, no host work between steps);
-graph outputs are checked bitwise against the eager step first.  ``value`` uses
-the fastest.  Per-stage kernel
-time comes from HIP events around repeated calls of each stage's entry point
-on the same stream.  ``cpu_baseline`` times the fp64 CPU oracle on a bounded
-sample of the same workload.
+Timing protocol (every figure is per call, on the stream the library launches on):
+  * cold: before each rep a kernel reads 512 MiB (twice the 256 MB Infinity Cache, far
+    more than the L2s) outside the timed region, then HIP events bracket the call;
+    median, p10 and p90 over the reps;
+  * warm (labelled as such): a captured HIP graph of 10 consecutive steps replayed
+    back to back, the GPU-side steady state of a captured decode loop.
+The headline line is the decode_8k workload (batch 1 at 8K context): ``value`` is
+context positions scored per second over the median cold step (the whole hot path),
+``ms_per_step`` that median.  The same protocol runs per stage (score, top-k,
+attention), for candidate-mode scoring (16,384 candidates per query, the pages'
+late-indexer comparison) and for the other workloads (``--also``).  ``cpu_baseline``
+times the fp64 CPU oracle on the same bytes.
 
-    python bench.py [--steps K] [--warmup W] [--workload decode_8k] [--also decode_512k]
+    python bench.py [--steps K] [--warmup W] [--workload decode_8k]
+                    [--also decode_512k,ragged_b32,replay_h100k]
 """
 from __future__ import annotations
 
@@ -35,6 +38,10 @@ METRIC = "context tokens scored/s and decode-attention us/step at 8K and 512K ct
 UNIT = "context tokens scored/s"
 HBM_PEAK_GBS = 8000.0
 MFMA_PEAK_TFLOPS = {"fp8": 5000.0, "bf16": 2500.0}
+FLUSH_BYTES = 512 << 20
+# cold reps per workload: at least 50 for the small batches, 20 for the large ones
+MIN_REPS = {"tiny": 50, "decode_8k": 50, "ragged_b32": 50, "decode_512k": 20, "replay_h100k": 20}
+N_CAND = 16384
 
 
 def parse():
@@ -43,17 +50,19 @@ def parse():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="decode_8k")
-    ap.add_argument("--also", default="decode_512k", help="comma list of extra workloads ('' = none)")
+    ap.add_argument("--also", default="decode_512k,ragged_b32,replay_h100k",
+                    help="comma list of extra workloads ('' = none)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu", action="store_true")
-    ap.add_argument("--no-graph", action="store_true")
-    ap.add_argument("--stage-only", default="", help="time only this stage entry point (profiling)")
+    ap.add_argument("--stage-only", default="", help="run only this stage entry point (profiling)")
+    ap.add_argument("--flush", default="read", choices=("read", "write"),
+                    help="cold-cache flush before each rep: read or write 512 MiB")
     return ap.parse_args()
 
 
 # ---------------------------------------------------------------- algorithmic work per stage
 
-def work(wl):
+def work(wl, n_cand=None):
     """Algorithmic bytes / flops of each stage for one step (what the method must move/compute)."""
     import numpy as np
     lengths = np.array(wl.meta["lengths"], dtype=np.int64)
@@ -78,18 +87,23 @@ def work(wl):
         "attend": dict(bytes=int(sel.sum()) * (row_b + 4) + wl.B * W * D + T * Hq * (D * 2 + D * 4 + 4),
                        flops=int(4 * Hq * D * (sel + vis).sum()), mfma="bf16"),
     }
+    if n_cand:
+        # candidate mode: each query reads its candidate list and those keys, writes n_cand scores
+        out["score_cand"] = dict(bytes=T * n_cand * (4 + Di + 4), flops=2 * Hi * Di * T * n_cand, mfma="bf16")
     return J, out
 
 
 # kernels behind each stage's entry point (what rocprofv3 lists for it)
 STAGE_KERNELS = {
     "score": "score_kernel | score_stream_kernel (one query per sequence, long rows)",
+    "score_cand": "score_kernel (candidate lists)",
     "topk": "topk_small_kernel (rows <= 16384) | topk_zero/hist/collect/finish_kernel",
     "attend": "sd::attend_kernel (dimension split; lat::/thr:: for other head counts and widths) "
               "+ attend_merge_kernel (split partials)",
 }
 TRAFFIC_MD = os.path.join(ROOT, "profiles", "pmc_traffic.md")
-SOURCES = {"score": ["score.hip"], "topk": ["topk.hip"], "attend": ["attend.hip", "attend_sd.hip"]}
+SOURCES = {"score": ["score.hip"], "score_cand": ["score.hip"], "topk": ["topk.hip"],
+           "attend": ["attend.hip", "attend_sd.hip"]}
 
 
 def source_digest(stage):
@@ -119,6 +133,9 @@ def measured_traffic(stage, workload):
 
 
 def roofline(stage, w, seconds, workload=None):
+    """Roofline record of one stage: achieved = algorithmic work per call / measured time per
+    call, against the MFMA peak when the stage's algorithmic flop/byte exceeds the ridge of
+    its MFMA type, else against HBM."""
     ai = w["flops"] / max(w["bytes"], 1)
     traffic = measured_traffic(stage, workload) if workload else None
     if w["mfma"] and ai > MFMA_PEAK_TFLOPS[w["mfma"]] * 1e12 / (HBM_PEAK_GBS * 1e9):
@@ -133,22 +150,103 @@ def roofline(stage, w, seconds, workload=None):
             "algorithmic_bytes": w["bytes"], "algorithmic_flops": w["flops"]}
 
 
+def stats(us):
+    """median / p10 / p90 / mean of per-rep times in microseconds."""
+    import numpy as np
+    a = np.asarray(us, dtype=np.float64)
+    return {"median": round(float(np.median(a)), 2), "p10": round(float(np.percentile(a, 10)), 2),
+            "p90": round(float(np.percentile(a, 90)), 2), "mean": round(float(a.mean()), 2), "reps": int(a.size)}
+
+
 # ---------------------------------------------------------------- GPU measurement
 
-def measure(name, steps, warmup, use_graph, stage_only="", fp8_baseline=True):
+class Timer:
+    """Per-call HIP-event timing on torch's current stream (the stream every entry point of
+    the binding launches on), cold or warm.  Cold: before each rep a kernel reads (default)
+    or writes a 512 MiB buffer.  Reading evicts the call's data from the L2s and the 256 MB
+    Infinity Cache and leaves only clean lines; a writing flush leaves up to 256 MB of
+    dirty lines that are written back while the next timed call runs, which charges that
+    call for the flush's own traffic."""
+
+    def __init__(self, dev, mode="read"):
+        import torch
+        self.torch = torch
+        self.mode = mode
+        self.flush_buf = torch.ones(FLUSH_BYTES // 4, dtype=torch.float32, device=dev)
+
+    def flush(self):
+        if self.mode == "write":
+            self.flush_buf.fill_(1.0)
+        else:
+            self.flush_buf.sum()
+
+    def cold(self, fn, reps, warmup=2):
+        torch = self.torch
+        for _ in range(warmup):
+            fn()
+        torch.cuda.synchronize()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+        for e0, e1 in ev:
+            self.flush()
+            e0.record()
+            fn()
+            e1.record()
+        torch.cuda.synchronize()
+        return [e0.elapsed_time(e1) * 1e3 for e0, e1 in ev]
+
+    def warm_graph(self, fn, steps=10, reps=5):
+        """Mean per-call time of a captured graph of `steps` back-to-back calls (warm)."""
+        torch = self.torch
+        g = torch.cuda.CUDAGraph()
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            fn()
+        torch.cuda.current_stream().wait_stream(s)
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g):
+            for _ in range(steps):
+                fn()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e3 / (reps * steps), g
+
+
+def hbm_reference(timer, dev):
+    """What plain streaming kernels reach on this machine (cold, GB/s): a 1 GiB device-to-device
+    copy (bytes read + written) and a 1 GiB read (a sum reduction)."""
+    import torch
+    src = torch.ones(1 << 28, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    cp = stats(timer.cold(lambda: dst.copy_(src), 10))["median"]
+    rd = stats(timer.cold(lambda: src.sum(), 10))["median"]
+    del src, dst
+    return {"copy_GBs": round(2 * (1 << 30) / (cp * 1e-6) / 1e9, 1),
+            "read_GBs": round((1 << 30) / (rd * 1e-6) / 1e9, 1)}
+
+
+def measure(name, steps, warmup, timer, primary=False, stage_only=""):
     import torch
     import synth
     import fp8_kv_cache_sparse_amd as smqa
 
+    reps = steps if primary else max(steps, MIN_REPS.get(name, 20))
+    reps_stage = max(steps, MIN_REPS.get(name, 20))
     wl = synth.generate(name, seed=0, device="cuda")
-    J, w = work(wl)
+    J, w = work(wl, N_CAND if wl.cand is None and wl.swa_clip is None else None)
     L = smqa.Batch(wl.seq_start, wl.q_start, wl.q_pos, wl.max_ctx)
     dev = wl.q.device
     out = torch.empty((wl.T, wl.Hq, wl.D), dtype=torch.float32, device=dev)
     lse = torch.empty((wl.T, wl.Hq), dtype=torch.float32, device=dev)
     idx = torch.empty((wl.T, wl.k), dtype=torch.int32, device=dev)
-    n_cand = 0 if wl.cand is None else wl.cand.shape[1]
-    ws = torch.empty(smqa.decode_step_workspace_size(L, wl.k, n_cand, wl.W, wl.Hq, wl.D) + 256,
+    ws = torch.empty(smqa.decode_step_workspace_size(L, wl.k, 0, wl.W, wl.Hq, wl.D) + 256,
                      dtype=torch.uint8, device=dev)
     args = (L, wl.qI, wl.w, wl.kI, wl.kscale, wl.cand, wl.q, wl.kv_codes, wl.kv_e8m0, wl.kv_rowscale,
             wl.swa, wl.swa_scale, wl.swa_pos0, wl.swa_clip, wl.k, wl.sm_scale)
@@ -156,235 +254,136 @@ def measure(name, steps, warmup, use_graph, stage_only="", fp8_baseline=True):
     def step():
         smqa.decode_step(*args, out=out, lse=lse, idx=idx, workspace=ws)
 
-    # stage buffers
     scores = torch.empty((wl.T, max(wl.max_ctx, 1)), dtype=torch.float32, device=dev)
     idx2 = torch.empty_like(idx)
     out2, lse2 = torch.empty_like(out), torch.empty_like(lse)
+    ws2 = torch.empty_like(ws)
 
     def st_score():
         smqa.sparse_mqa_score(L, wl.qI, wl.w, wl.kI, wl.kscale, wl.cand, scores=scores)
 
     def st_topk():
-        smqa.topk_select(L, scores, wl.k, cand=wl.cand, idx=idx2, workspace=ws)
+        smqa.topk_select(L, scores, wl.k, cand=wl.cand, idx=idx2, workspace=ws2)
 
     def st_attend():
         smqa.sparse_mqa_attend(L, wl.q, wl.kv_codes, wl.kv_e8m0, wl.kv_rowscale, idx2, wl.swa,
                                wl.swa_scale, wl.swa_pos0, wl.swa_clip, wl.sm_scale, out=out2, lse=lse2,
-                               workspace=ws)
-
-    copy_src = torch.empty(256 << 20, dtype=torch.uint8, device=dev) if stage_only == "copy" else None
-    copy_dst = torch.empty_like(copy_src) if copy_src is not None else None
-
-    def st_copy():                                 # plain 256 MiB device copy: PMC calibration
-        copy_dst.copy_(copy_src)
+                               workspace=ws2)
 
     stages = {"score": st_score, "topk": st_topk, "attend": st_attend}
-    if stage_only == "copy":
-        stages["copy"] = st_copy
-    if stage_only == "attend_nvfp4":
-        wlns = synth.with_nvfp4_kv(wl)
-        stages["attend_nvfp4"] = lambda: smqa.sparse_mqa_attend_nvfp4(
-            L, wl.q, wlns.kv_nv_codes, wlns.kv_nv_scales, wl.kv_rowscale, wlns.kv_nv_global, idx2,
-            wl.swa, wl.swa_scale, wl.swa_pos0, wl.swa_clip, wl.sm_scale, out=out2, lse=lse2,
-            workspace=ws)
-    if stage_only == "attend_fp8kv":
-        wl8s = synth.with_fp8_kv(wl)
-        stages["attend_fp8kv"] = lambda: smqa.sparse_mqa_attend_fp8kv(
-            L, wl.q, wl8s.kv_fp8, wl8s.kv_fp8_scale, idx2, wl.swa, wl.swa_scale, wl.swa_pos0,
-            wl.swa_clip, wl.sm_scale, out=out2, lse=lse2, workspace=ws)
     if stage_only:
-        fn = stages[stage_only]
+        # profiling: prepare the inputs, then `steps` calls of one entry point (cold)
+        if stage_only == "copy":
+            src = torch.empty(256 << 20, dtype=torch.uint8, device=dev)
+            dst = torch.empty_like(src)
+            stages["copy"] = lambda: dst.copy_(src)
+        if stage_only == "decode_step":
+            stages["decode_step"] = step
         st_score()
         st_topk()
-        for _ in range(warmup):
-            fn()
         torch.cuda.synchronize()
-        for _ in range(steps):
-            fn()
-        torch.cuda.synchronize()
+        timer.cold(stages[stage_only], steps, warmup)
         return {"workload": name, "stage_only": stage_only}
 
-    print(f"[bench] {name}: warmup", file=sys.stderr, flush=True)
+    print(f"[bench] {name}: warmup + eager check", file=sys.stderr, flush=True)
     for _ in range(warmup):
         step()
     torch.cuda.synchronize()
     ref_out, ref_lse, ref_idx = out.clone(), lse.clone(), idx.clone()
 
-    print(f"[bench] {name}: eager x{steps}", file=sys.stderr, flush=True)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(steps):
-        step()
-    torch.cuda.synchronize()
-    eager_s = (time.perf_counter() - t0) / steps
+    print(f"[bench] {name}: cold steps x{reps}", file=sys.stderr, flush=True)
+    step_us = timer.cold(step, reps, warmup=0)
+    ok = bool(torch.equal(out, ref_out) and torch.equal(lse, ref_lse) and torch.equal(idx, ref_idx))
 
-    graph_s = None
-    chain_s = None
-    graph_ok = None
-    if use_graph:
-        try:
-            g = torch.cuda.CUDAGraph()
-            s = torch.cuda.Stream()
-            s.wait_stream(torch.cuda.current_stream())
-            with torch.cuda.stream(s):
-                step()
-            torch.cuda.current_stream().wait_stream(s)
-            torch.cuda.synchronize()
-            with torch.cuda.graph(g):
-                step()
-            torch.cuda.synchronize()
-            graph_ok = True
-            for _ in range(3):                     # every replay must reproduce the eager result
-                out.zero_()
-                g.replay()
-                torch.cuda.synchronize()
-                graph_ok &= bool(torch.equal(out, ref_out) and torch.equal(lse, ref_lse)
-                                 and torch.equal(idx, ref_idx))
-            if graph_ok:
-                print(f"[bench] {name}: graph x{steps}", file=sys.stderr, flush=True)
-                for _ in range(warmup):
-                    g.replay()
-                torch.cuda.synchronize()
-                t0 = time.perf_counter()
-                for _ in range(steps):
-                    g.replay()
-                torch.cuda.synchronize()
-                graph_s = (time.perf_counter() - t0) / steps
-                # GPU-side steady state: G consecutive steps in one graph, as inside a captured
-                # decode of a whole model (no host work between the steps)
-                G = max(1, min(10, steps))
-                gc = torch.cuda.CUDAGraph()
-                with torch.cuda.graph(gc):
-                    for _ in range(G):
-                        step()
-                torch.cuda.synchronize()
-                out.zero_()
-                gc.replay()
-                torch.cuda.synchronize()
-                graph_ok &= bool(torch.equal(out, ref_out) and torch.equal(lse, ref_lse)
-                                 and torch.equal(idx, ref_idx))
-                reps = max(1, steps // G)
-                print(f"[bench] {name}: graph of {G} steps x{reps}", file=sys.stderr, flush=True)
-                torch.cuda.synchronize()
-                t0 = time.perf_counter()
-                for _ in range(reps):
-                    gc.replay()
-                torch.cuda.synchronize()
-                chain_s = (time.perf_counter() - t0) / (reps * G)
-        except Exception as e:  # graph capture unavailable: report eager only
-            print(f"[bench] graph capture failed: {e}", file=sys.stderr, flush=True)
-            graph_ok = False
+    print(f"[bench] {name}: warm graph of 10 steps", file=sys.stderr, flush=True)
+    warm_us, g = timer.warm_graph(step)
+    out.zero_()
+    g.replay()
+    torch.cuda.synchronize()
+    ok &= bool(torch.equal(out, ref_out) and torch.equal(lse, ref_lse) and torch.equal(idx, ref_idx))
+    del g
 
-    # per-stage time with HIP events on the launch stream: each stage's entry point is
-    # captured `steps` times into one graph (no host gaps between launches), replayed once
     st_us = {}
     st_score()
     st_topk()
     torch.cuda.synchronize()
-
-    def timed_us(fn):
-        for _ in range(2):
-            fn()
-        torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        if use_graph and graph_ok:
-            gs = torch.cuda.CUDAGraph()
-            with torch.cuda.graph(gs):
-                for _ in range(steps):
-                    fn()
-            torch.cuda.synchronize()
-            gs.replay()
-            torch.cuda.synchronize()
-            best = None
-            for _ in range(3):                     # the fastest of three timed replays
-                e0.record()
-                gs.replay()
-                e1.record()
-                torch.cuda.synchronize()
-                t_ms = e0.elapsed_time(e1)
-                best = t_ms if best is None else min(best, t_ms)
-        else:
-            e0.record()
-            for _ in range(steps):
-                fn()
-            e1.record()
-            torch.cuda.synchronize()
-            best = e0.elapsed_time(e1)
-        return best * 1e3 / steps
-
     for nm, fn in stages.items():
-        print(f"[bench] {name}: stage {nm} x{steps}", file=sys.stderr, flush=True)
-        st_us[nm] = timed_us(fn)
+        print(f"[bench] {name}: stage {nm} x{reps_stage} cold", file=sys.stderr, flush=True)
+        st_us[nm] = timer.cold(fn, reps_stage)
 
-    # the same attention over an FP8 global cache (E4M3 rows + row scale, the format the FP4
-    # cache replaces) and over the NVFP4 layout, on the same selection: what the formats cost
-    fp8kv = None
-    if fp8_baseline and wl.Hq % 32 == 0 and wl.D <= 1664:
-        print(f"[bench] {name}: FP8-cache attention x{steps}", file=sys.stderr, flush=True)
+    # candidate-mode scoring (late indexer layers: a fixed list of 16K candidate positions per
+    # query) next to dense scoring of the same batch: the pages' sparse-logits comparison
+    cand = None
+    if wl.cand is None and wl.swa_clip is None:
+        wlc = synth.generate(name, seed=0, device="cuda", n_cand=N_CAND)
+        Lc = smqa.Batch(wlc.seq_start, wlc.q_start, wlc.q_pos, wlc.max_ctx)
+        sc_c = torch.empty((wlc.T, N_CAND), dtype=torch.float32, device=dev)
+
+        def st_cand():
+            smqa.sparse_mqa_score(Lc, wlc.qI, wlc.w, wlc.kI, wlc.kscale, wlc.cand, scores=sc_c)
+        print(f"[bench] {name}: candidate scoring x{reps_stage} cold", file=sys.stderr, flush=True)
+        cu = timer.cold(st_cand, reps_stage)
+        st_us["score_cand"] = cu
+        cand = {"n_cand": N_CAND, "score_us": stats(cu),
+                "dense_over_candidate_time": round(stats(st_us["score"])["median"] / stats(cu)["median"], 2)}
+        del wlc, sc_c
+
+    # the same attention over the FP8 and NVFP4 global caches and in MegaAttention's fused
+    # form, on the same selection (cold)
+    formats = None
+    if wl.Hq % 32 == 0 and wl.D <= 1664:
+        fmt_us = {"mx_fp4": stats(st_us["attend"])}
         wl8 = synth.with_fp8_kv(wl)
-        torch.cuda.synchronize()
-
-        def st_attend8():
-            smqa.sparse_mqa_attend_fp8kv(L, wl.q, wl8.kv_fp8, wl8.kv_fp8_scale, idx2, wl.swa,
-                                         wl.swa_scale, wl.swa_pos0, wl.swa_clip, wl.sm_scale,
-                                         out=out2, lse=lse2, workspace=ws)
-        us8 = timed_us(st_attend8)
+        print(f"[bench] {name}: FP8-cache attention", file=sys.stderr, flush=True)
+        fmt_us["fp8"] = stats(timer.cold(lambda: smqa.sparse_mqa_attend_fp8kv(
+            L, wl.q, wl8.kv_fp8, wl8.kv_fp8_scale, idx2, wl.swa, wl.swa_scale, wl.swa_pos0, wl.swa_clip,
+            wl.sm_scale, out=out2, lse=lse2, workspace=ws2), reps_stage))
         del wl8
-        print(f"[bench] {name}: NVFP4-cache attention x{steps}", file=sys.stderr, flush=True)
         wln = synth.with_nvfp4_kv(wl)
-        torch.cuda.synchronize()
-
-        def st_attend_nv():
-            smqa.sparse_mqa_attend_nvfp4(L, wl.q, wln.kv_nv_codes, wln.kv_nv_scales, wl.kv_rowscale,
-                                         wln.kv_nv_global, idx2, wl.swa, wl.swa_scale, wl.swa_pos0,
-                                         wl.swa_clip, wl.sm_scale, out=out2, lse=lse2, workspace=ws)
-        usn = timed_us(st_attend_nv)
+        print(f"[bench] {name}: NVFP4-cache attention", file=sys.stderr, flush=True)
+        fmt_us["nvfp4"] = stats(timer.cold(lambda: smqa.sparse_mqa_attend_nvfp4(
+            L, wl.q, wln.kv_nv_codes, wln.kv_nv_scales, wl.kv_rowscale, wln.kv_nv_global, idx2, wl.swa,
+            wl.swa_scale, wl.swa_pos0, wl.swa_clip, wl.sm_scale, out=out2, lse=lse2, workspace=ws2),
+            reps_stage))
         del wln
-        # MegaAttention's fused form on the MX cache: query RoPE (64 rotary dims), the same
-        # attention, inverse RoPE and per-row FP8 output in one call
-        fused_us = None
-        if wl.D >= 64:
-            R = 32
-            th = torch.arange(wl.T * R, device=dev, dtype=torch.float32).view(wl.T, R) * 0.001
-            rc, rsn = th.cos().contiguous(), th.sin().contiguous()
-            o8 = torch.empty((wl.T, wl.Hq, wl.D), dtype=torch.uint8, device=dev)
-            osc = torch.empty((wl.T, wl.Hq), dtype=torch.float32, device=dev)
-            wsf = torch.empty(smqa.load().smqa_attend_fused_workspace_size(L.ref, wl.k, wl.W, wl.Hq, wl.D)
-                              + 256, dtype=torch.uint8, device=dev)
-            print(f"[bench] {name}: fused RoPE/FP8 attention x{steps}", file=sys.stderr, flush=True)
-
-            def st_fused():
-                smqa.sparse_mqa_attend_fused(L, wl.q, rc, rsn, wl.kv_codes, wl.kv_e8m0, wl.kv_rowscale,
-                                             idx2, wl.swa, wl.swa_scale, wl.swa_pos0, wl.swa_clip,
-                                             wl.sm_scale, out_fp8=o8, out_scale=osc, want_out=False,
-                                             lse=lse2, workspace=wsf)
-            fused_us = round(timed_us(st_fused), 2)
+        R = 32
+        th = torch.arange(wl.T * R, device=dev, dtype=torch.float32).view(wl.T, R) * 0.001
+        rc, rsn = th.cos().contiguous(), th.sin().contiguous()
+        o8 = torch.empty((wl.T, wl.Hq, wl.D), dtype=torch.uint8, device=dev)
+        osc = torch.empty((wl.T, wl.Hq), dtype=torch.float32, device=dev)
+        print(f"[bench] {name}: fused RoPE/FP8 attention", file=sys.stderr, flush=True)
+        fmt_us["fused_rope_fp8"] = stats(timer.cold(lambda: smqa.sparse_mqa_attend_fused(
+            L, wl.q, rc, rsn, wl.kv_codes, wl.kv_e8m0, wl.kv_rowscale, idx2, wl.swa, wl.swa_scale,
+            wl.swa_pos0, wl.swa_clip, wl.sm_scale, out_fp8=o8, out_scale=osc, want_out=False, lse=lse2,
+            workspace=ws2), reps_stage))
         rs = 4 if wl.kv_rowscale is not None else 0
-        fp8kv = {"attend_us": {"mx_fp4": round(st_us["attend"], 2), "nvfp4": round(usn, 2),
-                               "fp8": round(us8, 2)},
-                 "fp8_over_mx_fp4_time": round(us8 / st_us["attend"], 3),
-                 "nvfp4_over_mx_fp4_time": round(usn / st_us["attend"], 3),
-                 "global_row_bytes": {"mx_fp4": wl.D // 2 + wl.D // 32 + rs,
-                                      "nvfp4": wl.D // 2 + wl.D // 16 + rs, "fp8": wl.D + 4},
-                 "kernel": "attend: sd::attend_kernel<D, F> (F = MX FP4 / NVFP4 / FP8 rows in "
-                           "16-row tiles) + attend_merge_kernel",
-                 "fused_rope_fp8_us": fused_us,
-                 "fused_kernel": "sd::attend_kernel<D, MX> with query RoPE + attend_fused_epilogue_kernel "
-                                 "(inverse RoPE, E4M3 output)"}
-    dom = max(st_us, key=st_us.get)
-    best_s = min(x for x in (eager_s, graph_s, chain_s) if x)
+        m = fmt_us["mx_fp4"]["median"]
+        formats = {"attend_us": fmt_us,
+                   "fp8_over_mx_fp4_time": round(fmt_us["fp8"]["median"] / m, 3),
+                   "nvfp4_over_mx_fp4_time": round(fmt_us["nvfp4"]["median"] / m, 3),
+                   "global_row_bytes": {"mx_fp4": wl.D // 2 + wl.D // 32 + rs,
+                                        "nvfp4": wl.D // 2 + wl.D // 16 + rs, "fp8": wl.D + 4}}
+
+    step_st = stats(step_us)
+    st_stats = {k: stats(v) for k, v in st_us.items()}
+    # roofline figures divide algorithmic work by the mean per-call time (what a profiler's
+    # average kernel duration reports)
+    st_roof = {k: roofline(k, w[k], st_stats[k]["mean"] * 1e-6, name) for k in st_us if k in w}
+    main_stages = ("score", "topk", "attend")
+    dom = max(main_stages, key=lambda k: st_stats[k]["median"])
     res = {
         "workload": name, "T": wl.T, "B": wl.B, "scored_positions": J,
-        "us_per_step": round(best_s * 1e6, 2),
-        "us_per_step_eager": round(eager_s * 1e6, 2),
-        "us_per_step_graph": None if graph_s is None else round(graph_s * 1e6, 2),
-        "us_per_step_graph_chain": None if chain_s is None else round(chain_s * 1e6, 2),
-        "graph_replay_matches_eager": graph_ok,
-        "tokens_scored_per_s": J / best_s,
-        "stage_us": {k: round(v, 2) for k, v in st_us.items()},
-        "stage_roofline": {k: roofline(k, w[k], st_us[k] * 1e-6, name) for k in st_us},
-        "global_cache_formats": fp8kv,
-        "roofline": roofline(dom, w[dom], st_us[dom] * 1e-6, name),
+        "step_us_cold": step_st,
+        "step_us_warm_graph10": round(warm_us, 2),
+        "outputs_match_eager": ok,
+        "tokens_scored_per_s_step": J / (step_st["median"] * 1e-6),
+        "tokens_scored_per_s_score_stage": J / (st_stats["score"]["median"] * 1e-6),
+        "stage_us_cold": st_stats,
+        "stage_roofline": st_roof,
+        "candidate_scoring": cand,
+        "global_cache_formats": formats,
+        "dominant_stage": dom,
+        "roofline": st_roof[dom],
         "config": dict(wl.meta["params"], lengths=(wl.meta["lengths"] if wl.B <= 8 else
                                                   [min(wl.meta["lengths"]), max(wl.meta["lengths"])])),
     }
@@ -395,24 +394,43 @@ def measure(name, steps, warmup, use_graph, stage_only="", fp8_baseline=True):
 
 # ---------------------------------------------------------------- CPU oracle baseline
 
+def cpu_info():
+    model = None
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    blas, threads = None, None
+    try:
+        from threadpoolctl import threadpool_info
+        info = [i for i in threadpool_info() if i.get("user_api") == "blas"]
+        if info:
+            blas = f"{info[0].get('internal_api')} {info[0].get('version')}"
+            threads = max(i.get("num_threads", 1) for i in info)
+    except Exception:
+        pass
+    return model, blas, threads
+
+
 def cpu_baseline(name, seconds):
+    """The fp64 oracle's decode step on the same bytes the GPU run used (drawn on the GPU,
+    copied to the host), repeated for about `seconds`."""
     import numpy as np
     import torch
     import synth
     from oracle import ref
 
-    wl = synth.generate(name, seed=0, device="cpu")
+    wl = synth.generate(name, seed=0, device="cuda").cpu()
     J, _ = work(wl)
     a = {n: (None if getattr(wl, n) is None else getattr(wl, n).numpy())
          for n in ("seq_start", "q_start", "q_pos", "qI", "w", "kI", "kscale", "kv_codes", "kv_e8m0",
                    "kv_rowscale", "swa", "swa_scale", "swa_pos0", "swa_clip")}
     a["q"] = wl.q.view(torch.int16).numpy().view(np.uint16)
     a.update(k=wl.k, W=wl.W, sm_scale=wl.sm_scale)
-    try:
-        from threadpoolctl import threadpool_info
-        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    except Exception:
-        cores = os.cpu_count()
+    model, blas, threads = cpu_info()
     reps = 0
     t0 = time.perf_counter()
     while True:
@@ -421,9 +439,11 @@ def cpu_baseline(name, seconds):
         el = time.perf_counter() - t0
         if el >= seconds:
             break
-    return {"value": J * reps / el, "unit": UNIT, "cores": cores, "kind": "oracle",
-            "sample": f"{reps} full fp64 oracle decode steps of {name} ({J} scored positions each), "
-                      f"{el:.1f} s", "s_per_step": el / reps}
+    return {"value": J * reps / el, "unit": UNIT, "cores": threads or len(os.sched_getaffinity(0)),
+            "kind": "oracle",
+            "sample": f"{reps} full fp64 oracle decode steps of {name} on the GPU run's bytes "
+                      f"({J} scored positions each), {el:.1f} s",
+            "s_per_step": el / reps, "cpu_model": model, "blas": blas}
 
 
 def main():
@@ -432,29 +452,34 @@ def main():
         print(f"bench.py measures one GPU: --gpus {args.gpus} is not supported (the method's "
               f"multi-GPU sharding is described, not built)", file=sys.stderr)
         sys.exit(2)
+    # the oracle's BLAS uses every core this process may run on
+    os.environ.setdefault("OPENBLAS_NUM_THREADS", str(len(os.sched_getaffinity(0))))
     import torch
     import fp8_kv_cache_sparse_amd as smqa
     smqa.load()
     assert torch.cuda.is_available(), "bench.py needs a GPU"
+    timer = Timer("cuda", args.flush)
     if args.stage_only:
-        measure(args.workload, args.steps, args.warmup, False, args.stage_only)
+        measure(args.workload, args.steps, args.warmup, timer, stage_only=args.stage_only)
         print(json.dumps({"stage_only": args.stage_only, "workload": args.workload}))
         return
-    main_res = measure(args.workload, args.steps, args.warmup, not args.no_graph)
+    main_res = measure(args.workload, args.steps, args.warmup, timer, primary=True)
     extra = {}
-    for nm in [x for x in args.also.split(",") if x]:
-        extra[nm] = measure(nm, args.steps, args.warmup, not args.no_graph)
+    for nm in [x for x in args.also.split(",") if x and x != args.workload]:
+        extra[nm] = measure(nm, args.steps, args.warmup, timer)
+    hbm_ref = hbm_reference(timer, "cuda")
     cpu = None if args.no_cpu else cpu_baseline(args.workload, args.cpu_seconds)
     cfg = main_res["config"]
+    med = main_res["step_us_cold"]["median"]
     line = {
         "metric": METRIC,
-        "value": main_res["tokens_scored_per_s"],
+        "value": main_res["tokens_scored_per_s_step"],
         "unit": UNIT,
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": main_res["us_per_step"] / 1e3,
-        "us_per_step": main_res["us_per_step"],
+        "ms_per_step": med / 1e3,
+        "us_per_step": med,
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -464,9 +489,11 @@ def main():
                    "indexer": f"{cfg['Hi']}x{cfg['Di']} e4m3", "k": cfg["k"],
                    "attention": f"{cfg['Hq']} heads x {cfg['D']} latent (e2m1 + e8m0/32"
                                 f"{' + f32 row scale' if cfg['rowscale'] else ''})",
-                   "window": cfg["W"], "parallelism": "none (1 GPU)"},
+                   "window": cfg["W"], "parallelism": "none (1 GPU)",
+                   "timing": f"cold ({args.flush} of 512 MiB before each rep), median of per-call HIP events"},
         "roofline": main_res["roofline"],
         "cpu_baseline": cpu,
+        "hbm_measured_GBs": hbm_ref,
         "detail": main_res,
         "also": extra,
     }

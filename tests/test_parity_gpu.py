@@ -308,8 +308,8 @@ def test_attend_with_scales_and_padding(lib):
 
 
 def test_attend_peaked_rows_respect_the_clip(lib):
-    """One dominant row decides O: a dominant window row just before the clip must be excluded,
-    one at the clip start included, and a selected global row at the k-th slot used."""
+    """One dominant row decides O: a dominant window row just before the clip must be excluded
+    and one at the clip start included."""
     wl = gen("replay_h100k", B=1, lengths=3000, replay=(3000, 128))
     s = int(wl.swa_clip[0])
     W = wl.W
@@ -326,6 +326,69 @@ def test_attend_peaked_rows_respect_the_clip(lib):
     row_incl = wl.swa[0, u_incl].view(torch.float8_e4m3fn).float()
     # head 0 of query 0 is dominated by the included row
     assert torch.allclose(out[0, 0], row_incl, rtol=1e-2, atol=1e-2)
+
+
+def _dominant_fp4_row(q_head, mag_code=0x7):
+    """E2M1 codes of a latent row whose every element is +-6 (code 0x7 / 0xF) with the sign of
+    q_head: its logit tau * 6 * sum|q| dominates every random row's."""
+    neg = (q_head < 0).to(torch.uint8)
+    nib = mag_code | (neg << 3)
+    return (nib[0::2] | (nib[1::2] << 4)).to(torch.uint8)
+
+
+def test_decode_step_dominant_rows_at_the_topk_boundary(lib):
+    """Through decode_step: the oracle's k-th best position gets a latent row that dominates
+    head 0's softmax, and the (k+1)-th best an even stronger one (1.5x the row scale).  The
+    selection keeps the k-th and drops the (k+1)-th, so head 0's output is the k-th row; a
+    boundary off by one would make it the other row (a 50% change)."""
+    wl = gen("decode_8k", lengths=6000)
+    a = np_inputs(wl)
+    S = oracle_scores_for(a, [0])[0]
+    order = np.lexsort((np.arange(S.size), -S))
+    pk, pk1 = int(order[wl.k - 1]), int(order[wl.k])
+    assert S[pk] - S[pk1] > 2e-5 * abs(S[pk])            # outside the 1e-5 band: the set is unique
+    q0 = wl.q[0, 0].float()
+    for pos, rho in ((pk, 1.0), (pk1, 1.5)):
+        wl.kv_codes[pos] = _dominant_fp4_row(q0)
+        wl.kv_e8m0[pos] = 127
+        wl.kv_rowscale[pos] = rho
+    out, lse, idx = _decode_check(lib, wl)
+    sel = set(idx[0].cpu().numpy().tolist())
+    assert pk in sel and pk1 not in sel
+    row = 6.0 * torch.sign(q0)
+    assert torch.allclose(out[0, 0], row, rtol=0, atol=1e-3)
+
+
+def test_decode_step_position_in_both_branches_counts_twice(lib):
+    """Reading R4 through decode_step: a window position that top-k also selects contributes
+    its global row and its window row as two entries of one softmax.  Both rows are made
+    dominant with logits within ~1e-3 of each other and differ in one dim d* (where |q| is
+    smallest), +6 in one and -6 in the other: counted twice, head 0's output there is ~0;
+    counted once it would be +-6."""
+    wl = gen("decode_8k", lengths=6000)
+    n = 6000
+    P = n - 5                                             # inside the window [n-128, n-1]
+    u = P - int(wl.swa_pos0[0])
+    # make P's indexer score the largest: its key follows the weighted head sum of q
+    qI = wl.qI[0].view(torch.float8_e4m3fn).float()       # [Hi, Di]
+    dirn = torch.sign((wl.w[0][:, None] * qI).sum(0))
+    wl.kI[P] = synth.encode_e4m3(dirn * 8.0)
+    q0 = wl.q[0, 0].float()
+    dstar = int(torch.argmin(q0.abs()))
+    sgn = torch.sign(q0)
+    sgn[sgn == 0] = 1.0
+    wl.kv_codes[P] = _dominant_fp4_row(sgn)
+    wl.kv_e8m0[P] = 127
+    wl.kv_rowscale[P] = 1.0
+    w_row = 6.0 * sgn
+    w_row[dstar] = -w_row[dstar]
+    wl.swa[0, u] = synth.encode_e4m3(w_row)
+    out, lse, idx = _decode_check(lib, wl)
+    assert P in set(idx[0].cpu().numpy().tolist())
+    assert abs(float(out[0, 0, dstar])) < 0.1             # both copies: (+6 - 6) / 2
+    others = torch.ones(wl.D, dtype=torch.bool, device=out.device)
+    others[dstar] = False
+    assert torch.allclose(out[0, 0][others], (6.0 * sgn)[others], rtol=0, atol=1e-2)
 
 
 # ------------------------------------------------------------------ attend over an FP8 cache
