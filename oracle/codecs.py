@@ -148,3 +148,27 @@ def window_rows(codes: np.ndarray, scale) -> np.ndarray:
     if scale is not None:
         x = x * np.asarray(scale, dtype=np.float64)[..., None]
     return x
+
+
+def mxfp8_quantize(x: np.ndarray):
+    """OCP MX v1.0 MXFP8 (E4M3) quantisation along the last axis in blocks of 32: each block
+    gets the shared exponent E = floor(log2(amax)) - emax + 127 with emax = 8 (E4M3's largest
+    normal is 1.75 * 2^8), clamped to [0, 254] (0 for an all-zero block), and each element
+    the E4M3 code of x / 2^(E - 127), nearest even, saturating at 448.  Returns (codes uint8
+    [..., n], E uint8 [..., n/32]).  Dividing by a power of two is exact, so the only
+    rounding is the E4M3 one."""
+    x = np.asarray(x, dtype=np.float64)
+    assert x.shape[-1] % 32 == 0
+    blocks = x.reshape(x.shape[:-1] + (x.shape[-1] // 32, 32))
+    amax = np.abs(blocks).max(axis=-1)
+    _, ex = np.frexp(amax)                     # amax = m * 2^ex, m in [0.5, 1): floor(log2) = ex - 1
+    E = np.where(amax > 0, np.clip(ex.astype(np.int64) - 1 - 8 + 127, 0, 254), 0)
+    y = blocks / np.ldexp(1.0, E - 127)[..., None]
+    codes = e4m3_encode(y).reshape(x.shape)
+    return codes, E.astype(np.uint8)
+
+
+def mxfp8_decode(codes: np.ndarray, E: np.ndarray) -> np.ndarray:
+    """MXFP8 codes [..., n] with block exponents [..., n/32] -> float64 values."""
+    v = e4m3(codes)
+    return v * np.repeat(e8m0(E), 32, axis=-1)

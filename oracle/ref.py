@@ -33,6 +33,10 @@ Readings where the pages are silent (each restated where it is used):
   R17 FP8 output: per (query, head) row, scale = amax / 448 and codes =
       E4M3(x * 448 / amax), nearest even, saturating at 448 (an all-zero row:
       scale 0, codes 0)
+  R18 attention on scaled matrix cores (NEXT row f4): the query is quantised
+      to OCP MXFP8 (32-dim blocks, E8M0 = floor(log2 amax) - 8 + 127 clamped
+      to [0, 254], E4M3 elements nearest even, saturating) for the logits of
+      both branches; P * V keeps the exact values
 """
 from __future__ import annotations
 
@@ -127,10 +131,11 @@ def window_positions(t, b, q_pos, swa_pos0, swa_clip, W):
 
 
 def _attend_union(q, global_of, idx, swa, swa_scale, swa_pos0, swa_clip, seq_start, q_start,
-                  q_pos, W, sm_scale):
+                  q_pos, W, sm_scale, q_values=None):
     """One softmax per (query, head) over the selected global rows plus the visible window
-    rows; global_of(cache_rows) decodes the selected rows of the global cache."""
-    qv = codecs.bf16(q)
+    rows; global_of(cache_rows) decodes the selected rows of the global cache.  q_values, when
+    given, replaces the decoded bf16 query (float64 [T, Hq, D])."""
+    qv = codecs.bf16(q) if q_values is None else np.asarray(q_values, dtype=np.float64)
     T, Hq, D = qv.shape
     seq_start = np.asarray(seq_start, dtype=np.int64)
     qs = _q_seq(q_start)
@@ -218,6 +223,25 @@ def attend_nvfp4(q, kv_codes, kv_scales, kv_rowscale, kv_global_scale, idx, swa,
                                  kv_global_scale)
     return _attend_union(q, global_of, idx, swa, swa_scale, swa_pos0, swa_clip, seq_start,
                          q_start, q_pos, W, sm_scale)
+
+
+def attend_mxfp8q(q, kv_codes, kv_e8m0, kv_rowscale, idx, swa, swa_scale, swa_pos0, swa_clip,
+                  seq_start, q_start, q_pos, W, sm_scale):
+    """`attend` with the query quantised to MXFP8 (reading R18), the numerics of attention on
+    scaled matrix cores that read the FP4 rows and their E8M0 scales as stored (blog
+    §Kernels: MegaAttention reads the NVFP4 KV natively): every (query, head) row of q is
+    cut into 32-dim blocks, each with a shared E8M0 exponent and E4M3 elements
+    (`codecs.mxfp8_quantize`), and the decoded values replace q in both branches' logits;
+    the rows, the softmax and O are those of `attend`.  Returns (O, LSE) as `attend` does."""
+    codes, E = codecs.mxfp8_quantize(codecs.bf16(q))
+    qhat = codecs.mxfp8_decode(codes, E)
+    c, e8 = np.asarray(kv_codes), np.asarray(kv_e8m0)
+    rs = None if kv_rowscale is None else np.asarray(kv_rowscale)
+
+    def global_of(rows):
+        return codecs.global_rows(c[rows], e8[rows], None if rs is None else rs[rows])
+    return _attend_union(q, global_of, idx, swa, swa_scale, swa_pos0, swa_clip, seq_start,
+                         q_start, q_pos, W, sm_scale, q_values=qhat)
 
 
 def rope_rotate(x, rope_cos, rope_sin, inverse=False):

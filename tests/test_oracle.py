@@ -643,3 +643,105 @@ def test_window_membership_hand_cases():
     assert pos.tolist() == [12, 13] and u.tolist() == [2, 3]
     u, pos = ref.window_positions(1, 0, q_pos, np.array([13]), None, 1)
     assert pos.tolist() == [13]                   # W = 1: the query's own row only
+
+
+# ---------------------------------------------------------------- MXFP8 query (reading R18)
+
+def _e4m3_nearest_brute(y: Fraction) -> int:
+    """Nearest finite E4M3 code to the exact value y (ties to the even code, saturating at
+    448), by exact comparison against every non-negative code."""
+    mag = min(abs(y), Fraction(448))
+    best = None
+    for code in range(0x7F):
+        v = Fraction(brute.e4m3_scalar(code))
+        key = (abs(v - mag), code & 1)
+        if best is None or key < best[0]:
+            best = (key, code)
+    return best[1] | 0x80 if y < 0 else best[1]
+
+
+def test_mxfp8_quantize_matches_a_scalar_brute_force():
+    """Blocks of bf16-valued numbers over a wide range of magnitudes: the shared exponent is
+    floor(log2 amax) - 8 + 127 and every element the nearest E4M3 code of x / 2^(E-127),
+    computed with exact fractions."""
+    rng = np.random.default_rng(21)
+    x = codecs.bf16(codecs.bf16_round(rng.standard_normal((6, 64)) * 2.0 ** rng.integers(-20, 20, (6, 1))))
+    codes, E = codecs.mxfp8_quantize(x)
+    for r in range(x.shape[0]):
+        for blk in range(2):
+            vals = x[r, 32 * blk:32 * blk + 32]
+            amax = max(abs(float(v)) for v in vals)
+            e_ref = math.frexp(amax)[1] - 1 - 8 + 127
+            assert E[r, blk] == e_ref
+            for i, v in enumerate(vals):
+                y = Fraction(float(v)) / Fraction(2) ** (e_ref - 127)
+                want = _e4m3_nearest_brute(y)
+                got = int(codes[r, 32 * blk + i])
+                assert got == want
+
+
+def test_mxfp8_quantize_closed_forms():
+    # amax 448: scale 1, codes as E4M3 (midpoint 1.0625 -> 1.0); a block whose amax is a power
+    # of two 2^k: E = k + 119 and the amax maps to 256 (0x78); 1.9375 * 2^k maps to 496 and
+    # saturates at 448 (0x7E); an all-zero block gets exponent 0 and zero codes
+    z = [0.0] * 28
+    x = np.array([[448.0, 1.0625, -3.0, 0.0] + z,
+                  [2.0 ** -5, 2.0 ** -13, -(2.0 ** -6), 0.0] + z,
+                  [1.9375 * 8, 1.0, 0.0, 0.0] + z,
+                  [0.0] * 32])
+    codes, E = codecs.mxfp8_quantize(x)
+    assert E[:, 0].tolist() == [127, 114, 122, 0]
+    assert codes[0, :3].tolist() == [0x7E, 0x38, 0xC4]
+    assert codes[1, :3].tolist() == [0x78, 0x38, 0xF0]
+    assert codes[2, :2].tolist() == [0x7E, 0x60]
+    assert not codes[3].any()
+    deq = codecs.mxfp8_decode(codes, E)
+    assert deq[0, 0] == 448.0 and deq[1, 0] == 2.0 ** -5 and deq[2, 0] == 448 * 2.0 ** -5
+
+
+def _mxfp8_grid_query(shape, seed):
+    """bf16 bits of a query whose 32-dim blocks lie on the MXFP8 grid exactly: E4M3 values
+    with a block amax in [256, 448] (so E8M0 = 127), times a power of two per block."""
+    rng = np.random.default_rng(seed)
+    T, H, D = shape
+    c = rng.integers(0, 0x7F, (T, H, D)).astype(np.uint8) | (rng.integers(0, 2, (T, H, D)) << 7).astype(np.uint8)
+    c[..., ::32] = 0x7C                                   # one element of every block at 384
+    v = codecs.e4m3(c) * np.repeat(2.0 ** rng.integers(-12, 4, (T, H, D // 32)), 32, axis=-1)
+    return codecs.bf16_round(v)
+
+
+def test_attend_mxfp8q_is_attend_when_q_is_on_the_grid():
+    wl = tiny(22, B=2, lengths=(40, 70))
+    a = np_inputs(wl)
+    a["q"] = _mxfp8_grid_query(a["q"].shape, 22)
+    codes, E = codecs.mxfp8_quantize(codecs.bf16(a["q"]))
+    assert np.array_equal(codecs.mxfp8_decode(codes, E), codecs.bf16(a["q"]))
+    S = ref.score(a["qI"], a["w"], a["kI"], a["kscale"], a["seq_start"], a["q_start"], a["q_pos"])
+    idx = ref.topk(S, a["k"])
+    O, L = _attend(a, idx)
+    O8, L8 = ref.attend_mxfp8q(a["q"], a["kv_codes"], a["kv_e8m0"], a["kv_rowscale"], idx, a["swa"],
+                               a["swa_scale"], a["swa_pos0"], a["swa_clip"], a["seq_start"], a["q_start"],
+                               a["q_pos"], a["W"], a["sm_scale"])
+    assert np.array_equal(O8, O) and np.array_equal(L8, L)
+
+
+@pytest.mark.parametrize("seed", [0, 1])
+def test_attend_mxfp8q_matches_brute_on_the_quantised_query(seed):
+    """The variant against the scalar-loop attention fed the quantised query: the decoded
+    MXFP8 values have at most 4 significant bits, so they are exact bf16 values."""
+    wl = synth.with_scales(tiny(30 + seed, B=2, lengths=(20, 33), Hq=2, D=64, k=8, W=6), seed=seed)
+    a = np_inputs(wl)
+    S = ref.score(a["qI"], a["w"], a["kI"], a["kscale"], a["seq_start"], a["q_start"], a["q_pos"])
+    idx = ref.topk(S, a["k"])
+    O8, L8 = ref.attend_mxfp8q(a["q"], a["kv_codes"], a["kv_e8m0"], a["kv_rowscale"], idx, a["swa"],
+                               a["swa_scale"], a["swa_pos0"], a["swa_clip"], a["seq_start"], a["q_start"],
+                               a["q_pos"], a["W"], a["sm_scale"])
+    codes, E = codecs.mxfp8_quantize(codecs.bf16(a["q"]))
+    qhat = codecs.mxfp8_decode(codes, E)
+    a2 = dict(a)
+    a2["q"] = codecs.bf16_round(qhat)
+    assert np.array_equal(codecs.bf16(a2["q"]), qhat)
+    Ob, Lb = brute_attend(a2, idx)
+    assert np.allclose(O8, Ob, rtol=1e-12, atol=1e-14) and np.allclose(L8, Lb, rtol=1e-12, atol=1e-14)
+    # and the quantisation really changed the query
+    assert not np.array_equal(qhat, codecs.bf16(a["q"]))
