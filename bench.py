@@ -346,6 +346,11 @@ def measure(name, steps, warmup, timer, primary=False, stage_only=""):
             wl.swa_scale, wl.swa_pos0, wl.swa_clip, wl.sm_scale, out=out2, lse=lse2, workspace=ws2),
             reps_stage))
         del wln
+        # Q.K^T on the scaled matrix cores with the query quantised to MXFP8 (row f4)
+        print(f"[bench] {name}: MXFP8-query scaled-MFMA attention", file=sys.stderr, flush=True)
+        fmt_us["mx_fp4_mxfp8_query"] = stats(timer.cold(lambda: smqa.sparse_mqa_attend_mxfp8q(
+            L, wl.q, wl.kv_codes, wl.kv_e8m0, wl.kv_rowscale, idx2, wl.swa, wl.swa_scale, wl.swa_pos0,
+            wl.swa_clip, wl.sm_scale, out=out2, lse=lse2, workspace=ws2), reps_stage))
         R = 32
         th = torch.arange(wl.T * R, device=dev, dtype=torch.float32).view(wl.T, R) * 0.001
         rc, rsn = th.cos().contiguous(), th.sin().contiguous()
@@ -361,6 +366,9 @@ def measure(name, steps, warmup, timer, primary=False, stage_only=""):
         formats = {"attend_us": fmt_us,
                    "fp8_over_mx_fp4_time": round(fmt_us["fp8"]["median"] / m, 3),
                    "nvfp4_over_mx_fp4_time": round(fmt_us["nvfp4"]["median"] / m, 3),
+                   "mxfp8_query_over_mx_fp4_time": round(fmt_us["mx_fp4_mxfp8_query"]["median"] / m, 3),
+                   "mxfp8_query_roofline": roofline("attend", w["attend"],
+                                                    fmt_us["mx_fp4_mxfp8_query"]["mean"] * 1e-6),
                    "global_row_bytes": {"mx_fp4": wl.D // 2 + wl.D // 32 + rs,
                                         "nvfp4": wl.D // 2 + wl.D // 16 + rs, "fp8": wl.D + 4}}
 

@@ -57,6 +57,8 @@ _SIGS = {
                                      _P, _P, _P, _S, _P]),
     "sparse_mqa_attend_nvfp4": (_I, [_LP, _P, _P, _P, _P, _F, _P, _I, _P, _P, _P, _P, _I, _I, _I,
                                      _F, _P, _P, _P, _S, _P]),
+    "sparse_mqa_attend_mxfp8q": (_I, [_LP, _P, _P, _P, _P, _P, _I, _P, _P, _P, _P, _I, _I, _I, _F,
+                                      _P, _P, _P, _S, _P]),
     "sparse_mqa_attend_fused": (_I, [_LP, _P, _P, _P, _I, _P, _P, _P, _P, _I, _P, _P, _P, _P, _I,
                                      _I, _I, _F, _P, _P, _P, _P, _P, _S, _P]),
     "smqa_attend_fused_workspace_size": (_S, [_LP, _I, _I, _I, _I]),
@@ -207,6 +209,20 @@ def topk_select(L: Batch, scores, k: int, cand=None, idx=None, workspace=None, s
 def sparse_mqa_attend(L: Batch, q, kv_codes, kv_e8m0, kv_rowscale, idx, swa, swa_scale, swa_pos0,
                       swa_clip, sm_scale: float, out=None, lse=None, workspace=None, stream=None):
     """Sparse MQA attention -> (out float32 [T, Hq, D], lse float32 [T, Hq])."""
+    return _attend_mx("sparse_mqa_attend", L, q, kv_codes, kv_e8m0, kv_rowscale, idx, swa, swa_scale,
+                      swa_pos0, swa_clip, sm_scale, out, lse, workspace, stream)
+
+
+def sparse_mqa_attend_mxfp8q(L: Batch, q, kv_codes, kv_e8m0, kv_rowscale, idx, swa, swa_scale, swa_pos0,
+                             swa_clip, sm_scale: float, out=None, lse=None, workspace=None, stream=None):
+    """Sparse MQA attention on the scaled matrix cores with the query quantised to MXFP8
+    -> (out float32 [T, Hq, D], lse float32 [T, Hq])."""
+    return _attend_mx("sparse_mqa_attend_mxfp8q", L, q, kv_codes, kv_e8m0, kv_rowscale, idx, swa,
+                      swa_scale, swa_pos0, swa_clip, sm_scale, out, lse, workspace, stream)
+
+
+def _attend_mx(entry, L, q, kv_codes, kv_e8m0, kv_rowscale, idx, swa, swa_scale, swa_pos0, swa_clip,
+               sm_scale, out, lse, workspace, stream):
     lib = load()
     _dev(q, "q", torch.bfloat16, 3)
     _dev(kv_codes, "kv_codes", torch.uint8, 2)
@@ -230,10 +246,10 @@ def sparse_mqa_attend(L: Batch, q, kv_codes, kv_e8m0, kv_rowscale, idx, swa, swa
     if workspace is None:
         workspace = _workspace(need, q.device)
     wp, wb = _ws_ptr(workspace)
-    _check(lib.sparse_mqa_attend(L.ref, _ptr(q), _ptr(kv_codes), _ptr(kv_e8m0), _ptr(kv_rowscale),
-                                 _ptr(idx), k, _ptr(swa), _ptr(swa_scale), _ptr(swa_pos0),
-                                 _ptr(swa_clip), W, Hq, D, float(sm_scale), _ptr(out), _ptr(lse),
-                                 wp, wb, _stream(stream)))
+    _check(getattr(lib, entry)(L.ref, _ptr(q), _ptr(kv_codes), _ptr(kv_e8m0), _ptr(kv_rowscale),
+                               _ptr(idx), k, _ptr(swa), _ptr(swa_scale), _ptr(swa_pos0),
+                               _ptr(swa_clip), W, Hq, D, float(sm_scale), _ptr(out), _ptr(lse),
+                               wp, wb, _stream(stream)))
     return out, lse
 
 

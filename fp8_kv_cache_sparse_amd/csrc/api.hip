@@ -363,6 +363,33 @@ int sparse_mqa_attend_nvfp4(const smqa_layout* L, const uint16_t* q_bf16, const 
   return e == hipSuccess ? SMQA_OK : hip_fail(e, "sparse_mqa_attend_nvfp4 launch");
 }
 
+int sparse_mqa_attend_mxfp8q(const smqa_layout* L, const uint16_t* q_bf16, const uint8_t* kv_codes,
+                             const uint8_t* kv_e8m0, const float* kv_rowscale, const int32_t* idx,
+                             int32_t k, const uint8_t* swa_fp8, const float* swa_scale,
+                             const int32_t* swa_pos0, const int32_t* swa_clip, int32_t W, int32_t Hq,
+                             int32_t D, float sm_scale, float* out, float* lse, void* workspace,
+                             size_t workspace_bytes, void* stream) {
+  g_err.clear();
+  int st = check_layout(L);
+  if (st) return st;
+  if (L->num_q == 0) return SMQA_OK;
+  st = check_attend(q_bf16, kv_codes, kv_e8m0, kv_rowscale, idx, k, swa_fp8, swa_scale, swa_pos0,
+                    swa_clip, W, Hq, D, sm_scale, out, lse, true);
+  if (st) return st;
+  st = check_plan(L, k, W, Hq, D);
+  if (st) return st;
+  if (Hq % 32 != 0 || D > 1664)
+    return fail(SMQA_ERR_UNSUPPORTED, "MXFP8-query attention: Hq = %d, D = %d; supported Hq %% 32 == 0, D <= 1664",
+                Hq, D);
+  st = check_ws(workspace, workspace_bytes, smqa::attend_workspace_bytes(L->num_q, k, W, Hq, D));
+  if (st) return st;
+  smqa::AttendArgs a{L->seq_start, L->q_start, L->q_pos, L->num_seqs, L->num_q, q_bf16, kv_codes,
+                     kv_e8m0, kv_rowscale, idx, k, swa_fp8, swa_scale, swa_pos0, swa_clip, W, Hq, D,
+                     sm_scale, out, lse, workspace, smqa::kKvMXN, 1.0f, 1.0f};
+  hipError_t e = smqa::launch_attend_fmt(a, (hipStream_t)stream);
+  return e == hipSuccess ? SMQA_OK : hip_fail(e, "sparse_mqa_attend_mxfp8q launch");
+}
+
 int sparse_mqa_attend_fused(const smqa_layout* L, const uint16_t* q_bf16, const float* rope_cos,
                             const float* rope_sin, int32_t rope_pairs, const uint8_t* kv_codes,
                             const uint8_t* kv_e8m0, const float* kv_rowscale, const int32_t* idx,

@@ -1291,7 +1291,8 @@ hipError_t launch_attend_fused(const AttendArgs& a0, hipStream_t s) {
 hipError_t launch_attend_fmt(const AttendArgs& a, hipStream_t s) {
   if (a.T == 0) return hipSuccess;
   const AttPlan p = attend_plan(a.T, a.k, a.W, a.Hq, a.D);
-  if (p.S == 0 || !p.wide || a.D > 1664 || (a.kv_fmt != kKvFP8 && a.kv_fmt != kKvNV)) return hipErrorInvalidValue;
+  if (p.S == 0 || !p.wide || a.D > 1664 || (a.kv_fmt != kKvFP8 && a.kv_fmt != kKvNV && a.kv_fmt != kKvMXN))
+    return hipErrorInvalidValue;
   return launch_attend_sd(a, p.S, s);
 }
 

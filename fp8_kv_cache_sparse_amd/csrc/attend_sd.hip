@@ -81,8 +81,12 @@ constexpr int align16(int x) { return (x + 15) & ~15; }
 // plain kernel keeps its registers and neither ends in a branch between two epilogues):
 // kMXF, query RoPE and the FP8 epilogue in the kernel (one split), and kMXR, query RoPE
 // with split partials for attend_fused_epilogue_kernel.
-constexpr int kMX = kKvMX, kFP8 = kKvFP8, kNV = kKvNV, kMXF = kKvMXF, kMXR = kKvMXR;
-constexpr bool mx_like(int F) { return F == kMX || F == kMXF || F == kMXR; }
+// kMXN: the MX format with Q.K^T on the scaled matrix cores (v_mfma_scale_f32_32x32x64_
+// f8f6f4): the query is quantised to MXFP8 in the prologue, the gathered E2M1 codes and their
+// E8M0 bytes are the B operand and its scale as they sit in LDS, window rows are E4M3 with
+// scale 2^0; P.V is the MX one.
+constexpr int kMX = kKvMX, kFP8 = kKvFP8, kNV = kKvNV, kMXF = kKvMXF, kMXR = kKvMXR, kMXN = kKvMXN;
+constexpr bool mx_like(int F) { return F == kMX || F == kMXF || F == kMXR || F == kMXN; }
 
 // LDS geometry for latent width D and global format F (compile time, so every offset is an
 // immediate).
@@ -420,9 +424,60 @@ __global__ __launch_bounds__(kThreads) void attend_kernel(AttendArgs a, int S, i
     for (int u = 0; u < 3; ++u)
       if (c.tb + u < c.te && c.tb + u < c.ng) load_pos(c.tb + u, u);
   }
+  // kMXN: the query as the fp8 A operand of the scaled MFMA, one register octet per pair of
+  // this wave's blocks (K-block 0 = b0 + 2j, K-block 1 = b0 + 2j + 1).  Lane (r32, kh) holds
+  // dims 32 bA + 16 kh .. +16 of head h0 + r32 in bytes 0..15 and 32 bB + 16 kh .. +16 in
+  // bytes 16..31, and supplies the E8M0 scale of K-block kh (the instruction takes K-block
+  // b's scale from lane r32 + 32 b).  OCP MXFP8: E = floor(log2 amax) - 8 + 127 per 32-dim
+  // block (clamped at 0; 0 for a zero block), elements E4M3(x / 2^(E-127)), nearest even,
+  // saturated at 448.  A block's 32 values are split over lanes l and l ^ 32.
+  constexpr int NP = (G::NBW + 1) / 2;
+  v8i qf[NP];
+  int qsc[NP];
+  if constexpr (F == kMXN) {
+    SMQA_LANE_ROLES
+    const int nbw = G::BPW + (wave < G::EXTRA ? 1 : 0);
+    const uint16_t* qrow = a.q + ((int64_t)t * a.Hq + h0 + r32) * D + 16 * kh;
+#pragma unroll
+    for (int j = 0; j < NP; ++j) {
+      v4u raw[2][2];
+      int ex[2];
+#pragma unroll
+      for (int hb = 0; hb < 2; ++hb) {
+        const bool ok = 2 * j + hb < nbw;
+        const uint16_t* src = qrow + 32 * (b0 + 2 * j + hb);
+        raw[hb][0] = ok ? *(const v4u*)src : v4u{0u, 0u, 0u, 0u};
+        raw[hb][1] = ok ? *(const v4u*)(src + 8) : v4u{0u, 0u, 0u, 0u};
+        unsigned m = 0u;                             // |x| as bf16 magnitude bits
+#pragma unroll
+        for (int pc = 0; pc < 2; ++pc)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) m = max(m, max(raw[hb][pc][e] & 0x7FFFu, (raw[hb][pc][e] >> 16) & 0x7FFFu));
+        m = max(m, (unsigned)__shfl_xor((int)m, 32));
+        // floor(log2 amax) + 127 is the bf16 exponent field (normal amax); subnormal or zero
+        // blocks give E = 0
+        ex[hb] = max((int)(m >> 7) - 8, 0);
+      }
+      qsc[j] = kh ? ex[1] : ex[0];
+#pragma unroll
+      for (int hb = 0; hb < 2; ++hb) {
+        const float mul = e8m0_to_float(254 - ex[hb]);   // 2^(127 - E), exact scaling
+#pragma unroll
+        for (int dd = 0; dd < 4; ++dd) {
+          const unsigned w0 = raw[hb][dd >> 1][2 * (dd & 1)], w1 = raw[hb][dd >> 1][2 * (dd & 1) + 1];
+          auto q8 = [&](unsigned bits) {
+            return __builtin_amdgcn_fmed3f(__uint_as_float(bits) * mul, -448.0f, 448.0f);
+          };
+          int wd = __builtin_amdgcn_cvt_pk_fp8_f32(q8(w0 << 16), q8(w0 & 0xFFFF0000u), 0, false);
+          wd = __builtin_amdgcn_cvt_pk_fp8_f32(q8(w1 << 16), q8(w1 & 0xFFFF0000u), wd, true);
+          qf[j][4 * hb + dd] = wd;
+        }
+      }
+    }
+  }
   // A operands of Q.K^T: head h0 + r32, dims 32 b + 16 kh + 8 cc .. +8 of block b = b0 + i
   v8bf qa[G::NBW][2];
-  {
+  if constexpr (F != kMXN) {
     SMQA_LANE_ROLES
     const uint16_t* qrow = a.q + ((int64_t)t * a.Hq + h0 + r32) * D + 16 * kh;
 #pragma unroll
@@ -506,7 +561,41 @@ __global__ __launch_bounds__(kThreads) void attend_kernel(AttendArgs a, int S, i
     v16f acc;
 #pragma unroll
     for (int e = 0; e < 16; ++e) acc[e] = 0.0f;
-    if constexpr (decltype(FP4)::value) {
+    if constexpr (F == kMXN) {
+      const int nbw = G::BPW + (wave < G::EXTRA ? 1 : 0);
+      if constexpr (decltype(FP4)::value) {
+        // B = K^T in E2M1 as stored: lane (r32, kh) holds the 32 codes of row r32 in K-block
+        // kh (block b0 + 2j + kh, 16 bytes) and that block's E8M0 byte is its scale.  A half
+        // past this wave's blocks reads in-bounds LDS and is replaced by zeros.
+        const uint8_t* rowp = B + r32 * G::RS4 + 16 * b0;
+        const uint8_t* e8p = B + G::E8 + r32 * G::E8S + b0;
+#pragma unroll
+        for (int j = 0; j < NP; ++j) {
+          if (2 * j < nbw) {
+            const int blk = 2 * j + kh;
+            const bool ok = blk < nbw;
+            const v4u w = lds<v4u>(rowp + 16 * blk);
+            const int sb = ok ? (int)lds<uint8_t>(e8p + blk) : 127;
+            const v8i bv = {ok ? (int)w.x : 0, ok ? (int)w.y : 0, ok ? (int)w.z : 0, ok ? (int)w.w : 0, 0, 0, 0, 0};
+            acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(qf[j], bv, acc, 0, 4, 0, qsc[j], 0, sb);
+          }
+        }
+      } else {
+        // B = window rows in E4M3 (scale 2^0): lane (r32, kh) holds dims 32 bA + 16 kh .. +16
+        // in bytes 0..15 and 32 bB + 16 kh .. +16 in bytes 16..31 of row r32 & 15
+        const uint8_t* rowp = B + (r32 & 15) * G::RS8 + 16 * kh + 32 * b0;
+#pragma unroll
+        for (int j = 0; j < NP; ++j) {
+          if (2 * j < nbw) {
+            const v4u w0 = lds<v4u>(rowp + 64 * j);
+            v4u w1 = {0u, 0u, 0u, 0u};
+            if (2 * j + 1 < nbw) w1 = lds<v4u>(rowp + 64 * j + 32);
+            const v8i bv = {(int)w0.x, (int)w0.y, (int)w0.z, (int)w0.w, (int)w1.x, (int)w1.y, (int)w1.z, (int)w1.w};
+            acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(qf[j], bv, acc, 0, 0, 0, qsc[j], 0, 127);
+          }
+        }
+      }
+    } else if constexpr (decltype(FP4)::value) {
       const uint8_t* rowp = B + r32 * G::RS4 + 8 * kh + 16 * b0;
       const uint8_t* e8p = B + G::E8 + r32 * G::E8S + b0;
       const uint8_t* nvp = B + G::E8 + r32 * 4 + kh;
@@ -995,6 +1084,7 @@ hipError_t launch_attend_sd(const AttendArgs& a, int S, hipStream_t s) {
   case d:                                                         \
     return a.kv_fmt == sd::kFP8   ? sd::launch<d, sd::kFP8>(a, S, s)  \
            : a.kv_fmt == sd::kNV  ? sd::launch<d, sd::kNV>(a, S, s)   \
+           : a.kv_fmt == sd::kMXN ? sd::launch<d, sd::kMXN>(a, S, s)  \
            : a.kv_fmt == sd::kMXF ? sd::launch<d, sd::kMXF>(a, S, s)  \
            : a.kv_fmt == sd::kMXR ? sd::launch<d, sd::kMXR>(a, S, s)  \
                                   : sd::launch<d, sd::kMX>(a, S, s);

@@ -144,7 +144,9 @@ hipError_t launch_topk_from_hist(const TopkArgs& a, hipStream_t s);
 // 16, tensor scale kv_gscale.  kKvMXF / kKvMXR: the MX format with MegaAttention's fused query
 // RoPE and FP8 epilogue, in the attention kernel (one split) / through split partials (set by
 // launch_attend_fused only).
-enum KvFmt : int32_t { kKvMX = 0, kKvFP8 = 1, kKvNV = 2, kKvMXF = 3, kKvMXR = 4 };
+// kKvMXN: the MX format with Q.K^T on the scaled matrix cores, the query quantised to
+// MXFP8 in the kernel and the E2M1 rows and their E8M0 bytes consumed as stored.
+enum KvFmt : int32_t { kKvMX = 0, kKvFP8 = 1, kKvNV = 2, kKvMXF = 3, kKvMXR = 4, kKvMXN = 5 };
 
 struct AttendArgs {
   const int64_t* seq_start;
@@ -184,7 +186,7 @@ struct AttendArgs {
 int attend_splits(int32_t T, int32_t k, int32_t W, int32_t Hq, int32_t D, int32_t* lds = nullptr);
 size_t attend_workspace_bytes(int32_t T, int32_t k, int32_t W, int32_t Hq, int32_t D);
 hipError_t launch_attend(const AttendArgs& a, hipStream_t s);
-hipError_t launch_attend_fmt(const AttendArgs& a, hipStream_t s);
+hipError_t launch_attend_fmt(const AttendArgs& a, hipStream_t s);   // kKvFP8, kKvNV, kKvMXN
 size_t attend_fused_workspace_bytes(int32_t T, int32_t k, int32_t W, int32_t Hq, int32_t D);
 hipError_t launch_attend_fused(const AttendArgs& a, hipStream_t s);
 

@@ -254,6 +254,33 @@ int sparse_mqa_attend_nvfp4(const smqa_layout* L,
                             void* stream);
 
 /*
+ * sparse_mqa_attend_mxfp8q — sparse_mqa_attend with Q.K^T on gfx950's scaled matrix
+ * cores (v_mfma_scale_f32_32x32x64_f8f6f4), which read the gathered E2M1 rows and their
+ * E8M0 block exponents as stored (blog §Kernels: MegaAttention reads the NVFP4 KV
+ * natively).  Their other operand is 8-bit, so the query is quantised to OCP MXFP8 first:
+ * per (query, head) and 32-dim block, E = floor(log2 amax) - 8 + 127 (clamped at 0; 0 for
+ * a zero block) and elements E4M3(q / 2^(E-127)), nearest even, saturating at 448.  Both
+ * branches' logits use that quantised query (window rows enter as E4M3 with scale 2^0);
+ * the softmax, P*V (exact fp16 values, as in sparse_mqa_attend) and the outputs are those
+ * of sparse_mqa_attend, as are the arguments, layout, workspace
+ * (smqa_attend_workspace_size) and errors.
+ * Limits: those of sparse_mqa_attend plus Hq % 32 == 0 and D <= 1664.
+ * Arithmetic: the products of the MXFP8 query and the E2M1 / E4M3 rows are exact; each
+ * instruction sums its 64 products with an internal error of about 1e-5 of their
+ * absolute sum before the fp32 accumulation.
+ */
+int sparse_mqa_attend_mxfp8q(const smqa_layout* L,
+                             const uint16_t* q_bf16,
+                             const uint8_t* kv_codes, const uint8_t* kv_e8m0, const float* kv_rowscale,
+                             const int32_t* idx, int32_t k,
+                             const uint8_t* swa_fp8, const float* swa_scale,
+                             const int32_t* swa_pos0, const int32_t* swa_clip,
+                             int32_t W, int32_t Hq, int32_t D, float sm_scale,
+                             float* out, float* lse,
+                             void* workspace, size_t workspace_bytes,
+                             void* stream);
+
+/*
  * sparse_mqa_attend_fused — MegaAttention's fused form (blog §Kernels,
  * "MegaAttention avec KV compressé NVFP4": query RoPE, the sparse attention,
  * inverse RoPE on the output and FP8 conversion in one pass, written for the

@@ -29,6 +29,7 @@ def test_header_declares_the_boundary():
     names = declared_functions()
     for n in ("sparse_mqa_score", "topk_select", "sparse_mqa_attend", "sparse_mqa_attend_fp8kv",
               "sparse_mqa_attend_nvfp4", "sparse_mqa_attend_fused", "smqa_attend_fused_workspace_size",
+              "sparse_mqa_attend_mxfp8q",
               "decode_step_fused", "decode_step_noalloc",
               "decode_step",
               "smqa_topk_workspace_size", "smqa_attend_workspace_size",
@@ -284,3 +285,21 @@ def test_decode_step_noalloc_rejects_before_any_hip_call():
     for B, T, n in ((1, 1, 8192), (32, 32, 65536), (4, 4, 524288)):
         Lb = layout(T=T, B=B, max_ctx=n)
         assert 0 < lib().smqa_decode_step_workspace_size(ctypes.byref(Lb), 2048, 0, 128, 64, 1664) <= cap
+
+
+def test_attend_mxfp8q_validation():
+    L = layout()
+
+    def call(Lx=L, **kw):
+        a = dict(q=A16, c=A16, e=A4, rs=None, idx=A4, k=2048, swa=A16, ss=None, p0=A4, clip=None, W=128,
+                 Hq=64, D=1664, sc=0.0245, out=A16, lse=None, ws=None, nb=0)
+        a.update(kw)
+        return lib().sparse_mqa_attend_mxfp8q(ctypes.byref(Lx), a["q"], a["c"], a["e"], a["rs"], a["idx"],
+                                              a["k"], a["swa"], a["ss"], a["p0"], a["clip"], a["W"], a["Hq"],
+                                              a["D"], a["sc"], a["out"], a["lse"], a["ws"], a["nb"], None)
+    assert call(Hq=48) == -4 and "MXFP8" in err()
+    assert call(D=1792) == -4 and call(D=1600) == -4
+    assert call(c=None) == -1 and call(e=None) == -1 and call(idx=None) == -1
+    assert call(c=A16 + 4) == -3
+    assert call() == -5                                      # split partials need the workspace
+    assert call(Lx=layout(T=0)) == 0

@@ -498,6 +498,64 @@ def test_attend_nvfp4_window_only_and_padding(lib):
     _attend_nv_check(lib, wl, idx)
 
 
+# ------------------------------------------------------------------ scaled matrix cores, MXFP8 query
+
+def _attend_mx8q_check(lib, wl, idx_np=None):
+    a = np_inputs(wl)
+    if idx_np is None:
+        S = ref.score(a["qI"], a["w"], a["kI"], a["kscale"], a["seq_start"], a["q_start"], a["q_pos"])
+        idx_np = ref.topk(S, wl.k)
+    idx = torch.tensor(idx_np, dtype=torch.int32, device=DEV)
+    announce(f"attend_mxfp8q {wl.name} T={wl.T} Hq={wl.Hq} D={wl.D} k={wl.k}")
+    out, lse = lib.sparse_mqa_attend_mxfp8q(lib.Batch(wl.seq_start, wl.q_start, wl.q_pos, wl.max_ctx), wl.q,
+                                            wl.kv_codes, wl.kv_e8m0, wl.kv_rowscale, idx, wl.swa, wl.swa_scale,
+                                            wl.swa_pos0, wl.swa_clip, wl.sm_scale)
+    sync()
+    args = (a["kv_codes"], a["kv_e8m0"], a["kv_rowscale"], idx_np, a["swa"], a["swa_scale"], a["swa_pos0"],
+            a["swa_clip"], a["seq_start"], a["q_start"], a["q_pos"], a["W"], a["sm_scale"])
+    O, L = ref.attend_mxfp8q(a["q"], *args)
+    ok, msg = close_attention(out.cpu().numpy(), O, lse.cpu().numpy(), L)
+    assert ok, msg
+    return out, lse, O, ref.attend(a["q"], *args)[0]
+
+
+# Whole and partial tiles, several splits (decode) and one (replay), an odd number of 32-dim
+# blocks per wave (D = 640: 3 and 2; D = 128: one block on waves 0..3, none on 4..7), the
+# clipped replay window, with and without row scales.
+@pytest.mark.parametrize("name,kw,scales", [
+    ("decode_8k", dict(lengths=6000), True),
+    ("decode_8k", dict(B=3, lengths=(300, 2000), k=1000, W=100, rowscale=False), False),
+    ("decode_8k", dict(B=2, lengths=1500, Hq=32, D=128, k=256), True),
+    ("decode_8k", dict(B=2, lengths=1500, Hq=64, D=512, k=256), False),
+    ("decode_8k", dict(B=2, lengths=(700, 1500), Hq=32, D=640, k=300), True),
+    ("replay_h100k", dict(B=2, lengths=4000, replay=(4000, 128)), True),
+])
+def test_attend_mxfp8q(lib, name, kw, scales):
+    wl = gen(name, **kw)
+    if scales:
+        wl = synth.with_scales(wl)
+    out, _, O8, O = _attend_mx8q_check(lib, wl)
+    # the variant is not the plain attention: quantising q moves O well past the bar
+    assert np.abs(O8 - O).max() > 1e-3
+
+
+def test_attend_mxfp8q_window_only_and_padding(lib):
+    """Every index -1 (window rows only; query 0 sees none), then a selection padded with -1."""
+    import dataclasses
+    wl = gen("replay_h100k", B=1, lengths=2000, replay=(2000, 4))
+    clip = wl.swa_clip.clone()
+    clip[0] = wl.q_pos[0] + 1
+    wl = dataclasses.replace(wl, swa_clip=clip)
+    out, lse, _, _ = _attend_mx8q_check(lib, wl, np.full((wl.T, wl.k), -1, dtype=np.int32))
+    assert torch.all(out[0] == 0) and torch.all(torch.isneginf(lse[0]))
+    wl = gen("decode_8k", B=2, lengths=(1500, 2500), k=2048)
+    a = np_inputs(wl)
+    S = ref.score(a["qI"], a["w"], a["kI"], a["kscale"], a["seq_start"], a["q_start"], a["q_pos"])
+    idx = ref.topk(S, wl.k)
+    assert (idx == -1).any()
+    _attend_mx8q_check(lib, wl, idx)
+
+
 # ------------------------------------------------------------------ fused RoPE / FP8 epilogue
 
 def _angles(T, R, seed):
