@@ -14,7 +14,12 @@
 //            padded so both read patterns below are bank-conflict free), issued by all 8
 //            waves (waves 0-3 before their products, waves 4-7 after them); the raw E8M0
 //            bytes and the row scales land beside them.  Tile i+2 is in flight while tile
-//            i is scored and tile i-1 is accumulated.
+//            i is scored and tile i-1 is accumulated; a workgroup with at most four tiles
+//            (short contexts split over many workgroups) gathers all of them at once, so
+//            it waits for memory once instead of once per tile.
+//   q        staged through the idle tile buffers with coalesced direct-to-LDS loads, in
+//            the same round trip as the positions of the first tiles, then read into the
+//            MFMA operand registers.
 //   Q.K^T    v_mfma_f32_32x32x16_bf16, heads x rows: each lane reads 8 dims of one row
 //            (ds_read_b32 for E2M1, ds_read_b64 for E4M3) and converts them exactly to
 //            bf16 with the block's E8M0 scale (v_cvt_scalef32_pk_bf16_*); q stays in
@@ -421,105 +426,134 @@ __global__ __launch_bounds__(kThreads) void attend_kernel(AttendArgs a, int S, i
   // ---- prologue: positions of the first three tiles, q and the per-query values (one
   // round trip), then the rows of the first two tiles
   if (wave == 0) {
-    for (int u = 0; u < 3; ++u)
+    for (int u = 0; u < kNBuf; ++u)
       if (c.tb + u < c.te && c.tb + u < c.ng) load_pos(c.tb + u, u);
   }
-  // kMXN: the query as the fp8 A operand of the scaled MFMA, one register octet per pair of
-  // this wave's blocks (K-block 0 = b0 + 2j, K-block 1 = b0 + 2j + 1).  Lane (r32, kh) holds
-  // dims 32 bA + 16 kh .. +16 of head h0 + r32 in bytes 0..15 and 32 bB + 16 kh .. +16 in
-  // bytes 16..31, and supplies the E8M0 scale of K-block kh (the instruction takes K-block
-  // b's scale from lane r32 + 32 b).  OCP MXFP8: E = floor(log2 amax) - 8 + 127 per 32-dim
-  // block (clamped at 0; 0 for a zero block), elements E4M3(x / 2^(E-127)), nearest even,
-  // saturated at 448.  A block's 32 values are split over lanes l and l ^ 32.
   constexpr int NP = (G::NBW + 1) / 2;
   v8i qf[NP];
   int qsc[NP];
-  if constexpr (F == kMXN) {
-    SMQA_LANE_ROLES
-    const int nbw = G::BPW + (wave < G::EXTRA ? 1 : 0);
-    const uint16_t* qrow = a.q + ((int64_t)t * a.Hq + h0 + r32) * D + 16 * kh;
-#pragma unroll
-    for (int j = 0; j < NP; ++j) {
-      v4u raw[2][2];
-      int ex[2];
-#pragma unroll
-      for (int hb = 0; hb < 2; ++hb) {
-        const bool ok = 2 * j + hb < nbw;
-        const uint16_t* src = qrow + 32 * (b0 + 2 * j + hb);
-        raw[hb][0] = ok ? *(const v4u*)src : v4u{0u, 0u, 0u, 0u};
-        raw[hb][1] = ok ? *(const v4u*)(src + 8) : v4u{0u, 0u, 0u, 0u};
-        unsigned m = 0u;                             // |x| as bf16 magnitude bits
-#pragma unroll
-        for (int pc = 0; pc < 2; ++pc)
-#pragma unroll
-          for (int e = 0; e < 4; ++e) m = max(m, max(raw[hb][pc][e] & 0x7FFFu, (raw[hb][pc][e] >> 16) & 0x7FFFu));
-        m = max(m, (unsigned)__shfl_xor((int)m, 32));
-        // floor(log2 amax) + 127 is the bf16 exponent field (normal amax); subnormal or zero
-        // blocks give E = 0
-        ex[hb] = max((int)(m >> 7) - 8, 0);
-      }
-      qsc[j] = kh ? ex[1] : ex[0];
-#pragma unroll
-      for (int hb = 0; hb < 2; ++hb) {
-        const float mul = e8m0_to_float(254 - ex[hb]);   // 2^(127 - E), exact scaling
-#pragma unroll
-        for (int dd = 0; dd < 4; ++dd) {
-          const unsigned w0 = raw[hb][dd >> 1][2 * (dd & 1)], w1 = raw[hb][dd >> 1][2 * (dd & 1) + 1];
-          auto q8 = [&](unsigned bits) {
-            return __builtin_amdgcn_fmed3f(__uint_as_float(bits) * mul, -448.0f, 448.0f);
-          };
-          int wd = __builtin_amdgcn_cvt_pk_fp8_f32(q8(w0 << 16), q8(w0 & 0xFFFF0000u), 0, false);
-          wd = __builtin_amdgcn_cvt_pk_fp8_f32(q8(w1 << 16), q8(w1 & 0xFFFF0000u), wd, true);
-          qf[j][4 * hb + dd] = wd;
+  v8bf qa[G::NBW][2];
+  // q of the 32 heads: staged in LDS by coalesced loads (rows QS bytes apart: 16 mod 256, so
+  // the per-lane 16-byte reads below hit 16 distinct bank quads per 16 lanes), except for the
+  // fused RoPE forms, whose rotation tables are read beside q straight from global memory.
+  // qget: the 8 bf16 from element e of head h0 + r32's dims 16 kh ..
+  constexpr bool QLDS = !(F == kMXF || F == kMXR);
+  constexpr int QS = 2 * D + 16;
+  static_assert(32 * QS <= kNBuf * G::BUF, "q is staged in the idle tile buffers");
+  auto qget = [&](int r32, int kh, int e) __attribute__((always_inline)) -> v4u {
+    if constexpr (QLDS) return lds<v4u>(smem + r32 * QS + 32 * kh + 2 * e);
+    else return *(const v4u*)(a.q + ((int64_t)t * a.Hq + h0 + r32) * D + 16 * kh + e);
+  };
+  auto build_q = [&]() __attribute__((always_inline)) {
+    // kMXN: the query as the fp8 A operand of the scaled MFMA, one register octet per pair of
+    // this wave's blocks (K-block 0 = b0 + 2j, K-block 1 = b0 + 2j + 1).  Lane (r32, kh) holds
+    // dims 32 bA + 16 kh .. +16 of head h0 + r32 in bytes 0..15 and 32 bB + 16 kh .. +16 in
+    // bytes 16..31, and supplies the E8M0 scale of K-block kh (the instruction takes K-block
+    // b's scale from lane r32 + 32 b).  OCP MXFP8: E = floor(log2 amax) - 8 + 127 per 32-dim
+    // block (clamped at 0; 0 for a zero block), elements E4M3(x / 2^(E-127)), nearest even,
+    // saturated at 448.  A block's 32 values are split over lanes l and l ^ 32.
+    if constexpr (F == kMXN) {
+      SMQA_LANE_ROLES
+      const int nbw = G::BPW + (wave < G::EXTRA ? 1 : 0);
+  #pragma unroll
+      for (int j = 0; j < NP; ++j) {
+        v4u raw[2][2];
+        int ex[2];
+  #pragma unroll
+        for (int hb = 0; hb < 2; ++hb) {
+          const bool ok = 2 * j + hb < nbw;
+          const int e0 = 32 * (b0 + 2 * j + hb);
+          raw[hb][0] = ok ? qget(r32, kh, e0) : v4u{0u, 0u, 0u, 0u};
+          raw[hb][1] = ok ? qget(r32, kh, e0 + 8) : v4u{0u, 0u, 0u, 0u};
+          unsigned m = 0u;                             // |x| as bf16 magnitude bits
+  #pragma unroll
+          for (int pc = 0; pc < 2; ++pc)
+  #pragma unroll
+            for (int e = 0; e < 4; ++e) m = max(m, max(raw[hb][pc][e] & 0x7FFFu, (raw[hb][pc][e] >> 16) & 0x7FFFu));
+          m = max(m, (unsigned)__shfl_xor((int)m, 32));
+          // floor(log2 amax) + 127 is the bf16 exponent field (normal amax); subnormal or zero
+          // blocks give E = 0
+          ex[hb] = max((int)(m >> 7) - 8, 0);
+        }
+        qsc[j] = kh ? ex[1] : ex[0];
+  #pragma unroll
+        for (int hb = 0; hb < 2; ++hb) {
+          const float mul = e8m0_to_float(254 - ex[hb]);   // 2^(127 - E), exact scaling
+  #pragma unroll
+          for (int dd = 0; dd < 4; ++dd) {
+            const unsigned w0 = raw[hb][dd >> 1][2 * (dd & 1)], w1 = raw[hb][dd >> 1][2 * (dd & 1) + 1];
+            auto q8 = [&](unsigned bits) {
+              return __builtin_amdgcn_fmed3f(__uint_as_float(bits) * mul, -448.0f, 448.0f);
+            };
+            int wd = __builtin_amdgcn_cvt_pk_fp8_f32(q8(w0 << 16), q8(w0 & 0xFFFF0000u), 0, false);
+            wd = __builtin_amdgcn_cvt_pk_fp8_f32(q8(w1 << 16), q8(w1 & 0xFFFF0000u), wd, true);
+            qf[j][4 * hb + dd] = wd;
+          }
         }
       }
     }
-  }
-  // A operands of Q.K^T: head h0 + r32, dims 32 b + 16 kh + 8 cc .. +8 of block b = b0 + i
-  v8bf qa[G::NBW][2];
-  if constexpr (F != kMXN) {
-    SMQA_LANE_ROLES
-    const uint16_t* qrow = a.q + ((int64_t)t * a.Hq + h0 + r32) * D + 16 * kh;
-#pragma unroll
-    for (int i = 0; i < G::NBW; ++i)
-#pragma unroll
-      for (int cc = 0; cc < 2; ++cc) {
-        v4u v = {0u, 0u, 0u, 0u};
-        if (i < G::BPW || wave < G::EXTRA) v = *(const v4u*)(qrow + 32 * (b0 + i) + 8 * cc);
-        if constexpr (F == kMXF || F == kMXR) {
-          // fused query RoPE (blog §Kernels, MegaAttention): the pairs (2j, 2j+1) of the last
-          // 2 * rope_pairs dims rotate by query t's angle, rounded once to bf16 (RNE).  In
-          // fp64 the products of a bf16 and an fp32 value are exact, so each output is the
-          // exact rotation rounded once to fp64 and then once to bf16.
-          const int r0 = D - 2 * a.rope_pairs;
-          const int d0 = 32 * (b0 + i) + 16 * kh + 8 * cc;
-          if (a.rope_pairs > 0 && d0 >= r0 && (i < G::BPW || wave < G::EXTRA)) {
-            const int64_t pj = (int64_t)t * a.rope_pairs + (d0 - r0) / 2;
-            const v4f cs = *(const v4f*)(a.rope_cos + pj);
-            const v4f sn = *(const v4f*)(a.rope_sin + pj);
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-              const double x0 = __uint_as_float(v[j] << 16), x1 = __uint_as_float(v[j] & 0xFFFF0000u);
-              const double c = cs[j], sj = sn[j];
-              const double y0 = __builtin_fma(x0, c, -(x1 * sj));
-              const double y1 = __builtin_fma(x0, sj, x1 * c);
-              v[j] = bf16_rne(y0) | (bf16_rne(y1) << 16);
+    // A operands of Q.K^T: head h0 + r32, dims 32 b + 16 kh + 8 cc .. +8 of block b = b0 + i
+    if constexpr (F != kMXN) {
+      SMQA_LANE_ROLES
+  #pragma unroll
+      for (int i = 0; i < G::NBW; ++i)
+  #pragma unroll
+        for (int cc = 0; cc < 2; ++cc) {
+          v4u v = {0u, 0u, 0u, 0u};
+          if (i < G::BPW || wave < G::EXTRA) v = qget(r32, kh, 32 * (b0 + i) + 8 * cc);
+          if constexpr (F == kMXF || F == kMXR) {
+            // fused query RoPE (blog §Kernels, MegaAttention): the pairs (2j, 2j+1) of the last
+            // 2 * rope_pairs dims rotate by query t's angle, rounded once to bf16 (RNE).  In
+            // fp64 the products of a bf16 and an fp32 value are exact, so each output is the
+            // exact rotation rounded once to fp64 and then once to bf16.
+            const int r0 = D - 2 * a.rope_pairs;
+            const int d0 = 32 * (b0 + i) + 16 * kh + 8 * cc;
+            if (a.rope_pairs > 0 && d0 >= r0 && (i < G::BPW || wave < G::EXTRA)) {
+              const int64_t pj = (int64_t)t * a.rope_pairs + (d0 - r0) / 2;
+              const v4f cs = *(const v4f*)(a.rope_cos + pj);
+              const v4f sn = *(const v4f*)(a.rope_sin + pj);
+  #pragma unroll
+              for (int j = 0; j < 4; ++j) {
+                const double x0 = __uint_as_float(v[j] << 16), x1 = __uint_as_float(v[j] & 0xFFFF0000u);
+                const double c = cs[j], sj = sn[j];
+                const double y0 = __builtin_fma(x0, c, -(x1 * sj));
+                const double y1 = __builtin_fma(x0, sj, x1 * c);
+                v[j] = bf16_rne(y0) | (bf16_rne(y1) << 16);
+              }
             }
           }
-        }
-        if constexpr (NV) {
-          // NVFP4 scores in fp16: bf16 -> fp16 is exact for 2^-14 <= |q| <= 65504
-          v8h h;
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            h[2 * j] = (_Float16)__uint_as_float(v[j] << 16);
-            h[2 * j + 1] = (_Float16)__uint_as_float(v[j] & 0xFFFF0000u);
+          if constexpr (NV) {
+            // NVFP4 scores in fp16: bf16 -> fp16 is exact for 2^-14 <= |q| <= 65504
+            v8h h;
+  #pragma unroll
+            for (int j = 0; j < 4; ++j) {
+              h[2 * j] = (_Float16)__uint_as_float(v[j] << 16);
+              h[2 * j + 1] = (_Float16)__uint_as_float(v[j] & 0xFFFF0000u);
+            }
+            qa[i][cc] = __builtin_bit_cast(v8bf, h);
+          } else {
+            qa[i][cc] = __builtin_bit_cast(v8bf, v);
           }
-          qa[i][cc] = __builtin_bit_cast(v8bf, h);
-        } else {
-          qa[i][cc] = __builtin_bit_cast(v8bf, v);
         }
+    }
+  };
+  if constexpr (QLDS) {
+    // rows 8 rr + wave, 16-byte piece pc = 64 jj + lane of each (the tail instruction of a
+    // row runs on fewer lanes)
+    constexpr int QP = D / 8;
+    const uint8_t* qsrc = (const uint8_t*)(a.q + ((int64_t)t * a.Hq + h0) * D);
+    const int ln = opq(lane);
+#pragma unroll
+    for (int rr = 0; rr < 4; ++rr) {
+      const int r = 8 * rr + wave;
+#pragma unroll
+      for (int jj = 0; jj < (QP + 63) / 64; ++jj) {
+        const int pc = 64 * jj + ln;
+        if (pc < QP) gload16(qsrc + (int64_t)r * 2 * D + 16 * pc, lds_addr(smem + r * QS + 1024 * jj));
       }
+    }
+  } else {
+    build_q();
   }
   {
     const SeqInfo si = locate_seq(a, t, lane);
@@ -545,10 +579,16 @@ __global__ __launch_bounds__(kThreads) void attend_kernel(AttendArgs a, int S, i
     c.tb = min(c.tb, c.te);
   }
   const int tb = c.tb, te = c.te;
+  // a range of at most kNBuf tiles is gathered at once (one memory latency for all of it),
+  // a longer one two tiles ahead of the products
+  const bool pre = te - tb <= kNBuf;
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
-  if (tb < te) issue(tb, 0, 0);
-  if (tb + 1 < te) issue(tb + 1, 1, 1);
+  if constexpr (QLDS) {
+    build_q();
+    __syncthreads();                               // q read: the tile buffers are free
+  }
+  for (int u = 0; u < (pre ? te - tb : min(te - tb, 2)); ++u) issue(tb + u, u, u);
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
 
@@ -872,9 +912,9 @@ __global__ __launch_bounds__(kThreads) void attend_kernel(AttendArgs a, int S, i
     }
   };
 
-  // ---- pipeline.  Iteration i: gather tile i+2 (and the positions of tile i+3), P.V of
-  // tile i-1, Q.K^T of tile i, build the row data of tile i; barrier; softmax of tile i
-  // and wait for tile i+1; barrier.  Tiles are global (E2M1) rows first, then window (E4M3)
+  // ---- pipeline.  Iteration i: gather tile i+2 (and the positions of tile i+3) unless the
+  // prologue gathered every tile, P.V of tile i-1, Q.K^T of tile i, build the row data of
+  // tile i; barrier; softmax of tile i and wait for tile i+1; barrier.  Tiles are global (E2M1) rows first, then window (E4M3)
   // rows, so the iterations run as separate loops per pair of kinds and no inner loop
   // branches on the kind.
   using KN = std::integral_constant<int, 0>;      // no tile
@@ -883,9 +923,10 @@ __global__ __launch_bounds__(kThreads) void attend_kernel(AttendArgs a, int S, i
   auto body = [&](auto PVK, auto QKK, int i) __attribute__((always_inline)) {
     constexpr int pvk = decltype(PVK)::value, qkk = decltype(QKK)::value;
     const int n = i - tb;
-    const bool more = i + 2 < te;
+    const bool more = !pre && i + 2 < te;
     const bool more_g = i + 2 < c.ng;
-    if (wave == 0 && i + 3 < te && i + 3 < c.ng) load_pos(i + 3, (n + 3) & 3);
+    // the prologue loaded the positions of the first kNBuf tiles
+    if (wave == 0 && n >= 1 && i + 3 < te && i + 3 < c.ng) load_pos(i + 3, (n + 3) & 3);
     // waves 0..3 issue the loads of tile i+2 before their products, waves 4..7 after them,
     // so half the waves queue for the vector-memory path while the other half run MFMAs
     if (more && wave < 4) issue(i + 2, (n + 2) & 3, (n + 2) & 3);

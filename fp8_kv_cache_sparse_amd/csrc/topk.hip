@@ -366,17 +366,20 @@ __device__ void write_selection(const TopkArgs& a, int t, const unsigned* bits, 
 
 // ------------------------------------------------------------------ short rows
 
-// One 1024-thread workgroup per query.  Thread i owns columns 16i .. 16i+15 (keys staged
-// through LDS so the row is read with coalesced loads) and keeps their 32-bit keys in
-// registers.  Radix select over the keys finds tau with count(key > tau) < k <=
+// One 1024-thread workgroup per query.  Thread i owns columns PER i .. PER i + PER - 1
+// (keys staged through LDS so the row is read with coalesced loads) and keeps their 32-bit
+// keys in registers; PER = 8 for rows of at most 8192 columns, else 16 (the work per
+// column is VALU-bound on one CU, so a row is not padded to the larger width).  Radix select over the keys finds tau with count(key > tau) < k <=
 // count(key >= tau); when several columns share the key tau, the lowest columns among
 // them are taken.  Column order is thread order, so one block-wide scan of a packed
 // (ties, greater) count pair yields both each thread's tie rank and its output offset,
 // and the selection comes out in ascending column order.
+template <int PER>
 __global__ __launch_bounds__(1024) void topk_small_kernel(TopkArgs a) {
   constexpr int NT = 1024;
-  constexpr int PER = kSmallN / NT;               // 16
-  __shared__ __attribute__((aligned(16))) unsigned keys[kSmallN];
+  constexpr int N = NT * PER;                     // columns of the row this instance handles
+  static_assert(PER % 4 == 0 && N <= kSmallN, "keys are read back as 16-byte vectors");
+  __shared__ __attribute__((aligned(16))) unsigned keys[N];
   __shared__ __attribute__((aligned(16))) unsigned hist[2048];
   __shared__ unsigned red[2 * (NT / 64)];
   __shared__ int scan_lds[NT / 64];
@@ -523,7 +526,7 @@ __global__ __launch_bounds__(1024) void topk_small_kernel(TopkArgs a) {
   // (scores, when asked for, are the exact inverses of the keys, staged next to them)
   int* stage = (int*)keys;
   float* vstage = (float*)(keys + 4096);
-  static_assert(kSmallN >= 2 * 4096, "position and score staging for k <= 4096");
+  static_assert(N >= 2 * 4096, "position and score staging for k <= 4096");
 #pragma unroll
   for (int u = 0; u < PER; ++u) {
     bool sel = key[u] > tau;
@@ -850,7 +853,8 @@ __global__ __launch_bounds__(1024) void topk_finish_kernel(TopkArgs a, TopkWs w)
 hipError_t launch_topk(const TopkArgs& a, hipStream_t s) {
   if (a.T == 0) return hipSuccess;
   if (a.max_ctx <= kSmallN) {
-    hipLaunchKernelGGL(topk_small_kernel, dim3(a.T), dim3(1024), 0, s, a);
+    if (a.max_ctx <= 8192) hipLaunchKernelGGL(topk_small_kernel<8>, dim3(a.T), dim3(1024), 0, s, a);
+    else hipLaunchKernelGGL(topk_small_kernel<16>, dim3(a.T), dim3(1024), 0, s, a);
     return hipGetLastError();
   }
   TopkFill fill;
