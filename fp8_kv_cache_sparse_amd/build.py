@@ -2,9 +2,10 @@
 
     python -m fp8_kv_cache_sparse_amd.build
 
-Every translation unit under csrc/ is compiled for gfx950 only and linked into
-fp8_kv_cache_sparse_amd/libsmqa.so next to this file.  Packed-fp32 VALU
-instructions are disabled for the device code generation.
+The decode path's translation units under csrc/ are compiled for gfx950 only and
+linked into fp8_kv_cache_sparse_amd/libsmqa.so next to this file; the benchmark's
+streaming-read reference (bench_read.hip) goes into libsmqa_bench.so beside it.
+Packed-fp32 VALU instructions are disabled for the device code generation.
 """
 from __future__ import annotations
 
@@ -18,7 +19,9 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libsmqa.so")
+BENCH_LIB = os.path.join(PKG, "libsmqa_bench.so")
 SOURCES = ["api.hip", "score.hip", "topk.hip", "attend.hip", "attend_sd.hip"]
+BENCH_SOURCES = ["bench_read.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
@@ -43,18 +46,24 @@ def _compile(src: str, extra) -> str:
     return obj
 
 
-def build(extra_flags=(), verbose: bool = False) -> str:
-    os.makedirs(BUILD, exist_ok=True)
-    with ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
-        objs = list(ex.map(lambda s: _compile(s, list(extra_flags)), SOURCES))
-    tmp = LIB + ".tmp"
+def _link(objs, lib: str) -> None:
+    tmp = lib + ".tmp"
     cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
+
+
+def build(extra_flags=(), verbose: bool = False) -> str:
+    os.makedirs(BUILD, exist_ok=True)
+    srcs = SOURCES + BENCH_SOURCES
+    with ThreadPoolExecutor(max_workers=len(srcs)) as ex:
+        objs = list(ex.map(lambda s: _compile(s, list(extra_flags)), srcs))
+    _link(objs[:len(SOURCES)], LIB)
+    _link(objs[len(SOURCES):], BENCH_LIB)
     if verbose:
-        print(f"built {LIB}")
+        print(f"built {LIB} and {BENCH_LIB}")
     return LIB
 
 

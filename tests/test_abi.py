@@ -303,3 +303,23 @@ def test_attend_mxfp8q_validation():
     assert call(c=A16 + 4) == -3
     assert call() == -5                                      # split partials need the workspace
     assert call(Lx=layout(T=0)) == 0
+
+
+def test_bench_read_library_rejects_bad_arguments_before_any_hip_call():
+    """The benchmark's streaming-read reference (libsmqa_bench.so, built beside the path's
+    library) refuses null pointers, sizes that are not whole 16-byte words and unsupported
+    depths without touching the device."""
+    path = os.path.join(os.path.dirname(smqa.__file__), "libsmqa_bench.so")
+    lib = ctypes.CDLL(path)
+    fn = lib.smqa_bench_stream_read
+    fn.restype = ctypes.c_int
+    fn.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32,
+                   ctypes.c_void_p]
+    buf = ctypes.create_string_buffer(64)
+    p = ctypes.addressof(buf)
+    assert fn(None, 1 << 20, p, 256, 4, None) == -1
+    assert fn(p, 1 << 20, None, 256, 4, None) == -1
+    assert fn(p, 17, p, 256, 4, None) == -1
+    assert fn(p, 0, p, 256, 4, None) == -1
+    assert fn(p, 1 << 20, p, 0, 4, None) == -1
+    assert fn(p, 1 << 20, p, 256, 3, None) == -1
