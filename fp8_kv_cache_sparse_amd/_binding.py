@@ -8,6 +8,7 @@ If libsmqa.so has not been built, the first call raises.
 """
 from __future__ import annotations
 
+import contextlib
 import ctypes
 import os
 from typing import Optional
@@ -15,6 +16,8 @@ from typing import Optional
 import torch
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libsmqa.so")
+# the same library built with SMQA_DEBUG (device-side range checks, smqa_debug_flags)
+DEBUG_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libsmqa_debug.so")
 
 SMQA_OK = 0
 ERRORS = {-1: "SMQA_ERR_NULL", -2: "SMQA_ERR_SHAPE", -3: "SMQA_ERR_ALIGN",
@@ -74,6 +77,7 @@ _SIGS = {
     "smqa_attend_plan": (_I, [_LP, _I, _I, _I, _I, _P, _P]),
     "smqa_last_error": (ctypes.c_char_p, []),
     "smqa_version": (ctypes.c_char_p, []),
+    "smqa_debug_flags": (_I, [_P, _I]),
 }
 
 
@@ -93,6 +97,36 @@ def load(path: Optional[str] = None):
     if path is None:
         _lib = lib
     return lib
+
+
+_debug_lib = None
+
+
+@contextlib.contextmanager
+def debug_build():
+    """Inside the block every call of this binding goes to libsmqa_debug.so (the library built
+    with SMQA_DEBUG: device-side range checks whose findings debug_flags() reads)."""
+    global _lib, _debug_lib
+    prev = load()
+    if _debug_lib is None:
+        _debug_lib = load(DEBUG_LIB_PATH)
+    _lib = _debug_lib
+    try:
+        yield
+    finally:
+        _lib = prev
+
+
+def debug_flags(clear: bool = True) -> int:
+    """The debug word of the current device (SMQA_DEBUG_* bits; synchronises the device), then
+    cleared unless clear is False.  Raises SmqaError outside a debug build."""
+    v = ctypes.c_uint32(0)
+    _check(load().smqa_debug_flags(ctypes.byref(v), 1 if clear else 0))
+    return v.value
+
+
+SMQA_DEBUG_POSITION = 1
+SMQA_DEBUG_E8M0 = 2
 
 
 def _check(code: int):

@@ -3,8 +3,10 @@
     python -m fp8_kv_cache_sparse_amd.build
 
 The decode path's translation units under csrc/ are compiled for gfx950 only and
-linked into fp8_kv_cache_sparse_amd/libsmqa.so next to this file; the benchmark's
-streaming-read reference (bench_read.hip) goes into libsmqa_bench.so beside it.
+linked into fp8_kv_cache_sparse_amd/libsmqa.so next to this file, and once more with
+SMQA_DEBUG defined into libsmqa_debug.so (the same library with the device-side range
+checks reported by smqa_debug_flags); the benchmark's streaming-read reference
+(bench_read.hip) goes into libsmqa_bench.so beside them.
 Packed-fp32 VALU instructions are disabled for the device code generation.
 """
 from __future__ import annotations
@@ -20,6 +22,7 @@ CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libsmqa.so")
 BENCH_LIB = os.path.join(PKG, "libsmqa_bench.so")
+DEBUG_LIB = os.path.join(PKG, "libsmqa_debug.so")
 SOURCES = ["api.hip", "score.hip", "topk.hip", "attend.hip", "attend_sd.hip"]
 BENCH_SOURCES = ["bench_read.hip"]
 
@@ -33,8 +36,8 @@ CFLAGS = [
 ]
 
 
-def _compile(src: str, extra) -> str:
-    obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
+def _compile(src: str, extra, tag: str = "") -> str:
+    obj = os.path.join(BUILD, os.path.splitext(src)[0] + tag + ".o")
     cmd = [HIPCC, *CFLAGS, *extra, "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
@@ -57,13 +60,16 @@ def _link(objs, lib: str) -> None:
 
 def build(extra_flags=(), verbose: bool = False) -> str:
     os.makedirs(BUILD, exist_ok=True)
-    srcs = SOURCES + BENCH_SOURCES
-    with ThreadPoolExecutor(max_workers=len(srcs)) as ex:
-        objs = list(ex.map(lambda s: _compile(s, list(extra_flags)), srcs))
-    _link(objs[:len(SOURCES)], LIB)
-    _link(objs[len(SOURCES):], BENCH_LIB)
+    jobs = [(s, list(extra_flags), "") for s in SOURCES + BENCH_SOURCES]
+    jobs += [(s, list(extra_flags) + ["-DSMQA_DEBUG=1"], "_debug") for s in SOURCES]
+    with ThreadPoolExecutor(max_workers=min(len(jobs), 16)) as ex:
+        objs = list(ex.map(lambda j: _compile(*j), jobs))
+    n, nb = len(SOURCES), len(BENCH_SOURCES)
+    _link(objs[:n], LIB)
+    _link(objs[n:n + nb], BENCH_LIB)
+    _link(objs[n + nb:], DEBUG_LIB)
     if verbose:
-        print(f"built {LIB} and {BENCH_LIB}")
+        print(f"built {LIB}, {DEBUG_LIB} and {BENCH_LIB}")
     return LIB
 
 

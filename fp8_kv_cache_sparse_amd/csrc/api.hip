@@ -14,6 +14,54 @@
 // name is only a stand-in for the symbol: its device address comes from hipGetSymbolAddress.
 static __device__ __align__(256) uint8_t scratch[SMQA_NOALLOC_SCRATCH_BYTES];
 
+#ifdef SMQA_DEBUG
+// SMQA_DEBUG builds: the word the attention kernels OR their kDbg* findings into (one per
+// GPU; read and cleared by smqa_debug_flags).  Its device address comes from
+// hipGetSymbolAddress, like scratch's.
+static __device__ unsigned debug_word;
+#endif
+
+namespace {
+
+// Device address of a file-scope __device__ symbol on the current device, looked up once per
+// device and kept in `ptrs`; nullptr with the HIP error in *err when the lookup fails.
+template <class Sym>
+void* symbol_ptr(const Sym& sym, std::atomic<void*>* ptrs, hipError_t* err) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) {
+    *err = e;
+    return nullptr;
+  }
+  if (dev < smqa::kMaxDevices) {
+    if (void* p = ptrs[dev].load(std::memory_order_acquire)) return p;
+  }
+  void* p = nullptr;
+  e = hipGetSymbolAddress(&p, sym);
+  if (e != hipSuccess || !p) {
+    *err = e != hipSuccess ? e : hipErrorInvalidSymbol;
+    return nullptr;
+  }
+  if (dev < smqa::kMaxDevices) ptrs[dev].store(p, std::memory_order_release);
+  return p;
+}
+
+// SMQA_DEBUG builds point the attention kernels at the debug word; release builds leave
+// AttendArgs::dbg null.
+hipError_t attach_debug(smqa::AttendArgs& a) {
+#ifdef SMQA_DEBUG
+  static std::atomic<void*> ptrs[smqa::kMaxDevices];
+  hipError_t e = hipSuccess;
+  a.dbg = (unsigned*)symbol_ptr(HIP_SYMBOL(debug_word), ptrs, &e);
+  return a.dbg ? hipSuccess : e;
+#else
+  a.dbg = nullptr;
+  return hipSuccess;
+#endif
+}
+
+}  // namespace
+
 namespace {
 
 thread_local std::string g_err;
@@ -205,6 +253,31 @@ const char* smqa_last_error(void) { return g_err.c_str(); }
 
 const char* smqa_version(void) { return "smqa 0.1.0 gfx950"; }
 
+int smqa_debug_flags(uint32_t* flags, int32_t clear) {
+  g_err.clear();
+  if (!flags) return fail(SMQA_ERR_NULL, "flags is NULL");
+  *flags = 0u;
+#ifdef SMQA_DEBUG
+  static std::atomic<void*> ptrs[smqa::kMaxDevices];
+  hipError_t e = hipSuccess;
+  void* p = symbol_ptr(HIP_SYMBOL(debug_word), ptrs, &e);
+  if (!p) return hip_fail(e, "debug word lookup");
+  if ((e = hipDeviceSynchronize()) != hipSuccess) return hip_fail(e, "smqa_debug_flags synchronise");
+  unsigned v = 0u;
+  if ((e = hipMemcpy(&v, p, sizeof v, hipMemcpyDeviceToHost)) != hipSuccess) return hip_fail(e, "smqa_debug_flags read");
+  if (clear) {
+    const unsigned zero = 0u;
+    if ((e = hipMemcpy(p, &zero, sizeof zero, hipMemcpyHostToDevice)) != hipSuccess)
+      return hip_fail(e, "smqa_debug_flags clear");
+  }
+  *flags = v;
+  return SMQA_OK;
+#else
+  (void)clear;
+  return fail(SMQA_ERR_UNSUPPORTED, "smqa_debug_flags: not an SMQA_DEBUG build");
+#endif
+}
+
 size_t smqa_topk_workspace_size(const smqa_layout* L, int32_t k, int32_t n_cand) {
   if (check_layout(L) != SMQA_OK) return 0;
   return smqa::topk_workspace_bytes(L->num_q, n_cand > 0 ? n_cand : L->max_ctx, k);
@@ -299,6 +372,7 @@ int sparse_mqa_attend(const smqa_layout* L, const uint16_t* q_bf16, const uint8_
   smqa::AttendArgs a{L->seq_start, L->q_start, L->q_pos, L->num_seqs, L->num_q, q_bf16, kv_codes,
                      kv_e8m0, kv_rowscale, idx, k, swa_fp8, swa_scale, swa_pos0, swa_clip, W, Hq, D,
                      sm_scale, out, lse, workspace};
+  if (hipError_t e = attach_debug(a); e != hipSuccess) return hip_fail(e, "debug word lookup");
   hipError_t e = smqa::launch_attend(a, (hipStream_t)stream);
   return e == hipSuccess ? SMQA_OK : hip_fail(e, "sparse_mqa_attend launch");
 }
@@ -327,6 +401,7 @@ int sparse_mqa_attend_fp8kv(const smqa_layout* L, const uint16_t* q_bf16, const 
   smqa::AttendArgs a{L->seq_start, L->q_start, L->q_pos, L->num_seqs, L->num_q, q_bf16, kv_fp8,
                      nullptr, kv_rowscale, idx, k, swa_fp8, swa_scale, swa_pos0, swa_clip, W, Hq, D,
                      sm_scale, out, lse, workspace, smqa::kKvFP8, 1.0f};
+  if (hipError_t e = attach_debug(a); e != hipSuccess) return hip_fail(e, "debug word lookup");
   hipError_t e = smqa::launch_attend_fmt(a, (hipStream_t)stream);
   return e == hipSuccess ? SMQA_OK : hip_fail(e, "sparse_mqa_attend_fp8kv launch");
 }
@@ -359,6 +434,7 @@ int sparse_mqa_attend_nvfp4(const smqa_layout* L, const uint16_t* q_bf16, const 
   smqa::AttendArgs a{L->seq_start, L->q_start, L->q_pos, L->num_seqs, L->num_q, q_bf16, kv_codes,
                      kv_scales, kv_rowscale, idx, k, swa_fp8, swa_scale, swa_pos0, swa_clip, W, Hq, D,
                      sm_scale, out, lse, workspace, smqa::kKvNV, kv_global_scale, K};
+  if (hipError_t e = attach_debug(a); e != hipSuccess) return hip_fail(e, "debug word lookup");
   hipError_t e = smqa::launch_attend_fmt(a, (hipStream_t)stream);
   return e == hipSuccess ? SMQA_OK : hip_fail(e, "sparse_mqa_attend_nvfp4 launch");
 }
@@ -386,6 +462,7 @@ int sparse_mqa_attend_mxfp8q(const smqa_layout* L, const uint16_t* q_bf16, const
   smqa::AttendArgs a{L->seq_start, L->q_start, L->q_pos, L->num_seqs, L->num_q, q_bf16, kv_codes,
                      kv_e8m0, kv_rowscale, idx, k, swa_fp8, swa_scale, swa_pos0, swa_clip, W, Hq, D,
                      sm_scale, out, lse, workspace, smqa::kKvMXN, 1.0f, 1.0f};
+  if (hipError_t e = attach_debug(a); e != hipSuccess) return hip_fail(e, "debug word lookup");
   hipError_t e = smqa::launch_attend_fmt(a, (hipStream_t)stream);
   return e == hipSuccess ? SMQA_OK : hip_fail(e, "sparse_mqa_attend_mxfp8q launch");
 }
@@ -416,6 +493,7 @@ int sparse_mqa_attend_fused(const smqa_layout* L, const uint16_t* q_bf16, const 
                      sm_scale, out, lse, workspace, smqa::kKvMX, 1.0f, 1.0f,
                      rope_pairs > 0 ? rope_cos : nullptr, rope_pairs > 0 ? rope_sin : nullptr, rope_pairs,
                      out_fp8, out_scale};
+  if (hipError_t e = attach_debug(a); e != hipSuccess) return hip_fail(e, "debug word lookup");
   hipError_t e = smqa::launch_attend_fused(a, (hipStream_t)stream);
   return e == hipSuccess ? SMQA_OK : hip_fail(e, "sparse_mqa_attend_fused launch");
 }
@@ -428,23 +506,7 @@ namespace {
 // call on it) and kept; nullptr with the HIP error in *err when the lookup fails.
 void* scratch_ptr(hipError_t* err) {
   static std::atomic<void*> ptrs[smqa::kMaxDevices];
-  int dev = 0;
-  hipError_t e = hipGetDevice(&dev);
-  if (e != hipSuccess) {
-    *err = e;
-    return nullptr;
-  }
-  if (dev < smqa::kMaxDevices) {
-    if (void* p = ptrs[dev].load(std::memory_order_acquire)) return p;
-  }
-  void* p = nullptr;
-  e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
-  if (e != hipSuccess || !p) {
-    *err = e != hipSuccess ? e : hipErrorInvalidSymbol;
-    return nullptr;
-  }
-  if (dev < smqa::kMaxDevices) ptrs[dev].store(p, std::memory_order_release);
-  return p;
+  return symbol_ptr(HIP_SYMBOL(scratch), ptrs, err);
 }
 
 }  // namespace
@@ -511,6 +573,9 @@ int decode_step_impl(const smqa_layout* L, const uint8_t* q_fp8, const float* w,
                      nullptr, nullptr, 0};
   smqa::TopkArgs ta{L->seq_start, L->q_start, L->q_pos, L->num_seqs, L->num_q, cols,
                     scores, cols, cand, cand ? n_cand : 0, k, idx, ws + d.topk_off};
+  // the debug word (SMQA_DEBUG builds) is looked up before anything is launched
+  smqa::AttendArgs dbg_probe{};
+  if (hipError_t e = attach_debug(dbg_probe); e != hipSuccess) return hip_fail(e, "debug word lookup");
   // When the streaming score kernel runs, it also builds the top-k's first-digit histogram.
   hipError_t e = hipSuccess;
   if (smqa::score_streams(sa)) {
@@ -528,6 +593,7 @@ int decode_step_impl(const smqa_layout* L, const uint8_t* q_fp8, const float* w,
   smqa::AttendArgs aa{L->seq_start, L->q_start, L->q_pos, L->num_seqs, L->num_q, q_bf16, kv_codes,
                       kv_e8m0, kv_rowscale, idx, k, swa_fp8, swa_scale, swa_pos0, swa_clip, W, Hq, D,
                       sm_scale, out, lse, ws + d.attend_off};
+  aa.dbg = dbg_probe.dbg;
   if (fz) {
     aa.rope_pairs = fz->rope_pairs;
     aa.rope_cos = fz->rope_pairs > 0 ? fz->rope_cos : nullptr;

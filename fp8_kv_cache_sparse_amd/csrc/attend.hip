@@ -65,7 +65,7 @@ struct AttSmem {
 struct AttCtx {
   int D, W, k, NSS, RS4, RS8, QS, BUF;
   int ng, wt0, tb, te, gx0;
-  int b, p, lo_win, pos0;
+  int b, p, lo_win, pos0, jmax;
   int64_t base;
   float lscale;
 };
@@ -305,6 +305,7 @@ __global__ __launch_bounds__(kAttThreads) void attend_kernel(AttendArgs a, int S
   c.b = seq_of_query(a.q_start, a.B, t);
   c.base = a.seq_start[c.b];
   c.p = a.q_pos[t];
+  c.jmax = min(c.p, (int)(a.seq_start[c.b + 1] - c.base) - 1);
   c.lo_win = max(c.p - c.W + 1, 0);
   if (a.swa_clip) c.lo_win = max(c.lo_win, a.swa_clip[t]);
   c.pos0 = a.swa_pos0[c.b];
@@ -392,8 +393,16 @@ __global__ __launch_bounds__(kAttThreads) void attend_kernel(AttendArgs a, int S
       const int h = pc / per_row, cc = pc - h * per_row;
       qv[u] = *(const v4u*)(a.q + ((int64_t)t * a.Hq + h0 + h) * c.D + 8 * cc);
     }
-    if (x0 < gx1) sidx[x0 - c.gx0] = j0;
-    for (int x = x0 + kAttThreads; x < gx1; x += kAttThreads) sidx[x - c.gx0] = ip[x];
+    // positions outside the query's rows are skipped like -1 (flagged in debug builds)
+    if (x0 < gx1) {
+      dbg_flag(a.dbg, j0 != -1 && !takes_part(j0, c.jmax), kDbgPosition);
+      sidx[x0 - c.gx0] = takes_part(j0, c.jmax) ? j0 : -1;
+    }
+    for (int x = x0 + kAttThreads; x < gx1; x += kAttThreads) {
+      const int j = ip[x];
+      dbg_flag(a.dbg, j != -1 && !takes_part(j, c.jmax), kDbgPosition);
+      sidx[x - c.gx0] = takes_part(j, c.jmax) ? j : -1;
+    }
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
       const int pc = tid + kAttThreads * u;
@@ -571,7 +580,7 @@ struct Geo {
 struct AttCtx {
   int W, k;
   int ng, wt0, tb, te, gx0;
-  int b, p, lo_win, pos0;
+  int b, p, lo_win, pos0, jmax;
   int64_t base;
   float lscale;
 };
@@ -784,6 +793,7 @@ __global__ __launch_bounds__(kAttThreads) void attend_kernel(AttendArgs a, int S
   c.b = seq_of_query(a.q_start, a.B, t);
   c.base = a.seq_start[c.b];
   c.p = a.q_pos[t];
+  c.jmax = min(c.p, (int)(a.seq_start[c.b + 1] - c.base) - 1);
   c.lo_win = max(c.p - c.W + 1, 0);
   if (a.swa_clip) c.lo_win = max(c.lo_win, a.swa_clip[t]);
   c.pos0 = a.swa_pos0[c.b];
@@ -870,7 +880,12 @@ __global__ __launch_bounds__(kAttThreads) void attend_kernel(AttendArgs a, int S
         qa[s][mt] = __builtin_bit_cast(v8bf, v);
       }
     const int32_t* ip = a.idx + (int64_t)t * c.k;
-    for (int x = c.gx0 + tid; x < gx1; x += kAttThreads) sidx[x - c.gx0] = ip[x];
+    // positions outside the query's rows are skipped like -1 (flagged in debug builds)
+    for (int x = c.gx0 + tid; x < gx1; x += kAttThreads) {
+      const int j = ip[x];
+      dbg_flag(a.dbg, j != -1 && !takes_part(j, c.jmax), kDbgPosition);
+      sidx[x - c.gx0] = takes_part(j, c.jmax) ? j : -1;
+    }
     for (int u = tid; u < c.W; u += kAttThreads)
       ssig[u] = a.swa_scale ? a.swa_scale[(int64_t)c.b * c.W + u] : 1.0f;
     if (tid < kHG) {

@@ -135,7 +135,7 @@ struct Geo {
 struct Ctx {
   int k, W;
   int ng, wt0, tb, te, gx1;
-  int b, p, lo_win, pos0;
+  int b, p, lo_win, pos0, jmax;
   int64_t base;
   float lscale;
 };
@@ -216,12 +216,13 @@ __device__ __forceinline__ void gload4(const void* src, unsigned m0) {
 }
 
 // The per-query values: q_pos[t], swa_clip[t] and the sequence of query t (the largest b
-// with q_start[b] <= t) with its seq_start and swa_pos0 entries, by a 64-way search: each
-// lane reads one sample of the three arrays, so for B <= 64 everything arrives in a single
-// round trip to memory.
+// with q_start[b] <= t) with its seq_start (both ends) and swa_pos0 entries, by a 64-way
+// search: each lane reads one sample of the arrays, so for B <= 64 everything arrives in a
+// single round trip to memory.
 struct SeqInfo {
   int b;
   int64_t base;
+  int len;
   int pos0;
   int p;
   int clip;
@@ -235,8 +236,9 @@ __device__ __forceinline__ SeqInfo locate_seq(const AttendArgs& a, int t, int la
     const bool in = idx < hi;
     const int qs = in ? a.q_start[idx] : 0;
     const int64_t ss = in ? a.seq_start[idx] : 0;
+    const int64_t se = in ? a.seq_start[idx + 1] : 0;
     const int p0 = in ? a.swa_pos0[idx] : 0;
-    asm volatile("" ::"v"(qs), "v"(ss), "v"(p0), "v"(extra));   // one wait for all four loads
+    asm volatile("" ::"v"(qs), "v"(ss), "v"(se), "v"(p0), "v"(extra));   // one wait for all five loads
     const int L = max(__builtin_popcountll(__builtin_amdgcn_ballot_w64(in && qs <= t)) - 1, 0);
     if (step == 1) {
       SeqInfo r;
@@ -244,6 +246,10 @@ __device__ __forceinline__ SeqInfo locate_seq(const AttendArgs& a, int t, int la
       const uint64_t u = (uint64_t)ss;
       r.base = (int64_t)(((uint64_t)(unsigned)__builtin_amdgcn_readlane((int)(u >> 32), L) << 32) |
                          (unsigned)__builtin_amdgcn_readlane((int)u, L));
+      const uint64_t ue = (uint64_t)se;
+      const int64_t end = (int64_t)(((uint64_t)(unsigned)__builtin_amdgcn_readlane((int)(ue >> 32), L) << 32) |
+                                    (unsigned)__builtin_amdgcn_readlane((int)ue, L));
+      r.len = (int)(end - r.base);
       r.pos0 = __builtin_amdgcn_readlane(p0, L);
       r.p = __builtin_amdgcn_readlane(extra, 0);
       r.clip = __builtin_amdgcn_readlane(extra, 1);
@@ -344,14 +350,14 @@ __global__ __launch_bounds__(kThreads) void attend_kernel(AttendArgs a, int S, i
         for (int u = 0; u < kWRows / 8; ++u) {
           const int r = 8 * u + wave;
           const int j = __builtin_amdgcn_readlane(pall, r);
-          const bool ok = (xt + r < c.gx1) & (j >= 0);
+          const bool ok = (xt + r < c.gx1) & takes_part(j, c.jmax);
           const uint8_t* src = ok ? codes_base + (int64_t)j * D : dummy;
           if (ln < (G::PIECES8 < 64 ? G::PIECES8 : 64)) gload16(src + 16 * ln, lds_addr(B + r * G::RS8));
           if constexpr (G::PIECES8 > 64) {
             if (ln < G::PIECES8 - 64) gload16(src + 1024 + 16 * ln, lds_addr(B + r * G::RS8 + 1024));
           }
         }
-        const bool ok = a.kv_rowscale && xt + rr < c.gx1 && pr >= 0;
+        const bool ok = a.kv_rowscale && xt + rr < c.gx1 && takes_part(pr, c.jmax);
         const void* src = ok ? (const void*)(rho_base + pr) : (const void*)dummy;
         if (ln < 2) gload4(src, lds_addr(B + G::RHO + 16 * wave));
       } else {
@@ -370,7 +376,7 @@ __global__ __launch_bounds__(kThreads) void attend_kernel(AttendArgs a, int S, i
         for (int u = 0; u < kRows / 8; ++u) {
           const int r = 8 * u + wave;
           const int j = __builtin_amdgcn_readlane(pall, r);
-          const bool ok = (xt + r < c.gx1) & (j >= 0);
+          const bool ok = (xt + r < c.gx1) & takes_part(j, c.jmax);
           const uint8_t* row = codes_base + (int64_t)j * (D / 2);   // formed for every j, used when ok
           const uint8_t* src = ok ? row : dummy;
           if (ln < D / 32) gload16(src + 16 * ln, lds_addr(B + r * G::RS4));
@@ -380,7 +386,7 @@ __global__ __launch_bounds__(kThreads) void attend_kernel(AttendArgs a, int S, i
           // loads of 64 lanes per tile, dealt round the waves (the surplus repeat a load
           // another wave makes: same bytes to the same place)
           const int row = ln & 31;
-          const bool ok = (xt + row < c.gx1) & (pall >= 0);
+          const bool ok = (xt + row < c.gx1) & takes_part(pall, c.jmax);
 #pragma unroll
           for (int u = 0; u < G::NSC; ++u) {
             const int m = (wave + 8 * u) % (D / 128);
@@ -390,12 +396,12 @@ __global__ __launch_bounds__(kThreads) void attend_kernel(AttendArgs a, int S, i
           }
         } else {  // raw E8M0: rows 4 wave .. +4, contiguous
           const int dd = ln % per_row;
-          const bool ok = xt + re < c.gx1 && pe >= 0;
+          const bool ok = xt + re < c.gx1 && takes_part(pe, c.jmax);
           const uint8_t* s0 = ok ? e8_base + (int64_t)pe * (D / 32) : dummy;
           if (ln < 4 * per_row) gload4(s0 + 4 * dd, lds_addr(B + G::E8 + 4 * wave * G::E8S));
         }
         {  // rho of rows 8u + wave, u = lane < 4 -> RHO[wave][u]
-          const bool ok = a.kv_rowscale && xt + rr < c.gx1 && pr >= 0;
+          const bool ok = a.kv_rowscale && xt + rr < c.gx1 && takes_part(pr, c.jmax);
           const void* src = ok ? (const void*)(rho_base + pr) : (const void*)dummy;
           if (ln < 4) gload4(src, lds_addr(B + G::RHO + 16 * wave));
         }
@@ -564,6 +570,7 @@ __global__ __launch_bounds__(kThreads) void attend_kernel(AttendArgs a, int S, i
     rho_base = a.kv_rowscale ? a.kv_rowscale + si.base : nullptr;
     c.pos0 = si.pos0;
     c.p = si.p;
+    c.jmax = min(si.p, si.len - 1);
     c.lo_win = max(max(c.p - c.W + 1, 0), si.clip);
   }
   if (tid < 32) {
@@ -714,7 +721,9 @@ __global__ __launch_bounds__(kThreads) void attend_kernel(AttendArgs a, int S, i
       const int* pos = (const int*)(smem + G::RING) + rslot * kRows;
       // rows that take part, as a bit mask (every loader wave computes it)
       const int pl = pos[ln & 31];
-      const unsigned vmask = (unsigned)__builtin_amdgcn_ballot_w64(ln < kRows && tile * kRows + ln < c.gx1 && pl >= 0);
+      const bool in_range = ln < kRows && tile * kRows + ln < c.gx1;
+      const unsigned vmask = (unsigned)__builtin_amdgcn_ballot_w64(in_range && takes_part(pl, c.jmax));
+      dbg_flag(a.dbg, ct < 64 && in_range && pl != -1 && !takes_part(pl, c.jmax), kDbgPosition);
       // blocks 4 bq .. 4 bq + 3 of rows 2 pp, 2 pp + 1 (one dword of raw E8M0 per row)
       const int pp = ct & 15, bq = ct >> 4;
       if constexpr (NV) {
@@ -729,6 +738,12 @@ __global__ __launch_bounds__(kThreads) void attend_kernel(AttendArgs a, int S, i
         const unsigned w0 = lds<unsigned>(B + G::E8 + (2 * pp) * G::E8S + 4 * bq);
         const unsigned w1 = lds<unsigned>(B + G::E8 + (2 * pp + 1) * G::E8S + 4 * bq);
         const bool v0 = (vmask >> (2 * pp)) & 1u, v1 = (vmask >> (2 * pp + 1)) & 1u;
+#ifdef SMQA_DEBUG
+        bool bad = false;
+        for (int j = 0; j < 4; ++j)
+          bad |= (v0 && !e8m0_fp16_exact((w0 >> (8 * j)) & 0xFFu)) || (v1 && !e8m0_fp16_exact((w1 >> (8 * j)) & 0xFFu));
+        dbg_flag(a.dbg, bad, kDbgE8m0);
+#endif
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           // E8M0 e -> 2^(e-127) as the float e << 23 (e = 0 gives 0); exact in fp16 for
@@ -751,7 +766,9 @@ __global__ __launch_bounds__(kThreads) void attend_kernel(AttendArgs a, int S, i
       bool v;
       if constexpr (kind == 3) {
         const int pl = ((const int*)(smem + G::RING) + rslot * kRows)[ct & 15];
-        v = ct < kWRows && tile * kWRows + ct < c.gx1 && pl >= 0;
+        const bool in_range = ct < kWRows && tile * kWRows + ct < c.gx1;
+        v = in_range && takes_part(pl, c.jmax);
+        dbg_flag(a.dbg, in_range && pl != -1 && !v, kDbgPosition);
       } else {
         const int uu = kWRows * (c.wt0 + tile - c.ng) + ct;
         const int pos = c.pos0 + uu;

@@ -179,7 +179,31 @@ struct AttendArgs {
   int32_t rope_pairs;
   uint8_t* out_fp8;
   float* out_scale;
+  // SMQA_DEBUG builds: the device word the kernels OR kDbg* bits into; null otherwise
+  unsigned* dbg;
 };
+
+// A selected position j takes part iff 0 <= j <= jmax = min(p_t, len_b - 1); -1 pads the
+// selection, and any other value is skipped the same way (so a bad index never leads to a
+// gather outside the query's rows).  SMQA_DEBUG builds report such values (kDbgPosition).
+__host__ __device__ inline bool takes_part(int j, int jmax) { return j >= 0 && j <= jmax; }
+// E8M0 exponents whose 32 values P.V holds exactly in fp16 (-23 <= e - 127 <= 13), and 0
+// (scale 2^-127: the block's values are far below fp16's range and count as zeros).
+// SMQA_DEBUG builds report any other exponent of a row that takes part (kDbgE8m0).
+__host__ __device__ inline bool e8m0_fp16_exact(unsigned e) { return e == 0u || (e >= 104u && e <= 140u); }
+constexpr unsigned kDbgPosition = 1u;
+constexpr unsigned kDbgE8m0 = 2u;
+// OR `bit` into the debug word when `cond` holds (a vector atomic; compiled out of release
+// builds, where `w` is null anyway).
+__device__ __forceinline__ void dbg_flag(unsigned* w, bool cond, unsigned bit) {
+#ifdef SMQA_DEBUG
+  if (w != nullptr && cond) __hip_atomic_fetch_or(w, bit, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+#else
+  (void)w;
+  (void)cond;
+  (void)bit;
+#endif
+}
 // Tile-range splits per (query, head group) of a call of this shape, or 0 when no split
 // count fits the workgroup's LDS (the call is unsupported); lds receives the bytes per
 // workgroup (static + dynamic) of the chosen plan.

@@ -434,6 +434,31 @@ const char* smqa_last_error(void);
 /* Library version string. */
 const char* smqa_version(void);
 
+/* ---------------------------------------------------------------------------
+ * Range checks of the values stored inside device arrays (debug builds).
+ *
+ * Every build treats a selected position j outside [0, min(p_t, len_b - 1)] as
+ * skipped, like the padding value -1, so a bad index never makes an attention
+ * kernel read outside the query's rows.  A library built with SMQA_DEBUG
+ * defined (fp8_kv_cache_sparse_amd/libsmqa_debug.so, from the same sources)
+ * also reports what it met, in one word per GPU that the attention kernels OR
+ * bits into:
+ *   SMQA_DEBUG_POSITION  a selected position outside that range other than -1
+ *                        (sparse_mqa_attend*, decode_step*)
+ *   SMQA_DEBUG_E8M0      an E8M0 exponent e of a row that takes part, outside
+ *                        the range P*V holds exactly in fp16 (-23 <= e - 127
+ *                        <= 13) and not 0 (MX global caches)
+ * smqa_debug_flags waits for the current device to finish its work
+ * (hipDeviceSynchronize), stores the word in *flags and clears it when clear
+ * is nonzero.  It returns SMQA_OK in a debug build and SMQA_ERR_UNSUPPORTED
+ * (with *flags = 0) in a release build, SMQA_ERR_NULL for flags == NULL and
+ * SMQA_ERR_HIP when a HIP call fails.  Kernels never trap on these findings;
+ * outputs are computed with the offending positions skipped.
+ * ------------------------------------------------------------------------- */
+#define SMQA_DEBUG_POSITION 1u
+#define SMQA_DEBUG_E8M0 2u
+int smqa_debug_flags(uint32_t* flags, int32_t clear);
+
 #ifdef __cplusplus
 }
 #endif

@@ -323,3 +323,21 @@ def test_bench_read_library_rejects_bad_arguments_before_any_hip_call():
     assert fn(p, 0, p, 256, 4, None) == -1
     assert fn(p, 1 << 20, p, 0, 4, None) == -1
     assert fn(p, 1 << 20, p, 256, 3, None) == -1
+
+
+def test_debug_flags_outside_a_debug_build_and_in_one():
+    """smqa_debug_flags: SMQA_ERR_NULL for a null pointer in either build; the release
+    library answers SMQA_ERR_UNSUPPORTED with the word zeroed, without touching a device.
+    The debug library (same sources, SMQA_DEBUG) exports every symbol the header declares."""
+    rel = smqa.load()
+    v = ctypes.c_uint32(7)
+    assert rel.smqa_debug_flags(None, 1) == -1
+    assert rel.smqa_debug_flags(ctypes.byref(v), 1) == -4
+    assert v.value == 0
+    assert b"not an SMQA_DEBUG build" in rel.smqa_last_error()
+    with pytest.raises(smqa.SmqaError):
+        smqa.debug_flags()
+    dbg = ctypes.CDLL(smqa.DEBUG_LIB_PATH)
+    for name in declared_functions():
+        assert hasattr(dbg, name), name
+    assert dbg.smqa_debug_flags(None, 1) == -1
