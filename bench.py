@@ -307,6 +307,10 @@ def measure(name, steps, warmup, timer, primary=False, stage_only=""):
             stages["copy"] = lambda: dst.copy_(src)
         if stage_only == "decode_step":
             stages["decode_step"] = step
+        if stage_only == "score_fp8mma":
+            sc8 = torch.empty_like(scores)
+            stages["score_fp8mma"] = lambda: smqa.sparse_mqa_score_fp8mma(L, wl.qI, wl.w, wl.kI, wl.kscale,
+                                                                         wl.cand, scores=sc8)
         st_score()
         st_topk()
         torch.cuda.synchronize()
@@ -355,6 +359,32 @@ def measure(name, steps, warmup, timer, primary=False, stage_only=""):
         cand = {"n_cand": N_CAND, "score_us": stats(cu),
                 "dense_over_candidate_time": round(stats(st_us["score"])["median"] / stats(cu)["median"], 2)}
         del wlc, sc_c
+
+    # the indexer contraction on the FP8 matrix cores (sparse_mqa_score_fp8mma) beside the
+    # bf16 form: cold time, roofline against the FP8 peak, and its largest relative
+    # difference from the bf16 form's scores (which are exact products with fp32 sums)
+    score_forms = None
+    if wl.Di == 128:
+        scores8 = torch.empty_like(scores)
+
+        def st_score8():
+            smqa.sparse_mqa_score_fp8mma(L, wl.qI, wl.w, wl.kI, wl.kscale, wl.cand, scores=scores8)
+
+        print(f"[bench] {name}: FP8 matrix-core scoring x{reps_stage} cold", file=sys.stderr, flush=True)
+        u8 = timer.cold(st_score8, reps_stage)
+        st_score()
+        st_score8()
+        torch.cuda.synchronize()
+        fin = torch.isfinite(scores)
+        rel = ((scores8 - scores).abs() / scores.abs().clamp_min(1e-30))[fin]
+        w8 = dict(w["score"], mfma="fp8")
+        score_forms = {
+            "bf16_us": stats(st_us["score"]), "fp8_mfma_us": stats(u8),
+            "fp8_over_bf16_time": round(stats(u8)["median"] / stats(st_us["score"])["median"], 3),
+            "max_rel_diff_fp8_vs_bf16": float(rel.max()) if rel.numel() else 0.0,
+            "fp8_roofline": roofline("score", w8, stats(u8)["median"] * 1e-6),
+        }
+        del scores8
 
     # the same attention over the FP8 and NVFP4 global caches and in MegaAttention's fused
     # form, on the same selection (cold)
@@ -417,6 +447,7 @@ def measure(name, steps, warmup, timer, primary=False, stage_only=""):
         "stage_us_cold": st_stats,
         "stage_roofline": st_roof,
         "candidate_scoring": cand,
+        "score_forms": score_forms,
         "global_cache_formats": formats,
         "dominant_stage": dom,
         "roofline": st_roof[dom],

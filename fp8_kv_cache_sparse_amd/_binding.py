@@ -53,6 +53,7 @@ _LP = ctypes.POINTER(Layout)
 
 _SIGS = {
     "sparse_mqa_score": (_I, [_LP, _P, _P, _P, _P, _P, _I, _I, _I, _P, _L, _P]),
+    "sparse_mqa_score_fp8mma": (_I, [_LP, _P, _P, _P, _P, _P, _I, _I, _I, _P, _L, _P]),
     "topk_select": (_I, [_LP, _P, _L, _P, _I, _I, _P, _P, _P, _S, _P]),
     "sparse_mqa_attend": (_I, [_LP, _P, _P, _P, _P, _P, _I, _P, _P, _P, _P, _I, _I, _I, _F,
                                _P, _P, _P, _S, _P]),
@@ -200,6 +201,15 @@ def version() -> str:
 
 def sparse_mqa_score(L: Batch, q_fp8, w, k_fp8, k_scale=None, cand=None, scores=None, stream=None):
     """Indexer scores -> float32 [T, ld] (dense: ld = max_ctx; candidate mode: ld = n_cand)."""
+    return _score("sparse_mqa_score", L, q_fp8, w, k_fp8, k_scale, cand, scores, stream)
+
+
+def sparse_mqa_score_fp8mma(L: Batch, q_fp8, w, k_fp8, k_scale=None, cand=None, scores=None, stream=None):
+    """sparse_mqa_score with the contraction on the FP8 matrix cores (Di = 128)."""
+    return _score("sparse_mqa_score_fp8mma", L, q_fp8, w, k_fp8, k_scale, cand, scores, stream)
+
+
+def _score(entry, L, q_fp8, w, k_fp8, k_scale, cand, scores, stream):
     lib = load()
     _dev(q_fp8, "q_fp8", _U8, 3)
     _dev(w, "w", torch.float32, 2)
@@ -212,8 +222,8 @@ def sparse_mqa_score(L: Batch, q_fp8, w, k_fp8, k_scale=None, cand=None, scores=
         ld = n_cand if cand is not None else L.max_ctx
         scores = torch.empty((T, max(ld, 1)), dtype=torch.float32, device=q_fp8.device)
     _dev(scores, "scores", torch.float32, 2)
-    _check(lib.sparse_mqa_score(L.ref, _ptr(q_fp8), _ptr(w), _ptr(k_fp8), _ptr(k_scale), _ptr(cand),
-                                n_cand, Hi, Di, _ptr(scores), scores.shape[1], _stream(stream)))
+    _check(getattr(lib, entry)(L.ref, _ptr(q_fp8), _ptr(w), _ptr(k_fp8), _ptr(k_scale), _ptr(cand),
+                               n_cand, Hi, Di, _ptr(scores), scores.shape[1], _stream(stream)))
     return scores
 
 

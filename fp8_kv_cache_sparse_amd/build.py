@@ -24,7 +24,7 @@ LIB = os.path.join(PKG, "libsmqa.so")
 BENCH_LIB = os.path.join(PKG, "libsmqa_bench.so")
 DEBUG_LIB = os.path.join(PKG, "libsmqa_debug.so")
 SOURCES = ["api.hip", "score.hip", "topk.hip", "attend.hip", "attend_sd.hip"]
-BENCH_SOURCES = ["bench_read.hip"]
+BENCH_SOURCES = ["bench_read.hip", "bench_fp8_mfma.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

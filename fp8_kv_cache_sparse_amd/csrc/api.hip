@@ -247,6 +247,29 @@ DecodeWs decode_ws_layout(const smqa_layout* L, int32_t k, int32_t ncols, int32_
 
 }  // namespace
 
+namespace {
+
+// sparse_mqa_score and its FP8 matrix-core form (Di = 128 only).
+int score_entry(const smqa_layout* L, const uint8_t* q_fp8, const float* w, const uint8_t* k_fp8,
+                const float* k_scale, const int32_t* cand, int32_t n_cand, int32_t Hi, int32_t Di,
+                float* scores, int64_t ld_scores, void* stream, bool fp8mma) {
+  g_err.clear();
+  int st = check_layout(L);
+  if (st) return st;
+  if (L->num_q == 0) return SMQA_OK;
+  st = check_score(L, q_fp8, w, k_fp8, k_scale, cand, n_cand, Hi, Di, scores, ld_scores, true);
+  if (st) return st;
+  if (fp8mma && Di != 128)
+    return fail(SMQA_ERR_UNSUPPORTED, "sparse_mqa_score_fp8mma: Di = %d (the FP8 form needs Di = 128)", Di);
+  smqa::ScoreArgs a{L->seq_start, L->q_start, L->q_pos, L->num_seqs, L->num_q, L->max_ctx,
+                    q_fp8, w, k_fp8, k_scale, cand, cand ? n_cand : 0, Hi, Di, scores, ld_scores,
+                    nullptr, nullptr, 0, true, fp8mma};
+  hipError_t e = smqa::launch_score(a, (hipStream_t)stream);
+  return e == hipSuccess ? SMQA_OK : hip_fail(e, fp8mma ? "sparse_mqa_score_fp8mma launch" : "sparse_mqa_score launch");
+}
+
+}  // namespace
+
 extern "C" {
 
 const char* smqa_last_error(void) { return g_err.c_str(); }
@@ -322,17 +345,13 @@ size_t smqa_decode_step_workspace_size(const smqa_layout* L, int32_t k, int32_t 
 int sparse_mqa_score(const smqa_layout* L, const uint8_t* q_fp8, const float* w, const uint8_t* k_fp8,
                      const float* k_scale, const int32_t* cand, int32_t n_cand, int32_t Hi, int32_t Di,
                      float* scores, int64_t ld_scores, void* stream) {
-  g_err.clear();
-  int st = check_layout(L);
-  if (st) return st;
-  if (L->num_q == 0) return SMQA_OK;
-  st = check_score(L, q_fp8, w, k_fp8, k_scale, cand, n_cand, Hi, Di, scores, ld_scores, true);
-  if (st) return st;
-  smqa::ScoreArgs a{L->seq_start, L->q_start, L->q_pos, L->num_seqs, L->num_q, L->max_ctx,
-                    q_fp8, w, k_fp8, k_scale, cand, cand ? n_cand : 0, Hi, Di, scores, ld_scores,
-                    nullptr, nullptr, 0, true};
-  hipError_t e = smqa::launch_score(a, (hipStream_t)stream);
-  return e == hipSuccess ? SMQA_OK : hip_fail(e, "sparse_mqa_score launch");
+  return score_entry(L, q_fp8, w, k_fp8, k_scale, cand, n_cand, Hi, Di, scores, ld_scores, stream, false);
+}
+
+int sparse_mqa_score_fp8mma(const smqa_layout* L, const uint8_t* q_fp8, const float* w, const uint8_t* k_fp8,
+                            const float* k_scale, const int32_t* cand, int32_t n_cand, int32_t Hi, int32_t Di,
+                            float* scores, int64_t ld_scores, void* stream) {
+  return score_entry(L, q_fp8, w, k_fp8, k_scale, cand, n_cand, Hi, Di, scores, ld_scores, stream, true);
 }
 
 int topk_select(const smqa_layout* L, const float* scores, int64_t ld_scores, const int32_t* cand,

@@ -105,6 +105,8 @@ struct ScoreArgs {
   // Write -inf into the columns no score goes to: dense, [min(p_t, len_b - 1) + 1, ld);
   // candidate mode, [n_cand, ld) (the public call; decode_step's internal rows skip it).
   bool fill_tail;
+  // Contract on the FP8 matrix cores instead of bf16 ones (Di = 128; sparse_mqa_score_fp8mma)
+  bool fp8mma;
 };
 hipError_t launch_score(const ScoreArgs& a, hipStream_t s);
 // True when launch_score takes the streaming kernel, the one that can fill ScoreArgs::hist.

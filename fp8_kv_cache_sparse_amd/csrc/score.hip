@@ -53,9 +53,18 @@ struct RawKeys {
   int pos[TPW];   // position (CAND: from the list), -1 when the column is empty or invalid
 };
 
-template <int MT, int TPW, int DI, bool CAND>
+// F8: the contraction on the FP8 matrix cores (v_mfma_scale_f32_16x16x128_f8f6f4, unit
+// scales; DI = 128): q and the keys enter as the stored E4M3 bytes, one instruction per
+// 16 heads x 16 positions covering all 128 dims, instead of four bf16 ones after an exact
+// conversion.  Lane (g, n) already holds key bytes [32 g, 32 g + 32) of position n, which is
+// its operand for that instruction; q's bytes go in the same order, so every product pairs
+// the right dims.  The instruction adds its 128 exact products with an error of up to ~2^-15
+// of their absolute sum (measured on gfx950); the bf16 form adds them in fp32.
+template <int MT, int TPW, int DI, bool CAND, bool F8 = false>
 __global__ __launch_bounds__(kScoreThreads, 2) void score_kernel(ScoreArgs a) {
-  // two q buffers: query t is scored from one while query t+1 is written to the other
+  static_assert(!F8 || DI == 128, "the FP8 form covers 128 dims per instruction");
+  // two q buffers: query t is scored from one while query t+1 is written to the other (bf16
+  // rows, or the raw E4M3 bytes in the first half of each row for F8)
   __shared__ __align__(16) uint8_t q_lds[2][16 * MT * kQRow];
   __shared__ float w_lds[2][16 * MT];
   __shared__ int s_pmax;
@@ -158,9 +167,13 @@ __global__ __launch_bounds__(kScoreThreads, 2) void score_kernel(ScoreArgs a) {
       const int pc = tid + kScoreThreads * u;
       const int h = pc / (DI / 16), c = pc % (DI / 16);
       if (pc < kQPieces) {
-        uint8_t* dst = q_lds[buf] + h * kQRow + 32 * c;
-        *(v8bf*)dst = fp8x8_to_bf16(r.v[u].x, r.v[u].y);
-        *(v8bf*)(dst + 16) = fp8x8_to_bf16(r.v[u].z, r.v[u].w);
+        if constexpr (F8) {
+          *(v4u*)(q_lds[buf] + h * kQRow + 16 * c) = r.v[u];
+        } else {
+          uint8_t* dst = q_lds[buf] + h * kQRow + 32 * c;
+          *(v8bf*)dst = fp8x8_to_bf16(r.v[u].x, r.v[u].y);
+          *(v8bf*)(dst + 16) = fp8x8_to_bf16(r.v[u].z, r.v[u].w);
+        }
       }
     }
     if (tid < 16 * MT) w_lds[buf][tid] = r.w;
@@ -182,15 +195,21 @@ __global__ __launch_bounds__(kScoreThreads, 2) void score_kernel(ScoreArgs a) {
   // The next block's keys load while this block is scored.
   auto score_block = [&](RawKeys<TPW, DI>& rk) {
     // convert this block's keys (exact E4M3 -> bf16), then reuse rk for block + G
-    v8bf kb[TPW][NKS];
+    v8bf kb[F8 ? 1 : TPW][F8 ? 1 : NKS];
+    v8i k8[F8 ? TPW : 1];
     float kap[TPW];
     int kpos[TPW];
 #pragma unroll
     for (int i = 0; i < TPW; ++i) {
       const unsigned wds[8] = {rk.lo[i].x, rk.lo[i].y, rk.lo[i].z, rk.lo[i].w,
                                rk.hi[i].x, rk.hi[i].y, rk.hi[i].z, rk.hi[i].w};
+      if constexpr (F8) {
+        k8[i] = v8i{(int)wds[0], (int)wds[1], (int)wds[2], (int)wds[3],
+                    (int)wds[4], (int)wds[5], (int)wds[6], (int)wds[7]};
+      } else {
 #pragma unroll
-      for (int s2 = 0; s2 < NKS; ++s2) kb[i][s2] = fp8x8_to_bf16(wds[2 * s2], wds[2 * s2 + 1]);
+        for (int s2 = 0; s2 < NKS; ++s2) kb[i][s2] = fp8x8_to_bf16(wds[2 * s2], wds[2 * s2 + 1]);
+      }
       kap[i] = rk.kap[i];
       kpos[i] = rk.pos[i];
     }
@@ -218,23 +237,30 @@ __global__ __launch_bounds__(kScoreThreads, 2) void score_kernel(ScoreArgs a) {
         for (int i = 0; i < TPW; ++i) sum[i] = 0.0f;
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) {
-          v8bf qa[NKS];
           float wr[4];
-          {
+#pragma unroll
+          for (int r = 0; r < 4; ++r) wr[r] = w_lds[buf][16 * mt + 4 * g + r];
+          v4f acc[TPW];
+#pragma unroll
+          for (int i = 0; i < TPW; ++i) acc[i] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+          if constexpr (F8) {
+            const uint8_t* src = q_lds[buf] + (16 * mt + n) * kQRow + 32 * g;
+            const v4u q0 = *(const v4u*)src, q1 = *(const v4u*)(src + 16);
+            const v8i qa = {(int)q0.x, (int)q0.y, (int)q0.z, (int)q0.w, (int)q1.x, (int)q1.y, (int)q1.z, (int)q1.w};
+#pragma unroll
+            for (int i = 0; i < TPW; ++i)
+              acc[i] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(qa, k8[i], acc[i], 0, 0, 0, 127, 0, 127);
+          } else {
+            v8bf qa[NKS];
             const uint8_t* src = q_lds[buf] + (16 * mt + n) * kQRow + 2 * g * (DI / 4);
 #pragma unroll
             for (int s2 = 0; s2 < NKS; ++s2) qa[s2] = *(const v8bf*)(src + 16 * s2);
 #pragma unroll
-            for (int r = 0; r < 4; ++r) wr[r] = w_lds[buf][16 * mt + 4 * g + r];
+            for (int s2 = 0; s2 < NKS; ++s2)
+#pragma unroll
+              for (int i = 0; i < TPW; ++i)
+                acc[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[s2], kb[i][s2], acc[i], 0, 0, 0);
           }
-          v4f acc[TPW];
-#pragma unroll
-          for (int i = 0; i < TPW; ++i) acc[i] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-          for (int s2 = 0; s2 < NKS; ++s2)
-#pragma unroll
-            for (int i = 0; i < TPW; ++i)
-              acc[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[s2], kb[i][s2], acc[i], 0, 0, 0);
 #pragma unroll
           for (int i = 0; i < TPW; ++i)
 #pragma unroll
@@ -479,7 +505,7 @@ static int resident_workgroups(K kernel) {
   return cus * per_cu;
 }
 
-template <int MT, int TPW, int DI, bool CAND>
+template <int MT, int TPW, int DI, bool CAND, bool F8 = false>
 static hipError_t launch_score_t(const ScoreArgs& a, hipStream_t s, bool persistent) {
   constexpr int per_wg = 4 * 16 * TPW;
   const int rows = CAND ? a.T : a.B;
@@ -488,11 +514,11 @@ static hipError_t launch_score_t(const ScoreArgs& a, hipStream_t s, bool persist
   // blocks with the next block's keys in flight; otherwise one block per workgroup
   int gx = nblk;
   if (persistent) {
-    const int res = resident_workgroups(score_kernel<MT, TPW, DI, CAND>);
+    const int res = resident_workgroups(score_kernel<MT, TPW, DI, CAND, F8>);
     gx = std::min(nblk, std::max(1, res / std::max(rows, 1)));
   }
   if (gx == 0 || rows == 0) return hipSuccess;
-  hipLaunchKernelGGL((score_kernel<MT, TPW, DI, CAND>), dim3(gx, rows), dim3(kScoreThreads), 0, s, a);
+  hipLaunchKernelGGL((score_kernel<MT, TPW, DI, CAND, F8>), dim3(gx, rows), dim3(kScoreThreads), 0, s, a);
   return hipGetLastError();
 }
 
@@ -523,8 +549,23 @@ static int stream_grid(const ScoreArgs& a, int resident) {
 
 bool score_streams(const ScoreArgs& a) { return stream_applies(a); }
 
+// The FP8 matrix-core form (DI = 128): score_kernel for every shape, with the launch
+// choices of the bf16 form (the streaming kernel, whose decode rows are bound by HBM, has no
+// FP8 form).
+template <int MT>
+static hipError_t launch_score_f8(const ScoreArgs& a, hipStream_t s) {
+  const bool small = small_problem(a);
+  if (a.cand) return small ? launch_score_t<MT, 1, 128, true, true>(a, s, false)
+                           : launch_score_t<MT, 4, 128, true, true>(a, s, true);
+  if (small) return launch_score_t<MT, 1, 128, false, true>(a, s, false);
+  return launch_score_t<MT, 4, 128, false, true>(a, s, a.T == a.B);
+}
+
 template <int MT, int DI>
 static hipError_t launch_score_mt(const ScoreArgs& a, hipStream_t s) {
+  if constexpr (DI == 128) {
+    if (a.fp8mma) return launch_score_f8<MT>(a, s);
+  }
   const bool small = small_problem(a);
   if (a.cand) return small ? launch_score_t<MT, 1, DI, true>(a, s, false) : launch_score_t<MT, 4, DI, true>(a, s, true);
   // Several queries per sequence make a block compute-bound (q is restaged per query), so

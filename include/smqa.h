@@ -134,6 +134,29 @@ int sparse_mqa_score(const smqa_layout* L,
                      void* stream);
 
 /*
+ * sparse_mqa_score_fp8mma — sparse_mqa_score with the contraction on the FP8
+ * matrix cores (blog §Kernels: the indexer's logits are computed in FP8).  Same
+ * arguments, outputs and errors, plus SMQA_ERR_UNSUPPORTED unless Di == 128.
+ * The E4M3 bytes of q and k enter v_mfma_scale_f32_16x16x128_f8f6f4 as stored
+ * (unit scales), one instruction per 16 heads x 16 positions x 128 dims.
+ * Arithmetic: the products are exact, but the instruction adds the 128 of one
+ * logit with an error of up to about 2^-15 of their absolute sum (measured on
+ * gfx950); the head sum, ReLU and kappa are fp32 as in sparse_mqa_score.  So a
+ * score S carries an error up to about 2^-15 * sum_h |w_h| * sum_d |q_hd k_d|
+ * (times kappa): relative to S this stays below 1e-4 when the head weights are
+ * non-negative and the logits do not nearly cancel, not for every input.
+ * sparse_mqa_score (exact products, fp32 sums) is the reference form;
+ * decode_step uses it.
+ */
+int sparse_mqa_score_fp8mma(const smqa_layout* L,
+                            const uint8_t* q_fp8, const float* w,
+                            const uint8_t* k_fp8, const float* k_scale,
+                            const int32_t* cand, int32_t n_cand,
+                            int32_t Hi, int32_t Di,
+                            float* scores, int64_t ld_scores,
+                            void* stream);
+
+/*
  * topk_select — the k best positions per query (blog §TL;DR: DeepSelect, a
  * top-k library for DeepSeek Sparse Attention; §Kernels: the indexer's top-k
  * over the scored positions).

@@ -341,3 +341,25 @@ def test_debug_flags_outside_a_debug_build_and_in_one():
     for name in declared_functions():
         assert hasattr(dbg, name), name
     assert dbg.smqa_debug_flags(None, 1) == -1
+
+
+def score_fp8mma(L, Hi=64, Di=128, **kw):
+    a = dict(q=A16, w=A4, k=A16, ks=None, cand=None, n_cand=0, s=A4, ld=8192)
+    a.update(kw)
+    if L is None:
+        return lib().sparse_mqa_score_fp8mma(None, a["q"], a["w"], a["k"], a["ks"], a["cand"], a["n_cand"],
+                                             Hi, Di, a["s"], a["ld"], None)
+    return lib().sparse_mqa_score_fp8mma(ctypes.byref(L), a["q"], a["w"], a["k"], a["ks"], a["cand"],
+                                         a["n_cand"], Hi, Di, a["s"], a["ld"], None)
+
+
+def test_score_fp8mma_validation():
+    """The FP8 matrix-core form validates like sparse_mqa_score and also rejects Di != 128,
+    all before any HIP call."""
+    L = layout()
+    assert score_fp8mma(None) == -1
+    assert score_fp8mma(L, q=None) == -1 and "q_fp8" in err()
+    assert score_fp8mma(L, Di=96) == -4
+    assert score_fp8mma(L, Di=64) == -4 and "Di = 128" in err()
+    assert score_fp8mma(L, ld=100) == -2
+    assert score_fp8mma(layout(T=0)) == 0
