@@ -116,3 +116,36 @@ def test_score_fp8mma_mixed_sign_weights_stay_within_the_bound(lib):
                       ld=S.shape[1])
     ok, msg = _bound_ok(a, 0, S.cpu().numpy()[0], S_ref[0])
     assert ok, msg
+
+
+@pytest.mark.parametrize("form", [0, 1], ids=["scale_16x16x128_f8f6f4", "16x16x32_fp8_fp8"])
+def test_fp8_instruction_summation_error(lib, form):
+    """The measurement behind the bound above: decode_8k's 64 x 8192 indexer logits from the
+    benchmark library's FP8-instruction kernel against exact fp64 dot products.  Products of
+    E4M3 values are exact, so any difference is the instruction's summation; it is nonzero
+    (the sum is not exact in fp32) and below 2^-14 of the absolute sum of the products."""
+    import ctypes
+    import os
+    path = os.path.join(os.path.dirname(lib.__file__), "libsmqa_bench.so")
+    blib = ctypes.CDLL(path)
+    fn = blib.smqa_bench_fp8_mfma_logits
+    fn.restype = ctypes.c_int
+    fn.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p,
+                   ctypes.c_int32, ctypes.c_void_p]
+    wl = synth.generate("decode_8k", seed=0, device=DEV)
+    announce(f"fp8 instruction error form {form}")
+    qI = wl.qI[0].contiguous()
+    kI = wl.kI.contiguous()
+    H, N = qI.shape[0], kI.shape[0]
+    assert qI.shape[1] == 128 and H % 16 == 0 and N % 16 == 0
+    out = torch.empty((H, N), dtype=torch.float32, device=DEV)
+    assert fn(qI.data_ptr(), kI.data_ptr(), H, N, out.data_ptr(), form, None) == 0
+    torch.cuda.synchronize()
+    Q = codecs.e4m3(qI.cpu().numpy()).astype(np.float64)
+    K = codecs.e4m3(kI.cpu().numpy()).astype(np.float64)
+    L = Q @ K.T
+    A = np.abs(Q) @ np.abs(K).T
+    nz = A > 0
+    ratio = np.abs(out.cpu().numpy().astype(np.float64) - L)[nz] / A[nz]
+    assert ratio.max() > 0.0
+    assert ratio.max() <= 2.0 ** -14, f"max error / sum|qk| = {ratio.max():.3e}"
