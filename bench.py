@@ -483,18 +483,21 @@ def cpu_info():
 
 
 def cu_clock_mhz():
-    """Current GPU core clock (MHz) as rocm-smi reports it (run as a child process), or None."""
+    """Highest core (sclk) clock level of GPU 0 in MHz, from `rocm-smi -s` run as a child process,
+    or None."""
     import re
     import subprocess
-    for cmd in (["rocm-smi", "--showsclk"], ["amd-smi", "metric", "--clock"]):
-        try:
-            r = subprocess.run(cmd, capture_output=True, text=True, timeout=20)
-        except (OSError, subprocess.SubprocessError):
-            continue
-        m = re.findall(r"(\d+(?:\.\d+)?)\s*Mhz", r.stdout, flags=re.I)
-        if m:
-            return float(m[0])
-    return None
+    try:
+        r = subprocess.run(["rocm-smi", "-s"], capture_output=True, text=True, timeout=30)
+    except (OSError, subprocess.SubprocessError):
+        return None
+    txt = r.stdout
+    i = txt.find("Supported sclk frequencies")
+    if i < 0:
+        return None
+    j = txt.find("Supported", i + 10)
+    vals = [float(v) for v in re.findall(r"(\d+(?:\.\d+)?)\s*Mhz", txt[i:j if j > 0 else None], flags=re.I)]
+    return max(vals) if vals else None
 
 
 def cpu_baseline(name, seconds):
@@ -581,7 +584,7 @@ def main():
                    "attention": f"{cfg['Hq']} heads x {cfg['D']} latent (e2m1 + e8m0/32"
                                 f"{' + f32 row scale' if cfg['rowscale'] else ''})",
                    "window": cfg["W"], "parallelism": "none (1 GPU)", "seed": 0,
-                   "cu_clock_MHz": cu_clock_mhz(),
+                   "cu_clock_max_MHz": cu_clock_mhz(),
                    "timing": f"cold ({args.flush} of 512 MiB before each rep), median of per-call HIP events"},
         "roofline": main_res["roofline"],
         "cpu_baseline": cpu,
