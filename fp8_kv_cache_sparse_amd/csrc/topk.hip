@@ -13,14 +13,14 @@
 // Short rows (<= kSmallN columns): one 1024-thread workgroup per query keeps the
 // keys in LDS and runs the whole select there.
 // Long rows: (1) many workgroups per query build a 4096-bin histogram of the top
-// 12 key bits; the last one to finish finds the bin d1 holding the k-th entry;
-// (2) many workgroups per query write the bitmap words of their columns (every
+// 12 key bits; (2) many workgroups per query each find the bin d1 holding the k-th
+// entry from the finished histogram, write the bitmap words of their columns (every
 // entry above d1 selected) with wave ballots and append the entries of bin d1 to
 // a candidate list; (3) one workgroup per query finishes the select inside d1
 // (from LDS, or by re-reading the row when d1 holds more than kCap entries),
 // sets those bits, and reads the bitmap out in order.  When the producer of the
 // scores already built the histogram (the streaming score kernel), step (1) is
-// skipped and every step-(2) workgroup finds d1 from the histogram itself.
+// skipped.
 #include "common.h"
 
 namespace smqa {
@@ -35,7 +35,6 @@ struct TopkState {
   int above;     // entries in bins > d1 (all selected)
   int cnt1;      // entries in bin d1
   int nvalid;    // entries in the scored set
-  int done;      // finished histogram workgroups
   int ncand;     // entries appended to cand
   int ncols;     // columns of the query's row (stored by whoever builds the histogram)
   int pad;
@@ -562,15 +561,6 @@ struct Threshold {
   int d1, above, cnt1;
 };
 
-// From the first-digit histogram (in LDS) of a row with nvalid scored entries: the bin d1
-// holding the k-th entry, the count above it and its own count (d1 = -1: all are taken).
-template <int NT>
-__device__ Threshold find_threshold(const unsigned* hist, int nvalid, int k, int* scan_lds, int* sh) {
-  if (nvalid <= k) return Threshold{-1, nvalid, 0};
-  block_find_digit<NT>(hist, kHistBins, k, scan_lds, sh);
-  return Threshold{sh[0], sh[1], (int)hist[sh[0]]};
-}
-
 // A workgroup counts HC consecutive chunks of a row into one LDS histogram before adding its
 // nonzero bins to the query's global one: on long rows the global atomics, not the row
 // reads, bound this kernel (HC = 4 from 20 chunks per row on; shorter rows keep one chunk
@@ -579,64 +569,40 @@ template <int HC>
 __global__ __launch_bounds__(kLongThreads) void topk_hist_kernel(TopkArgs a, TopkWs w) {
   constexpr int NT = kLongThreads;
   __shared__ unsigned hist[kHistBins];
-  __shared__ int scan_lds[NT / 64];
-  __shared__ int sh[4];
   const int t = blockIdx.y;
-  const int ncols = ncols_of(a, t);
-  if (blockIdx.x == 0 && threadIdx.x == 0) w.st[t].ncols = ncols;
-  const int nch = (ncols + HC * kChunk - 1) / (HC * kChunk);
-  if ((int)blockIdx.x >= nch) return;
   const int c0 = blockIdx.x * HC * kChunk;
   const float* row = a.scores + (int64_t)t * a.ld;
-  for (int i = threadIdx.x; i < kHistBins; i += NT) hist[i] = 0;
-  if (threadIdx.x == 0) sh[2] = 0;
-  __syncthreads();
-  // every load of the workgroup's columns goes out before the first is counted
+  // every load of the workgroup's columns goes out first, bounded by the row width (known
+  // without any load; the grid covers it), while the query's column count (a chain of small
+  // dependent loads) is read; columns past that count are masked afterwards
   float v[HC * kPerThread];
 #pragma unroll
   for (int u = 0; u < HC * kPerThread; ++u) {
     const int i = c0 + threadIdx.x + NT * u;
-    v[u] = i < ncols ? row[i] : -__builtin_inff();
+    v[u] = i < a.max_ctx ? row[i] : -__builtin_inff();
   }
-  int cnt = 0;
+  const int ncols = ncols_of(a, t);
+  if (blockIdx.x == 0 && threadIdx.x == 0) w.st[t].ncols = ncols;
+  const int nch = (ncols + HC * kChunk - 1) / (HC * kChunk);
+  if ((int)blockIdx.x >= nch) return;
+  for (int i = threadIdx.x; i < kHistBins; i += NT) hist[i] = 0;
+  __syncthreads();
 #pragma unroll
   for (int u = 0; u < HC * kPerThread; ++u) {
-    const unsigned key = score_key(v[u]);
-    if (key) {
-      atomicAdd(&hist[key >> 20], 1u);
-      ++cnt;
-    }
+    const unsigned key = c0 + (int)threadIdx.x + NT * u < ncols ? score_key(v[u]) : 0u;
+    if (key) atomicAdd(&hist[key >> 20], 1u);
   }
-  if (cnt) atomicAdd(&sh[2], cnt);
   __syncthreads();
+  // the nonzero bins into the query's global histogram; the collect kernel, launched after
+  // this one completes, finds the threshold bin from it
   unsigned* gh = w.hist + (size_t)t * kHistBins;
   for (int i = threadIdx.x; i < kHistBins; i += NT)
     if (hist[i]) atomicAdd(&gh[i], hist[i]);
-  if (threadIdx.x == 0 && sh[2]) atomicAdd(&w.st[t].nvalid, sh[2]);
-  // Device-scope atomics are performed at the memory side, coherent across XCDs; waiting
-  // for their completion orders them before the ticket without an L2 writeback.
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
-  if (threadIdx.x == 0) sh[3] = (atomicAdd(&w.st[t].done, 1) == nch - 1);
-  __syncthreads();
-  if (!sh[3]) return;
-  // last workgroup of this query: find the bin holding the k-th entry (coherent loads)
-  for (int i = threadIdx.x; i < kHistBins; i += NT)
-    hist[i] = __hip_atomic_load(&gh[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  const int nvalid = __hip_atomic_load(&w.st[t].nvalid, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  __syncthreads();
-  const Threshold th = find_threshold<NT>(hist, nvalid, a.k, scan_lds, sh);
-  if (threadIdx.x == 0) {
-    w.st[t].d1 = th.d1;
-    w.st[t].above = th.above;
-    w.st[t].cnt1 = th.cnt1;
-  }
 }
 
-// FROM_HIST: the histogram was filled by the score producer; each workgroup reads it (16 KB,
-// issued with the row loads) and finds d1 itself, and the query's first chunk publishes it
-// for the finish kernel.  Otherwise d1 comes from the histogram kernel.
-template <bool FROM_HIST>
+// The query's histogram was completed by an earlier kernel (the histogram kernel, or the
+// streaming score kernel); each workgroup reads it (16 KB, issued with the row loads) and
+// finds d1 itself, and the query's first chunk publishes it for the finish kernel.
 __global__ __launch_bounds__(kLongThreads) void topk_collect_kernel(TopkArgs a, TopkWs w) {
   constexpr int NT = kLongThreads;
   __shared__ uint2 buf[kChunk];
@@ -658,7 +624,7 @@ __global__ __launch_bounds__(kLongThreads) void topk_collect_kernel(TopkArgs a, 
     v[u] = i < a.max_ctx ? row[i] : -__builtin_inff();
   }
   int d1, cnt1;
-  if (FROM_HIST) {
+  {
     // Thread i holds bins [16i, 16i + 16) in registers (four 16-byte loads; the histogram
     // was completed by an earlier kernel, so plain loads see it).  One block scan of the
     // per-thread counts gives the total and, as total - prefix - own, the count above each
@@ -708,10 +674,6 @@ __global__ __launch_bounds__(kLongThreads) void topk_collect_kernel(TopkArgs a, 
       w.st[t].cnt1 = th.cnt1;
       w.st[t].nvalid = nvalid;
     }
-  } else {
-    if (c0 >= st0.ncols) return;
-    d1 = st0.d1;
-    cnt1 = st0.cnt1;
   }
   const int ncols = st0.ncols;
 #pragma unroll
@@ -867,7 +829,7 @@ hipError_t launch_topk(const TopkArgs& a, hipStream_t s) {
   } else {
     hipLaunchKernelGGL(topk_hist_kernel<1>, dim3(nch, a.T), dim3(kLongThreads), 0, s, a, w);
   }
-  hipLaunchKernelGGL(topk_collect_kernel<false>, dim3(nch, a.T), dim3(kLongThreads), 0, s, a, w);
+  hipLaunchKernelGGL(topk_collect_kernel, dim3(nch, a.T), dim3(kLongThreads), 0, s, a, w);
   hipLaunchKernelGGL(topk_finish_kernel, dim3(a.T), dim3(1024), 0, s, a, w);
   return hipGetLastError();
 }
@@ -890,7 +852,7 @@ hipError_t launch_topk_from_hist(const TopkArgs& a, hipStream_t s) {
   if (a.max_ctx <= kSmallN) return launch_topk(a, s);
   TopkWs w = carve(a.ws, a.T, a.max_ctx);
   const int nch = (a.max_ctx + kChunk - 1) / kChunk;
-  hipLaunchKernelGGL(topk_collect_kernel<true>, dim3(nch, a.T), dim3(kLongThreads), 0, s, a, w);
+  hipLaunchKernelGGL(topk_collect_kernel, dim3(nch, a.T), dim3(kLongThreads), 0, s, a, w);
   hipLaunchKernelGGL(topk_finish_kernel, dim3(a.T), dim3(1024), 0, s, a, w);
   return hipGetLastError();
 }
