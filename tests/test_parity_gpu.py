@@ -737,13 +737,41 @@ def test_decode_step_full_size(lib, name, ts):
     _decode_check(lib, gen(name), ts)
 
 
-def test_decode_step_deterministic(lib):
-    wl = gen("ragged_b32", B=3, lengths=(20000, 40000))
-    announce("decode_step determinism")
+# run to run, bit for bit: the split merge sums partials in a fixed order and the top-k
+# histogram's atomics only add integers
+@pytest.mark.parametrize("name,kw", [
+    ("ragged_b32", dict(B=3, lengths=(20000, 40000))),
+    ("decode_512k", {}),                                      # full size: histogram atomics
+    ("replay_h100k", dict(B=2, lengths=20000, replay=(20000, 128))),
+])
+def test_decode_step_deterministic(lib, name, kw):
+    wl = gen(name, **kw)
+    announce(f"decode_step determinism {name}")
     o1, l1, i1 = gpu_decode(lib, wl)
     o2, l2, i2 = gpu_decode(lib, wl)
     sync()
     assert torch.equal(i1, i2) and torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+# full-size scores in the configurations the benchmark times: every query at 512K, sampled
+# queries of the ragged batch and of the replay chunk (the oracle's cost)
+@pytest.mark.parametrize("name,ts", [
+    ("decode_512k", None),
+    ("ragged_b32", [0, 13, 31]),
+    ("replay_h100k", [0, 127, 128, 700, 1023]),
+])
+def test_score_full_size(lib, name, ts):
+    wl = gen(name)
+    announce(f"score full size {name} T={wl.T}")
+    S = gpu_score(lib, wl)
+    sync()
+    a = np_inputs(wl)
+    ts = list(range(wl.T)) if ts is None else ts
+    S_ref = oracle_scores_for(a, ts)
+    S_gpu = S.cpu().numpy()
+    for i, t in enumerate(ts):
+        ok, msg = close_scores(S_gpu[t], S_ref[i])
+        assert ok, f"query {t}: {msg}"
 
 
 # decode_step inside a captured HIP graph (no allocation, memset or host synchronisation in
