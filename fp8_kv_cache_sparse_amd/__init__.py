@@ -9,5 +9,6 @@ from ._binding import (  # noqa: F401
     sparse_mqa_attend,
     sparse_mqa_attend_fp8kv, sparse_mqa_attend_nvfp4, sparse_mqa_attend_fused, sparse_mqa_attend_mxfp8q,
     decode_step, decode_step_fused, decode_step_noalloc, decode_step_workspace_size, LIB_PATH,
-    DEBUG_LIB_PATH, debug_build, debug_flags, SMQA_DEBUG_POSITION, SMQA_DEBUG_E8M0,
+    DEBUG_LIB_PATH, debug_build, debug_flags, SMQA_DEBUG_POSITION, SMQA_DEBUG_E8M0, SMQA_DEBUG_LAYOUT,
+    SMQA_DEBUG_CAND,
 )

@@ -128,6 +128,8 @@ def debug_flags(clear: bool = True) -> int:
 
 SMQA_DEBUG_POSITION = 1
 SMQA_DEBUG_E8M0 = 2
+SMQA_DEBUG_LAYOUT = 4
+SMQA_DEBUG_CAND = 8
 
 
 def _check(code: int):

@@ -46,19 +46,23 @@ void* symbol_ptr(const Sym& sym, std::atomic<void*>* ptrs, hipError_t* err) {
   return p;
 }
 
-// SMQA_DEBUG builds point the attention kernels at the debug word; release builds leave
-// AttendArgs::dbg null.
-hipError_t attach_debug(smqa::AttendArgs& a) {
+// The debug word's device address on the current device (SMQA_DEBUG builds); null in
+// release builds, whose kernels never touch it.
+hipError_t debug_word_ptr(unsigned** out) {
 #ifdef SMQA_DEBUG
   static std::atomic<void*> ptrs[smqa::kMaxDevices];
   hipError_t e = hipSuccess;
-  a.dbg = (unsigned*)symbol_ptr(HIP_SYMBOL(debug_word), ptrs, &e);
-  return a.dbg ? hipSuccess : e;
+  *out = (unsigned*)symbol_ptr(HIP_SYMBOL(debug_word), ptrs, &e);
+  return *out ? hipSuccess : e;
 #else
-  a.dbg = nullptr;
+  *out = nullptr;
   return hipSuccess;
 #endif
 }
+
+// SMQA_DEBUG builds point the attention kernels at the debug word; release builds leave
+// AttendArgs::dbg null.
+hipError_t attach_debug(smqa::AttendArgs& a) { return debug_word_ptr(&a.dbg); }
 
 }  // namespace
 
@@ -264,6 +268,7 @@ int score_entry(const smqa_layout* L, const uint8_t* q_fp8, const float* w, cons
   smqa::ScoreArgs a{L->seq_start, L->q_start, L->q_pos, L->num_seqs, L->num_q, L->max_ctx,
                     q_fp8, w, k_fp8, k_scale, cand, cand ? n_cand : 0, Hi, Di, scores, ld_scores,
                     nullptr, nullptr, 0, true, fp8mma};
+  if (hipError_t e = debug_word_ptr(&a.dbg); e != hipSuccess) return hip_fail(e, "debug word lookup");
   hipError_t e = smqa::launch_score(a, (hipStream_t)stream);
   return e == hipSuccess ? SMQA_OK : hip_fail(e, fp8mma ? "sparse_mqa_score_fp8mma launch" : "sparse_mqa_score launch");
 }
@@ -595,6 +600,7 @@ int decode_step_impl(const smqa_layout* L, const uint8_t* q_fp8, const float* w,
   // the debug word (SMQA_DEBUG builds) is looked up before anything is launched
   smqa::AttendArgs dbg_probe{};
   if (hipError_t e = attach_debug(dbg_probe); e != hipSuccess) return hip_fail(e, "debug word lookup");
+  sa.dbg = dbg_probe.dbg;
   // When the streaming score kernel runs, it also builds the top-k's first-digit histogram.
   hipError_t e = hipSuccess;
   if (smqa::score_streams(sa)) {

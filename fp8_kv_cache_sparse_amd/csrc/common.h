@@ -107,6 +107,8 @@ struct ScoreArgs {
   bool fill_tail;
   // Contract on the FP8 matrix cores instead of bf16 ones (Di = 128; sparse_mqa_score_fp8mma)
   bool fp8mma;
+  // SMQA_DEBUG builds: the device word the kernels OR kDbg* bits into; null otherwise
+  unsigned* dbg;
 };
 hipError_t launch_score(const ScoreArgs& a, hipStream_t s);
 // True when launch_score takes the streaming kernel, the one that can fill ScoreArgs::hist.
@@ -195,6 +197,8 @@ __host__ __device__ inline bool takes_part(int j, int jmax) { return j >= 0 && j
 __host__ __device__ inline bool e8m0_fp16_exact(unsigned e) { return e == 0u || (e >= 104u && e <= 140u); }
 constexpr unsigned kDbgPosition = 1u;
 constexpr unsigned kDbgE8m0 = 2u;
+constexpr unsigned kDbgLayout = 4u;     // seq_start or q_start decreasing, or a negative q_pos
+constexpr unsigned kDbgCand = 8u;       // a candidate list not strictly ascending
 // OR `bit` into the debug word when `cond` holds (a vector atomic; compiled out of release
 // builds, where `w` is null anyway).
 __device__ __forceinline__ void dbg_flag(unsigned* w, bool cond, unsigned bit) {

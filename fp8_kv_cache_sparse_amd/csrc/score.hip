@@ -89,10 +89,16 @@ __global__ __launch_bounds__(kScoreThreads, 2) void score_kernel(ScoreArgs a) {
   const int64_t base = a.seq_start[b];
   const int len = (int)(a.seq_start[b + 1] - base);
   const int ncols = CAND ? a.n_cand : len;
+#ifdef SMQA_DEBUG
+  if (blockIdx.x == 0) {
+    dbg_flag(a.dbg, threadIdx.x == 0 && (len < 0 || t1 < t0), kDbgLayout);
+    for (int t = t0 + (int)threadIdx.x; t < t1; t += kScoreThreads) dbg_flag(a.dbg, a.q_pos[t] < 0, kDbgLayout);
+  }
+#endif
   if (a.fill_tail) {
     if (CAND) fill_tail(a, t0, a.n_cand);
     else
-      for (int t = t0; t < t1; ++t) fill_tail(a, t, min(a.q_pos[t], len - 1) + 1);
+      for (int t = t0; t < t1; ++t) fill_tail(a, t, max(min(a.q_pos[t], len - 1) + 1, 0));
   }
   int nblk = (ncols + kPosPerWG - 1) / kPosPerWG;
   int blk = blockIdx.x;
@@ -115,6 +121,9 @@ __global__ __launch_bounds__(kScoreThreads, 2) void score_kernel(ScoreArgs a) {
       bool ok = col < ncols;
       if (CAND) {
         pos = ok ? a.cand[(int64_t)t0 * a.n_cand + col] : -1;
+#ifdef SMQA_DEBUG
+        dbg_flag(a.dbg, ok && col + 1 < a.n_cand && a.cand[(int64_t)t0 * a.n_cand + col + 1] <= pos, kDbgCand);
+#endif
         ok = ok && pos >= 0 && pos < len;
       }
       const int64_t rowi = base + (ok ? pos : 0);
@@ -362,9 +371,14 @@ __global__ __launch_bounds__(kScoreThreads) void score_stream_kernel(ScoreArgs a
 
   for (int t = t0; t < t1; ++t) {
     const int p = __builtin_amdgcn_readfirstlane(a.q_pos[t]);
+#ifdef SMQA_DEBUG
+    dbg_flag(a.dbg, blockIdx.x == 0 && threadIdx.x == 0 && (p < 0 || len < 0 || t1 < t0), kDbgLayout);
+#endif
     // (readfirstlane: keeps the compiler from treating the buffer resources built from it
     // as divergent, which would wrap every load in a waterfall loop)
-    const int nvalid = __builtin_amdgcn_readfirstlane(min(min(len, p + 1), a.max_ctx));
+    // clamped at 0: a negative position (outside the stated range) scores nothing and never
+    // moves the -inf fill before the row
+    const int nvalid = __builtin_amdgcn_readfirstlane(max(min(min(len, p + 1), a.max_ctx), 0));
     const int nblk = (nvalid + kPosPerWG - 1) / kPosPerWG;
     if (HIST && blockIdx.x == 0 && tid == 0) a.qcols[(int64_t)t * a.qcols_stride] = nvalid;
     if (a.fill_tail) fill_tail(a, t, nvalid);

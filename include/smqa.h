@@ -462,7 +462,8 @@ const char* smqa_version(void);
  *
  * Every build treats a selected position j outside [0, min(p_t, len_b - 1)] as
  * skipped, like the padding value -1, so a bad index never makes an attention
- * kernel read outside the query's rows.  A library built with SMQA_DEBUG
+ * kernel read outside the query's rows; a negative q_pos scores nothing (its row
+ * is all -INFINITY) and a decreasing seq_start reads as an empty sequence.  A library built with SMQA_DEBUG
  * defined (fp8_kv_cache_sparse_amd/libsmqa_debug.so, from the same sources)
  * also reports what it met, in one word per GPU that the attention kernels OR
  * bits into:
@@ -471,6 +472,10 @@ const char* smqa_version(void);
  *   SMQA_DEBUG_E8M0      an E8M0 exponent e of a row that takes part, outside
  *                        the range P*V holds exactly in fp16 (-23 <= e - 127
  *                        <= 13) and not 0 (MX global caches)
+ *   SMQA_DEBUG_LAYOUT    seq_start or q_start decreasing, or a negative q_pos
+ *                        (sparse_mqa_score*, decode_step*)
+ *   SMQA_DEBUG_CAND      a candidate list that is not strictly ascending
+ *                        (sparse_mqa_score*, decode_step* in candidate mode)
  * smqa_debug_flags waits for the current device to finish its work
  * (hipDeviceSynchronize), stores the word in *flags and clears it when clear
  * is nonzero.  It returns SMQA_OK in a debug build and SMQA_ERR_UNSUPPORTED
@@ -480,6 +485,8 @@ const char* smqa_version(void);
  * ------------------------------------------------------------------------- */
 #define SMQA_DEBUG_POSITION 1u
 #define SMQA_DEBUG_E8M0 2u
+#define SMQA_DEBUG_LAYOUT 4u
+#define SMQA_DEBUG_CAND 8u
 int smqa_debug_flags(uint32_t* flags, int32_t clear);
 
 #ifdef __cplusplus

@@ -136,3 +136,50 @@ def test_decode_step_in_the_debug_library_reports_nothing(lib):
         assert lib.debug_flags() == 0
     assert torch.equal(idx_d, idx_r)
     assert torch.equal(_bits(out_d), _bits(out_r)) and torch.equal(_bits(lse_d), _bits(lse_r))
+
+
+@pytest.mark.parametrize("kw", [
+    pytest.param(dict(B=2, lengths=3000), id="short-rows"),
+    pytest.param(dict(B=2, lengths=300000), id="streaming-rows"),
+])
+def test_negative_query_position_scores_nothing(lib, kw):
+    """A negative q_pos (outside the stated range) leaves its row all -inf and every other
+    row as in a clean call, in both libraries; the debug library reports it as a layout
+    finding.  The bad query is the second, so even a fill that started before its row would
+    land in the first row (inside the buffer), where the comparison sees it."""
+    from helpers import gpu_score
+    announce(f"debug negative q_pos {kw}")
+    wl = synth.generate("decode_8k", seed=6, device=DEV, **kw)
+    S_clean = gpu_score(lib, wl).clone()
+    wl.q_pos[1] = -5
+    S = gpu_score(lib, wl)
+    torch.cuda.synchronize()
+    assert torch.equal(S[0], S_clean[0])
+    assert bool(torch.all(S[1] == -float("inf")))
+    with lib.debug_build():
+        lib.debug_flags(clear=True)
+        S_d = gpu_score(lib, wl)
+        assert lib.debug_flags() == lib.SMQA_DEBUG_LAYOUT
+    assert torch.equal(_bits(S_d), _bits(S))
+
+
+def test_unordered_candidates_are_reported(lib):
+    """Two swapped entries of one candidate list: the debug library reports it and, like the
+    release library, scores each column at the position it names."""
+    from helpers import gpu_score
+    announce("debug candidate order")
+    wl = synth.generate("decode_8k", seed=7, device=DEV, B=2, lengths=(20000, 40000), n_cand=4096)
+    with lib.debug_build():
+        lib.debug_flags(clear=True)
+        gpu_score(lib, wl)
+        assert lib.debug_flags() == 0
+    c = wl.cand[0, 10].clone()
+    wl.cand[0, 10] = wl.cand[0, 11]
+    wl.cand[0, 11] = c
+    S = gpu_score(lib, wl)
+    torch.cuda.synchronize()
+    with lib.debug_build():
+        lib.debug_flags(clear=True)
+        S_d = gpu_score(lib, wl)
+        assert lib.debug_flags() == lib.SMQA_DEBUG_CAND
+    assert torch.equal(_bits(S_d), _bits(S))
