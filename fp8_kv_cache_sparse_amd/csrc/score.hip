@@ -138,19 +138,6 @@ __global__ __launch_bounds__(kScoreThreads, 2) void score_kernel(ScoreArgs a) {
   RawKeys<TPW, DI> raw;
   load_keys(blk, raw);
 
-  // largest query position of the sequence: blocks past it are never scored (dense)
-  int pmax = 0x7FFFFFFF;
-  if (!CAND) {
-    if (tid == 0) s_pmax = -1;
-    __syncthreads();
-    int pm = -1;
-    for (int t = t0 + tid; t < t1; t += kScoreThreads) pm = max(pm, a.q_pos[t]);
-    if (pm >= 0) atomicMax(&s_pmax, pm);
-    __syncthreads();
-    pmax = s_pmax;
-    nblk = min(nblk, pmax / kPosPerWG + 1);
-  }
-
   // q of query t staged in LDS as bf16 (E4M3 -> bf16 exact), converted once per query:
   // fetch_q reads it into registers (16 bytes of E4M3 per piece), put_q converts and
   // stores it into one of the two buffers
@@ -192,12 +179,32 @@ __global__ __launch_bounds__(kScoreThreads, 2) void score_kernel(ScoreArgs a) {
     fetch_q(t, r);
     put_q(buf, r);
   };
-  // One query per sequence (decode): q, w and the position are loaded once, so the block
-  // loop issues no load besides the key prefetch and never waits for it early.
+  // One query per sequence (decode): q, w and the position are loaded once, in the same
+  // round trip as the first block's keys, so the block loop issues no load besides the key
+  // prefetch and never waits for it early.
   const bool single = t1 - t0 == 1;
   const int p0 = __builtin_amdgcn_readfirstlane(a.q_pos[t0]);
+  QRegs q0;
+  if (single) fetch_q(t0, q0);
+
+  // largest query position of the sequence: blocks past it are never scored (dense)
+  int pmax = 0x7FFFFFFF;
+  if (!CAND) {
+    if (single) {
+      pmax = p0;
+    } else {
+      if (tid == 0) s_pmax = -1;
+      __syncthreads();
+      int pm = -1;
+      for (int t = t0 + tid; t < t1; t += kScoreThreads) pm = max(pm, a.q_pos[t]);
+      if (pm >= 0) atomicMax(&s_pmax, pm);
+      __syncthreads();
+      pmax = s_pmax;
+    }
+    nblk = min(nblk, pmax / kPosPerWG + 1);
+  }
   if (single) {
-    stage_q(t0, 0);
+    put_q(0, q0);
     __syncthreads();
   }
 
