@@ -391,29 +391,8 @@ __global__ __launch_bounds__(kScoreThreads) void score_stream_kernel(ScoreArgs a
     if (a.fill_tail) fill_tail(a, t, nvalid);
     if ((int)blockIdx.x >= nblk) continue;
 
-    __syncthreads();   // the previous query's q and histogram are no longer read
-    if (HIST)
-      for (int i = tid; i < kTopkBins; i += kScoreThreads) khist[i] = 0u;
-    for (int pc = tid; pc < 16 * MT * (DI / 16); pc += kScoreThreads) {
-      const int h = pc / (DI / 16), c = pc % (DI / 16);
-      v4u v = {0u, 0u, 0u, 0u};
-      if (h < a.Hi) v = *(const v4u*)(a.q_fp8 + ((int64_t)t * a.Hi + h) * DI + 16 * c);
-      uint8_t* dst = q_lds + h * kQRow + 32 * c;
-      *(v8bf*)dst = fp8x8_to_bf16(v.x, v.y);
-      *(v8bf*)(dst + 16) = fp8x8_to_bf16(v.z, v.w);
-    }
-    if (tid < 16 * MT) w_lds[tid] = tid < a.Hi ? a.w[(int64_t)t * a.Hi + tid] : 0.0f;
-    __syncthreads();
     v8bf qa[MT][NKS];
     float wr[MT][4];
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt) {
-#pragma unroll
-      for (int s2 = 0; s2 < NKS; ++s2)
-        qa[mt][s2] = *(const v8bf*)(q_lds + (16 * mt + n) * kQRow + 2 * (64 * (s2 >> 1) + 16 * g + 8 * (s2 & 1)));
-#pragma unroll
-      for (int r = 0; r < 4; ++r) wr[mt][r] = w_lds[16 * mt + 4 * g + r];
-    }
 
     const __amdgpu_buffer_rsrc_t kr = range_rsrc(a.k_fp8 + base * DI, nvalid * DI);
     const __amdgpu_buffer_rsrc_t sr = range_rsrc(has_scale ? (const void*)(a.k_scale + base) : (const void*)a.k_fp8,
@@ -491,6 +470,40 @@ __global__ __launch_bounds__(kScoreThreads) void score_stream_kernel(ScoreArgs a
     }
     load_kap(r1, blk + G);
     __builtin_amdgcn_sched_barrier(0);
+    // q and the head weights are requested after the first two blocks' keys, so that both
+    // arrive in one round trip to memory
+    constexpr int kQPieces = 16 * MT * (DI / 16);     // 16-byte pieces of the q slice
+    constexpr int kQPer = (kQPieces + kScoreThreads - 1) / kScoreThreads;
+    v4u qv[kQPer];
+#pragma unroll
+    for (int u = 0; u < kQPer; ++u) {
+      const int pc = tid + u * kScoreThreads, h = pc / (DI / 16), c = pc % (DI / 16);
+      qv[u] = v4u{0u, 0u, 0u, 0u};
+      if (pc < kQPieces && h < a.Hi) qv[u] = *(const v4u*)(a.q_fp8 + ((int64_t)t * a.Hi + h) * DI + 16 * c);
+    }
+    const float wv = tid < 16 * MT && tid < a.Hi ? a.w[(int64_t)t * a.Hi + tid] : 0.0f;
+    __syncthreads();   // the previous query's q and histogram are no longer read
+    if (HIST)
+      for (int i = tid; i < kTopkBins; i += kScoreThreads) khist[i] = 0u;
+#pragma unroll
+    for (int u = 0; u < kQPer; ++u) {
+      const int pc = tid + u * kScoreThreads, h = pc / (DI / 16), c = pc % (DI / 16);
+      if (pc < kQPieces) {
+        uint8_t* dst = q_lds + h * kQRow + 32 * c;
+        *(v8bf*)dst = fp8x8_to_bf16(qv[u].x, qv[u].y);
+        *(v8bf*)(dst + 16) = fp8x8_to_bf16(qv[u].z, qv[u].w);
+      }
+    }
+    if (tid < 16 * MT) w_lds[tid] = wv;
+    __syncthreads();
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+#pragma unroll
+      for (int s2 = 0; s2 < NKS; ++s2)
+        qa[mt][s2] = *(const v8bf*)(q_lds + (16 * mt + n) * kQRow + 2 * (64 * (s2 >> 1) + 16 * g + 8 * (s2 & 1)));
+#pragma unroll
+      for (int r = 0; r < 4; ++r) wr[mt][r] = w_lds[16 * mt + 4 * g + r];
+    }
     for (; blk < nblk; blk += 2 * G) {
       run(r0, blk, blk + 2 * G);
       __builtin_amdgcn_sched_barrier(0);   // no conversion of r1 hoisted into r0's half
