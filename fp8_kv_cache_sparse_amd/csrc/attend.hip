@@ -1027,11 +1027,13 @@ __global__ __launch_bounds__(128) void attend_merge_kernel(AttendArgs a, int S) 
   const float* ml = opart + (size_t)S * a.T * a.Hq * D;
   const size_t sstride = (size_t)a.T * a.Hq * D;
   const int d = 4 * (blockIdx.x * 128 + threadIdx.x);
+  // every slot loads a valid partial (slots past S repeat the last one, whose weight is 0),
+  // so the loads carry no branches and all of them are in flight before the first wait
   v4f v[SMAX];
   {
     const float* src = opart + ((int64_t)t * a.Hq + h) * D + (d < D ? d : 0);
 #pragma unroll
-    for (int s = 0; s < SMAX; ++s) v[s] = s < S ? *(const v4f*)(src + s * sstride) : v4f{0.0f, 0.0f, 0.0f, 0.0f};
+    for (int s = 0; s < SMAX; ++s) v[s] = *(const v4f*)(src + min(s, S - 1) * sstride);
   }
   if (threadIdx.x < 64) {
     const int s = threadIdx.x;
@@ -1060,8 +1062,7 @@ __global__ __launch_bounds__(128) void attend_merge_kernel(AttendArgs a, int S) 
   if (d < D) {
     v4f acc = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-    for (int s = 0; s < SMAX; ++s)
-      if (s < S) acc += wts[s] * v[s];
+    for (int s = 0; s < SMAX; ++s) acc += wts[s] * v[s];   // wts[s] = 0 for s >= S
     *(v4f*)(a.out + ((int64_t)t * a.Hq + h) * D + d) = acc * inv;
   }
   if (blockIdx.x == 0 && threadIdx.x == 0 && a.lse)
@@ -1088,9 +1089,10 @@ __global__ __launch_bounds__(512) void attend_fused_epilogue_kernel(AttendArgs a
   const bool act = d < D;
   v4f v[SMAX];
   {
+    // branch-free loads as in attend_merge_kernel (slots past S repeat the last partial)
     const float* src = opart + ((int64_t)t * a.Hq + h) * D + (act ? d : 0);
 #pragma unroll
-    for (int s = 0; s < SMAX; ++s) v[s] = s < S ? *(const v4f*)(src + s * sstride) : v4f{0.0f, 0.0f, 0.0f, 0.0f};
+    for (int s = 0; s < SMAX; ++s) v[s] = *(const v4f*)(src + min(s, S - 1) * sstride);
   }
   if (threadIdx.x < 64) {
     const int s = threadIdx.x;
@@ -1118,8 +1120,7 @@ __global__ __launch_bounds__(512) void attend_fused_epilogue_kernel(AttendArgs a
   const float inv = L > 0.0f ? 1.0f / L : 0.0f;
   v4f acc = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-  for (int s = 0; s < SMAX; ++s)
-    if (s < S) acc += wts[s] * v[s];
+  for (int s = 0; s < SMAX; ++s) acc += wts[s] * v[s];     // wts[s] = 0 for s >= S
   acc *= inv;
   const int r0 = D - 2 * a.rope_pairs;
   if (act && a.rope_pairs > 0 && d >= r0) {
