@@ -371,15 +371,22 @@ __global__ __launch_bounds__(kThreads) void attend_kernel(AttendArgs a, int S, i
         const int pe = pos[re & 31];
         const int rr = 8 * (ln & 3) + wave;
         const int pr = pos[rr];
-        // code rows 8u + wave, u = 0..3
+        // code rows 8u + wave, u = 0..3.  Lane r (r < 32) forms row r's source address once
+        // (the dummy row when the row takes no part), so a row's load costs two readlanes
+        // instead of a scalar bounds check and 64-bit multiply per row.
+        {
+          const bool okl = (xt + (ln & 31) < c.gx1) & takes_part(pall, c.jmax);
+          const uint64_t al = (uint64_t)(okl ? codes_base + (int64_t)pall * (D / 2) : dummy);
+          const unsigned alo = (unsigned)al, ahi = (unsigned)(al >> 32);
 #pragma unroll
-        for (int u = 0; u < kRows / 8; ++u) {
-          const int r = 8 * u + wave;
-          const int j = __builtin_amdgcn_readlane(pall, r);
-          const bool ok = (xt + r < c.gx1) & takes_part(j, c.jmax);
-          const uint8_t* row = codes_base + (int64_t)j * (D / 2);   // formed for every j, used when ok
-          const uint8_t* src = ok ? row : dummy;
-          if (ln < D / 32) gload16(src + 16 * ln, lds_addr(B + r * G::RS4));
+          for (int u = 0; u < kRows / 8; ++u) {
+            const int r = 8 * u + wave;
+            // (readlane returns int: both halves widen through unsigned, so the low word is
+            // not sign-extended into the high one)
+            const uint64_t ar = ((uint64_t)(unsigned)__builtin_amdgcn_readlane(ahi, r) << 32) |
+                                (uint64_t)(unsigned)__builtin_amdgcn_readlane(alo, r);
+            if (ln < D / 32) gload16((const uint8_t*)ar + 16 * ln, lds_addr(B + r * G::RS4));
+          }
         }
         if constexpr (NV) {
           // E4M3 scale dwords q = 2m + lane / 32 of row lane % 32 -> table[q][row]: D/128
