@@ -613,12 +613,26 @@ int decode_step_impl(const smqa_layout* L, const uint8_t* q_fp8, const float* w,
   }
   e = smqa::launch_score(sa, s);
   if (e != hipSuccess) return hip_fail(e, "decode_step score launch");
-  e = sa.hist ? smqa::launch_topk_from_hist(ta, s) : smqa::launch_topk(ta, s);
-  if (e != hipSuccess) return hip_fail(e, "decode_step topk launch");
+  // Dense rows of at most kSelCols columns at D = 1664: every attention workgroup takes the
+  // query's selection from the scores itself (same selection as topk_select), so the step has
+  // no top-k launch and the workgroups start on q while the select runs.
+  const bool sel_in_attend = !fz && !cand && L->max_ctx <= smqa::kSelCols &&
+                             smqa::attend_select_fits(L->num_q, k, W, Hq, D);
+  if (!sel_in_attend) {
+    e = sa.hist ? smqa::launch_topk_from_hist(ta, s) : smqa::launch_topk(ta, s);
+    if (e != hipSuccess) return hip_fail(e, "decode_step topk launch");
+  }
   smqa::AttendArgs aa{L->seq_start, L->q_start, L->q_pos, L->num_seqs, L->num_q, q_bf16, kv_codes,
                       kv_e8m0, kv_rowscale, idx, k, swa_fp8, swa_scale, swa_pos0, swa_clip, W, Hq, D,
                       sm_scale, out, lse, ws + d.attend_off};
   aa.dbg = dbg_probe.dbg;
+  if (sel_in_attend) {
+    aa.kv_fmt = smqa::kKvMXS;
+    aa.sel_scores = scores;
+    aa.sel_ld = cols;
+    aa.sel_max_ctx = L->max_ctx;
+    aa.sel_idx = idx;
+  }
   if (fz) {
     aa.rope_pairs = fz->rope_pairs;
     aa.rope_cos = fz->rope_pairs > 0 ? fz->rope_cos : nullptr;

@@ -1222,6 +1222,16 @@ int attend_splits(int32_t T, int32_t k, int32_t W, int32_t Hq, int32_t D, int32_
   return p.S;
 }
 
+// Whether decode_step may take the selection in the attention kernel (kKvMXS): the
+// dimension-split kernel at D = 1664, every split of at most four tiles (so a workgroup's
+// positions fit its ring; the kernel cuts ranges of ceil(nominal / S) tiles at most).
+bool attend_select_fits(int32_t T, int32_t k, int32_t W, int32_t Hq, int32_t D) {
+  const AttPlan p = attend_plan(T, k, W, Hq, D);
+  if (p.S == 0 || !p.wide || D != 1664) return false;
+  const int nominal = (k + kGRows - 1) / kGRows + (W + kWRows - 1) / kWRows;
+  return (nominal + p.S - 1) / p.S <= 4;
+}
+
 size_t attend_workspace_bytes(int32_t T, int32_t k, int32_t W, int32_t Hq, int32_t D) {
   const int S = attend_splits(T, k, W, Hq, D);
   if (S <= 1) return 0;

@@ -47,6 +47,12 @@
 //
 // Several tile ranges of one (query, head group) leave unnormalised partials that
 // attend_merge_kernel combines by log-sum-exp.
+//
+// kMXS (decode_step on dense rows of at most kSelCols columns, D = 1664): instead of reading
+// the positions of its tiles, every workgroup of a query loads the query's scores with q and
+// computes the whole top-k itself (the selection topk_select makes, bit for bit) before its
+// first gather; the first workgroup of the query writes the selection out.  The step then has
+// no top-k launch, and the q staging overlaps the score loads.
 #include <type_traits>
 
 #include "common.h"
@@ -91,7 +97,8 @@ constexpr int align16(int x) { return (x + 15) & ~15; }
 // E8M0 bytes are the B operand and its scale as they sit in LDS, window rows are E4M3 with
 // scale 2^0; P.V is the MX one.
 constexpr int kMX = kKvMX, kFP8 = kKvFP8, kNV = kKvNV, kMXF = kKvMXF, kMXR = kKvMXR, kMXN = kKvMXN;
-constexpr bool mx_like(int F) { return F == kMX || F == kMXF || F == kMXR || F == kMXN; }
+constexpr int kMXS = kKvMXS;
+constexpr bool mx_like(int F) { return F == kMX || F == kMXF || F == kMXR || F == kMXN || F == kMXS; }
 
 // LDS geometry for latent width D and global format F (compile time, so every offset is an
 // immediate).
@@ -268,6 +275,9 @@ template <int D, int F>
 __global__ __launch_bounds__(kThreads) void attend_kernel(AttendArgs a, int S, int ngroups, int total) {
   using G = Geo<D, F>;
   constexpr bool G8 = F == kFP8, NV = F == kNV;
+  // kMXS: the workgroup takes the query's selection from its scores itself (below) instead of
+  // reading positions; every range then holds at most kNBuf tiles (checked by the caller)
+  constexpr bool SEL = F == kMXS;
   constexpr int GR = G8 ? kWRows : kRows;         // global rows per tile
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
 
@@ -438,7 +448,7 @@ __global__ __launch_bounds__(kThreads) void attend_kernel(AttendArgs a, int S, i
 
   // ---- prologue: positions of the first three tiles, q and the per-query values (one
   // round trip), then the rows of the first two tiles
-  if (wave == 0) {
+  if (!SEL && wave == 0) {
     for (int u = 0; u < kNBuf; ++u)
       if (c.tb + u < c.te && c.tb + u < c.ng) load_pos(c.tb + u, u);
   }
@@ -568,6 +578,17 @@ __global__ __launch_bounds__(kThreads) void attend_kernel(AttendArgs a, int S, i
   } else {
     build_q();
   }
+  // kMXS: the query's scores, columns tid + 512 u, requested with q
+  constexpr int kSPer = kSelCols / kThreads;
+  float sv[SEL ? kSPer : 1];
+  if constexpr (SEL) {
+    const float* srow = a.sel_scores + (int64_t)t * a.sel_ld;
+#pragma unroll
+    for (int u = 0; u < kSPer; ++u) {
+      const int col = tid + kThreads * u;
+      sv[u] = col < a.sel_max_ctx ? srow[col] : -__builtin_inff();
+    }
+  }
   {
     const SeqInfo si = locate_seq(a, t, lane);
     c.b = si.b;
@@ -598,6 +619,171 @@ __global__ __launch_bounds__(kThreads) void attend_kernel(AttendArgs a, int S, i
   const bool pre = te - tb <= kNBuf;
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
+  if constexpr (SEL) {
+    // The query's top-k as topk_select takes it (the k largest scores of columns 0 ..
+    // min(p, len - 1), ties to the lower column, -1 past the valid columns), computed by every
+    // workgroup of the query: 11-bit radix digits after the bits every valid key shares, then
+    // one block scan of packed (ties, greater) counts gives each thread the output offsets of
+    // its 16 consecutive columns.  The positions of this range's tiles go to the ring; the
+    // first workgroup of the query also writes the selection out.  LDS: keys in the logits
+    // area, the histogram past the staged q, counters in the P area (all idle until the
+    // first tile).
+    static_assert(kSelCols * 4 <= 8 * 32 * kRows * 4, "the keys fit the logits area");
+    static_assert(32 * QS + 2048 * 4 <= kNBuf * G::BUF, "the histogram fits past the staged q");
+    unsigned* keys = (unsigned*)(smem + G::RED);
+    unsigned* hist = (unsigned*)(smem + 32 * QS);
+    int* scr = (int*)(smem + G::PS);                 // partials [3][8], scan [8], sh [4]
+    int* scan = scr + 24;
+    int* sh = scr + 32;
+    int* ring = (int*)(smem + G::RING);
+    const int ncols = max(0, min(c.jmax + 1, a.sel_max_ctx));
+#pragma unroll
+    for (int u = 0; u < kSPer; ++u) {
+      const int col = tid + kThreads * u;
+      keys[col] = col < ncols ? score_key(sv[u]) : 0u;
+    }
+    for (int i = tid; i < 2048; i += kThreads) hist[i] = 0u;
+    if (tid < kNBuf * kRows) ring[tid] = -1;
+    __syncthreads();
+    unsigned key[kSPer];
+#pragma unroll
+    for (int u = 0; u < kSPer; u += 4) {
+      const v4u k4 = *(const v4u*)(keys + kSPer * tid + u);
+      key[u] = k4.x;
+      key[u + 1] = k4.y;
+      key[u + 2] = k4.z;
+      key[u + 3] = k4.w;
+    }
+    const int c0 = kSPer * tid;
+    // valid count and the min / max valid key (min as the max of ~key)
+    int cnt = 0;
+    unsigned nlo = 0u, hi = 0u;
+#pragma unroll
+    for (int u = 0; u < kSPer; ++u) {
+      cnt += key[u] != 0u;
+      nlo = key[u] ? max(nlo, ~key[u]) : nlo;
+      hi = max(hi, key[u]);
+    }
+    cnt = wave_inclusive_sum(cnt);
+    nlo = wave_inclusive_max(nlo);
+    hi = wave_inclusive_max(hi);
+    if (lane == 63) {
+      scr[wave] = cnt;
+      scr[8 + wave] = (int)nlo;
+      scr[16 + wave] = (int)hi;
+    }
+    __syncthreads();
+    int nvalid = 0;
+    nlo = 0u;
+    hi = 0u;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      nvalid += scr[i];
+      nlo = max(nlo, (unsigned)scr[8 + i]);
+      hi = max(hi, (unsigned)scr[16 + i]);
+    }
+    const unsigned lo = ~nlo;
+    unsigned tau = 1u;                               // every valid key is >= 1
+    int tie_need = kSelCols;
+    if (nvalid > a.k) {
+      int nbits = lo == hi ? 32 : __clz((int)(lo ^ hi));
+      unsigned prefix = nbits == 32 ? lo : (nbits == 0 ? 0u : (lo >> (32 - nbits)) << (32 - nbits));
+      int need = a.k;
+      bool whole_bin = false;
+      while (nbits < 32) {
+        const int dbits = min(11, 32 - nbits);
+        const int shift = 32 - nbits - dbits;
+        const unsigned dmask = (1u << dbits) - 1u;
+#pragma unroll
+        for (int u = 0; u < kSPer; ++u) {
+          const bool match = key[u] != 0u && (nbits == 0 || (key[u] >> (32 - nbits)) == (prefix >> (32 - nbits)));
+          if (match) atomicAdd(&hist[(key[u] >> shift) & dmask], 1u);
+        }
+        __syncthreads();
+        // thread i holds bins 2047 - 4i .. 2044 - 4i (counting down with the thread index, so
+        // a prefix sum counts the keys above)
+        int hb[4], local = 0;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          hb[j] = (int)hist[2047 - 4 * tid - j];
+          local += hb[j];
+        }
+        const int incl = wave_inclusive_sum(local);
+        if (lane == 63) scan[wave] = incl;
+        if (tid == 0) sh[0] = -1;
+        __syncthreads();
+        int cum = incl - local;
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+          if (i < wave) cum += scan[i];
+        if (cum < need && need <= cum + local) {
+          int cc = cum;
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            if (cc < need && need <= cc + hb[j]) {
+              sh[0] = 2047 - 4 * tid - j;
+              sh[1] = cc;
+              sh[2] = hb[j];
+            }
+            cc += hb[j];
+          }
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j) hist[4 * tid + j] = 0u;   // every bin was read before the barrier
+        __syncthreads();
+        const int d = sh[0];
+        if (d < 0) break;                            // cannot happen: nvalid > k
+        need -= sh[1];
+        const int inbin = sh[2];
+        prefix |= (unsigned)d << shift;
+        nbits += dbits;
+        if (inbin == need) {                         // the whole bin is taken
+          whole_bin = true;
+          break;
+        }
+      }
+      tau = max(prefix, 1u);                         // a bin's lower bound may be the invalid key 0
+      if (!whole_bin) tie_need = need;               // tau fully resolved: `need` of its ties
+    }
+    int ngt = 0, nties = 0;
+#pragma unroll
+    for (int u = 0; u < kSPer; ++u) {
+      ngt += key[u] > tau;
+      nties += key[u] == tau;
+    }
+    const int x = (nties << 16) | ngt;               // both counts fit 16 bits
+    const int xi = wave_inclusive_sum(x);
+    if (lane == 63) scan[wave] = xi;
+    __syncthreads();
+    int pre_x = xi - x, total = 0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int si = scan[i];
+      pre_x += i < wave ? si : 0;
+      total += si;
+    }
+    int tie_rank = pre_x >> 16;
+    int off = (pre_x & 0xFFFF) + min(tie_rank, tie_need);
+    const int nsel = (total & 0xFFFF) + min(total >> 16, tie_need);
+    const bool writer = split == 0 && grp == 0;
+    int32_t* dst = a.sel_idx + (int64_t)t * a.k;
+    const int r0 = kRows * tb, r1 = kRows * min(te, c.ng);
+#pragma unroll
+    for (int u = 0; u < kSPer; ++u) {
+      bool sel = key[u] > tau;
+      if (key[u] == tau) sel = tie_rank++ < tie_need;
+      if (sel) {
+        if (off < a.k) {
+          if (writer) dst[off] = c0 + u;
+          if (off >= r0 && off < r1) ring[off - r0] = c0 + u;
+        }
+        ++off;
+      }
+    }
+    if (writer)
+      for (int i = nsel + tid; i < a.k; i += kThreads) dst[i] = -1;
+    __syncthreads();
+  }
   if constexpr (QLDS) {
     build_q();
     __syncthreads();                               // q read: the tile buffers are free
@@ -950,7 +1136,7 @@ __global__ __launch_bounds__(kThreads) void attend_kernel(AttendArgs a, int S, i
     const bool more = !pre && i + 2 < te;
     const bool more_g = i + 2 < c.ng;
     // the prologue loaded the positions of the first kNBuf tiles
-    if (wave == 0 && n >= 1 && i + 3 < te && i + 3 < c.ng) load_pos(i + 3, (n + 3) & 3);
+    if (!SEL && wave == 0 && n >= 1 && i + 3 < te && i + 3 < c.ng) load_pos(i + 3, (n + 3) & 3);
     // waves 0..3 issue the loads of tile i+2 before their products, waves 4..7 after them,
     // so half the waves queue for the vector-memory path while the other half run MFMAs
     if (more && wave < 4) issue(i + 2, (n + 2) & 3, (n + 2) & 3);
@@ -1123,6 +1309,13 @@ hipError_t launch(const AttendArgs& a, int S, hipStream_t s) {
   return e != hipSuccess ? e : ((F == kMXF || F == kMXR) ? hipSuccess : launch_attend_merge(a, S, s));
 }
 
+// kMXS (decode_step's selection in the attention kernel) exists at D = 1664 only
+template <int D>
+hipError_t launch_sel(const AttendArgs& a, int S, hipStream_t s) {
+  if constexpr (D == 1664) return launch<D, kMXS>(a, S, s);
+  else return hipErrorInvalidValue;
+}
+
 }  // namespace sd
 
 int sd_lds_bytes(int32_t D) {
@@ -1147,7 +1340,8 @@ hipError_t launch_attend_sd(const AttendArgs& a, int S, hipStream_t s) {
   switch (a.D) {
 #define SMQA_SD_D(d)                                              \
   case d:                                                         \
-    return a.kv_fmt == sd::kFP8   ? sd::launch<d, sd::kFP8>(a, S, s)  \
+    return a.kv_fmt == sd::kMXS   ? sd::launch_sel<d>(a, S, s)        \
+           : a.kv_fmt == sd::kFP8 ? sd::launch<d, sd::kFP8>(a, S, s)  \
            : a.kv_fmt == sd::kNV  ? sd::launch<d, sd::kNV>(a, S, s)   \
            : a.kv_fmt == sd::kMXN ? sd::launch<d, sd::kMXN>(a, S, s)  \
            : a.kv_fmt == sd::kMXF ? sd::launch<d, sd::kMXF>(a, S, s)  \

@@ -42,6 +42,31 @@ __device__ __forceinline__ float key_score(unsigned key) {
   return __uint_as_float((key & 0x80000000u) ? (key ^ 0x80000000u) : ~key);
 }
 
+// Inclusive prefix sum over a wave with DPP row shifts and row broadcasts: within each
+// row of 16 lanes by shifts of 1, 2, 4, 8 (lanes shifted in from outside the row read
+// 0), then the total of row 0 into row 1 and of row 2 into row 3, then the total of
+// rows 0-1 into rows 2-3.
+__device__ __forceinline__ int wave_inclusive_sum(int v) {
+  v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xf, 0xf, true);   // row_shr:1
+  v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xf, 0xf, true);   // row_shr:2
+  v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xf, 0xf, true);   // row_shr:4
+  v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xf, 0xf, true);   // row_shr:8
+  v += __builtin_amdgcn_update_dpp(0, v, 0x142, 0xa, 0xf, false);  // row_bcast:15 -> rows 1, 3
+  v += __builtin_amdgcn_update_dpp(0, v, 0x143, 0xc, 0xf, false);  // row_bcast:31 -> rows 2, 3
+  return v;
+}
+
+// Inclusive running maximum over a wave (unsigned; 0 is the identity), same DPP pattern.
+__device__ __forceinline__ unsigned wave_inclusive_max(unsigned v) {
+  v = max(v, (unsigned)__builtin_amdgcn_update_dpp(0, (int)v, 0x111, 0xf, 0xf, true));
+  v = max(v, (unsigned)__builtin_amdgcn_update_dpp(0, (int)v, 0x112, 0xf, 0xf, true));
+  v = max(v, (unsigned)__builtin_amdgcn_update_dpp(0, (int)v, 0x114, 0xf, 0xf, true));
+  v = max(v, (unsigned)__builtin_amdgcn_update_dpp(0, (int)v, 0x118, 0xf, 0xf, true));
+  v = max(v, (unsigned)__builtin_amdgcn_update_dpp(0, (int)v, 0x142, 0xa, 0xf, false));
+  v = max(v, (unsigned)__builtin_amdgcn_update_dpp(0, (int)v, 0x143, 0xc, 0xf, false));
+  return v;
+}
+
 // Largest b with q_start[b] <= t (queries are grouped by sequence).
 __device__ __forceinline__ int seq_of_query(const int32_t* q_start, int B, int t) {
   int lo = 0, hi = B;
@@ -150,7 +175,10 @@ hipError_t launch_topk_from_hist(const TopkArgs& a, hipStream_t s);
 // launch_attend_fused only).
 // kKvMXN: the MX format with Q.K^T on the scaled matrix cores, the query quantised to
 // MXFP8 in the kernel and the E2M1 rows and their E8M0 bytes consumed as stored.
-enum KvFmt : int32_t { kKvMX = 0, kKvFP8 = 1, kKvNV = 2, kKvMXF = 3, kKvMXR = 4, kKvMXN = 5 };
+// kKvMXS: the MX format, the selection computed in the attention kernel from the query's
+// scores (decode_step on rows of at most kSelCols columns; set by decode_step only).
+enum KvFmt : int32_t { kKvMX = 0, kKvFP8 = 1, kKvNV = 2, kKvMXF = 3, kKvMXR = 4, kKvMXN = 5, kKvMXS = 6 };
+constexpr int kSelCols = 8192;   // the longest row kKvMXS selects from (512 threads x 16)
 
 struct AttendArgs {
   const int64_t* seq_start;
@@ -185,6 +213,12 @@ struct AttendArgs {
   float* out_scale;
   // SMQA_DEBUG builds: the device word the kernels OR kDbg* bits into; null otherwise
   unsigned* dbg;
+  // kKvMXS: the scores [T][sel_ld] the selection is taken from (columns < sel_max_ctx read),
+  // and the selection's output [T][k] (idx above is not read)
+  const float* sel_scores;
+  int32_t sel_ld;
+  int32_t sel_max_ctx;
+  int32_t* sel_idx;
 };
 
 // A selected position j takes part iff 0 <= j <= jmax = min(p_t, len_b - 1); -1 pads the
@@ -215,6 +249,7 @@ __device__ __forceinline__ void dbg_flag(unsigned* w, bool cond, unsigned bit) {
 // workgroup (static + dynamic) of the chosen plan.
 int attend_splits(int32_t T, int32_t k, int32_t W, int32_t Hq, int32_t D, int32_t* lds = nullptr);
 size_t attend_workspace_bytes(int32_t T, int32_t k, int32_t W, int32_t Hq, int32_t D);
+bool attend_select_fits(int32_t T, int32_t k, int32_t W, int32_t Hq, int32_t D);
 hipError_t launch_attend(const AttendArgs& a, hipStream_t s);
 hipError_t launch_attend_fmt(const AttendArgs& a, hipStream_t s);   // kKvFP8, kKvNV, kKvMXN
 size_t attend_fused_workspace_bytes(int32_t T, int32_t k, int32_t W, int32_t Hq, int32_t D);

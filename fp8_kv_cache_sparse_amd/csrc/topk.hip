@@ -85,31 +85,6 @@ __device__ __forceinline__ int ncols_of(const TopkArgs& a, int t) {
 }
 
 
-// Inclusive prefix sum over a wave with DPP row shifts and row broadcasts: within each
-// row of 16 lanes by shifts of 1, 2, 4, 8 (lanes shifted in from outside the row read
-// 0), then the total of row 0 into row 1 and of row 2 into row 3, then the total of
-// rows 0-1 into rows 2-3.
-__device__ __forceinline__ int wave_inclusive_sum(int v) {
-  v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xf, 0xf, true);   // row_shr:1
-  v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xf, 0xf, true);   // row_shr:2
-  v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xf, 0xf, true);   // row_shr:4
-  v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xf, 0xf, true);   // row_shr:8
-  v += __builtin_amdgcn_update_dpp(0, v, 0x142, 0xa, 0xf, false);  // row_bcast:15 -> rows 1, 3
-  v += __builtin_amdgcn_update_dpp(0, v, 0x143, 0xc, 0xf, false);  // row_bcast:31 -> rows 2, 3
-  return v;
-}
-
-// Inclusive running maximum over a wave (unsigned; 0 is the identity), same DPP pattern.
-__device__ __forceinline__ unsigned wave_inclusive_max(unsigned v) {
-  v = max(v, (unsigned)__builtin_amdgcn_update_dpp(0, (int)v, 0x111, 0xf, 0xf, true));
-  v = max(v, (unsigned)__builtin_amdgcn_update_dpp(0, (int)v, 0x112, 0xf, 0xf, true));
-  v = max(v, (unsigned)__builtin_amdgcn_update_dpp(0, (int)v, 0x114, 0xf, 0xf, true));
-  v = max(v, (unsigned)__builtin_amdgcn_update_dpp(0, (int)v, 0x118, 0xf, 0xf, true));
-  v = max(v, (unsigned)__builtin_amdgcn_update_dpp(0, (int)v, 0x142, 0xa, 0xf, false));
-  v = max(v, (unsigned)__builtin_amdgcn_update_dpp(0, (int)v, 0x143, 0xc, 0xf, false));
-  return v;
-}
-
 // Digit search by one wave: hist[nbins] (nbins = 64 * per), lane l owning the per bins
 // below nbins - per * l, in descending order.  Writes sh[0] = d with
 // count(bins > d) < need <= count(bins >= d) (-1 if none) and sh[1] = count(bins > d).

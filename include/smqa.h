@@ -355,7 +355,10 @@ int sparse_mqa_attend_fused(const smqa_layout* L,
  * launches between them).  Arguments mean what they mean in the three calls;
  * idx_out (int32 [T][k]) optionally receives the selection.  Works for any
  * layout: decode (one query per sequence at p = len - 1) and bounded-replay
- * chunks (several queries per sequence with swa_clip).
+ * chunks (several queries per sequence with swa_clip).  On dense rows of at
+ * most 8192 columns with D = 1664 the attention kernel takes the selection
+ * from the scores itself (no separate top-k launch); the selection, the
+ * output and the LSE are those of the three separate calls, bit for bit.
  */
 int decode_step(const smqa_layout* L,
                 const uint8_t* q_fp8, const float* w,
