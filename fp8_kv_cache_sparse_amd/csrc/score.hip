@@ -37,10 +37,12 @@ __device__ __forceinline__ v8bf fp8x8_to_bf16(unsigned w0, unsigned w1) {
 __device__ __forceinline__ float relu(float x) { return __int_as_float(max(__float_as_int(x), 0)); }
 
 // -inf into columns [from, a.ld) of query t's score row, spread over the workgroups along x.
-__device__ __forceinline__ void fill_tail(const ScoreArgs& a, int t, int from) {
-  for (int64_t c = from + (int64_t)blockIdx.x * kScoreThreads + threadIdx.x; c < a.ld;
-       c += (int64_t)gridDim.x * kScoreThreads)
+__device__ __forceinline__ void fill_tail(const ScoreArgs& a, int t, int from, int wg, int nwg) {
+  for (int64_t c = from + (int64_t)wg * kScoreThreads + threadIdx.x; c < a.ld; c += (int64_t)nwg * kScoreThreads)
     a.scores[(int64_t)t * a.ld + c] = -__builtin_inff();
+}
+__device__ __forceinline__ void fill_tail(const ScoreArgs& a, int t, int from) {
+  fill_tail(a, t, from, blockIdx.x, gridDim.x);
 }
 
 constexpr int kQRow = 272;   // LDS bytes per head row of bf16 q (256 + 16 pad: conflict-free b128 reads)
@@ -362,13 +364,84 @@ __global__ __launch_bounds__(kScoreThreads) void score_stream_kernel(ScoreArgs a
   __shared__ __align__(16) uint8_t q_lds[16 * MT * kQRow];
   __shared__ float w_lds[16 * MT];
   __shared__ unsigned khist[HIST ? kTopkBins : 1];
+  __shared__ int s_scan[kScoreThreads / 64];
+  __shared__ int64_t s_own[4];
   constexpr int TPW = 4, NKS = DI / 32, NH = DI / 64;
   constexpr int kPosPerWG = 4 * 16 * TPW;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, g = lane >> 4, n = lane & 15;
-  const int b = blockIdx.y, G = gridDim.x;
-  const int t0 = a.q_start[b], t1 = a.q_start[b + 1];
-  const int64_t base = a.seq_start[b];
-  const int len = (int)(a.seq_start[b + 1] - base);
+  // The workgroups of the 1D grid are dealt to the sequences in proportion to their work (at
+  // least one each), so rows of different lengths finish together: with work_i = the blocks
+  // of min(len_i, max_ctx) times the queries of sequence i, P_i its exclusive prefix and N the
+  // total, sequence i owns workgroups [F_i, F_{i+1}), F_i = i + floor(P_i (G - B) / N) and
+  // F_B = G, and a workgroup strides over its sequence's blocks with the sequence's count.
+  // The thread that finds the owner passes the sequence's bounds on, so the mapping adds a
+  // block scan and no round trip to memory.  Thread tid takes sequences tid * spt .. + spt - 1.
+  int b, wl, Gb, t0, t1, len;
+  int64_t base;
+  {
+    const int B = a.B, Gt = gridDim.x, w = blockIdx.x;
+    const int spt = (B + kScoreThreads - 1) / kScoreThreads;
+    auto work = [&](int i, int64_t& sb, int& ln, int& q0, int& q1) {
+      sb = a.seq_start[i];
+      ln = (int)(a.seq_start[i + 1] - sb);
+      q0 = a.q_start[i];
+      q1 = a.q_start[i + 1];
+      return ((max(min(ln, a.max_ctx), 0) + kPosPerWG - 1) / kPosPerWG) * max(q1 - q0, 0);
+    };
+    int mine = 0;
+    for (int j = 0; j < spt; ++j) {
+      const int i = tid * spt + j;
+      int64_t sb;
+      int ln, q0, q1;
+      if (i < B) mine += work(i, sb, ln, q0, q1);
+    }
+    const int incl = wave_inclusive_sum(mine);
+    if (lane == 63) s_scan[wave] = incl;
+    __syncthreads();
+    int P = incl - mine, N = 0;
+#pragma unroll
+    for (int i = 0; i < kScoreThreads / 64; ++i) {
+      P += i < wave ? s_scan[i] : 0;
+      N += s_scan[i];
+    }
+    const int64_t spare = Gt - B;
+    for (int j = 0; j < spt; ++j) {
+      const int i = tid * spt + j;
+      if (i < B) {
+        int64_t sb;
+        int ln, q0, q1;
+        const int wk = work(i, sb, ln, q0, q1);
+        const int f0 = i + (N > 0 ? (int)((int64_t)P * spare / N) : 0);
+        const int f1 = i + 1 == B ? Gt : i + 1 + (N > 0 ? (int)((int64_t)(P + wk) * spare / N) : 0);
+        if (f0 <= w && w < f1) {
+          s_own[0] = ((int64_t)i << 32) | (unsigned)(w - f0);
+          s_own[1] = ((int64_t)(f1 - f0) << 32) | (unsigned)ln;
+          s_own[2] = ((int64_t)q0 << 32) | (unsigned)q1;
+          s_own[3] = sb;
+        }
+        P += wk;
+      }
+    }
+    __syncthreads();
+    b = (int)(s_own[0] >> 32);
+    wl = (int)(unsigned)s_own[0];
+    Gb = (int)(s_own[1] >> 32);
+    len = (int)(unsigned)s_own[1];
+    t0 = (int)(s_own[2] >> 32);
+    t1 = (int)(unsigned)s_own[2];
+    base = s_own[3];
+    // (uniform by construction; readfirstlane lets the compiler build the buffer resources
+    // from them in scalar registers)
+    b = __builtin_amdgcn_readfirstlane(b);
+    wl = __builtin_amdgcn_readfirstlane(wl);
+    Gb = __builtin_amdgcn_readfirstlane(Gb);
+    t0 = __builtin_amdgcn_readfirstlane(t0);
+    t1 = __builtin_amdgcn_readfirstlane(t1);
+    len = __builtin_amdgcn_readfirstlane(len);
+    base = (int64_t)(((uint64_t)(unsigned)__builtin_amdgcn_readfirstlane((int)(base >> 32)) << 32) |
+                     (uint64_t)(unsigned)__builtin_amdgcn_readfirstlane((int)base));
+  }
+  const int G = Gb;
   const bool has_scale = a.k_scale != nullptr;
 
   struct Slot {
@@ -379,7 +452,7 @@ __global__ __launch_bounds__(kScoreThreads) void score_stream_kernel(ScoreArgs a
   for (int t = t0; t < t1; ++t) {
     const int p = __builtin_amdgcn_readfirstlane(a.q_pos[t]);
 #ifdef SMQA_DEBUG
-    dbg_flag(a.dbg, blockIdx.x == 0 && threadIdx.x == 0 && (p < 0 || len < 0 || t1 < t0), kDbgLayout);
+    dbg_flag(a.dbg, wl == 0 && threadIdx.x == 0 && (p < 0 || len < 0 || t1 < t0), kDbgLayout);
 #endif
     // (readfirstlane: keeps the compiler from treating the buffer resources built from it
     // as divergent, which would wrap every load in a waterfall loop)
@@ -387,9 +460,9 @@ __global__ __launch_bounds__(kScoreThreads) void score_stream_kernel(ScoreArgs a
     // moves the -inf fill before the row
     const int nvalid = __builtin_amdgcn_readfirstlane(max(min(min(len, p + 1), a.max_ctx), 0));
     const int nblk = (nvalid + kPosPerWG - 1) / kPosPerWG;
-    if (HIST && blockIdx.x == 0 && tid == 0) a.qcols[(int64_t)t * a.qcols_stride] = nvalid;
-    if (a.fill_tail) fill_tail(a, t, nvalid);
-    if ((int)blockIdx.x >= nblk) continue;
+    if (HIST && wl == 0 && tid == 0) a.qcols[(int64_t)t * a.qcols_stride] = nvalid;
+    if (a.fill_tail) fill_tail(a, t, nvalid, wl, Gb);
+    if (wl >= nblk) continue;
 
     v8bf qa[MT][NKS];
     float wr[MT][4];
@@ -455,7 +528,7 @@ __global__ __launch_bounds__(kScoreThreads) void score_stream_kernel(ScoreArgs a
 
     // Issue order matters: the loop consumes tiles in this order and waits on the count of
     // loads issued after each one, so the scheduler may not reorder the prologue's loads.
-    int blk = blockIdx.x;
+    int blk = wl;
     Slot r0, r1;
 #pragma unroll
     for (int i = 0; i < TPW; ++i) {
@@ -610,10 +683,10 @@ static hipError_t launch_score_mt(const ScoreArgs& a, hipStream_t s) {
     constexpr int M = MT <= 4 ? MT : 4;
     if (a.hist) {
       const int gx = stream_grid(a, resident_workgroups(score_stream_kernel<M, DI, true>));
-      hipLaunchKernelGGL((score_stream_kernel<M, DI, true>), dim3(gx, a.B), dim3(kScoreThreads), 0, s, a);
+      hipLaunchKernelGGL((score_stream_kernel<M, DI, true>), dim3(gx * a.B), dim3(kScoreThreads), 0, s, a);
     } else {
       const int gx = stream_grid(a, resident_workgroups(score_stream_kernel<M, DI, false>));
-      hipLaunchKernelGGL((score_stream_kernel<M, DI, false>), dim3(gx, a.B), dim3(kScoreThreads), 0, s, a);
+      hipLaunchKernelGGL((score_stream_kernel<M, DI, false>), dim3(gx * a.B), dim3(kScoreThreads), 0, s, a);
     }
     return hipGetLastError();
   }

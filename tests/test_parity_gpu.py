@@ -74,6 +74,22 @@ def test_score_dense_streaming(lib, Hi, Di, scaled):
         assert ok, f"query {t}: {msg}"
 
 
+def test_score_dense_streaming_lengths_an_order_of_magnitude_apart(lib):
+    """The streaming kernel deals its workgroups to the sequences in proportion to their
+    lengths: five rows between 17K and 300K positions, every score against the oracle."""
+    wl = gen("decode_8k", B=5, lengths=(17000, 300000))
+    announce(f"score streaming lengths {wl.seq_start.tolist()}")
+    S = gpu_score(lib, wl)
+    sync()
+    a = np_inputs(wl)
+    S_ref = ref.score(a["qI"], a["w"], a["kI"], a["kscale"], a["seq_start"], a["q_start"], a["q_pos"],
+                      ld=wl.max_ctx)
+    S_gpu = S.cpu().numpy().astype(np.float64)
+    for t in range(wl.T):
+        ok, msg = close_scores(S_gpu[t], S_ref[t])
+        assert ok, f"query {t}: {msg}"
+
+
 def test_score_dense_streaming_uneven_queries(lib):
     """As many queries as sequences, but two on one sequence (one mid-sequence) and none on
     the other: the streaming kernel re-streams the keys per query and scores only j <= p."""
@@ -709,6 +725,10 @@ def _with_queries(wl, q_start, q_pos):
 
 def test_decode_step_streaming_histogram(lib):
     _decode_check(lib, gen("decode_512k", B=2, lengths=(140000, 160000)))
+
+
+def test_decode_step_streaming_unequal_lengths(lib):
+    _decode_check(lib, gen("decode_512k", B=4, lengths=(20000, 250000)))
 
 
 def test_decode_step_streaming_short_query(lib):
