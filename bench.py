@@ -224,10 +224,13 @@ class Timer:
 STREAM_READ_SHAPES = ((256, 8), (512, 4), (1024, 2), (1024, 1), (2048, 1))
 
 
-def hbm_reference(timer, dev):
+def hbm_reference(timer, dev, sizes=()):
     """What plain streaming kernels reach on this machine (cold, GB/s): a 1 GiB device-to-device
     copy (bytes read + written), a 1 GiB read by torch's sum, and the same 1 GiB read by the
-    streaming-read reference kernel (libsmqa_bench.so) at its best launch shape."""
+    streaming-read reference kernel (libsmqa_bench.so) at its best launch shape.  The same
+    kernel also reads each byte count in `sizes` (an HBM-bound stage's algorithmic bytes), at
+    the best of its launch shapes for that count, so the stage can be set against a plain
+    read of exactly its bytes (launch ramp and tail included)."""
     import ctypes
     import torch
     src = torch.ones(1 << 28, dtype=torch.float32, device=dev)
@@ -245,17 +248,29 @@ def hbm_reference(timer, dev):
                        ctypes.c_void_p]
         out = torch.empty(max(g for g, _ in STREAM_READ_SHAPES) * 256, dtype=torch.int32, device=dev)
         stream = torch.cuda.current_stream().cuda_stream
-        best = None
-        for grid, depth in STREAM_READ_SHAPES:
-            def call():
-                if fn(src.data_ptr(), 1 << 30, out.data_ptr(), grid, depth, stream) != 0:
-                    raise RuntimeError("smqa_bench_stream_read failed")
-            us = stats(timer.cold(call, 10))["median"]
-            gbs = (1 << 30) / (us * 1e-6) / 1e9
-            if best is None or gbs > best[0]:
-                best = (gbs, grid, depth)
+
+        def best_read(nbytes):
+            best = None
+            for grid, depth in STREAM_READ_SHAPES:
+                def call():
+                    if fn(src.data_ptr(), nbytes, out.data_ptr(), grid, depth, stream) != 0:
+                        raise RuntimeError("smqa_bench_stream_read failed")
+                us = stats(timer.cold(call, 10))["median"]
+                gbs = nbytes / (us * 1e-6) / 1e9
+                if best is None or gbs > best[0]:
+                    best = (gbs, grid, depth, us)
+            return best
+
+        best = best_read(1 << 30)
         res["stream_read_GBs"] = round(best[0], 1)
         res["stream_read_shape"] = {"workgroups": best[1], "loads_in_flight_per_thread": best[2]}
+        same = {}
+        for nbytes in sorted({min(int(n) // 16 * 16, 1 << 30) for n in sizes if n >= 16}):
+            b = best_read(nbytes)
+            same[str(nbytes)] = {"us": round(b[3], 2), "GBs": round(b[0], 1),
+                                 "shape": {"workgroups": b[1], "loads_in_flight_per_thread": b[2]}}
+        if same:
+            res["stream_read_same_bytes"] = same
     del src, dst
     return res
 
@@ -552,13 +567,18 @@ def main():
     extra = {}
     for nm in [x for x in args.also.split(",") if x and x != args.workload]:
         extra[nm] = measure(nm, args.steps, args.warmup, timer)
-    hbm_ref = hbm_reference(timer, "cuda")
-    # HBM-bound stages also against the streaming read measured on this machine
+    hbm_rows = [r for res in [main_res, *extra.values()] for r in res.get("stage_roofline", {}).values()
+                if r["bound"] == "hbm"]
+    hbm_ref = hbm_reference(timer, "cuda", [r["algorithmic_bytes"] for r in hbm_rows])
+    # HBM-bound stages also against the streaming read measured on this machine: of 1 GiB, and
+    # of exactly the stage's algorithmic bytes
     if hbm_ref.get("stream_read_GBs"):
-        for res in [main_res, *extra.values()]:
-            for r in res.get("stage_roofline", {}).values():
-                if r["bound"] == "hbm":
-                    r["frac_of_stream_read"] = round(r["achieved"] / hbm_ref["stream_read_GBs"], 4)
+        same = hbm_ref.get("stream_read_same_bytes", {})
+        for r in hbm_rows:
+            r["frac_of_stream_read"] = round(r["achieved"] / hbm_ref["stream_read_GBs"], 4)
+            ref = same.get(str(min(int(r["algorithmic_bytes"]) // 16 * 16, 1 << 30)))
+            if ref:
+                r["frac_of_same_bytes_read"] = round(r["achieved"] / ref["GBs"], 4)
     cpu = None if args.no_cpu else cpu_baseline(args.workload, args.cpu_seconds)
     cfg = main_res["config"]
     med = main_res["step_us_cold"]["median"]

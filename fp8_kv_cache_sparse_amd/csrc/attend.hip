@@ -1015,7 +1015,9 @@ __global__ __launch_bounds__(kAttThreads) void attend_kernel(AttendArgs a, int S
 // dims per thread with 16-byte loads and stores (the boundary requires a 256-byte aligned
 // workspace and a 16-byte aligned output; D is a multiple of 128).  Every thread issues its
 // S partial loads before the weights are known, so the merge costs one round trip to
-// memory (SMAX >= S partials per output, at most 64).
+// memory (SMAX >= S partials per output, at most 64; the instantiations 16, 24, 32, 64
+// cover the split counts the planner makes with few repeated loads: k = 2048 with up to
+// five queries takes 24).
 template <int SMAX>
 __global__ __launch_bounds__(128) void attend_merge_kernel(AttendArgs a, int S) {
   __shared__ float wts[64];
@@ -1242,6 +1244,7 @@ hipError_t launch_attend_merge(const AttendArgs& a, int S, hipStream_t s) {
   if (S == 1) return hipSuccess;
   const dim3 grid((a.D / 4 + 127) / 128, a.T * a.Hq);
   if (S <= 16) hipLaunchKernelGGL(attend_merge_kernel<16>, grid, dim3(128), 0, s, a, S);
+  else if (S <= 24) hipLaunchKernelGGL(attend_merge_kernel<24>, grid, dim3(128), 0, s, a, S);
   else if (S <= 32) hipLaunchKernelGGL(attend_merge_kernel<32>, grid, dim3(128), 0, s, a, S);
   else hipLaunchKernelGGL(attend_merge_kernel<64>, grid, dim3(128), 0, s, a, S);
   return hipGetLastError();
@@ -1307,6 +1310,7 @@ hipError_t launch_attend_fused(const AttendArgs& a0, hipStream_t s) {
   if (e != hipSuccess || p.S == 1) return e;
   const dim3 grid(a.T * a.Hq);
   if (p.S <= 16) hipLaunchKernelGGL(attend_fused_epilogue_kernel<16>, grid, dim3(512), 0, s, a, p.S);
+  else if (p.S <= 24) hipLaunchKernelGGL(attend_fused_epilogue_kernel<24>, grid, dim3(512), 0, s, a, p.S);
   else if (p.S <= 32) hipLaunchKernelGGL(attend_fused_epilogue_kernel<32>, grid, dim3(512), 0, s, a, p.S);
   else hipLaunchKernelGGL(attend_fused_epilogue_kernel<64>, grid, dim3(512), 0, s, a, p.S);
   return hipGetLastError();

@@ -112,6 +112,34 @@ def test_score_dense_streaming_uneven_queries(lib):
         assert ok, f"query {t}: {msg}"
 
 
+# Several queries per sequence: the block kernel splits each sequence's queries into up to
+# eight equal parts (grid z) to fill the resident workgroup slots.  Uneven query counts (one
+# sequence without queries, parts of one query, empty trailing parts) and queries in the
+# middle of their rows, on the 64- and the 256-position block widths.
+@pytest.mark.parametrize("lengths,qps", [(3000, 8), (140000, 6)])
+def test_score_dense_query_parts_uneven(lib, lengths, qps):
+    import dataclasses
+    wl = gen("replay_h100k", B=3, lengths=lengths, replay=(lengths, qps))
+    T = wl.T
+    n = int(wl.seq_start[1])
+    q_start = torch.tensor([0, qps - 1, qps - 1, T], dtype=torch.int32, device=DEV)
+    q_pos = wl.q_pos.clone()
+    q_pos[1] = n // 2                        # mid-row queries in the first and last sequence
+    q_pos[T - 3] = n // 3
+    q_pos[T - 1] = 5
+    wl = dataclasses.replace(wl, q_start=q_start, q_pos=q_pos)
+    announce(f"score query parts lengths={lengths} q_start={q_start.tolist()}")
+    S = gpu_score(lib, wl)
+    sync()
+    a = np_inputs(wl)
+    S_ref = ref.score(a["qI"], a["w"], a["kI"], a["kscale"], a["seq_start"], a["q_start"], a["q_pos"],
+                      ld=wl.max_ctx)
+    S_gpu = S.cpu().numpy().astype(np.float64)
+    for t in range(T):
+        ok, msg = close_scores(S_gpu[t], S_ref[t])
+        assert ok, f"query {t}: {msg}"
+
+
 def test_score_integer_inputs_bit_exact(lib):
     announce("score integer-valued inputs")
     g = torch.Generator(device=DEV).manual_seed(5)
