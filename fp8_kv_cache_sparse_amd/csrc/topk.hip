@@ -263,16 +263,23 @@ __device__ __forceinline__ int wave_append(int* counter, bool flag) {
 // an earlier kernel) plus the nwin columns win[] (in LDS).  Rounds of NT*PER words: each
 // thread puts its PER consecutive words in the LDS bitmap `lbits` (transposed: word j of
 // thread i at j * NT + i, so every access of a wave is conflict-free), the round's winners
-// are OR-ed in, one block scan of the per-thread counts gives each thread its output offset,
-// each thread writes its columns to the LDS staging array `out` (k entries), and the round's
-// outputs are copied to dst with coalesced stores (positions looked up in the candidate
-// list there, in parallel).  first[] holds this thread's words of the first round, loaded
-// by the caller in advance (garbage past nwords is masked here).
+// are OR-ed in, and one block scan of the per-thread bit counts gives each thread the output
+// offset of its first bit.  Each nonzero word whose first bit is an output is then filed
+// under that offset as one 8-byte pair in `fw` (its bits and its first column; kMaxK
+// entries, the bits cleared to 0 beforehand), and the output slots are shared out over the
+// threads: the thread of a
+// slot where a word starts writes that word's columns to the LDS staging array `out`.  A
+// thread's loop then runs over the bits of one word, not over every bit of its PER words
+// (a short row leaves most threads without words and a few with hundreds of bits).  The
+// round's outputs are copied to dst with coalesced stores (positions looked up in the
+// candidate list there, in parallel).  first[] holds this thread's words of the first round,
+// loaded by the caller in advance (garbage past nwords is masked here).
 constexpr int kSelPer = 16;
+constexpr int kMaxK = 4096;            // the largest k the read-out stages
 template <int NT>
 __device__ void write_selection(const TopkArgs& a, int t, const unsigned* bits, int nwords,
                                 const uint4 (&first)[kSelPer / 4], const int* win, int nwin,
-                                unsigned* lbits, int* out, int32_t* dst, int* scan_lds) {
+                                unsigned* lbits, uint2* fw, int* out, int32_t* dst, int* scan_lds) {
   constexpr int PER = kSelPer;
   int done = 0;
   for (int r0 = 0; r0 < nwords && done < a.k; r0 += NT * PER) {
@@ -309,17 +316,25 @@ __device__ void write_selection(const TopkArgs& a, int t, const unsigned* bits, 
     int cnt = 0;
 #pragma unroll
     for (int j = 0; j < PER; ++j) cnt += __popc(wv[j]);
+    for (int i = threadIdx.x; i < kMaxK; i += NT) fw[i].x = 0u;
+    // (the block scan's barriers order the clearing before the filing below)
     int total;
     int off = block_exclusive_scan<NT>(cnt, scan_lds, &total);
     const int nout = min(total, a.k - done);
-    if (off < nout) {
 #pragma unroll
-      for (int j = 0; j < PER; ++j) {
-        unsigned m = wv[j];
-        while (m && off < nout) {
-          out[off++] = 32 * (w0 + j) + __ffs(m) - 1;
-          m &= m - 1;
-        }
+    for (int j = 0; j < PER; ++j) {
+      if (wv[j] != 0u && off < nout) fw[off] = make_uint2(wv[j], (unsigned)(32 * (w0 + j)));
+      off += __popc(wv[j]);
+    }
+    __syncthreads();
+    for (int o = threadIdx.x; o < nout; o += NT) {
+      const uint2 f = fw[o];
+      unsigned m = f.x;
+      const int c0 = (int)f.y;
+      int p = o;
+      while (m && p < nout) {
+        out[p++] = c0 + __ffs(m) - 1;
+        m &= m - 1;
       }
     }
     __syncthreads();
@@ -718,8 +733,9 @@ __global__ __launch_bounds__(1024) void topk_finish_kernel(TopkArgs a, TopkWs w)
   __shared__ int scan_lds[NT / 64];
   __shared__ int sh[4];
   __shared__ int nwin;
-  __shared__ int out[4096];           // read-out staging (k <= 4096)
-  static_assert(2 * kCap >= NT * kSelPer, "read-out bitmap does not fit");
+  __shared__ int out[kMaxK];          // read-out staging (k <= 4096)
+  // the read-out's LDS bitmap (NT * kSelPer words), then its filed words and columns
+  static_assert(2 * kCap >= NT * kSelPer + 2 * kMaxK, "read-out bitmap does not fit");
   unsigned* ck = pool;
   int* cc = (int*)(pool + kCap);
   int* win = (int*)hist;
@@ -732,11 +748,14 @@ __global__ __launch_bounds__(1024) void topk_finish_kernel(TopkArgs a, TopkWs w)
   // the first kPre candidates of the list (inside its kCap slots).
   constexpr int kPre = 3;
   const TopkState st = w.st[t];
+  // (a thread past the bitmap loads its last words instead, so every load is issued
+  // without a branch; the read-out masks words past the row's count)
   uint4 first[kSelPer / 4];
+  {
+    const int fw = min(kSelPer * (int)threadIdx.x, w.bw - kSelPer);
 #pragma unroll
-  for (int j = 0; j < kSelPer / 4; ++j)
-    first[j] = kSelPer * (int)threadIdx.x < w.bw ? *(const uint4*)(bits + kSelPer * threadIdx.x + 4 * j)
-                                                  : make_uint4(0u, 0u, 0u, 0u);
+    for (int j = 0; j < kSelPer / 4; ++j) first[j] = *(const uint4*)(bits + fw + 4 * j);
+  }
   uint2 pre[kPre];
 #pragma unroll
   for (int j = 0; j < kPre; ++j) pre[j] = cand[threadIdx.x + NT * j];
@@ -783,8 +802,8 @@ __global__ __launch_bounds__(1024) void topk_finish_kernel(TopkArgs a, TopkWs w)
     }
   }
   __syncthreads();
-  write_selection<NT>(a, t, bits, (ncols + 31) / 32, first, win, nwin, pool, out, a.idx + (int64_t)t * a.k,
-                      scan_lds);
+  write_selection<NT>(a, t, bits, (ncols + 31) / 32, first, win, nwin, pool, (uint2*)(pool + NT * kSelPer),
+                      out, a.idx + (int64_t)t * a.k, scan_lds);
 }
 
 hipError_t launch_topk(const TopkArgs& a, hipStream_t s) {

@@ -237,8 +237,9 @@ def _topk_case(lib, S_host, k, cand=None, q_pos=None):
     return idx
 
 
+# (rows past 524,288 columns read their selection out in two rounds of 16,384 bitmap words)
 @pytest.mark.parametrize("n,k", [(8192, 2048), (4096, 256), (16384, 4096), (100_000, 2048),
-                                 (524_288, 2048), (30_000, 7)])
+                                 (524_288, 2048), (30_000, 7), (1_000_000, 4096)])
 def test_topk_random(lib, n, k):
     announce(f"topk random n={n} k={k}")
     rng = np.random.default_rng(n + k)
