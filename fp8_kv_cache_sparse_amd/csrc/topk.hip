@@ -592,24 +592,32 @@ __global__ __launch_bounds__(kLongThreads) void topk_hist_kernel(TopkArgs a, Top
 
 // The query's histogram was completed by an earlier kernel (the histogram kernel, or the
 // streaming score kernel); each workgroup reads it (16 KB, issued with the row loads) and
-// finds d1 itself, and the query's first chunk publishes it for the finish kernel.
+// finds d1 itself, and the query's first chunk publishes it for the finish kernel.  A
+// workgroup takes HC consecutive chunks (HC = 2 when a call has thousands of chunks, so the
+// histogram read and the threshold scan are paid once per two chunks; one chunk otherwise,
+// for parallelism).  Its candidates (entries of bin d1) go to the query's list with one
+// atomic per workgroup: staged in LDS with one chunk, written straight from registers after
+// a block scan of the per-thread counts with two (an LDS stage for two chunks would cost
+// occupancy).
+template <int HC>
 __global__ __launch_bounds__(kLongThreads) void topk_collect_kernel(TopkArgs a, TopkWs w) {
   constexpr int NT = kLongThreads;
-  __shared__ uint2 buf[kChunk];
+  constexpr int NV = HC * kPerThread;
+  __shared__ uint2 buf[HC == 1 ? kChunk : 1];
   __shared__ int scan_lds[NT / 64];
   __shared__ int sh[4];
   __shared__ int nbuf, gbase;
   const int t = blockIdx.y;
-  const int c0 = blockIdx.x * kChunk;
+  const int c0 = blockIdx.x * HC * kChunk;
   const float* row = a.scores + (int64_t)t * a.ld;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   // Every load is issued before the query's column count arrives: the row bounded by the
   // host's max_ctx (<= ld), then masked to the query's own count.
   // wave `wave`, step u covers columns c0 + 64*(wave + 4u) + lane
   const TopkState st0 = w.st[t];
-  float v[kPerThread];
+  float v[NV];
 #pragma unroll
-  for (int u = 0; u < kPerThread; ++u) {
+  for (int u = 0; u < NV; ++u) {
     const int i = c0 + 64 * (wave + 4 * u) + lane;
     v[u] = i < a.max_ctx ? row[i] : -__builtin_inff();
   }
@@ -667,35 +675,77 @@ __global__ __launch_bounds__(kLongThreads) void topk_collect_kernel(TopkArgs a, 
   }
   const int ncols = st0.ncols;
 #pragma unroll
-  for (int u = 0; u < kPerThread; ++u)
+  for (int u = 0; u < NV; ++u)
     if (c0 + 64 * (wave + 4 * u) + lane >= ncols) v[u] = -__builtin_inff();
   const bool keep_bin = d1 >= 0 && cnt1 <= kCap;
-  if (threadIdx.x == 0) nbuf = 0;
-  __syncthreads();
   unsigned* bits = w.bits + (size_t)t * w.bw;
+  const int bcols = 32 * w.bw;                       // columns the query's bitmap covers
+  int cin = 0;
+  if (HC == 1) {
+    if (threadIdx.x == 0) nbuf = 0;
+    __syncthreads();
+  }
 #pragma unroll
-  for (int u = 0; u < kPerThread; ++u) {
+  for (int u = 0; u < NV; ++u) {
     const int cb = c0 + 64 * (wave + 4 * u);
     const unsigned key = score_key(v[u]);
     const int digit = (int)(key >> 20);
     const bool up = key != 0u && (d1 < 0 || digit > d1);
     const bool in = key != 0u && keep_bin && digit == d1;
     const unsigned long long m = __ballot(up);
-    if (lane == 0) {
+    if (lane == 0 && cb < bcols) {                   // (a last workgroup's chunks may pass it)
       bits[cb / 32] = (unsigned)m;
       bits[cb / 32 + 1] = (unsigned)(m >> 32);
     }
-    const int slot = wave_append(&nbuf, in);
-    if (in) buf[slot] = make_uint2(key, (unsigned)(cb + lane));
+    if constexpr (HC == 1) {
+      const int slot = wave_append(&nbuf, in);
+      if (in) buf[slot] = make_uint2(key, (unsigned)(cb + lane));
+    } else {
+      cin += in;
+    }
   }
+  if constexpr (HC == 1) {
+    // one chunk: the candidates were staged in LDS, one atomic and a coalesced copy
+    __syncthreads();
+    const int nb = nbuf;
+    if (nb == 0) return;
+    if (threadIdx.x == 0) gbase = atomicAdd(&w.st[t].ncand, nb);
+    __syncthreads();
+    uint2* cand = w.cand + (int64_t)t * kCap;
+    for (int i = threadIdx.x; i < nb; i += NT)
+      if (gbase + i < kCap) cand[gbase + i] = buf[i];
+    return;
+  }
+  int ntot;
+  int off = block_exclusive_scan<NT>(cin, scan_lds, &ntot);
+  if (ntot == 0) return;                             // uniform
+  if (threadIdx.x == 0) gbase = atomicAdd(&w.st[t].ncand, ntot);
   __syncthreads();
-  const int nb = nbuf;
-  if (nb == 0) return;
-  if (threadIdx.x == 0) gbase = atomicAdd(&w.st[t].ncand, nb);
-  __syncthreads();
+  off += gbase;
   uint2* cand = w.cand + (int64_t)t * kCap;
-  for (int i = threadIdx.x; i < nb; i += NT)
-    if (gbase + i < kCap) cand[gbase + i] = buf[i];
+#pragma unroll
+  for (int u = 0; u < NV; ++u) {
+    // (the key is recomputed rather than kept from the first pass: 64 more live registers
+    // would cut the workgroups per CU)
+    float x = v[u];
+    asm volatile("" : "+v"(x));
+    const unsigned key = score_key(x);
+    if (key != 0u && keep_bin && (int)(key >> 20) == d1) {
+      if (off < kCap) cand[off] = make_uint2(key, (unsigned)(c0 + 64 * (wave + 4 * u) + lane));
+      ++off;
+    }
+  }
+}
+
+// Chunks per collect workgroup: two once a call has thousands of chunks (the replay chunk's
+// 25,600: 348 -> 308 us for the top-k; four chunks held 199 registers and were slower), else
+// one.
+static hipError_t launch_collect(const TopkArgs& a, const TopkWs& w, int nch, hipStream_t s) {
+  if ((int64_t)nch * a.T >= 4096)
+    hipLaunchKernelGGL(topk_collect_kernel<2>, dim3((nch + 1) / 2, a.T), dim3(kLongThreads), 0, s, a, w);
+  else
+    hipLaunchKernelGGL(topk_collect_kernel<1>, dim3(nch, a.T), dim3(kLongThreads), 0, s, a, w);
+  return hipGetLastError();
 }
 
 struct LdsPairSrc {
@@ -823,7 +873,7 @@ hipError_t launch_topk(const TopkArgs& a, hipStream_t s) {
   } else {
     hipLaunchKernelGGL(topk_hist_kernel<1>, dim3(nch, a.T), dim3(kLongThreads), 0, s, a, w);
   }
-  hipLaunchKernelGGL(topk_collect_kernel, dim3(nch, a.T), dim3(kLongThreads), 0, s, a, w);
+  launch_collect(a, w, nch, s);
   hipLaunchKernelGGL(topk_finish_kernel, dim3(a.T), dim3(1024), 0, s, a, w);
   return hipGetLastError();
 }
@@ -846,7 +896,7 @@ hipError_t launch_topk_from_hist(const TopkArgs& a, hipStream_t s) {
   if (a.max_ctx <= kSmallN) return launch_topk(a, s);
   TopkWs w = carve(a.ws, a.T, a.max_ctx);
   const int nch = (a.max_ctx + kChunk - 1) / kChunk;
-  hipLaunchKernelGGL(topk_collect_kernel, dim3(nch, a.T), dim3(kLongThreads), 0, s, a, w);
+  launch_collect(a, w, nch, s);
   hipLaunchKernelGGL(topk_finish_kernel, dim3(a.T), dim3(1024), 0, s, a, w);
   return hipGetLastError();
 }
