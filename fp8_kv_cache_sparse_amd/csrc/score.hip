@@ -621,9 +621,9 @@ static int resident_workgroups(K kernel) {
 // workgroups resident at once: the count that maximises the filled share of the last
 // round, less 1.5% per extra part (each part reloads its block's keys and restages q), at
 // most 8 parts and no more than the queries per sequence.  One block per workgroup is a
-// coarse unit: eight sessions of 100K positions make 3,136 workgroups, 3.06 rounds at four
-// per CU, so the last round runs a twentieth of the CUs; four parts (0.94 of the last
-// round filled) score the same bits 4-6% faster.
+// coarse unit: eight sessions of 100K positions make 3,128 workgroups, 6.1 rounds of the 512
+// that the occupancy query reports resident at once, so the last round is a ninth full;
+// three parts (the last of 19 rounds 0.97 full) score the same bits 4-6% faster.
 static int query_parts(int64_t wgs, int T, int B, int slots) {
   const int qmax = std::max(1, std::min(8, (T + B - 1) / std::max(B, 1)));
   int best = 1;
