@@ -247,6 +247,28 @@ def test_topk_random(lib, n, k):
     _topk_case(lib, S, k, q_pos=np.array([n - 1, n // 2, n - 3]))
 
 
+def test_topk_many_chunks_two_per_workgroup(lib):
+    """Calls of at least 4,096 chunks of 4,096 columns take the collect kernel with two chunks
+    per workgroup: an odd chunk count (the last workgroup's second chunk lies past the
+    bitmap), rows ending mid-chunk, just past one chunk and shorter than k, a row whose
+    threshold bin overflows the candidate list (every score equal), and one with a tie
+    crowd at the k-th place."""
+    n, T, k = 346_000, 49, 2048                      # 85 chunks x 49 queries
+    rng = np.random.default_rng(5)
+    S = (rng.standard_normal((T, n)) * 10 + 50).astype(np.float32)
+    S[3] = 7.0                                       # one bin holds the whole row
+    S[4, : 2 * k] = 120.0                            # 4,096 ties across the k-th place
+    q_pos = np.full(T, n - 1)
+    q_pos[1] = n // 2 + 3
+    q_pos[2] = 4097
+    q_pos[5] = 100
+    q_pos[6] = 8191
+    idx = _topk_case(lib, S, k, q_pos=q_pos)
+    assert idx[3].tolist() == list(range(k))
+    assert idx[4].tolist() == list(range(k))
+    assert np.all(idx[5, 101:] == -1) and idx[5, :101].tolist() == list(range(101))
+
+
 @pytest.mark.parametrize("n", [5000, 60_000])
 def test_topk_ties_take_lowest_positions(lib, n):
     announce(f"topk constant scores n={n}")
