@@ -49,10 +49,10 @@
 // attend_merge_kernel combines by log-sum-exp.
 //
 // kMXS (decode_step on dense rows of at most kSelCols columns, D = 1664): instead of reading
-// the positions of its tiles, every workgroup of a query loads the query's scores with q and
+// the positions of its tiles, every workgroup of a query loads the query's scores and
 // computes the whole top-k itself (the selection topk_select makes, bit for bit) before its
 // first gather; the first workgroup of the query writes the selection out.  The step then has
-// no top-k launch, and the q staging overlaps the score loads.
+// no top-k launch, and q is staged into LDS while the selection runs.
 #include <type_traits>
 
 #include "common.h"
@@ -560,7 +560,7 @@ __global__ __launch_bounds__(kThreads) void attend_kernel(AttendArgs a, int S, i
         }
     }
   };
-  if constexpr (QLDS) {
+  auto stage_q = [&]() __attribute__((always_inline)) {
     // rows 8 rr + wave, 16-byte piece pc = 64 jj + lane of each (the tail instruction of a
     // row runs on fewer lanes)
     constexpr int QP = D / 8;
@@ -575,10 +575,16 @@ __global__ __launch_bounds__(kThreads) void attend_kernel(AttendArgs a, int S, i
         if (pc < QP) gload16(qsrc + (int64_t)r * 2 * D + 16 * pc, lds_addr(smem + r * QS + 1024 * jj));
       }
     }
+  };
+  // kMXS stages q after its scores and the sequence lookup have arrived, so the select starts
+  // on them while q is still in flight (the q copies land where the select does not work)
+  if constexpr (QLDS) {
+    if constexpr (!SEL) stage_q();
   } else {
     build_q();
   }
-  // kMXS: the query's scores, columns tid + 512 u, requested with q
+  // kMXS: the query's scores, columns tid + 512 u, requested first (q follows the sequence
+  // lookup)
   constexpr int kSPer = kSelCols / kThreads;
   float sv[SEL ? kSPer : 1];
   if constexpr (SEL) {
@@ -601,6 +607,7 @@ __global__ __launch_bounds__(kThreads) void attend_kernel(AttendArgs a, int S, i
     c.jmax = min(si.p, si.len - 1);
     c.lo_win = max(max(c.p - c.W + 1, 0), si.clip);
   }
+  if constexpr (SEL && QLDS) stage_q();
   if (tid < 32) {
     mref[tid] = -__builtin_inff();
     malpha[tid] = 1.0f;
@@ -617,7 +624,7 @@ __global__ __launch_bounds__(kThreads) void attend_kernel(AttendArgs a, int S, i
   // a range of at most kNBuf tiles is gathered at once (one memory latency for all of it),
   // a longer one two tiles ahead of the products
   const bool pre = te - tb <= kNBuf;
-  __builtin_amdgcn_s_waitcnt(0);
+  if constexpr (!SEL) __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   if constexpr (SEL) {
     // The query's top-k as topk_select takes it (the k largest scores of columns 0 ..
@@ -785,6 +792,10 @@ __global__ __launch_bounds__(kThreads) void attend_kernel(AttendArgs a, int S, i
     __syncthreads();
   }
   if constexpr (QLDS) {
+    if constexpr (SEL) {
+      __builtin_amdgcn_s_waitcnt(0);               // this wave's q copies landed
+      __syncthreads();
+    }
     build_q();
     __syncthreads();                               // q read: the tile buffers are free
   }
