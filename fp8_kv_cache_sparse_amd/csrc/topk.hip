@@ -26,7 +26,7 @@
 namespace smqa {
 
 constexpr int kSmallN = 16384;
-constexpr int kChunk = 4096;          // columns per workgroup in the long-row kernels
+constexpr int kChunk = 4096;          // columns per chunk (a long-row workgroup takes 1, 2 or 4)
 constexpr int kCap = 12288;           // candidate-list capacity per query (entries of bin d1)
 constexpr int kHistBins = kTopkBins;
 
